@@ -1,0 +1,447 @@
+"""Pins for the CPU oracle: each checks it against something other than itself.
+
+Kinds of pin used here: brute force written from 3D token coordinates in the
+original order (no fractal permutation involved), exhaustive subset search,
+closed forms, library routines (torch scaled_dot_product_attention, scipy
+softmax) and the hand-worked examples in tests/golden/. The mutation test at
+the bottom plants plausible mistakes in the oracle and checks that some pin
+fails for each one.
+"""
+import itertools
+import json
+import math
+import os
+from fractions import Fraction
+
+import numpy as np
+import pytest
+import scipy.special
+import torch
+
+from oracle import nabla_ref as R
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+
+
+def _rand(shape, seed):
+    return np.random.default_rng(seed).standard_normal(shape)
+
+
+def _coords(g):
+    t, y, x = np.meshgrid(np.arange(g.T), np.arange(g.Hs), np.arange(g.Ws), indexing="ij")
+    return t.reshape(-1), y.reshape(-1), x.reshape(-1)
+
+
+def _attention_original_order(Q, K, V, allowed, scale):
+    """Brute force in the original token order, one query at a time."""
+    N = Q.shape[0]
+    O = np.zeros_like(V)
+    for n in range(N):
+        a = allowed(n)
+        if not a.any():
+            continue
+        s = scale * (K[a] @ Q[n])
+        w = np.exp(s - s.max())
+        O[n] = (w / w.sum()) @ V[a]
+    return O
+
+
+# ---------------------------------------------------------------- P1
+def test_p1_full_threshold_is_full_attention():
+    """thr = 1 keeps every block, so the path must equal plain softmax(QK^T/sqrt(d))V."""
+    g = R.Geom(B=1, H=2, T=3, Hs=16, Ws=24, d=16)
+    Q, K, V = (_rand((g.B, g.H, g.N, g.d), s) for s in (1, 2, 3))
+    for sta in [(0, 0, 0), (3, 3, 3)]:
+        res = R.nabla_attention(Q, K, V, g, R.MaskParams(mode="cdf", thr=1.0, sta=sta))
+        assert res.mask.mask.all()
+        ref = torch.nn.functional.scaled_dot_product_attention(
+            torch.from_numpy(Q), torch.from_numpy(K), torch.from_numpy(V)).numpy()
+        np.testing.assert_allclose(res.O, ref, rtol=1e-12, atol=1e-12)
+        # LSE against the library log-sum-exp of the full score rows (fractal order).
+        Qr, Kr = R.reorder(Q, g), R.reorder(K, g)
+        lse = scipy.special.logsumexp(Qr @ np.swapaxes(Kr, -1, -2) / math.sqrt(g.d), axis=-1)
+        np.testing.assert_allclose(res.lse_r, lse, rtol=1e-12)
+
+
+# ---------------------------------------------------------------- P2
+@pytest.mark.parametrize("window", [(3, 3, 3), (1, 3, 5), (3, 1, 1), (5, 5, 5)])
+def test_p2_pure_sta_equals_bruteforce_window(window):
+    """thr = 0 leaves only STA: token (t,y,x) sees (t',y',x') iff every patch offset is within the window."""
+    g = R.Geom(B=1, H=1, T=4, Hs=16, Ws=24, d=8)
+    Q, K, V = (_rand((g.N, g.d), s) for s in (4, 5, 6))
+    res = R.nabla_attention(Q[None, None], K[None, None], V[None, None], g,
+                            R.MaskParams(mode="cdf", thr=0.0, sta=window))
+    t, y, x = _coords(g)
+    r = [(w - 1) // 2 for w in window]
+
+    def allowed(n):
+        return ((np.abs(t - t[n]) <= r[0]) & (np.abs(y // g.P - y[n] // g.P) <= r[1])
+                & (np.abs(x // g.P - x[n] // g.P) <= r[2]))
+
+    ref = _attention_original_order(Q, K, V, allowed, 1 / math.sqrt(g.d))
+    np.testing.assert_allclose(res.O[0, 0], ref, rtol=1e-11, atol=1e-12)
+
+
+def test_p2_random_block_mask_bruteforce():
+    """An arbitrary (asymmetric) block mask, expanded by coordinates in the original order."""
+    g = R.Geom(B=1, H=1, T=3, Hs=16, Ws=16, d=8)
+    Q, K, V = (_rand((g.N, g.d), s) for s in (7, 8, 9))
+    rng = np.random.default_rng(10)
+    M = rng.random((g.nb, g.nb)) < 0.35
+    M[3] = False  # one empty row
+    t, y, x = _coords(g)
+    blk = (t * g.nbh + y // g.P) * g.nbw + x // g.P  # block numbering convention (frame, patch row, patch col)
+    ref = _attention_original_order(Q, K, V, lambda n: M[blk[n], blk], 1 / math.sqrt(g.d))
+    Qr, Kr, Vr = (R.reorder(a, g) for a in (Q, K, V))
+    Or, lse = R.masked_attention_head(Qr, Kr, Vr, M, g, 1 / math.sqrt(g.d))
+    np.testing.assert_allclose(R.inverse_reorder(Or, g), ref, rtol=1e-11, atol=1e-12)
+    assert np.isneginf(lse[3 * g.bs:4 * g.bs]).all() and np.isfinite(np.delete(lse, np.s_[3 * g.bs:4 * g.bs])).all()
+
+
+# ---------------------------------------------------------------- P3
+def _min_prefix_bruteforce(p_frac, thr_frac):
+    """Smallest subset size whose exact mass reaches thr, and all subsets of that size that do."""
+    n = len(p_frac)
+    for size in range(n + 1):
+        hits = [set(c) for c in itertools.combinations(range(n), size) if sum(p_frac[i] for i in c) >= thr_frac]
+        if hits:
+            return size, hits
+    return None, []
+
+
+@pytest.mark.parametrize("seed", range(40))
+def test_p3_minimal_prefix_bruteforce(seed):
+    rng = np.random.default_rng(seed)
+    n = int(rng.integers(1, 11))
+    ints = rng.integers(1, 50, size=n)
+    if seed % 3 == 0 and n > 2:
+        ints[rng.integers(n)] = ints[0]  # force ties
+    tot = int(ints.sum())
+    p_frac = [Fraction(int(v), tot) for v in ints]
+    p = np.array([float(f) for f in p_frac])
+    for thr_num in range(1, 2 * tot, 3):
+        thr_frac = Fraction(2 * thr_num + 1, 4 * tot)  # never equal to a subset mass
+        if thr_frac >= 1:
+            break
+        keep, _ = R.cdf_select_row(p, float(thr_frac))
+        size, hits = _min_prefix_bruteforce(p_frac, thr_frac)
+        kept = set(np.nonzero(keep)[0].tolist())
+        assert len(kept) == size and kept in hits
+        # Among equal probabilities, lower indices are kept first.
+        for i, j in itertools.combinations(range(n), 2):
+            if p_frac[i] == p_frac[j] and j in kept:
+                assert i in kept
+        if kept and len(kept) < n:
+            assert min(p[list(kept)]) >= max(np.delete(p, list(kept)))
+
+
+def test_p3_invariants_on_generated_rows():
+    from gen import WORKLOADS, make_qkv
+    w = WORKLOADS["tiny"]
+    g = R.Geom(w.B, w.H, w.T, w.Hs, w.Ws, w.d, w.P)
+    Q, K, V = make_qkv(w)
+    Qr, Kr = R.reorder(R.to64(Q), g), R.reorder(R.to64(K), g)
+    res = R.build_block_mask(R.block_means(Qr, g), R.block_means(Kr, g), g,
+                             R.MaskParams(mode="cdf", thr=w.thr, sta=(0, 0, 0)))
+    for idx in np.ndindex(res.sel.shape[:-1]):
+        p, k = res.Pm[idx], res.sel[idx]
+        assert p[k].sum() >= w.thr
+        assert p[k].sum() - p[k].min() < w.thr
+        if (~k).any():
+            assert p[k].min() >= p[~k].max()
+
+
+# ---------------------------------------------------------------- P4
+@pytest.mark.parametrize("T,Hs,Ws,thr,expect", [(21, 32, 56, 0.7, 412), (5, 24, 24, 0.5, 23), (1, 8, 8, 0.3, 1)])
+def test_p4_uniform_rows_keep_lowest_indices(T, Hs, Ws, thr, expect):
+    """All pooled keys equal -> P = 1/nb -> exactly ceil(thr*nb) blocks, the lowest indices."""
+    g = R.Geom(B=1, H=1, T=T, Hs=Hs, Ws=Ws, d=4)
+    assert math.ceil(thr * g.nb) == expect
+    Q = _rand((1, 1, g.N, g.d), 11)
+    K = np.ones((1, 1, g.N, g.d)) * 0.5
+    res = R.build_block_mask(R.block_means(R.reorder(Q, g), g), R.block_means(R.reorder(K, g), g), g,
+                             R.MaskParams(mode="cdf", thr=thr, sta=(0, 0, 0)))
+    expected = np.zeros(g.nb, dtype=bool)
+    expected[:expect] = True
+    assert (res.mask[0, 0] == expected[None, :]).all()
+
+
+def test_dominant_block_row_softmax():
+    """One pooled key dominates every row -> only that block survives a modest threshold.
+
+    Rows, not columns, are normalised: with every row dominated by block 0, a
+    column-wise softmax would spread block 0's mass over all rows.
+    """
+    g = R.Geom(B=1, H=1, T=2, Hs=16, Ws=16, d=4)
+    qbar = np.ones((1, 1, g.nb, g.d))
+    kbar = np.zeros((1, 1, g.nb, g.d))
+    kbar[0, 0, 0] = 10.0
+    res = R.build_block_mask(qbar, kbar, g, R.MaskParams(mode="cdf", thr=0.9, sta=(0, 0, 0)))
+    S = 0.5 * qbar[0, 0] @ kbar[0, 0].T
+    np.testing.assert_allclose(res.Pm[0, 0], scipy.special.softmax(S, axis=-1), rtol=1e-13)
+    assert res.Pm[0, 0, 0, 0] > 0.9
+    assert (res.mask[0, 0, :, 0]).all() and res.mask[0, 0].sum() == g.nb
+
+
+# ---------------------------------------------------------------- P5
+def test_p5_nesting_and_limits():
+    from gen import WORKLOADS, make_qkv
+    w = WORKLOADS["tiny"]
+    g = R.Geom(w.B, w.H, w.T, w.Hs, w.Ws, w.d, w.P)
+    Q, K, _ = make_qkv(w)
+    qbar = R.block_means(R.reorder(R.to64(Q), g), g)
+    kbar = R.block_means(R.reorder(R.to64(K), g), g)
+    prev = None
+    for thr in [0.0, 0.1, 0.3, 0.5, 0.8, 0.95, 0.999, 1.0]:
+        m = R.build_block_mask(qbar, kbar, g, R.MaskParams(mode="cdf", thr=thr, sta=(0, 0, 0))).mask
+        if prev is not None:
+            assert (prev <= m).all()
+        prev = m
+    assert prev.all()
+    prev = None
+    for tau in [0.0, 0.5, 1.0, 2.0, 4.0, 8.0, 1e9]:
+        res = R.build_block_mask(qbar, kbar, g, R.MaskParams(mode="dyn", tau=tau, sta=(0, 0, 0)))
+        if prev is not None:
+            assert (prev <= res.mask).all()
+        if tau == 0.0:
+            assert (res.mask == (res.S == res.S.max(axis=-1, keepdims=True))).all()
+        prev = res.mask
+    assert prev.all()
+
+
+# ---------------------------------------------------------------- P6
+def test_p6_reorder_is_blockwise_bijection():
+    g = R.Geom(B=2, H=3, T=3, Hs=16, Ws=24, d=5)
+    X = _rand((g.B, g.H, g.N, g.d), 12)
+    Xr = R.reorder(X, g)
+    assert np.array_equal(R.inverse_reorder(Xr, g), X)
+    pos = R.fractal_positions(g)
+    assert np.array_equal(np.sort(pos), np.arange(g.N))
+    # Block i of the reordered sequence holds exactly the tokens of patch coords(i).
+    t, y, x = _coords(g)
+    c = R.block_coords(g)
+    for i in range(g.nb):
+        members = np.nonzero(pos // g.bs == i)[0]
+        want = np.nonzero((t == c[i, 0]) & (y // g.P == c[i, 1]) & (x // g.P == c[i, 2]))[0]
+        assert np.array_equal(np.sort(members), want)
+    # Time order is kept: every token of frame t comes before every token of frame t+1.
+    assert (np.diff(pos[np.argsort(pos)] // (g.N // g.T)) >= 0).all()
+    assert (pos // (g.N // g.T) == t).all()
+    # Pooled means: sum over blocks times block size equals the sum over tokens.
+    qbar = R.block_means(Xr, g)
+    np.testing.assert_allclose(qbar.sum(axis=-2) * g.bs, X.sum(axis=-2), rtol=1e-12)
+    np.testing.assert_allclose(qbar[0, 0, 2], X[0, 0][(t == c[2, 0]) & (y // g.P == c[2, 1]) & (x // g.P == c[2, 2])].mean(0))
+
+
+# ---------------------------------------------------------------- P7
+def test_p7_attention_identities():
+    g = R.Geom(B=1, H=1, T=2, Hs=16, Ws=16, d=8)
+    rng = np.random.default_rng(13)
+    M = rng.random((g.nb, g.nb)) < 0.3
+    M[np.arange(g.nb), np.arange(g.nb)] = True
+    Qr, Kr = _rand((g.N, g.d), 14), _rand((g.N, g.d), 15)
+    Vc = np.full((g.N, g.d), 0.75)
+    O, _ = R.masked_attention_head(Qr, Kr, Vc, M, g, 0.3)
+    np.testing.assert_allclose(O, 0.75, rtol=1e-13)
+    Vr = _rand((g.N, g.d), 16)
+    O, _ = R.masked_attention_head(np.zeros_like(Qr), Kr, Vr, M, g, 0.3)
+    allowed = R.expand_to_tokens(M, g)
+    mean = (allowed @ Vr) / allowed.sum(1, keepdims=True)
+    np.testing.assert_allclose(O, mean, rtol=1e-11, atol=1e-13)
+    onehot = np.eye(g.N)[:, : g.N]
+    O, _ = R.masked_attention_head(Qr, Kr, onehot, M, g, 0.3)
+    np.testing.assert_allclose(O.sum(1), 1.0, rtol=1e-12)
+    assert (O[~allowed] == 0).all()
+
+
+# ---------------------------------------------------------------- P9
+def test_p9_dyn_vs_probability_ratio():
+    from gen import WORKLOADS, make_qkv
+    w = WORKLOADS["tiny"]
+    g = R.Geom(w.B, w.H, w.T, w.Hs, w.Ws, w.d, w.P)
+    Q, K, _ = make_qkv(w)
+    qbar = R.block_means(R.reorder(R.to64(Q), g), g)
+    kbar = R.block_means(R.reorder(R.to64(K), g), g)
+    for tau in [0.05, 0.2, 1.0]:
+        res = R.build_block_mask(qbar, kbar, g, R.MaskParams(mode="dyn", tau=tau, sta=(0, 0, 0)))
+        ratio = res.Pm / res.Pm.max(axis=-1, keepdims=True)
+        assert (ratio[res.mask] >= math.exp(-tau) * (1 - 1e-12)).all()
+        assert (ratio[~res.mask] < math.exp(-tau) * (1 + 1e-12)).all()
+
+
+# ---------------------------------------------------------------- golden rows and packing
+def test_golden_cdf_rows():
+    with open(os.path.join(GOLDEN, "cdf_examples.json")) as f:
+        rows = json.load(f)["rows"]
+    for r in rows:
+        p = np.array(r["p"])
+        keep, _ = R.cdf_select_row(p, r["thr"])
+        assert np.nonzero(keep)[0].tolist() == r["kept"], r
+        if 0 < r["thr"] < 1:
+            # The page's literal wording: ascending order, cumulative probability > 1 - thr.
+            asc = np.lexsort((-np.arange(len(p)), p))
+            cum = np.cumsum(p[asc])
+            lit = np.zeros(len(p), bool)
+            lit[asc] = cum > 1 - r["thr"] + 1e-12
+            assert np.nonzero(lit)[0].tolist() == r["kept"], r
+
+
+def test_pack_bits_layout():
+    m = np.zeros((2, 70), dtype=bool)
+    m[0, [0, 5, 31, 32, 69]] = True
+    m[1, 33] = True
+    w = R.pack_bits(m)
+    assert w.shape == (2, 3) and w.dtype == np.uint32
+    assert w[0].tolist() == [1 | 32 | (1 << 31), 1, 1 << 5]
+    assert w[1].tolist() == [0, 2, 0]
+    assert np.array_equal(R.unpack_bits(w, 70), m)
+    counts, lists = R.kept_lists(m)
+    assert counts.tolist() == [5, 1]
+    assert lists[0, :5].tolist() == [0, 5, 31, 32, 69] and (lists[0, 5:] == -1).all()
+
+
+def test_sta_counts_closed_form():
+    """Blocks kept by STA alone: product over axes of the truncated window lengths."""
+    g = R.Geom(B=1, H=1, T=21, Hs=32, Ws=56, d=4)
+    sta = R.sta_block_mask(g, (3, 3, 3))
+    c = R.block_coords(g)
+
+    def span(v, n):
+        return min(v + 1, n - 1) - max(v - 1, 0) + 1
+
+    want = np.array([span(a, g.T) * span(b, g.nbh) * span(e, g.nbw) for a, b, e in c])
+    assert np.array_equal(sta.sum(1), want)
+    assert abs(sta.mean() - 0.0335) < 5e-4
+    assert (sta == sta.T).all() and sta.diagonal().all()
+
+
+# ---------------------------------------------------------------- planted mistakes
+PINS = [
+    test_p1_full_threshold_is_full_attention,
+    lambda: test_p2_pure_sta_equals_bruteforce_window((3, 3, 3)),
+    lambda: test_p2_pure_sta_equals_bruteforce_window((1, 3, 5)),
+    test_p2_random_block_mask_bruteforce,
+    lambda: [test_p3_minimal_prefix_bruteforce(s) for s in (0, 1, 3, 6)],
+    test_p3_invariants_on_generated_rows,
+    lambda: test_p4_uniform_rows_keep_lowest_indices(21, 32, 56, 0.7, 412),
+    test_dominant_block_row_softmax,
+    test_p5_nesting_and_limits,
+    test_p6_reorder_is_blockwise_bijection,
+    test_p7_attention_identities,
+    test_p9_dyn_vs_probability_ratio,
+    test_golden_cdf_rows,
+    test_pack_bits_layout,
+    test_sta_counts_closed_form,
+]
+
+
+_ORIG = {n: getattr(R, n) for n in ("cdf_select_row", "sta_block_mask", "masked_attention_head", "reorder")}
+
+
+def _m_sort_ascending(p):
+    return np.lexsort((np.arange(p.shape[-1]), p))
+
+
+def _m_tie_high_first(p):
+    return np.lexsort((-np.arange(p.shape[-1]), -p))
+
+
+def _m_cdf_inclusive(p, thr):
+    order = R.rank_order(p)
+    c = np.empty(len(p))
+    c[order] = np.cumsum(p[order])
+    return (c < thr) | (thr >= 1), c
+
+
+def _m_cdf_le(p, thr):
+    keep, c = _ORIG['cdf_select_row'](p, thr)
+    return (c <= thr) | (thr >= 1), c
+
+
+def _m_positions_patch_transposed(g):
+    t, y, x = np.meshgrid(np.arange(g.T), np.arange(g.Hs), np.arange(g.Ws), indexing="ij")
+    block = (t * g.nbw + x // g.P) * g.nbh + y // g.P
+    return (block * g.bs + (y % g.P) * g.P + x % g.P).reshape(-1)
+
+
+def _m_positions_time_inner(g):
+    t, y, x = np.meshgrid(np.arange(g.T), np.arange(g.Hs), np.arange(g.Ws), indexing="ij")
+    block = ((y // g.P) * g.nbw + x // g.P) * g.T + t
+    return (block * g.bs + (y % g.P) * g.P + x % g.P).reshape(-1)
+
+
+def _m_sta_wide(g, window):
+    return _ORIG['sta_block_mask'](g, tuple(w + 2 if w else 0 for w in window))
+
+
+def _m_block_sums(Xr, g):
+    Xr = np.asarray(Xr, np.float64)
+    return Xr.reshape(Xr.shape[:-2] + (g.nb, g.bs, Xr.shape[-1])).sum(axis=-2)
+
+
+def _m_softmax_cols(S):
+    m = S.max(axis=-2, keepdims=True)
+    e = np.exp(S - m)
+    return e / e.sum(axis=-2, keepdims=True)
+
+
+def _m_dyn_strict(s, tau):
+    return s > s.max() - tau
+
+
+def _m_dyn_from_min(s, tau):
+    return s <= s.min() + tau
+
+
+def _m_pack_msb(mask):
+    nb = mask.shape[-1]
+    out = np.zeros(mask.shape[:-1] + ((nb + 31) // 32,), dtype=np.uint64)
+    for j in range(nb):
+        out[..., j // 32] |= mask[..., j].astype(np.uint64) << np.uint64(31 - j % 32)
+    return out.astype(np.uint32)
+
+
+def _m_attn_transposed(Qr, Kr, Vr, block_mask, g, scale, rows=None, chunk=256):
+    return _ORIG['masked_attention_head'](Qr, Kr, Vr, block_mask.T, g, scale, rows, chunk)
+
+
+def _m_attn_no_scale(Qr, Kr, Vr, block_mask, g, scale, rows=None, chunk=256):
+    return _ORIG['masked_attention_head'](Qr, Kr, Vr, block_mask, g, 1.0, rows, chunk)
+
+
+def _m_inverse_as_forward(Xr, g):
+    return _ORIG['reorder'](Xr, g)
+
+
+MUTATIONS = {
+    "rank ascending": ("rank_order", _m_sort_ascending),
+    "ties high index first": ("rank_order", _m_tie_high_first),
+    "cdf inclusive mass": ("cdf_select_row", _m_cdf_inclusive),
+    "cdf <= instead of <": ("cdf_select_row", _m_cdf_le),
+    "patch rows/cols swapped in reorder": ("fractal_positions", _m_positions_patch_transposed),
+    "time not outermost": ("fractal_positions", _m_positions_time_inner),
+    "sta window too wide": ("sta_block_mask", _m_sta_wide),
+    "pool sums not means": ("block_means", _m_block_sums),
+    "column softmax": ("softmax_rows", _m_softmax_cols),
+    "dyn strict": ("dyn_select_row", _m_dyn_strict),
+    "dyn from row min": ("dyn_select_row", _m_dyn_from_min),
+    "pack msb first": ("pack_bits", _m_pack_msb),
+    "mask transposed in attention": ("masked_attention_head", _m_attn_transposed),
+    "attention scale dropped": ("masked_attention_head", _m_attn_no_scale),
+    "inverse reorder = forward": ("inverse_reorder", _m_inverse_as_forward),
+}
+
+
+@pytest.mark.parametrize("name", sorted(MUTATIONS))
+def test_planted_mistake_is_caught(name, monkeypatch):
+    attr, fn = MUTATIONS[name]
+    orig = getattr(R, attr)
+    monkeypatch.setattr(R, attr, fn)
+    failed = []
+    for pin in PINS:
+        try:
+            pin()
+        except (AssertionError, ValueError, IndexError):
+            failed.append(pin)
+    monkeypatch.setattr(R, attr, orig)
+    assert failed, f"no pin detects the planted mistake: {name}"
