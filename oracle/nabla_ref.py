@@ -147,8 +147,13 @@ def block_means(Xr: np.ndarray, g: Geom) -> np.ndarray:
 # block representations.
 # --------------------------------------------------------------------------
 def pooled_logits(qbar: np.ndarray, kbar: np.ndarray, scale: float) -> np.ndarray:
-    """S_ij = scale * <qbar_i, kbar_j> (pre-softmax), [..., nb, nb]."""
-    return scale * np.matmul(qbar, np.swapaxes(kbar, -1, -2))
+    """S_ij = scale * <qbar_i, kbar_j> (pre-softmax), [..., nb, nb].
+
+    Every dot product is summed in the same order (numpy's own loop, not a
+    blocked BLAS kernel), so blocks with identical pooled keys get identical
+    logits and stay exactly tied, as the definition makes them.
+    """
+    return scale * np.einsum("...ic,...jc->...ij", qbar, kbar, optimize=False)
 
 
 def softmax_rows(S: np.ndarray) -> np.ndarray:

@@ -183,6 +183,27 @@ def test_dominant_block_row_softmax():
     assert (res.mask[0, 0, :, 0]).all() and res.mask[0, 0].sum() == g.nb
 
 
+def test_identical_pooled_keys_tie_exactly():
+    """Blocks with equal pooled keys have equal probabilities (then the lower index ranks first)."""
+    rng = np.random.default_rng(21)
+    nb, d = 700, 128
+    kbar = rng.standard_normal((nb, d))
+    dup_src = rng.choice(nb, 40, replace=False)
+    dup_dst = rng.choice(np.setdiff1d(np.arange(nb), dup_src), 40, replace=False)
+    kbar[dup_dst] = kbar[dup_src]
+    qbar = rng.standard_normal((nb, d))
+    S = R.pooled_logits(qbar[None], kbar[None], 0.1)[0]
+    assert np.array_equal(S[:, dup_dst], S[:, dup_src])
+    np.testing.assert_allclose(S, 0.1 * qbar @ kbar.T, rtol=1e-12, atol=1e-12)
+    g = R.Geom(B=1, H=1, T=7, Hs=80, Ws=80, d=d)
+    assert g.nb == nb
+    res = R.build_block_mask(qbar[None, None], kbar[None, None], g, R.MaskParams(mode="cdf", thr=0.5, sta=(0, 0, 0)))
+    for a, b in zip(dup_src, dup_dst):
+        lo, hi = min(a, b), max(a, b)
+        assert res.Pm[0, 0, :, a].tolist() == res.Pm[0, 0, :, b].tolist()
+        assert not (res.sel[0, 0, :, hi] & ~res.sel[0, 0, :, lo]).any()
+
+
 # ---------------------------------------------------------------- P5
 def test_p5_nesting_and_limits():
     from gen import WORKLOADS, make_qkv
