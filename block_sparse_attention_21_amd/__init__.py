@@ -1,0 +1,310 @@
+"""Python binding of libabla: NABLA block-sparse video attention on MI355X.
+
+Thin ctypes marshalling over the C-ABI declared in include/abla.h: tensors are
+checked (device, dtype, shape, contiguity) and their device pointers are passed
+with the current HIP stream. Every step of the computation runs in the HIP
+kernels of libabla.so; if the library is missing, importing this package fails.
+Build it with `python -m block_sparse_attention_21_amd.build`.
+"""
+from __future__ import annotations
+
+import ctypes
+import dataclasses
+import math
+import os
+from typing import Optional
+
+import torch
+
+_LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libabla.so")
+
+OK, ERR_INVALID, ERR_UNSUPPORTED, ERR_WORKSPACE, ERR_HIP = range(5)
+F32, BF16 = 0, 1
+LAYOUT_TOKENS, LAYOUT_BLOCK_T = 0, 1
+MASK_CDF, MASK_DYN = 0, 1
+
+
+class AblaError(RuntimeError):
+    def __init__(self, code: int, what: str):
+        self.code = code
+        super().__init__(f"{what}: {status_str(code)} (status {code})")
+
+
+class _Geom(ctypes.Structure):
+    _fields_ = [("B", ctypes.c_int64), ("H", ctypes.c_int64), ("T", ctypes.c_int64), ("Hs", ctypes.c_int64),
+                ("Ws", ctypes.c_int64), ("d", ctypes.c_int64), ("P", ctypes.c_int32)]
+
+
+class _MaskParams(ctypes.Structure):
+    _fields_ = [("mode", ctypes.c_int32), ("thr", ctypes.c_double), ("tau", ctypes.c_double),
+                ("pool_scale", ctypes.c_double), ("sta_t", ctypes.c_int32), ("sta_h", ctypes.c_int32),
+                ("sta_w", ctypes.c_int32)]
+
+
+def _load():
+    if not os.path.exists(_LIB_PATH):
+        raise ImportError(f"{_LIB_PATH} is missing; build it with `python -m block_sparse_attention_21_amd.build`")
+    lib = ctypes.CDLL(_LIB_PATH)
+    vp, i32, f32, sz = ctypes.c_void_p, ctypes.c_int32, ctypes.c_float, ctypes.c_size_t
+    G = ctypes.POINTER(_Geom)
+    sigs = {
+        "abla_reorder": (i32, [G, i32, i32, i32, vp, vp, vp, vp]),
+        "abla_build_mask_workspace_bytes": (sz, [G]),
+        "abla_build_mask": (i32, [G, ctypes.POINTER(_MaskParams), vp, vp, vp, vp, vp, vp, sz, vp]),
+        "abla_sparse_attn_workspace_bytes": (sz, [G]),
+        "abla_sparse_attn_fwd": (i32, [G, i32, f32, vp, vp, vp, vp, vp, vp, i32, vp, vp, sz, vp]),
+        "abla_status_str": (ctypes.c_char_p, [i32]),
+        "abla_version": (i32, []),
+    }
+    for name, (res, args) in sigs.items():
+        fn = getattr(lib, name)
+        fn.restype, fn.argtypes = res, args
+    return lib
+
+
+_lib = _load()
+EXPORTED = ("abla_reorder", "abla_build_mask_workspace_bytes", "abla_build_mask", "abla_sparse_attn_workspace_bytes",
+            "abla_sparse_attn_fwd", "abla_status_str", "abla_version")
+
+
+def status_str(code: int) -> str:
+    return _lib.abla_status_str(code).decode()
+
+
+def version() -> int:
+    return _lib.abla_version()
+
+
+@dataclasses.dataclass(frozen=True)
+class Geometry:
+    """B batches, H heads, T frames of Hs x Ws tokens, head dim d, patch P (P*P-token blocks)."""
+
+    B: int
+    H: int
+    T: int
+    Hs: int
+    Ws: int
+    d: int
+    P: int = 8
+
+    @property
+    def N(self) -> int:
+        return self.T * self.Hs * self.Ws
+
+    @property
+    def nb(self) -> int:
+        return self.T * (self.Hs // self.P) * (self.Ws // self.P)
+
+    @property
+    def words(self) -> int:
+        return (self.nb + 31) // 32
+
+    def c(self) -> _Geom:
+        return _Geom(self.B, self.H, self.T, self.Hs, self.Ws, self.d, self.P)
+
+
+@dataclasses.dataclass(frozen=True)
+class MaskParams:
+    """mode 'cdf' (thr) or 'dyn' (tau); pool_scale 0 -> 1/sqrt(d); sta (0,0,0) -> no sliding-tile window."""
+
+    mode: str = "cdf"
+    thr: float = 0.9
+    tau: float = 4.0
+    pool_scale: float = 0.0
+    sta: tuple = (3, 3, 3)
+
+    def c(self) -> _MaskParams:
+        mode = {"cdf": MASK_CDF, "dyn": MASK_DYN}.get(self.mode, -1) if isinstance(self.mode, str) else self.mode
+        return _MaskParams(mode, self.thr, self.tau, self.pool_scale, *self.sta)
+
+
+_DT = {torch.float32: F32, torch.bfloat16: BF16}
+
+
+def _ptr(t: Optional[torch.Tensor]):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(t: torch.Tensor):
+    return ctypes.c_void_p(torch.cuda.current_stream(t.device).cuda_stream)
+
+
+def _need(t: torch.Tensor, name: str, shape, dtype, device):
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if t.device != device:
+        raise ValueError(f"{name} is on {t.device}, expected {device}")
+    if tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} has shape {tuple(t.shape)}, expected {tuple(shape)}")
+    if t.dtype != dtype:
+        raise ValueError(f"{name} has dtype {t.dtype}, expected {dtype}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+
+
+def _check(code: int, what: str):
+    if code != OK:
+        raise AblaError(code, what)
+
+
+def _device(x: torch.Tensor) -> torch.device:
+    if x.device.type != "cuda":
+        raise ValueError("abla runs on a HIP device; got a tensor on " + str(x.device))
+    return x.device
+
+
+# ---------------------------------------------------------------- entry points
+def reorder(x: torch.Tensor, geom: Geometry, *, inverse: bool = False, layout: str = "tokens",
+            out: Optional[torch.Tensor] = None, pooled: Optional[torch.Tensor] = None,
+            want_pooled: bool = False):
+    """abla_reorder. Returns y (and the float64 pooled block means if requested)."""
+    dev = _device(x)
+    if x.dtype not in _DT:
+        raise ValueError(f"unsupported dtype {x.dtype}")
+    _need(x, "x", (geom.B, geom.H, geom.N, geom.d), x.dtype, dev)
+    lay = {"tokens": LAYOUT_TOKENS, "block_t": LAYOUT_BLOCK_T}[layout]
+    yshape = (geom.B, geom.H, geom.N, geom.d) if lay == LAYOUT_TOKENS else (geom.B, geom.H, geom.nb, geom.d, 64)
+    if out is None:
+        out = torch.empty(yshape, dtype=x.dtype, device=dev)
+    _need(out, "out", yshape, x.dtype, dev)
+    if want_pooled and pooled is None:
+        pooled = torch.empty((geom.B, geom.H, geom.nb, geom.d), dtype=torch.float64, device=dev)
+    if pooled is not None:
+        _need(pooled, "pooled", (geom.B, geom.H, geom.nb, geom.d), torch.float64, dev)
+    g = geom.c()
+    _check(_lib.abla_reorder(ctypes.byref(g), _DT[x.dtype], int(inverse), lay, _ptr(x), _ptr(out), _ptr(pooled),
+                             _stream(x)), "abla_reorder")
+    return (out, pooled) if pooled is not None else out
+
+
+def build_mask_workspace_bytes(geom: Geometry) -> int:
+    g = geom.c()
+    return _lib.abla_build_mask_workspace_bytes(ctypes.byref(g))
+
+
+def sparse_attn_workspace_bytes(geom: Geometry) -> int:
+    g = geom.c()
+    return _lib.abla_sparse_attn_workspace_bytes(ctypes.byref(g))
+
+
+def build_mask(qbar: torch.Tensor, kbar: torch.Tensor, geom: Geometry, params: MaskParams, *,
+               words: Optional[torch.Tensor] = None, counts: Optional[torch.Tensor] = None,
+               lists: Optional[torch.Tensor] = None, want_lists: bool = True,
+               workspace: Optional[torch.Tensor] = None):
+    """abla_build_mask. Returns (words uint32 as int32 view, counts, lists or None)."""
+    dev = _device(qbar)
+    shp = (geom.B, geom.H, geom.nb, geom.d)
+    _need(qbar, "qbar", shp, torch.float64, dev)
+    _need(kbar, "kbar", shp, torch.float64, dev)
+    if words is None:
+        words = torch.empty((geom.B, geom.H, geom.nb, geom.words), dtype=torch.int32, device=dev)
+    if counts is None:
+        counts = torch.empty((geom.B, geom.H, geom.nb), dtype=torch.int32, device=dev)
+    if lists is None and want_lists:
+        lists = torch.empty((geom.B, geom.H, geom.nb, geom.nb), dtype=torch.int32, device=dev)
+    _need(words, "words", (geom.B, geom.H, geom.nb, geom.words), torch.int32, dev)
+    _need(counts, "counts", (geom.B, geom.H, geom.nb), torch.int32, dev)
+    if lists is not None:
+        _need(lists, "lists", (geom.B, geom.H, geom.nb, geom.nb), torch.int32, dev)
+    nbytes = build_mask_workspace_bytes(geom)
+    if workspace is None:
+        workspace = torch.empty(max(nbytes, 1), dtype=torch.uint8, device=dev)
+    g, p = geom.c(), params.c()
+    _check(_lib.abla_build_mask(ctypes.byref(g), ctypes.byref(p), _ptr(qbar), _ptr(kbar), _ptr(words),
+                                _ptr(counts), _ptr(lists), _ptr(workspace), workspace.numel(), _stream(qbar)),
+           "abla_build_mask")
+    return words, counts, lists
+
+
+def sparse_attn_fwd(q_r: torch.Tensor, k_r: torch.Tensor, v_rt: torch.Tensor, counts: torch.Tensor,
+                    lists: torch.Tensor, geom: Geometry, *, scale: float = 0.0, out_original_order: bool = True,
+                    out: Optional[torch.Tensor] = None, lse: Optional[torch.Tensor] = None, want_lse: bool = False,
+                    workspace: Optional[torch.Tensor] = None):
+    """abla_sparse_attn_fwd. Returns out (and lse if requested)."""
+    dev = _device(q_r)
+    dt = q_r.dtype
+    if dt not in _DT:
+        raise ValueError(f"unsupported dtype {dt}")
+    tok = (geom.B, geom.H, geom.N, geom.d)
+    _need(q_r, "q_r", tok, dt, dev)
+    _need(k_r, "k_r", tok, dt, dev)
+    _need(v_rt, "v_rt", (geom.B, geom.H, geom.nb, geom.d, 64), dt, dev)
+    _need(counts, "counts", (geom.B, geom.H, geom.nb), torch.int32, dev)
+    _need(lists, "lists", (geom.B, geom.H, geom.nb, geom.nb), torch.int32, dev)
+    if out is None:
+        out = torch.empty(tok, dtype=dt, device=dev)
+    _need(out, "out", tok, dt, dev)
+    if want_lse and lse is None:
+        lse = torch.empty((geom.B, geom.H, geom.N), dtype=torch.float32, device=dev)
+    if lse is not None:
+        _need(lse, "lse", (geom.B, geom.H, geom.N), torch.float32, dev)
+    nbytes = sparse_attn_workspace_bytes(geom)
+    if workspace is None:
+        workspace = torch.empty(max(nbytes, 1), dtype=torch.uint8, device=dev)
+    g = geom.c()
+    _check(_lib.abla_sparse_attn_fwd(ctypes.byref(g), _DT[dt], float(scale), _ptr(q_r), _ptr(k_r), _ptr(v_rt),
+                                     _ptr(counts), _ptr(lists), _ptr(out), int(out_original_order), _ptr(lse),
+                                     _ptr(workspace), workspace.numel(), _stream(q_r)), "abla_sparse_attn_fwd")
+    return (out, lse) if lse is not None else out
+
+
+class NablaAttention:
+    """The whole forward path for one geometry, with every buffer allocated once.
+
+    __call__(q, k, v) runs: reorder Q (+pool), reorder K (+pool), reorder V
+    (channel-major blocks), build the mask, block-sparse attention writing the
+    output in the original token order. Intermediate results stay available as
+    attributes (q_r, k_r, v_rt, qbar, kbar, words, counts, lists, lse).
+    """
+
+    def __init__(self, geom: Geometry, params: MaskParams, dtype=torch.bfloat16, device="cuda",
+                 scale: float = 0.0, want_lse: bool = False):
+        self.geom, self.params, self.scale = geom, params, scale
+        dev = torch.device(device)
+        g = geom
+        tok = (g.B, g.H, g.N, g.d)
+        self.q_r = torch.empty(tok, dtype=dtype, device=dev)
+        self.k_r = torch.empty(tok, dtype=dtype, device=dev)
+        self.v_rt = torch.empty((g.B, g.H, g.nb, g.d, 64), dtype=dtype, device=dev)
+        self.qbar = torch.empty((g.B, g.H, g.nb, g.d), dtype=torch.float64, device=dev)
+        self.kbar = torch.empty_like(self.qbar)
+        self.words = torch.empty((g.B, g.H, g.nb, g.words), dtype=torch.int32, device=dev)
+        self.counts = torch.empty((g.B, g.H, g.nb), dtype=torch.int32, device=dev)
+        self.lists = torch.empty((g.B, g.H, g.nb, g.nb), dtype=torch.int32, device=dev)
+        self.out = torch.empty(tok, dtype=dtype, device=dev)
+        self.lse = torch.empty((g.B, g.H, g.N), dtype=torch.float32, device=dev) if want_lse else None
+        self.ws_mask = torch.empty(max(build_mask_workspace_bytes(g), 1), dtype=torch.uint8, device=dev)
+        self.ws_attn = torch.empty(max(sparse_attn_workspace_bytes(g), 1), dtype=torch.uint8, device=dev)
+
+    def reorder_pool(self, q, k, v):
+        reorder(q, self.geom, out=self.q_r, pooled=self.qbar)
+        reorder(k, self.geom, out=self.k_r, pooled=self.kbar)
+        reorder(v, self.geom, layout="block_t", out=self.v_rt)
+
+    def mask(self):
+        build_mask(self.qbar, self.kbar, self.geom, self.params, words=self.words, counts=self.counts,
+                   lists=self.lists, workspace=self.ws_mask)
+
+    def attend(self):
+        sparse_attn_fwd(self.q_r, self.k_r, self.v_rt, self.counts, self.lists, self.geom, scale=self.scale,
+                        out=self.out, lse=self.lse, workspace=self.ws_attn)
+
+    def __call__(self, q, k, v):
+        self.reorder_pool(q, k, v)
+        self.mask()
+        self.attend()
+        return self.out
+
+
+def dense_flops(geom: Geometry) -> float:
+    """4*B*H*N^2*d: the matrix-product FLOPs of full attention over the same tokens."""
+    return 4.0 * geom.B * geom.H * geom.N * geom.N * geom.d
+
+
+def kept_flops(geom: Geometry, total_kept_blocks: int) -> float:
+    """4*64*64*d per kept (query block, key block) pair."""
+    return 4.0 * 64 * 64 * geom.d * float(total_kept_blocks)
+
+
+def default_scale(geom: Geometry) -> float:
+    return 1.0 / math.sqrt(geom.d)

@@ -1,0 +1,343 @@
+// Content-adaptive block mask: reduced attention over pooled blocks, a per-row
+// cut, the sliding-tile union, bit packing and ascending kept lists.
+//
+// NABLA, Method: "reduced attention" (a full attention map over the pooled
+// block vectors), "CDF thresholding" (each row ranked by probability; the
+// blocks needed for the row's cumulative probability to reach thr are kept,
+// per head and per input), hybrid with STA (M = M_nabla OR M_STA).
+// DynamicRad, Methodology A, Dynamic-Threshold mode: the pre-softmax logits
+// serve as importance and are filtered by a threshold.
+//
+// Two kernels:
+//  k_scores  S = pool_scale * Qbar Kbar^T per (b, h), a float64 tile GEMM
+//            written to the caller's workspace (fixed summation order).
+//  k_select  one workgroup per row (b, h, i): row max, softmax, then either
+//            the CDF cut (LDS-resident bitonic sort of 64-bit keys holding
+//            the probability's exponent and top 40 mantissa bits above 13
+//            bits of ~j, i.e. P descending then j ascending, and an exclusive
+//            prefix sum of the sorted masses) or the logit threshold; OR the
+//            STA window; pack bits, count, list.
+//
+// The decisions are taken in float64 so that two blocks whose probabilities
+// agree to float32 precision are still ranked as exactly as the definition
+// asks. The prefix sum runs on integers: each probability is converted
+// exactly to a 2^-62 fixed-point value, so the cumulative mass before every
+// rank is an exact, order-independent sum.
+#include <math.h>
+
+#include "common.h"
+
+namespace abla {
+namespace {
+
+// ---------------------------------------------------------------- scores
+constexpr int kTile = 64;
+constexpr int kKc = 32;  // reduction chunk
+
+__global__ __launch_bounds__(256) void k_scores(const double* __restrict__ qbar, const double* __restrict__ kbar,
+                                                double* __restrict__ S, int nb, int d, double scale) {
+  __shared__ double qs[kTile][kKc + 1];
+  __shared__ double ks[kTile][kKc + 1];
+  const int t = threadIdx.x;
+  const int tx = t & 15, ty = t >> 4;
+  const int j0 = blockIdx.x * kTile, i0 = blockIdx.y * kTile;
+  const long long bh = blockIdx.z;
+  const double* qh = qbar + bh * nb * d;
+  const double* kh = kbar + bh * nb * d;
+  double acc[4][4];
+#pragma unroll
+  for (int a = 0; a < 4; ++a)
+#pragma unroll
+    for (int b = 0; b < 4; ++b) acc[a][b] = 0.0;
+
+  for (int k0 = 0; k0 < d; k0 += kKc) {
+    for (int idx = t; idx < kTile * kKc / 2; idx += 256) {
+      const int row = idx / (kKc / 2), c2 = (idx % (kKc / 2)) * 2;
+      double2 qv = make_double2(0.0, 0.0), kv = qv;
+      if (i0 + row < nb) qv = *reinterpret_cast<const double2*>(qh + (long long)(i0 + row) * d + k0 + c2);
+      if (j0 + row < nb) kv = *reinterpret_cast<const double2*>(kh + (long long)(j0 + row) * d + k0 + c2);
+      qs[row][c2] = qv.x; qs[row][c2 + 1] = qv.y;
+      ks[row][c2] = kv.x; ks[row][c2 + 1] = kv.y;
+    }
+    __syncthreads();
+#pragma unroll 8
+    for (int kk = 0; kk < kKc; ++kk) {
+      double av[4], bv[4];
+#pragma unroll
+      for (int a = 0; a < 4; ++a) av[a] = qs[ty + 16 * a][kk];
+#pragma unroll
+      for (int b = 0; b < 4; ++b) bv[b] = ks[tx + 16 * b][kk];
+#pragma unroll
+      for (int a = 0; a < 4; ++a)
+#pragma unroll
+        for (int b = 0; b < 4; ++b) acc[a][b] = fma(av[a], bv[b], acc[a][b]);
+    }
+    __syncthreads();
+  }
+#pragma unroll
+  for (int a = 0; a < 4; ++a) {
+    const int i = i0 + ty + 16 * a;
+    if (i >= nb) continue;
+#pragma unroll
+    for (int b = 0; b < 4; ++b) {
+      const int j = j0 + tx + 16 * b;
+      if (j < nb) S[(bh * nb + i) * nb + j] = acc[a][b] * scale;
+    }
+  }
+}
+
+// ---------------------------------------------------------------- select
+constexpr int kSelThreads = 256;
+constexpr int kWaves = kSelThreads / 64;
+
+struct SelArgs {
+  int mode;        // ABLA_MASK_CDF / ABLA_MASK_DYN
+  int cdf_all;     // thr >= 1
+  int cdf_none;    // thr <= 0
+  unsigned long long thr_fx;  // thr in 2^-62 fixed point (CDF, 0 < thr < 1)
+  double tau;
+  int sta_on, rt, rh, rw;
+  int np;          // bitonic size: power of two >= nb
+  int W;           // words per row
+};
+
+__device__ __forceinline__ double wave_max(double v) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v = fmax(v, __shfl_xor(v, o));
+  return v;
+}
+
+__device__ __forceinline__ double wave_sum(double v) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o);
+  return v;
+}
+
+constexpr int kIdxBits = 13;  // block index field of a sort key (nb <= 4096 < 2^13)
+
+// Sort key: probability bits (sign 0, exponent, top 40 mantissa bits) above ~j.
+__device__ __forceinline__ unsigned long long make_key(double p, int j) {
+  const unsigned long long pb = (unsigned long long)__double_as_longlong(p) >> 12;
+  return (pb << kIdxBits) | (unsigned long long)((1 << kIdxBits) - 1 - j);
+}
+
+// Probability carried by a key (its truncated value) in 2^-62 fixed point; exact conversion.
+__device__ __forceinline__ unsigned long long mass_fx(unsigned long long key) {
+  const double p = __longlong_as_double((long long)((key >> kIdxBits) << 12));
+  return (unsigned long long)(p * 4611686018427387904.0);
+}
+
+template <int NPT>
+__global__ __launch_bounds__(kSelThreads) void k_select(const double* __restrict__ S, uint32_t* __restrict__ words,
+                                                        int32_t* __restrict__ counts, int32_t* __restrict__ lists,
+                                                        KGeom g, SelArgs a) {
+  constexpr int CAP = kSelThreads * NPT;
+  __shared__ unsigned long long keys[CAP];
+  __shared__ uint32_t wbits[CAP / 32];
+  __shared__ int wpre[CAP / 32];
+  __shared__ double redf[kWaves];
+  __shared__ unsigned long long redu[kWaves];
+  __shared__ unsigned long long kmin_s;
+
+  const int t = threadIdx.x, lane = t & 63, wv = t >> 6;
+  const long long row = blockIdx.x;
+  const int nb = g.nb;
+  const int i = (int)(row % nb);
+  const double* Srow = S + row * nb;
+
+  double s[NPT];
+  double mx = -INFINITY;
+#pragma unroll
+  for (int k = 0; k < NPT; ++k) {
+    const int j = t + kSelThreads * k;
+    s[k] = j < nb ? Srow[j] : -INFINITY;
+    mx = fmax(mx, s[k]);
+  }
+  mx = wave_max(mx);
+  if (lane == 0) redf[wv] = mx;
+  __syncthreads();
+  mx = redf[0];
+#pragma unroll
+  for (int w = 1; w < kWaves; ++w) mx = fmax(mx, redf[w]);
+  __syncthreads();
+
+  bool keep[NPT];
+  if (a.mode == ABLA_MASK_DYN) {
+    const double edge = mx - a.tau;
+#pragma unroll
+    for (int k = 0; k < NPT; ++k) keep[k] = (t + kSelThreads * k < nb) && s[k] >= edge;
+  } else if (a.cdf_all || a.cdf_none) {
+#pragma unroll
+    for (int k = 0; k < NPT; ++k) keep[k] = a.cdf_all && (t + kSelThreads * k < nb);
+  } else {
+    // Softmax of the row (max-shifted exponentials, fixed-order sum).
+    double e[NPT];
+    double z = 0.0;
+#pragma unroll
+    for (int k = 0; k < NPT; ++k) {
+      e[k] = (t + kSelThreads * k < nb) ? exp(s[k] - mx) : 0.0;
+      z += e[k];
+    }
+    z = wave_sum(z);
+    if (lane == 0) redf[wv] = z;
+    __syncthreads();
+    z = redf[0];
+#pragma unroll
+    for (int w = 1; w < kWaves; ++w) z += redf[w];
+
+    unsigned long long key[NPT];
+#pragma unroll
+    for (int k = 0; k < NPT; ++k) {
+      const int j = t + kSelThreads * k;
+      key[k] = j < nb ? make_key(e[k] / z, j) : 0ull;
+      if (j < a.np) keys[j] = key[k];
+    }
+    if (t == 0) kmin_s = ~0ull;
+    __syncthreads();
+
+    // Bitonic sort, descending.
+    const int np = a.np;
+    for (int size = 2; size <= np; size <<= 1) {
+      for (int stride = size >> 1; stride > 0; stride >>= 1) {
+        for (int pidx = t; pidx < (np >> 1); pidx += kSelThreads) {
+          const int lo = ((pidx & ~(stride - 1)) << 1) | (pidx & (stride - 1));
+          const int hi = lo + stride;
+          const unsigned long long x = keys[lo], y = keys[hi];
+          const bool desc = (lo & size) == 0;
+          if (desc ? (x < y) : (x > y)) {
+            keys[lo] = y;
+            keys[hi] = x;
+          }
+        }
+        __syncthreads();
+      }
+    }
+
+    // Exclusive prefix sum of the sorted masses; thread t owns a contiguous segment.
+    const int seg = (np + kSelThreads - 1) / kSelThreads;
+    const int p0 = t * seg;
+    unsigned long long local = 0;
+    for (int q = 0; q < seg; ++q)
+      if (p0 + q < nb) local += mass_fx(keys[p0 + q]);
+    // Inclusive wave scan, then across waves.
+    unsigned long long incl = local;
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+      const unsigned long long v = __shfl_up(incl, o);
+      if (lane >= o) incl += v;
+    }
+    if (lane == 63) redu[wv] = incl;
+    __syncthreads();
+    unsigned long long before = incl - local;
+    for (int w = 0; w < wv; ++w) before += redu[w];
+    // Walk the segment: rank r is kept iff the mass before it is < thr.
+    unsigned long long c = before;
+    for (int q = 0; q < seg; ++q) {
+      const int pos = p0 + q;
+      if (pos >= nb) break;
+      const bool kp = c < a.thr_fx;
+      const unsigned long long mq = mass_fx(keys[pos]);
+      const bool next_kept = (pos + 1 < nb) && (c + mq < a.thr_fx);
+      if (kp && !next_kept) kmin_s = keys[pos];
+      c += mq;
+    }
+    __syncthreads();
+    const unsigned long long kmin = kmin_s;
+#pragma unroll
+    for (int k = 0; k < NPT; ++k) keep[k] = (t + kSelThreads * k < nb) && key[k] >= kmin;
+  }
+
+  // Sliding-tile window around block i.
+  if (a.sta_on) {
+    const int per_frame = g.nbh * g.nbw;
+    const int ti = i / per_frame, hi = (i % per_frame) / g.nbw, wi = i % g.nbw;
+#pragma unroll
+    for (int k = 0; k < NPT; ++k) {
+      const int j = t + kSelThreads * k;
+      const int tj = j / per_frame, hj = (j % per_frame) / g.nbw, wj = j % g.nbw;
+      keep[k] = keep[k] || (j < nb && abs(tj - ti) <= a.rt && abs(hj - hi) <= a.rh && abs(wj - wi) <= a.rw);
+    }
+  }
+
+  // Pack: a wave's ballot covers 64 consecutive blocks = two words.
+#pragma unroll
+  for (int k = 0; k < NPT; ++k) {
+    const unsigned long long b = __ballot(keep[k]);
+    if (lane == 0) {
+      const int w0 = (kSelThreads * k + 64 * wv) >> 5;
+      wbits[w0] = (uint32_t)b;
+      wbits[w0 + 1] = (uint32_t)(b >> 32);
+    }
+  }
+  __syncthreads();
+  const int W = a.W;
+  for (int w = t; w < W; w += kSelThreads) {
+    int pre = 0;
+    for (int u = 0; u < w; ++u) pre += __popc(wbits[u]);
+    wpre[w] = pre;
+    words[row * W + w] = wbits[w];
+  }
+  __syncthreads();
+  if (t == 0) counts[row] = wpre[W - 1] + __popc(wbits[W - 1]);
+  if (lists) {
+    int32_t* lrow = lists + row * nb;
+    for (int w = t; w < W; w += kSelThreads) {
+      uint32_t b = wbits[w];
+      int o = wpre[w];
+      while (b) {
+        const int bit = __ffs(b) - 1;
+        lrow[o++] = w * 32 + bit;
+        b &= b - 1;
+      }
+    }
+  }
+}
+
+template <int NPT>
+void launch_select(const KGeom& g, const double* S, uint32_t* words, int32_t* counts, int32_t* lists,
+                   const SelArgs& a, hipStream_t s) {
+  k_select<NPT><<<dim3((unsigned)((long long)g.B * g.H * g.nb)), kSelThreads, 0, s>>>(S, words, counts, lists, g,
+                                                                                   a);
+}
+
+}  // namespace
+
+hipError_t launch_build_mask(const KGeom& g, const abla_mask_params& p, const double* qbar, const double* kbar,
+                             uint32_t* words, int32_t* counts, int32_t* lists, double* scores, hipStream_t s) {
+  const double scale = p.pool_scale > 0.0 ? p.pool_scale : 1.0 / sqrt((double)g.d);
+  const int tiles = (g.nb + kTile - 1) / kTile;
+  k_scores<<<dim3(tiles, tiles, (unsigned)(g.B * g.H)), 256, 0, s>>>(qbar, kbar, scores, g.nb, g.d, scale);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+
+  SelArgs a{};
+  a.mode = p.mode;
+  a.cdf_all = p.thr >= 1.0;
+  a.cdf_none = p.thr <= 0.0;
+  if (!a.cdf_all && !a.cdf_none) {
+    unsigned long long fx = (unsigned long long)(p.thr * 4611686018427387904.0);
+    a.thr_fx = fx ? fx : 1ull;
+  }
+  a.tau = p.tau;
+  a.sta_on = (p.sta_t | p.sta_h | p.sta_w) != 0;
+  a.rt = (p.sta_t - 1) / 2;
+  a.rh = (p.sta_h - 1) / 2;
+  a.rw = (p.sta_w - 1) / 2;
+  int np = 2;
+  while (np < g.nb) np <<= 1;
+  a.np = np;
+  a.W = (g.nb + 31) / 32;
+  if (np <= 256)
+    launch_select<1>(g, scores, words, counts, lists, a, s);
+  else if (np <= 512)
+    launch_select<2>(g, scores, words, counts, lists, a, s);
+  else if (np <= 1024)
+    launch_select<4>(g, scores, words, counts, lists, a, s);
+  else if (np <= 2048)
+    launch_select<8>(g, scores, words, counts, lists, a, s);
+  else
+    launch_select<16>(g, scores, words, counts, lists, a, s);
+  return hipGetLastError();
+}
+
+}  // namespace abla

@@ -1,0 +1,172 @@
+// Fractal reordering of the token axis, fused with block mean-pooling.
+//
+// NABLA, Method: "Fractal Flattening" makes the tokens of each P x P patch one
+// contiguous run while frames stay outermost; "down-sampling" mean-pools Q
+// and K over those 64-token blocks.
+//
+// One workgroup moves one 64-token block. The source block is 8 runs of 8
+// tokens (one run per patch row), each run d*sizeof(E)*8 bytes contiguous in
+// the original order; the destination block is contiguous. Every thread moves
+// 16-byte chunks: consecutive threads take consecutive chunks of a token row,
+// so both the reads and the writes of a wave cover whole rows. The pooled
+// mean is accumulated in float64 in a fixed order (per thread over its rows,
+// then over threads): exact for bf16 inputs and deterministic. HBM-bound: read
+// + write of the tensor plus d*8 bytes of pooled output per block.
+#include "common.h"
+
+namespace abla {
+namespace {
+
+constexpr int kThreads = 256;
+
+template <typename E, int D>
+struct Shape {
+  static constexpr int EPC = 16 / sizeof(E);         // elements per 16-byte chunk
+  static constexpr int CPR = D / EPC;                 // chunks per token row
+  static constexpr int RPP = kThreads / CPR;          // token rows per pass
+  static constexpr int PASSES = kBlock / RPP;         // passes over the 64 rows
+  static_assert(kThreads % CPR == 0 && kBlock % RPP == 0, "unsupported head dim");
+};
+
+template <typename E>
+__device__ __forceinline__ void add_chunk(double* acc, const uint4& v);
+
+template <>
+__device__ __forceinline__ void add_chunk<float>(double* acc, const uint4& v) {
+  acc[0] += (double)__uint_as_float(v.x);
+  acc[1] += (double)__uint_as_float(v.y);
+  acc[2] += (double)__uint_as_float(v.z);
+  acc[3] += (double)__uint_as_float(v.w);
+}
+
+template <>
+__device__ __forceinline__ void add_chunk<uint16_t>(double* acc, const uint4& v) {
+  const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+  for (int k = 0; k < 4; ++k) {
+    acc[2 * k] += (double)__uint_as_float(w[k] << 16);
+    acc[2 * k + 1] += (double)__uint_as_float(w[k] & 0xFFFF0000u);
+  }
+}
+
+// Forward: original order -> fractal order (token rows, or channel-major blocks).
+template <typename E, int D, bool POOL, bool BLOCK_T>
+__global__ __launch_bounds__(kThreads) void k_reorder_fwd(const E* __restrict__ x, E* __restrict__ y,
+                                                          double* __restrict__ pooled, KGeom g) {
+  using S = Shape<E, D>;
+  constexpr int TILE_STRIDE = D + S::EPC;  // padded LDS row (elements) for the channel-major transpose
+  __shared__ __attribute__((aligned(16))) E tile[BLOCK_T ? kBlock * TILE_STRIDE : 1];
+  __shared__ double red[POOL ? kThreads * S::EPC : 1];
+
+  const int blk = blockIdx.x;
+  const int bh = blk / g.nb;
+  const int i = blk - bh * g.nb;
+  const int t = threadIdx.x;
+  const int cc = t % S::CPR;
+  const int r0 = t / S::CPR;
+  const E* xh = x + (long long)bh * g.N * D;
+
+  double acc[S::EPC];
+#pragma unroll
+  for (int e = 0; e < S::EPC; ++e) acc[e] = 0.0;
+
+#pragma unroll
+  for (int p = 0; p < S::PASSES; ++p) {
+    const int r = r0 + p * S::RPP;
+    const long long n = token_of(g, i, r);
+    const uint4 v = *reinterpret_cast<const uint4*>(xh + n * D + cc * S::EPC);
+    if constexpr (BLOCK_T) {
+      *reinterpret_cast<uint4*>(&tile[r * TILE_STRIDE + cc * S::EPC]) = v;
+    } else {
+      *reinterpret_cast<uint4*>(y + ((long long)bh * g.N + (long long)i * kBlock + r) * D + cc * S::EPC) = v;
+    }
+    if constexpr (POOL) add_chunk<E>(acc, v);
+  }
+
+  if constexpr (BLOCK_T) {
+    __syncthreads();
+    // Output block is [D][64]; chunk oc covers channel c = oc % D, tokens g*EPC .. +EPC-1.
+    constexpr int OUT_CHUNKS = D * kBlock / S::EPC;
+    E* yb = y + ((long long)bh * g.nb + i) * D * kBlock;
+#pragma unroll
+    for (int oc = t; oc < OUT_CHUNKS; oc += kThreads) {
+      const int c = oc % D;
+      const int grp = oc / D;
+      E vals[S::EPC];
+#pragma unroll
+      for (int e = 0; e < S::EPC; ++e) vals[e] = tile[(grp * S::EPC + e) * TILE_STRIDE + c];
+      uint4 v;
+      __builtin_memcpy(&v, vals, 16);
+      *reinterpret_cast<uint4*>(yb + c * kBlock + grp * S::EPC) = v;
+    }
+  }
+
+  if constexpr (POOL) {
+#pragma unroll
+    for (int e = 0; e < S::EPC; ++e) red[t * S::EPC + e] = acc[e];
+    __syncthreads();
+    if (t < D) {
+      const int c = t;
+      const int ccc = c / S::EPC, e = c % S::EPC;
+      double s = 0.0;
+      for (int rr = 0; rr < S::RPP; ++rr) s += red[(rr * S::CPR + ccc) * S::EPC + e];
+      pooled[((long long)bh * g.nb + i) * D + c] = s * (1.0 / kBlock);
+    }
+  }
+}
+
+// Inverse: fractal order (token rows) -> original order.
+template <typename E, int D>
+__global__ __launch_bounds__(kThreads) void k_reorder_inv(const E* __restrict__ x, E* __restrict__ y, KGeom g) {
+  using S = Shape<E, D>;
+  const int blk = blockIdx.x;
+  const int bh = blk / g.nb;
+  const int i = blk - bh * g.nb;
+  const int t = threadIdx.x;
+  const int cc = t % S::CPR;
+  const int r0 = t / S::CPR;
+  E* yh = y + (long long)bh * g.N * D;
+#pragma unroll
+  for (int p = 0; p < S::PASSES; ++p) {
+    const int r = r0 + p * S::RPP;
+    const uint4 v = *reinterpret_cast<const uint4*>(x + ((long long)bh * g.N + (long long)i * kBlock + r) * D +
+                                                    cc * S::EPC);
+    *reinterpret_cast<uint4*>(yh + token_of(g, i, r) * D + cc * S::EPC) = v;
+  }
+}
+
+template <typename E, int D>
+hipError_t dispatch(const KGeom& g, int inverse, int layout, const void* x, void* y, double* pooled,
+                    hipStream_t s) {
+  const dim3 grid((unsigned)(g.B * g.H * g.nb));
+  const E* xi = static_cast<const E*>(x);
+  E* yo = static_cast<E*>(y);
+  if (inverse) {
+    k_reorder_inv<E, D><<<grid, kThreads, 0, s>>>(xi, yo, g);
+  } else if (layout == ABLA_LAYOUT_BLOCK_T) {
+    if (pooled)
+      k_reorder_fwd<E, D, true, true><<<grid, kThreads, 0, s>>>(xi, yo, pooled, g);
+    else
+      k_reorder_fwd<E, D, false, true><<<grid, kThreads, 0, s>>>(xi, yo, nullptr, g);
+  } else {
+    if (pooled)
+      k_reorder_fwd<E, D, true, false><<<grid, kThreads, 0, s>>>(xi, yo, pooled, g);
+    else
+      k_reorder_fwd<E, D, false, false><<<grid, kThreads, 0, s>>>(xi, yo, nullptr, g);
+  }
+  return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_reorder(const KGeom& g, int dtype, int inverse, int layout, const void* x, void* y,
+                          double* pooled, hipStream_t s) {
+  if (dtype == ABLA_F32) {
+    return g.d == 64 ? dispatch<float, 64>(g, inverse, layout, x, y, pooled, s)
+                     : dispatch<float, 128>(g, inverse, layout, x, y, pooled, s);
+  }
+  return g.d == 64 ? dispatch<uint16_t, 64>(g, inverse, layout, x, y, pooled, s)
+                   : dispatch<uint16_t, 128>(g, inverse, layout, x, y, pooled, s);
+}
+
+}  // namespace abla

@@ -1,0 +1,172 @@
+/*
+ * abla -- block-sparse 3D self-attention for video diffusion transformers on
+ * AMD Instinct MI355X (gfx950).
+ *
+ * The library computes the NABLA attention path ("NABLA: Neighborhood Adaptive
+ * Block-Level Attention", technical summary, Method section) and the
+ * dynamic-threshold selection of "DynamicRad: Content-Adaptive Sparse
+ * Attention for Long Video Diffusion" (Methodology A, Dynamic-Threshold mode):
+ *
+ *   abla_reorder          fractal flattening of the tokens + block mean-pooling
+ *   abla_build_mask       reduced attention over pooled blocks, per-row CDF cut
+ *                         (or logit threshold), OR the sliding-tile window
+ *   abla_sparse_attn_fwd  attention restricted to the kept 64 x 64 blocks
+ *
+ * Conventions shared by all entry points
+ * --------------------------------------
+ * - Geometry: a video latent of T frames of Hs x Ws tokens, N = T*Hs*Ws tokens,
+ *   B batches, H heads, head dim d. Blocks are P x P spatial patches of one
+ *   frame; only P*P = 64 is implemented. nbh = Hs/P, nbw = Ws/P,
+ *   nb = T*nbh*nbw. Block i has coordinates (t, hp, wp) with
+ *   i = (t*nbh + hp)*nbw + wp.
+ * - Original token order: n = (t*Hs + y)*Ws + x.
+ * - Fractal order: token (t, y, x) sits at m = i*64 + (y % P)*P + (x % P)
+ *   where i is its block: each patch is one contiguous run, frames stay
+ *   outermost ("Fractal Flattening", NABLA Method section).
+ * - All pointers are device pointers owned by the caller, contiguous,
+ *   row-major and 16-byte aligned. The library never allocates, frees or
+ *   synchronises, keeps no pointer after a call returns and has no mutable
+ *   global state. Work is enqueued on `stream` (a hipStream_t; NULL is the
+ *   default stream) and results are valid when the stream reaches them.
+ * - Arguments are validated on the host before anything is enqueued, so
+ *   every ABLA_ERR_INVALID / _UNSUPPORTED / _WORKSPACE return has enqueued
+ *   nothing. ABLA_ERR_HIP means a launch failed (hipGetLastError).
+ * - No C++ exception crosses this interface.
+ */
+#ifndef ABLA_H
+#define ABLA_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  ABLA_OK = 0,
+  ABLA_ERR_INVALID = 1,     /* null pointer, bad size, NaN threshold, even window, aliasing */
+  ABLA_ERR_UNSUPPORTED = 2, /* valid but not implemented: P*P != 64, d not in {64,128}, nb > 4096 */
+  ABLA_ERR_WORKSPACE = 3,   /* workspace pointer null or smaller than the *_workspace_bytes value */
+  ABLA_ERR_HIP = 4          /* a kernel launch failed */
+} abla_status;
+
+typedef enum { ABLA_F32 = 0, ABLA_BF16 = 1 } abla_dtype;
+
+/* Output layout of abla_reorder.
+ * ABLA_LAYOUT_TOKENS:  [B, H, N, d], token-major, fractal order.
+ * ABLA_LAYOUT_BLOCK_T: [B, H, nb, d, 64]: each 64-token block stored
+ *                      channel-major (element (m, c) of block i at
+ *                      ((b*H + h)*nb + i)*d*64 + c*64 + m%64). This is the
+ *                      layout abla_sparse_attn_fwd takes V in. */
+typedef enum { ABLA_LAYOUT_TOKENS = 0, ABLA_LAYOUT_BLOCK_T = 1 } abla_layout;
+
+typedef struct {
+  int64_t B, H, T, Hs, Ws, d;
+  int32_t P;
+} abla_geom;
+
+typedef enum { ABLA_MASK_CDF = 0, ABLA_MASK_DYN = 1 } abla_mask_mode;
+
+typedef struct {
+  int32_t mode;       /* abla_mask_mode */
+  double thr;         /* CDF mode: probability-mass threshold; >= 1 keeps all, <= 0 keeps none */
+  double tau;         /* DYN mode: keep j iff S_ij >= max_j S_ij - tau (pooled, scaled logits) */
+  double pool_scale;  /* scale of the pooled logits; 0 means 1/sqrt(d) */
+  int32_t sta_t, sta_h, sta_w; /* sliding-tile window in blocks, odd; all 0 = no STA */
+} abla_mask_params;
+
+/* Fractal reordering and block mean-pooling of one tensor.
+ * Source: NABLA, Method -- "Fractal Flattening" (patch tokens made contiguous,
+ * time order kept) and "down-sampling" (Q and K mean-pooled over 64-token
+ * blocks).
+ *
+ * inverse = 0: x is [B,H,N,d] in original order; y receives the fractal-order
+ *   tensor in `layout`. If `pooled` is not NULL it receives [B,H,nb,d] float64
+ *   block means: the 64 input values of a block summed in float64 (exact for
+ *   bf16 inputs) and divided by 64. The mask decisions downstream are taken in
+ *   float64 so that they do not hinge on float32 rounding.
+ * inverse = 1: x is [B,H,N,d] in fractal order (ABLA_LAYOUT_TOKENS only) and
+ *   y receives the original order; `pooled` must be NULL.
+ * dtype: element type of x and y. x and y must not overlap.
+ * Errors: INVALID for null x/y, x == y, bad geometry, unknown dtype or layout,
+ * inverse with BLOCK_T or with pooled; UNSUPPORTED for P*P != 64 or d not in
+ * {64, 128}. */
+abla_status abla_reorder(const abla_geom* g, int32_t dtype, int32_t inverse, int32_t layout,
+                         const void* x, void* y, double* pooled, void* stream);
+
+/* Bytes of scratch abla_build_mask needs: B*H*nb*nb*8 (the float64 pooled score matrix). */
+size_t abla_build_mask_workspace_bytes(const abla_geom* g);
+
+/* Block mask from pooled Q and K.
+ * Source: NABLA, Method -- "reduced attention" (softmax over the pooled block
+ * scores), "CDF thresholding" (rank each row, keep the blocks needed for the
+ * row's cumulative probability to reach thr), hybrid with STA
+ * (M = M_nabla OR M_STA); DynamicRad, Methodology A -- Dynamic-Threshold mode
+ * (pre-softmax logits filtered by a threshold).
+ *
+ * qbar, kbar: [B,H,nb,d] float64 (as written by abla_reorder).
+ * Per row (b,h,i): S_ij = pool_scale * <qbar_i, kbar_j>, all in float64.
+ *   CDF: P_i. = softmax(S_i.); rank blocks by (P desc, index asc); keep the
+ *        block at rank r iff the mass ranked before it is < thr.
+ *   DYN: keep j iff S_ij >= max_j S_ij - tau.
+ *   Then OR the STA window: |t_i-t_j| <= (sta_t-1)/2 and likewise for hp, wp.
+ * Outputs:
+ *   mask_words [B,H,nb,ceil(nb/32)] uint32: bit j%32 of word j/32 (LSB first)
+ *              is block j; pad bits are 0.
+ *   counts     [B,H,nb] int32: kept blocks per row.
+ *   lists      [B,H,nb,nb] int32 or NULL: the kept block indices of each row in
+ *              ascending order in the first counts[row] entries; the rest of
+ *              the row is left untouched.
+ * workspace: at least abla_build_mask_workspace_bytes(g) bytes of device memory.
+ * Errors: INVALID for null inputs/outputs, unknown mode, NaN thr/tau, negative
+ * or NaN pool_scale, windows that are even, negative or partly zero;
+ * UNSUPPORTED for nb > 4096 or the geometry limits of abla_reorder;
+ * WORKSPACE if the workspace is missing or too small. */
+abla_status abla_build_mask(const abla_geom* g, const abla_mask_params* p,
+                            const double* qbar, const double* kbar,
+                            uint32_t* mask_words, int32_t* counts, int32_t* lists,
+                            void* workspace, size_t workspace_bytes, void* stream);
+
+/* Bytes of scratch abla_sparse_attn_fwd needs: B*H*nb*4 (longest-first row order). */
+size_t abla_sparse_attn_workspace_bytes(const abla_geom* g);
+
+/* Block-sparse attention forward over the kept 64 x 64 blocks.
+ * Source: NABLA, Method -- "expansion" (the block mask names which N x N
+ * attention blocks are computed) and the block-sparse attention it feeds.
+ *
+ * For every query token m of block i (fractal order):
+ *   O[m] = sum over keys m' in the blocks listed for row i of
+ *          softmax_m'(scale * <Q[m], K[m']>) * V[m'].
+ * q_r, k_r: [B,H,N,d] fractal order, ABLA_LAYOUT_TOKENS.
+ * v_rt:     fractal order, ABLA_LAYOUT_BLOCK_T.
+ * counts, lists: as produced by abla_build_mask (lists ascending).
+ * out: [B,H,N,d], same dtype; original token order if out_original_order != 0,
+ *      else fractal order.
+ * lse: [B,H,N] float32 or NULL: natural-log sum of exp(scale * scores) over
+ *      the allowed keys, indexed in fractal order; -inf for a row whose list
+ *      is empty (its output is 0).
+ * scale: 0 means 1/sqrt(d).
+ * Arithmetic: bf16 inputs use bf16 matrix-core products with float32
+ * accumulation and a float32 online softmax; the probabilities are rounded
+ * to bf16 for the value product and the output is rounded once. float32
+ * inputs are computed in float32 throughout.
+ * workspace: at least abla_sparse_attn_workspace_bytes(g) bytes.
+ * Errors: as abla_reorder, plus INVALID for null counts/lists/out, q_r/k_r/v_rt
+ * aliasing out, and WORKSPACE. */
+abla_status abla_sparse_attn_fwd(const abla_geom* g, int32_t dtype, float scale,
+                                 const void* q_r, const void* k_r, const void* v_rt,
+                                 const int32_t* counts, const int32_t* lists,
+                                 void* out, int32_t out_original_order, float* lse,
+                                 void* workspace, size_t workspace_bytes, void* stream);
+
+/* Static, NUL-terminated description of a status code. */
+const char* abla_status_str(int32_t status);
+
+/* Library version as MAJOR*10000 + MINOR*100 + PATCH. */
+int32_t abla_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* ABLA_H */

@@ -1,0 +1,94 @@
+"""Comparison helpers for the GPU parity tests (test infrastructure).
+
+Mask rule: the GPU's block mask must equal the oracle's bit for bit, except on
+blocks whose decision sits within 1e-5 of the threshold (cumulative mass in CDF
+mode, logit edge in dynamic mode); STA blocks are never exempt.
+Attention rule: evaluated on the GPU's own mask (after it passed the mask
+check), bf16: max |dO| <= 2e-2 and ||dO||_2 / ||O||_2 <= 5e-3; float32: max |dO| <= 1e-4.
+"""
+import dataclasses
+
+import numpy as np
+import torch
+
+from oracle import nabla_ref as R
+
+BF16_MAX_ABS = 2e-2
+BF16_REL_L2 = 5e-3
+F32_MAX_ABS = 1e-4
+BAND = 1e-5
+
+
+def geoms(B, H, T, Hs, Ws, d, P=8):
+    import block_sparse_attention_21_amd as A
+    return A.Geometry(B, H, T, Hs, Ws, d, P), R.Geom(B, H, T, Hs, Ws, d, P)
+
+
+def oracle_params(p) -> R.MaskParams:
+    return R.MaskParams(mode=p.mode, thr=p.thr, tau=p.tau, pool_scale=p.pool_scale, sta=tuple(p.sta))
+
+
+def host_words(words: torch.Tensor) -> np.ndarray:
+    return words.cpu().numpy().view(np.uint32)
+
+
+@dataclasses.dataclass
+class MaskReport:
+    diff: int
+    exempt_diff: int
+    kept: int
+    total: int
+
+
+def check_mask(words, counts, lists, mres: R.MaskResult, prm: R.MaskParams, og: R.Geom, heads=None) -> MaskReport:
+    """Compare GPU mask outputs (device tensors) with the oracle's MaskResult; returns GPU bool mask."""
+    w = host_words(words)
+    gm = R.unpack_bits(w, og.nb)
+    om = mres.mask
+    if heads is not None:
+        gm = gm[:, heads]
+    assert gm.shape == om.shape
+    # Pad bits beyond nb are zero.
+    pad = og.nb % 32
+    if pad:
+        assert (w[..., -1] >> np.uint32(pad) == 0).all()
+    ex = R.exemption_sets(mres, prm, BAND)
+    diff = gm != om
+    bad = diff & ~ex
+    assert not bad.any(), f"{int(bad.sum())} mask bits differ outside the {BAND} band, first at {np.argwhere(bad)[:5]}"
+    # STA blocks are always kept.
+    assert (gm | ~mres.sta[None, None]).all()
+    # counts = popcount; lists ascending and equal to the set bits.
+    c = counts.cpu().numpy()
+    if heads is not None:
+        c = c[:, heads]
+    assert np.array_equal(c, gm.sum(-1))
+    if lists is not None:
+        L = lists.cpu().numpy()
+        if heads is not None:
+            L = L[:, heads]
+        for idx in np.ndindex(gm.shape[:-1]):
+            n = c[idx]
+            assert np.array_equal(L[idx][:n], np.nonzero(gm[idx])[0]), idx
+    return MaskReport(int(diff.sum()), int((diff & ex).sum()), int(gm.sum()), int(gm.size))
+
+
+def gpu_mask(words, og: R.Geom) -> np.ndarray:
+    return R.unpack_bits(host_words(words), og.nb)
+
+
+def compare_attention(out_gpu: np.ndarray, out_ref: np.ndarray, dtype: str):
+    d = np.abs(out_gpu.astype(np.float64) - out_ref)
+    max_abs = float(d.max()) if d.size else 0.0
+    rel = float(np.linalg.norm(d) / max(np.linalg.norm(out_ref), 1e-300))
+    if dtype == "bf16":
+        assert max_abs <= BF16_MAX_ABS, f"max |dO| {max_abs}"
+        assert rel <= BF16_REL_L2, f"rel L2 {rel}"
+    else:
+        assert max_abs <= F32_MAX_ABS, f"max |dO| {max_abs}"
+    return max_abs, rel
+
+
+def sample_rows(og: R.Geom, blocks) -> np.ndarray:
+    """All 64 query rows (fractal order) of the given query blocks."""
+    return np.concatenate([np.arange(b * og.bs, (b + 1) * og.bs) for b in blocks])

@@ -1,0 +1,126 @@
+"""The C-ABI library without a GPU: it loads, exports what include/abla.h declares,
+and rejects bad arguments on the host before anything is enqueued."""
+import ctypes
+import math
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+LIB = os.path.join(ROOT, "block_sparse_attention_21_amd", "libabla.so")
+
+pytestmark = pytest.mark.skipif(not os.path.exists(LIB), reason="libabla.so not built")
+
+FAKE = ctypes.c_void_p(0x10000)  # never dereferenced: every call below fails validation first
+FAKE2 = ctypes.c_void_p(0x90000000)
+
+
+@pytest.fixture(scope="module")
+def A():
+    import block_sparse_attention_21_amd as A
+    return A
+
+
+def declared_functions():
+    with open(os.path.join(ROOT, "include", "abla.h")) as f:
+        src = f.read()
+    return sorted(set(re.findall(r"\b(abla_[a-z_]+)\s*\(", src)))
+
+
+def test_exports_every_declared_symbol(A):
+    names = declared_functions()
+    assert len(names) == 7
+    lib = ctypes.CDLL(LIB)
+    for n in names:
+        assert hasattr(lib, n), n
+    assert set(names) == set(A.EXPORTED)
+    assert A.version() == 100
+    assert A.status_str(0) == "ok" and A.status_str(99) == "unknown status"
+
+
+def G(A, **kw):
+    base = dict(B=1, H=2, T=3, Hs=16, Ws=24, d=128, P=8)
+    base.update(kw)
+    return A.Geometry(**base).c()
+
+
+def reorder(A, g, dtype=1, inverse=0, layout=0, x=FAKE, y=FAKE2, pooled=None):
+    return A._lib.abla_reorder(ctypes.byref(g), dtype, inverse, layout, x, y, pooled, None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(B=0), 1), (dict(H=-1), 1), (dict(T=0), 1), (dict(Hs=12), 1), (dict(Ws=20), 1), (dict(d=0), 1),
+    (dict(P=4, Hs=16, Ws=24), 2), (dict(d=96), 2), (dict(d=256), 2), (dict(B=1 << 40), 2),
+])
+def test_reorder_geometry_errors(A, kw, code):
+    assert reorder(A, G(A, **kw)) == code
+
+
+def test_reorder_argument_errors(A):
+    g = G(A)
+    assert reorder(A, g, dtype=7) == 1
+    assert reorder(A, g, x=None) == 1
+    assert reorder(A, g, y=None) == 1
+    assert reorder(A, g, y=FAKE) == 1  # x == y
+    assert reorder(A, g, y=ctypes.c_void_p(0x10000 + 64)) == 1  # overlapping
+    assert reorder(A, g, layout=5) == 1
+    assert reorder(A, g, inverse=1, layout=1) == 1
+    assert reorder(A, g, inverse=1, pooled=ctypes.c_void_p(0x7000000)) == 1
+    assert reorder(A, g, inverse=2) == 1
+    assert A._lib.abla_reorder(None, 1, 0, 0, FAKE, FAKE2, None, None) == 1
+
+
+def mask_call(A, g, p, ws=FAKE, ws_bytes=1 << 40, q=FAKE, k=FAKE, words=FAKE2, counts=FAKE2):
+    return A._lib.abla_build_mask(ctypes.byref(g), ctypes.byref(p), q, k, words, counts, None, ws, ws_bytes, None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(mode=5), 1), (dict(thr=math.nan), 1), (dict(tau=math.nan), 1), (dict(pool_scale=-1.0), 1),
+    (dict(pool_scale=math.nan), 1), (dict(pool_scale=math.inf), 1),
+    (dict(sta=(2, 3, 3)), 1), (dict(sta=(3, 0, 3)), 1), (dict(sta=(-1, 3, 3)), 1), (dict(sta=(3, 3, 4)), 1),
+])
+def test_mask_param_errors(A, kw, code):
+    p = A.MaskParams(**kw).c()
+    assert mask_call(A, G(A), p) == code
+
+
+def test_mask_pointer_workspace_and_size_errors(A):
+    g, p = G(A), A.MaskParams().c()
+    assert mask_call(A, g, p, q=None) == 1
+    assert mask_call(A, g, p, counts=None) == 1
+    assert mask_call(A, g, p, ws=None) == 3
+    need = A.build_mask_workspace_bytes(A.Geometry(1, 2, 3, 16, 24, 128))
+    assert need == 2 * 18 * 18 * 8
+    assert mask_call(A, g, p, ws_bytes=need - 1) == 3
+    big = G(A, T=4097, Hs=8, Ws=8)  # nb = 4097 > one LDS-resident row
+    assert mask_call(A, big, p) == 2
+    assert A._lib.abla_build_mask_workspace_bytes(ctypes.byref(G(A, d=96))) == 0
+
+
+def attn_call(A, g, dtype=1, scale=0.0, q=FAKE, k=ctypes.c_void_p(0x20000), v=ctypes.c_void_p(0x30000),
+              counts=FAKE, lists=FAKE, out=FAKE2, ws=FAKE, ws_bytes=1 << 40):
+    return A._lib.abla_sparse_attn_fwd(ctypes.byref(g), dtype, scale, q, k, v, counts, lists, out, 1, None, ws,
+                                       ws_bytes, None)
+
+
+def test_attention_errors(A):
+    g = G(A)
+    assert attn_call(A, g, dtype=3) == 1
+    assert attn_call(A, g, q=None) == 1
+    assert attn_call(A, g, lists=None) == 1
+    assert attn_call(A, g, out=None) == 1
+    assert attn_call(A, g, out=FAKE) == 1  # aliases q
+    assert attn_call(A, g, scale=math.nan) == 1
+    assert attn_call(A, g, scale=-0.5) == 1
+    assert attn_call(A, g, ws=None) == 3
+    assert attn_call(A, g, ws_bytes=2 * 18 * 4 - 1) == 3
+    assert attn_call(A, G(A, d=32)) == 2
+    assert A.sparse_attn_workspace_bytes(A.Geometry(1, 2, 3, 16, 24, 128)) == 2 * 18 * 4
+
+
+def test_binding_rejects_cpu_tensors(A):
+    import torch
+    geom = A.Geometry(1, 1, 1, 8, 8, 64)
+    with pytest.raises(ValueError):
+        A.reorder(torch.zeros(1, 1, 64, 64), geom)

@@ -1,0 +1,228 @@
+"""HIP path vs the CPU oracle, through the C-ABI (via the ctypes binding).
+
+Small geometries are compared element by element; the five workloads run at
+their full sizes with the masks compared in full and the attention compared on
+sampled query blocks (every row of each sampled block), including each head's
+longest and shortest row.
+"""
+import math
+
+import numpy as np
+import pytest
+import torch
+
+from gen import WORKLOADS, make_qkv, make_random_qkv
+from oracle import nabla_ref as R
+from tests import parity as PT
+
+pytestmark = pytest.mark.gpu
+
+DEV = "cuda"
+
+
+@pytest.fixture(scope="module")
+def A():
+    import block_sparse_attention_21_amd as A
+    assert torch.cuda.is_available(), "the gpu tests need a HIP device"
+    return A
+
+
+def _bits(t: torch.Tensor) -> np.ndarray:
+    t = t.cpu()
+    return (t.view(torch.int16) if t.dtype == torch.bfloat16 else t.view(torch.int32)).numpy()
+
+
+def _pooled_oracle(x: torch.Tensor, og: R.Geom) -> np.ndarray:
+    """Oracle block means, one head at a time (keeps host memory small at the big sizes)."""
+    out = np.empty((og.B, og.H, og.nb, og.d))
+    for h in range(og.H):
+        gh = R.Geom(og.B, 1, og.T, og.Hs, og.Ws, og.d, og.P)
+        out[:, h:h + 1] = R.block_means(R.reorder(R.to64(x[:, h:h + 1]), gh), gh)
+    return out
+
+
+# ---------------------------------------------------------------- reorder + pool
+@pytest.mark.parametrize("dtype,d,geo", [
+    ("f32", 64, (1, 2, 8, 16, 16)), ("bf16", 128, (1, 3, 3, 24, 40)), ("bf16", 64, (2, 1, 2, 16, 8)),
+    ("f32", 128, (1, 1, 5, 8, 24)), ("bf16", 128, (1, 1, 1, 8, 8)),
+])
+def test_reorder_and_pool(A, dtype, d, geo):
+    B, H, T, Hs, Ws = geo
+    geom, og = PT.geoms(B, H, T, Hs, Ws, d)
+    x = make_random_qkv(B, H, T, Hs, Ws, d, dtype, seed=3, device=DEV)[0]
+    y, pooled = A.reorder(x, geom, want_pooled=True)
+    yt = A.reorder(x, geom, layout="block_t")
+    back = A.reorder(y, geom, inverse=True)
+    torch.cuda.synchronize()
+    xb = _bits(x)
+    ref = R.reorder(xb, og)
+    assert np.array_equal(_bits(y), ref)
+    ref_t = ref.reshape(B, H, og.nb, 64, d).transpose(0, 1, 2, 4, 3)
+    assert np.array_equal(_bits(yt), ref_t)
+    assert np.array_equal(_bits(back), xb)
+    pref = R.block_means(R.reorder(R.to64(x), og), og)
+    np.testing.assert_allclose(pooled.cpu().numpy(), pref, rtol=1e-13, atol=1e-15)
+
+
+# ---------------------------------------------------------------- small end-to-end, every element
+SMALL = [
+    # (name, dtype, d, (B,H,T,Hs,Ws), MaskParams kwargs)
+    ("tiny-like", "f32", 64, (1, 2, 8, 16, 16), dict(mode="cdf", thr=0.8)),
+    ("ragged-bf16", "bf16", 128, (1, 2, 3, 24, 88), dict(mode="cdf", thr=0.7)),  # nb = 99
+    ("d64-bf16", "bf16", 64, (2, 1, 4, 16, 40), dict(mode="cdf", thr=0.9)),
+    ("dyn-bf16", "bf16", 128, (1, 2, 3, 32, 32), dict(mode="dyn", tau=2.0)),
+    ("no-sta", "bf16", 128, (1, 1, 5, 16, 24), dict(mode="cdf", thr=0.6, sta=(0, 0, 0))),
+    ("full", "bf16", 128, (1, 1, 2, 16, 32), dict(mode="cdf", thr=1.0)),
+    ("f32-d128", "f32", 128, (1, 1, 3, 16, 16), dict(mode="cdf", thr=0.5, sta=(1, 3, 3))),
+    ("one-block", "bf16", 128, (1, 2, 1, 8, 8), dict(mode="cdf", thr=0.5)),
+    ("nb-300", "bf16", 64, (1, 1, 3, 80, 80), dict(mode="cdf", thr=0.95)),  # 2 keys/thread in the select
+    ("nb-600", "bf16", 64, (1, 1, 6, 80, 80), dict(mode="cdf", thr=0.95, sta=(0, 0, 0))),
+]
+
+
+def _run_small(A, dtype, d, geo, pkw, qk_scale=1.0, seed=5):
+    B, H, T, Hs, Ws = geo
+    geom, og = PT.geoms(B, H, T, Hs, Ws, d)
+    prm = A.MaskParams(**pkw)
+    q, k, v = make_random_qkv(B, H, T, Hs, Ws, d, dtype, seed=seed, device=DEV, scale=qk_scale)
+    # Give the pooled keys some structure so the CDF cut is not trivial.
+    k = (k.float() + 2.0 * q.float()).to(q.dtype)
+    run = A.NablaAttention(geom, prm, dtype=q.dtype, want_lse=True)
+    run(q, k, v)
+    torch.cuda.synchronize()
+    return geom, og, prm, q, k, v, run
+
+
+@pytest.mark.parametrize("case", SMALL, ids=[c[0] for c in SMALL])
+def test_small_end_to_end(A, case):
+    name, dtype, d, geo, pkw = case
+    geom, og, prm, q, k, v, run = _run_small(A, dtype, d, geo, pkw)
+    op = PT.oracle_params(prm)
+    res = R.nabla_attention(q, k, v, og, op)
+    rep = PT.check_mask(run.words, run.counts, run.lists, res.mask, op, og)
+    gm = PT.gpu_mask(run.words, og)
+    ref = R.nabla_attention(q, k, v, og, op, block_mask=gm)
+    out = run.out.float().cpu().numpy()
+    max_abs, rel = PT.compare_attention(out, ref.O, dtype)
+    lse = run.lse.cpu().numpy()
+    fin = np.isfinite(ref.lse_r)
+    assert np.array_equal(np.isfinite(lse), fin)
+    np.testing.assert_allclose(lse[fin], ref.lse_r[fin], rtol=0, atol=1e-4 if dtype == "f32" else 2e-3)
+    print(f"{name}: kept {rep.kept}/{rep.total}, band diffs {rep.exempt_diff}, max|dO| {max_abs:.2e}, rel {rel:.2e}")
+
+
+def test_empty_rows_give_zero(A):
+    geom, og, prm, q, k, v, run = _run_small(A, "bf16", 128, (1, 2, 2, 16, 16), dict(mode="cdf", thr=0.0,
+                                                                                     sta=(0, 0, 0)))
+    assert int(run.counts.sum()) == 0
+    assert int(run.words.abs().sum()) == 0
+    assert torch.count_nonzero(run.out) == 0
+    assert torch.isneginf(run.lse).all()
+
+
+def test_dyn_tau_zero_keeps_argmax(A):
+    geom, og, prm, q, k, v, run = _run_small(A, "bf16", 128, (1, 1, 3, 16, 24), dict(mode="dyn", tau=0.0,
+                                                                                     sta=(0, 0, 0)))
+    op = PT.oracle_params(prm)
+    res = R.nabla_attention(q, k, v, og, op)
+    PT.check_mask(run.words, run.counts, run.lists, res.mask, op, og)
+    assert (run.counts >= 1).all()
+
+
+def test_fractal_order_output_and_determinism(A):
+    geom, og, prm, q, k, v, run = _run_small(A, "bf16", 128, (1, 2, 3, 16, 24), dict(mode="cdf", thr=0.8))
+    out1 = run.out.clone()
+    run(q, k, v)
+    torch.cuda.synchronize()
+    assert torch.equal(out1, run.out)
+    o_r = A.sparse_attn_fwd(run.q_r, run.k_r, run.v_rt, run.counts, run.lists, geom, out_original_order=False)
+    back = A.reorder(o_r, geom, inverse=True)
+    torch.cuda.synchronize()
+    assert torch.equal(back, out1)
+
+
+def test_binding_errors_on_device(A):
+    geom = A.Geometry(1, 1, 1, 8, 8, 128)
+    x = torch.zeros(1, 1, 64, 128, dtype=torch.bfloat16, device=DEV)
+    with pytest.raises(A.AblaError) as e:
+        A.build_mask(torch.zeros(1, 1, 1, 128, device=DEV, dtype=torch.float64),
+                     torch.zeros(1, 1, 1, 128, device=DEV, dtype=torch.float64), geom,
+                     A.MaskParams(thr=math.nan))
+    assert e.value.code == A.ERR_INVALID
+    with pytest.raises(ValueError):
+        A.reorder(x[..., :64], geom)
+
+
+# ---------------------------------------------------------------- the five workloads at full size
+def _workload(A, name, **over):
+    w = WORKLOADS[name].with_(**over) if over else WORKLOADS[name]
+    geom, og = PT.geoms(w.B, w.H, w.T, w.Hs, w.Ws, w.d, w.P)
+    prm = A.MaskParams(mode=w.mode, thr=w.thr, tau=w.tau, sta=tuple(w.sta))
+    q, k, v = make_qkv(w, device=DEV)
+    run = A.NablaAttention(geom, prm, dtype=q.dtype, want_lse=True)
+    run(q, k, v)
+    torch.cuda.synchronize()
+    return w, geom, og, prm, q, k, v, run
+
+
+def _check_workload_mask(A, w, og, prm, q, k, run):
+    qbar = _pooled_oracle(q, og)
+    kbar = qbar if torch.equal(q, k) else _pooled_oracle(k, og)
+    op = PT.oracle_params(prm)
+    mres = R.build_block_mask(qbar, kbar, og, op)
+    rep = PT.check_mask(run.words, run.counts, run.lists, mres, op, og)
+    return mres, rep
+
+
+def _check_workload_attention(w, og, q, k, v, run, n_heads=2, n_rand=3):
+    counts = run.counts.cpu().numpy()
+    gm = PT.gpu_mask(run.words, og)
+    pos = R.fractal_positions(og)
+    inv = np.argsort(pos)  # fractal position -> original token
+    scale = 1.0 / math.sqrt(og.d)
+    rng = np.random.default_rng(0)
+    heads = sorted(set([0, og.H - 1] + rng.integers(0, og.H, n_heads).tolist()))[: max(n_heads, 2)]
+    worst = (0.0, 0.0)
+    gpu_all, ref_all = [], []
+    for h in heads:
+        c = counts[0, h]
+        blocks = sorted(set([int(c.argmax()), int(c.argmin())] + rng.integers(0, og.nb, n_rand).tolist()))
+        rows = PT.sample_rows(og, blocks)
+        gh = R.Geom(1, 1, og.T, og.Hs, og.Ws, og.d, og.P)
+        Qr = R.reorder(R.to64(q[0, h]), gh)
+        Kr = Qr if torch.equal(q[0, h], k[0, h]) else R.reorder(R.to64(k[0, h]), gh)
+        Vr = R.reorder(R.to64(v[0, h]), gh)
+        O_ref, lse_ref = R.masked_attention_head(Qr, Kr, Vr, gm[0, h], gh, scale, rows=rows)
+        O_gpu = run.out[0, h, torch.from_numpy(inv[rows]).to(DEV)].float().cpu().numpy()
+        lse_gpu = run.lse[0, h, torch.from_numpy(rows).to(DEV)].cpu().numpy()
+        np.testing.assert_allclose(lse_gpu, lse_ref, rtol=0, atol=2e-3)
+        gpu_all.append(O_gpu)
+        ref_all.append(O_ref)
+    return PT.compare_attention(np.concatenate(gpu_all), np.concatenate(ref_all), w.dtype)
+
+
+def test_workload_tiny(A):
+    w, geom, og, prm, q, k, v, run = _workload(A, "tiny")
+    op = PT.oracle_params(prm)
+    res = R.nabla_attention(q, k, v, og, op)
+    rep = PT.check_mask(run.words, run.counts, run.lists, res.mask, op, og)
+    assert rep.diff == 0
+    ref = R.nabla_attention(q, k, v, og, op, block_mask=PT.gpu_mask(run.words, og))
+    max_abs, rel = PT.compare_attention(run.out.cpu().numpy(), ref.O, "f32")
+    print(f"tiny: keep {rep.kept / rep.total:.4f}, max|dO| {max_abs:.2e}")
+
+
+@pytest.mark.parametrize("name", ["480p", "480p-dyn", "720p", "long"])
+def test_workload_full_size(A, name):
+    w, geom, og, prm, q, k, v, run = _workload(A, name)
+    mres, rep = _check_workload_mask(A, w, og, prm, q, k, run)
+    max_abs, rel = _check_workload_attention(w, og, q, k, v, run)
+    print(f"{name}: keep {rep.kept / rep.total:.4f}, band diffs {rep.exempt_diff}, "
+          f"max|dO| {max_abs:.2e}, rel {rel:.2e}")
+
+
+@pytest.mark.parametrize("tau", [2.0, 8.0])
+def test_dyn_tau_sweep_masks(A, tau):
+    w, geom, og, prm, q, k, v, run = _workload(A, "480p-dyn", tau=tau)
+    mres, rep = _check_workload_mask(A, w, og, prm, q, k, run)
+    print(f"480p-dyn tau={tau}: keep {rep.kept / rep.total:.4f}, band diffs {rep.exempt_diff}")
