@@ -4,7 +4,7 @@ Thin ctypes marshalling over the C-ABI declared in include/abla.h: tensors are
 checked (device, dtype, shape, contiguity) and their device pointers are passed
 with the current HIP stream. Every step of the computation runs in the HIP
 kernels of libabla.so; if the library is missing, importing this package fails.
-Build it with `python -m block_sparse_attention_21_amd.build`.
+Build it with `python block_sparse_attention_21_amd/build.py`.
 """
 from __future__ import annotations
 
@@ -43,7 +43,7 @@ class _MaskParams(ctypes.Structure):
 
 def _load():
     if not os.path.exists(_LIB_PATH):
-        raise ImportError(f"{_LIB_PATH} is missing; build it with `python -m block_sparse_attention_21_amd.build`")
+        raise ImportError(f"{_LIB_PATH} is missing; build it with `python block_sparse_attention_21_amd/build.py`")
     lib = ctypes.CDLL(_LIB_PATH)
     vp, i32, f32, sz = ctypes.c_void_p, ctypes.c_int32, ctypes.c_float, ctypes.c_size_t
     G = ctypes.POINTER(_Geom)

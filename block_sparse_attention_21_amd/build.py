@@ -1,6 +1,6 @@
 """Build libabla.so (the HIP kernels and the C-ABI) in-tree for gfx950.
 
-Usage: python -m block_sparse_attention_21_amd.build [-v]
+Usage: python block_sparse_attention_21_amd/build.py [-v]   (or __graft_entry__.build())
 """
 import os
 import shutil
@@ -53,7 +53,7 @@ def build(verbose: bool = False) -> str:
     with ThreadPoolExecutor(max_workers=min(4, os.cpu_count() or 1)) as ex:
         list(ex.map(lambda c: _run(c, verbose), jobs))
     tmp = LIB + ".tmp"
-    _run([cc, "--offload-arch=gfx950", "-shared", "-fPIC", *objs, "-o", tmp], verbose)
+    _run([cc, "--offload-arch=gfx950", "-shared", "-fPIC", "-Wl,--no-undefined", *objs, "-o", tmp], verbose)
     os.replace(tmp, LIB)
     return LIB
 

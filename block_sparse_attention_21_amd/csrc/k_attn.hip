@@ -33,10 +33,12 @@ struct AttnArgs {
   const uint16_t* vt;
   const int32_t* counts;
   const int32_t* lists;
-  const int32_t* order;
+  const int32_t* order;  // pair ids, longest first within each (b, h)
   uint16_t* out;
   float* lse;
   KGeom g;
+  int pairs;    // query-block pairs per (b, h): ceil(T/2) * nbh * nbw
+  int grid;     // total workgroups
   float c2;     // scale * log2(e)
   float scale;
   int orig;
@@ -52,37 +54,23 @@ struct Tile {
   static constexpr int KCH = D / 8;               // 16-byte chunks per K row
   static constexpr int KUNITS = KBYTES / 16;
   static constexpr int VUNITS = VBYTES / 16;
-  static constexpr int LOADS_PER_WAVE = (KUNITS + VUNITS) / 128;
+  static constexpr int KLOADS = KUNITS / 256;     // per thread per tile
+  static constexpr int VLOADS = VUNITS / 256;
 };
 
-// Swizzled chunk position of logical 16-byte chunk ch in K row r.
+// 16-byte chunk swizzles (bank-conflict-free MFMA operand reads).
 template <int D>
 __device__ __forceinline__ int k_swz(int r) {
   return D == 128 ? (r & 15) : ((r >> 1) & 7);
 }
 __device__ __forceinline__ int v_swz(int d) { return (d >> 1) & 7; }
 
-template <int D>
-__device__ __forceinline__ void issue_tile_loads(char* stage, const uint16_t* kblk, const uint16_t* vblk, int w,
-                                                 int lane) {
-  using TT = Tile<D>;
-#pragma unroll
-  for (int it = 0; it < TT::KUNITS / 128; ++it) {
-    const int u0 = w * 64 + it * 128;
-    const int u = u0 + lane;
-    const int r = u / TT::KCH, pc = u % TT::KCH;
-    const int ch = pc ^ k_swz<D>(r);
-    __builtin_amdgcn_global_load_lds(kblk + r * D + ch * 8, (lds_ptr_t)(stage + u0 * 16), 16, 0, 0);
-  }
-#pragma unroll
-  for (int it = 0; it < TT::VUNITS / 128; ++it) {
-    const int u0 = w * 64 + it * 128;
-    const int u = u0 + lane;
-    const int dd = u >> 3, pc = u & 7;
-    const int ch = pc ^ v_swz(dd);
-    __builtin_amdgcn_global_load_lds(vblk + dd * kBlock + ch * 8, (lds_ptr_t)(stage + TT::KBYTES + u0 * 16), 16, 0,
-                                     0);
-  }
+// LDS row r of the K tile holds key kperm(r): rows 4-7 and 8-11 of every 16 are swapped,
+// which makes each lane's S^T registers cover 8 consecutive keys (see the file header).
+__device__ __forceinline__ int kperm(int r) {
+  const int m = r & 15;
+  const int s = (m >= 4 && m < 8) ? 4 : ((m >= 8 && m < 12) ? -4 : 0);
+  return r + s;
 }
 
 __device__ __forceinline__ float exp2_fast(float x) { return __builtin_amdgcn_exp2f(x); }
@@ -97,118 +85,241 @@ __device__ __forceinline__ float swap_sum(float v) {
   return __uint_as_float(r[0]) + __uint_as_float(r[1]);
 }
 
-template <int D>
-__global__ __launch_bounds__(128) __attribute__((amdgpu_waves_per_eu(2, 2))) void k_attn_bf16(AttnArgs a) {
-  using TT = Tile<D>;
-  __shared__ __attribute__((aligned(1024))) char smem[TT::BYTES];
+// Read-only metadata (counts, lists, order) through the constant address space so that
+// wave-uniform reads become scalar loads: their waits then do not wait for the
+// outstanding K/V tile loads.
+typedef const __attribute__((address_space(4))) int32_t* cint_ptr;
+__device__ __forceinline__ int ld_const(const int32_t* p, long long i) {
+  return ((cint_ptr)p)[i];
+}
 
-  const int lane = threadIdx.x & 63;
-  const int w = threadIdx.x >> 6;
+// Waits and barriers written with builtins the compiler's wait-count pass understands
+// (gfx9 s_waitcnt encoding: vmcnt [3:0]+[15:14], expcnt [6:4], lgkmcnt [11:8]), and
+// without a release fence: a fence would also wait for the next tile's loads that are
+// meant to stay in flight. Empty asm statements keep memory accesses on their side.
+constexpr int waitcnt_vm(int n) { return (n & 15) | (7 << 4) | (15 << 8) | ((n >> 4) << 14); }
+constexpr int kWaitLgkm0 = 15 | (7 << 4) | (0 << 8) | (3 << 14);
+
+template <int N>
+__device__ __forceinline__ void wait_vm_barrier() {
+  __builtin_amdgcn_s_waitcnt(waitcnt_vm(N));
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+}
+__device__ __forceinline__ void wait_lgkm_barrier() {
+  __builtin_amdgcn_s_waitcnt(kWaitLgkm0);
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+}
+
+// Rescale the running output only when a row maximum grows by more than 2^8 in the
+// exponent; below that the stale maximum keeps every probability <= 256.
+constexpr float kRescaleLog2 = 8.0f;
+
+// Issue this thread's 16-byte global->LDS loads of key tile j into LDS stage `stage`.
+template <int D>
+__device__ __forceinline__ void issue_tile(char* smem, int stage, int w, const char* kbase, const char* vbase,
+                                           int j, const uint32_t* koff, const uint32_t* voff) {
+  using TT = Tile<D>;
+  const char* kb = kbase + (long long)j * TT::KBYTES;
+  const char* vb = vbase + (long long)j * TT::VBYTES;
+  char* dst = smem + stage * TT::BYTES + w * 64 * 16;
+#pragma unroll
+  for (int it = 0; it < TT::KLOADS; ++it)
+    __builtin_amdgcn_global_load_lds(kb + koff[it], (lds_ptr_t)(dst + it * 256 * 16), 16, 0, 0);
+#pragma unroll
+  for (int it = 0; it < TT::VLOADS; ++it)
+    __builtin_amdgcn_global_load_lds(vb + voff[it], (lds_ptr_t)(dst + TT::KBYTES + it * 256 * 16), 16, 0, 0);
+}
+
+// The union of two ascending kept lists, walked in ascending block order.
+struct ListPair {
+  const int32_t* la;
+  const int32_t* lb;
+  int ca, cb, nb;
+  int pa, pb;
+
+  __device__ __forceinline__ bool next(int& j, bool& need_a, bool& need_b) {
+    const int ja = pa < ca ? min(max(ld_const(la, pa), 0), nb - 1) : 0x7fffffff;
+    const int jb = pb < cb ? min(max(ld_const(lb, pb), 0), nb - 1) : 0x7fffffff;
+    if (ja == 0x7fffffff && jb == 0x7fffffff) return false;
+    j = min(ja, jb);
+    need_a = ja == j;
+    need_b = jb == j;
+    pa += need_a;
+    pb += need_b;
+    return true;
+  }
+};
+
+template <int D>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) void k_attn_bf16(AttnArgs a) {
+  using TT = Tile<D>;
+  __shared__ __attribute__((aligned(1024))) char smem[2 * TT::BYTES];
+
+  const int t = threadIdx.x;
+  const int lane = t & 63;
+  const int w = t >> 6;          // waves 0,1: block A; waves 2,3: block B
+  const int hi = lane >> 5;
   const KGeom& g = a.g;
   const int nb = g.nb;
-  const int bh = blockIdx.x / nb;
-  const int pos = blockIdx.x - bh * nb;
-  const int i = a.order ? a.order[(long long)bh * nb + pos] : pos;
-  const long long row = (long long)bh * nb + i;
-  const int cnt = min(max(a.counts[row], 0), nb);
-  const int32_t* lst = a.lists + row * nb;
-  const int q_local = w * 32 + (lane & 31);
-  const int hi = lane >> 5;
+  const int F = g.nbh * g.nbw;
+
+  // XCD-aware placement: consecutive logical items run on the same XCD (dispatch is
+  // round-robin over 8 XCDs), so one XCD's L2 serves one head's K/V at a time.
+  const int p = blockIdx.x;
+  const int base = a.grid >> 3, rem = a.grid & 7, x = p & 7;
+  const int logical = x * base + min(x, rem) + (p >> 3);
+  const int bh = logical / a.pairs;
+  const int pos = logical - bh * a.pairs;
+  const int pair = ld_const(a.order, (long long)bh * a.pairs + pos);
+  const int blk_a = (pair / F) * 2 * F + pair % F;
+  const int blk_b = blk_a + F < nb ? blk_a + F : -1;
+  const int my_blk = (w < 2) ? blk_a : blk_b;
+  const bool active = my_blk >= 0;
+
+  const long long row_a = (long long)bh * nb + blk_a;
+  const long long row_b = (long long)bh * nb + (blk_b >= 0 ? blk_b : blk_a);
+  const int ca = min(max(ld_const(a.counts, row_a), 0), nb);
+  const int cb = blk_b >= 0 ? min(max(ld_const(a.counts, row_b), 0), nb) : 0;
+  const int32_t* la = a.lists + row_a * nb;
+  const int32_t* lb = a.lists + row_b * nb;
+
+  const int q_local = (w & 1) * 32 + (lane & 31);
 
   // Q operand: lane holds Q[q_local][ks*16 + 8*hi .. +7] for every k-step.
   bf16x8_t qv[D / 16];
-  {
-    const uint16_t* qrow = a.q + ((long long)bh * g.N + (long long)i * kBlock + q_local) * D + 8 * hi;
+  if (active) {
+    const uint16_t* qrow = a.q + ((long long)bh * g.N + (long long)my_blk * kBlock + q_local) * D + 8 * hi;
 #pragma unroll
     for (int ks = 0; ks < D / 16; ++ks) qv[ks] = *reinterpret_cast<const bf16x8_t*>(qrow + ks * 16);
   }
+
+  // Per-thread byte offsets of its 16-byte loads inside a tile (the same for every tile).
+  uint32_t koff[TT::KLOADS], voff[TT::VLOADS];
+#pragma unroll
+  for (int it = 0; it < TT::KLOADS; ++it) {
+    const int u = it * 256 + t;
+    const int r = u / TT::KCH, pc = u % TT::KCH;
+    koff[it] = (uint32_t)(kperm(r) * D * 2 + ((pc ^ k_swz<D>(r)) * 16));
+  }
+#pragma unroll
+  for (int it = 0; it < TT::VLOADS; ++it) {
+    const int u = it * 256 + t;
+    const int dd = u >> 3, pc = u & 7;
+    voff[it] = (uint32_t)(dd * kBlock * 2 + ((pc ^ v_swz(dd)) * 16));
+  }
+  const char* kbase = reinterpret_cast<const char*>(a.k + (long long)bh * g.N * D);
+  const char* vbase = reinterpret_cast<const char*>(a.vt + (long long)bh * nb * D * kBlock);
+  ListPair lp{la, lb, ca, cb, nb, 0, 0};
 
   f32x16_t o[D / 32];
 #pragma unroll
   for (int dt = 0; dt < D / 32; ++dt)
 #pragma unroll
     for (int r = 0; r < 16; ++r) o[dt][r] = 0.f;
-  float m_run = -INFINITY;
+  float m_run = -INFINITY;  // in log2 units (scores * c2)
   float l_run = 0.f;
 
-  const uint16_t* kbase = a.k + (long long)bh * g.N * D;
-  const uint16_t* vbase = a.vt + (long long)bh * nb * D * kBlock;
-  const char* ks_lds = smem;
-  const char* vs_lds = smem + TT::KBYTES;
-
-  for (int tt = 0; tt < cnt; ++tt) {
-    const int j = min(max(lst[tt], 0), nb - 1);
-    issue_tile_loads<D>(smem, kbase + (long long)j * kBlock * D, vbase + (long long)j * D * kBlock, w, lane);
-    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-    __syncthreads();
-
-    // S^T = K Q^T for the two 32-key halves of the tile.
-    f32x16_t sacc[2];
-#pragma unroll
-    for (int kh = 0; kh < 2; ++kh) {
-#pragma unroll
-      for (int r = 0; r < 16; ++r) sacc[kh][r] = 0.f;
-      const int krow = kh * 32 + (lane & 31);
-      const char* rowp = ks_lds + krow * (D * 2);
-      const int swz = k_swz<D>(krow);
-#pragma unroll
-      for (int ks = 0; ks < D / 16; ++ks) {
-        const int ch = (ks * 2 + hi) ^ swz;
-        const bf16x8_t av = *reinterpret_cast<const bf16x8_t*>(rowp + ch * 16);
-        sacc[kh] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av, qv[ks], sacc[kh], 0, 0, 0);
-      }
+  int j_cur;
+  bool na_cur, nb_cur;
+  bool have = lp.next(j_cur, na_cur, nb_cur);
+  if (have) issue_tile<D>(smem, 0, w, kbase, vbase, j_cur, koff, voff);
+  __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));  // Q registers and the first tile
+  int stage = 0;
+  while (have) {
+    int j_nxt;
+    bool na_nxt, nb_nxt;
+    const bool have_nxt = lp.next(j_nxt, na_nxt, nb_nxt);
+    if (have_nxt) {
+      issue_tile<D>(smem, stage ^ 1, w, kbase, vbase, j_nxt, koff, voff);
+      wait_vm_barrier<TT::KLOADS + TT::VLOADS>();  // this tile's loads done, the next tile's in flight
+    } else {
+      wait_vm_barrier<0>();
     }
 
-    // Online softmax for this lane's query over the tile's 64 keys.
-    float mx = sacc[0][0];
+    const bool mine = (w < 2) ? na_cur : nb_cur;
+    if (mine) {
+      const char* ks_lds = smem + stage * TT::BYTES;
+      const char* vs_lds = ks_lds + TT::KBYTES;
+      // S^T = K Q^T for the two 32-key halves of the tile.
+      f32x16_t sacc[2];
 #pragma unroll
-    for (int kh = 0; kh < 2; ++kh)
+      for (int kh = 0; kh < 2; ++kh) {
 #pragma unroll
-      for (int r = 0; r < 16; ++r) mx = fmaxf(mx, sacc[kh][r]);
-    mx = swap_max(mx);
-    const float m_new = fmaxf(m_run, mx);
-    const float alpha = exp2_fast((m_run - m_new) * a.c2);
-    m_run = m_new;
-    const float mc = m_new * a.c2;
-    float psum = 0.f;
-    bf16x8_t pb[4];
+        for (int r = 0; r < 16; ++r) sacc[kh][r] = 0.f;
+        const int krow = kh * 32 + (lane & 31);
+        const char* rowp = ks_lds + krow * (D * 2);
+        const int swz = k_swz<D>(krow);
+        bf16x8_t kv[D / 16];
 #pragma unroll
-    for (int kh = 0; kh < 2; ++kh)
+        for (int ks = 0; ks < D / 16; ++ks)
+          kv[ks] = *reinterpret_cast<const bf16x8_t*>(rowp + (((ks * 2 + hi) ^ swz) * 16));
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const float p = exp2_fast(fmaf(sacc[kh][r], a.c2, -mc));
-        psum += p;
-        pb[kh * 2 + (r >> 3)][r & 7] = (__bf16)p;
+        for (int ks = 0; ks < D / 16; ++ks)
+          sacc[kh] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kv[ks], qv[ks], sacc[kh], 0, 0, 0);
       }
-    l_run = l_run * alpha + psum;
-#pragma unroll
-    for (int dt = 0; dt < D / 32; ++dt)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) o[dt][r] *= alpha;
 
-    // O^T += V^T P^T.
+      // Online softmax in log2 units for this lane's query.
+      float mx = sacc[0][0];
 #pragma unroll
-    for (int dt = 0; dt < D / 32; ++dt) {
-      const int dd = dt * 32 + (lane & 31);
-      const char* vrow = vs_lds + dd * (kBlock * 2);
-      const int swz = v_swz(dd);
+      for (int kh = 0; kh < 2; ++kh)
 #pragma unroll
-      for (int kk = 0; kk < 4; ++kk) {
-        const uint2 lo = *reinterpret_cast<const uint2*>(vrow + (((2 * kk) ^ swz) * 16) + 8 * hi);
-        const uint2 hi8 = *reinterpret_cast<const uint2*>(vrow + (((2 * kk + 1) ^ swz) * 16) + 8 * hi);
-        const uint4 packed = make_uint4(lo.x, lo.y, hi8.x, hi8.y);
-        bf16x8_t av;
-        __builtin_memcpy(&av, &packed, 16);
-        o[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av, pb[kk], o[dt], 0, 0, 0);
+        for (int r = 0; r < 16; ++r) mx = fmaxf(mx, sacc[kh][r]);
+      mx = swap_max(mx) * a.c2;
+      if (__builtin_amdgcn_ballot_w64(mx > m_run + kRescaleLog2)) {
+        const float m_new = fmaxf(m_run, mx);
+        const float alpha = exp2_fast(m_run - m_new);
+        m_run = m_new;
+        l_run *= alpha;
+#pragma unroll
+        for (int dt = 0; dt < D / 32; ++dt)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) o[dt][r] *= alpha;
+      }
+      float psum = 0.f;
+      bf16x8_t pb[4];
+#pragma unroll
+      for (int kh = 0; kh < 2; ++kh)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const float pv = exp2_fast(fmaf(sacc[kh][r], a.c2, -m_run));
+          psum += pv;
+          pb[kh * 2 + (r >> 3)][r & 7] = (__bf16)pv;
+        }
+      l_run += psum;
+
+      // O^T += V^T P^T: lane reads 8 consecutive keys of one channel row.
+#pragma unroll
+      for (int dt = 0; dt < D / 32; ++dt) {
+        const int dd = dt * 32 + (lane & 31);
+        const char* vrow = vs_lds + dd * (kBlock * 2);
+        const int swz = v_swz(dd);
+        bf16x8_t vv[4];
+#pragma unroll
+        for (int kk = 0; kk < 4; ++kk)
+          vv[kk] = *reinterpret_cast<const bf16x8_t*>(vrow + (((2 * kk + hi) ^ swz) * 16));
+#pragma unroll
+        for (int kk = 0; kk < 4; ++kk)
+          o[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vv[kk], pb[kk], o[dt], 0, 0, 0);
       }
     }
-    __syncthreads();
+    wait_lgkm_barrier();  // every wave is done reading this stage before it is refilled
+    have = have_nxt;
+    j_cur = j_nxt;
+    na_cur = na_nxt;
+    nb_cur = nb_nxt;
+    stage ^= 1;
   }
 
+  if (!active) return;
   // Epilogue: normalise, round once to bf16, write (original order if asked).
+  const int cnt = (w < 2) ? ca : cb;
   const float l_tot = swap_sum(l_run);
   const float inv = cnt > 0 ? 1.0f / l_tot : 0.f;
-  const long long n = a.orig ? token_of(g, i, q_local) : (long long)i * kBlock + q_local;
+  const long long n = a.orig ? token_of(g, my_blk, q_local) : (long long)my_blk * kBlock + q_local;
   uint16_t* orow = a.out + ((long long)bh * g.N + n) * D;
 #pragma unroll
   for (int dt = 0; dt < D / 32; ++dt)
@@ -222,8 +333,8 @@ __global__ __launch_bounds__(128) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
       *reinterpret_cast<uint2*>(orow + dt * 32 + 8 * g4 + 4 * hi) = v;
     }
   if (a.lse && hi == 0) {
-    a.lse[(long long)bh * g.N + (long long)i * kBlock + q_local] =
-        cnt > 0 ? m_run * a.scale + logf(l_tot) : -INFINITY;
+    a.lse[(long long)bh * g.N + (long long)my_blk * kBlock + q_local] =
+        cnt > 0 ? (m_run + log2f(l_tot)) * 0.6931471805599453f : -INFINITY;
   }
 }
 
@@ -323,7 +434,42 @@ __global__ __launch_bounds__(128) void k_attn_f32(AttnArgsF32 a) {
     a.lse[(long long)bh * g.N + (long long)i * kBlock + r] = cnt > 0 ? m_run + logf(l_run) : -INFINITY;
 }
 
-// Longest-first order of the query blocks of each (b, h): a counting sort of the kept counts.
+// Longest-first order of the query-block pairs (i, i + nbh*nbw) of each (b, h): a counting
+// sort on the pair's total kept count. Pair p covers blocks a = (p / F)*2F + p % F and a + F.
+__global__ __launch_bounds__(1024) void k_pair_order(const int32_t* __restrict__ counts, int32_t* __restrict__ order,
+                                                     int nb, int F, int pairs) {
+  __shared__ int hist[2 * kMaxBlocks + 1];
+  const int t = threadIdx.x;
+  const long long bh = blockIdx.x;
+  const int32_t* c = counts + bh * nb;
+  const int kmax = 2 * nb;
+  auto key = [&](int pr) {
+    const int blk = (pr / F) * 2 * F + pr % F;
+    int k = min(max(c[blk], 0), nb);
+    if (blk + F < nb) k += min(max(c[blk + F], 0), nb);
+    return k;
+  };
+  for (int v = t; v <= kmax; v += 1024) hist[v] = 0;
+  __syncthreads();
+  for (int pr = t; pr < pairs; pr += 1024) atomicAdd(&hist[key(pr)], 1);
+  __syncthreads();
+  if (t == 0) {
+    // hist[v] becomes the first position of key v in descending order.
+    int run = 0;
+    for (int v = kmax; v >= 0; --v) {
+      const int h = hist[v];
+      hist[v] = run;
+      run += h;
+    }
+  }
+  __syncthreads();
+  for (int pr = t; pr < pairs; pr += 1024) {
+    const int pos = atomicAdd(&hist[key(pr)], 1);
+    order[bh * pairs + pos] = pr;
+  }
+}
+
+// Longest-first order of the query blocks of each (b, h), for the float32 path.
 __global__ __launch_bounds__(1024) void k_row_order(const int32_t* __restrict__ counts, int32_t* __restrict__ order,
                                                     int nb) {
   __shared__ int hist[kMaxBlocks + 1];
@@ -335,7 +481,6 @@ __global__ __launch_bounds__(1024) void k_row_order(const int32_t* __restrict__ 
   for (int r = t; r < nb; r += 1024) atomicAdd(&hist[min(max(c[r], 0), nb)], 1);
   __syncthreads();
   if (t == 0) {
-    // hist[v] becomes the first position of count v in descending order.
     int run = 0;
     for (int v = nb; v >= 0; --v) {
       const int h = hist[v];
@@ -356,11 +501,12 @@ hipError_t launch_sparse_attn(const KGeom& g, int dtype, float scale, const void
                               const void* vt, const int32_t* counts, const int32_t* lists, void* out,
                               int out_original_order, float* lse, int32_t* row_order, hipStream_t s) {
   const unsigned bhs = (unsigned)(g.B * g.H);
-  k_row_order<<<dim3(bhs), 1024, 0, s>>>(counts, row_order, g.nb);
-  hipError_t e = hipGetLastError();
-  if (e != hipSuccess) return e;
-  const dim3 grid((unsigned)((long long)bhs * g.nb));
   if (dtype == ABLA_BF16) {
+    const int F = g.nbh * g.nbw;
+    const int pairs = ((g.T + 1) / 2) * F;
+    k_pair_order<<<dim3(bhs), 1024, 0, s>>>(counts, row_order, g.nb, F, pairs);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
     AttnArgs a;
     a.q = static_cast<const uint16_t*>(q);
     a.k = static_cast<const uint16_t*>(k);
@@ -371,14 +517,20 @@ hipError_t launch_sparse_attn(const KGeom& g, int dtype, float scale, const void
     a.out = static_cast<uint16_t*>(out);
     a.lse = lse;
     a.g = g;
+    a.pairs = pairs;
+    a.grid = (int)((long long)bhs * pairs);
     a.scale = scale;
     a.c2 = scale * 1.4426950408889634f;
     a.orig = out_original_order;
+    const dim3 grid((unsigned)a.grid);
     if (g.d == 128)
-      k_attn_bf16<128><<<grid, 128, 0, s>>>(a);
+      k_attn_bf16<128><<<grid, 256, 0, s>>>(a);
     else
-      k_attn_bf16<64><<<grid, 128, 0, s>>>(a);
+      k_attn_bf16<64><<<grid, 256, 0, s>>>(a);
   } else {
+    k_row_order<<<dim3(bhs), 1024, 0, s>>>(counts, row_order, g.nb);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
     AttnArgsF32 a;
     a.q = static_cast<const float*>(q);
     a.k = static_cast<const float*>(k);
@@ -391,6 +543,7 @@ hipError_t launch_sparse_attn(const KGeom& g, int dtype, float scale, const void
     a.g = g;
     a.scale = scale;
     a.orig = out_original_order;
+    const dim3 grid((unsigned)((long long)bhs * g.nb));
     if (g.d == 128)
       k_attn_f32<128><<<grid, 128, 0, s>>>(a);
     else
