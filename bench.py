@@ -38,7 +38,21 @@ def parse():
     ap.add_argument("--cpu-seconds", type=float, default=15.0, help="budget of the CPU oracle sample (0: skip)")
     ap.add_argument("--traffic", default=os.path.join(ROOT, "profiles", "traffic.json"),
                     help="measured HBM bytes per attention launch (from rocprofv3 counters)")
+    ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
+                    help="only run a plain device copy of MIB MiB (reference for the FETCH/WRITE_SIZE counters)")
     return ap.parse_args()
+
+
+def copy_calibration(mib, reps=5):
+    """A plain copy of a known size: under rocprofv3 --pmc its FETCH_SIZE / WRITE_SIZE per dispatch
+    give the factor that turns the counters into bytes."""
+    import torch
+    n = mib * (1 << 20) // 4
+    src = torch.ones(n, dtype=torch.float32, device="cuda")
+    dst = torch.empty_like(src)
+    ms = timed(lambda: dst.copy_(src), reps, torch.cuda.current_stream())
+    print(json.dumps({"copy_bytes": n * 4, "reps": reps, "ms": round(ms, 4),
+                      "GB/s (read+write)": round(2 * n * 4 / (ms * 1e-3) / 1e9, 1)}), flush=True)
 
 
 def timed(fn, reps, stream):
@@ -153,6 +167,9 @@ def main():
     if not torch.cuda.is_available():
         print(json.dumps({"error": "no HIP device"}))
         sys.exit(1)
+    if args.copy_calibration:
+        copy_calibration(args.copy_calibration)
+        return
     r = measure(args.workload, args.steps, args.warmup)
     w, geom = r["w"], r["geom"]
     value = r["dense_flops"] / (r["ms_step"] * 1e-3) / 1e12
