@@ -22,6 +22,7 @@ OK, ERR_INVALID, ERR_UNSUPPORTED, ERR_WORKSPACE, ERR_HIP = range(5)
 F32, BF16 = 0, 1
 LAYOUT_TOKENS, LAYOUT_BLOCK_T = 0, 1
 MASK_CDF, MASK_DYN = 0, 1
+CUT_RADIX, CUT_BITONIC = 0, 1
 
 
 class AblaError(RuntimeError):
@@ -38,7 +39,7 @@ class _Geom(ctypes.Structure):
 class _MaskParams(ctypes.Structure):
     _fields_ = [("mode", ctypes.c_int32), ("thr", ctypes.c_double), ("tau", ctypes.c_double),
                 ("pool_scale", ctypes.c_double), ("sta_t", ctypes.c_int32), ("sta_h", ctypes.c_int32),
-                ("sta_w", ctypes.c_int32)]
+                ("sta_w", ctypes.c_int32), ("cut", ctypes.c_int32)]
 
 
 def _load():
@@ -105,17 +106,20 @@ class Geometry:
 
 @dataclasses.dataclass(frozen=True)
 class MaskParams:
-    """mode 'cdf' (thr) or 'dyn' (tau); pool_scale 0 -> 1/sqrt(d); sta (0,0,0) -> no sliding-tile window."""
+    """mode 'cdf' (thr) or 'dyn' (tau); pool_scale 0 -> 1/sqrt(d); sta (0,0,0) -> no sliding-tile window;
+    cut 'radix' (default) or 'bitonic' (how the CDF cut is found; same result)."""
 
     mode: str = "cdf"
     thr: float = 0.9
     tau: float = 4.0
     pool_scale: float = 0.0
     sta: tuple = (3, 3, 3)
+    cut: str = "radix"
 
     def c(self) -> _MaskParams:
         mode = {"cdf": MASK_CDF, "dyn": MASK_DYN}.get(self.mode, -1) if isinstance(self.mode, str) else self.mode
-        return _MaskParams(mode, self.thr, self.tau, self.pool_scale, *self.sta)
+        cut = {"radix": CUT_RADIX, "bitonic": CUT_BITONIC}.get(self.cut, -1) if isinstance(self.cut, str) else self.cut
+        return _MaskParams(mode, self.thr, self.tau, self.pool_scale, *self.sta, cut)
 
 
 _DT = {torch.float32: F32, torch.bfloat16: BF16}

@@ -94,6 +94,7 @@ abla_status abla_build_mask(const abla_geom* g, const abla_mask_params* p, const
   if (st != ABLA_OK) return st;
   if (!p || !qbar || !kbar || !mask_words || !counts) return ABLA_ERR_INVALID;
   if (p->mode != ABLA_MASK_CDF && p->mode != ABLA_MASK_DYN) return ABLA_ERR_INVALID;
+  if (p->cut != ABLA_CUT_RADIX && p->cut != ABLA_CUT_BITONIC) return ABLA_ERR_INVALID;
   if (isnan(p->thr) || isnan(p->tau) || isnan(p->pool_scale) || p->pool_scale < 0.0 || isinf(p->pool_scale))
     return ABLA_ERR_INVALID;
   if (!window_ok(p->sta_t, p->sta_h, p->sta_w)) return ABLA_ERR_INVALID;

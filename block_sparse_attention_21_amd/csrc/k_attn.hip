@@ -434,11 +434,38 @@ __global__ __launch_bounds__(128) void k_attn_f32(AttnArgsF32 a) {
     a.lse[(long long)bh * g.N + (long long)i * kBlock + r] = cnt > 0 ? m_run + logf(l_run) : -INFINITY;
 }
 
+// In place: h[v] <- sum of h[v'] for v' > v (the first position of key v in descending
+// order). 1024 threads, each owning a contiguous run of keys; `part` holds 16 ints.
+__device__ void desc_exclusive_scan(int* h, int n, int* part) {
+  const int t = threadIdx.x, lane = t & 63, wv = t >> 6;
+  const int per = (n + 1023) / 1024;
+  const int lo = t * per, hi = min(lo + per, n);
+  int local = 0;
+  for (int v = lo; v < hi; ++v) local += h[v];
+  int incl = local;  // inclusive suffix sum over the lanes of this wave
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    const int x = __shfl_down(incl, o);
+    if (lane + o < 64) incl += x;
+  }
+  if (lane == 0) part[wv] = incl;
+  __syncthreads();
+  int run = incl - local;
+  for (int w = wv + 1; w < 16; ++w) run += part[w];
+  for (int v = hi - 1; v >= lo; --v) {
+    const int c = h[v];
+    h[v] = run;
+    run += c;
+  }
+  __syncthreads();
+}
+
 // Longest-first order of the query-block pairs (i, i + nbh*nbw) of each (b, h): a counting
 // sort on the pair's total kept count. Pair p covers blocks a = (p / F)*2F + p % F and a + F.
 __global__ __launch_bounds__(1024) void k_pair_order(const int32_t* __restrict__ counts, int32_t* __restrict__ order,
                                                      int nb, int F, int pairs) {
   __shared__ int hist[2 * kMaxBlocks + 1];
+  __shared__ int scan_part[16];
   const int t = threadIdx.x;
   const long long bh = blockIdx.x;
   const int32_t* c = counts + bh * nb;
@@ -453,16 +480,7 @@ __global__ __launch_bounds__(1024) void k_pair_order(const int32_t* __restrict__
   __syncthreads();
   for (int pr = t; pr < pairs; pr += 1024) atomicAdd(&hist[key(pr)], 1);
   __syncthreads();
-  if (t == 0) {
-    // hist[v] becomes the first position of key v in descending order.
-    int run = 0;
-    for (int v = kmax; v >= 0; --v) {
-      const int h = hist[v];
-      hist[v] = run;
-      run += h;
-    }
-  }
-  __syncthreads();
+  desc_exclusive_scan(hist, kmax + 1, scan_part);
   for (int pr = t; pr < pairs; pr += 1024) {
     const int pos = atomicAdd(&hist[key(pr)], 1);
     order[bh * pairs + pos] = pr;
@@ -473,6 +491,7 @@ __global__ __launch_bounds__(1024) void k_pair_order(const int32_t* __restrict__
 __global__ __launch_bounds__(1024) void k_row_order(const int32_t* __restrict__ counts, int32_t* __restrict__ order,
                                                     int nb) {
   __shared__ int hist[kMaxBlocks + 1];
+  __shared__ int scan_part[16];
   const int t = threadIdx.x;
   const long long bh = blockIdx.x;
   const int32_t* c = counts + bh * nb;
@@ -480,15 +499,7 @@ __global__ __launch_bounds__(1024) void k_row_order(const int32_t* __restrict__ 
   __syncthreads();
   for (int r = t; r < nb; r += 1024) atomicAdd(&hist[min(max(c[r], 0), nb)], 1);
   __syncthreads();
-  if (t == 0) {
-    int run = 0;
-    for (int v = nb; v >= 0; --v) {
-      const int h = hist[v];
-      hist[v] = run;
-      run += h;
-    }
-  }
-  __syncthreads();
+  desc_exclusive_scan(hist, nb + 1, scan_part);
   for (int r = t; r < nb; r += 1024) {
     const int p = atomicAdd(&hist[min(max(c[r], 0), nb)], 1);
     order[bh * nb + p] = r;

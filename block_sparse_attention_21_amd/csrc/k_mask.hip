@@ -12,11 +12,14 @@
 //  k_scores  S = pool_scale * Qbar Kbar^T per (b, h), a float64 tile GEMM
 //            written to the caller's workspace (fixed summation order).
 //  k_select  one workgroup per row (b, h, i): row max, softmax, then either
-//            the CDF cut (LDS-resident bitonic sort of 64-bit keys holding
-//            the probability's exponent and top 40 mantissa bits above 13
-//            bits of ~j, i.e. P descending then j ascending, and an exclusive
-//            prefix sum of the sorted masses) or the logit threshold; OR the
-//            STA window; pack bits, count, list.
+//            the CDF cut or the logit threshold; OR the STA window; pack bits,
+//            count, list. The CDF cut ranks 64-bit keys holding the
+//            probability's exponent and top 40 mantissa bits above 13 bits of
+//            ~j (P descending, then j ascending) and finds the last kept rank:
+//            the smallest key K with (mass of keys above K) < thr. Two
+//            algorithms give the same bits: a radix select over the keys with
+//            exact mass histograms (11-bit digits, usually 2-3 passes), or an
+//            LDS-resident bitonic sort followed by an exclusive prefix sum.
 //
 // The decisions are taken in float64 so that two blocks whose probabilities
 // agree to float32 precision are still ranked as exactly as the definition
@@ -92,6 +95,7 @@ constexpr int kWaves = kSelThreads / 64;
 
 struct SelArgs {
   int mode;        // ABLA_MASK_CDF / ABLA_MASK_DYN
+  int cut;         // ABLA_CUT_RADIX / ABLA_CUT_BITONIC
   int cdf_all;     // thr >= 1
   int cdf_none;    // thr <= 0
   unsigned long long thr_fx;  // thr in 2^-62 fixed point (CDF, 0 < thr < 1)
@@ -127,12 +131,103 @@ __device__ __forceinline__ unsigned long long mass_fx(unsigned long long key) {
   return (unsigned long long)(p * 4611686018427387904.0);
 }
 
+constexpr int kDigitBits = 11;
+constexpr int kBuckets = 1 << kDigitBits;
+constexpr int kBucketsPerThread = kBuckets / kSelThreads;
+
+struct RadixScratch {
+  unsigned long long mass[kBuckets];
+  unsigned int cnt[kBuckets];
+  unsigned long long part[kWaves];  // per-wave bucket-mass totals
+  unsigned long long cand_cum[kSelThreads];
+  int bsel;
+  unsigned long long found;
+};
+
+// Smallest key K among this row's keys such that the total mass of the keys above K
+// is < thr_fx: the last rank the CDF cut keeps. MSB-first radix select: each pass
+// histograms (count, exact fixed-point mass) the next 11-bit digit of the keys that
+// match the prefix fixed so far and descends into the lowest bucket whose top key is
+// still kept. Stops when that bucket holds one key.
+template <int NPT>
+__device__ unsigned long long radix_last_kept(const unsigned long long* key, int t, int nb,
+                                              unsigned long long thr_fx, RadixScratch& rs) {
+  const int lane = t & 63, wv = t >> 6;
+  unsigned long long pmask = 0, pval = 0, above = 0;
+  int shift = 64;
+  while (true) {
+    const int db = shift >= kDigitBits ? kDigitBits : shift;
+    shift -= db;
+    const unsigned long long dmask = (1ull << db) - 1;
+    for (int b = t; b < kBuckets; b += kSelThreads) {
+      rs.mass[b] = 0;
+      rs.cnt[b] = 0;
+    }
+    if (t == 0) rs.bsel = kBuckets;
+    __syncthreads();
+#pragma unroll
+    for (int k = 0; k < NPT; ++k) {
+      if (t + kSelThreads * k < nb && (key[k] & pmask) == pval) {
+        const int d = (int)((key[k] >> shift) & dmask);
+        atomicAdd(&rs.mass[d], mass_fx(key[k]));
+        atomicAdd(&rs.cnt[d], 1u);
+      }
+    }
+    __syncthreads();
+    // Thread t owns buckets [t*BPT, t*BPT + BPT). Mass of all buckets above its range.
+    const int b0 = t * kBucketsPerThread;
+    unsigned long long local = 0;
+#pragma unroll
+    for (int q = 0; q < kBucketsPerThread; ++q) local += rs.mass[b0 + q];
+    unsigned long long incl = local;  // inclusive suffix sum over the lanes of this wave
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+      const unsigned long long v = __shfl_down(incl, o);
+      if (lane + o < 64) incl += v;
+    }
+    if (lane == 0) rs.part[wv] = incl;
+    __syncthreads();
+    unsigned long long run = above + (incl - local);
+    for (int w = wv + 1; w < kWaves; ++w) run += rs.part[w];
+    // Walk down my range: the lowest non-empty bucket whose top key is kept.
+    int cand = kBuckets;
+    unsigned long long cand_cum = 0;
+#pragma unroll
+    for (int q = kBucketsPerThread - 1; q >= 0; --q) {
+      const int b = b0 + q;
+      if (rs.cnt[b] > 0 && run < thr_fx) {
+        cand = b;
+        cand_cum = run;
+      }
+      run += rs.mass[b];
+    }
+    rs.cand_cum[t] = cand_cum;
+    if (cand < kBuckets) atomicMin(&rs.bsel, cand);
+    __syncthreads();
+    const int bs = rs.bsel;
+    above = rs.cand_cum[bs / kBucketsPerThread];
+    const unsigned int n_in = rs.cnt[bs];
+    pmask |= dmask << shift;
+    pval |= (unsigned long long)bs << shift;
+    __syncthreads();  // the next pass clears the histogram
+    if (n_in == 1 || shift == 0) break;
+  }
+  if (shift == 0) return pval;
+  // The single key in the selected bucket.
+#pragma unroll
+  for (int k = 0; k < NPT; ++k)
+    if (t + kSelThreads * k < nb && (key[k] & pmask) == pval) rs.found = key[k];
+  __syncthreads();
+  return rs.found;
+}
+
 template <int NPT>
 __global__ __launch_bounds__(kSelThreads) void k_select(const double* __restrict__ S, uint32_t* __restrict__ words,
                                                         int32_t* __restrict__ counts, int32_t* __restrict__ lists,
                                                         KGeom g, SelArgs a) {
   constexpr int CAP = kSelThreads * NPT;
-  __shared__ unsigned long long keys[CAP];
+  constexpr int KEYS_WORDS = (sizeof(RadixScratch) + 7) / 8 > CAP ? (sizeof(RadixScratch) + 7) / 8 : CAP;
+  __shared__ unsigned long long keys[KEYS_WORDS];  // bitonic keys, or the radix-select scratch
   __shared__ uint32_t wbits[CAP / 32];
   __shared__ int wpre[CAP / 32];
   __shared__ double redf[kWaves];
@@ -190,58 +285,68 @@ __global__ __launch_bounds__(kSelThreads) void k_select(const double* __restrict
     for (int k = 0; k < NPT; ++k) {
       const int j = t + kSelThreads * k;
       key[k] = j < nb ? make_key(e[k] / z, j) : 0ull;
-      if (j < a.np) keys[j] = key[k];
     }
-    if (t == 0) kmin_s = ~0ull;
-    __syncthreads();
-
-    // Bitonic sort, descending.
-    const int np = a.np;
-    for (int size = 2; size <= np; size <<= 1) {
-      for (int stride = size >> 1; stride > 0; stride >>= 1) {
-        for (int pidx = t; pidx < (np >> 1); pidx += kSelThreads) {
-          const int lo = ((pidx & ~(stride - 1)) << 1) | (pidx & (stride - 1));
-          const int hi = lo + stride;
-          const unsigned long long x = keys[lo], y = keys[hi];
-          const bool desc = (lo & size) == 0;
-          if (desc ? (x < y) : (x > y)) {
-            keys[lo] = y;
-            keys[hi] = x;
-          }
-        }
-        __syncthreads();
-      }
-    }
-
-    // Exclusive prefix sum of the sorted masses; thread t owns a contiguous segment.
-    const int seg = (np + kSelThreads - 1) / kSelThreads;
-    const int p0 = t * seg;
-    unsigned long long local = 0;
-    for (int q = 0; q < seg; ++q)
-      if (p0 + q < nb) local += mass_fx(keys[p0 + q]);
-    // Inclusive wave scan, then across waves.
-    unsigned long long incl = local;
+    if (a.cut == ABLA_CUT_RADIX) {
+      const unsigned long long km = radix_last_kept<NPT>(key, t, nb, a.thr_fx, *reinterpret_cast<RadixScratch*>(keys));
+      if (t == 0) kmin_s = km;
+      __syncthreads();
+    } else {
 #pragma unroll
-    for (int o = 1; o < 64; o <<= 1) {
-      const unsigned long long v = __shfl_up(incl, o);
-      if (lane >= o) incl += v;
+      for (int k = 0; k < NPT; ++k) {
+        const int j = t + kSelThreads * k;
+        if (j < a.np) keys[j] = key[k];
+      }
+      if (t == 0) kmin_s = ~0ull;
+      __syncthreads();
+
+      // Bitonic sort, descending.
+      const int np = a.np;
+      for (int size = 2; size <= np; size <<= 1) {
+        for (int stride = size >> 1; stride > 0; stride >>= 1) {
+          for (int pidx = t; pidx < (np >> 1); pidx += kSelThreads) {
+            const int lo = ((pidx & ~(stride - 1)) << 1) | (pidx & (stride - 1));
+            const int hi = lo + stride;
+            const unsigned long long x = keys[lo], y = keys[hi];
+            const bool desc = (lo & size) == 0;
+            if (desc ? (x < y) : (x > y)) {
+              keys[lo] = y;
+              keys[hi] = x;
+            }
+          }
+          __syncthreads();
+        }
+      }
+
+      // Exclusive prefix sum of the sorted masses; thread t owns a contiguous segment.
+      const int seg = (np + kSelThreads - 1) / kSelThreads;
+      const int p0 = t * seg;
+      unsigned long long local = 0;
+      for (int q = 0; q < seg; ++q)
+        if (p0 + q < nb) local += mass_fx(keys[p0 + q]);
+      // Inclusive wave scan, then across waves.
+      unsigned long long incl = local;
+#pragma unroll
+      for (int o = 1; o < 64; o <<= 1) {
+        const unsigned long long v = __shfl_up(incl, o);
+        if (lane >= o) incl += v;
+      }
+      if (lane == 63) redu[wv] = incl;
+      __syncthreads();
+      unsigned long long before = incl - local;
+      for (int w = 0; w < wv; ++w) before += redu[w];
+      // Walk the segment: rank r is kept iff the mass before it is < thr.
+      unsigned long long c = before;
+      for (int q = 0; q < seg; ++q) {
+        const int pos = p0 + q;
+        if (pos >= nb) break;
+        const bool kp = c < a.thr_fx;
+        const unsigned long long mq = mass_fx(keys[pos]);
+        const bool next_kept = (pos + 1 < nb) && (c + mq < a.thr_fx);
+        if (kp && !next_kept) kmin_s = keys[pos];
+        c += mq;
+      }
+      __syncthreads();
     }
-    if (lane == 63) redu[wv] = incl;
-    __syncthreads();
-    unsigned long long before = incl - local;
-    for (int w = 0; w < wv; ++w) before += redu[w];
-    // Walk the segment: rank r is kept iff the mass before it is < thr.
-    unsigned long long c = before;
-    for (int q = 0; q < seg; ++q) {
-      const int pos = p0 + q;
-      if (pos >= nb) break;
-      const bool kp = c < a.thr_fx;
-      const unsigned long long mq = mass_fx(keys[pos]);
-      const bool next_kept = (pos + 1 < nb) && (c + mq < a.thr_fx);
-      if (kp && !next_kept) kmin_s = keys[pos];
-      c += mq;
-    }
-    __syncthreads();
     const unsigned long long kmin = kmin_s;
 #pragma unroll
     for (int k = 0; k < NPT; ++k) keep[k] = (t + kSelThreads * k < nb) && key[k] >= kmin;
@@ -271,14 +376,24 @@ __global__ __launch_bounds__(kSelThreads) void k_select(const double* __restrict
   }
   __syncthreads();
   const int W = a.W;
-  for (int w = t; w < W; w += kSelThreads) {
-    int pre = 0;
-    for (int u = 0; u < w; ++u) pre += __popc(wbits[u]);
-    wpre[w] = pre;
-    words[row * W + w] = wbits[w];
+  // Exclusive prefix of the words' popcounts (W <= 128): wave 0, two words per lane.
+  if (wv == 0) {
+    const int w0 = 2 * lane;
+    const int c0 = w0 < W ? __popc(wbits[w0]) : 0;
+    const int c1 = w0 + 1 < W ? __popc(wbits[w0 + 1]) : 0;
+    int incl = c0 + c1;
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+      const int v = __shfl_up(incl, o);
+      if (lane >= o) incl += v;
+    }
+    const int excl = incl - c0 - c1;
+    if (w0 < W) wpre[w0] = excl;
+    if (w0 + 1 < W) wpre[w0 + 1] = excl + c0;
+    if (lane == 63) counts[row] = incl;
   }
+  for (int w = t; w < W; w += kSelThreads) words[row * W + w] = wbits[w];
   __syncthreads();
-  if (t == 0) counts[row] = wpre[W - 1] + __popc(wbits[W - 1]);
   if (lists) {
     int32_t* lrow = lists + row * nb;
     for (int w = t; w < W; w += kSelThreads) {
@@ -312,6 +427,7 @@ hipError_t launch_build_mask(const KGeom& g, const abla_mask_params& p, const do
 
   SelArgs a{};
   a.mode = p.mode;
+  a.cut = p.cut;
   a.cdf_all = p.thr >= 1.0;
   a.cdf_none = p.thr <= 0.0;
   if (!a.cdf_all && !a.cdf_none) {

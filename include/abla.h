@@ -68,12 +68,19 @@ typedef struct {
 
 typedef enum { ABLA_MASK_CDF = 0, ABLA_MASK_DYN = 1 } abla_mask_mode;
 
+/* How the CDF cut finds the last kept rank of a row. Both give the same bits.
+ * ABLA_CUT_RADIX:   radix select on the 64-bit (probability, ~index) keys with exact
+ *                   fixed-point mass histograms (default; no full sort).
+ * ABLA_CUT_BITONIC: full LDS bitonic sort of the keys, then an exact prefix sum. */
+typedef enum { ABLA_CUT_RADIX = 0, ABLA_CUT_BITONIC = 1 } abla_cut_algorithm;
+
 typedef struct {
   int32_t mode;       /* abla_mask_mode */
   double thr;         /* CDF mode: probability-mass threshold; >= 1 keeps all, <= 0 keeps none */
   double tau;         /* DYN mode: keep j iff S_ij >= max_j S_ij - tau (pooled, scaled logits) */
   double pool_scale;  /* scale of the pooled logits; 0 means 1/sqrt(d) */
   int32_t sta_t, sta_h, sta_w; /* sliding-tile window in blocks, odd; all 0 = no STA */
+  int32_t cut;        /* abla_cut_algorithm (CDF mode) */
 } abla_mask_params;
 
 /* Fractal reordering and block mean-pooling of one tensor.
@@ -119,7 +126,7 @@ size_t abla_build_mask_workspace_bytes(const abla_geom* g);
  *              ascending order in the first counts[row] entries; the rest of
  *              the row is left untouched.
  * workspace: at least abla_build_mask_workspace_bytes(g) bytes of device memory.
- * Errors: INVALID for null inputs/outputs, unknown mode, NaN thr/tau, negative
+ * Errors: INVALID for null inputs/outputs, unknown mode or cut algorithm, NaN thr/tau, negative
  * or NaN pool_scale, windows that are even, negative or partly zero;
  * UNSUPPORTED for nb > 4096 or the geometry limits of abla_reorder;
  * WORKSPACE if the workspace is missing or too small. */

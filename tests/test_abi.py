@@ -25,7 +25,8 @@ def A():
 def declared_functions():
     with open(os.path.join(ROOT, "include", "abla.h")) as f:
         src = f.read()
-    return sorted(set(re.findall(r"\b(abla_[a-z_]+)\s*\(", src)))
+    decl = r"^\s*(?:abla_status|size_t|const char\s*\*|int32_t)\s+(abla_[a-z_]+)\s*\("
+    return sorted(set(re.findall(decl, src, flags=re.MULTILINE)))
 
 
 def test_exports_every_declared_symbol(A):
@@ -76,7 +77,7 @@ def mask_call(A, g, p, ws=FAKE, ws_bytes=1 << 40, q=FAKE, k=FAKE, words=FAKE2, c
 
 
 @pytest.mark.parametrize("kw,code", [
-    (dict(mode=5), 1), (dict(thr=math.nan), 1), (dict(tau=math.nan), 1), (dict(pool_scale=-1.0), 1),
+    (dict(mode=5), 1), (dict(cut=3), 1), (dict(thr=math.nan), 1), (dict(tau=math.nan), 1), (dict(pool_scale=-1.0), 1),
     (dict(pool_scale=math.nan), 1), (dict(pool_scale=math.inf), 1),
     (dict(sta=(2, 3, 3)), 1), (dict(sta=(3, 0, 3)), 1), (dict(sta=(-1, 3, 3)), 1), (dict(sta=(3, 3, 4)), 1),
 ])

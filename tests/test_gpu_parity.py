@@ -226,3 +226,42 @@ def test_dyn_tau_sweep_masks(A, tau):
     w, geom, og, prm, q, k, v, run = _workload(A, "480p-dyn", tau=tau)
     mres, rep = _check_workload_mask(A, w, og, prm, q, k, run)
     print(f"480p-dyn tau={tau}: keep {rep.kept / rep.total:.4f}, band diffs {rep.exempt_diff}")
+
+
+# ---------------------------------------------------------------- the two CDF-cut algorithms agree
+@pytest.mark.parametrize("name", ["tiny", "480p", "720p", "long"])
+def test_cut_algorithms_agree(A, name):
+    """Radix select and the bitonic sort find the same last kept rank: identical bits, counts, lists."""
+    import dataclasses
+    w = WORKLOADS[name]
+    geom, og = PT.geoms(w.B, w.H, w.T, w.Hs, w.Ws, w.d, w.P)
+    q, k, _ = make_qkv(w, device=DEV)
+    qr, qbar = A.reorder(q, geom, want_pooled=True)
+    kr, kbar = A.reorder(k, geom, want_pooled=True)
+    out = {}
+    for thr in (w.thr, 0.5, 0.999):
+        for cut in ("radix", "bitonic"):
+            prm = A.MaskParams(mode="cdf", thr=thr, sta=tuple(w.sta), cut=cut)
+            out[cut] = A.build_mask(qbar, kbar, geom, prm)
+        torch.cuda.synchronize()
+        assert torch.equal(out["radix"][0], out["bitonic"][0])
+        assert torch.equal(out["radix"][1], out["bitonic"][1])
+        c = out["radix"][1]
+        L1, L2 = out["radix"][2], out["bitonic"][2]
+        ar = torch.arange(geom.nb, device=DEV)
+        valid = ar[None, None, None, :] < c[..., None]
+        assert torch.equal(torch.where(valid, L1, 0), torch.where(valid, L2, 0))
+
+
+def test_cut_algorithms_agree_small(A):
+    for geo, thr in [((1, 2, 3, 24, 88), 0.7), ((1, 1, 1, 8, 8), 0.5), ((1, 1, 6, 80, 80), 0.95),
+                     ((1, 2, 2, 16, 16), 1e-9), ((1, 1, 5, 16, 24), 0.999999)]:
+        B, H, T, Hs, Ws = geo
+        geom, og = PT.geoms(B, H, T, Hs, Ws, 128)
+        q, k, _ = make_random_qkv(B, H, T, Hs, Ws, 128, "bf16", seed=11, device=DEV)
+        _, qbar = A.reorder(q, geom, want_pooled=True)
+        _, kbar = A.reorder((k.float() + q.float()).to(q.dtype), geom, want_pooled=True)
+        res = [A.build_mask(qbar, kbar, geom, A.MaskParams(mode="cdf", thr=thr, sta=(0, 0, 0), cut=c))
+               for c in ("radix", "bitonic")]
+        torch.cuda.synchronize()
+        assert torch.equal(res[0][0], res[1][0]) and torch.equal(res[0][1], res[1][1]), geo
