@@ -4,8 +4,12 @@
 // blocks are computed; everything else is skipped. For query block i the
 // kernel walks the ascending list of kept key blocks with an online softmax.
 //
-// bf16 path (k_attn_bf16), one workgroup per query block, two waves of 32
-// query rows each, gfx950 MFMA v_mfma_f32_32x32x16_bf16:
+// bf16 path (k_attn_bf16): one workgroup of four waves per pair of query blocks
+// (i, i + nbh*nbw), i.e. the same patch in two consecutive frames, whose kept lists
+// overlap heavily; waves 0-1 hold block i, waves 2-3 block i + nbh*nbw, 32 query rows
+// per wave. The pair walks the union of its two lists once (a schedule built in LDS
+// at start), so a key/value tile is fetched once for both blocks; each wave skips the
+// tiles its own block does not keep. gfx950 MFMA v_mfma_f32_32x32x16_bf16:
 //   S^T = K Q^T   A = K rows from LDS, B = Q rows held in registers. The
 //                 result puts one query per lane (lanes l and l^32 share it),
 //                 so the row max / sum stay in-lane plus one permlane swap.
@@ -13,11 +17,16 @@
 //                 block by the reorder pass), B = the probabilities exactly as
 //                 the S^T registers hold them, rounded to bf16. The key order
 //                 of the S^T result (keys 0-3,8-11 in lanes 0-31, 4-7,12-15 in
-//                 lanes 32-63 of each 16-key step) is matched by the V^T read.
-// K and V^T tiles go global -> LDS directly (global_load_lds_dwordx4), with a
-// per-row XOR swizzle of 16-byte chunks so the MFMA operand reads are free of
-// bank conflicts. Rows are visited longest-first within each head (row_order)
-// so the long rows of the kept-count distribution do not form the tail.
+//                 lanes 32-63 of each 16-key step) is matched by loading K rows
+//                 4-7 and 8-11 of every 16 swapped, so each V^T read is one chunk.
+// Software pipeline: K tiles run one step ahead of V^T tiles (two LDS slots each),
+// so while a wave turns the scores of tile u into probabilities it already runs
+// the score MFMAs of tile u+1, and the value MFMAs of tile u run under the
+// maximum of tile u+1 (an explicit MFMA / LDS-read / VALU interleave). One barrier
+// per step. Tiles move global -> LDS directly (buffer_load ... lds), with a per-row
+// XOR swizzle of 16-byte chunks so the MFMA operand reads are free of bank
+// conflicts. Pairs are visited longest-first within each head (pair_order) so the
+// long rows of the kept-count distribution do not form the tail.
 //
 // float32 path (k_attn_f32): plain FMA arithmetic, two threads per query row.
 #include <math.h>
@@ -100,15 +109,8 @@ __device__ __forceinline__ int ld_const(const int32_t* p, long long i) {
 constexpr int waitcnt_vm(int n) { return (n & 15) | (7 << 4) | (15 << 8) | ((n >> 4) << 14); }
 constexpr int kWaitLgkm0 = 15 | (7 << 4) | (0 << 8) | (3 << 14);
 
-template <int N>
-__device__ __forceinline__ void wait_vm_barrier() {
-  __builtin_amdgcn_s_waitcnt(waitcnt_vm(N));
-  asm volatile("" ::: "memory");
-  __builtin_amdgcn_s_barrier();
-  asm volatile("" ::: "memory");
-}
-__device__ __forceinline__ void wait_lgkm_barrier() {
-  __builtin_amdgcn_s_waitcnt(kWaitLgkm0);
+__device__ __forceinline__ void wait_vm_lgkm_barrier() {
+  __builtin_amdgcn_s_waitcnt(waitcnt_vm(0) & kWaitLgkm0);
   asm volatile("" ::: "memory");
   __builtin_amdgcn_s_barrier();
   asm volatile("" ::: "memory");
@@ -118,46 +120,266 @@ __device__ __forceinline__ void wait_lgkm_barrier() {
 // exponent; below that the stale maximum keeps every probability <= 256.
 constexpr float kRescaleLog2 = 8.0f;
 
-// Issue this thread's 16-byte global->LDS loads of key tile j into LDS stage `stage`.
+// LDS map of the bf16 kernel: two K slots, two V^T slots, then the pair's schedule.
 template <int D>
-__device__ __forceinline__ void issue_tile(char* smem, int stage, int w, const char* kbase, const char* vbase,
-                                           int j, const uint32_t* koff, const uint32_t* voff) {
-  using TT = Tile<D>;
-  const char* kb = kbase + (long long)j * TT::KBYTES;
-  const char* vb = vbase + (long long)j * TT::VBYTES;
-  char* dst = smem + stage * TT::BYTES + w * 64 * 16;
-#pragma unroll
-  for (int it = 0; it < TT::KLOADS; ++it)
-    __builtin_amdgcn_global_load_lds(kb + koff[it], (lds_ptr_t)(dst + it * 256 * 16), 16, 0, 0);
-#pragma unroll
-  for (int it = 0; it < TT::VLOADS; ++it)
-    __builtin_amdgcn_global_load_lds(vb + voff[it], (lds_ptr_t)(dst + TT::KBYTES + it * 256 * 16), 16, 0, 0);
+struct Lds {
+  static constexpr int K0 = 0;
+  static constexpr int V0 = 2 * Tile<D>::KBYTES;
+  static constexpr int SCHED = V0 + 2 * Tile<D>::VBYTES;  // uint16 entries, kMaxBlocks of them
+  static constexpr int BYTES = SCHED + kMaxBlocks * 2;
+  __device__ static constexpr int kslot(int s) { return K0 + s * Tile<D>::KBYTES; }
+  __device__ static constexpr int vslot(int s) { return V0 + s * Tile<D>::VBYTES; }
+};
+
+// Schedule entry: key block j in bits 0-11, bit 12 = block A keeps it, bit 13 = block B keeps it.
+constexpr int kSchedJ = 0xfff;
+constexpr int kSchedA = 1 << 12;
+constexpr int kSchedB = 1 << 13;
+
+// Buffer resource (gfx9 V#) over `bytes` bytes at `base`: raw addressing, no stride.
+// Tile loads go through buffer_load ... lds rather than global_load_lds: the compiler's
+// wait-count pass tracks the buffer form on the vector-memory counter only, so the LDS
+// operand reads of the current tile keep partial lgkmcnt waits while the next tile's
+// loads are in flight.
+typedef int32_t i32x4_t __attribute__((ext_vector_type(4)));
+__device__ void raw_buffer_load_lds(i32x4_t rsrc, __attribute__((address_space(3))) uint32_t* lds, int size,
+                                    int voffset, int soffset, int offset, int aux)
+    __asm("llvm.amdgcn.raw.buffer.load.lds");
+
+__device__ __forceinline__ i32x4_t make_rsrc(const void* base, uint32_t bytes) {
+  const uint64_t p = reinterpret_cast<uint64_t>(base);
+  i32x4_t r;
+  r.x = __builtin_amdgcn_readfirstlane((int)(uint32_t)p);
+  r.y = __builtin_amdgcn_readfirstlane((int)(uint32_t)(p >> 32));  // stride 0
+  r.z = (int)bytes;                                                 // num_records (bytes)
+  r.w = 0x00020000;                                                 // 32-bit data format
+  return r;
 }
 
-// The union of two ascending kept lists, walked in ascending block order.
-struct ListPair {
-  const int32_t* la;
-  const int32_t* lb;
-  int ca, cb, nb;
-  int pa, pb;
+// Issue this thread's 16-byte global->LDS loads of one K tile (or one V^T tile) that
+// starts `tile` bytes into the resource. Load `it` of thread t fills LDS unit it*256 + t
+// of the slot; its source is `off` + it*4096 bytes into the tile (for both tile kinds and
+// both head dims the swizzled source of unit it*256 + t is 4096 bytes past that of unit
+// t: 16 K rows of 256 bytes, 32 K rows of 128 bytes, 32 V^T rows of 128 bytes, all with
+// a swizzle that repeats every 16 or 32 rows). `w` is the wave index (uniform).
+template <int BYTES>
+__device__ __forceinline__ void issue_rows(char* dst_slot, int w, i32x4_t rsrc, uint32_t tile, uint32_t off) {
+  constexpr int LOADS = BYTES / 16 / 256;
+  char* dst = dst_slot + w * 64 * 16;
+#pragma unroll
+  for (int it = 0; it < LOADS; ++it)
+    raw_buffer_load_lds(rsrc, (__attribute__((address_space(3))) uint32_t*)(dst + it * 256 * 16), 16, (int)off,
+                        (int)(tile + it * 4096), 0, 0);
+}
 
-  __device__ __forceinline__ bool next(int& j, bool& need_a, bool& need_b) {
-    const int ja = pa < ca ? min(max(ld_const(la, pa), 0), nb - 1) : 0x7fffffff;
-    const int jb = pb < cb ? min(max(ld_const(lb, pb), 0), nb - 1) : 0x7fffffff;
-    if (ja == 0x7fffffff && jb == 0x7fffffff) return false;
-    j = min(ja, jb);
-    need_a = ja == j;
-    need_b = jb == j;
-    pa += need_a;
-    pb += need_b;
-    return true;
+// Merge the two ascending kept lists of the pair into one ascending schedule in LDS
+// (the union of the two sets, each entry flagged with the blocks that keep it), through
+// two bitmaps and a prefix count of their OR. Returns the schedule length. Uses the
+// K/V staging area as scratch; ends with a barrier.
+__device__ int build_schedule(char* smem_stage, uint16_t* sched, const int32_t* la, int ca, const int32_t* lb, int cb,
+                              int nb) {
+  const int t = threadIdx.x, lane = t & 63, wv = t >> 6;
+  const int nw = (nb + 31) >> 5;  // <= 128 words
+  uint32_t* bma = reinterpret_cast<uint32_t*>(smem_stage);
+  uint32_t* bmb = bma + 128;
+  int* part = reinterpret_cast<int*>(bmb + 128);  // 4 wave totals + the length
+  if (t < 128) {
+    bma[t] = 0;
+    bmb[t] = 0;
   }
+  __syncthreads();
+  for (int p = t; p < ca; p += 256) {
+    const int j = min(max(la[p], 0), nb - 1);
+    atomicOr(&bma[j >> 5], 1u << (j & 31));
+  }
+  for (int p = t; p < cb; p += 256) {
+    const int j = min(max(lb[p], 0), nb - 1);
+    atomicOr(&bmb[j >> 5], 1u << (j & 31));
+  }
+  __syncthreads();
+  const uint32_t wa = t < nw ? bma[t] : 0u, wb = t < nw ? bmb[t] : 0u;
+  const uint32_t wu = wa | wb;
+  const int c = __builtin_popcount(wu);
+  int incl = c;  // inclusive prefix count over the lanes of this wave
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    const int x = __shfl_up(incl, o);
+    if (lane >= o) incl += x;
+  }
+  if (lane == 63) part[wv] = incl;
+  __syncthreads();
+  int base = incl - c;
+  for (int v = 0; v < wv; ++v) base += part[v];
+  if (t == 0) part[4] = part[0] + part[1] + part[2] + part[3];
+  uint32_t bits = wu;
+  while (bits) {
+    const int b = __builtin_ctz(bits);
+    bits &= bits - 1;
+    const int j = t * 32 + b;
+    sched[base++] = (uint16_t)(j | (((wa >> b) & 1u) ? kSchedA : 0) | (((wb >> b) & 1u) ? kSchedB : 0));
+  }
+  __syncthreads();
+  const int n = part[4];
+  __syncthreads();  // the staging area is reused by the first tile loads
+  return n;
+}
+
+// S^T for one staged K tile: s[kh] holds keys kh*32 .. kh*32+31 (in the kperm row order)
+// against this wave's 32 queries. koff[ks]: this lane's byte offset of its K chunk for
+// k-step ks inside a slot; the two key halves are 32 rows apart.
+template <int D, int SLOT>
+__device__ __forceinline__ void tile_scores(const char* smem, const uint32_t* klds, const bf16x8_t* qv,
+                                            f32x16_t (&s)[2]) {
+#pragma unroll
+  for (int kh = 0; kh < 2; ++kh)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) s[kh][r] = 0.f;
+#pragma unroll
+  for (int ks = 0; ks < D / 16; ++ks) {
+#pragma unroll
+    for (int kh = 0; kh < 2; ++kh) {
+      const bf16x8_t kv =
+          *reinterpret_cast<const bf16x8_t*>(smem + Lds<D>::kslot(SLOT) + kh * 32 * D * 2 + klds[ks]);
+      s[kh] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kv, qv[ks], s[kh], 0, 0, 0);
+    }
+  }
+}
+
+// Largest raw score of this lane's query over the tile (both lanes of the query agree).
+__device__ __forceinline__ float tile_max(const f32x16_t (&s)[2]) {
+  float mx = fmaxf(s[0][0], s[0][1]);
+#pragma unroll
+  for (int r = 2; r < 16; ++r) mx = fmaxf(mx, s[0][r]);
+#pragma unroll
+  for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[1][r]);
+  return swap_max(mx);
+}
+
+// Probabilities exp2(c2*s - m) rounded to bf16 in the V^T-operand order; returns their
+// float32 sum over this lane's 32 keys (four partial sums, no long dependency chain).
+__device__ __forceinline__ float tile_probs(const f32x16_t (&s)[2], float c2, float m, bf16x8_t (&pb)[4]) {
+  float ps[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int kh = 0; kh < 2; ++kh)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      const float pv = exp2_fast(fmaf(s[kh][r], c2, -m));
+      ps[r & 3] += pv;
+      pb[kh * 2 + (r >> 3)][r & 7] = (__bf16)pv;
+    }
+  return (ps[0] + ps[1]) + (ps[2] + ps[3]);
+}
+
+// O^T += V^T P^T for one staged V^T tile. vlds[kk]: this lane's byte offset of its 8-key
+// chunk kk of channel row (lane & 31) inside a slot; channel tile dt is 32 rows further.
+template <int D, int SLOT>
+__device__ __forceinline__ void tile_values(const char* smem, const uint32_t* vlds, const bf16x8_t (&pb)[4],
+                                            f32x16_t* o) {
+#pragma unroll
+  for (int kk = 0; kk < 4; ++kk)
+#pragma unroll
+    for (int dt = 0; dt < D / 32; ++dt) {
+      const bf16x8_t vv =
+          *reinterpret_cast<const bf16x8_t*>(smem + Lds<D>::vslot(SLOT) + dt * 32 * kBlock * 2 + vlds[kk]);
+      o[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vv, pb[kk], o[dt], 0, 0, 0);
+    }
+}
+
+// Raise the running maximum when a tile's maximum exceeds it by more than 2^8 (log2 units).
+template <int D>
+__device__ __forceinline__ void raise_max(float mx_raw, float c2, float& m_run, float& l_run, f32x16_t* o) {
+  const float mx = mx_raw * c2;
+  if (__builtin_amdgcn_ballot_w64(mx > m_run + kRescaleLog2)) {
+    const float m_new = fmaxf(m_run, mx);
+    const float alpha = exp2_fast(m_run - m_new);
+    m_run = m_new;
+    l_run *= alpha;
+#pragma unroll
+    for (int dt = 0; dt < D / 32; ++dt)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) o[dt][r] *= alpha;
+  }
+}
+
+// Instruction interleave of the steady state: the next tile's score MFMAs run under this
+// tile's exp/convert/sum work, then the value MFMAs under the next tile's maximum.
+// Masks: 0x008 MFMA, 0x100 LDS read, 0x402 VALU or transcendental.
+template <int D>
+__device__ __forceinline__ void schedule_overlap() {
+  constexpr int NS = 2 * (D / 16);    // score MFMAs per tile
+  constexpr int NPV = 4 * (D / 32);   // value MFMAs per tile
+  constexpr int VA = 112 / NS;        // VALU slots under each score MFMA
+  __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
+#pragma unroll
+  for (int i = 0; i < NS; ++i) {
+    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+    __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+    __builtin_amdgcn_sched_group_barrier(0x402, VA, 0);
+  }
+#pragma unroll
+  for (int i = 0; i < NPV; ++i) {
+    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+    __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+    __builtin_amdgcn_sched_group_barrier(0x402, 2, 0);
+  }
+}
+
+struct Walk {
+  int u, n;        // position in the schedule and its length
+  int ec, en, ef;  // entries u, u+1, u+2 (0 past the end)
 };
+
+// One step of the schedule at position u, whose K/V^T slots have parity P:
+//   K(u) in K slot P (already consumed), K(u+1) in K slot P^1, V(u) in V slot P.
+// Issues K(u+2) into K slot P and V(u+1) into V slot P^1, then, for this wave's block,
+// finishes tile u (probabilities, values) and starts tile u+1 (scores, maximum).
+// sc holds S(u) if the block keeps u; sn receives S(u+1).
+template <int D, int P>
+__device__ __forceinline__ void walk_step(char* smem, const uint16_t* sched, Walk& wk, int mine, int w,
+                                          i32x4_t krs, i32x4_t vrs, uint32_t koff,
+                                          uint32_t voff, const uint32_t* klds, const uint32_t* vlds,
+                                          const bf16x8_t* qv, float c2, f32x16_t (&sc)[2], f32x16_t (&sn)[2],
+                                          f32x16_t* o, float& m_run, float& l_run) {
+  using TT = Tile<D>;
+  wait_vm_lgkm_barrier();  // K(u+1), V(u) landed; every wave is done with step u-1
+  if (wk.u + 2 < wk.n)
+    issue_rows<TT::KBYTES>(smem + Lds<D>::kslot(P), w, krs, (uint32_t)(wk.ef & kSchedJ) * TT::KBYTES, koff);
+  if (wk.u + 1 < wk.n)
+    issue_rows<TT::VBYTES>(smem + Lds<D>::vslot(P ^ 1), w, vrs, (uint32_t)(wk.en & kSchedJ) * TT::VBYTES, voff);
+  const int look = min(wk.u + 3, wk.n - 1);
+  const int raw = sched[look];  // entry u+3, read now and used next step
+
+  const bool mc = (wk.ec & mine) != 0;
+  const bool mn = (wk.en & mine) != 0;  // en is 0 past the end
+  if (mc && mn) {
+    bf16x8_t pb[4];
+    tile_scores<D, P ^ 1>(smem, klds, qv, sn);
+    const float psum = tile_probs(sc, c2, m_run, pb);
+    tile_values<D, P>(smem, vlds, pb, o);
+    const float mx = tile_max(sn);
+    schedule_overlap<D>();
+    l_run += psum;
+    raise_max<D>(mx, c2, m_run, l_run, o);
+  } else if (mc) {
+    bf16x8_t pb[4];
+    const float psum = tile_probs(sc, c2, m_run, pb);
+    tile_values<D, P>(smem, vlds, pb, o);
+    l_run += psum;
+  } else if (mn) {
+    tile_scores<D, P ^ 1>(smem, klds, qv, sn);
+    raise_max<D>(tile_max(sn), c2, m_run, l_run, o);
+  }
+  wk.u += 1;
+  wk.ec = wk.en;
+  wk.en = wk.ef;
+  wk.ef = wk.u + 2 < wk.n ? __builtin_amdgcn_readfirstlane(raw) : 0;
+}
 
 template <int D>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) void k_attn_bf16(AttnArgs a) {
   using TT = Tile<D>;
-  __shared__ __attribute__((aligned(1024))) char smem[2 * TT::BYTES];
+  __shared__ __attribute__((aligned(1024))) char smem[Lds<D>::BYTES];
+  uint16_t* sched = reinterpret_cast<uint16_t*>(smem + Lds<D>::SCHED);
 
   const int t = threadIdx.x;
   const int lane = t & 63;
@@ -184,8 +406,6 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
   const long long row_b = (long long)bh * nb + (blk_b >= 0 ? blk_b : blk_a);
   const int ca = min(max(ld_const(a.counts, row_a), 0), nb);
   const int cb = blk_b >= 0 ? min(max(ld_const(a.counts, row_b), 0), nb) : 0;
-  const int32_t* la = a.lists + row_a * nb;
-  const int32_t* lb = a.lists + row_b * nb;
 
   const int q_local = (w & 1) * 32 + (lane & 31);
 
@@ -197,23 +417,27 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
     for (int ks = 0; ks < D / 16; ++ks) qv[ks] = *reinterpret_cast<const bf16x8_t*>(qrow + ks * 16);
   }
 
-  // Per-thread byte offsets of its 16-byte loads inside a tile (the same for every tile).
-  uint32_t koff[TT::KLOADS], voff[TT::VLOADS];
+  Walk wk;
+  wk.n = build_schedule(smem, sched, a.lists + row_a * nb, ca, a.lists + row_b * nb, cb, nb);
+
+  // Per-thread global byte offsets of its 16-byte tile loads, and per-lane LDS byte
+  // offsets of its MFMA operand chunks (both the same for every tile).
+  uint32_t klds[D / 16], vlds[4];
+  const uint32_t koff = (uint32_t)(kperm(t / TT::KCH) * D * 2 + (((t % TT::KCH) ^ k_swz<D>(t / TT::KCH)) * 16));
+  const uint32_t voff = (uint32_t)((t >> 3) * kBlock * 2 + (((t & 7) ^ v_swz(t >> 3)) * 16));
+  {
+    const int r0 = lane & 31;  // rows r0 and r0 + 32 share the swizzle
 #pragma unroll
-  for (int it = 0; it < TT::KLOADS; ++it) {
-    const int u = it * 256 + t;
-    const int r = u / TT::KCH, pc = u % TT::KCH;
-    koff[it] = (uint32_t)(kperm(r) * D * 2 + ((pc ^ k_swz<D>(r)) * 16));
-  }
+    for (int ks = 0; ks < D / 16; ++ks) klds[ks] = (uint32_t)(r0 * D * 2 + (((ks * 2 + hi) ^ k_swz<D>(r0)) * 16));
 #pragma unroll
-  for (int it = 0; it < TT::VLOADS; ++it) {
-    const int u = it * 256 + t;
-    const int dd = u >> 3, pc = u & 7;
-    voff[it] = (uint32_t)(dd * kBlock * 2 + ((pc ^ v_swz(dd)) * 16));
+    for (int kk = 0; kk < 4; ++kk) vlds[kk] = (uint32_t)(r0 * kBlock * 2 + (((2 * kk + hi) ^ v_swz(r0)) * 16));
   }
-  const char* kbase = reinterpret_cast<const char*>(a.k + (long long)bh * g.N * D);
-  const char* vbase = reinterpret_cast<const char*>(a.vt + (long long)bh * nb * D * kBlock);
-  ListPair lp{la, lb, ca, cb, nb, 0, 0};
+  // One resource per head: K and V^T of head bh are each N*D*2 bytes, at most 64 MiB
+  // (nb <= 4096 blocks of 64 tokens, d <= 128), so 32-bit offsets cover them.
+  const uint32_t head_bytes = (uint32_t)(g.N * D * 2);
+  const i32x4_t krs = make_rsrc(a.k + (long long)bh * g.N * D, head_bytes);
+  const i32x4_t vrs = make_rsrc(a.vt + (long long)bh * nb * D * kBlock, head_bytes);
+  const int mine = (w < 2) ? kSchedA : kSchedB;
 
   f32x16_t o[D / 32];
 #pragma unroll
@@ -223,95 +447,29 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
   float m_run = -INFINITY;  // in log2 units (scores * c2)
   float l_run = 0.f;
 
-  int j_cur;
-  bool na_cur, nb_cur;
-  bool have = lp.next(j_cur, na_cur, nb_cur);
-  if (have) issue_tile<D>(smem, 0, w, kbase, vbase, j_cur, koff, voff);
-  __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));  // Q registers and the first tile
-  int stage = 0;
-  while (have) {
-    int j_nxt;
-    bool na_nxt, nb_nxt;
-    const bool have_nxt = lp.next(j_nxt, na_nxt, nb_nxt);
-    if (have_nxt) {
-      issue_tile<D>(smem, stage ^ 1, w, kbase, vbase, j_nxt, koff, voff);
-      wait_vm_barrier<TT::KLOADS + TT::VLOADS>();  // this tile's loads done, the next tile's in flight
-    } else {
-      wait_vm_barrier<0>();
+  wk.u = 0;
+  wk.ec = wk.n > 0 ? __builtin_amdgcn_readfirstlane((int)sched[0]) : 0;
+  wk.en = wk.n > 1 ? __builtin_amdgcn_readfirstlane((int)sched[1]) : 0;
+  wk.ef = wk.n > 2 ? __builtin_amdgcn_readfirstlane((int)sched[2]) : 0;
+  f32x16_t s0[2], s1[2];
+  if (wk.n > 0) {
+    issue_rows<TT::KBYTES>(smem + Lds<D>::kslot(0), w, krs, (uint32_t)(wk.ec & kSchedJ) * TT::KBYTES, koff);
+    issue_rows<TT::VBYTES>(smem + Lds<D>::vslot(0), w, vrs, (uint32_t)(wk.ec & kSchedJ) * TT::VBYTES, voff);
+    if (wk.n > 1)
+      issue_rows<TT::KBYTES>(smem + Lds<D>::kslot(1), w, krs, (uint32_t)(wk.en & kSchedJ) * TT::KBYTES, koff);
+    wait_vm_lgkm_barrier();
+    if (wk.ec & mine) {
+      tile_scores<D, 0>(smem, klds, qv, s0);
+      raise_max<D>(tile_max(s0), a.c2, m_run, l_run, o);
     }
-
-    const bool mine = (w < 2) ? na_cur : nb_cur;
-    if (mine) {
-      const char* ks_lds = smem + stage * TT::BYTES;
-      const char* vs_lds = ks_lds + TT::KBYTES;
-      // S^T = K Q^T for the two 32-key halves of the tile.
-      f32x16_t sacc[2];
-#pragma unroll
-      for (int kh = 0; kh < 2; ++kh) {
-#pragma unroll
-        for (int r = 0; r < 16; ++r) sacc[kh][r] = 0.f;
-        const int krow = kh * 32 + (lane & 31);
-        const char* rowp = ks_lds + krow * (D * 2);
-        const int swz = k_swz<D>(krow);
-        bf16x8_t kv[D / 16];
-#pragma unroll
-        for (int ks = 0; ks < D / 16; ++ks)
-          kv[ks] = *reinterpret_cast<const bf16x8_t*>(rowp + (((ks * 2 + hi) ^ swz) * 16));
-#pragma unroll
-        for (int ks = 0; ks < D / 16; ++ks)
-          sacc[kh] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kv[ks], qv[ks], sacc[kh], 0, 0, 0);
-      }
-
-      // Online softmax in log2 units for this lane's query.
-      float mx = sacc[0][0];
-#pragma unroll
-      for (int kh = 0; kh < 2; ++kh)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) mx = fmaxf(mx, sacc[kh][r]);
-      mx = swap_max(mx) * a.c2;
-      if (__builtin_amdgcn_ballot_w64(mx > m_run + kRescaleLog2)) {
-        const float m_new = fmaxf(m_run, mx);
-        const float alpha = exp2_fast(m_run - m_new);
-        m_run = m_new;
-        l_run *= alpha;
-#pragma unroll
-        for (int dt = 0; dt < D / 32; ++dt)
-#pragma unroll
-          for (int r = 0; r < 16; ++r) o[dt][r] *= alpha;
-      }
-      float psum = 0.f;
-      bf16x8_t pb[4];
-#pragma unroll
-      for (int kh = 0; kh < 2; ++kh)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const float pv = exp2_fast(fmaf(sacc[kh][r], a.c2, -m_run));
-          psum += pv;
-          pb[kh * 2 + (r >> 3)][r & 7] = (__bf16)pv;
-        }
-      l_run += psum;
-
-      // O^T += V^T P^T: lane reads 8 consecutive keys of one channel row.
-#pragma unroll
-      for (int dt = 0; dt < D / 32; ++dt) {
-        const int dd = dt * 32 + (lane & 31);
-        const char* vrow = vs_lds + dd * (kBlock * 2);
-        const int swz = v_swz(dd);
-        bf16x8_t vv[4];
-#pragma unroll
-        for (int kk = 0; kk < 4; ++kk)
-          vv[kk] = *reinterpret_cast<const bf16x8_t*>(vrow + (((2 * kk + hi) ^ swz) * 16));
-#pragma unroll
-        for (int kk = 0; kk < 4; ++kk)
-          o[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vv[kk], pb[kk], o[dt], 0, 0, 0);
-      }
+    while (true) {
+      walk_step<D, 0>(smem, sched, wk, mine, w, krs, vrs, koff, voff, klds, vlds, qv, a.c2, s0, s1, o, m_run,
+                      l_run);
+      if (wk.u >= wk.n) break;
+      walk_step<D, 1>(smem, sched, wk, mine, w, krs, vrs, koff, voff, klds, vlds, qv, a.c2, s1, s0, o, m_run,
+                      l_run);
+      if (wk.u >= wk.n) break;
     }
-    wait_lgkm_barrier();  // every wave is done reading this stage before it is refilled
-    have = have_nxt;
-    j_cur = j_nxt;
-    na_cur = na_nxt;
-    nb_cur = nb_nxt;
-    stage ^= 1;
   }
 
   if (!active) return;
