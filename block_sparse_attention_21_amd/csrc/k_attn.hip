@@ -224,12 +224,40 @@ __device__ int build_schedule(char* smem_stage, uint16_t* sched, const int32_t* 
   return n;
 }
 
+// The next tiles' loads of one step: K(u+2) into K slot `kdst`, V^T(u+1) into V slot
+// `vdst`. load(i) issues this thread's i-th 16-byte load (K first, then V^T), so a caller
+// can spread the step's loads between its MFMAs instead of issuing them as one burst
+// (a burst of 1 KB loads from every wave stalls the issuing waves in the address unit).
+template <int D>
+struct StepLoads {
+  char* kdst;
+  char* vdst;
+  i32x4_t krs, vrs;
+  uint32_t ktile, vtile, koff, voff;
+  static constexpr int NK = Tile<D>::KBYTES / 16 / 256;
+  static constexpr int NV = Tile<D>::VBYTES / 16 / 256;
+  __device__ __forceinline__ void load(int i) const {
+    if (i < NK)
+      raw_buffer_load_lds(krs, (__attribute__((address_space(3))) uint32_t*)(kdst + i * 256 * 16), 16, (int)koff,
+                          (int)(ktile + i * 4096), 0, 0);
+    else
+      raw_buffer_load_lds(vrs, (__attribute__((address_space(3))) uint32_t*)(vdst + (i - NK) * 256 * 16), 16,
+                          (int)voff, (int)(vtile + (i - NK) * 4096), 0, 0);
+  }
+  __device__ __forceinline__ void load_all() const {
+#pragma unroll
+    for (int i = 0; i < NK + NV; ++i) load(i);
+  }
+};
+
 // S^T for one staged K tile: s[kh] holds keys kh*32 .. kh*32+31 (in the kperm row order)
-// against this wave's 32 queries. koff[ks]: this lane's byte offset of its K chunk for
-// k-step ks inside a slot; the two key halves are 32 rows apart.
-template <int D, int SLOT>
+// against this wave's 32 queries. klds[ks]: this lane's byte offset of its K chunk for
+// k-step ks inside a slot; the two key halves are 32 rows apart. With a StepLoads, one
+// of the step's loads goes out after each k-step (D/16 k-steps, D/16 loads).
+template <int D, int SLOT, bool LOADS>
 __device__ __forceinline__ void tile_scores(const char* smem, const uint32_t* klds, const bf16x8_t* qv,
-                                            f32x16_t (&s)[2]) {
+                                            f32x16_t (&s)[2], const StepLoads<D>* ld) {
+  static_assert(StepLoads<D>::NK + StepLoads<D>::NV == D / 16, "one load per k-step");
 #pragma unroll
   for (int kh = 0; kh < 2; ++kh)
 #pragma unroll
@@ -242,6 +270,7 @@ __device__ __forceinline__ void tile_scores(const char* smem, const uint32_t* kl
           *reinterpret_cast<const bf16x8_t*>(smem + Lds<D>::kslot(SLOT) + kh * 32 * D * 2 + klds[ks]);
       s[kh] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kv, qv[ks], s[kh], 0, 0, 0);
     }
+    if constexpr (LOADS) ld->load(ks);
   }
 }
 
@@ -302,8 +331,9 @@ __device__ __forceinline__ void raise_max(float mx_raw, float c2, float& m_run, 
 }
 
 // Instruction interleave of the steady state: the next tile's score MFMAs run under this
-// tile's exp/convert/sum work, then the value MFMAs under the next tile's maximum.
-// Masks: 0x008 MFMA, 0x100 LDS read, 0x402 VALU or transcendental.
+// tile's exp/convert/sum work and the step's tile loads, then the value MFMAs under the
+// next tile's maximum. Masks: 0x008 MFMA, 0x100 LDS read, 0x402 VALU or transcendental,
+// 0x010 vector memory.
 template <int D>
 __device__ __forceinline__ void schedule_overlap() {
   constexpr int NS = 2 * (D / 16);    // score MFMAs per tile
@@ -315,6 +345,7 @@ __device__ __forceinline__ void schedule_overlap() {
     __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
     __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
     __builtin_amdgcn_sched_group_barrier(0x402, VA, 0);
+    if (i & 1) __builtin_amdgcn_sched_group_barrier(0x010, 1, 0);  // one tile load per k-step
   }
 #pragma unroll
   for (int i = 0; i < NPV; ++i) {
@@ -342,10 +373,17 @@ __device__ __forceinline__ void walk_step(char* smem, const uint16_t* sched, Wal
                                           f32x16_t* o, float& m_run, float& l_run) {
   using TT = Tile<D>;
   wait_vm_lgkm_barrier();  // K(u+1), V(u) landed; every wave is done with step u-1
-  if (wk.u + 2 < wk.n)
-    issue_rows<TT::KBYTES>(smem + Lds<D>::kslot(P), w, krs, (uint32_t)(wk.ef & kSchedJ) * TT::KBYTES, koff);
-  if (wk.u + 1 < wk.n)
-    issue_rows<TT::VBYTES>(smem + Lds<D>::vslot(P ^ 1), w, vrs, (uint32_t)(wk.en & kSchedJ) * TT::VBYTES, voff);
+  // Past the end of the schedule the loads fetch block 0 into the free slot (never read):
+  // that keeps the step free of branches around its loads.
+  StepLoads<D> ld;
+  ld.kdst = smem + Lds<D>::kslot(P) + w * 64 * 16;
+  ld.vdst = smem + Lds<D>::vslot(P ^ 1) + w * 64 * 16;
+  ld.krs = krs;
+  ld.vrs = vrs;
+  ld.ktile = (uint32_t)(wk.ef & kSchedJ) * TT::KBYTES;  // ef, en are 0 past the end
+  ld.vtile = (uint32_t)(wk.en & kSchedJ) * TT::VBYTES;
+  ld.koff = koff;
+  ld.voff = voff;
   const int look = min(wk.u + 3, wk.n - 1);
   const int raw = sched[look];  // entry u+3, read now and used next step
 
@@ -353,7 +391,7 @@ __device__ __forceinline__ void walk_step(char* smem, const uint16_t* sched, Wal
   const bool mn = (wk.en & mine) != 0;  // en is 0 past the end
   if (mc && mn) {
     bf16x8_t pb[4];
-    tile_scores<D, P ^ 1>(smem, klds, qv, sn);
+    tile_scores<D, P ^ 1, true>(smem, klds, qv, sn, &ld);
     const float psum = tile_probs(sc, c2, m_run, pb);
     tile_values<D, P>(smem, vlds, pb, o);
     const float mx = tile_max(sn);
@@ -361,13 +399,16 @@ __device__ __forceinline__ void walk_step(char* smem, const uint16_t* sched, Wal
     l_run += psum;
     raise_max<D>(mx, c2, m_run, l_run, o);
   } else if (mc) {
+    ld.load_all();
     bf16x8_t pb[4];
     const float psum = tile_probs(sc, c2, m_run, pb);
     tile_values<D, P>(smem, vlds, pb, o);
     l_run += psum;
   } else if (mn) {
-    tile_scores<D, P ^ 1>(smem, klds, qv, sn);
+    tile_scores<D, P ^ 1, true>(smem, klds, qv, sn, &ld);
     raise_max<D>(tile_max(sn), c2, m_run, l_run, o);
+  } else {
+    ld.load_all();
   }
   wk.u += 1;
   wk.ec = wk.en;
@@ -389,11 +430,11 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
   const int nb = g.nb;
   const int F = g.nbh * g.nbw;
 
-  // XCD-aware placement: consecutive logical items run on the same XCD (dispatch is
-  // round-robin over 8 XCDs), so one XCD's L2 serves one head's K/V at a time.
-  const int p = blockIdx.x;
-  const int base = a.grid >> 3, rem = a.grid & 7, x = p & 7;
-  const int logical = x * base + min(x, rem) + (p >> 3);
+  // Plain dispatch order: the resident workgroups of all eight XCDs work on the same one
+  // or two heads at a time, whose K/V (tens of MB) stay in the shared last-level cache;
+  // grouping consecutive items per XCD instead spreads eight heads over the XCDs and
+  // measured slower once their K/V outgrow that cache.
+  const int logical = blockIdx.x;
   const int bh = logical / a.pairs;
   const int pos = logical - bh * a.pairs;
   const int pair = ld_const(a.order, (long long)bh * a.pairs + pos);
@@ -459,7 +500,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
       issue_rows<TT::KBYTES>(smem + Lds<D>::kslot(1), w, krs, (uint32_t)(wk.en & kSchedJ) * TT::KBYTES, koff);
     wait_vm_lgkm_barrier();
     if (wk.ec & mine) {
-      tile_scores<D, 0>(smem, klds, qv, s0);
+      tile_scores<D, 0, false>(smem, klds, qv, s0, nullptr);
       raise_max<D>(tile_max(s0), a.c2, m_run, l_run, o);
     }
     while (true) {
