@@ -330,23 +330,27 @@ __device__ __forceinline__ void raise_max(float mx_raw, float c2, float& m_run, 
   }
 }
 
-// Instruction interleave of the steady state: the next tile's score MFMAs run under this
-// tile's exp/convert/sum work and the step's tile loads, then the value MFMAs under the
-// next tile's maximum. Masks: 0x008 MFMA, 0x100 LDS read, 0x402 VALU or transcendental,
-// 0x010 vector memory.
+// Instruction interleave of the steady state, in two scheduling regions. Phase A: the
+// next tile's score MFMAs run under this tile's exp/convert/sum work and the step's tile
+// loads. Phase B: the value MFMAs run under the next tile's maximum. Masks: 0x008 MFMA,
+// 0x100 LDS read, 0x402 VALU or transcendental, 0x010 vector memory.
 template <int D>
-__device__ __forceinline__ void schedule_overlap() {
-  constexpr int NS = 2 * (D / 16);    // score MFMAs per tile
-  constexpr int NPV = 4 * (D / 32);   // value MFMAs per tile
-  constexpr int VA = 112 / NS;        // VALU slots under each score MFMA
+__device__ __forceinline__ void schedule_phase_a() {
+  constexpr int NS = 2 * (D / 16);
+  constexpr int VA = 112 / NS;
   __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
 #pragma unroll
   for (int i = 0; i < NS; ++i) {
     __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
     __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
     __builtin_amdgcn_sched_group_barrier(0x402, VA, 0);
-    if (i & 1) __builtin_amdgcn_sched_group_barrier(0x010, 1, 0);  // one tile load per k-step
+    if (i & 1) __builtin_amdgcn_sched_group_barrier(0x010, 1, 0);
   }
+}
+template <int D>
+__device__ __forceinline__ void schedule_phase_b() {
+  constexpr int NPV = 4 * (D / 32);
+  __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
 #pragma unroll
   for (int i = 0; i < NPV; ++i) {
     __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
@@ -391,11 +395,18 @@ __device__ __forceinline__ void walk_step(char* smem, const uint16_t* sched, Wal
   const bool mn = (wk.en & mine) != 0;  // en is 0 past the end
   if (mc && mn) {
     bf16x8_t pb[4];
+    // Phase A (exp-heavy) runs at raised wave priority and phase B (MFMA-dense) at the
+    // default: the two waves sharing a SIMD then tend to sit in opposite phases, which
+    // measured 3-8% faster than equal priorities.
+    __builtin_amdgcn_s_setprio(1);
     tile_scores<D, P ^ 1, true>(smem, klds, qv, sn, &ld);
     const float psum = tile_probs(sc, c2, m_run, pb);
+    schedule_phase_a<D>();
+    __builtin_amdgcn_s_setprio(0);
     tile_values<D, P>(smem, vlds, pb, o);
     const float mx = tile_max(sn);
-    schedule_overlap<D>();
+    schedule_phase_b<D>();
+    __builtin_amdgcn_s_setprio(0);  // no-op for priority; closes phase B's scheduling region
     l_run += psum;
     raise_max<D>(mx, c2, m_run, l_run, o);
   } else if (mc) {
