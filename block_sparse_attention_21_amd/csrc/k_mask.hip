@@ -9,8 +9,8 @@
 // serve as importance and are filtered by a threshold.
 //
 // Two kernels:
-//  k_scores  S = pool_scale * Qbar Kbar^T per (b, h), a float64 tile GEMM
-//            written to the caller's workspace (fixed summation order).
+//  k_scores  S = pool_scale * Qbar Kbar^T per (b, h), a float64 matrix-core
+//            GEMM written to the caller's workspace (fixed summation order).
 //  k_select  one workgroup per row (b, h, i): row max, softmax, then either
 //            the CDF cut or the logit threshold; OR the STA window; pack bits,
 //            count, list. The CDF cut ranks 64-bit keys holding the
@@ -34,59 +34,80 @@ namespace abla {
 namespace {
 
 // ---------------------------------------------------------------- scores
-constexpr int kTile = 64;
-constexpr int kKc = 32;  // reduction chunk
+// S = pool_scale * Qbar Kbar^T on the float64 matrix cores (v_mfma_f64_16x16x4_f64,
+// same peak rate as float64 FMA but a quarter of the operand traffic per FMA).
+// Operand layout of one 16x16x4 product: lane l holds A[l % 16][l / 16] and
+// B[l / 16][l % 16]; the result register r of lane l is D[4r + l / 16][l % 16].
+// A workgroup of four waves computes a TM x TM tile, each wave a (TM/2)^2 quarter as
+// (TM/32)^2 16x16 tiles. The reduction runs in chunks of 16 channels; within a chunk,
+// product step s uses channel k0 + 4*(l / 16) + s in lane l for both operands, so every
+// output element sums its 128 (or 64) products in one fixed order, and two identical
+// Kbar rows give bit-identical scores.
+typedef double f64x4_t __attribute__((ext_vector_type(4)));
 
-__global__ __launch_bounds__(256) void k_scores(const double* __restrict__ qbar, const double* __restrict__ kbar,
-                                                double* __restrict__ S, int nb, int d, double scale) {
-  __shared__ double qs[kTile][kKc + 1];
-  __shared__ double ks[kTile][kKc + 1];
-  const int t = threadIdx.x;
-  const int tx = t & 15, ty = t >> 4;
-  const int j0 = blockIdx.x * kTile, i0 = blockIdx.y * kTile;
+template <int TM>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void k_scores(
+    const double* __restrict__ qbar, const double* __restrict__ kbar, double* __restrict__ S, int nb, int d,
+    double scale) {
+  constexpr int NT = TM / 32;  // 16x16 tiles per wave side
+  const int t = threadIdx.x, lane = t & 63, w = t >> 6;
+  const int r16 = lane & 15, kq = lane >> 4;
+  const int i0 = blockIdx.y * TM + (w >> 1) * (TM / 2);
+  const int j0 = blockIdx.x * TM + (w & 1) * (TM / 2);
   const long long bh = blockIdx.z;
   const double* qh = qbar + bh * nb * d;
   const double* kh = kbar + bh * nb * d;
-  double acc[4][4];
-#pragma unroll
-  for (int a = 0; a < 4; ++a)
-#pragma unroll
-    for (int b = 0; b < 4; ++b) acc[a][b] = 0.0;
 
-  for (int k0 = 0; k0 < d; k0 += kKc) {
-    for (int idx = t; idx < kTile * kKc / 2; idx += 256) {
-      const int row = idx / (kKc / 2), c2 = (idx % (kKc / 2)) * 2;
-      double2 qv = make_double2(0.0, 0.0), kv = qv;
-      if (i0 + row < nb) qv = *reinterpret_cast<const double2*>(qh + (long long)(i0 + row) * d + k0 + c2);
-      if (j0 + row < nb) kv = *reinterpret_cast<const double2*>(kh + (long long)(j0 + row) * d + k0 + c2);
-      qs[row][c2] = qv.x; qs[row][c2 + 1] = qv.y;
-      ks[row][c2] = kv.x; ks[row][c2 + 1] = kv.y;
+  f64x4_t acc[NT][NT];
+#pragma unroll
+  for (int a = 0; a < NT; ++a)
+#pragma unroll
+    for (int b = 0; b < NT; ++b) acc[a][b] = f64x4_t{0.0, 0.0, 0.0, 0.0};
+
+  for (int k0 = 0; k0 < d; k0 += 16) {
+    double av[NT][4], bv[NT][4];
+#pragma unroll
+    for (int a = 0; a < NT; ++a) {
+      const int i = i0 + a * 16 + r16;
+      double2 x = make_double2(0.0, 0.0), y = x;
+      if (i < nb) {
+        const double2* src = reinterpret_cast<const double2*>(qh + (long long)i * d + k0 + 4 * kq);
+        x = src[0];
+        y = src[1];
+      }
+      av[a][0] = x.x; av[a][1] = x.y; av[a][2] = y.x; av[a][3] = y.y;
     }
-    __syncthreads();
-#pragma unroll 8
-    for (int kk = 0; kk < kKc; ++kk) {
-      double av[4], bv[4];
 #pragma unroll
-      for (int a = 0; a < 4; ++a) av[a] = qs[ty + 16 * a][kk];
-#pragma unroll
-      for (int b = 0; b < 4; ++b) bv[b] = ks[tx + 16 * b][kk];
-#pragma unroll
-      for (int a = 0; a < 4; ++a)
-#pragma unroll
-        for (int b = 0; b < 4; ++b) acc[a][b] = fma(av[a], bv[b], acc[a][b]);
+    for (int b = 0; b < NT; ++b) {
+      const int j = j0 + b * 16 + r16;
+      double2 x = make_double2(0.0, 0.0), y = x;
+      if (j < nb) {
+        const double2* src = reinterpret_cast<const double2*>(kh + (long long)j * d + k0 + 4 * kq);
+        x = src[0];
+        y = src[1];
+      }
+      bv[b][0] = x.x; bv[b][1] = x.y; bv[b][2] = y.x; bv[b][3] = y.y;
     }
-    __syncthreads();
+#pragma unroll
+    for (int st = 0; st < 4; ++st)
+#pragma unroll
+      for (int a = 0; a < NT; ++a)
+#pragma unroll
+        for (int b = 0; b < NT; ++b)
+          acc[a][b] = __builtin_amdgcn_mfma_f64_16x16x4f64(av[a][st], bv[b][st], acc[a][b], 0, 0, 0);
   }
 #pragma unroll
-  for (int a = 0; a < 4; ++a) {
-    const int i = i0 + ty + 16 * a;
-    if (i >= nb) continue;
+  for (int a = 0; a < NT; ++a)
 #pragma unroll
-    for (int b = 0; b < 4; ++b) {
-      const int j = j0 + tx + 16 * b;
-      if (j < nb) S[(bh * nb + i) * nb + j] = acc[a][b] * scale;
+    for (int r = 0; r < 4; ++r) {
+      const int i = i0 + a * 16 + 4 * r + kq;
+      if (i >= nb) continue;
+#pragma unroll
+      for (int b = 0; b < NT; ++b) {
+        const int j = j0 + b * 16 + r16;
+        if (j < nb) S[(bh * nb + i) * nb + j] = acc[a][b][r] * scale;
+      }
     }
-  }
 }
 
 // ---------------------------------------------------------------- select
@@ -145,16 +166,47 @@ struct RadixScratch {
 };
 
 // Smallest key K among this row's keys such that the total mass of the keys above K
-// is < thr_fx: the last rank the CDF cut keeps. MSB-first radix select: each pass
-// histograms (count, exact fixed-point mass) the next 11-bit digit of the keys that
-// match the prefix fixed so far and descends into the lowest bucket whose top key is
-// still kept. Stops when that bucket holds one key.
+// is < thr_fx: the last rank the CDF cut keeps. MSB-first radix select below the row's
+// common key prefix: each pass histograms (count, exact fixed-point mass) the next
+// 11-bit digit of the keys that match the prefix fixed so far and descends into the
+// lowest bucket whose top key is still kept. Stops when that bucket holds one key.
 template <int NPT>
 __device__ unsigned long long radix_last_kept(const unsigned long long* key, int t, int nb,
                                               unsigned long long thr_fx, RadixScratch& rs) {
   const int lane = t & 63, wv = t >> 6;
-  unsigned long long pmask = 0, pval = 0, above = 0;
-  int shift = 64;
+  // All keys of the row share the bits above the highest bit in which the largest and
+  // the smallest key differ (sign and high exponent bits, typically): start the digits
+  // there, so the first pass already spreads the keys over many buckets.
+  unsigned long long kmax = 0, kmin = ~0ull;
+#pragma unroll
+  for (int k = 0; k < NPT; ++k)
+    if (t + kSelThreads * k < nb) {
+      kmax = key[k] > kmax ? key[k] : kmax;
+      kmin = key[k] < kmin ? key[k] : kmin;
+    }
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) {
+    const unsigned long long a = __shfl_xor(kmax, o), b = __shfl_xor(kmin, o);
+    kmax = a > kmax ? a : kmax;
+    kmin = b < kmin ? b : kmin;
+  }
+  if (lane == 0) {
+    rs.part[wv] = kmax;
+    rs.cand_cum[wv] = kmin;
+  }
+  __syncthreads();
+  kmax = rs.part[0];
+  kmin = rs.cand_cum[0];
+#pragma unroll
+  for (int w = 1; w < kWaves; ++w) {
+    kmax = rs.part[w] > kmax ? rs.part[w] : kmax;
+    kmin = rs.cand_cum[w] < kmin ? rs.cand_cum[w] : kmin;
+  }
+  __syncthreads();
+  if (kmax == kmin) return kmax;  // one key (or all equal): it is the last kept
+  int shift = 64 - __clzll((long long)(kmax ^ kmin));  // bits below the common prefix
+  unsigned long long pmask = shift == 64 ? 0ull : ~((1ull << shift) - 1);
+  unsigned long long pval = kmax & pmask, above = 0;
   while (true) {
     const int db = shift >= kDigitBits ? kDigitBits : shift;
     shift -= db;
@@ -420,8 +472,15 @@ void launch_select(const KGeom& g, const double* S, uint32_t* words, int32_t* co
 hipError_t launch_build_mask(const KGeom& g, const abla_mask_params& p, const double* qbar, const double* kbar,
                              uint32_t* words, int32_t* counts, int32_t* lists, double* scores, hipStream_t s) {
   const double scale = p.pool_scale > 0.0 ? p.pool_scale : 1.0 / sqrt((double)g.d);
-  const int tiles = (g.nb + kTile - 1) / kTile;
-  k_scores<<<dim3(tiles, tiles, (unsigned)(g.B * g.H)), 256, 0, s>>>(qbar, kbar, scores, g.nb, g.d, scale);
+  // 128 x 128 tiles when they fill the GPU several times over, else 64 x 64.
+  const long long t128 = (g.nb + 127) / 128;
+  if (t128 * t128 * g.B * g.H >= 2048) {
+    k_scores<128><<<dim3((unsigned)t128, (unsigned)t128, (unsigned)(g.B * g.H)), 256, 0, s>>>(qbar, kbar, scores,
+                                                                                           g.nb, g.d, scale);
+  } else {
+    const unsigned t64 = (unsigned)((g.nb + 63) / 64);
+    k_scores<64><<<dim3(t64, t64, (unsigned)(g.B * g.H)), 256, 0, s>>>(qbar, kbar, scores, g.nb, g.d, scale);
+  }
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
 
