@@ -54,8 +54,11 @@ template <typename E, int D, bool POOL, bool BLOCK_T>
 __global__ __launch_bounds__(kThreads) void k_reorder_fwd(const E* __restrict__ x, E* __restrict__ y,
                                                           double* __restrict__ pooled, KGeom g) {
   using S = Shape<E, D>;
-  constexpr int TILE_STRIDE = D + S::EPC;  // padded LDS row (elements) for the channel-major transpose
-  __shared__ __attribute__((aligned(16))) E tile[BLOCK_T ? kBlock * TILE_STRIDE : 1];
+  // Channel-major transpose tile: token row r holds its D elements as CPR 16-byte chunks, chunk
+  // cc stored at position cc ^ ((r / EPC) % CPR). The gathers below (EPC tokens of one channel
+  // per lane, one group of EPC tokens per lane of a run of kBlock/EPC lanes) then hit distinct
+  // banks, and the 16-byte row writes stay conflict-free.
+  __shared__ __attribute__((aligned(16))) E tile[BLOCK_T ? kBlock * D : 1];
   __shared__ double red[POOL ? kThreads * S::EPC : 1];
 
   const int blk = blockIdx.x;
@@ -76,7 +79,7 @@ __global__ __launch_bounds__(kThreads) void k_reorder_fwd(const E* __restrict__ 
     const long long n = token_of(g, i, r);
     const uint4 v = *reinterpret_cast<const uint4*>(xh + n * D + cc * S::EPC);
     if constexpr (BLOCK_T) {
-      *reinterpret_cast<uint4*>(&tile[r * TILE_STRIDE + cc * S::EPC]) = v;
+      *reinterpret_cast<uint4*>(&tile[r * D + ((cc ^ ((r / S::EPC) % S::CPR)) * S::EPC)]) = v;
     } else {
       *reinterpret_cast<uint4*>(y + ((long long)bh * g.N + (long long)i * kBlock + r) * D + cc * S::EPC) = v;
     }
@@ -85,16 +88,20 @@ __global__ __launch_bounds__(kThreads) void k_reorder_fwd(const E* __restrict__ 
 
   if constexpr (BLOCK_T) {
     __syncthreads();
-    // Output block is [D][64]; chunk oc covers channel c = oc % D, tokens g*EPC .. +EPC-1.
+    // Output block is [D][64]; chunk oc covers tokens grp*EPC .. +EPC-1 of channel c, with
+    // grp = oc % G and c = oc / G (G = 64 / EPC): each run of G lanes writes one channel's
+    // whole 128- or 256-byte row.
+    constexpr int G = kBlock / S::EPC;
     constexpr int OUT_CHUNKS = D * kBlock / S::EPC;
     E* yb = y + ((long long)bh * g.nb + i) * D * kBlock;
 #pragma unroll
     for (int oc = t; oc < OUT_CHUNKS; oc += kThreads) {
-      const int c = oc % D;
-      const int grp = oc / D;
+      const int grp = oc % G;
+      const int c = oc / G;
+      const int pos = ((c / S::EPC) ^ (grp % S::CPR)) * S::EPC + c % S::EPC;  // rows grp*EPC+e share r/EPC = grp
       E vals[S::EPC];
 #pragma unroll
-      for (int e = 0; e < S::EPC; ++e) vals[e] = tile[(grp * S::EPC + e) * TILE_STRIDE + c];
+      for (int e = 0; e < S::EPC; ++e) vals[e] = tile[(grp * S::EPC + e) * D + pos];
       uint4 v;
       __builtin_memcpy(&v, vals, 16);
       *reinterpret_cast<uint4*>(yb + c * kBlock + grp * S::EPC) = v;
