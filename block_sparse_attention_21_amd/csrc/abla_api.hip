@@ -106,7 +106,8 @@ abla_status abla_build_mask(const abla_geom* g, const abla_mask_params* p, const
 
 size_t abla_sparse_attn_workspace_bytes(const abla_geom* g) {
   if (check_geom(g) != ABLA_OK) return 0;
-  return (size_t)(g->B * g->H * nb_of(g)) * sizeof(int32_t);
+  // Visiting order (at most nb ints per (b, h)), then one int of walk mode, padded to 256 bytes.
+  return (size_t)(g->B * g->H * nb_of(g)) * sizeof(int32_t) + 256;
 }
 
 abla_status abla_sparse_attn_fwd(const abla_geom* g, int32_t dtype, float scale, const void* q_r,

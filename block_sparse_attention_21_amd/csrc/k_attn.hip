@@ -25,7 +25,9 @@
 // maximum of tile u+1 (an explicit MFMA / LDS-read / VALU interleave). One barrier
 // per step. Tiles move global -> LDS directly (buffer_load ... lds), with a per-row
 // XOR swizzle of 16-byte chunks so the MFMA operand reads are free of bank
-// conflicts. Pairs are visited longest-first within each head (pair_order) so the
+// conflicts. The visiting order of the pairs (k_pair_order) depends on the list
+// lengths: with short lists, whole temporal columns of one patch per XCD (neighbouring
+// workgroups then share key blocks in L2); with long lists, longest-first per head so the
 // long rows of the kept-count distribution do not form the tail.
 //
 // float32 path (k_attn_f32): plain FMA arithmetic, two threads per query row.
@@ -42,7 +44,8 @@ struct AttnArgs {
   const uint16_t* vt;
   const int32_t* counts;
   const int32_t* lists;
-  const int32_t* order;  // pair ids, longest first within each (b, h)
+  const int32_t* order;  // pair ids per (b, h) in visiting order (see k_pair_order)
+  const int32_t* walk_mode;  // one int written by k_pair_order: 1 = column order
   uint16_t* out;
   float* lse;
   KGeom g;
@@ -445,7 +448,20 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
   // or two heads at a time, whose K/V (tens of MB) stay in the shared last-level cache;
   // grouping consecutive items per XCD instead spreads eight heads over the XCDs and
   // measured slower once their K/V outgrow that cache.
-  const int logical = blockIdx.x;
+  int logical = blockIdx.x;
+  if (ld_const(a.walk_mode, 0)) {
+    // Column order: columns (all C frame pairs of one patch) are dealt round-robin to the
+    // 8 XCDs, so on XCD x queue rank k runs column 8*(k / C) + x, frame pair k % C: the
+    // workgroups that start one after another on an XCD are temporally adjacent pairs with
+    // largely the same key blocks. Columns that do not fill a last round of 8 keep the
+    // plain mapping.
+    const int C = a.pairs / F;
+    const int full = (a.grid / C / 8) * 8 * C;
+    if (logical < full) {
+      const int x = logical & 7, k = logical >> 3;
+      logical = (8 * (k / C) + x) * C + k % C;
+    }
+  }
   const int bh = logical / a.pairs;
   const int pos = logical - bh * a.pairs;
   const int pair = ld_const(a.order, (long long)bh * a.pairs + pos);
@@ -670,20 +686,66 @@ __device__ void desc_exclusive_scan(int* h, int n, int* part) {
   __syncthreads();
 }
 
-// Longest-first order of the query-block pairs (i, i + nbh*nbw) of each (b, h): a counting
-// sort on the pair's total kept count. Pair p covers blocks a = (p / F)*2F + p % F and a + F.
+// Visiting order of the query-block pairs (i, i + F) of each (b, h), F = nbh*nbw; pair p covers
+// blocks a = (p / F)*2F + p % F and a + F, so pair tp*F + s is frame pair tp of patch s.
+// Two orders, chosen once per launch from the mean kept count per row over all heads:
+//  - short lists (mean <= kColumnMaxCount): column order. Patches longest-first by their
+//    total kept count, each patch's C frame pairs in time order. Workgroups then start
+//    about one step apart on an XCD next to temporally adjacent pairs, which share most
+//    key blocks, so their tile loads hit in L2.
+//  - otherwise: pairs longest-first by their kept count (counting sort), so the long rows
+//    do not form the tail; with long lists neighbouring workgroups start too far apart
+//    for L2 reuse and the balance matters more.
+// Every workgroup computes the same mean (a fixed-order sum); workgroup 0 stores the mode.
+constexpr int kColumnMaxCount = 96;
+
 __global__ __launch_bounds__(1024) void k_pair_order(const int32_t* __restrict__ counts, int32_t* __restrict__ order,
-                                                     int nb, int F, int pairs) {
+                                                     int32_t* __restrict__ mode_out, int nb, int F, int pairs,
+                                                     long long rows) {
   __shared__ int hist[2 * kMaxBlocks + 1];
   __shared__ int scan_part[16];
-  const int t = threadIdx.x;
+  __shared__ long long wsum[16];
+  const int t = threadIdx.x, lane = t & 63, wv = t >> 6;
   const long long bh = blockIdx.x;
   const int32_t* c = counts + bh * nb;
+
+  long long part = 0;
+  for (long long r = t; r < rows; r += 1024) part += min(max(counts[r], 0), nb);
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) part += __shfl_xor(part, o);
+  if (lane == 0) wsum[wv] = part;
+  __syncthreads();
+  long long total = 0;
+  for (int w = 0; w < 16; ++w) total += wsum[w];
+  const bool column = total <= (long long)kColumnMaxCount * rows;
+  if (bh == 0 && t == 0) mode_out[0] = column ? 1 : 0;
+
+  auto blk_count = [&](int blk) { return min(max(c[blk], 0), nb); };
+  if (column) {
+    const int C = pairs / F;
+    int* tot = hist;  // F <= nb <= kMaxBlocks
+    for (int s = t; s < F; s += 1024) {
+      int sum = 0;
+      for (int tp = 0; tp < C; ++tp) {
+        const int blk = tp * 2 * F + s;
+        sum += blk_count(blk);
+        if (blk + F < nb) sum += blk_count(blk + F);
+      }
+      tot[s] = sum;
+    }
+    __syncthreads();
+    for (int s = t; s < F; s += 1024) {
+      int rank = 0;
+      for (int q = 0; q < F; ++q) rank += (tot[q] > tot[s]) || (tot[q] == tot[s] && q < s);
+      for (int tp = 0; tp < C; ++tp) order[bh * pairs + (long long)rank * C + tp] = tp * F + s;
+    }
+    return;
+  }
   const int kmax = 2 * nb;
   auto key = [&](int pr) {
     const int blk = (pr / F) * 2 * F + pr % F;
-    int k = min(max(c[blk], 0), nb);
-    if (blk + F < nb) k += min(max(c[blk + F], 0), nb);
+    int k = blk_count(blk);
+    if (blk + F < nb) k += blk_count(blk + F);
     return k;
   };
   for (int v = t; v <= kmax; v += 1024) hist[v] = 0;
@@ -725,7 +787,8 @@ hipError_t launch_sparse_attn(const KGeom& g, int dtype, float scale, const void
   if (dtype == ABLA_BF16) {
     const int F = g.nbh * g.nbw;
     const int pairs = ((g.T + 1) / 2) * F;
-    k_pair_order<<<dim3(bhs), 1024, 0, s>>>(counts, row_order, g.nb, F, pairs);
+    int32_t* mode = row_order + (long long)bhs * g.nb;  // after the order array (pairs <= nb per head)
+    k_pair_order<<<dim3(bhs), 1024, 0, s>>>(counts, row_order, mode, g.nb, F, pairs, (long long)bhs * g.nb);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     AttnArgs a;
@@ -735,6 +798,7 @@ hipError_t launch_sparse_attn(const KGeom& g, int dtype, float scale, const void
     a.counts = counts;
     a.lists = lists;
     a.order = row_order;
+    a.walk_mode = mode;
     a.out = static_cast<uint16_t*>(out);
     a.lse = lse;
     a.g = g;

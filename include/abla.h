@@ -135,7 +135,8 @@ abla_status abla_build_mask(const abla_geom* g, const abla_mask_params* p,
                             uint32_t* mask_words, int32_t* counts, int32_t* lists,
                             void* workspace, size_t workspace_bytes, void* stream);
 
-/* Bytes of scratch abla_sparse_attn_fwd needs: B*H*nb*4 (longest-first row order). */
+/* Bytes of scratch abla_sparse_attn_fwd needs: B*H*nb*4 + 256 (the visiting order of the
+ * query blocks, chosen from the kept counts on the device, and one word of walk mode). */
 size_t abla_sparse_attn_workspace_bytes(const abla_geom* g);
 
 /* Block-sparse attention forward over the kept 64 x 64 blocks.

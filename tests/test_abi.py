@@ -117,7 +117,7 @@ def test_attention_errors(A):
     assert attn_call(A, g, ws=None) == 3
     assert attn_call(A, g, ws_bytes=2 * 18 * 4 - 1) == 3
     assert attn_call(A, G(A, d=32)) == 2
-    assert A.sparse_attn_workspace_bytes(A.Geometry(1, 2, 3, 16, 24, 128)) == 2 * 18 * 4
+    assert A.sparse_attn_workspace_bytes(A.Geometry(1, 2, 3, 16, 24, 128)) == 2 * 18 * 4 + 256
 
 
 def test_binding_rejects_cpu_tensors(A):
