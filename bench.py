@@ -5,13 +5,15 @@ reorder Q (+ block means), reorder K (+ block means), reorder V (channel-major
 blocks), build the mask, block-sparse attention writing O in the original order.
 
 Prints ONE JSON line. `value` is the dense-equivalent throughput
-4*B*H*N^2*d / (time per layer); `ms_per_step` is the time per layer.
+4*B*H*N^2*d / (time per layer); `ms_per_step` is the time per layer. Steps are
+launched eagerly; with --graph each step replays the whole path captured once in a
+HIP graph, and `ms_per_layer_eager` then gives the eager time for comparison.
 The `roofline` object is for the attention kernel (the dominant one): the
 FLOPs of the kept 64x64 blocks per launch over its average launch time, timed
 with HIP events on the stream the kernels run on. `cpu_baseline` times the CPU
 oracle on a bounded sample of the same workload and scales it to the layer.
 
-Usage: python bench.py [--gpus 1] [--steps 10] [--warmup 3] [--workload 480p] [--secondary 720p]
+Usage: python bench.py [--gpus 1] [--steps 10] [--warmup 20] [--workload 480p] [--secondary 720p] [--graph]
 """
 import argparse
 import json
@@ -32,12 +34,15 @@ def parse():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=10)
-    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--warmup", type=int, default=20,
+                    help="untimed steps first (a few ms of load is not enough for the clocks to settle)")
     ap.add_argument("--workload", default="480p")
     ap.add_argument("--secondary", default="720p", help="second workload reported alongside ('' for none)")
     ap.add_argument("--cpu-seconds", type=float, default=15.0, help="budget of the CPU oracle sample (0: skip)")
     ap.add_argument("--traffic", default=os.path.join(ROOT, "profiles", "traffic.json"),
                     help="measured HBM bytes per attention launch (from rocprofv3 counters)")
+    ap.add_argument("--graph", action="store_true",
+                    help="replay the step captured in a HIP graph instead of launching it eagerly")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="only run a plain device copy of MIB MiB (reference for the FETCH/WRITE_SIZE counters)")
     return ap.parse_args()
@@ -68,7 +73,7 @@ def timed(fn, reps, stream):
     return start.elapsed_time(end) / reps
 
 
-def measure(name, steps, warmup):
+def measure(name, steps, warmup, use_graph=False):
     import torch
     import block_sparse_attention_21_amd as A
     from gen import WORKLOADS, make_qkv
@@ -79,15 +84,20 @@ def measure(name, steps, warmup):
     q, k, v = make_qkv(w, device="cuda")
     run = A.NablaAttention(geom, prm, dtype=q.dtype)
     stream = torch.cuda.current_stream()
+    # One step = the whole path on resident inputs, launched eagerly, or with --graph replayed
+    # from a HIP graph (same kernels, same arguments; measured no faster on this path).
+    graph = run.capture(q, k, v) if use_graph else None
+    step = graph.replay if graph is not None else (lambda: run(q, k, v))
     for _ in range(warmup):
-        run(q, k, v)
+        step()
     torch.cuda.synchronize()
 
     # The timed region: exactly `steps` whole-path steps.
     torch.cuda.synchronize()
     t0 = time.perf_counter()
-    ms_step = timed(lambda: run(q, k, v), steps, stream)
+    ms_step = timed(step, steps, stream)
     wall = (time.perf_counter() - t0) * 1e3 / steps
+    ms_eager = timed(lambda: run(q, k, v), steps, stream) if graph is not None else ms_step
 
     # Per-stage averages (same inputs, state left by the path).
     ms_reorder = timed(lambda: run.reorder_pool(q, k, v), steps, stream)
@@ -103,7 +113,8 @@ def measure(name, steps, warmup):
     pooled_bytes = w.B * w.H * w.nb * w.d * 8
     reorder_bytes = 6 * tensor_bytes + 2 * pooled_bytes
     return dict(
-        w=w, geom=geom, kept=kept, keep_fraction=kept / total, ms_step=ms_step, wall_ms_step=wall,
+        w=w, geom=geom, kept=kept, keep_fraction=kept / total, ms_step=ms_step, wall_ms_step=wall, ms_eager=ms_eager,
+        graph=graph is not None,
         ms_reorder=ms_reorder, ms_mask=ms_mask, ms_attn=ms_attn, dense_flops=dense, kept_flops=kept_fl,
         reorder_gbs=reorder_bytes / (ms_reorder * 1e-3) / 1e9, tensor_bytes=tensor_bytes,
         counts=run.counts, run=run, q=q, k=k, v=v,
@@ -170,7 +181,7 @@ def main():
     if args.copy_calibration:
         copy_calibration(args.copy_calibration)
         return
-    r = measure(args.workload, args.steps, args.warmup)
+    r = measure(args.workload, args.steps, args.warmup, use_graph=args.graph)
     w, geom = r["w"], r["geom"]
     value = r["dense_flops"] / (r["ms_step"] * 1e-3) / 1e12
     attn_tflops = r["kept_flops"] / (r["ms_attn"] * 1e-3) / 1e12
@@ -193,8 +204,10 @@ def main():
             "workload": w.name, "B": w.B, "H": w.H, "T": w.T, "Hs": w.Hs, "Ws": w.Ws, "d": w.d, "tokens": w.N,
             "blocks": w.nb, "mask": w.mode, "thr": w.thr if w.mode == "cdf" else None,
             "tau": w.tau if w.mode == "dyn" else None, "sta": list(w.sta), "parallelism": "none (1 GPU)",
+            "launch": "hip graph replay of the whole step" if r["graph"] else "eager",
         },
         "ms_per_layer": round(r["ms_step"], 4),
+        "ms_per_layer_eager": round(r["ms_eager"], 4),
         "ms_per_stage": {"reorder_pool_qkv": round(r["ms_reorder"], 4), "mask": round(r["ms_mask"], 4),
                          "attention": round(r["ms_attn"], 4)},
         "keep_fraction": round(r["keep_fraction"], 5),
@@ -211,7 +224,7 @@ def main():
         },
     }
     if args.secondary:
-        s = measure(args.secondary, args.steps, args.warmup)
+        s = measure(args.secondary, args.steps, args.warmup, use_graph=args.graph)
         out["secondary"] = {
             "workload": s["w"].name, "tokens": s["w"].N, "ms_per_layer": round(s["ms_step"], 4),
             "effective_tflops": round(s["dense_flops"] / (s["ms_step"] * 1e-3) / 1e12, 3),

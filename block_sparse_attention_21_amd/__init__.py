@@ -299,6 +299,22 @@ class NablaAttention:
         self.attend()
         return self.out
 
+    def capture(self, q, k, v):
+        """Record one whole step on these input tensors into a HIP graph (torch.cuda.CUDAGraph).
+
+        graph.replay() then reruns reorder, mask and attention on whatever q, k, v hold, without
+        per-kernel launch overhead. The path allocates nothing and issues no memsets, so it is
+        capturable; the inputs and every buffer of this object must stay alive and in place."""
+        side = torch.cuda.Stream(device=self.out.device)
+        side.wait_stream(torch.cuda.current_stream(self.out.device))
+        with torch.cuda.stream(side):
+            self(q, k, v)  # warm-up outside the graph
+        torch.cuda.current_stream(self.out.device).wait_stream(side)
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph):
+            self(q, k, v)
+        return graph
+
 
 def dense_flops(geom: Geometry) -> float:
     """4*B*H*N^2*d: the matrix-product FLOPs of full attention over the same tokens."""
