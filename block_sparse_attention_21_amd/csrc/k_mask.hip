@@ -18,7 +18,8 @@
 //            ~j (P descending, then j ascending) and finds the last kept rank:
 //            the smallest key K with (mass of keys above K) < thr. Two
 //            algorithms give the same bits: a radix select over the keys with
-//            exact mass histograms (11-bit digits, usually 2-3 passes), or an
+//            exact mass histograms (8-bit digits below the row's common key
+//            prefix, one bucket per thread), or an
 //            LDS-resident bitonic sort followed by an exclusive prefix sum.
 //
 // The decisions are taken in float64 so that two blocks whose probabilities
@@ -152,7 +153,7 @@ __device__ __forceinline__ unsigned long long mass_fx(unsigned long long key) {
   return (unsigned long long)(p * 4611686018427387904.0);
 }
 
-constexpr int kDigitBits = 11;
+constexpr int kDigitBits = 8;  // one bucket per thread: cheap clears and scans per pass
 constexpr int kBuckets = 1 << kDigitBits;
 constexpr int kBucketsPerThread = kBuckets / kSelThreads;
 
@@ -168,7 +169,7 @@ struct RadixScratch {
 // Smallest key K among this row's keys such that the total mass of the keys above K
 // is < thr_fx: the last rank the CDF cut keeps. MSB-first radix select below the row's
 // common key prefix: each pass histograms (count, exact fixed-point mass) the next
-// 11-bit digit of the keys that match the prefix fixed so far and descends into the
+// 8-bit digit of the keys that match the prefix fixed so far and descends into the
 // lowest bucket whose top key is still kept. Stops when that bucket holds one key.
 template <int NPT>
 __device__ unsigned long long radix_last_kept(const unsigned long long* key, int t, int nb,
