@@ -43,6 +43,9 @@ def parse():
                     help="measured HBM bytes per attention launch (from rocprofv3 counters)")
     ap.add_argument("--graph", action="store_true",
                     help="replay the step captured in a HIP graph instead of launching it eagerly")
+    ap.add_argument("--report", action="store_true",
+                    help="instead of the JSON line, print a markdown report over every workload (and the "
+                         "dynamic-threshold sweep) with per-pass times, fractions and per-head keep")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="only run a plain device copy of MIB MiB (reference for the FETCH/WRITE_SIZE counters)")
     return ap.parse_args()
@@ -78,7 +81,7 @@ def measure(name, steps, warmup, use_graph=False):
     import block_sparse_attention_21_amd as A
     from gen import WORKLOADS, make_qkv
 
-    w = WORKLOADS[name]
+    w = WORKLOADS[name] if isinstance(name, str) else name
     geom = A.Geometry(w.B, w.H, w.T, w.Hs, w.Ws, w.d, w.P)
     prm = A.MaskParams(mode=w.mode, thr=w.thr, tau=w.tau, sta=tuple(w.sta))
     q, k, v = make_qkv(w, device="cuda")
@@ -161,6 +164,47 @@ def cpu_baseline(r, budget_s):
     }
 
 
+def report(args):
+    """Markdown report over every workload: per-pass times, dense-equivalent and actual TFLOP/s,
+    MFMA fraction (against the 2.5 PFLOP/s datasheet peak and against a large bf16 library GEMM
+    timed on the same board), HBM fractions of the reorder and mask passes, keep per head."""
+    import torch
+    from gen import WORKLOADS
+
+    n = 8192
+    a = torch.randn(n, n, device="cuda", dtype=torch.bfloat16)
+    b = torch.randn(n, n, device="cuda", dtype=torch.bfloat16)
+    for _ in range(20):
+        torch.matmul(a, b)
+    gemm = 2.0 * n ** 3 / (timed(lambda: torch.matmul(a, b), 20, torch.cuda.current_stream()) * 1e-3) / 1e12
+    del a, b
+    cases = [WORKLOADS["tiny"], WORKLOADS["480p"], WORKLOADS["720p"], WORKLOADS["480p-dyn"],
+             WORKLOADS["480p-dyn"].with_(tau=2.0), WORKLOADS["480p-dyn"].with_(tau=8.0), WORKLOADS["long"]]
+    print(f"bf16 GEMM reference (torch.matmul {n}^3): {gemm:,.0f} TFLOP/s\n")
+    print("| workload | mask | keep | reorder ms (TB/s) | mask ms (GB/s) | attention ms | layer ms | "
+          "dense-eq TFLOP/s (layer / attn) | actual TFLOP/s | of 2.5 PF | of GEMM ref | keep per head |")
+    print("|---|---|---|---|---|---|---|---|---|---|---|---|")
+    for w in cases:
+        r = measure(w, args.steps, args.warmup)
+        g = r["geom"]
+        counts = r["counts"].double()
+        per_head = (counts.sum(dim=-1) / (g.nb * g.nb)).flatten().cpu().tolist()
+        e = 2 if w.dtype == "bf16" else 4
+        pooled = g.B * g.H * g.nb * g.d * 8
+        mask_bytes = (2 * pooled + 2 * g.B * g.H * g.nb * g.nb * 8 + g.B * g.H * g.nb * (g.words + 1) * 4
+                      + r["kept"] * 4)
+        attn_tf = r["kept_flops"] / (r["ms_attn"] * 1e-3) / 1e12
+        mode = f"cdf {w.thr}" if w.mode == "cdf" else f"dyn tau={w.tau}"
+        heads = ", ".join(f"{x:.3f}" for x in per_head[:12]) + (" ..." if len(per_head) > 12 else "")
+        print(f"| {w.name} ({w.dtype}, {w.N} tok) | {mode} | {r['keep_fraction']:.4f} | "
+              f"{r['ms_reorder']:.4f} ({r['reorder_gbs'] / 1e3:.2f}) | {r['ms_mask']:.4f} "
+              f"({mask_bytes / (r['ms_mask'] * 1e-3) / 1e9:,.0f}) | {r['ms_attn']:.4f} | {r['ms_step']:.4f} | "
+              f"{r['dense_flops'] / (r['ms_step'] * 1e-3) / 1e12:,.1f} / "
+              f"{r['dense_flops'] / (r['ms_attn'] * 1e-3) / 1e12:,.1f} | {attn_tf:,.1f} | "
+              f"{attn_tf / MFMA_BF16_PEAK_TFLOPS:.3f} | {attn_tf / gemm:.3f} | {heads} |", flush=True)
+        del r
+
+
 def traffic_for(path, name):
     try:
         with open(path) as f:
@@ -180,6 +224,9 @@ def main():
         sys.exit(1)
     if args.copy_calibration:
         copy_calibration(args.copy_calibration)
+        return
+    if args.report:
+        report(args)
         return
     r = measure(args.workload, args.steps, args.warmup, use_graph=args.graph)
     w, geom = r["w"], r["geom"]
