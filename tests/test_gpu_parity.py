@@ -250,6 +250,17 @@ def test_workload_full_size(A, name):
           f"max|dO| {max_abs:.2e}, rel {rel:.2e}")
 
 
+def test_maximum_blocks_per_row(A):
+    """The largest supported row: nb = 4096 key blocks (16 frames of 128 x 128 tokens, one head,
+    d = 64), the limit of the LDS-resident mask row and of the attention's 12-bit schedule."""
+    w, geom, og, prm, q, k, v, run = _workload(A, "480p", H=1, T=16, Hs=128, Ws=128, d=64)
+    assert geom.nb == 4096
+    mres, rep = _check_workload_mask(A, w, og, prm, q, k, run)
+    max_abs, rel = _check_workload_attention(w, og, q, k, v, run, n_heads=1)
+    print(f"max-nb: keep {rep.kept / rep.total:.4f}, band diffs {rep.exempt_diff}, "
+          f"max|dO| {max_abs:.2e}, rel {rel:.2e}")
+
+
 @pytest.mark.parametrize("tau", [2.0, 8.0])
 def test_dyn_tau_sweep_masks(A, tau):
     w, geom, og, prm, q, k, v, run = _workload(A, "480p-dyn", tau=tau)
