@@ -325,6 +325,40 @@ def masked_attention_head(Qr, Kr, Vr, block_mask, g: Geom, scale: float,
     return O, lse
 
 
+def masked_attention_backward_head(Qr, Kr, Vr, dOr, block_mask, g: Geom, scale: float, chunk: int = 256):
+    """Gradients of the block-sparse attention of one head (fractal order), float64.
+
+    With S = scale * Q K^T restricted to the allowed blocks, P = row softmax of S (zero
+    outside the allowed blocks, and zero rows where nothing is allowed), O = P V and the
+    incoming gradient dO, the chain rule gives
+        dV = P^T dO,   dP = dO V^T,   D_i = sum_j P_ij dP_ij = <dO_i, O_i>,
+        dS = P * (dP - D),   dQ = scale * dS K,   dK = scale * dS^T Q.
+    Returns (dQ, dK, dV), each [N, d]. Rows are processed in chunks of `chunk` queries.
+    """
+    Qr, Kr, Vr, dOr = (np.asarray(x, np.float64) for x in (Qr, Kr, Vr, dOr))
+    key_block = np.arange(g.N) // g.bs
+    dQ = np.zeros_like(Qr)
+    dK = np.zeros_like(Kr)
+    dV = np.zeros_like(Vr)
+    for s in range(0, g.N, chunk):
+        r = np.arange(s, min(s + chunk, g.N))
+        allowed = block_mask[(r // g.bs)[:, None], key_block[None, :]]
+        sc = np.where(allowed, scale * (Qr[r] @ Kr.T), -np.inf)
+        mx = sc.max(axis=1)
+        live = np.isfinite(mx)
+        P = np.zeros_like(sc)
+        e = np.exp(sc[live] - mx[live, None])
+        P[live] = e / e.sum(axis=1, keepdims=True)
+        O = P @ Vr
+        dP = dOr[r] @ Vr.T
+        D = np.sum(dOr[r] * O, axis=1)
+        dS = P * (dP - D[:, None])
+        dQ[r] = scale * (dS @ Kr)
+        dK += scale * (dS.T @ Qr[r])
+        dV += P.T @ dOr[r]
+    return dQ, dK, dV
+
+
 @dataclasses.dataclass
 class NablaResult:
     O: np.ndarray  # [B,H,N,d] original order

@@ -336,6 +336,64 @@ def test_sta_counts_closed_form():
     assert (sta == sta.T).all() and sta.diagonal().all()
 
 
+# ---------------------------------------------------------------- backward (gradients)
+def _bwd_case(seed=0):
+    g = R.Geom(1, 1, 2, 16, 16, 8, 8)
+    rng = np.random.default_rng(seed)
+    Q, K, V, G = (rng.standard_normal((g.N, g.d)) for _ in range(4))
+    M = rng.random((g.nb, g.nb)) < 0.5
+    M[0] = False  # an empty row
+    M[1] = True   # a full row
+    return g, Q, K, V, G, M, 1.0 / math.sqrt(g.d)
+
+
+def test_p10_backward_finite_differences():
+    """Central differences of L = sum(O * G) match the closed-form gradients (dO = G)."""
+    g, Q, K, V, G, M, sc = _bwd_case()
+    dQ, dK, dV = R.masked_attention_backward_head(Q, K, V, G, M, g, sc)
+    rng = np.random.default_rng(1)
+
+    def loss(Qx, Kx, Vx):
+        O, _ = _ORIG['masked_attention_head'](Qx, Kx, Vx, M, g, sc)
+        return float(np.sum(O * G))
+
+    h = 1e-6
+    for which, grad in ((0, dQ), (1, dK), (2, dV)):
+        for _ in range(8):
+            i, c = int(rng.integers(g.N)), int(rng.integers(g.d))
+            args_p, args_m = [Q.copy(), K.copy(), V.copy()], [Q.copy(), K.copy(), V.copy()]
+            args_p[which][i, c] += h
+            args_m[which][i, c] -= h
+            fd = (loss(*args_p) - loss(*args_m)) / (2 * h)
+            assert abs(fd - grad[i, c]) < 1e-6 * max(1.0, abs(fd)), (which, i, c, fd, grad[i, c])
+
+
+def test_p11_backward_full_mask_matches_autograd():
+    """With every block allowed the gradients are those of dense softmax attention (torch autograd, float64)."""
+    g, Q, K, V, G, _, sc = _bwd_case(2)
+    M = np.ones((g.nb, g.nb), dtype=bool)
+    dQ, dK, dV = R.masked_attention_backward_head(Q, K, V, G, M, g, sc)
+    q, k, v = (torch.tensor(x, requires_grad=True) for x in (Q, K, V))
+    o = torch.softmax(sc * q @ k.T, dim=-1) @ v
+    (o * torch.tensor(G)).sum().backward()
+    np.testing.assert_allclose(dQ, q.grad.numpy(), atol=1e-12, rtol=1e-10)
+    np.testing.assert_allclose(dK, k.grad.numpy(), atol=1e-12, rtol=1e-10)
+    np.testing.assert_allclose(dV, v.grad.numpy(), atol=1e-12, rtol=1e-10)
+
+
+def test_p12_backward_invariants():
+    """Sum over keys of dK is zero (each row of dS sums to zero); sum over keys of dV equals the
+    sum of dO over rows that see any key (each live row of P sums to one); rows with nothing
+    allowed get dQ = 0."""
+    g, Q, K, V, G, M, sc = _bwd_case(3)
+    dQ, dK, dV = R.masked_attention_backward_head(Q, K, V, G, M, g, sc)
+    live = M.any(axis=1)[np.arange(g.N) // g.bs]
+    assert np.abs(dK.sum(axis=0)).max() < 1e-12
+    np.testing.assert_allclose(dV.sum(axis=0), G[live].sum(axis=0), atol=1e-12)
+    assert not live[:g.bs].any() and np.all(dQ[:g.bs] == 0)
+    assert np.abs(dQ[live]).max() > 0
+
+
 # ---------------------------------------------------------------- planted mistakes
 PINS = [
     test_p1_full_threshold_is_full_attention,
@@ -353,10 +411,14 @@ PINS = [
     test_golden_cdf_rows,
     test_pack_bits_layout,
     test_sta_counts_closed_form,
+    test_p10_backward_finite_differences,
+    test_p11_backward_full_mask_matches_autograd,
+    test_p12_backward_invariants,
 ]
 
 
-_ORIG = {n: getattr(R, n) for n in ("cdf_select_row", "sta_block_mask", "masked_attention_head", "reorder")}
+_ORIG = {n: getattr(R, n) for n in ("cdf_select_row", "sta_block_mask", "masked_attention_head", "reorder",
+                                    "masked_attention_backward_head")}
 
 
 def _m_sort_ascending(p):
@@ -434,6 +496,30 @@ def _m_inverse_as_forward(Xr, g):
     return _ORIG['reorder'](Xr, g)
 
 
+def _bwd_flawed(flaw):
+    """The backward of the oracle rewritten with one planted flaw."""
+    def f(Qr, Kr, Vr, dOr, block_mask, g, scale, chunk=256):
+        bm = block_mask.T if flaw == "mask transposed" else block_mask
+        key_block = np.arange(g.N) // g.bs
+        dQ, dK, dV = np.zeros_like(Qr), np.zeros_like(Kr), np.zeros_like(Vr)
+        r = np.arange(g.N)
+        allowed = bm[(r // g.bs)[:, None], key_block[None, :]]
+        sc = np.where(allowed, scale * (Qr @ Kr.T), -np.inf)
+        mx = sc.max(axis=1)
+        live = np.isfinite(mx)
+        P = np.zeros_like(sc)
+        e = np.exp(sc[live] - mx[live, None])
+        P[live] = e / e.sum(axis=1, keepdims=True)
+        dP = dOr @ Vr.T
+        D = np.sum(dOr * (P @ Vr), axis=1)
+        dS = P * dP if flaw == "no D" else P * (dP - D[:, None])
+        dQ = scale * (dS @ Kr)
+        dK = (1.0 if flaw == "dK unscaled" else scale) * (dS.T @ Qr)
+        dV = dS.T @ dOr if flaw == "dV from dS" else P.T @ dOr
+        return dQ, dK, dV
+    return f
+
+
 MUTATIONS = {
     "rank ascending": ("rank_order", _m_sort_ascending),
     "ties high index first": ("rank_order", _m_tie_high_first),
@@ -450,6 +536,10 @@ MUTATIONS = {
     "mask transposed in attention": ("masked_attention_head", _m_attn_transposed),
     "attention scale dropped": ("masked_attention_head", _m_attn_no_scale),
     "inverse reorder = forward": ("inverse_reorder", _m_inverse_as_forward),
+    "backward without D": ("masked_attention_backward_head", _bwd_flawed("no D")),
+    "backward mask transposed": ("masked_attention_backward_head", _bwd_flawed("mask transposed")),
+    "backward dK unscaled": ("masked_attention_backward_head", _bwd_flawed("dK unscaled")),
+    "backward dV from dS": ("masked_attention_backward_head", _bwd_flawed("dV from dS")),
 }
 
 
