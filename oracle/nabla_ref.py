@@ -325,7 +325,9 @@ def masked_attention_head(Qr, Kr, Vr, block_mask, g: Geom, scale: float,
     return O, lse
 
 
-def masked_attention_backward_head(Qr, Kr, Vr, dOr, block_mask, g: Geom, scale: float, chunk: int = 256):
+def masked_attention_backward_head(Qr, Kr, Vr, dOr, block_mask, g: Geom, scale: float,
+                                   rows: Optional[np.ndarray] = None, O: Optional[np.ndarray] = None,
+                                   chunk: int = 256):
     """Gradients of the block-sparse attention of one head (fractal order), float64.
 
     With S = scale * Q K^T restricted to the allowed blocks, P = row softmax of S (zero
@@ -333,15 +335,22 @@ def masked_attention_backward_head(Qr, Kr, Vr, dOr, block_mask, g: Geom, scale: 
     incoming gradient dO, the chain rule gives
         dV = P^T dO,   dP = dO V^T,   D_i = sum_j P_ij dP_ij = <dO_i, O_i>,
         dS = P * (dP - D),   dQ = scale * dS K,   dK = scale * dS^T Q.
-    Returns (dQ, dK, dV), each [N, d]. Rows are processed in chunks of `chunk` queries.
+    Returns (dQ, dK, dV): dQ [R, d] for the query rows `rows` (default: all N), dK and dV
+    [N, d] summed over those rows only. A query row contributes nothing to the keys of the
+    blocks its mask row drops, so dK / dV of a key block are complete once `rows` holds
+    every row of every query block that keeps it. Rows are processed in chunks of `chunk`.
+    `O` ([N, d], fractal order) is the forward output the backward is handed, as stored (for
+    instance rounded to bf16); D is then <dO_i, O_i> of that O. By default O is the exact
+    P V recomputed here.
     """
     Qr, Kr, Vr, dOr = (np.asarray(x, np.float64) for x in (Qr, Kr, Vr, dOr))
+    rows = np.arange(g.N) if rows is None else np.asarray(rows)
     key_block = np.arange(g.N) // g.bs
-    dQ = np.zeros_like(Qr)
+    dQ = np.zeros((len(rows), Qr.shape[-1]))
     dK = np.zeros_like(Kr)
     dV = np.zeros_like(Vr)
-    for s in range(0, g.N, chunk):
-        r = np.arange(s, min(s + chunk, g.N))
+    for s in range(0, len(rows), chunk):
+        r = rows[s:s + chunk]
         allowed = block_mask[(r // g.bs)[:, None], key_block[None, :]]
         sc = np.where(allowed, scale * (Qr[r] @ Kr.T), -np.inf)
         mx = sc.max(axis=1)
@@ -349,11 +358,11 @@ def masked_attention_backward_head(Qr, Kr, Vr, dOr, block_mask, g: Geom, scale: 
         P = np.zeros_like(sc)
         e = np.exp(sc[live] - mx[live, None])
         P[live] = e / e.sum(axis=1, keepdims=True)
-        O = P @ Vr
+        Orow = P @ Vr if O is None else np.asarray(O, np.float64)[r]
         dP = dOr[r] @ Vr.T
-        D = np.sum(dOr[r] * O, axis=1)
+        D = np.sum(dOr[r] * Orow, axis=1)
         dS = P * (dP - D[:, None])
-        dQ[r] = scale * (dS @ Kr)
+        dQ[s:s + len(r)] = scale * (dS @ Kr)
         dK += scale * (dS.T @ Qr[r])
         dV += P.T @ dOr[r]
     return dQ, dK, dV

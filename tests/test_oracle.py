@@ -394,6 +394,48 @@ def test_p12_backward_invariants():
     assert np.abs(dQ[live]).max() > 0
 
 
+def test_p13_backward_row_subsets():
+    """Restricted to a set of query rows, dQ equals the full result on those rows, and dK / dV
+    equal it on every key block whose column (the query blocks keeping it) lies inside the set."""
+    g, Q, K, V, G, M, sc = _bwd_case(4)
+    dQ, dK, dV = R.masked_attention_backward_head(Q, K, V, G, M, g, sc)
+    j = 2
+    qblocks = np.nonzero(M[:, j])[0]
+    rows = np.concatenate([np.arange(b * g.bs, (b + 1) * g.bs) for b in qblocks])
+    sQ, sK, sV = R.masked_attention_backward_head(Q, K, V, G, M, g, sc, rows=rows, chunk=48)
+    np.testing.assert_allclose(sQ, dQ[rows], atol=1e-13)
+    kr = slice(j * g.bs, (j + 1) * g.bs)
+    np.testing.assert_allclose(sK[kr], dK[kr], atol=1e-13)
+    np.testing.assert_allclose(sV[kr], dV[kr], atol=1e-13)
+    # Leaving out one query block that keeps j changes block j's gradients.
+    tQ, tK, tV = R.masked_attention_backward_head(Q, K, V, G, M, g, sc, rows=rows[g.bs:])
+    assert np.abs(tV[kr] - dV[kr]).max() > 1e-6
+
+
+def test_p14_backward_given_output():
+    """Handing the backward the exact O changes nothing; a perturbed O' moves only D:
+    dV is unchanged and dQ changes by -scale * <dO_i, O'_i - O_i> (P K)_i."""
+    g, Q, K, V, G, M, sc = _bwd_case(5)
+    dQ, dK, dV = R.masked_attention_backward_head(Q, K, V, G, M, g, sc)
+    O, _ = _ORIG['masked_attention_head'](Q, K, V, M, g, sc)
+    eQ, eK, eV = R.masked_attention_backward_head(Q, K, V, G, M, g, sc, O=O)
+    for a, b in ((eQ, dQ), (eK, dK), (eV, dV)):
+        np.testing.assert_allclose(a, b, atol=1e-13)
+    delta = 1e-3 * np.random.default_rng(6).standard_normal(O.shape)
+    pQ, pK, pV = R.masked_attention_backward_head(Q, K, V, G, M, g, sc, O=O + delta)
+    np.testing.assert_allclose(pV, dV, atol=1e-13)
+    key_block = np.arange(g.N) // g.bs
+    allowed = M[key_block[:, None], key_block[None, :]]
+    S = np.where(allowed, sc * Q @ K.T, -np.inf)
+    P = np.zeros_like(S)
+    live = allowed.any(axis=1)
+    E = np.exp(S[live] - S[live].max(axis=1, keepdims=True))
+    P[live] = E / E.sum(axis=1, keepdims=True)
+    dD = np.sum(G * delta, axis=1)
+    np.testing.assert_allclose(pQ - dQ, -sc * dD[:, None] * (P @ K), atol=1e-12)
+    assert np.abs(pK - dK).max() > 1e-6
+
+
 # ---------------------------------------------------------------- planted mistakes
 PINS = [
     test_p1_full_threshold_is_full_attention,
@@ -414,6 +456,8 @@ PINS = [
     test_p10_backward_finite_differences,
     test_p11_backward_full_mask_matches_autograd,
     test_p12_backward_invariants,
+    test_p13_backward_row_subsets,
+    test_p14_backward_given_output,
 ]
 
 
@@ -498,24 +542,25 @@ def _m_inverse_as_forward(Xr, g):
 
 def _bwd_flawed(flaw):
     """The backward of the oracle rewritten with one planted flaw."""
-    def f(Qr, Kr, Vr, dOr, block_mask, g, scale, chunk=256):
+    def f(Qr, Kr, Vr, dOr, block_mask, g, scale, rows=None, O=None, chunk=256):
         bm = block_mask.T if flaw == "mask transposed" else block_mask
         key_block = np.arange(g.N) // g.bs
-        dQ, dK, dV = np.zeros_like(Qr), np.zeros_like(Kr), np.zeros_like(Vr)
-        r = np.arange(g.N)
+        r = np.arange(g.N) if rows is None else np.asarray(rows)
+        dK, dV = np.zeros_like(Kr), np.zeros_like(Vr)
         allowed = bm[(r // g.bs)[:, None], key_block[None, :]]
-        sc = np.where(allowed, scale * (Qr @ Kr.T), -np.inf)
+        sc = np.where(allowed, scale * (Qr[r] @ Kr.T), -np.inf)
         mx = sc.max(axis=1)
         live = np.isfinite(mx)
         P = np.zeros_like(sc)
         e = np.exp(sc[live] - mx[live, None])
         P[live] = e / e.sum(axis=1, keepdims=True)
-        dP = dOr @ Vr.T
-        D = np.sum(dOr * (P @ Vr), axis=1)
+        dP = dOr[r] @ Vr.T
+        Orow = P @ Vr if (O is None or flaw == "ignores O") else O[r]
+        D = np.sum(dOr[r] * Orow, axis=1)
         dS = P * dP if flaw == "no D" else P * (dP - D[:, None])
         dQ = scale * (dS @ Kr)
-        dK = (1.0 if flaw == "dK unscaled" else scale) * (dS.T @ Qr)
-        dV = dS.T @ dOr if flaw == "dV from dS" else P.T @ dOr
+        dK = (1.0 if flaw == "dK unscaled" else scale) * (dS.T @ Qr[r])
+        dV = dS.T @ dOr[r] if flaw == "dV from dS" else P.T @ dOr[r]
         return dQ, dK, dV
     return f
 
@@ -540,6 +585,7 @@ MUTATIONS = {
     "backward mask transposed": ("masked_attention_backward_head", _bwd_flawed("mask transposed")),
     "backward dK unscaled": ("masked_attention_backward_head", _bwd_flawed("dK unscaled")),
     "backward dV from dS": ("masked_attention_backward_head", _bwd_flawed("dV from dS")),
+    "backward ignores the given O": ("masked_attention_backward_head", _bwd_flawed("ignores O")),
 }
 
 
