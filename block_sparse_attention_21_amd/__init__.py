@@ -54,6 +54,8 @@ def _load():
         "abla_build_mask": (i32, [G, ctypes.POINTER(_MaskParams), vp, vp, vp, vp, vp, vp, sz, vp]),
         "abla_sparse_attn_workspace_bytes": (sz, [G]),
         "abla_sparse_attn_fwd": (i32, [G, i32, f32, vp, vp, vp, vp, vp, vp, i32, vp, vp, sz, vp]),
+        "abla_sparse_attn_bwd_workspace_bytes": (sz, [G]),
+        "abla_sparse_attn_bwd": (i32, [G, i32, f32] + [vp] * 13 + [sz, vp]),
         "abla_status_str": (ctypes.c_char_p, [i32]),
         "abla_version": (i32, []),
     }
@@ -65,7 +67,8 @@ def _load():
 
 _lib = _load()
 EXPORTED = ("abla_reorder", "abla_build_mask_workspace_bytes", "abla_build_mask", "abla_sparse_attn_workspace_bytes",
-            "abla_sparse_attn_fwd", "abla_status_str", "abla_version")
+            "abla_sparse_attn_fwd", "abla_sparse_attn_bwd_workspace_bytes", "abla_sparse_attn_bwd", "abla_status_str",
+            "abla_version")
 
 
 def status_str(code: int) -> str:
@@ -252,6 +255,40 @@ def sparse_attn_fwd(q_r: torch.Tensor, k_r: torch.Tensor, v_rt: torch.Tensor, co
     return (out, lse) if lse is not None else out
 
 
+def sparse_attn_bwd_workspace_bytes(geom: Geometry) -> int:
+    g = geom.c()
+    return _lib.abla_sparse_attn_bwd_workspace_bytes(ctypes.byref(g))
+
+
+def sparse_attn_bwd(q, k, v, o, dout, lse, words, counts, lists, geom: Geometry, *, scale: float = 0.0,
+                    dq=None, dk=None, dv=None, workspace=None):
+    """abla_sparse_attn_bwd: gradients (dq, dk, dv) of the block-sparse attention, all tensors
+    [B,H,N,d] bf16 in the original token order; lse [B,H,N] float32 in fractal order from the
+    forward; words / counts / lists the mask of build_mask."""
+    dev = _device(q)
+    tok = (geom.B, geom.H, geom.N, geom.d)
+    for t, n in ((q, "q"), (k, "k"), (v, "v"), (o, "o"), (dout, "dout")):
+        _need(t, n, tok, torch.bfloat16, dev)
+    _need(lse, "lse", (geom.B, geom.H, geom.N), torch.float32, dev)
+    _need(words, "words", (geom.B, geom.H, geom.nb, geom.words), torch.int32, dev)
+    _need(counts, "counts", (geom.B, geom.H, geom.nb), torch.int32, dev)
+    _need(lists, "lists", (geom.B, geom.H, geom.nb, geom.nb), torch.int32, dev)
+    dq = torch.empty(tok, dtype=torch.bfloat16, device=dev) if dq is None else dq
+    dk = torch.empty(tok, dtype=torch.bfloat16, device=dev) if dk is None else dk
+    dv = torch.empty(tok, dtype=torch.bfloat16, device=dev) if dv is None else dv
+    for t, n in ((dq, "dq"), (dk, "dk"), (dv, "dv")):
+        _need(t, n, tok, torch.bfloat16, dev)
+    nbytes = sparse_attn_bwd_workspace_bytes(geom)
+    if workspace is None:
+        workspace = torch.empty(max(nbytes, 1), dtype=torch.uint8, device=dev)
+    g = geom.c()
+    _check(_lib.abla_sparse_attn_bwd(ctypes.byref(g), _DT[torch.bfloat16], float(scale), _ptr(q), _ptr(k), _ptr(v),
+                                     _ptr(o), _ptr(dout), _ptr(lse), _ptr(words), _ptr(counts), _ptr(lists),
+                                     _ptr(dq), _ptr(dk), _ptr(dv), _ptr(workspace), workspace.numel(), _stream(q)),
+           "abla_sparse_attn_bwd")
+    return dq, dk, dv
+
+
 class NablaAttention:
     """The whole forward path for one geometry, with every buffer allocated once.
 
@@ -298,6 +335,14 @@ class NablaAttention:
         self.mask()
         self.attend()
         return self.out
+
+    def backward(self, q, k, v, dout, workspace=None):
+        """Gradients (dq, dk, dv) of the last __call__(q, k, v) for the incoming gradient dout
+        (all [B,H,N,d] bf16, original order). Needs want_lse=True (the forward's log-sum-exp)."""
+        if self.lse is None:
+            raise ValueError("backward needs the forward's log-sum-exp: construct with want_lse=True")
+        return sparse_attn_bwd(q, k, v, self.out, dout, self.lse, self.words, self.counts, self.lists, self.geom,
+                               scale=self.scale, workspace=workspace)
 
     def capture(self, q, k, v):
         """Record one whole step on these input tensors into a HIP graph (torch.cuda.CUDAGraph).

@@ -15,7 +15,7 @@ INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(PKG, "libabla.so")
 OBJ = os.path.join(PKG, "_build")
 
-SOURCES = ["abla_api.hip", "k_reorder.hip", "k_mask.hip", "k_attn.hip"]
+SOURCES = ["abla_api.hip", "k_reorder.hip", "k_mask.hip", "k_attn.hip", "k_attn_bwd.hip"]
 
 FLAGS = [
     "--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC",

@@ -9,7 +9,7 @@ using namespace abla;
 
 namespace {
 
-constexpr int kVersion = 100;  // 0.1.0
+constexpr int kVersion = 200;  // 0.2.0: adds the backward entry points
 
 abla_status check_geom(const abla_geom* g) {
   if (!g) return ABLA_ERR_INVALID;
@@ -22,13 +22,20 @@ abla_status check_geom(const abla_geom* g) {
     return ABLA_ERR_UNSUPPORTED;
   const long double nb = (long double)g->T * (g->Hs / g->P) * (g->Ws / g->P);
   if ((long double)g->B * g->H * nb > (long double)INT_MAX) return ABLA_ERR_UNSUPPORTED;  // grid size
+  if ((long double)g->T * g->Hs * g->Ws > (long double)INT_MAX) return ABLA_ERR_UNSUPPORTED;  // tokens per head
   if ((long double)g->B * g->H * g->T * g->Hs * g->Ws * g->d > 9.0e18L) return ABLA_ERR_UNSUPPORTED;
   return ABLA_OK;
 }
 
 bool valid_dtype(int32_t dt) { return dt == ABLA_F32 || dt == ABLA_BF16; }
 
-int64_t nb_of(const abla_geom* g) { return g->T * (g->Hs / g->P) * (g->Ws / g->P); }
+int64_t nb_of(const abla_geom* g) { return (int64_t)g->T * (g->Hs / g->P) * (g->Ws / g->P); }
+
+// B*H, and the element count of one [B,H,N,d] tensor, in 64-bit arithmetic.
+size_t bh_of(const abla_geom* g) { return (size_t)g->B * (size_t)g->H; }
+size_t tok_elems(const abla_geom* g) {
+  return bh_of(g) * (size_t)g->T * (size_t)g->Hs * (size_t)g->Ws * (size_t)g->d;
+}
 
 bool window_ok(int32_t t, int32_t h, int32_t w) {
   if (t == 0 && h == 0 && w == 0) return true;
@@ -46,6 +53,26 @@ bool overlaps(const void* a, size_t na, const void* b, size_t nb) {
 }
 
 abla_status from_hip(hipError_t e) { return e == hipSuccess ? ABLA_OK : ABLA_ERR_HIP; }
+
+size_t align256(size_t n) { return (n + 255) & ~(size_t)255; }
+
+// Backward scratch: seven fractal copies of a [B,H,N,d] bf16 tensor, D and L2 ([B,H,N]
+// float32), column counts [B,H,nb] and column lists [B,H,nb,nb] (int32), each 256-aligned.
+size_t bwd_parts(const abla_geom* g, BwdWorkspace* ws, char* base) {
+  const size_t bh = bh_of(g), nb = (size_t)nb_of(g);
+  const size_t n = (size_t)g->T * (size_t)g->Hs * (size_t)g->Ws;
+  const size_t x = align256(bh * n * (size_t)g->d * 2), rows = align256(bh * n * 4);
+  const size_t cc = align256(bh * nb * 4), cl = align256(bh * nb * nb * 4);
+  if (ws) {
+    uint16_t** t[7] = {&ws->q_r, &ws->q_rt, &ws->k_r, &ws->k_rt, &ws->v_r, &ws->do_r, &ws->do_rt};
+    for (int i = 0; i < 7; ++i) *t[i] = reinterpret_cast<uint16_t*>(base + i * x);
+    ws->D = reinterpret_cast<float*>(base + 7 * x);
+    ws->L2 = reinterpret_cast<float*>(base + 7 * x + rows);
+    ws->col_counts = reinterpret_cast<int32_t*>(base + 7 * x + 2 * rows);
+    ws->col_lists = reinterpret_cast<int32_t*>(base + 7 * x + 2 * rows + cc);
+  }
+  return 7 * x + 2 * rows + cc + cl;
+}
 
 }  // namespace
 
@@ -72,10 +99,10 @@ abla_status abla_reorder(const abla_geom* g, int32_t dtype, int32_t inverse, int
   if (layout != ABLA_LAYOUT_TOKENS && layout != ABLA_LAYOUT_BLOCK_T) return ABLA_ERR_INVALID;
   if (inverse != 0 && inverse != 1) return ABLA_ERR_INVALID;
   if (inverse && (layout != ABLA_LAYOUT_TOKENS || pooled)) return ABLA_ERR_INVALID;
-  const size_t bytes = (size_t)(g->B * g->H * g->T * g->Hs * g->Ws * g->d) * elem_bytes(dtype);
+  const size_t bytes = tok_elems(g) * elem_bytes(dtype);
   if (overlaps(x, bytes, y, bytes)) return ABLA_ERR_INVALID;
   if (pooled) {
-    const size_t pbytes = (size_t)(g->B * g->H * nb_of(g) * g->d) * sizeof(double);
+    const size_t pbytes = bh_of(g) * (size_t)nb_of(g) * (size_t)g->d * sizeof(double);
     if (overlaps(pooled, pbytes, x, bytes) || overlaps(pooled, pbytes, y, bytes)) return ABLA_ERR_INVALID;
   }
   return from_hip(launch_reorder(make_kgeom(*g), dtype, inverse, layout, x, y, pooled, (hipStream_t)stream));
@@ -84,7 +111,7 @@ abla_status abla_reorder(const abla_geom* g, int32_t dtype, int32_t inverse, int
 size_t abla_build_mask_workspace_bytes(const abla_geom* g) {
   if (check_geom(g) != ABLA_OK) return 0;
   const int64_t nb = nb_of(g);
-  return (size_t)(g->B * g->H * nb * nb) * sizeof(double);
+  return bh_of(g) * (size_t)nb * (size_t)nb * sizeof(double);
 }
 
 abla_status abla_build_mask(const abla_geom* g, const abla_mask_params* p, const double* qbar, const double* kbar,
@@ -107,7 +134,7 @@ abla_status abla_build_mask(const abla_geom* g, const abla_mask_params* p, const
 size_t abla_sparse_attn_workspace_bytes(const abla_geom* g) {
   if (check_geom(g) != ABLA_OK) return 0;
   // Visiting order (at most nb ints per (b, h)), then one int of walk mode, padded to 256 bytes.
-  return (size_t)(g->B * g->H * nb_of(g)) * sizeof(int32_t) + 256;
+  return bh_of(g) * (size_t)nb_of(g) * sizeof(int32_t) + 256;
 }
 
 abla_status abla_sparse_attn_fwd(const abla_geom* g, int32_t dtype, float scale, const void* q_r,
@@ -119,7 +146,7 @@ abla_status abla_sparse_attn_fwd(const abla_geom* g, int32_t dtype, float scale,
   if (!valid_dtype(dtype) || !q_r || !k_r || !v_rt || !counts || !lists || !out) return ABLA_ERR_INVALID;
   if (isnan(scale) || scale < 0.f || isinf(scale)) return ABLA_ERR_INVALID;
   if (nb_of(g) > kMaxBlocks) return ABLA_ERR_UNSUPPORTED;
-  const size_t bytes = (size_t)(g->B * g->H * g->T * g->Hs * g->Ws * g->d) * elem_bytes(dtype);
+  const size_t bytes = tok_elems(g) * elem_bytes(dtype);
   if (overlaps(out, bytes, q_r, bytes) || overlaps(out, bytes, k_r, bytes) || overlaps(out, bytes, v_rt, bytes))
     return ABLA_ERR_INVALID;
   if (!workspace || workspace_bytes < abla_sparse_attn_workspace_bytes(g)) return ABLA_ERR_WORKSPACE;
@@ -127,6 +154,41 @@ abla_status abla_sparse_attn_fwd(const abla_geom* g, int32_t dtype, float scale,
   return from_hip(launch_sparse_attn(make_kgeom(*g), dtype, s, q_r, k_r, v_rt, counts, lists, out,
                                      out_original_order != 0, lse, static_cast<int32_t*>(workspace),
                                      (hipStream_t)stream));
+}
+
+size_t abla_sparse_attn_bwd_workspace_bytes(const abla_geom* g) {
+  if (check_geom(g) != ABLA_OK) return 0;
+  return bwd_parts(g, nullptr, nullptr);
+}
+
+abla_status abla_sparse_attn_bwd(const abla_geom* g, int32_t dtype, float scale, const void* q, const void* k,
+                                 const void* v, const void* o, const void* dout, const float* lse,
+                                 const uint32_t* mask_words, const int32_t* counts, const int32_t* lists,
+                                 void* dq, void* dk, void* dv, void* workspace, size_t workspace_bytes,
+                                 void* stream) {
+  abla_status st = check_geom(g);
+  if (st != ABLA_OK) return st;
+  if (!valid_dtype(dtype)) return ABLA_ERR_INVALID;
+  if (dtype != ABLA_BF16) return ABLA_ERR_UNSUPPORTED;
+  if (!q || !k || !v || !o || !dout || !lse || !mask_words || !counts || !lists || !dq || !dk || !dv)
+    return ABLA_ERR_INVALID;
+  if (isnan(scale) || scale < 0.f || isinf(scale)) return ABLA_ERR_INVALID;
+  if (nb_of(g) > kMaxBlocks) return ABLA_ERR_UNSUPPORTED;
+  const size_t bytes = tok_elems(g) * 2;
+  const void* ins[5] = {q, k, v, o, dout};
+  void* outs[3] = {dq, dk, dv};
+  for (int a = 0; a < 3; ++a) {
+    for (int b = 0; b < 5; ++b)
+      if (overlaps(outs[a], bytes, ins[b], bytes)) return ABLA_ERR_INVALID;
+    for (int b = a + 1; b < 3; ++b)
+      if (overlaps(outs[a], bytes, outs[b], bytes)) return ABLA_ERR_INVALID;
+  }
+  if (!workspace || workspace_bytes < abla_sparse_attn_bwd_workspace_bytes(g)) return ABLA_ERR_WORKSPACE;
+  BwdWorkspace ws;
+  bwd_parts(g, &ws, static_cast<char*>(workspace));
+  const float s = scale > 0.f ? scale : 1.0f / sqrtf((float)g->d);
+  return from_hip(launch_sparse_attn_bwd(make_kgeom(*g), s, q, k, v, o, dout, lse, mask_words, counts, lists, dq,
+                                         dk, dv, ws, (hipStream_t)stream));
 }
 
 }  // extern "C"

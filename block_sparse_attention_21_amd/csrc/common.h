@@ -56,4 +56,16 @@ hipError_t launch_sparse_attn(const KGeom& g, int dtype, float scale, const void
                               const void* vt, const int32_t* counts, const int32_t* lists, void* out,
                               int out_original_order, float* lse, int32_t* row_order, hipStream_t s);
 
+// Device scratch of the backward pass, carved out of the caller's workspace
+// (see abla_sparse_attn_bwd_workspace_bytes).
+struct BwdWorkspace {
+  uint16_t *q_r, *q_rt, *k_r, *k_rt, *v_r, *do_r, *do_rt;  // fractal copies, [B,H,N,d] each
+  float *D, *L2;                                              // [B,H,N] fractal order
+  int32_t *col_counts, *col_lists;                            // [B,H,nb], [B,H,nb,nb]
+};
+hipError_t launch_sparse_attn_bwd(const KGeom& g, float scale, const void* q, const void* k, const void* v,
+                                  const void* o, const void* dout, const float* lse, const uint32_t* words,
+                                  const int32_t* counts, const int32_t* lists, void* dq, void* dk, void* dv,
+                                  const BwdWorkspace& ws, hipStream_t s);
+
 }  // namespace abla

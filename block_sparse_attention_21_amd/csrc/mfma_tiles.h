@@ -1,0 +1,112 @@
+// Shared device helpers of the attention kernels (forward and backward): LDS tile
+// geometry and swizzles for the gfx950 32x32x16 bf16 MFMA operands, the key-row
+// permutation that makes a score tile's accumulators reusable as the next MFMA's
+// operand, global->LDS tile loads and wait/barrier primitives.
+#pragma once
+
+#include "common.h"
+
+namespace abla {
+namespace {
+
+typedef __attribute__((address_space(3))) void* lds_ptr_t;
+
+template <int D>
+struct Tile {
+  static constexpr int KBYTES = kBlock * D * 2;   // K tile, token-major
+  static constexpr int VBYTES = D * kBlock * 2;   // V^T tile, channel-major
+  static constexpr int BYTES = KBYTES + VBYTES;
+  static constexpr int KCH = D / 8;               // 16-byte chunks per K row
+  static constexpr int KUNITS = KBYTES / 16;
+  static constexpr int VUNITS = VBYTES / 16;
+  static constexpr int KLOADS = KUNITS / 256;     // per thread per tile
+  static constexpr int VLOADS = VUNITS / 256;
+};
+
+// 16-byte chunk swizzles (bank-conflict-free MFMA operand reads).
+template <int D>
+__device__ __forceinline__ int k_swz(int r) {
+  return D == 128 ? (r & 15) : ((r >> 1) & 7);
+}
+__device__ __forceinline__ int v_swz(int d) { return (d >> 1) & 7; }
+
+// LDS row r of the K tile holds key kperm(r): rows 4-7 and 8-11 of every 16 are swapped,
+// which makes each lane's S^T registers cover 8 consecutive keys (see the file header).
+__device__ __forceinline__ int kperm(int r) {
+  const int m = r & 15;
+  const int s = (m >= 4 && m < 8) ? 4 : ((m >= 8 && m < 12) ? -4 : 0);
+  return r + s;
+}
+
+__device__ __forceinline__ float exp2_fast(float x) { return __builtin_amdgcn_exp2f(x); }
+
+__device__ __forceinline__ float swap_max(float v) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+
+__device__ __forceinline__ float swap_sum(float v) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
+// Read-only metadata (counts, lists, order) through the constant address space so that
+// wave-uniform reads become scalar loads: their waits then do not wait for the
+// outstanding K/V tile loads.
+typedef const __attribute__((address_space(4))) int32_t* cint_ptr;
+__device__ __forceinline__ int ld_const(const int32_t* p, long long i) {
+  return ((cint_ptr)p)[i];
+}
+
+// Waits and barriers written with builtins the compiler's wait-count pass understands
+// (gfx9 s_waitcnt encoding: vmcnt [3:0]+[15:14], expcnt [6:4], lgkmcnt [11:8]), and
+// without a release fence: a fence would also wait for the next tile's loads that are
+// meant to stay in flight. Empty asm statements keep memory accesses on their side.
+constexpr int waitcnt_vm(int n) { return (n & 15) | (7 << 4) | (15 << 8) | ((n >> 4) << 14); }
+constexpr int kWaitLgkm0 = 15 | (7 << 4) | (0 << 8) | (3 << 14);
+
+__device__ __forceinline__ void wait_vm_lgkm_barrier() {
+  __builtin_amdgcn_s_waitcnt(waitcnt_vm(0) & kWaitLgkm0);
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+}
+
+// Buffer resource (gfx9 V#) over `bytes` bytes at `base`: raw addressing, no stride.
+// Tile loads go through buffer_load ... lds rather than global_load_lds: the compiler's
+// wait-count pass tracks the buffer form on the vector-memory counter only, so the LDS
+// operand reads of the current tile keep partial lgkmcnt waits while the next tile's
+// loads are in flight.
+typedef int32_t i32x4_t __attribute__((ext_vector_type(4)));
+__device__ void raw_buffer_load_lds(i32x4_t rsrc, __attribute__((address_space(3))) uint32_t* lds, int size,
+                                    int voffset, int soffset, int offset, int aux)
+    __asm("llvm.amdgcn.raw.buffer.load.lds");
+
+__device__ __forceinline__ i32x4_t make_rsrc(const void* base, uint32_t bytes) {
+  const uint64_t p = reinterpret_cast<uint64_t>(base);
+  i32x4_t r;
+  r.x = __builtin_amdgcn_readfirstlane((int)(uint32_t)p);
+  r.y = __builtin_amdgcn_readfirstlane((int)(uint32_t)(p >> 32));  // stride 0
+  r.z = (int)bytes;                                                 // num_records (bytes)
+  r.w = 0x00020000;                                                 // 32-bit data format
+  return r;
+}
+
+// Issue this thread's 16-byte global->LDS loads of one K tile (or one V^T tile) that
+// starts `tile` bytes into the resource. Load `it` of thread t fills LDS unit it*256 + t
+// of the slot; its source is `off` + it*4096 bytes into the tile (for both tile kinds and
+// both head dims the swizzled source of unit it*256 + t is 4096 bytes past that of unit
+// t: 16 K rows of 256 bytes, 32 K rows of 128 bytes, 32 V^T rows of 128 bytes, all with
+// a swizzle that repeats every 16 or 32 rows). `w` is the wave index (uniform).
+template <int BYTES>
+__device__ __forceinline__ void issue_rows(char* dst_slot, int w, i32x4_t rsrc, uint32_t tile, uint32_t off) {
+  constexpr int LOADS = BYTES / 16 / 256;
+  char* dst = dst_slot + w * 64 * 16;
+#pragma unroll
+  for (int it = 0; it < LOADS; ++it)
+    raw_buffer_load_lds(rsrc, (__attribute__((address_space(3))) uint32_t*)(dst + it * 256 * 16), 16, (int)off,
+                        (int)(tile + it * 4096), 0, 0);
+}
+
+}  // namespace
+}  // namespace abla

@@ -202,3 +202,10 @@ def make_random_qkv(B, H, T, Hs, Ws, d, dtype="bf16", seed=0, device="cpu", scal
     g.manual_seed(_seed_for(seed, 99, 99, 99))
     N = T * Hs * Ws
     return tuple((scale * torch.randn((B, H, N, d), generator=g, device=device)).to(dt) for _ in range(3))
+
+
+def make_dout(B, H, N, d, seed=0, device="cpu"):
+    """Incoming gradient dO for the backward: i.i.d. standard normal [B, H, N, d], bf16."""
+    g = torch.Generator(device=device)
+    g.manual_seed(_seed_for(seed, 77, 77, 77))
+    return torch.randn((B, H, N, d), generator=g, device=device).to(torch.bfloat16)

@@ -11,6 +11,7 @@
  *   abla_build_mask       reduced attention over pooled blocks, per-row CDF cut
  *                         (or logit threshold), OR the sliding-tile window
  *   abla_sparse_attn_fwd  attention restricted to the kept 64 x 64 blocks
+ *   abla_sparse_attn_bwd  its gradients dQ, dK, dV through the same mask
  *
  * Conventions shared by all entry points
  * --------------------------------------
@@ -97,8 +98,8 @@ typedef struct {
  *   y receives the original order; `pooled` must be NULL.
  * dtype: element type of x and y. x and y must not overlap.
  * Errors: INVALID for null x/y, x == y, bad geometry, unknown dtype or layout,
- * inverse with BLOCK_T or with pooled; UNSUPPORTED for P*P != 64 or d not in
- * {64, 128}. */
+ * inverse with BLOCK_T or with pooled; UNSUPPORTED for P*P != 64, d not in
+ * {64, 128}, more than 2^31 - 1 tokens per head or B*H*nb above 2^31 - 1. */
 abla_status abla_reorder(const abla_geom* g, int32_t dtype, int32_t inverse, int32_t layout,
                          const void* x, void* y, double* pooled, void* stream);
 
@@ -167,6 +168,37 @@ abla_status abla_sparse_attn_fwd(const abla_geom* g, int32_t dtype, float scale,
                                  const int32_t* counts, const int32_t* lists,
                                  void* out, int32_t out_original_order, float* lse,
                                  void* workspace, size_t workspace_bytes, void* stream);
+
+/* Bytes of scratch abla_sparse_attn_bwd needs: seven fractal copies of one [B,H,N,d] bf16
+ * tensor, two [B,H,N] float32 rows, and the column counts [B,H,nb] and lists [B,H,nb,nb] int32,
+ * each rounded up to 256 bytes. */
+size_t abla_sparse_attn_bwd_workspace_bytes(const abla_geom* g);
+
+/* Gradients of the block-sparse attention forward (abla_sparse_attn_fwd with the same mask).
+ * Source: NABLA, Results -- the mask is used in training as well (forward and backward through
+ * the same block mask). With S = scale * Q K^T on the kept blocks, P its row softmax, O = P V:
+ *   dV = P^T dO,  dP = dO V^T,  D = rowsum(dO * O),  dS = P * (dP - D),
+ *   dQ = scale * dS K,  dK = scale * dS^T Q.
+ *
+ * q, k, v, o, dout: [B,H,N,d] bf16 in the ORIGINAL token order (o is the forward's output,
+ *   dout the incoming gradient).
+ * lse: [B,H,N] float32 in fractal order, as written by abla_sparse_attn_fwd for the same inputs
+ *   (natural log); P is recomputed from it.
+ * mask_words, counts, lists: the mask of abla_build_mask (words and lists must agree).
+ * dq, dk, dv: [B,H,N,d] bf16 outputs in the original order; no overlap with each other or the
+ *   inputs. Rows of dq whose block keeps nothing are 0; keys no block keeps get dk = dv = 0.
+ * scale: 0 means 1/sqrt(d); it must equal the forward's.
+ * Arithmetic: bf16 matrix-core products with float32 accumulation; P and dS are rounded to bf16
+ *   for the products, D is summed in float32, the outputs are rounded once.
+ * workspace: at least abla_sparse_attn_bwd_workspace_bytes(g) bytes.
+ * Errors: INVALID for null pointers, NaN/negative scale, unknown dtype, overlapping outputs;
+ * UNSUPPORTED for float32 inputs, nb > 4096 and the geometry limits of abla_reorder;
+ * WORKSPACE if the workspace is missing or too small. */
+abla_status abla_sparse_attn_bwd(const abla_geom* g, int32_t dtype, float scale, const void* q, const void* k,
+                                 const void* v, const void* o, const void* dout, const float* lse,
+                                 const uint32_t* mask_words, const int32_t* counts, const int32_t* lists,
+                                 void* dq, void* dk, void* dv, void* workspace, size_t workspace_bytes,
+                                 void* stream);
 
 /* Static, NUL-terminated description of a status code. */
 const char* abla_status_str(int32_t status);

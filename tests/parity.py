@@ -5,8 +5,13 @@ blocks whose decision sits within 1e-5 of the threshold (cumulative mass in CDF
 mode, logit edge in dynamic mode); STA blocks are never exempt.
 Attention rule: evaluated on the GPU's own mask (after it passed the mask
 check), bf16: max |dO| <= 2e-2 and ||dO||_2 / ||O||_2 <= 5e-3; float32: max |dO| <= 1e-4.
+Gradient rule (bf16 backward, on the GPU's mask, O and lse): per tensor,
+||dG||_2 / ||G||_2 <= 1e-2 and max |dG| <= 2e-2 * max |G|. The kernels round P and dS to
+bf16 for the products (relative error <= 2^-9 each) and the results to bf16 (another
+2^-9): about 2e-3 in relative L2 for sums of many terms, so 1e-2 leaves a 5x margin.
 """
 import dataclasses
+import math
 
 import numpy as np
 import torch
@@ -87,6 +92,27 @@ def compare_attention(out_gpu: np.ndarray, out_ref: np.ndarray, dtype: str):
     else:
         assert max_abs <= F32_MAX_ABS, f"max |dO| {max_abs}"
     return max_abs, rel
+
+
+BWD_REL_L2 = 1e-2
+BWD_MAX_REL = 2e-2
+
+
+def grad_errors(gpu: np.ndarray, ref: np.ndarray):
+    """(relative L2 error, max error / max |ref|); (0, 0) when both are zero, inf when only ref is."""
+    d = np.abs(gpu.astype(np.float64) - ref)
+    peak = float(np.abs(ref).max()) if ref.size else 0.0
+    if peak == 0.0:
+        return (0.0, 0.0) if not d.any() else (math.inf, math.inf)
+    return float(np.linalg.norm(d) / np.linalg.norm(ref)), float(d.max()) / peak
+
+
+def compare_grad(gpu: np.ndarray, ref: np.ndarray, name: str):
+    """Gradient rule: relative L2 and max error relative to the largest reference entry."""
+    rel, mx = grad_errors(gpu, ref)
+    assert rel <= BWD_REL_L2, f"{name}: rel L2 {rel:.3e}"
+    assert mx <= BWD_MAX_REL, f"{name}: max err / max |ref| {mx:.3e}"
+    return rel, mx
 
 
 def sample_rows(og: R.Geom, blocks) -> np.ndarray:

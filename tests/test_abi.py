@@ -31,12 +31,12 @@ def declared_functions():
 
 def test_exports_every_declared_symbol(A):
     names = declared_functions()
-    assert len(names) == 7
+    assert len(names) == 9
     lib = ctypes.CDLL(LIB)
     for n in names:
         assert hasattr(lib, n), n
     assert set(names) == set(A.EXPORTED)
-    assert A.version() == 100
+    assert A.version() == 200
     assert A.status_str(0) == "ok" and A.status_str(99) == "unknown status"
 
 
@@ -53,6 +53,7 @@ def reorder(A, g, dtype=1, inverse=0, layout=0, x=FAKE, y=FAKE2, pooled=None):
 @pytest.mark.parametrize("kw,code", [
     (dict(B=0), 1), (dict(H=-1), 1), (dict(T=0), 1), (dict(Hs=12), 1), (dict(Ws=20), 1), (dict(d=0), 1),
     (dict(P=4, Hs=16, Ws=24), 2), (dict(d=96), 2), (dict(d=256), 2), (dict(B=1 << 40), 2),
+    (dict(T=1 << 16, Hs=1 << 8, Ws=1 << 8), 2),  # 2^32 tokens per head
 ])
 def test_reorder_geometry_errors(A, kw, code):
     assert reorder(A, G(A, **kw)) == code
@@ -118,6 +119,36 @@ def test_attention_errors(A):
     assert attn_call(A, g, ws_bytes=2 * 18 * 4 - 1) == 3
     assert attn_call(A, G(A, d=32)) == 2
     assert A.sparse_attn_workspace_bytes(A.Geometry(1, 2, 3, 16, 24, 128)) == 2 * 18 * 4 + 256
+
+
+def bwd_call(A, g, dtype=1, scale=0.0, ws_bytes=1 << 40, **over):
+    # Fake device addresses 4 GiB apart (no two overlap); every call below fails validation first.
+    names = ("q", "k", "v", "o", "dout", "lse", "words", "counts", "lists", "dq", "dk", "dv", "ws")
+    p = {n: ctypes.c_void_p((i + 1) << 32) for i, n in enumerate(names)}
+    p.update(over)
+    return A._lib.abla_sparse_attn_bwd(ctypes.byref(g), dtype, scale, *[p[n] for n in names[:-1]], p["ws"],
+                                       ws_bytes, None)
+
+
+def test_backward_errors(A):
+    g = G(A)
+    for n in ("q", "k", "v", "o", "dout", "lse", "words", "counts", "lists", "dq", "dk", "dv"):
+        assert bwd_call(A, g, **{n: None}) == 1, n
+    assert bwd_call(A, g, dtype=3) == 1
+    assert bwd_call(A, g, dtype=0) == 2  # float32 gradients are not implemented
+    assert bwd_call(A, g, scale=math.nan) == 1
+    assert bwd_call(A, g, scale=-1.0) == 1
+    assert bwd_call(A, g, dk=ctypes.c_void_p(1 << 32)) == 1  # dk aliases q
+    assert bwd_call(A, g, dv=ctypes.c_void_p(10 << 32)) == 1  # dv aliases dq
+    assert bwd_call(A, g, ws=None) == 3
+    need = A.sparse_attn_bwd_workspace_bytes(A.Geometry(1, 2, 3, 16, 24, 128))
+    def al(n):
+        return (n + 255) // 256 * 256
+
+    x = al(2 * 1152 * 128 * 2)  # one [B,H,N,d] bf16 tensor (B*H = 2, N = 1152, nb = 18)
+    assert need == 7 * x + 2 * al(2 * 1152 * 4) + al(2 * 18 * 4) + al(2 * 18 * 18 * 4)
+    assert bwd_call(A, g, ws_bytes=need - 1) == 3
+    assert bwd_call(A, G(A, d=32)) == 2
 
 
 def test_binding_rejects_cpu_tensors(A):

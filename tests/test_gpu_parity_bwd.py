@@ -1,0 +1,291 @@
+"""Backward (dQ, dK, dV) of the block-sparse attention: HIP path vs the CPU oracle, through the C-ABI.
+
+Two kinds of check, both under the gradient rule of tests/parity.py:
+- kernel parity: the backward entry point is handed the oracle's forward output O (rounded
+  to bf16, as the forward stores it) and log-sum-exp, and the oracle's backward takes D from
+  that same O, so both sides see identical inputs; the mask is the GPU's own (checked
+  against the oracle by the forward tests) or a random one built here;
+- end to end: the GPU forward's O and lse feed the GPU backward, compared with the oracle's
+  exact gradients.
+Small geometries are compared in full; the 480p workload runs at full size, both ways, with
+dQ checked on sampled query blocks and dK / dV on sampled key blocks (the oracle then
+processes every query block that keeps the key block).
+
+Inputs use Q.K scores of order one: when one key dominates every row, P is nearly one-hot,
+dP - D cancels to a few ulps of dP and the gradients carry no accurate digits in any
+precision that stores O in bf16, which tests nothing about the kernels.
+"""
+import math
+
+import numpy as np
+import pytest
+import torch
+
+from gen import WORKLOADS, make_dout, make_qkv, make_random_qkv
+from oracle import nabla_ref as R
+from tests import parity as PT
+
+pytestmark = pytest.mark.gpu
+
+DEV = "cuda"
+NAMES = ("dq", "dk", "dv")
+
+
+@pytest.fixture(scope="module")
+def A():
+    import block_sparse_attention_21_amd as A
+    assert torch.cuda.is_available(), "the gpu tests need a HIP device"
+    return A
+
+
+def _head(x, b, h, og):
+    """Fractal-order float64 copy of one (b, h) slice of an original-order [B,H,N,d] tensor."""
+    gh = R.Geom(1, 1, og.T, og.Hs, og.Ws, og.d, og.P)
+    return R.reorder(R.to64(x[b, h]), gh), gh
+
+
+def _oracle_forward(q, k, v, gm, og):
+    """Oracle O (original order, rounded to bf16) and lse (fractal order, float32) on mask gm."""
+    scale = 1.0 / math.sqrt(og.d)
+    O = np.empty((og.B, og.H, og.N, og.d))
+    lse = np.empty((og.B, og.H, og.N))
+    for b in range(og.B):
+        for h in range(og.H):
+            Qr, gh = _head(q, b, h, og)
+            Kr, _ = _head(k, b, h, og)
+            Vr, _ = _head(v, b, h, og)
+            Or, lse[b, h] = R.masked_attention_head(Qr, Kr, Vr, gm[b, h], gh, scale)
+            O[b, h] = R.inverse_reorder(Or, gh)
+    o = torch.from_numpy(O).to(torch.bfloat16).to(DEV)
+    return o, torch.from_numpy(lse.astype(np.float32)).to(DEV)
+
+
+def _check_full(og, q, k, v, dout, gm, dq, dk, dv, tag, o_given=None):
+    """Every element of the three gradients against the oracle, head by head. With o_given
+    the oracle takes D from that (bf16) forward output."""
+    scale = 1.0 / math.sqrt(og.d)
+    got = {n: [] for n in NAMES}
+    ref = {n: [] for n in NAMES}
+    for b in range(og.B):
+        for h in range(og.H):
+            Qr, gh = _head(q, b, h, og)
+            Kr, _ = _head(k, b, h, og)
+            Vr, _ = _head(v, b, h, og)
+            dOr, _ = _head(dout, b, h, og)
+            Og = None if o_given is None else _head(o_given, b, h, og)[0]
+            rs = R.masked_attention_backward_head(Qr, Kr, Vr, dOr, gm[b, h], gh, scale, O=Og)
+            for n, t, r in zip(NAMES, (dq, dk, dv), rs):
+                got[n].append(_head(t, b, h, og)[0])
+                ref[n].append(r)
+    errs = {n: PT.grad_errors(np.stack(got[n]), np.stack(ref[n])) for n in NAMES}
+    print(f"{tag}: " + ", ".join(f"{n} rel {r:.2e} max {m:.2e}" for n, (r, m) in errs.items()), flush=True)
+    for n in NAMES:
+        PT.compare_grad(np.stack(got[n]), np.stack(ref[n]), f"{tag} {n}")
+    return errs
+
+
+def _inputs(B, H, T, Hs, Ws, d, seed, mix=0.25):
+    q, k, v = make_random_qkv(B, H, T, Hs, Ws, d, "bf16", seed=seed, device=DEV)
+    # A little of Q in K gives the pooled scores some structure for the mask.
+    k = (k.float() + mix * q.float()).to(q.dtype)
+    dout = make_dout(B, H, T * Hs * Ws, d, seed=seed + 1, device=DEV)
+    return q, k, v, dout
+
+
+SMALL = [
+    # (name, d, (B,H,T,Hs,Ws), MaskParams kwargs)
+    ("ragged", 128, (1, 2, 3, 24, 88), dict(mode="cdf", thr=0.7)),  # nb = 99
+    ("d64", 64, (2, 1, 4, 16, 40), dict(mode="cdf", thr=0.9)),
+    ("dyn", 128, (1, 2, 3, 32, 32), dict(mode="dyn", tau=2.0)),
+    ("no-sta", 128, (1, 1, 5, 16, 24), dict(mode="cdf", thr=0.6, sta=(0, 0, 0))),
+    ("full", 128, (1, 1, 2, 16, 32), dict(mode="cdf", thr=1.0)),
+    ("one-block", 128, (1, 2, 1, 8, 8), dict(mode="cdf", thr=0.5)),
+    ("d64-nb300", 64, (1, 1, 3, 80, 80), dict(mode="cdf", thr=0.95)),
+]
+
+
+@pytest.mark.parametrize("case", SMALL, ids=[c[0] for c in SMALL])
+def test_backward_kernel_parity(A, case):
+    """The backward entry point on the oracle's O and lse, every element."""
+    name, d, (B, H, T, Hs, Ws), pkw = case
+    geom, og = PT.geoms(B, H, T, Hs, Ws, d)
+    q, k, v, dout = _inputs(B, H, T, Hs, Ws, d, seed=11)
+    run = A.NablaAttention(geom, A.MaskParams(**pkw), dtype=torch.bfloat16, want_lse=True)
+    run(q, k, v)
+    torch.cuda.synchronize()
+    gm = PT.gpu_mask(run.words, og)
+    o, lse = _oracle_forward(q, k, v, gm, og)
+    print(f"backward {name}: B{B} H{H} nb{geom.nb} d{d} kept {int(gm.sum())}", flush=True)
+    dq, dk, dv = A.sparse_attn_bwd(q, k, v, o, dout, lse, run.words, run.counts, run.lists, geom)
+    torch.cuda.synchronize()
+    _check_full(og, q, k, v, dout, gm, dq, dk, dv, name, o_given=o)
+
+
+@pytest.mark.parametrize("case", [SMALL[0], SMALL[1]], ids=[SMALL[0][0], SMALL[1][0]])
+def test_backward_end_to_end(A, case):
+    """GPU forward then GPU backward (NablaAttention.backward) against the exact oracle."""
+    name, d, (B, H, T, Hs, Ws), pkw = case
+    geom, og = PT.geoms(B, H, T, Hs, Ws, d)
+    q, k, v, dout = _inputs(B, H, T, Hs, Ws, d, seed=12)
+    run = A.NablaAttention(geom, A.MaskParams(**pkw), dtype=torch.bfloat16, want_lse=True)
+    run(q, k, v)
+    dq, dk, dv = run.backward(q, k, v, dout)
+    torch.cuda.synchronize()
+    _check_full(og, q, k, v, dout, PT.gpu_mask(run.words, og), dq, dk, dv, f"e2e {name}")
+
+
+def _random_mask_inputs(og, rng, p_keep=0.3):
+    """A random block mask with an empty row, an empty column and a full row, as words / counts / lists."""
+    M = rng.random((og.B, og.H, og.nb, og.nb)) < p_keep
+    M[..., 0, :] = False   # query block 0 keeps nothing
+    M[..., 2, :] = True    # query block 2 keeps everything but key block 1
+    M[..., :, 1] = False   # no query block keeps key block 1
+    words = torch.from_numpy(np.ascontiguousarray(R.pack_bits(M)).view(np.int32)).to(DEV)
+    counts = torch.from_numpy(M.sum(-1).astype(np.int32)).to(DEV)
+    lists = np.zeros((og.B, og.H, og.nb, og.nb), dtype=np.int32)
+    for idx in np.ndindex(M.shape[:-1]):
+        nz = np.nonzero(M[idx])[0]
+        lists[idx][: len(nz)] = nz
+    return M, words, counts, torch.from_numpy(lists).to(DEV)
+
+
+@pytest.mark.parametrize("d", [128, 64])
+def test_backward_random_mask(A, d):
+    """Masks not made by the mask builder: an empty row, an empty column, a full row."""
+    B, H, T, Hs, Ws = 1, 2, 2, 24, 40
+    geom, og = PT.geoms(B, H, T, Hs, Ws, d)
+    M, words, counts, lists = _random_mask_inputs(og, np.random.default_rng(d))
+    q, k, v, dout = _inputs(B, H, T, Hs, Ws, d, seed=21, mix=0.0)
+    o, lse = _oracle_forward(q, k, v, M, og)
+    print(f"backward random mask d{d}: nb{geom.nb} kept {int(M.sum())}", flush=True)
+    dq, dk, dv = A.sparse_attn_bwd(q, k, v, o, dout, lse, words, counts, lists, geom)
+    torch.cuda.synchronize()
+    _check_full(og, q, k, v, dout, M, dq, dk, dv, f"random-d{d}", o_given=o)
+    # Rows of the empty query block get dQ = 0 exactly; keys of the empty column get dK = dV = 0.
+    inv = torch.from_numpy(np.argsort(R.fractal_positions(og))).to(DEV)
+    assert torch.count_nonzero(dq[:, :, inv[:64]]) == 0
+    assert torch.count_nonzero(dk[:, :, inv[64:128]]) == 0
+    assert torch.count_nonzero(dv[:, :, inv[64:128]]) == 0
+
+
+def test_backward_empty_mask_gives_zero(A):
+    geom, og = PT.geoms(1, 2, 2, 16, 16, 128)
+    q, k, v, dout = _inputs(1, 2, 2, 16, 16, 128, seed=5)
+    run = A.NablaAttention(geom, A.MaskParams(mode="cdf", thr=0.0, sta=(0, 0, 0)), want_lse=True)
+    run(q, k, v)
+    dq, dk, dv = run.backward(q, k, v, dout)
+    torch.cuda.synchronize()
+    assert int(run.counts.sum()) == 0
+    for t in (dq, dk, dv):
+        assert torch.count_nonzero(t) == 0
+
+
+def test_backward_deterministic_and_reusable_workspace(A):
+    """Two calls with the same workspace give bit-identical gradients (no atomics in the path)."""
+    geom, og = PT.geoms(1, 2, 3, 24, 40, 128)
+    q, k, v, dout = _inputs(1, 2, 3, 24, 40, 128, seed=6)
+    run = A.NablaAttention(geom, A.MaskParams(mode="cdf", thr=0.8), want_lse=True)
+    run(q, k, v)
+    ws = torch.empty(A.sparse_attn_bwd_workspace_bytes(geom), dtype=torch.uint8, device=DEV)
+    a = [t.clone() for t in run.backward(q, k, v, dout, workspace=ws)]
+    b = run.backward(q, k, v, dout, workspace=ws)
+    torch.cuda.synchronize()
+    for x, y in zip(a, b):
+        assert torch.equal(x.view(torch.int16), y.view(torch.int16))
+
+
+def _sampled_480p(A, w, og, geom, q, k, v, dout, run):
+    """Sampled blocks of two heads: (head, query blocks, key blocks, rows whose O / lse decide them)."""
+    gm = PT.gpu_mask(run.words, og)
+    rng = np.random.default_rng(1)
+    picks = []
+    for h in (0, og.H - 1):
+        m = gm[0, h]
+        qblocks = sorted(set([int(m.sum(1).argmax())] + rng.integers(0, og.nb, 2).tolist()))
+        col = m.sum(0)
+        kblocks = sorted(set([int(col.argmax()), int(col.argmin()), int(rng.integers(0, og.nb))]))
+        need = sorted(set(qblocks).union(*[np.nonzero(m[:, j])[0].tolist() for j in kblocks]))
+        picks.append((h, qblocks, kblocks, need))
+    return gm, picks
+
+
+def _compare_sampled(og, q, k, v, dout, gm, picks, dq, dk, dv, tag, o_given=None):
+    scale = 1.0 / math.sqrt(og.d)
+    inv = np.argsort(R.fractal_positions(og))
+    got = {n: [] for n in NAMES}
+    ref = {n: [] for n in NAMES}
+    for h, qblocks, kblocks, _ in picks:
+        Qr, gh = _head(q, 0, h, og)
+        Kr, _ = _head(k, 0, h, og)
+        Vr, _ = _head(v, 0, h, og)
+        dOr, _ = _head(dout, 0, h, og)
+        Og = None if o_given is None else _head(o_given, 0, h, og)[0]
+        m = gm[0, h]
+        rows = PT.sample_rows(og, qblocks)
+        rq, _, _ = R.masked_attention_backward_head(Qr, Kr, Vr, dOr, m, gh, scale, rows=rows, O=Og)
+        got["dq"].append(dq[0, h, torch.from_numpy(inv[rows]).to(DEV)].float().cpu().numpy())
+        ref["dq"].append(rq)
+        for j in kblocks:
+            keeps = np.nonzero(m[:, j])[0]
+            krows = PT.sample_rows(og, [j])
+            qrows = PT.sample_rows(og, keeps) if len(keeps) else np.zeros(0, dtype=np.int64)
+            _, rk, rv = R.masked_attention_backward_head(Qr, Kr, Vr, dOr, m, gh, scale, rows=qrows, O=Og)
+            sel = torch.from_numpy(inv[krows]).to(DEV)
+            got["dk"].append(dk[0, h, sel].float().cpu().numpy())
+            got["dv"].append(dv[0, h, sel].float().cpu().numpy())
+            ref["dk"].append(rk[krows])
+            ref["dv"].append(rv[krows])
+    errs = {n: PT.grad_errors(np.concatenate(got[n]), np.concatenate(ref[n])) for n in NAMES}
+    print(f"{tag}: " + ", ".join(f"{n} rel {r:.2e} max {m:.2e}" for n, (r, m) in errs.items()), flush=True)
+    for n in NAMES:
+        PT.compare_grad(np.concatenate(got[n]), np.concatenate(ref[n]), f"{tag} {n}")
+
+
+def _setup_480p(A):
+    w = WORKLOADS["480p"]
+    geom, og = PT.geoms(w.B, w.H, w.T, w.Hs, w.Ws, w.d, w.P)
+    q, k, v = make_qkv(w, device=DEV)
+    dout = make_dout(w.B, w.H, geom.N, w.d, seed=7, device=DEV)
+    run = A.NablaAttention(geom, A.MaskParams(mode=w.mode, thr=w.thr, tau=w.tau, sta=tuple(w.sta)),
+                           want_lse=True)
+    run(q, k, v)
+    torch.cuda.synchronize()
+    return w, geom, og, q, k, v, dout, run
+
+
+def test_backward_480p_kernel_parity_sampled(A):
+    """Full-size 480p (12 heads, nb = 588): the backward entry point handed the oracle's O (bf16)
+    and lse on every row that the sampled outputs depend on (the sampled query blocks and every
+    query block keeping a sampled key block). The remaining rows get O = 0 and an lse of
+    float32 max, which makes their P zero; they only feed outputs that are not compared."""
+    w, geom, og, q, k, v, dout, run = _setup_480p(A)
+    gm, picks = _sampled_480p(A, w, og, geom, q, k, v, dout, run)
+    scale = 1.0 / math.sqrt(og.d)
+    pos = R.fractal_positions(og)
+    O = np.zeros((og.B, og.H, og.N, og.d))
+    lse = np.full((og.B, og.H, og.N), np.finfo(np.float32).max)
+    for h, _, _, need in picks:
+        Qr, gh = _head(q, 0, h, og)
+        Kr, _ = _head(k, 0, h, og)
+        Vr, _ = _head(v, 0, h, og)
+        rows = PT.sample_rows(og, need)
+        Or, lr = R.masked_attention_head(Qr, Kr, Vr, gm[0, h], gh, scale, rows=rows)
+        inv = np.argsort(pos)
+        O[0, h, inv[rows]] = Or
+        lse[0, h, rows] = lr
+    o = torch.from_numpy(O).to(torch.bfloat16).to(DEV)
+    lse_t = torch.from_numpy(lse.astype(np.float32)).to(DEV)
+    print("backward 480p full size, oracle O / lse", flush=True)
+    dq, dk, dv = A.sparse_attn_bwd(q, k, v, o, dout, lse_t, run.words, run.counts, run.lists, geom)
+    torch.cuda.synchronize()
+    _compare_sampled(og, q, k, v, dout, gm, picks, dq, dk, dv, "480p kernel", o_given=o)
+
+
+def test_backward_480p_end_to_end_sampled(A):
+    """Full-size 480p, GPU forward then GPU backward, against the exact oracle gradients."""
+    w, geom, og, q, k, v, dout, run = _setup_480p(A)
+    gm, picks = _sampled_480p(A, w, og, geom, q, k, v, dout, run)
+    print("backward 480p full size, end to end", flush=True)
+    dq, dk, dv = run.backward(q, k, v, dout)
+    torch.cuda.synchronize()
+    _compare_sampled(og, q, k, v, dout, gm, picks, dq, dk, dv, "480p e2e")
