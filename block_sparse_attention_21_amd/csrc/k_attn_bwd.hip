@@ -7,23 +7,24 @@
 //   dV = P^T dO,  dP = dO V^T,  D_i = <dO_i, O_i>,  dS = P * (dP - D),
 //   dQ = scale * dS K,  dK = scale * dS^T Q.
 //
-// Pre-passes: D and log2(e) * lse per fractal row (k_bwd_delta); for every key block the
-// ascending list of query blocks that keep it (k_col_lists); fractal reorders of Q, K, V, dO
-// into the token-major and channel-major layouts the MFMA operands read.
+// Pre-passes: token-major fractal copies of Q, K, V, dO; D and log2(e) * lse per fractal row
+// (k_bwd_delta); for every key block the ascending list of query blocks that keep it
+// (k_col_lists).
 //
-// k_bwd_dq, one workgroup (two waves of 32 queries) per query block, walks the block's kept
-// list like the forward: S^T = K Q^T and dP^T = V dO^T with the K / V rows in the forward's
-// key permutation, so each lane's accumulators hold 8 consecutive keys of its query;
-// dS^T = P^T * (dP^T - D) rounded to bf16 is then the B operand of dQ^T += K^T dS^T, with
-// K^T rows read from the channel-major copy of K.
+// k_bwd_dq, one workgroup of four waves per query block, walks the block's kept list: wave
+// (qh, kh) forms S^T = K Q^T and dP^T = V dO^T for keys kh*32.. and queries qh*32.. with the K /
+// V rows in the forward's key permutation, so each lane's accumulators hold 8 consecutive keys
+// of its query; dS^T = P^T * (dP^T - D) rounded to bf16 is then the B operand of
+// dQ^T += K^T dS^T, whose K^T operand is read from the same token-major K tile with the gfx950
+// LDS transpose load. The two key halves are summed through LDS at the end.
 //
-// k_bwd_dkdv, one workgroup (two waves of 32 keys) per key block, walks the key block's
-// column list with the roles of Q and K swapped: S = Q K^T and dP = dO V^T with the query
-// rows permuted, so each lane holds 8 consecutive queries of its key; then
-// dV^T += dO^T P and dK^T += Q^T dS with channel-major copies of dO and Q.
+// k_bwd_dkdv, one workgroup of four waves per key block, walks the key block's column list with
+// the roles of Q and K swapped: S = Q K^T and dP = dO V^T with the query rows permuted, then
+// dV^T += dO^T P and dK^T += Q^T dS with dO^T and Q^T read by transpose loads.
 //
-// Both write their gradient rows in the original token order. bf16 inputs and outputs,
-// float32 accumulation, P and dS rounded to bf16 for the MFMA products.
+// Both kernels double-buffer their tiles in LDS (the loads of tile u+1 run during the products
+// of tile u) and write their gradient rows in the original token order. bf16 inputs and
+// outputs, float32 accumulation, P and dS rounded to bf16 for the MFMA products.
 #include <math.h>
 
 #include "common.h"
@@ -32,7 +33,6 @@
 namespace abla {
 namespace {
 
-constexpr int kBwdThreads = 128;  // two waves, 32 rows each
 constexpr float kLog2e = 1.4426950408889634f;
 
 // ------------------------------------------------------------------- pre-passes
@@ -84,31 +84,15 @@ __global__ __launch_bounds__(256) void k_col_lists(const uint32_t* __restrict__ 
   col_counts[bh * nb + j] = c;
 }
 
-// ------------------------------------------------------------------- tile loads
-// 128-thread global->LDS loads of one 64-row tile. Token-major tiles (K, V, Q, dO rows) take
-// the forward's K layout: LDS row r holds row kperm(r), its 16-byte chunks XOR-swizzled by
-// k_swz(r). Channel-major tiles (K^T, Q^T, dO^T) take the forward's V^T layout. Unit u of the
-// tile sits at LDS byte u*16; thread t fills units it*128 + t.
-template <int D, bool TOKEN_MAJOR>
-__device__ __forceinline__ void load_tile128(char* slot, i32x4_t rsrc, uint32_t tile) {
-  constexpr int UNITS = kBlock * D * 2 / 16;
-  constexpr int LOADS = UNITS / kBwdThreads;
-  const int t = threadIdx.x, w = t >> 6;
-#pragma unroll
-  for (int it = 0; it < LOADS; ++it) {
-    const int u = it * kBwdThreads + t;
-    uint32_t off;
-    if constexpr (TOKEN_MAJOR) {
-      constexpr int KCH = D / 8;
-      const int r = u / KCH, pc = u % KCH;
-      off = (uint32_t)(kperm(r) * D * 2 + ((pc ^ k_swz<D>(r)) * 16));
-    } else {
-      const int dd = u >> 3, pc = u & 7;
-      off = (uint32_t)(dd * kBlock * 2 + ((pc ^ v_swz(dd)) * 16));
-    }
-    raw_buffer_load_lds(rsrc, (__attribute__((address_space(3))) uint32_t*)(slot + it * kBwdThreads * 16 + w * 1024),
-                        16, (int)off, (int)tile, 0, 0);
-  }
+// ------------------------------------------------------------------- operands
+// Offset (bytes, within a tile) of the 16-byte source chunk that LDS unit t of a token-major
+// tile holds: LDS row r = t / KCH holds row kperm(r) of the block, its chunks XOR-swizzled by
+// k_swz(r). issue_rows advances it by 4096 bytes per further load of the thread.
+template <int D>
+__device__ __forceinline__ uint32_t token_tile_off(int t) {
+  constexpr int KCH = D / 8;
+  const int r = t / KCH, pc = t % KCH;
+  return (uint32_t)(kperm(r) * D * 2 + ((pc ^ k_swz<D>(r)) * 16));
 }
 
 // A-operand chunk of a token-major tile: row (half*32 + lane%32), k-step ks.
@@ -119,36 +103,75 @@ __device__ __forceinline__ bf16x8_t row_chunk(const char* tile, int half, int la
   return *reinterpret_cast<const bf16x8_t*>(tile + row * D * 2 + c * 16);
 }
 
-// A-operand chunk of a channel-major tile: channel (dt*32 + lane%32), 16-row step kk.
-__device__ __forceinline__ bf16x8_t chan_chunk(const char* tile, int dt, int lane, int kk) {
-  const int ch = dt * 32 + (lane & 31);
-  const int c = (2 * kk + (lane >> 5)) ^ v_swz(ch);
-  return *reinterpret_cast<const bf16x8_t*>(tile + ch * kBlock * 2 + c * 16);
+typedef short i16x4_t __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) i16x4_t* lds_i16x4_ptr;
+
+// A-operand chunk of the TRANSPOSE of a token-major tile X, read with the gfx950 LDS transpose
+// load: lane l receives X^T[dt*32 + l%32][tb + 8*(l/32) + e], e = 0..7, i.e. 8 consecutive
+// tokens of one channel. ds_read_tr16_b64 works on groups of 16 lanes: each lane names 8 bytes
+// (4 bf16) and lane i of the group receives element i%4 of the read named by lane 4e + i/4 as its
+// element e. So lane m of a group names token tb + 8*hi + 4*half + m/4, channels
+// c0 + 4*(m%4) .. +3 (c0 = dt*32 + 16*(group&1)), and lane i then holds channel c0 + i of four
+// consecutive tokens; two such reads give the 8 tokens.
+template <int D>
+__device__ __forceinline__ bf16x8_t tr_chunk(const char* tile, int dt, int tb, int lane) {
+  const int g = lane >> 4, m = lane & 15;
+  const int ch = dt * 32 + 16 * (g & 1) + 4 * (m & 3);
+  const int tok = tb + 8 * (g >> 1) + (m >> 2);
+  const int r0 = kperm(tok), r1 = kperm(tok + 4);
+  const char* p0 = tile + r0 * D * 2 + (((ch >> 3) ^ k_swz<D>(r0)) << 4) + (ch & 7) * 2;
+  const char* p1 = tile + r1 * D * 2 + (((ch >> 3) ^ k_swz<D>(r1)) << 4) + (ch & 7) * 2;
+  const i16x4_t a = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4_ptr)p0);
+  const i16x4_t b = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4_ptr)p1);
+  const i16x4_t both[2] = {a, b};
+  bf16x8_t out;
+  __builtin_memcpy(&out, both, 16);
+  return out;
 }
 
-// Write one wave's transposed accumulators acc[dt][r] = X^T[channel dt*32 + 8*(r/4) + 4*hi + r%4]
-// [row lane%32] as bf16 rows x * mul of the original-order tensor y, row = token of (blk, row_local).
-template <int D>
+// Write rows of one wave's transposed accumulators acc[k][r] = X^T[channel (dt0+k)*32 + 8*(r/4)
+// + 4*hi + r%4][row lane%32], k < NDT, as bf16 x * mul into the original-order tensor y, row =
+// token of (blk, row_local).
+template <int D, int NDT>
 __device__ __forceinline__ void write_rows(uint16_t* y, const KGeom& g, long long bh, int blk, int row_local,
-                                           const f32x16_t* acc, float mul, int hi) {
+                                           const f32x16_t* acc, int dt0, float mul, int hi) {
   const long long n = token_of(g, blk, row_local);
-  uint16_t* orow = y + (bh * g.N + n) * D;
+  uint16_t* orow = y + (bh * g.N + n) * D + dt0 * 32 + 4 * hi;
 #pragma unroll
-  for (int dt = 0; dt < D / 32; ++dt)
+  for (int k = 0; k < NDT; ++k)
 #pragma unroll
     for (int g4 = 0; g4 < 4; ++g4) {
       __bf16 h[4];
 #pragma unroll
-      for (int e = 0; e < 4; ++e) h[e] = (__bf16)(acc[dt][4 * g4 + e] * mul);
+      for (int e = 0; e < 4; ++e) h[e] = (__bf16)(acc[k][4 * g4 + e] * mul);
       uint2 v;
       __builtin_memcpy(&v, h, 8);
-      *reinterpret_cast<uint2*>(orow + dt * 32 + 8 * g4 + 4 * hi) = v;
+      *reinterpret_cast<uint2*>(orow + k * 32 + 8 * g4) = v;
     }
 }
 
+// Store / add NT accumulator tiles acc[first .. first+NT) through LDS, layout float [NT][16][64]
+// (lane-contiguous). Indices are compile-time so the accumulators stay in registers.
+template <int FIRST, int NT>
+__device__ __forceinline__ void stash(float* dst, const f32x16_t* acc, int lane) {
+#pragma unroll
+  for (int k = 0; k < NT; ++k)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) dst[(k * 16 + r) * 64 + lane] = acc[FIRST + k][r];
+}
+template <int FIRST, int NT>
+__device__ __forceinline__ void unstash_add(const float* src, f32x16_t* acc, int lane) {
+#pragma unroll
+  for (int k = 0; k < NT; ++k)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) acc[FIRST + k][r] += src[(k * 16 + r) * 64 + lane];
+}
+
+constexpr int kBwdThreads = 256;  // four waves
+
 // ------------------------------------------------------------------- dQ
 struct DqArgs {
-  const uint16_t *q_r, *k_r, *k_rt, *v_r, *do_r;
+  const uint16_t *q_r, *k_r, *v_r, *do_r;
   const float *Dm, *L2;
   const int32_t *counts, *lists;
   uint16_t* dq;
@@ -156,22 +179,24 @@ struct DqArgs {
   float c2, scale;
 };
 
+// One workgroup per query block i, four waves: wave (qh, kh) takes queries qh*32.. and keys
+// kh*32.. of every kept key tile. K and V tiles (token-major) are double-buffered in LDS: the
+// loads of tile u+1 run during the products of tile u.
 template <int D>
-__global__ __launch_bounds__(kBwdThreads) void k_bwd_dq(DqArgs a) {
+__global__ __launch_bounds__(kBwdThreads) __attribute__((amdgpu_waves_per_eu(2, 2))) void k_bwd_dq(DqArgs a) {
   constexpr int TB = kBlock * D * 2;
-  __shared__ __attribute__((aligned(1024))) char smem[3 * TB];  // K, V (token-major), K^T
-  char* ks_lds = smem;
-  char* vs_lds = smem + TB;
-  char* kt_lds = smem + 2 * TB;
-
+  constexpr int DT = D / 32;
+  __shared__ __attribute__((aligned(1024))) char smem[4 * TB];  // K0, K1, V0, V1
   const KGeom& g = a.g;
   const int nb = g.nb;
-  const int t = threadIdx.x, lane = t & 63, w = t >> 6, hi = lane >> 5;
+  const int t = threadIdx.x, lane = t & 63, hi = lane >> 5;
+  const int w = __builtin_amdgcn_readfirstlane(t >> 6);
+  const int qh = w & 1, kh = w >> 1;
   const long long bh = blockIdx.x / nb;
   const int i = blockIdx.x - (int)(bh * nb);
   const long long row = bh * nb + i;
   const int cnt = min(max(ld_const(a.counts, row), 0), nb);
-  const int q_local = w * 32 + (lane & 31);
+  const int q_local = qh * 32 + (lane & 31);
   const long long m = (long long)i * kBlock + q_local;  // fractal row of this lane's query
 
   bf16x8_t qv[D / 16], dov[D / 16];
@@ -190,57 +215,81 @@ __global__ __launch_bounds__(kBwdThreads) void k_bwd_dq(DqArgs a) {
   const uint32_t head_bytes = (uint32_t)(g.N * D * 2);
   const i32x4_t krs = make_rsrc(a.k_r + bh * g.N * D, head_bytes);
   const i32x4_t vrs = make_rsrc(a.v_r + bh * g.N * D, head_bytes);
-  const i32x4_t ktrs = make_rsrc(a.k_rt + bh * g.N * D, head_bytes);
+  const uint32_t off = token_tile_off<D>(t);
 
-  f32x16_t acc[D / 32];
+  f32x16_t acc[DT];
 #pragma unroll
-  for (int dt = 0; dt < D / 32; ++dt)
+  for (int dt = 0; dt < DT; ++dt)
 #pragma unroll
     for (int r = 0; r < 16; ++r) acc[dt][r] = 0.f;
 
   const int32_t* lst = a.lists + row * nb;
-  for (int u = 0; u < cnt; ++u) {
-    const int j = min(max(ld_const(lst, u), 0), nb - 1);
-    load_tile128<D, true>(ks_lds, krs, (uint32_t)j * TB);
-    load_tile128<D, true>(vs_lds, vrs, (uint32_t)j * TB);
-    load_tile128<D, false>(kt_lds, ktrs, (uint32_t)j * TB);
-    wait_vm_lgkm_barrier();
-
-    f32x16_t s[2], dp[2];
-#pragma unroll
-    for (int kh = 0; kh < 2; ++kh) {
-#pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        s[kh][r] = 0.f;
-        dp[kh][r] = 0.f;
-      }
-#pragma unroll
-      for (int ks = 0; ks < D / 16; ++ks) {
-        s[kh] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(row_chunk<D>(ks_lds, kh, lane, ks), qv[ks], s[kh], 0, 0, 0);
-        dp[kh] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(row_chunk<D>(vs_lds, kh, lane, ks), dov[ks], dp[kh], 0, 0, 0);
-      }
-    }
-    bf16x8_t dsb[4];
-#pragma unroll
-    for (int kh = 0; kh < 2; ++kh)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const float p = exp2_fast(fmaf(s[kh][r], a.c2, -l2));
-        dsb[kh * 2 + (r >> 3)][r & 7] = (__bf16)(p * (dp[kh][r] - dq_d));
-      }
-#pragma unroll
-    for (int kk = 0; kk < 4; ++kk)
-#pragma unroll
-      for (int dt = 0; dt < D / 32; ++dt)
-        acc[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(chan_chunk(kt_lds, dt, lane, kk), dsb[kk], acc[dt], 0, 0, 0);
-    wait_vm_lgkm_barrier();  // every wave is done with the tiles before they are refilled
+  if (cnt > 0) {
+    const uint32_t j0 = (uint32_t)min(max(ld_const(lst, 0), 0), nb - 1);
+    issue_rows<TB>(smem, w, krs, j0 * TB, off);
+    issue_rows<TB>(smem + 2 * TB, w, vrs, j0 * TB, off);
   }
-  write_rows<D>(a.dq, g, bh, i, q_local, acc, a.scale, hi);
+  for (int u = 0; u < cnt; ++u) {
+    wait_vm_lgkm_barrier();  // tile u has landed; every wave is done with tile u-1
+    if (u + 1 < cnt) {
+      const uint32_t jn = (uint32_t)min(max(ld_const(lst, u + 1), 0), nb - 1);
+      issue_rows<TB>(smem + ((u + 1) & 1) * TB, w, krs, jn * TB, off);
+      issue_rows<TB>(smem + 2 * TB + ((u + 1) & 1) * TB, w, vrs, jn * TB, off);
+    }
+    const char* ks_lds = smem + (u & 1) * TB;
+    const char* vs_lds = smem + 2 * TB + (u & 1) * TB;
+
+    // S^T and dP^T for keys kh*32.. (rows of the MFMA) and this wave's 32 queries (columns).
+    f32x16_t s, dp;
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      s[r] = 0.f;
+      dp[r] = 0.f;
+    }
+#pragma unroll
+    for (int ks = 0; ks < D / 16; ++ks) {
+      s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(row_chunk<D>(ks_lds, kh, lane, ks), qv[ks], s, 0, 0, 0);
+      dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(row_chunk<D>(vs_lds, kh, lane, ks), dov[ks], dp, 0, 0, 0);
+    }
+    // Register r holds key kh*32 + 16*(r/8) + 8*hi + r%8 of this lane's query.
+    bf16x8_t dsb[2];
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      const float p = exp2_fast(fmaf(s[r], a.c2, -l2));
+      dsb[r >> 3][r & 7] = (__bf16)(p * (dp[r] - dq_d));
+    }
+    // dQ^T += K^T dS^T over this wave's 32 keys; K^T comes from the K tile by transpose loads.
+#pragma unroll
+    for (int kk = 0; kk < 2; ++kk)
+#pragma unroll
+      for (int dt = 0; dt < DT; ++dt)
+        acc[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(tr_chunk<D>(ks_lds, dt, kh * 32 + kk * 16, lane), dsb[kk],
+                                                          acc[dt], 0, 0, 0);
+  }
+  // Waves (qh, 0) and (qh, 1) hold partial dQ^T over their key halves: wave (qh, kh) finishes
+  // channel tiles [kh*DT/2, kh*DT/2 + DT/2) and hands the other half to its partner.
+  wait_vm_lgkm_barrier();
+  constexpr int H = DT / 2;
+  float* xch = reinterpret_cast<float*>(smem);
+  float* mine = xch + (qh * 2 + kh) * (H * 16 * 64);
+  const float* theirs = xch + (qh * 2 + (1 - kh)) * (H * 16 * 64);
+  if (kh == 0)
+    stash<H, H>(mine, acc, lane);
+  else
+    stash<0, H>(mine, acc, lane);
+  wait_vm_lgkm_barrier();
+  if (kh == 0) {
+    unstash_add<0, H>(theirs, acc, lane);
+    write_rows<D, H>(a.dq, g, bh, i, q_local, acc, 0, a.scale, hi);
+  } else {
+    unstash_add<H, H>(theirs, acc, lane);
+    write_rows<D, H>(a.dq, g, bh, i, q_local, acc + H, H, a.scale, hi);
+  }
 }
 
 // ------------------------------------------------------------------- dK, dV
 struct DkvArgs {
-  const uint16_t *k_r, *v_r, *q_r, *q_rt, *do_r, *do_rt;
+  const uint16_t *k_r, *v_r, *q_r, *do_r;
   const float *Dm, *L2;
   const int32_t *col_counts, *col_lists;
   uint16_t *dk, *dv;
@@ -248,25 +297,25 @@ struct DkvArgs {
   float c2, scale;
 };
 
+// One workgroup per key block j, four waves: wave (kh, qh) takes keys kh*32.. and queries
+// qh*32.. of every query tile in the block's column list. Q and dO tiles (token-major) and the
+// tiles' L2 / D rows are double-buffered in LDS.
 template <int D>
-__global__ __launch_bounds__(kBwdThreads) __attribute__((amdgpu_waves_per_eu(1, 1))) void k_bwd_dkdv(DkvArgs a) {
+__global__ __launch_bounds__(kBwdThreads) __attribute__((amdgpu_waves_per_eu(2, 2))) void k_bwd_dkdv(DkvArgs a) {
   constexpr int TB = kBlock * D * 2;
-  __shared__ __attribute__((aligned(1024))) char smem[4 * TB + 2 * kBlock * 4];  // Q, dO, Q^T, dO^T, L2, D
-  char* q_lds = smem;
-  char* do_lds = smem + TB;
-  char* qt_lds = smem + 2 * TB;
-  char* dot_lds = smem + 3 * TB;
-  float* l2_lds = reinterpret_cast<float*>(smem + 4 * TB);
-  float* d_lds = l2_lds + kBlock;
-
+  constexpr int DT = D / 32;
+  __shared__ __attribute__((aligned(1024))) char smem[4 * TB + 4 * kBlock * 4];  // Q0,Q1,dO0,dO1, L2/D x2
+  float* rows_lds = reinterpret_cast<float*>(smem + 4 * TB);                     // [slot][L2 | D][64]
   const KGeom& g = a.g;
   const int nb = g.nb;
-  const int t = threadIdx.x, lane = t & 63, w = t >> 6, hi = lane >> 5;
+  const int t = threadIdx.x, lane = t & 63, hi = lane >> 5;
+  const int w = __builtin_amdgcn_readfirstlane(t >> 6);
+  const int kh = w & 1, qh = w >> 1;
   const long long bh = blockIdx.x / nb;
   const int j = blockIdx.x - (int)(bh * nb);
   const long long col = bh * nb + j;
   const int cnt = min(max(ld_const(a.col_counts, col), 0), nb);
-  const int k_local = w * 32 + (lane & 31);
+  const int k_local = kh * 32 + (lane & 31);
   const long long mk = (long long)j * kBlock + k_local;  // fractal row of this lane's key
 
   bf16x8_t kb[D / 16], vb[D / 16];
@@ -282,80 +331,102 @@ __global__ __launch_bounds__(kBwdThreads) __attribute__((amdgpu_waves_per_eu(1, 
   const uint32_t head_bytes = (uint32_t)(g.N * D * 2);
   const i32x4_t qrs = make_rsrc(a.q_r + bh * g.N * D, head_bytes);
   const i32x4_t dors = make_rsrc(a.do_r + bh * g.N * D, head_bytes);
-  const i32x4_t qtrs = make_rsrc(a.q_rt + bh * g.N * D, head_bytes);
-  const i32x4_t dotrs = make_rsrc(a.do_rt + bh * g.N * D, head_bytes);
   const i32x4_t l2rs = make_rsrc(a.L2 + bh * g.N, (uint32_t)(g.N * 4));
   const i32x4_t drs = make_rsrc(a.Dm + bh * g.N, (uint32_t)(g.N * 4));
+  const uint32_t off = token_tile_off<D>(t);
 
-  f32x16_t dk[D / 32], dv[D / 32];
+  f32x16_t dk[DT], dv[DT];
 #pragma unroll
-  for (int dt = 0; dt < D / 32; ++dt)
+  for (int dt = 0; dt < DT; ++dt)
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
       dk[dt][r] = 0.f;
       dv[dt][r] = 0.f;
     }
 
+  // Loads of query tile i into slot sl: Q and dO tiles, and 64 floats each of L2 and D (wave 0,
+  // lanes 0-15 with 16 bytes each).
+  auto issue = [&](int sl, int i) {
+    issue_rows<TB>(smem + sl * TB, w, qrs, (uint32_t)i * TB, off);
+    issue_rows<TB>(smem + (2 + sl) * TB, w, dors, (uint32_t)i * TB, off);
+    if (t < 16) {
+      raw_buffer_load_lds(l2rs, (__attribute__((address_space(3))) uint32_t*)(rows_lds + sl * 128), 16, t * 16,
+                          i * kBlock * 4, 0, 0);
+      raw_buffer_load_lds(drs, (__attribute__((address_space(3))) uint32_t*)(rows_lds + sl * 128 + 64), 16, t * 16,
+                          i * kBlock * 4, 0, 0);
+    }
+  };
   const int32_t* lst = a.col_lists + col * nb;
+  if (cnt > 0) issue(0, min(max(ld_const(lst, 0), 0), nb - 1));
   for (int u = 0; u < cnt; ++u) {
-    const int i = min(max(ld_const(lst, u), 0), nb - 1);
-    load_tile128<D, true>(q_lds, qrs, (uint32_t)i * TB);
-    load_tile128<D, true>(do_lds, dors, (uint32_t)i * TB);
-    load_tile128<D, false>(qt_lds, qtrs, (uint32_t)i * TB);
-    load_tile128<D, false>(dot_lds, dotrs, (uint32_t)i * TB);
-    if (t < 16) {  // 64 floats of L2 and 64 of D: 16 lanes x 16 bytes each
-      raw_buffer_load_lds(l2rs, (__attribute__((address_space(3))) uint32_t*)l2_lds, 16, t * 16, i * kBlock * 4, 0, 0);
-      raw_buffer_load_lds(drs, (__attribute__((address_space(3))) uint32_t*)d_lds, 16, t * 16, i * kBlock * 4, 0, 0);
-    }
-    wait_vm_lgkm_barrier();
+    wait_vm_lgkm_barrier();  // tile u has landed; every wave is done with tile u-1
+    if (u + 1 < cnt) issue((u + 1) & 1, min(max(ld_const(lst, u + 1), 0), nb - 1));
+    const char* q_lds = smem + (u & 1) * TB;
+    const char* do_lds = smem + (2 + (u & 1)) * TB;
+    const float* l2_lds = rows_lds + (u & 1) * 128;
+    const float* d_lds = l2_lds + 64;
 
-    // S = Q K^T, dP = dO V^T: accumulator register r of half qh holds query
-    // qh*32 + 16*(r/8) + 8*hi + r%8 of this lane's key (query rows permuted like K rows).
-    f32x16_t s[2], dp[2];
+    // S = Q K^T and dP = dO V^T for queries qh*32.. (rows) and this lane's key (column):
+    // register r holds query qh*32 + 16*(r/8) + 8*hi + r%8.
+    f32x16_t s, dp;
 #pragma unroll
-    for (int qh = 0; qh < 2; ++qh) {
+    for (int r = 0; r < 16; ++r) {
+      s[r] = 0.f;
+      dp[r] = 0.f;
+    }
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        s[qh][r] = 0.f;
-        dp[qh][r] = 0.f;
-      }
+    for (int ks = 0; ks < D / 16; ++ks) {
+      s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(row_chunk<D>(q_lds, qh, lane, ks), kb[ks], s, 0, 0, 0);
+      dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(row_chunk<D>(do_lds, qh, lane, ks), vb[ks], dp, 0, 0, 0);
+    }
+    bf16x8_t pb[2], dsb[2];
 #pragma unroll
-      for (int ks = 0; ks < D / 16; ++ks) {
-        s[qh] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(row_chunk<D>(q_lds, qh, lane, ks), kb[ks], s[qh], 0, 0, 0);
-        dp[qh] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(row_chunk<D>(do_lds, qh, lane, ks), vb[ks], dp[qh], 0, 0, 0);
+    for (int q8 = 0; q8 < 2; ++q8) {
+      const int q0 = qh * 32 + 16 * q8 + 8 * hi;
+      const float4 la = *reinterpret_cast<const float4*>(l2_lds + q0);
+      const float4 lb = *reinterpret_cast<const float4*>(l2_lds + q0 + 4);
+      const float4 da = *reinterpret_cast<const float4*>(d_lds + q0);
+      const float4 db = *reinterpret_cast<const float4*>(d_lds + q0 + 4);
+      const float lq[8] = {la.x, la.y, la.z, la.w, lb.x, lb.y, lb.z, lb.w};
+      const float dd[8] = {da.x, da.y, da.z, da.w, db.x, db.y, db.z, db.w};
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const int r = q8 * 8 + e;
+        const float p = exp2_fast(fmaf(s[r], a.c2, -lq[e]));
+        pb[q8][e] = (__bf16)p;
+        dsb[q8][e] = (__bf16)(p * (dp[r] - dd[e]));
       }
     }
-    bf16x8_t pb[4], dsb[4];
+    // dV^T += dO^T P and dK^T += Q^T dS over this wave's 32 queries; the transposed operands
+    // come from the token-major tiles by transpose loads.
 #pragma unroll
-    for (int qh = 0; qh < 2; ++qh)
+    for (int q8 = 0; q8 < 2; ++q8)
 #pragma unroll
-      for (int q8 = 0; q8 < 2; ++q8) {
-        const int q0 = qh * 32 + 16 * q8 + 8 * hi;
-        const float4 la = *reinterpret_cast<const float4*>(l2_lds + q0);
-        const float4 lb = *reinterpret_cast<const float4*>(l2_lds + q0 + 4);
-        const float4 da = *reinterpret_cast<const float4*>(d_lds + q0);
-        const float4 db = *reinterpret_cast<const float4*>(d_lds + q0 + 4);
-        const float lq[8] = {la.x, la.y, la.z, la.w, lb.x, lb.y, lb.z, lb.w};
-        const float dd[8] = {da.x, da.y, da.z, da.w, db.x, db.y, db.z, db.w};
-#pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          const int r = q8 * 8 + e;
-          const float p = exp2_fast(fmaf(s[qh][r], a.c2, -lq[e]));
-          pb[qh * 2 + q8][e] = (__bf16)p;
-          dsb[qh * 2 + q8][e] = (__bf16)(p * (dp[qh][r] - dd[e]));
-        }
+      for (int dt = 0; dt < DT; ++dt) {
+        dv[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(tr_chunk<D>(do_lds, dt, qh * 32 + q8 * 16, lane), pb[q8],
+                                                         dv[dt], 0, 0, 0);
+        dk[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(tr_chunk<D>(q_lds, dt, qh * 32 + q8 * 16, lane), dsb[q8],
+                                                         dk[dt], 0, 0, 0);
       }
-#pragma unroll
-    for (int kk = 0; kk < 4; ++kk)
-#pragma unroll
-      for (int dt = 0; dt < D / 32; ++dt) {
-        dv[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(chan_chunk(dot_lds, dt, lane, kk), pb[kk], dv[dt], 0, 0, 0);
-        dk[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(chan_chunk(qt_lds, dt, lane, kk), dsb[kk], dk[dt], 0, 0, 0);
-      }
-    wait_vm_lgkm_barrier();  // every wave is done with the tiles before they are refilled
   }
-  write_rows<D>(a.dk, g, bh, j, k_local, dk, a.scale, hi);
-  write_rows<D>(a.dv, g, bh, j, k_local, dv, 1.0f, hi);
+  // Waves (kh, 0) and (kh, 1) hold partial dK^T and dV^T over their query halves: wave qh = 0
+  // finishes dK, wave qh = 1 finishes dV; each hands the other its partial.
+  wait_vm_lgkm_barrier();
+  float* xch = reinterpret_cast<float*>(smem);
+  float* mine = xch + (kh * 2 + qh) * (DT * 16 * 64);
+  const float* theirs = xch + (kh * 2 + (1 - qh)) * (DT * 16 * 64);
+  if (qh == 0)
+    stash<0, DT>(mine, dv, lane);
+  else
+    stash<0, DT>(mine, dk, lane);
+  wait_vm_lgkm_barrier();
+  if (qh == 0) {
+    unstash_add<0, DT>(theirs, dk, lane);
+    write_rows<D, DT>(a.dk, g, bh, j, k_local, dk, 0, a.scale, hi);
+  } else {
+    unstash_add<0, DT>(theirs, dv, lane);
+    write_rows<D, DT>(a.dv, g, bh, j, k_local, dv, 0, 1.0f, hi);
+  }
 }
 
 }  // namespace
@@ -364,15 +435,12 @@ hipError_t launch_sparse_attn_bwd(const KGeom& g, float scale, const void* q, co
                                   const void* o, const void* dout, const float* lse, const uint32_t* words,
                                   const int32_t* counts, const int32_t* lists, void* dq, void* dk, void* dv,
                                   const BwdWorkspace& ws, hipStream_t s) {
-  // Fractal copies: token-major Q, K, V, dO; channel-major Q, K, dO.
+  // Token-major fractal copies of Q, K, V, dO.
   hipError_t e;
   if ((e = launch_reorder(g, ABLA_BF16, 0, ABLA_LAYOUT_TOKENS, q, ws.q_r, nullptr, s)) != hipSuccess) return e;
-  if ((e = launch_reorder(g, ABLA_BF16, 0, ABLA_LAYOUT_BLOCK_T, q, ws.q_rt, nullptr, s)) != hipSuccess) return e;
   if ((e = launch_reorder(g, ABLA_BF16, 0, ABLA_LAYOUT_TOKENS, k, ws.k_r, nullptr, s)) != hipSuccess) return e;
-  if ((e = launch_reorder(g, ABLA_BF16, 0, ABLA_LAYOUT_BLOCK_T, k, ws.k_rt, nullptr, s)) != hipSuccess) return e;
   if ((e = launch_reorder(g, ABLA_BF16, 0, ABLA_LAYOUT_TOKENS, v, ws.v_r, nullptr, s)) != hipSuccess) return e;
   if ((e = launch_reorder(g, ABLA_BF16, 0, ABLA_LAYOUT_TOKENS, dout, ws.do_r, nullptr, s)) != hipSuccess) return e;
-  if ((e = launch_reorder(g, ABLA_BF16, 0, ABLA_LAYOUT_BLOCK_T, dout, ws.do_rt, nullptr, s)) != hipSuccess) return e;
 
   const long long rows = (long long)g.B * g.H * g.N;
   const unsigned bhs = (unsigned)(g.B * g.H);
@@ -391,14 +459,13 @@ hipError_t launch_sparse_attn_bwd(const KGeom& g, float scale, const void* q, co
 
   const float c2 = scale * kLog2e;
   const dim3 grid((unsigned)((long long)bhs * g.nb));
-  DqArgs qa{ws.q_r, ws.k_r, ws.k_rt, ws.v_r, ws.do_r, ws.D, ws.L2, counts, lists,
-            static_cast<uint16_t*>(dq), g, c2, scale};
+  DqArgs qa{ws.q_r, ws.k_r, ws.v_r, ws.do_r, ws.D, ws.L2, counts, lists, static_cast<uint16_t*>(dq), g, c2, scale};
   if (g.d == 128)
     k_bwd_dq<128><<<grid, kBwdThreads, 0, s>>>(qa);
   else
     k_bwd_dq<64><<<grid, kBwdThreads, 0, s>>>(qa);
   if ((e = hipGetLastError()) != hipSuccess) return e;
-  DkvArgs ka{ws.k_r, ws.v_r, ws.q_r, ws.q_rt, ws.do_r, ws.do_rt, ws.D, ws.L2, ws.col_counts, ws.col_lists,
+  DkvArgs ka{ws.k_r, ws.v_r, ws.q_r, ws.do_r, ws.D, ws.L2, ws.col_counts, ws.col_lists,
              static_cast<uint16_t*>(dk), static_cast<uint16_t*>(dv), g, c2, scale};
   if (g.d == 128)
     k_bwd_dkdv<128><<<grid, kBwdThreads, 0, s>>>(ka);

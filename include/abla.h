@@ -169,7 +169,7 @@ abla_status abla_sparse_attn_fwd(const abla_geom* g, int32_t dtype, float scale,
                                  void* out, int32_t out_original_order, float* lse,
                                  void* workspace, size_t workspace_bytes, void* stream);
 
-/* Bytes of scratch abla_sparse_attn_bwd needs: seven fractal copies of one [B,H,N,d] bf16
+/* Bytes of scratch abla_sparse_attn_bwd needs: four fractal copies of one [B,H,N,d] bf16
  * tensor, two [B,H,N] float32 rows, and the column counts [B,H,nb] and lists [B,H,nb,nb] int32,
  * each rounded up to 256 bytes. */
 size_t abla_sparse_attn_bwd_workspace_bytes(const abla_geom* g);
