@@ -15,7 +15,9 @@ order the pages give them. Sources (page title, then section):
 * [DynamicRad] "DynamicRad: Content-Adaptive Sparse Attention for Long Video
   Diffusion" -- Methodology A, dual-mode strategy: the Dynamic-Threshold mode
   uses pre-softmax attention logits as the importance proxy and filters by a
-  threshold.
+  threshold; the Static-Ratio mode scores nothing and keeps blocks at a fixed
+  retention ratio that depends on the temporal distance (decay coefficient
+  gamma, long-range factor lambda).
 
 Readings taken where the pages leave a step open (each is also listed in the
 design notes):
@@ -36,6 +38,14 @@ design notes):
 8. STA window (wt, wh, ww), odd sizes, centred and truncated at the grid
    border; (0, 0, 0) turns it off.
 9. A query row with no allowed key gives O = 0 and LSE = -inf.
+10. Static-Ratio retention law (the pages name gamma and lambda but give no
+    formula): r(0) = 1 and r(dt) = r(dt - 1) * gamma, an exponential decay in
+    the frame distance dt evaluated by repeated multiplication; a key frame at
+    distance dt keeps k(dt) = min(F, max(ceil(F * lambda), ceil(F * r(dt))))
+    of its F blocks, lambda being the long-range floor; the kept blocks of a
+    frame are the k(dt) nearest to the query block's spatial position, ordered
+    by squared distance in blocks, ties by lower position index. The result is
+    OR-ed with the STA window like the other modes.
 
 Parity pins: every function is checked in tests/test_oracle.py against brute
 force, closed forms or library routines. The 1/sqrt(d) scales (reading 4) are
@@ -89,11 +99,13 @@ class Geom:
 
 @dataclasses.dataclass(frozen=True)
 class MaskParams:
-    mode: str = "cdf"  # "cdf" or "dyn"
+    mode: str = "cdf"  # "cdf", "dyn" or "static"
     thr: float = 0.9
     tau: float = 4.0
     pool_scale: float = 0.0  # 0 -> 1/sqrt(d)
     sta: tuple = (3, 3, 3)  # (0, 0, 0) -> off
+    gamma: float = 0.5  # static: retention decay per frame of distance
+    lam: float = 0.05  # static: long-range floor of the retention ratio
 
 
 # --------------------------------------------------------------------------
@@ -212,6 +224,47 @@ def sta_block_mask(g: Geom, window: Sequence[int]) -> np.ndarray:
     return (dt <= rt) & (dh <= rh) & (dw <= rw)
 
 
+# --------------------------------------------------------------------------
+# [DynamicRad] Methodology A, Static-Ratio mode: no content scoring; each key
+# frame keeps a share of its blocks fixed by its temporal distance to the query
+# block (reading 10 above for the law the pages leave open).
+# --------------------------------------------------------------------------
+def static_ratio_counts(g: Geom, gamma: float, lam: float) -> np.ndarray:
+    """k(dt) for dt = 0 .. T-1: blocks kept in a key frame at frame distance dt."""
+    F = g.nbh * g.nbw
+    floor_k = math.ceil(F * lam)
+    out = np.empty(g.T, dtype=np.int64)
+    r = 1.0
+    for dt in range(g.T):
+        out[dt] = min(F, max(floor_k, math.ceil(F * r)))
+        r = r * gamma
+    return out
+
+
+def static_ratio_ranks(g: Geom) -> np.ndarray:
+    """rank[p, q]: place of frame position q in the ordering of all positions of a frame by
+    (squared block distance to position p, position index); positions p = hp * nbw + wp."""
+    F = g.nbh * g.nbw
+    hp, wp = np.divmod(np.arange(F), g.nbw)
+    rank = np.empty((F, F), dtype=np.int64)
+    for p in range(F):
+        d2 = (hp - hp[p]) ** 2 + (wp - wp[p]) ** 2
+        order = np.lexsort((np.arange(F), d2))  # by d2, then by index
+        rank[p, order] = np.arange(F)
+    return rank
+
+
+def static_ratio_block_mask(g: Geom, gamma: float, lam: float) -> np.ndarray:
+    """[nb, nb] bool: query block i keeps key block j iff j's rank around i's position is
+    below the count of j's frame distance."""
+    c = block_coords(g)
+    k = static_ratio_counts(g, gamma, lam)
+    rank = static_ratio_ranks(g)
+    pos = c[:, 1] * g.nbw + c[:, 2]
+    dt = np.abs(c[:, None, 0] - c[None, :, 0])
+    return rank[pos[:, None], pos[None, :]] < k[dt]
+
+
 @dataclasses.dataclass
 class MaskResult:
     S: np.ndarray  # pooled logits [B,H,nb,nb]
@@ -223,7 +276,12 @@ class MaskResult:
 
 
 def build_block_mask(qbar: np.ndarray, kbar: np.ndarray, g: Geom, prm: MaskParams) -> MaskResult:
-    """Steps: reduced attention -> per-row selection (CDF or dynamic threshold) -> OR STA."""
+    """Steps: reduced attention -> per-row selection (CDF or dynamic threshold) -> OR STA.
+    Static-Ratio mode: the content-independent selection -> OR STA (qbar, kbar unused)."""
+    if prm.mode == "static":
+        sel = np.broadcast_to(static_ratio_block_mask(g, prm.gamma, prm.lam), (g.B, g.H, g.nb, g.nb)).copy()
+        sta = sta_block_mask(g, prm.sta)
+        return MaskResult(S=None, Pm=None, sel=sel, sta=sta, mask=sel | sta, c_excl=None)
     scale = prm.pool_scale if prm.pool_scale > 0 else 1.0 / math.sqrt(g.d)
     S = pooled_logits(np.asarray(qbar, np.float64), np.asarray(kbar, np.float64), scale)
     Pm = softmax_rows(S)
@@ -245,6 +303,8 @@ def exemption_sets(res: MaskResult, prm: MaskParams, band: float = 1e-5) -> np.n
 
     CDF mode: |C_excl - thr| <= band. Dynamic mode: |S_ij - (max_j S_ij - tau)| <= band.
     """
+    if prm.mode == "static":
+        return np.zeros(res.mask.shape, dtype=bool)
     if prm.mode == "cdf":
         if prm.thr >= 1.0 or prm.thr <= 0.0:
             ex = np.zeros(res.mask.shape, dtype=bool)

@@ -436,6 +436,65 @@ def test_p14_backward_given_output():
     assert np.abs(pK - dK).max() > 1e-6
 
 
+# ---------------------------------------------------------------- Static-Ratio mode
+def test_p15_static_counts_hand_values():
+    """k(dt) written out by hand for 28 blocks per frame (4 x 7), gamma 1/2, lambda 0.05:
+    28, 28/2 = 14, 28/4 = 7, ceil(28/8 = 3.5) = 4, ceil(1.75) = 2, then the floor
+    ceil(28 * 0.05 = 1.4) = 2; and the limits gamma = 1 (all), gamma = lambda = 0 (own frame)."""
+    g = R.Geom(1, 1, 8, 32, 56, 64, 8)
+    assert R.static_ratio_counts(g, 0.5, 0.05).tolist() == [28, 14, 7, 4, 2, 2, 2, 2]
+    assert R.static_ratio_counts(g, 0.5, 0.0).tolist() == [28, 14, 7, 4, 2, 1, 1, 1]
+    assert R.static_ratio_counts(g, 1.0, 0.0).tolist() == [28] * 8
+    assert R.static_ratio_counts(g, 0.0, 0.0).tolist() == [28] + [0] * 7
+    assert R.static_ratio_counts(g, 0.0, 1.0).tolist() == [28] * 8
+
+
+def _nearest_bruteforce(g, i, frame, k):
+    """The k positions of `frame` nearest to block i's position, by explicit pairwise comparison."""
+    ti, rem = divmod(i, g.nbh * g.nbw)
+    hi, wi = divmod(rem, g.nbw)
+    cand = []
+    for p in range(g.nbh * g.nbw):
+        hp, wp = divmod(p, g.nbw)
+        cand.append(((hp - hi) * (hp - hi) + (wp - wi) * (wp - wi), p))
+    chosen = []
+    for _ in range(k):  # selection by repeated minimum
+        best = min(c for c in cand if c not in chosen)
+        chosen.append(best)
+    return {frame * g.nbh * g.nbw + p for _, p in chosen}
+
+
+def test_p16_static_mask_bruteforce():
+    """Every row keeps, in every key frame, exactly the k(|dt|) nearest positions."""
+    g = R.Geom(1, 1, 5, 40, 24, 64, 8)  # 5 x 3 blocks per frame, 5 frames
+    for gamma, lam in ((0.5, 0.1), (0.7, 0.0), (0.3, 0.3)):
+        m = R.static_ratio_block_mask(g, gamma, lam)
+        k = R.static_ratio_counts(g, gamma, lam)
+        F = g.nbh * g.nbw
+        for i in range(g.nb):
+            for f in range(g.T):
+                want = _nearest_bruteforce(g, i, f, int(k[abs(i // F - f)]))
+                got = {j for j in range(f * F, (f + 1) * F) if m[i, j]}
+                assert got == want, (gamma, lam, i, f)
+
+
+def test_p17_static_special_cases():
+    """gamma = 1 keeps everything; gamma = lambda = 0 keeps exactly the own frame; the mode
+    ignores the pooled vectors and ORs the STA window."""
+    g = R.Geom(1, 2, 4, 16, 24, 64, 8)
+    assert R.static_ratio_block_mask(g, 1.0, 0.0).all()
+    own = R.block_coords(g)[:, 0]
+    assert np.array_equal(R.static_ratio_block_mask(g, 0.0, 0.0), own[:, None] == own[None, :])
+    rng = np.random.default_rng(0)
+    a = R.build_block_mask(rng.standard_normal((1, 2, g.nb, 64)), rng.standard_normal((1, 2, g.nb, 64)), g,
+                           R.MaskParams(mode="static", gamma=0.4, lam=0.0, sta=(3, 3, 3)))
+    b = R.build_block_mask(np.zeros((1, 2, g.nb, 64)), np.ones((1, 2, g.nb, 64)), g,
+                           R.MaskParams(mode="static", gamma=0.4, lam=0.0, sta=(3, 3, 3)))
+    assert np.array_equal(a.mask, b.mask)
+    expect = R.static_ratio_block_mask(g, 0.4, 0.0) | R.sta_block_mask(g, (3, 3, 3))
+    assert np.array_equal(a.mask[0, 1], expect)
+
+
 # ---------------------------------------------------------------- planted mistakes
 PINS = [
     test_p1_full_threshold_is_full_attention,
@@ -458,11 +517,14 @@ PINS = [
     test_p12_backward_invariants,
     test_p13_backward_row_subsets,
     test_p14_backward_given_output,
+    test_p15_static_counts_hand_values,
+    test_p16_static_mask_bruteforce,
+    test_p17_static_special_cases,
 ]
 
 
 _ORIG = {n: getattr(R, n) for n in ("cdf_select_row", "sta_block_mask", "masked_attention_head", "reorder",
-                                    "masked_attention_backward_head")}
+                                    "masked_attention_backward_head", "static_ratio_counts")}
 
 
 def _m_sort_ascending(p):
@@ -565,6 +627,35 @@ def _bwd_flawed(flaw):
     return f
 
 
+def _m_static_chebyshev(g):
+    F = g.nbh * g.nbw
+    hp, wp = np.divmod(np.arange(F), g.nbw)
+    rank = np.empty((F, F), dtype=np.int64)
+    for p in range(F):
+        d = np.maximum(np.abs(hp - hp[p]), np.abs(wp - wp[p]))
+        rank[p, np.lexsort((np.arange(F), d))] = np.arange(F)
+    return rank
+
+
+def _m_static_tie_high(g):
+    F = g.nbh * g.nbw
+    hp, wp = np.divmod(np.arange(F), g.nbw)
+    rank = np.empty((F, F), dtype=np.int64)
+    for p in range(F):
+        d2 = (hp - hp[p]) ** 2 + (wp - wp[p]) ** 2
+        rank[p, np.lexsort((-np.arange(F), d2))] = np.arange(F)
+    return rank
+
+
+def _m_static_no_floor(g, gamma, lam):
+    return _ORIG['static_ratio_counts'](g, gamma, 0.0)
+
+
+def _m_static_decay_from_one(g, gamma, lam):
+    c = _ORIG['static_ratio_counts'](g, gamma, lam)
+    return np.concatenate([c[1:], c[-1:]])
+
+
 MUTATIONS = {
     "rank ascending": ("rank_order", _m_sort_ascending),
     "ties high index first": ("rank_order", _m_tie_high_first),
@@ -586,6 +677,10 @@ MUTATIONS = {
     "backward dK unscaled": ("masked_attention_backward_head", _bwd_flawed("dK unscaled")),
     "backward dV from dS": ("masked_attention_backward_head", _bwd_flawed("dV from dS")),
     "backward ignores the given O": ("masked_attention_backward_head", _bwd_flawed("ignores O")),
+    "static Chebyshev distance": ("static_ratio_ranks", _m_static_chebyshev),
+    "static ties high index first": ("static_ratio_ranks", _m_static_tie_high),
+    "static floor ignored": ("static_ratio_counts", _m_static_no_floor),
+    "static decay one frame early": ("static_ratio_counts", _m_static_decay_from_one),
 }
 
 
