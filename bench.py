@@ -83,7 +83,7 @@ def measure(name, steps, warmup, use_graph=False):
 
     w = WORKLOADS[name] if isinstance(name, str) else name
     geom = A.Geometry(w.B, w.H, w.T, w.Hs, w.Ws, w.d, w.P)
-    prm = A.MaskParams(mode=w.mode, thr=w.thr, tau=w.tau, sta=tuple(w.sta))
+    prm = A.MaskParams(mode=w.mode, thr=w.thr, tau=w.tau, sta=tuple(w.sta), gamma=w.gamma, lam=w.lam)
     q, k, v = make_qkv(w, device="cuda")
     run = A.NablaAttention(geom, prm, dtype=q.dtype)
     stream = torch.cuda.current_stream()
@@ -124,6 +124,34 @@ def measure(name, steps, warmup, use_graph=False):
     )
 
 
+def measure_backward(w, steps, warmup):
+    """Time abla_sparse_attn_bwd (all its passes) after one forward, on the same workload, with
+    a seeded incoming gradient. Algorithmic FLOPs: 10*64*64*d per kept block pair (S, dP, dV,
+    dK, dQ); the kernels issue 14*64*64*d (S and dP are formed once for dQ and once for dK/dV)."""
+    import torch
+    import block_sparse_attention_21_amd as A
+    from gen import make_dout, make_qkv
+
+    geom = A.Geometry(w.B, w.H, w.T, w.Hs, w.Ws, w.d, w.P)
+    prm = A.MaskParams(mode=w.mode, thr=w.thr, tau=w.tau, sta=tuple(w.sta), gamma=w.gamma, lam=w.lam)
+    q, k, v = make_qkv(w, device="cuda")
+    dout = make_dout(w.B, w.H, geom.N, w.d, seed=7, device="cuda")
+    run = A.NablaAttention(geom, prm, dtype=q.dtype, want_lse=True)
+    run(q, k, v)
+    ws = torch.empty(A.sparse_attn_bwd_workspace_bytes(geom), dtype=torch.uint8, device="cuda")
+    dq, dk, dv = (torch.empty_like(q) for _ in range(3))
+
+    def bwd():
+        A.sparse_attn_bwd(q, k, v, run.out, dout, run.lse, run.words, run.counts, run.lists, geom,
+                          dq=dq, dk=dk, dv=dv, workspace=ws)
+
+    for _ in range(warmup):
+        bwd()
+    ms = timed(bwd, steps, torch.cuda.current_stream())
+    kept = int(run.counts.sum().item())
+    return dict(kept=kept, ms=ms, alg_flops=10.0 * 64 * 64 * w.d * kept, mfma_flops=14.0 * 64 * 64 * w.d * kept)
+
+
 def cpu_baseline(r, budget_s):
     """Time the CPU oracle on a bounded sample (one head: pool + mask in full, attention on sampled
     query blocks until the budget is spent) and scale it to the whole layer."""
@@ -132,7 +160,7 @@ def cpu_baseline(r, budget_s):
 
     w = r["w"]
     g1 = R.Geom(1, 1, w.T, w.Hs, w.Ws, w.d, w.P)
-    prm = R.MaskParams(mode=w.mode, thr=w.thr, tau=w.tau, sta=tuple(w.sta))
+    prm = R.MaskParams(mode=w.mode, thr=w.thr, tau=w.tau, sta=tuple(w.sta), gamma=w.gamma, lam=w.lam)
     q, k, v = (x[0, 0].float().cpu().numpy().astype(np.float64) for x in (r["q"], r["k"], r["v"]))
     t0 = time.perf_counter()
     Qr, Kr, Vr = R.reorder(q, g1), R.reorder(k, g1), R.reorder(v, g1)
@@ -179,8 +207,10 @@ def report(args):
     gemm = 2.0 * n ** 3 / (timed(lambda: torch.matmul(a, b), 20, torch.cuda.current_stream()) * 1e-3) / 1e12
     del a, b
     cases = [WORKLOADS["tiny"], WORKLOADS["480p"], WORKLOADS["720p"], WORKLOADS["480p-dyn"],
-             WORKLOADS["480p-dyn"].with_(tau=2.0), WORKLOADS["480p-dyn"].with_(tau=8.0), WORKLOADS["long"]]
+             WORKLOADS["480p-dyn"].with_(tau=2.0), WORKLOADS["480p-dyn"].with_(tau=8.0), WORKLOADS["480p-static"],
+             WORKLOADS["long"]]
     print(f"bf16 GEMM reference (torch.matmul {n}^3): {gemm:,.0f} TFLOP/s\n")
+    fwd_attn_ms = {}
     print("| workload | mask | keep | reorder ms (TB/s) | mask ms (GB/s) | attention ms | layer ms | "
           "dense-eq TFLOP/s (layer / attn) | actual TFLOP/s | of 2.5 PF | of GEMM ref | keep per head |")
     print("|---|---|---|---|---|---|---|---|---|---|---|---|")
@@ -191,10 +221,12 @@ def report(args):
         per_head = (counts.sum(dim=-1) / (g.nb * g.nb)).flatten().cpu().tolist()
         e = 2 if w.dtype == "bf16" else 4
         pooled = g.B * g.H * g.nb * g.d * 8
-        mask_bytes = (2 * pooled + 2 * g.B * g.H * g.nb * g.nb * 8 + g.B * g.H * g.nb * (g.words + 1) * 4
-                      + r["kept"] * 4)
+        out_bytes = g.B * g.H * g.nb * (g.words + 1) * 4 + r["kept"] * 4  # words, counts, lists
+        # Scored modes also read the pooled vectors and write + read the float64 score matrix.
+        mask_bytes = out_bytes + (0 if w.mode == "static" else 2 * pooled + 2 * g.B * g.H * g.nb * g.nb * 8)
         attn_tf = r["kept_flops"] / (r["ms_attn"] * 1e-3) / 1e12
-        mode = f"cdf {w.thr}" if w.mode == "cdf" else f"dyn tau={w.tau}"
+        mode = {"cdf": f"cdf {w.thr}", "dyn": f"dyn tau={w.tau}",
+                "static": f"static gamma={w.gamma} lambda={w.lam}"}[w.mode]
         heads = ", ".join(f"{x:.3f}" for x in per_head[:12]) + (" ..." if len(per_head) > 12 else "")
         print(f"| {w.name} ({w.dtype}, {w.N} tok) | {mode} | {r['keep_fraction']:.4f} | "
               f"{r['ms_reorder']:.4f} ({r['reorder_gbs'] / 1e3:.2f}) | {r['ms_mask']:.4f} "
@@ -202,7 +234,22 @@ def report(args):
               f"{r['dense_flops'] / (r['ms_step'] * 1e-3) / 1e12:,.1f} / "
               f"{r['dense_flops'] / (r['ms_attn'] * 1e-3) / 1e12:,.1f} | {attn_tf:,.1f} | "
               f"{attn_tf / MFMA_BF16_PEAK_TFLOPS:.3f} | {attn_tf / gemm:.3f} | {heads} |", flush=True)
+        fwd_attn_ms[w.name + (f"-tau{w.tau}" if w.mode == "dyn" else "")] = r["ms_attn"]
         del r
+    print("\nBackward (abla_sparse_attn_bwd, every pass: 7 fractal copies, D / column lists, dQ, dK+dV), "
+          "bf16 workloads:\n")
+    print("| workload | keep | backward ms | algorithmic TFLOP/s (10*64^2*d per kept pair) | of 2.5 PF | "
+          "issued MFMA TFLOP/s (14*64^2*d) | backward / forward attention |")
+    print("|---|---|---|---|---|---|---|")
+    for w in cases:
+        if w.dtype != "bf16":
+            continue
+        b = measure_backward(w, args.steps, args.warmup)
+        key = w.name + (f"-tau{w.tau}" if w.mode == "dyn" else "")
+        alg = b["alg_flops"] / (b["ms"] * 1e-3) / 1e12
+        print(f"| {key} | {b['kept'] / (w.B * w.H * w.nb * w.nb):.4f} | {b['ms']:.3f} | {alg:,.1f} | "
+              f"{alg / MFMA_BF16_PEAK_TFLOPS:.3f} | {b['mfma_flops'] / (b['ms'] * 1e-3) / 1e12:,.1f} | "
+              f"{b['ms'] / fwd_attn_ms[key]:.2f} |", flush=True)
 
 
 def traffic_for(path, name):

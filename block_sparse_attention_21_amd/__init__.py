@@ -21,7 +21,7 @@ _LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libabla.so
 OK, ERR_INVALID, ERR_UNSUPPORTED, ERR_WORKSPACE, ERR_HIP = range(5)
 F32, BF16 = 0, 1
 LAYOUT_TOKENS, LAYOUT_BLOCK_T = 0, 1
-MASK_CDF, MASK_DYN = 0, 1
+MASK_CDF, MASK_DYN, MASK_STATIC = 0, 1, 2
 CUT_RADIX, CUT_BITONIC = 0, 1
 
 
@@ -39,7 +39,8 @@ class _Geom(ctypes.Structure):
 class _MaskParams(ctypes.Structure):
     _fields_ = [("mode", ctypes.c_int32), ("thr", ctypes.c_double), ("tau", ctypes.c_double),
                 ("pool_scale", ctypes.c_double), ("sta_t", ctypes.c_int32), ("sta_h", ctypes.c_int32),
-                ("sta_w", ctypes.c_int32), ("cut", ctypes.c_int32)]
+                ("sta_w", ctypes.c_int32), ("cut", ctypes.c_int32), ("gamma", ctypes.c_double),
+                ("lam", ctypes.c_double)]
 
 
 def _load():
@@ -109,8 +110,9 @@ class Geometry:
 
 @dataclasses.dataclass(frozen=True)
 class MaskParams:
-    """mode 'cdf' (thr) or 'dyn' (tau); pool_scale 0 -> 1/sqrt(d); sta (0,0,0) -> no sliding-tile window;
-    cut 'radix' (default) or 'bitonic' (how the CDF cut is found; same result)."""
+    """mode 'cdf' (thr), 'dyn' (tau) or 'static' (gamma, lam: retention decay per frame of
+    distance and its long-range floor); pool_scale 0 -> 1/sqrt(d); sta (0,0,0) -> no sliding-tile
+    window; cut 'radix' (default) or 'bitonic' (how the CDF cut is found; same result)."""
 
     mode: str = "cdf"
     thr: float = 0.9
@@ -118,11 +120,14 @@ class MaskParams:
     pool_scale: float = 0.0
     sta: tuple = (3, 3, 3)
     cut: str = "radix"
+    gamma: float = 0.5
+    lam: float = 0.05
 
     def c(self) -> _MaskParams:
-        mode = {"cdf": MASK_CDF, "dyn": MASK_DYN}.get(self.mode, -1) if isinstance(self.mode, str) else self.mode
+        modes = {"cdf": MASK_CDF, "dyn": MASK_DYN, "static": MASK_STATIC}
+        mode = modes.get(self.mode, -1) if isinstance(self.mode, str) else self.mode
         cut = {"radix": CUT_RADIX, "bitonic": CUT_BITONIC}.get(self.cut, -1) if isinstance(self.cut, str) else self.cut
-        return _MaskParams(mode, self.thr, self.tau, self.pool_scale, *self.sta, cut)
+        return _MaskParams(mode, self.thr, self.tau, self.pool_scale, *self.sta, cut, self.gamma, self.lam)
 
 
 _DT = {torch.float32: F32, torch.bfloat16: BF16}
@@ -213,12 +218,13 @@ def build_mask(qbar: torch.Tensor, kbar: torch.Tensor, geom: Geometry, params: M
     _need(counts, "counts", (geom.B, geom.H, geom.nb), torch.int32, dev)
     if lists is not None:
         _need(lists, "lists", (geom.B, geom.H, geom.nb, geom.nb), torch.int32, dev)
-    nbytes = build_mask_workspace_bytes(geom)
-    if workspace is None:
-        workspace = torch.empty(max(nbytes, 1), dtype=torch.uint8, device=dev)
+    scored = params.mode != "static"
+    if workspace is None and scored:
+        workspace = torch.empty(max(build_mask_workspace_bytes(geom), 1), dtype=torch.uint8, device=dev)
     g, p = geom.c(), params.c()
     _check(_lib.abla_build_mask(ctypes.byref(g), ctypes.byref(p), _ptr(qbar), _ptr(kbar), _ptr(words),
-                                _ptr(counts), _ptr(lists), _ptr(workspace), workspace.numel(), _stream(qbar)),
+                                _ptr(counts), _ptr(lists), _ptr(workspace),
+                                0 if workspace is None else workspace.numel(), _stream(qbar)),
            "abla_build_mask")
     return words, counts, lists
 
@@ -314,7 +320,8 @@ class NablaAttention:
         self.lists = torch.empty((g.B, g.H, g.nb, g.nb), dtype=torch.int32, device=dev)
         self.out = torch.empty(tok, dtype=dtype, device=dev)
         self.lse = torch.empty((g.B, g.H, g.N), dtype=torch.float32, device=dev) if want_lse else None
-        self.ws_mask = torch.empty(max(build_mask_workspace_bytes(g), 1), dtype=torch.uint8, device=dev)
+        self.ws_mask = (None if params.mode == "static" else
+                        torch.empty(max(build_mask_workspace_bytes(g), 1), dtype=torch.uint8, device=dev))
         self.ws_attn = torch.empty(max(sparse_attn_workspace_bytes(g), 1), dtype=torch.uint8, device=dev)
 
     def reorder_pool(self, q, k, v):

@@ -119,14 +119,18 @@ abla_status abla_build_mask(const abla_geom* g, const abla_mask_params* p, const
                             size_t workspace_bytes, void* stream) {
   abla_status st = check_geom(g);
   if (st != ABLA_OK) return st;
-  if (!p || !qbar || !kbar || !mask_words || !counts) return ABLA_ERR_INVALID;
-  if (p->mode != ABLA_MASK_CDF && p->mode != ABLA_MASK_DYN) return ABLA_ERR_INVALID;
+  if (!p || !mask_words || !counts) return ABLA_ERR_INVALID;
+  if (p->mode != ABLA_MASK_CDF && p->mode != ABLA_MASK_DYN && p->mode != ABLA_MASK_STATIC) return ABLA_ERR_INVALID;
+  const bool scored = p->mode != ABLA_MASK_STATIC;
+  if (scored && (!qbar || !kbar)) return ABLA_ERR_INVALID;
+  if (!scored && !(p->gamma >= 0.0 && p->gamma <= 1.0 && p->lambda >= 0.0 && p->lambda <= 1.0))
+    return ABLA_ERR_INVALID;  // also rejects NaN
   if (p->cut != ABLA_CUT_RADIX && p->cut != ABLA_CUT_BITONIC) return ABLA_ERR_INVALID;
   if (isnan(p->thr) || isnan(p->tau) || isnan(p->pool_scale) || p->pool_scale < 0.0 || isinf(p->pool_scale))
     return ABLA_ERR_INVALID;
   if (!window_ok(p->sta_t, p->sta_h, p->sta_w)) return ABLA_ERR_INVALID;
   if (nb_of(g) > kMaxBlocks) return ABLA_ERR_UNSUPPORTED;
-  if (!workspace || workspace_bytes < abla_build_mask_workspace_bytes(g)) return ABLA_ERR_WORKSPACE;
+  if (scored && (!workspace || workspace_bytes < abla_build_mask_workspace_bytes(g))) return ABLA_ERR_WORKSPACE;
   return from_hip(launch_build_mask(make_kgeom(*g), *p, qbar, kbar, mask_words, counts, lists,
                                     static_cast<double*>(workspace), (hipStream_t)stream));
 }

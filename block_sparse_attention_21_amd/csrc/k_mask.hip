@@ -6,7 +6,8 @@
 // blocks needed for the row's cumulative probability to reach thr are kept,
 // per head and per input), hybrid with STA (M = M_nabla OR M_STA).
 // DynamicRad, Methodology A, Dynamic-Threshold mode: the pre-softmax logits
-// serve as importance and are filtered by a threshold.
+// serve as importance and are filtered by a threshold; Static-Ratio mode: no
+// scores, a share of each key frame's blocks fixed by temporal distance.
 //
 // Two kernels:
 //  k_scores  S = pool_scale * Qbar Kbar^T per (b, h), a float64 matrix-core
@@ -116,7 +117,7 @@ constexpr int kSelThreads = 256;
 constexpr int kWaves = kSelThreads / 64;
 
 struct SelArgs {
-  int mode;        // ABLA_MASK_CDF / ABLA_MASK_DYN
+  int mode;        // ABLA_MASK_CDF / ABLA_MASK_DYN / ABLA_MASK_STATIC
   int cut;         // ABLA_CUT_RADIX / ABLA_CUT_BITONIC
   int cdf_all;     // thr >= 1
   int cdf_none;    // thr <= 0
@@ -125,6 +126,8 @@ struct SelArgs {
   int sta_on, rt, rh, rw;
   int np;          // bitonic size: power of two >= nb
   int W;           // words per row
+  double gamma;    // STATIC: retention decay per frame of distance
+  int floor_k;     // STATIC: ceil(F * lambda), F = blocks per frame
 };
 
 __device__ __forceinline__ double wave_max(double v) {
@@ -293,12 +296,13 @@ __global__ __launch_bounds__(kSelThreads) void k_select(const double* __restrict
   const int i = (int)(row % nb);
   const double* Srow = S + row * nb;
 
+  const bool scored = a.mode != ABLA_MASK_STATIC;
   double s[NPT];
   double mx = -INFINITY;
 #pragma unroll
   for (int k = 0; k < NPT; ++k) {
     const int j = t + kSelThreads * k;
-    s[k] = j < nb ? Srow[j] : -INFINITY;
+    s[k] = (scored && j < nb) ? Srow[j] : -INFINITY;
     mx = fmax(mx, s[k]);
   }
   mx = wave_max(mx);
@@ -310,7 +314,44 @@ __global__ __launch_bounds__(kSelThreads) void k_select(const double* __restrict
   __syncthreads();
 
   bool keep[NPT];
-  if (a.mode == ABLA_MASK_DYN) {
+  if (a.mode == ABLA_MASK_STATIC) {
+    // DynamicRad Static-Ratio: per frame position p, its rank around block i's position
+    // (squared block distance, then index), and k(dt) per frame distance; keep j iff its
+    // position's rank is below k(|t_j - t_i|). Both tables live in the key scratch
+    // (F + T <= 2 nb ints).
+    const int F = g.nbh * g.nbw;
+    int* rank_s = reinterpret_cast<int*>(keys);
+    int* kc_s = rank_s + F;
+    const int ti = i / F, pi = i - ti * F;
+    const int hi = pi / g.nbw, wi = pi - hi * g.nbw;
+    for (int p = t; p < F; p += kSelThreads) {
+      const int hp = p / g.nbw, wp = p - hp * g.nbw;
+      const int d2p = (hp - hi) * (hp - hi) + (wp - wi) * (wp - wi);
+      int r = 0;
+      for (int q = 0; q < F; ++q) {
+        const int hq = q / g.nbw, wq = q - hq * g.nbw;
+        const int d2q = (hq - hi) * (hq - hi) + (wq - wi) * (wq - wi);
+        r += (d2q < d2p) || (d2q == d2p && q < p);
+      }
+      rank_s[p] = r;
+    }
+    for (int dt = t; dt < g.T; dt += kSelThreads) {
+      double ratio = 1.0;
+      for (int k = 0; k < dt; ++k) ratio = ratio * a.gamma;  // the float64 products of the definition
+      kc_s[dt] = min(F, max(a.floor_k, (int)ceil((double)F * ratio)));
+    }
+    __syncthreads();
+#pragma unroll
+    for (int k = 0; k < NPT; ++k) {
+      const int j = t + kSelThreads * k;
+      if (j < nb) {
+        const int tj = j / F;
+        keep[k] = rank_s[j - tj * F] < kc_s[abs(tj - ti)];
+      } else {
+        keep[k] = false;
+      }
+    }
+  } else if (a.mode == ABLA_MASK_DYN) {
     const double edge = mx - a.tau;
 #pragma unroll
     for (int k = 0; k < NPT; ++k) keep[k] = (t + kSelThreads * k < nb) && s[k] >= edge;
@@ -472,18 +513,20 @@ void launch_select(const KGeom& g, const double* S, uint32_t* words, int32_t* co
 
 hipError_t launch_build_mask(const KGeom& g, const abla_mask_params& p, const double* qbar, const double* kbar,
                              uint32_t* words, int32_t* counts, int32_t* lists, double* scores, hipStream_t s) {
-  const double scale = p.pool_scale > 0.0 ? p.pool_scale : 1.0 / sqrt((double)g.d);
-  // 128 x 128 tiles when they fill the GPU several times over, else 64 x 64.
-  const long long t128 = (g.nb + 127) / 128;
-  if (t128 * t128 * g.B * g.H >= 2048) {
-    k_scores<128><<<dim3((unsigned)t128, (unsigned)t128, (unsigned)(g.B * g.H)), 256, 0, s>>>(qbar, kbar, scores,
-                                                                                           g.nb, g.d, scale);
-  } else {
-    const unsigned t64 = (unsigned)((g.nb + 63) / 64);
-    k_scores<64><<<dim3(t64, t64, (unsigned)(g.B * g.H)), 256, 0, s>>>(qbar, kbar, scores, g.nb, g.d, scale);
+  if (p.mode != ABLA_MASK_STATIC) {
+    const double scale = p.pool_scale > 0.0 ? p.pool_scale : 1.0 / sqrt((double)g.d);
+    // 128 x 128 tiles when they fill the GPU several times over, else 64 x 64.
+    const long long t128 = (g.nb + 127) / 128;
+    if (t128 * t128 * g.B * g.H >= 2048) {
+      k_scores<128><<<dim3((unsigned)t128, (unsigned)t128, (unsigned)(g.B * g.H)), 256, 0, s>>>(qbar, kbar, scores,
+                                                                                             g.nb, g.d, scale);
+    } else {
+      const unsigned t64 = (unsigned)((g.nb + 63) / 64);
+      k_scores<64><<<dim3(t64, t64, (unsigned)(g.B * g.H)), 256, 0, s>>>(qbar, kbar, scores, g.nb, g.d, scale);
+    }
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
   }
-  hipError_t e = hipGetLastError();
-  if (e != hipSuccess) return e;
 
   SelArgs a{};
   a.mode = p.mode;
@@ -503,6 +546,8 @@ hipError_t launch_build_mask(const KGeom& g, const abla_mask_params& p, const do
   while (np < g.nb) np <<= 1;
   a.np = np;
   a.W = (g.nb + 31) / 32;
+  a.gamma = p.gamma;
+  a.floor_k = (int)ceil((double)(g.nbh * g.nbw) * p.lambda);
   if (np <= 256)
     launch_select<1>(g, scores, words, counts, lists, a, s);
   else if (np <= 512)

@@ -43,9 +43,11 @@ class Workload:
     rho: float = 0.0  # lag-1 temporal correlation (video recipe)
     copy_frac: float = 0.0  # fraction of blocks overwritten by a distant block (video recipe)
     qk_noise: float = 0.0  # std of independent noise added to Q and K before normalisation
-    mode: str = "cdf"  # "cdf" or "dyn"
+    mode: str = "cdf"  # "cdf", "dyn" or "static"
     thr: float = 0.0
     tau: float = 0.0
+    gamma: float = 0.5  # static mode: retention decay per frame of distance
+    lam: float = 0.05  # static mode: long-range floor of the retention ratio
     sta: tuple = (3, 3, 3)
     seed: int = 0
 
@@ -61,8 +63,9 @@ class Workload:
         return dataclasses.replace(self, **kw)
 
 
-# The five workloads. Geometry, dtype and mask parameters are fixed by the
-# benchmark definition; the field recipe is the reading written up in the design notes.
+# The five benchmark workloads (geometry, dtype and mask parameters fixed by the benchmark
+# definition; the field recipe is the reading written up in the design notes), plus
+# 480p-static: the 480p geometry under the DynamicRad Static-Ratio mask.
 WORKLOADS = {
     "tiny": Workload("tiny", B=1, H=2, d=64, T=8, Hs=16, Ws=16, P=8, dtype="f32",
                      recipe="tiny", sigma=2.0, qk_noise=0.3, mode="cdf", thr=0.8),
@@ -72,6 +75,9 @@ WORKLOADS = {
                      recipe="video", sigma=3.0, rho=0.9, copy_frac=0.05, mode="cdf", thr=0.9),
     "480p-dyn": Workload("480p-dyn", B=1, H=12, d=128, T=21, Hs=32, Ws=56, P=8, dtype="bf16",
                          recipe="video", sigma=3.0, rho=0.9, copy_frac=0.05, mode="dyn", tau=4.0),
+    "480p-static": Workload("480p-static", B=1, H=12, d=128, T=21, Hs=32, Ws=56, P=8, dtype="bf16",
+                            recipe="video", sigma=3.0, rho=0.9, copy_frac=0.05, mode="static", gamma=0.5,
+                            lam=0.05),
     "long": Workload("long", B=1, H=12, d=128, T=105, Hs=32, Ws=56, P=8, dtype="bf16",
                      recipe="video", sigma=3.0, rho=0.95, copy_frac=0.05, mode="cdf", thr=0.9),
 }

@@ -67,7 +67,7 @@ typedef struct {
   int32_t P;
 } abla_geom;
 
-typedef enum { ABLA_MASK_CDF = 0, ABLA_MASK_DYN = 1 } abla_mask_mode;
+typedef enum { ABLA_MASK_CDF = 0, ABLA_MASK_DYN = 1, ABLA_MASK_STATIC = 2 } abla_mask_mode;
 
 /* How the CDF cut finds the last kept rank of a row. Both give the same bits.
  * ABLA_CUT_RADIX:   radix select on the 64-bit (probability, ~index) keys with exact
@@ -82,6 +82,8 @@ typedef struct {
   double pool_scale;  /* scale of the pooled logits; 0 means 1/sqrt(d) */
   int32_t sta_t, sta_h, sta_w; /* sliding-tile window in blocks, odd; all 0 = no STA */
   int32_t cut;        /* abla_cut_algorithm (CDF mode) */
+  double gamma;       /* STATIC mode: retention decay per frame of temporal distance, in [0, 1] */
+  double lambda;      /* STATIC mode: long-range floor of the retention ratio, in [0, 1] */
 } abla_mask_params;
 
 /* Fractal reordering and block mean-pooling of one tensor.
@@ -103,7 +105,8 @@ typedef struct {
 abla_status abla_reorder(const abla_geom* g, int32_t dtype, int32_t inverse, int32_t layout,
                          const void* x, void* y, double* pooled, void* stream);
 
-/* Bytes of scratch abla_build_mask needs: B*H*nb*nb*8 (the float64 pooled score matrix). */
+/* Bytes of scratch abla_build_mask needs: B*H*nb*nb*8 (the float64 pooled score matrix;
+ * not used by the STATIC mode). */
 size_t abla_build_mask_workspace_bytes(const abla_geom* g);
 
 /* Block mask from pooled Q and K.
@@ -111,13 +114,22 @@ size_t abla_build_mask_workspace_bytes(const abla_geom* g);
  * scores), "CDF thresholding" (rank each row, keep the blocks needed for the
  * row's cumulative probability to reach thr), hybrid with STA
  * (M = M_nabla OR M_STA); DynamicRad, Methodology A -- Dynamic-Threshold mode
- * (pre-softmax logits filtered by a threshold).
+ * (pre-softmax logits filtered by a threshold) and Static-Ratio mode (no content
+ * scoring; a retention ratio fixed by temporal distance, decay gamma, long-range
+ * factor lambda).
  *
- * qbar, kbar: [B,H,nb,d] float64 (as written by abla_reorder).
+ * qbar, kbar: [B,H,nb,d] float64 (as written by abla_reorder); not read, and may be
+ * NULL, in STATIC mode.
  * Per row (b,h,i): S_ij = pool_scale * <qbar_i, kbar_j>, all in float64.
  *   CDF: P_i. = softmax(S_i.); rank blocks by (P desc, index asc); keep the
  *        block at rank r iff the mass ranked before it is < thr.
  *   DYN: keep j iff S_ij >= max_j S_ij - tau.
+ *   STATIC (no scores; the pages name gamma and lambda but give no law, this is the
+ *        one implemented): with F = nbh*nbw blocks per frame, r(0) = 1 and
+ *        r(dt) = r(dt-1) * gamma (float64 products), a key frame at frame distance
+ *        dt = |t_i - t_j| keeps k(dt) = min(F, max(ceil(F*lambda), ceil(F*r(dt))))
+ *        blocks: the ones nearest to block i's position (hp, wp), ordered by squared
+ *        distance in blocks, ties by lower position index. Identical for every (b, h).
  *   Then OR the STA window: |t_i-t_j| <= (sta_t-1)/2 and likewise for hp, wp.
  * Outputs:
  *   mask_words [B,H,nb,ceil(nb/32)] uint32: bit j%32 of word j/32 (LSB first)
@@ -126,9 +138,11 @@ size_t abla_build_mask_workspace_bytes(const abla_geom* g);
  *   lists      [B,H,nb,nb] int32 or NULL: the kept block indices of each row in
  *              ascending order in the first counts[row] entries; the rest of
  *              the row is left untouched.
- * workspace: at least abla_build_mask_workspace_bytes(g) bytes of device memory.
+ * workspace: at least abla_build_mask_workspace_bytes(g) bytes of device memory (may be
+ * NULL in STATIC mode).
  * Errors: INVALID for null inputs/outputs, unknown mode or cut algorithm, NaN thr/tau, negative
- * or NaN pool_scale, windows that are even, negative or partly zero;
+ * or NaN pool_scale, gamma or lambda outside [0, 1] in STATIC mode, windows that are even,
+ * negative or partly zero;
  * UNSUPPORTED for nb > 4096 or the geometry limits of abla_reorder;
  * WORKSPACE if the workspace is missing or too small. */
 abla_status abla_build_mask(const abla_geom* g, const abla_mask_params* p,

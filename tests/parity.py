@@ -30,7 +30,8 @@ def geoms(B, H, T, Hs, Ws, d, P=8):
 
 
 def oracle_params(p) -> R.MaskParams:
-    return R.MaskParams(mode=p.mode, thr=p.thr, tau=p.tau, pool_scale=p.pool_scale, sta=tuple(p.sta))
+    return R.MaskParams(mode=p.mode, thr=p.thr, tau=p.tau, pool_scale=p.pool_scale, sta=tuple(p.sta),
+                        gamma=p.gamma, lam=p.lam)
 
 
 def host_words(words: torch.Tensor) -> np.ndarray:

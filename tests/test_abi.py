@@ -81,6 +81,8 @@ def mask_call(A, g, p, ws=FAKE, ws_bytes=1 << 40, q=FAKE, k=FAKE, words=FAKE2, c
     (dict(mode=5), 1), (dict(cut=3), 1), (dict(thr=math.nan), 1), (dict(tau=math.nan), 1), (dict(pool_scale=-1.0), 1),
     (dict(pool_scale=math.nan), 1), (dict(pool_scale=math.inf), 1),
     (dict(sta=(2, 3, 3)), 1), (dict(sta=(3, 0, 3)), 1), (dict(sta=(-1, 3, 3)), 1), (dict(sta=(3, 3, 4)), 1),
+    (dict(mode="static", gamma=-0.1), 1), (dict(mode="static", gamma=1.5), 1), (dict(mode="static", gamma=math.nan), 1),
+    (dict(mode="static", lam=math.nan), 1), (dict(mode="static", lam=2.0), 1), (dict(mode="static", lam=-1e-9), 1),
 ])
 def test_mask_param_errors(A, kw, code):
     p = A.MaskParams(**kw).c()
@@ -98,6 +100,11 @@ def test_mask_pointer_workspace_and_size_errors(A):
     big = G(A, T=4097, Hs=8, Ws=8)  # nb = 4097 > one LDS-resident row
     assert mask_call(A, big, p) == 2
     assert A._lib.abla_build_mask_workspace_bytes(ctypes.byref(G(A, d=96))) == 0
+    # The static mode reads no pooled vectors and no workspace: with those NULL it gets as far
+    # as the size check.
+    st = A.MaskParams(mode="static").c()
+    assert mask_call(A, big, st, q=None, k=None, ws=None, ws_bytes=0) == 2
+    assert mask_call(A, g, st, q=None, counts=None, ws=None) == 1
 
 
 def attn_call(A, g, dtype=1, scale=0.0, q=FAKE, k=ctypes.c_void_p(0x20000), v=ctypes.c_void_p(0x30000),

@@ -77,6 +77,9 @@ SMALL = [
     ("one-block", "bf16", 128, (1, 2, 1, 8, 8), dict(mode="cdf", thr=0.5)),
     ("nb-300", "bf16", 64, (1, 1, 3, 80, 80), dict(mode="cdf", thr=0.95)),  # 2 keys/thread in the select
     ("nb-600", "bf16", 64, (1, 1, 6, 80, 80), dict(mode="cdf", thr=0.95, sta=(0, 0, 0))),
+    ("static", "bf16", 128, (1, 2, 5, 24, 40), dict(mode="static", gamma=0.5, lam=0.1)),
+    ("static-f32-no-sta", "f32", 64, (1, 1, 6, 16, 24), dict(mode="static", gamma=0.3, lam=0.0, sta=(0, 0, 0))),
+    ("static-gamma1", "bf16", 64, (1, 1, 3, 16, 16), dict(mode="static", gamma=1.0, lam=0.0)),
 ]
 
 
@@ -186,7 +189,7 @@ def test_binding_errors_on_device(A):
 def _workload(A, name, **over):
     w = WORKLOADS[name].with_(**over) if over else WORKLOADS[name]
     geom, og = PT.geoms(w.B, w.H, w.T, w.Hs, w.Ws, w.d, w.P)
-    prm = A.MaskParams(mode=w.mode, thr=w.thr, tau=w.tau, sta=tuple(w.sta))
+    prm = A.MaskParams(mode=w.mode, thr=w.thr, tau=w.tau, sta=tuple(w.sta), gamma=w.gamma, lam=w.lam)
     q, k, v = make_qkv(w, device=DEV)
     run = A.NablaAttention(geom, prm, dtype=q.dtype, want_lse=True)
     run(q, k, v)
@@ -241,7 +244,7 @@ def test_workload_tiny(A):
     print(f"tiny: keep {rep.kept / rep.total:.4f}, max|dO| {max_abs:.2e}")
 
 
-@pytest.mark.parametrize("name", ["480p", "480p-dyn", "720p", "long"])
+@pytest.mark.parametrize("name", ["480p", "480p-dyn", "480p-static", "720p", "long"])
 def test_workload_full_size(A, name):
     w, geom, og, prm, q, k, v, run = _workload(A, name)
     mres, rep = _check_workload_mask(A, w, og, prm, q, k, run)
@@ -259,6 +262,32 @@ def test_maximum_blocks_per_row(A):
     max_abs, rel = _check_workload_attention(w, og, q, k, v, run, n_heads=1)
     print(f"max-nb: keep {rep.kept / rep.total:.4f}, band diffs {rep.exempt_diff}, "
           f"max|dO| {max_abs:.2e}, rel {rel:.2e}")
+
+
+@pytest.mark.parametrize("name,over", [
+    ("720p", {}), ("long", dict(gamma=0.7, lam=0.02)), ("480p", dict(H=1, T=16, Hs=128, Ws=128, d=64)),
+])
+def test_static_masks_bit_exact(A, name, over):
+    """The Static-Ratio mask has no floating-point decision near a threshold: bit-exact against
+    the oracle at full size (720p, the long clip, and nb = 4096), identical for every head."""
+    w = WORKLOADS[name].with_(mode="static", **over)
+    geom, og = PT.geoms(w.B, w.H, w.T, w.Hs, w.Ws, w.d, w.P)
+    prm = A.MaskParams(mode="static", sta=tuple(w.sta), gamma=w.gamma, lam=w.lam)
+    # The static mode reads no pooled vectors: zeros stand in for them.
+    qbar = torch.zeros((w.B, w.H, geom.nb, w.d), dtype=torch.float64, device=DEV)
+    words, counts, lists = A.build_mask(qbar, qbar, geom, prm)
+    torch.cuda.synchronize()
+    op = PT.oracle_params(prm)
+    gh = R.Geom(1, 1, og.T, og.Hs, og.Ws, og.d, og.P)
+    mres = R.build_block_mask(np.zeros((1, 1, og.nb, 1)), np.zeros((1, 1, og.nb, 1)), gh, op)
+    gm = PT.gpu_mask(words, og)
+    assert np.array_equal(gm, np.broadcast_to(mres.mask[0, 0], gm.shape))
+    c = counts.cpu().numpy()
+    assert np.array_equal(c, gm.sum(-1))
+    L = lists[0, 0].cpu().numpy()
+    for i in range(0, og.nb, max(1, og.nb // 64)):
+        assert np.array_equal(L[i][: c[0, 0, i]], np.nonzero(gm[0, 0, i])[0])
+    print(f"static {name} {over}: nb {og.nb}, keep {gm.mean():.4f}")
 
 
 @pytest.mark.parametrize("tau", [2.0, 8.0])

@@ -246,7 +246,7 @@ def _setup_480p(A):
     geom, og = PT.geoms(w.B, w.H, w.T, w.Hs, w.Ws, w.d, w.P)
     q, k, v = make_qkv(w, device=DEV)
     dout = make_dout(w.B, w.H, geom.N, w.d, seed=7, device=DEV)
-    run = A.NablaAttention(geom, A.MaskParams(mode=w.mode, thr=w.thr, tau=w.tau, sta=tuple(w.sta)),
+    run = A.NablaAttention(geom, A.MaskParams(mode=w.mode, thr=w.thr, tau=w.tau, sta=tuple(w.sta), gamma=w.gamma, lam=w.lam),
                            want_lse=True)
     run(q, k, v)
     torch.cuda.synchronize()
