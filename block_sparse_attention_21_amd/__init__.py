@@ -22,6 +22,7 @@ OK, ERR_INVALID, ERR_UNSUPPORTED, ERR_WORKSPACE, ERR_HIP = range(5)
 F32, BF16 = 0, 1
 LAYOUT_TOKENS, LAYOUT_BLOCK_T = 0, 1
 MASK_CDF, MASK_DYN, MASK_STATIC = 0, 1, 2
+ATTN_OUT_ORIGINAL, ATTN_QK_ORIGINAL = 1, 2
 CUT_RADIX, CUT_BITONIC = 0, 1
 
 
@@ -168,17 +169,23 @@ def _device(x: torch.Tensor) -> torch.device:
 # ---------------------------------------------------------------- entry points
 def reorder(x: torch.Tensor, geom: Geometry, *, inverse: bool = False, layout: str = "tokens",
             out: Optional[torch.Tensor] = None, pooled: Optional[torch.Tensor] = None,
-            want_pooled: bool = False):
-    """abla_reorder. Returns y (and the float64 pooled block means if requested)."""
+            want_pooled: bool = False, pool_only: bool = False):
+    """abla_reorder. Returns y (and the float64 pooled block means if requested). With
+    pool_only the tensor is not reordered and only the pooled means are returned."""
     dev = _device(x)
     if x.dtype not in _DT:
         raise ValueError(f"unsupported dtype {x.dtype}")
     _need(x, "x", (geom.B, geom.H, geom.N, geom.d), x.dtype, dev)
     lay = {"tokens": LAYOUT_TOKENS, "block_t": LAYOUT_BLOCK_T}[layout]
     yshape = (geom.B, geom.H, geom.N, geom.d) if lay == LAYOUT_TOKENS else (geom.B, geom.H, geom.nb, geom.d, 64)
-    if out is None:
+    if pool_only:
+        if inverse or lay != LAYOUT_TOKENS or out is not None:
+            raise ValueError("pool_only takes the forward token layout and no output tensor")
+        want_pooled = True
+    elif out is None:
         out = torch.empty(yshape, dtype=x.dtype, device=dev)
-    _need(out, "out", yshape, x.dtype, dev)
+    if out is not None:
+        _need(out, "out", yshape, x.dtype, dev)
     if want_pooled and pooled is None:
         pooled = torch.empty((geom.B, geom.H, geom.nb, geom.d), dtype=torch.float64, device=dev)
     if pooled is not None:
@@ -186,6 +193,8 @@ def reorder(x: torch.Tensor, geom: Geometry, *, inverse: bool = False, layout: s
     g = geom.c()
     _check(_lib.abla_reorder(ctypes.byref(g), _DT[x.dtype], int(inverse), lay, _ptr(x), _ptr(out), _ptr(pooled),
                              _stream(x)), "abla_reorder")
+    if pool_only:
+        return pooled
     return (out, pooled) if pooled is not None else out
 
 
@@ -231,9 +240,11 @@ def build_mask(qbar: torch.Tensor, kbar: torch.Tensor, geom: Geometry, params: M
 
 def sparse_attn_fwd(q_r: torch.Tensor, k_r: torch.Tensor, v_rt: torch.Tensor, counts: torch.Tensor,
                     lists: torch.Tensor, geom: Geometry, *, scale: float = 0.0, out_original_order: bool = True,
-                    out: Optional[torch.Tensor] = None, lse: Optional[torch.Tensor] = None, want_lse: bool = False,
+                    qk_original_order: bool = False, out: Optional[torch.Tensor] = None,
+                    lse: Optional[torch.Tensor] = None, want_lse: bool = False,
                     workspace: Optional[torch.Tensor] = None):
-    """abla_sparse_attn_fwd. Returns out (and lse if requested)."""
+    """abla_sparse_attn_fwd. Returns out (and lse if requested). With qk_original_order, q_r and k_r
+    are the caller's Q and K in the original token order (no reordered copies needed)."""
     dev = _device(q_r)
     dt = q_r.dtype
     if dt not in _DT:
@@ -255,8 +266,9 @@ def sparse_attn_fwd(q_r: torch.Tensor, k_r: torch.Tensor, v_rt: torch.Tensor, co
     if workspace is None:
         workspace = torch.empty(max(nbytes, 1), dtype=torch.uint8, device=dev)
     g = geom.c()
+    flags = (ATTN_OUT_ORIGINAL if out_original_order else 0) | (ATTN_QK_ORIGINAL if qk_original_order else 0)
     _check(_lib.abla_sparse_attn_fwd(ctypes.byref(g), _DT[dt], float(scale), _ptr(q_r), _ptr(k_r), _ptr(v_rt),
-                                     _ptr(counts), _ptr(lists), _ptr(out), int(out_original_order), _ptr(lse),
+                                     _ptr(counts), _ptr(lists), _ptr(out), flags, _ptr(lse),
                                      _ptr(workspace), workspace.numel(), _stream(q_r)), "abla_sparse_attn_fwd")
     return (out, lse) if lse is not None else out
 
@@ -298,20 +310,23 @@ def sparse_attn_bwd(q, k, v, o, dout, lse, words, counts, lists, geom: Geometry,
 class NablaAttention:
     """The whole forward path for one geometry, with every buffer allocated once.
 
-    __call__(q, k, v) runs: reorder Q (+pool), reorder K (+pool), reorder V
-    (channel-major blocks), build the mask, block-sparse attention writing the
-    output in the original token order. Intermediate results stay available as
-    attributes (q_r, k_r, v_rt, qbar, kbar, words, counts, lists, lse).
+    __call__(q, k, v) runs: pool Q and K into block means, reorder V (channel-major
+    blocks), build the mask, block-sparse attention reading Q and K in their original
+    order and writing the output in the original token order. With fused=False, Q and K
+    are first copied to fractal order (reorder + pool in one pass) and the attention
+    reads the copies; the results are identical. Intermediate results stay available as
+    attributes (q_r, k_r when not fused, v_rt, qbar, kbar, words, counts, lists, lse).
     """
 
     def __init__(self, geom: Geometry, params: MaskParams, dtype=torch.bfloat16, device="cuda",
-                 scale: float = 0.0, want_lse: bool = False):
-        self.geom, self.params, self.scale = geom, params, scale
+                 scale: float = 0.0, want_lse: bool = False, fused: bool = True):
+        self.geom, self.params, self.scale, self.fused = geom, params, scale, fused
         dev = torch.device(device)
         g = geom
         tok = (g.B, g.H, g.N, g.d)
-        self.q_r = torch.empty(tok, dtype=dtype, device=dev)
-        self.k_r = torch.empty(tok, dtype=dtype, device=dev)
+        self.q_r = None if fused else torch.empty(tok, dtype=dtype, device=dev)
+        self.k_r = None if fused else torch.empty(tok, dtype=dtype, device=dev)
+        self._q = self._k = None
         self.v_rt = torch.empty((g.B, g.H, g.nb, g.d, 64), dtype=dtype, device=dev)
         self.qbar = torch.empty((g.B, g.H, g.nb, g.d), dtype=torch.float64, device=dev)
         self.kbar = torch.empty_like(self.qbar)
@@ -325,8 +340,13 @@ class NablaAttention:
         self.ws_attn = torch.empty(max(sparse_attn_workspace_bytes(g), 1), dtype=torch.uint8, device=dev)
 
     def reorder_pool(self, q, k, v):
-        reorder(q, self.geom, out=self.q_r, pooled=self.qbar)
-        reorder(k, self.geom, out=self.k_r, pooled=self.kbar)
+        if self.fused:
+            reorder(q, self.geom, pooled=self.qbar, pool_only=True)
+            reorder(k, self.geom, pooled=self.kbar, pool_only=True)
+            self._q, self._k = q, k
+        else:
+            reorder(q, self.geom, out=self.q_r, pooled=self.qbar)
+            reorder(k, self.geom, out=self.k_r, pooled=self.kbar)
         reorder(v, self.geom, layout="block_t", out=self.v_rt)
 
     def mask(self):
@@ -334,8 +354,12 @@ class NablaAttention:
                    lists=self.lists, workspace=self.ws_mask)
 
     def attend(self):
-        sparse_attn_fwd(self.q_r, self.k_r, self.v_rt, self.counts, self.lists, self.geom, scale=self.scale,
-                        out=self.out, lse=self.lse, workspace=self.ws_attn)
+        if self.fused:
+            sparse_attn_fwd(self._q, self._k, self.v_rt, self.counts, self.lists, self.geom, scale=self.scale,
+                            qk_original_order=True, out=self.out, lse=self.lse, workspace=self.ws_attn)
+        else:
+            sparse_attn_fwd(self.q_r, self.k_r, self.v_rt, self.counts, self.lists, self.geom, scale=self.scale,
+                            out=self.out, lse=self.lse, workspace=self.ws_attn)
 
     def __call__(self, q, k, v):
         self.reorder_pool(q, k, v)

@@ -95,15 +95,17 @@ abla_status abla_reorder(const abla_geom* g, int32_t dtype, int32_t inverse, int
                          void* y, double* pooled, void* stream) {
   abla_status st = check_geom(g);
   if (st != ABLA_OK) return st;
-  if (!valid_dtype(dtype) || !x || !y) return ABLA_ERR_INVALID;
+  if (!valid_dtype(dtype) || !x) return ABLA_ERR_INVALID;
   if (layout != ABLA_LAYOUT_TOKENS && layout != ABLA_LAYOUT_BLOCK_T) return ABLA_ERR_INVALID;
   if (inverse != 0 && inverse != 1) return ABLA_ERR_INVALID;
   if (inverse && (layout != ABLA_LAYOUT_TOKENS || pooled)) return ABLA_ERR_INVALID;
+  // y may be NULL only to pool without reordering (forward, token layout, pooled given).
+  if (!y && (inverse || layout != ABLA_LAYOUT_TOKENS || !pooled)) return ABLA_ERR_INVALID;
   const size_t bytes = tok_elems(g) * elem_bytes(dtype);
-  if (overlaps(x, bytes, y, bytes)) return ABLA_ERR_INVALID;
+  if (y && overlaps(x, bytes, y, bytes)) return ABLA_ERR_INVALID;
   if (pooled) {
     const size_t pbytes = bh_of(g) * (size_t)nb_of(g) * (size_t)g->d * sizeof(double);
-    if (overlaps(pooled, pbytes, x, bytes) || overlaps(pooled, pbytes, y, bytes)) return ABLA_ERR_INVALID;
+    if (overlaps(pooled, pbytes, x, bytes) || (y && overlaps(pooled, pbytes, y, bytes))) return ABLA_ERR_INVALID;
   }
   return from_hip(launch_reorder(make_kgeom(*g), dtype, inverse, layout, x, y, pooled, (hipStream_t)stream));
 }
@@ -143,11 +145,12 @@ size_t abla_sparse_attn_workspace_bytes(const abla_geom* g) {
 
 abla_status abla_sparse_attn_fwd(const abla_geom* g, int32_t dtype, float scale, const void* q_r,
                                  const void* k_r, const void* v_rt, const int32_t* counts, const int32_t* lists,
-                                 void* out, int32_t out_original_order, float* lse, void* workspace,
+                                 void* out, int32_t layout_flags, float* lse, void* workspace,
                                  size_t workspace_bytes, void* stream) {
   abla_status st = check_geom(g);
   if (st != ABLA_OK) return st;
   if (!valid_dtype(dtype) || !q_r || !k_r || !v_rt || !counts || !lists || !out) return ABLA_ERR_INVALID;
+  if (layout_flags & ~(ABLA_ATTN_OUT_ORIGINAL | ABLA_ATTN_QK_ORIGINAL)) return ABLA_ERR_INVALID;
   if (isnan(scale) || scale < 0.f || isinf(scale)) return ABLA_ERR_INVALID;
   if (nb_of(g) > kMaxBlocks) return ABLA_ERR_UNSUPPORTED;
   const size_t bytes = tok_elems(g) * elem_bytes(dtype);
@@ -156,8 +159,9 @@ abla_status abla_sparse_attn_fwd(const abla_geom* g, int32_t dtype, float scale,
   if (!workspace || workspace_bytes < abla_sparse_attn_workspace_bytes(g)) return ABLA_ERR_WORKSPACE;
   const float s = scale > 0.f ? scale : 1.0f / sqrtf((float)g->d);
   return from_hip(launch_sparse_attn(make_kgeom(*g), dtype, s, q_r, k_r, v_rt, counts, lists, out,
-                                     out_original_order != 0, lse, static_cast<int32_t*>(workspace),
-                                     (hipStream_t)stream));
+                                     (layout_flags & ABLA_ATTN_OUT_ORIGINAL) != 0,
+                                     (layout_flags & ABLA_ATTN_QK_ORIGINAL) != 0, lse,
+                                     static_cast<int32_t*>(workspace), (hipStream_t)stream));
 }
 
 size_t abla_sparse_attn_bwd_workspace_bytes(const abla_geom* g) {

@@ -55,7 +55,35 @@ struct AttnArgs {
   float c2;     // scale * log2(e)
   float scale;
   int orig;
+  // Q and K in the original token order (else fractal order): exact division of block
+  // indices (< 2^16) by F = nbh*nbw and by nbw as (j * magic) >> 32, magic = 2^32 / x + 1.
+  int qk_orig;
+  unsigned long long magic_f, magic_w;
 };
+
+// Byte offset of key block j's first token (its top-left corner) inside one head, and the
+// offsets that walk a tile: a tile load of 256 threads covers 256 / (D/8) LDS rows, i.e. 2
+// (d = 128) or 4 (d = 64) rows of the 8 x 8 patch, so consecutive loads of a thread are
+// 512 * Ws bytes apart in the original order (4096 bytes, 16 or 32 whole rows, in fractal
+// order).
+template <int D, bool QKO>
+__device__ __forceinline__ uint32_t k_tile_base(int j, const AttnArgs& a) {
+  if constexpr (!QKO) {
+    return (uint32_t)j * Tile<D>::KBYTES;
+  } else {
+    const KGeom& g = a.g;
+    const uint32_t uj = (uint32_t)j;
+    const uint32_t t = (uint32_t)(((unsigned long long)uj * a.magic_f) >> 32);
+    const uint32_t rem = uj - t * (uint32_t)(g.nbh * g.nbw);
+    const uint32_t hp = (uint32_t)(((unsigned long long)rem * a.magic_w) >> 32);
+    const uint32_t wp = rem - hp * (uint32_t)g.nbw;
+    return ((t * (uint32_t)g.Hs + hp * kP) * (uint32_t)g.Ws + wp * kP) * (uint32_t)(D * 2);
+  }
+}
+template <bool QKO>
+__device__ __forceinline__ uint32_t k_tile_stride(const KGeom& g) {
+  return QKO ? 512u * (uint32_t)g.Ws : 4096u;
+}
 
 // Rescale the running output only when a row maximum grows by more than 2^8 in the
 // exponent; below that the stale maximum keeps every probability <= 256.
@@ -138,13 +166,13 @@ struct StepLoads {
   char* kdst;
   char* vdst;
   i32x4_t krs, vrs;
-  uint32_t ktile, vtile, koff, voff;
+  uint32_t ktile, vtile, koff, voff, kstride;
   static constexpr int NK = Tile<D>::KBYTES / 16 / 256;
   static constexpr int NV = Tile<D>::VBYTES / 16 / 256;
   __device__ __forceinline__ void load(int i) const {
     if (i < NK)
       raw_buffer_load_lds(krs, (__attribute__((address_space(3))) uint32_t*)(kdst + i * 256 * 16), 16, (int)koff,
-                          (int)(ktile + i * 4096), 0, 0);
+                          (int)(ktile + i * kstride), 0, 0);
     else
       raw_buffer_load_lds(vrs, (__attribute__((address_space(3))) uint32_t*)(vdst + (i - NK) * 256 * 16), 16,
                           (int)voff, (int)(vtile + (i - NK) * 4096), 0, 0);
@@ -274,8 +302,9 @@ struct Walk {
 // Issues K(u+2) into K slot P and V(u+1) into V slot P^1, then, for this wave's block,
 // finishes tile u (probabilities, values) and starts tile u+1 (scores, maximum).
 // sc holds S(u) if the block keeps u; sn receives S(u+1).
-template <int D, int P>
-__device__ __forceinline__ void walk_step(char* smem, const uint16_t* sched, Walk& wk, int mine, int w,
+template <int D, int P, bool QKO>
+__device__ __forceinline__ void walk_step(const AttnArgs& a, char* smem, const uint16_t* sched, Walk& wk, int mine,
+                                          int w,
                                           i32x4_t krs, i32x4_t vrs, uint32_t koff,
                                           uint32_t voff, const uint32_t* klds, const uint32_t* vlds,
                                           const bf16x8_t* qv, float c2, f32x16_t (&sc)[2], f32x16_t (&sn)[2],
@@ -289,7 +318,8 @@ __device__ __forceinline__ void walk_step(char* smem, const uint16_t* sched, Wal
   ld.vdst = smem + Lds<D>::vslot(P ^ 1) + w * 64 * 16;
   ld.krs = krs;
   ld.vrs = vrs;
-  ld.ktile = (uint32_t)(wk.ef & kSchedJ) * TT::KBYTES;  // ef, en are 0 past the end
+  ld.ktile = k_tile_base<D, QKO>(wk.ef & kSchedJ, a);  // ef, en are 0 past the end
+  ld.kstride = k_tile_stride<QKO>(a.g);
   ld.vtile = (uint32_t)(wk.en & kSchedJ) * TT::VBYTES;
   ld.koff = koff;
   ld.voff = voff;
@@ -332,7 +362,7 @@ __device__ __forceinline__ void walk_step(char* smem, const uint16_t* sched, Wal
   wk.ef = wk.u + 2 < wk.n ? __builtin_amdgcn_readfirstlane(raw) : 0;
 }
 
-template <int D>
+template <int D, bool QKO>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) void k_attn_bf16(AttnArgs a) {
   using TT = Tile<D>;
   __shared__ __attribute__((aligned(1024))) char smem[Lds<D>::BYTES];
@@ -382,7 +412,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
   // Q operand: lane holds Q[q_local][ks*16 + 8*hi .. +7] for every k-step.
   bf16x8_t qv[D / 16];
   if (active) {
-    const uint16_t* qrow = a.q + ((long long)bh * g.N + (long long)my_blk * kBlock + q_local) * D + 8 * hi;
+    const long long qn = QKO ? token_of(g, my_blk, q_local) : (long long)my_blk * kBlock + q_local;
+    const uint16_t* qrow = a.q + ((long long)bh * g.N + qn) * D + 8 * hi;
 #pragma unroll
     for (int ks = 0; ks < D / 16; ++ks) qv[ks] = *reinterpret_cast<const bf16x8_t*>(qrow + ks * 16);
   }
@@ -393,7 +424,12 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
   // Per-thread global byte offsets of its 16-byte tile loads, and per-lane LDS byte
   // offsets of its MFMA operand chunks (both the same for every tile).
   uint32_t klds[D / 16], vlds[4];
-  const uint32_t koff = (uint32_t)(kperm(t / TT::KCH) * D * 2 + (((t % TT::KCH) ^ k_swz<D>(t / TT::KCH)) * 16));
+  // K: LDS row r of a tile holds key kperm(r) of the block; in the original order that key
+  // sits (kperm(r) / 8) rows of Ws tokens and kperm(r) % 8 tokens past the block's corner.
+  const int kr = kperm(t / TT::KCH);
+  const uint32_t krow = QKO ? (uint32_t)((kr >> 3) * g.Ws + (kr & 7)) : (uint32_t)kr;
+  const uint32_t koff = krow * (uint32_t)(D * 2) + (uint32_t)(((t % TT::KCH) ^ k_swz<D>(t / TT::KCH)) * 16);
+  const uint32_t kstride = k_tile_stride<QKO>(g);
   const uint32_t voff = (uint32_t)((t >> 3) * kBlock * 2 + (((t & 7) ^ v_swz(t >> 3)) * 16));
   {
     const int r0 = lane & 31;  // rows r0 and r0 + 32 share the swizzle
@@ -423,21 +459,23 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
   wk.ef = wk.n > 2 ? __builtin_amdgcn_readfirstlane((int)sched[2]) : 0;
   f32x16_t s0[2], s1[2];
   if (wk.n > 0) {
-    issue_rows<TT::KBYTES>(smem + Lds<D>::kslot(0), w, krs, (uint32_t)(wk.ec & kSchedJ) * TT::KBYTES, koff);
+    issue_rows<TT::KBYTES>(smem + Lds<D>::kslot(0), w, krs, k_tile_base<D, QKO>(wk.ec & kSchedJ, a), koff,
+                           kstride);
     issue_rows<TT::VBYTES>(smem + Lds<D>::vslot(0), w, vrs, (uint32_t)(wk.ec & kSchedJ) * TT::VBYTES, voff);
     if (wk.n > 1)
-      issue_rows<TT::KBYTES>(smem + Lds<D>::kslot(1), w, krs, (uint32_t)(wk.en & kSchedJ) * TT::KBYTES, koff);
+      issue_rows<TT::KBYTES>(smem + Lds<D>::kslot(1), w, krs, k_tile_base<D, QKO>(wk.en & kSchedJ, a), koff,
+                             kstride);
     wait_vm_lgkm_barrier();
     if (wk.ec & mine) {
       tile_scores<D, 0, false>(smem, klds, qv, s0, nullptr);
       raise_max<D>(tile_max(s0), a.c2, m_run, l_run, o);
     }
     while (true) {
-      walk_step<D, 0>(smem, sched, wk, mine, w, krs, vrs, koff, voff, klds, vlds, qv, a.c2, s0, s1, o, m_run,
-                      l_run);
+      walk_step<D, 0, QKO>(a, smem, sched, wk, mine, w, krs, vrs, koff, voff, klds, vlds, qv, a.c2, s0, s1, o,
+                           m_run, l_run);
       if (wk.u >= wk.n) break;
-      walk_step<D, 1>(smem, sched, wk, mine, w, krs, vrs, koff, voff, klds, vlds, qv, a.c2, s1, s0, o, m_run,
-                      l_run);
+      walk_step<D, 1, QKO>(a, smem, sched, wk, mine, w, krs, vrs, koff, voff, klds, vlds, qv, a.c2, s1, s0, o,
+                           m_run, l_run);
       if (wk.u >= wk.n) break;
     }
   }
@@ -480,6 +518,7 @@ struct AttnArgsF32 {
   KGeom g;
   float scale;
   int orig;
+  int qk_orig;  // Q and K in the original token order
 };
 
 template <int D>
@@ -500,7 +539,8 @@ __global__ __launch_bounds__(128) void k_attn_f32(AttnArgsF32 a) {
   const int32_t* lst = a.lists + row * nb;
 
   float q[H2], o[H2];
-  const float* qrow = a.q + ((long long)bh * g.N + (long long)i * kBlock + r) * D + half * H2;
+  const long long qn = a.qk_orig ? token_of(g, i, r) : (long long)i * kBlock + r;
+  const float* qrow = a.q + ((long long)bh * g.N + qn) * D + half * H2;
 #pragma unroll
   for (int c = 0; c < H2; ++c) {
     q[c] = qrow[c];
@@ -512,10 +552,11 @@ __global__ __launch_bounds__(128) void k_attn_f32(AttnArgsF32 a) {
 
   for (int tt = 0; tt < cnt; ++tt) {
     const int j = min(max(lst[tt], 0), nb - 1);
-    const float4* kg = reinterpret_cast<const float4*>(kbase + (long long)j * kBlock * D);
     const float4* vg = reinterpret_cast<const float4*>(vbase + (long long)j * D * kBlock);
     for (int u = t; u < kBlock * D / 4; u += 128) {
-      reinterpret_cast<float4*>(ks)[u] = kg[u];
+      const int kr = u / (D / 4);  // key row of the tile, in fractal position order
+      const long long kn = a.qk_orig ? token_of(g, j, kr) : (long long)j * kBlock + kr;
+      reinterpret_cast<float4*>(ks)[u] = *reinterpret_cast<const float4*>(kbase + kn * D + (u % (D / 4)) * 4);
       reinterpret_cast<float4*>(vs)[u] = vg[u];
     }
     __syncthreads();
@@ -684,7 +725,8 @@ __global__ __launch_bounds__(1024) void k_row_order(const int32_t* __restrict__ 
 
 hipError_t launch_sparse_attn(const KGeom& g, int dtype, float scale, const void* q, const void* k,
                               const void* vt, const int32_t* counts, const int32_t* lists, void* out,
-                              int out_original_order, float* lse, int32_t* row_order, hipStream_t s) {
+                              int out_original_order, int qk_original_order, float* lse, int32_t* row_order,
+                              hipStream_t s) {
   const unsigned bhs = (unsigned)(g.B * g.H);
   if (dtype == ABLA_BF16) {
     const int F = g.nbh * g.nbw;
@@ -709,11 +751,21 @@ hipError_t launch_sparse_attn(const KGeom& g, int dtype, float scale, const void
     a.scale = scale;
     a.c2 = scale * 1.4426950408889634f;
     a.orig = out_original_order;
+    a.qk_orig = qk_original_order;
+    a.magic_f = (1ull << 32) / (unsigned long long)F + 1;
+    a.magic_w = (1ull << 32) / (unsigned long long)g.nbw + 1;
     const dim3 grid((unsigned)a.grid);
-    if (g.d == 128)
-      k_attn_bf16<128><<<grid, 256, 0, s>>>(a);
-    else
-      k_attn_bf16<64><<<grid, 256, 0, s>>>(a);
+    if (qk_original_order) {
+      if (g.d == 128)
+        k_attn_bf16<128, true><<<grid, 256, 0, s>>>(a);
+      else
+        k_attn_bf16<64, true><<<grid, 256, 0, s>>>(a);
+    } else {
+      if (g.d == 128)
+        k_attn_bf16<128, false><<<grid, 256, 0, s>>>(a);
+      else
+        k_attn_bf16<64, false><<<grid, 256, 0, s>>>(a);
+    }
   } else {
     k_row_order<<<dim3(bhs), 1024, 0, s>>>(counts, row_order, g.nb);
     hipError_t e = hipGetLastError();
@@ -730,6 +782,7 @@ hipError_t launch_sparse_attn(const KGeom& g, int dtype, float scale, const void
     a.g = g;
     a.scale = scale;
     a.orig = out_original_order;
+    a.qk_orig = qk_original_order;
     const dim3 grid((unsigned)((long long)bhs * g.nb));
     if (g.d == 128)
       k_attn_f32<128><<<grid, 128, 0, s>>>(a);

@@ -11,7 +11,9 @@
 // so both the reads and the writes of a wave cover whole rows. The pooled
 // mean is accumulated in float64 in a fixed order (per thread over its rows,
 // then over threads): exact for bf16 inputs and deterministic. HBM-bound: read
-// + write of the tensor plus d*8 bytes of pooled output per block.
+// + write of the tensor plus d*8 bytes of pooled output per block. Without an
+// output tensor the pass only pools (read + pooled output), for consumers that
+// read the tensor in its original order themselves.
 #include "common.h"
 
 namespace abla {
@@ -49,8 +51,9 @@ __device__ __forceinline__ void add_chunk<uint16_t>(double* acc, const uint4& v)
   }
 }
 
-// Forward: original order -> fractal order (token rows, or channel-major blocks).
-template <typename E, int D, bool POOL, bool BLOCK_T>
+// Forward: original order -> fractal order (token rows, or channel-major blocks); with
+// STORE = false only the pooled means are written.
+template <typename E, int D, bool POOL, bool BLOCK_T, bool STORE = true>
 __global__ __launch_bounds__(kThreads) void k_reorder_fwd(const E* __restrict__ x, E* __restrict__ y,
                                                           double* __restrict__ pooled, KGeom g) {
   using S = Shape<E, D>;
@@ -80,7 +83,7 @@ __global__ __launch_bounds__(kThreads) void k_reorder_fwd(const E* __restrict__ 
     const uint4 v = *reinterpret_cast<const uint4*>(xh + n * D + cc * S::EPC);
     if constexpr (BLOCK_T) {
       *reinterpret_cast<uint4*>(&tile[r * D + ((cc ^ ((r / S::EPC) % S::CPR)) * S::EPC)]) = v;
-    } else {
+    } else if constexpr (STORE) {
       *reinterpret_cast<uint4*>(y + ((long long)bh * g.N + (long long)i * kBlock + r) * D + cc * S::EPC) = v;
     }
     if constexpr (POOL) add_chunk<E>(acc, v);
@@ -155,6 +158,8 @@ hipError_t dispatch(const KGeom& g, int inverse, int layout, const void* x, void
       k_reorder_fwd<E, D, true, true><<<grid, kThreads, 0, s>>>(xi, yo, pooled, g);
     else
       k_reorder_fwd<E, D, false, true><<<grid, kThreads, 0, s>>>(xi, yo, nullptr, g);
+  } else if (!yo) {
+    k_reorder_fwd<E, D, true, false, false><<<grid, kThreads, 0, s>>>(xi, nullptr, pooled, g);
   } else {
     if (pooled)
       k_reorder_fwd<E, D, true, false><<<grid, kThreads, 0, s>>>(xi, yo, pooled, g);

@@ -94,18 +94,20 @@ __device__ __forceinline__ i32x4_t make_rsrc(const void* base, uint32_t bytes) {
 
 // Issue this thread's 16-byte global->LDS loads of one K tile (or one V^T tile) that
 // starts `tile` bytes into the resource. Load `it` of thread t fills LDS unit it*256 + t
-// of the slot; its source is `off` + it*4096 bytes into the tile (for both tile kinds and
+// of the slot; its source is `off` + it*stride bytes into the tile (for both tile kinds and
 // both head dims the swizzled source of unit it*256 + t is 4096 bytes past that of unit
-// t: 16 K rows of 256 bytes, 32 K rows of 128 bytes, 32 V^T rows of 128 bytes, all with
-// a swizzle that repeats every 16 or 32 rows). `w` is the wave index (uniform).
+// t in fractal order: 16 K rows of 256 bytes, 32 K rows of 128 bytes, 32 V^T rows of 128
+// bytes, all with a swizzle that repeats every 16 or 32 rows; a K tile read in the
+// original token order passes its own stride). `w` is the wave index (uniform).
 template <int BYTES>
-__device__ __forceinline__ void issue_rows(char* dst_slot, int w, i32x4_t rsrc, uint32_t tile, uint32_t off) {
+__device__ __forceinline__ void issue_rows(char* dst_slot, int w, i32x4_t rsrc, uint32_t tile, uint32_t off,
+                                           uint32_t stride = 4096) {
   constexpr int LOADS = BYTES / 16 / 256;
   char* dst = dst_slot + w * 64 * 16;
 #pragma unroll
   for (int it = 0; it < LOADS; ++it)
     raw_buffer_load_lds(rsrc, (__attribute__((address_space(3))) uint32_t*)(dst + it * 256 * 16), 16, (int)off,
-                        (int)(tile + it * 4096), 0, 0);
+                        (int)(tile + it * stride), 0, 0);
 }
 
 }  // namespace

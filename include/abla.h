@@ -96,11 +96,14 @@ typedef struct {
  *   block means: the 64 input values of a block summed in float64 (exact for
  *   bf16 inputs) and divided by 64. The mask decisions downstream are taken in
  *   float64 so that they do not hinge on float32 rounding.
+ *   With y = NULL (ABLA_LAYOUT_TOKENS, pooled given) only the block means are
+ *   written: the pooling pass for consumers that read x in its original order
+ *   (abla_sparse_attn_fwd with ABLA_ATTN_QK_ORIGINAL).
  * inverse = 1: x is [B,H,N,d] in fractal order (ABLA_LAYOUT_TOKENS only) and
  *   y receives the original order; `pooled` must be NULL.
  * dtype: element type of x and y. x and y must not overlap.
- * Errors: INVALID for null x/y, x == y, bad geometry, unknown dtype or layout,
- * inverse with BLOCK_T or with pooled; UNSUPPORTED for P*P != 64, d not in
+ * Errors: INVALID for null x, null y other than the pooling-only form, x == y, bad
+ * geometry, unknown dtype or layout, inverse with BLOCK_T or with pooled; UNSUPPORTED for P*P != 64, d not in
  * {64, 128}, more than 2^31 - 1 tokens per head or B*H*nb above 2^31 - 1. */
 abla_status abla_reorder(const abla_geom* g, int32_t dtype, int32_t inverse, int32_t layout,
                          const void* x, void* y, double* pooled, void* stream);
@@ -161,11 +164,15 @@ size_t abla_sparse_attn_workspace_bytes(const abla_geom* g);
  * For every query token m of block i (fractal order):
  *   O[m] = sum over keys m' in the blocks listed for row i of
  *          softmax_m'(scale * <Q[m], K[m']>) * V[m'].
- * q_r, k_r: [B,H,N,d] fractal order, ABLA_LAYOUT_TOKENS.
+ * q_r, k_r: [B,H,N,d] fractal order, ABLA_LAYOUT_TOKENS; or, with ABLA_ATTN_QK_ORIGINAL,
+ *           the caller's [B,H,N,d] tensors in the original token order (the kernel then
+ *           gathers each 64-token block as its 8 runs of 8 tokens, so no reordered copies of
+ *           Q and K are needed; the result is the same).
  * v_rt:     fractal order, ABLA_LAYOUT_BLOCK_T.
  * counts, lists: as produced by abla_build_mask (lists ascending).
- * out: [B,H,N,d], same dtype; original token order if out_original_order != 0,
- *      else fractal order.
+ * layout_flags: ABLA_ATTN_OUT_ORIGINAL (out in the original token order, else fractal order)
+ *      | ABLA_ATTN_QK_ORIGINAL (q_r / k_r given in the original order); other bits INVALID.
+ * out: [B,H,N,d], same dtype, in the order layout_flags names.
  * lse: [B,H,N] float32 or NULL: natural-log sum of exp(scale * scores) over
  *      the allowed keys, indexed in fractal order; -inf for a row whose list
  *      is empty (its output is 0).
@@ -176,11 +183,13 @@ size_t abla_sparse_attn_workspace_bytes(const abla_geom* g);
  * inputs are computed in float32 throughout.
  * workspace: at least abla_sparse_attn_workspace_bytes(g) bytes.
  * Errors: as abla_reorder, plus INVALID for null counts/lists/out, q_r/k_r/v_rt
- * aliasing out, and WORKSPACE. */
+ * aliasing out, unknown layout_flags bits, and WORKSPACE. */
+enum { ABLA_ATTN_OUT_ORIGINAL = 1, ABLA_ATTN_QK_ORIGINAL = 2 };
+
 abla_status abla_sparse_attn_fwd(const abla_geom* g, int32_t dtype, float scale,
                                  const void* q_r, const void* k_r, const void* v_rt,
                                  const int32_t* counts, const int32_t* lists,
-                                 void* out, int32_t out_original_order, float* lse,
+                                 void* out, int32_t layout_flags, float* lse,
                                  void* workspace, size_t workspace_bytes, void* stream);
 
 /* Bytes of scratch abla_sparse_attn_bwd needs: four fractal copies of one [B,H,N,d] bf16

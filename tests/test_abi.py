@@ -63,7 +63,11 @@ def test_reorder_argument_errors(A):
     g = G(A)
     assert reorder(A, g, dtype=7) == 1
     assert reorder(A, g, x=None) == 1
-    assert reorder(A, g, y=None) == 1
+    assert reorder(A, g, y=None) == 1  # no output and nothing to pool
+    P = ctypes.c_void_p(0x7000000)
+    assert reorder(A, g, y=None, pooled=P, layout=1) == 1  # pooling only takes the token layout
+    assert reorder(A, g, y=None, pooled=P, inverse=1) == 1
+    assert reorder(A, g, y=None, pooled=ctypes.c_void_p(0x10000 + 64)) == 1  # pooled overlaps x
     assert reorder(A, g, y=FAKE) == 1  # x == y
     assert reorder(A, g, y=ctypes.c_void_p(0x10000 + 64)) == 1  # overlapping
     assert reorder(A, g, layout=5) == 1
@@ -108,8 +112,8 @@ def test_mask_pointer_workspace_and_size_errors(A):
 
 
 def attn_call(A, g, dtype=1, scale=0.0, q=FAKE, k=ctypes.c_void_p(0x20000), v=ctypes.c_void_p(0x30000),
-              counts=FAKE, lists=FAKE, out=FAKE2, ws=FAKE, ws_bytes=1 << 40):
-    return A._lib.abla_sparse_attn_fwd(ctypes.byref(g), dtype, scale, q, k, v, counts, lists, out, 1, None, ws,
+              counts=FAKE, lists=FAKE, out=FAKE2, ws=FAKE, ws_bytes=1 << 40, flags=1):
+    return A._lib.abla_sparse_attn_fwd(ctypes.byref(g), dtype, scale, q, k, v, counts, lists, out, flags, None, ws,
                                        ws_bytes, None)
 
 
@@ -123,6 +127,9 @@ def test_attention_errors(A):
     assert attn_call(A, g, scale=math.nan) == 1
     assert attn_call(A, g, scale=-0.5) == 1
     assert attn_call(A, g, ws=None) == 3
+    assert attn_call(A, g, flags=4) == 1  # unknown layout flag
+    assert attn_call(A, g, flags=-1) == 1
+    assert attn_call(A, g, flags=3, ws=None) == 3  # both known flags pass the argument checks
     assert attn_call(A, g, ws_bytes=2 * 18 * 4 - 1) == 3
     assert attn_call(A, G(A, d=32)) == 2
     assert A.sparse_attn_workspace_bytes(A.Geometry(1, 2, 3, 16, 24, 128)) == 2 * 18 * 4 + 256

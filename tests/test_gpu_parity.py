@@ -138,10 +138,36 @@ def test_fractal_order_output_and_determinism(A):
     run(q, k, v)
     torch.cuda.synchronize()
     assert torch.equal(out1, run.out)
-    o_r = A.sparse_attn_fwd(run.q_r, run.k_r, run.v_rt, run.counts, run.lists, geom, out_original_order=False)
+    o_r = A.sparse_attn_fwd(q, k, run.v_rt, run.counts, run.lists, geom, out_original_order=False,
+                            qk_original_order=True)
     back = A.reorder(o_r, geom, inverse=True)
     torch.cuda.synchronize()
     assert torch.equal(back, out1)
+
+
+@pytest.mark.parametrize("dtype,d,geo", [
+    ("bf16", 128, (1, 2, 3, 24, 88)), ("bf16", 64, (2, 1, 4, 16, 40)), ("f32", 64, (1, 2, 4, 16, 16)),
+    ("bf16", 128, (1, 1, 2, 8, 8)), ("bf16", 64, (1, 1, 5, 8, 136)),
+])
+def test_fused_and_unfused_paths_agree(A, dtype, d, geo):
+    """Q and K read in the original order (the default path: pooling only, no reordered copies)
+    give bit-identically the output and LSE of the path that reads fractal-order copies; the
+    pooling-only pass writes the same block means as the reorder + pool pass."""
+    B, H, T, Hs, Ws = geo
+    geom, og = PT.geoms(B, H, T, Hs, Ws, d)
+    q, k, v = make_random_qkv(B, H, T, Hs, Ws, d, dtype, seed=9, device=DEV)
+    k = (k.float() + 2.0 * q.float()).to(q.dtype)
+    prm = A.MaskParams(mode="cdf", thr=0.7)
+    fused = A.NablaAttention(geom, prm, dtype=q.dtype, want_lse=True)
+    plain = A.NablaAttention(geom, prm, dtype=q.dtype, want_lse=True, fused=False)
+    fused(q, k, v)
+    plain(q, k, v)
+    torch.cuda.synchronize()
+    assert fused.q_r is None and plain.q_r is not None
+    assert torch.equal(fused.qbar, plain.qbar) and torch.equal(fused.kbar, plain.kbar)
+    assert torch.equal(fused.words, plain.words)
+    assert np.array_equal(_bits(fused.out), _bits(plain.out))
+    assert torch.equal(fused.lse, plain.lse)
 
 
 def test_graph_replay_matches_eager(A):
