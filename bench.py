@@ -44,6 +44,8 @@ def parse():
                     help="measured HBM bytes per attention launch (from rocprofv3 counters)")
     ap.add_argument("--graph", action="store_true",
                     help="replay the step captured in a HIP graph instead of launching it eagerly")
+    ap.add_argument("--backward", action="store_true",
+                    help="time the backward (abla_sparse_attn_bwd) on --workload instead; one JSON line")
     ap.add_argument("--report", action="store_true",
                     help="instead of the JSON line, print a markdown report over every workload (and the "
                          "dynamic-threshold sweep) with per-pass times, fractions and per-head keep")
@@ -277,6 +279,18 @@ def main():
         return
     if args.report:
         report(args)
+        return
+    if args.backward:
+        from gen import WORKLOADS
+        w = WORKLOADS[args.workload]
+        b = measure_backward(w, args.steps, args.warmup)
+        alg = b["alg_flops"] / (b["ms"] * 1e-3) / 1e12
+        print(json.dumps({
+            "what": "block-sparse attention backward (abla_sparse_attn_bwd, every pass)", "workload": w.name,
+            "steps": args.steps, "warmup": args.warmup, "ms": round(b["ms"], 4), "kept_pairs": b["kept"],
+            "algorithmic_tflops": round(alg, 2), "frac_of_2.5PF": round(alg / MFMA_BF16_PEAK_TFLOPS, 4),
+            "issued_mfma_tflops": round(b["mfma_flops"] / (b["ms"] * 1e-3) / 1e12, 2),
+        }), flush=True)
         return
     r = measure(args.workload, args.steps, args.warmup, use_graph=args.graph)
     w, geom = r["w"], r["geom"]
