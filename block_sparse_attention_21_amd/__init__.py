@@ -22,7 +22,7 @@ OK, ERR_INVALID, ERR_UNSUPPORTED, ERR_WORKSPACE, ERR_HIP = range(5)
 F32, BF16 = 0, 1
 LAYOUT_TOKENS, LAYOUT_BLOCK_T = 0, 1
 MASK_CDF, MASK_DYN, MASK_STATIC = 0, 1, 2
-ATTN_OUT_ORIGINAL, ATTN_QK_ORIGINAL = 1, 2
+ATTN_OUT_ORIGINAL, ATTN_QK_ORIGINAL, ATTN_V_ORIGINAL = 1, 2, 4
 CUT_RADIX, CUT_BITONIC = 0, 1
 
 
@@ -240,11 +240,13 @@ def build_mask(qbar: torch.Tensor, kbar: torch.Tensor, geom: Geometry, params: M
 
 def sparse_attn_fwd(q_r: torch.Tensor, k_r: torch.Tensor, v_rt: torch.Tensor, counts: torch.Tensor,
                     lists: torch.Tensor, geom: Geometry, *, scale: float = 0.0, out_original_order: bool = True,
-                    qk_original_order: bool = False, out: Optional[torch.Tensor] = None,
+                    qk_original_order: bool = False, v_original_order: bool = False,
+                    out: Optional[torch.Tensor] = None,
                     lse: Optional[torch.Tensor] = None, want_lse: bool = False,
                     workspace: Optional[torch.Tensor] = None):
     """abla_sparse_attn_fwd. Returns out (and lse if requested). With qk_original_order, q_r and k_r
-    are the caller's Q and K in the original token order (no reordered copies needed)."""
+    are the caller's Q and K in the original token order (no reordered copies needed); with
+    v_original_order, v_rt is the caller's V in the original order ([B,H,N,d])."""
     dev = _device(q_r)
     dt = q_r.dtype
     if dt not in _DT:
@@ -252,7 +254,7 @@ def sparse_attn_fwd(q_r: torch.Tensor, k_r: torch.Tensor, v_rt: torch.Tensor, co
     tok = (geom.B, geom.H, geom.N, geom.d)
     _need(q_r, "q_r", tok, dt, dev)
     _need(k_r, "k_r", tok, dt, dev)
-    _need(v_rt, "v_rt", (geom.B, geom.H, geom.nb, geom.d, 64), dt, dev)
+    _need(v_rt, "v_rt", tok if v_original_order else (geom.B, geom.H, geom.nb, geom.d, 64), dt, dev)
     _need(counts, "counts", (geom.B, geom.H, geom.nb), torch.int32, dev)
     _need(lists, "lists", (geom.B, geom.H, geom.nb, geom.nb), torch.int32, dev)
     if out is None:
@@ -266,7 +268,8 @@ def sparse_attn_fwd(q_r: torch.Tensor, k_r: torch.Tensor, v_rt: torch.Tensor, co
     if workspace is None:
         workspace = torch.empty(max(nbytes, 1), dtype=torch.uint8, device=dev)
     g = geom.c()
-    flags = (ATTN_OUT_ORIGINAL if out_original_order else 0) | (ATTN_QK_ORIGINAL if qk_original_order else 0)
+    flags = ((ATTN_OUT_ORIGINAL if out_original_order else 0) | (ATTN_QK_ORIGINAL if qk_original_order else 0)
+             | (ATTN_V_ORIGINAL if v_original_order else 0))
     _check(_lib.abla_sparse_attn_fwd(ctypes.byref(g), _DT[dt], float(scale), _ptr(q_r), _ptr(k_r), _ptr(v_rt),
                                      _ptr(counts), _ptr(lists), _ptr(out), flags, _ptr(lse),
                                      _ptr(workspace), workspace.numel(), _stream(q_r)), "abla_sparse_attn_fwd")
@@ -319,15 +322,16 @@ class NablaAttention:
     """
 
     def __init__(self, geom: Geometry, params: MaskParams, dtype=torch.bfloat16, device="cuda",
-                 scale: float = 0.0, want_lse: bool = False, fused: bool = True):
+                 scale: float = 0.0, want_lse: bool = False, fused: bool = True, fuse_v: bool = False):
         self.geom, self.params, self.scale, self.fused = geom, params, scale, fused
+        self.fuse_v = fused and fuse_v
         dev = torch.device(device)
         g = geom
         tok = (g.B, g.H, g.N, g.d)
         self.q_r = None if fused else torch.empty(tok, dtype=dtype, device=dev)
         self.k_r = None if fused else torch.empty(tok, dtype=dtype, device=dev)
-        self._q = self._k = None
-        self.v_rt = torch.empty((g.B, g.H, g.nb, g.d, 64), dtype=dtype, device=dev)
+        self._q = self._k = self._v = None
+        self.v_rt = None if self.fuse_v else torch.empty((g.B, g.H, g.nb, g.d, 64), dtype=dtype, device=dev)
         self.qbar = torch.empty((g.B, g.H, g.nb, g.d), dtype=torch.float64, device=dev)
         self.kbar = torch.empty_like(self.qbar)
         self.words = torch.empty((g.B, g.H, g.nb, g.words), dtype=torch.int32, device=dev)
@@ -343,11 +347,12 @@ class NablaAttention:
         if self.fused:
             reorder(q, self.geom, pooled=self.qbar, pool_only=True)
             reorder(k, self.geom, pooled=self.kbar, pool_only=True)
-            self._q, self._k = q, k
+            self._q, self._k, self._v = q, k, v
         else:
             reorder(q, self.geom, out=self.q_r, pooled=self.qbar)
             reorder(k, self.geom, out=self.k_r, pooled=self.kbar)
-        reorder(v, self.geom, layout="block_t", out=self.v_rt)
+        if not self.fuse_v:
+            reorder(v, self.geom, layout="block_t", out=self.v_rt)
 
     def mask(self):
         build_mask(self.qbar, self.kbar, self.geom, self.params, words=self.words, counts=self.counts,
@@ -355,8 +360,10 @@ class NablaAttention:
 
     def attend(self):
         if self.fused:
-            sparse_attn_fwd(self._q, self._k, self.v_rt, self.counts, self.lists, self.geom, scale=self.scale,
-                            qk_original_order=True, out=self.out, lse=self.lse, workspace=self.ws_attn)
+            v = self._v if self.fuse_v else self.v_rt
+            sparse_attn_fwd(self._q, self._k, v, self.counts, self.lists, self.geom, scale=self.scale,
+                            qk_original_order=True, v_original_order=self.fuse_v, out=self.out, lse=self.lse,
+                            workspace=self.ws_attn)
         else:
             sparse_attn_fwd(self.q_r, self.k_r, self.v_rt, self.counts, self.lists, self.geom, scale=self.scale,
                             out=self.out, lse=self.lse, workspace=self.ws_attn)

@@ -150,7 +150,8 @@ abla_status abla_sparse_attn_fwd(const abla_geom* g, int32_t dtype, float scale,
   abla_status st = check_geom(g);
   if (st != ABLA_OK) return st;
   if (!valid_dtype(dtype) || !q_r || !k_r || !v_rt || !counts || !lists || !out) return ABLA_ERR_INVALID;
-  if (layout_flags & ~(ABLA_ATTN_OUT_ORIGINAL | ABLA_ATTN_QK_ORIGINAL)) return ABLA_ERR_INVALID;
+  if (layout_flags & ~(ABLA_ATTN_OUT_ORIGINAL | ABLA_ATTN_QK_ORIGINAL | ABLA_ATTN_V_ORIGINAL))
+    return ABLA_ERR_INVALID;
   if (isnan(scale) || scale < 0.f || isinf(scale)) return ABLA_ERR_INVALID;
   if (nb_of(g) > kMaxBlocks) return ABLA_ERR_UNSUPPORTED;
   const size_t bytes = tok_elems(g) * elem_bytes(dtype);
@@ -160,7 +161,8 @@ abla_status abla_sparse_attn_fwd(const abla_geom* g, int32_t dtype, float scale,
   const float s = scale > 0.f ? scale : 1.0f / sqrtf((float)g->d);
   return from_hip(launch_sparse_attn(make_kgeom(*g), dtype, s, q_r, k_r, v_rt, counts, lists, out,
                                      (layout_flags & ABLA_ATTN_OUT_ORIGINAL) != 0,
-                                     (layout_flags & ABLA_ATTN_QK_ORIGINAL) != 0, lse,
+                                     (layout_flags & ABLA_ATTN_QK_ORIGINAL) != 0,
+                                     (layout_flags & ABLA_ATTN_V_ORIGINAL) != 0, lse,
                                      static_cast<int32_t*>(workspace), (hipStream_t)stream));
 }
 

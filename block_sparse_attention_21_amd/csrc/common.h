@@ -54,8 +54,8 @@ hipError_t launch_build_mask(const KGeom& g, const abla_mask_params& p, const do
                              uint32_t* words, int32_t* counts, int32_t* lists, double* scores, hipStream_t s);
 hipError_t launch_sparse_attn(const KGeom& g, int dtype, float scale, const void* q, const void* k,
                               const void* vt, const int32_t* counts, const int32_t* lists, void* out,
-                              int out_original_order, int qk_original_order, float* lse, int32_t* row_order,
-                              hipStream_t s);
+                              int out_original_order, int qk_original_order, int v_original_order, float* lse,
+                              int32_t* row_order, hipStream_t s);
 
 // Device scratch of the backward pass, carved out of the caller's workspace
 // (see abla_sparse_attn_bwd_workspace_bytes).

@@ -66,9 +66,9 @@ struct AttnArgs {
 // (d = 128) or 4 (d = 64) rows of the 8 x 8 patch, so consecutive loads of a thread are
 // 512 * Ws bytes apart in the original order (4096 bytes, 16 or 32 whole rows, in fractal
 // order).
-template <int D, bool QKO>
+template <int D, bool ORIG>
 __device__ __forceinline__ uint32_t k_tile_base(int j, const AttnArgs& a) {
-  if constexpr (!QKO) {
+  if constexpr (!ORIG) {
     return (uint32_t)j * Tile<D>::KBYTES;
   } else {
     const KGeom& g = a.g;
@@ -80,9 +80,9 @@ __device__ __forceinline__ uint32_t k_tile_base(int j, const AttnArgs& a) {
     return ((t * (uint32_t)g.Hs + hp * kP) * (uint32_t)g.Ws + wp * kP) * (uint32_t)(D * 2);
   }
 }
-template <bool QKO>
+template <bool ORIG>
 __device__ __forceinline__ uint32_t k_tile_stride(const KGeom& g) {
-  return QKO ? 512u * (uint32_t)g.Ws : 4096u;
+  return ORIG ? 512u * (uint32_t)g.Ws : 4096u;
 }
 
 // Rescale the running output only when a row maximum grows by more than 2^8 in the
@@ -166,7 +166,7 @@ struct StepLoads {
   char* kdst;
   char* vdst;
   i32x4_t krs, vrs;
-  uint32_t ktile, vtile, koff, voff, kstride;
+  uint32_t ktile, vtile, koff, voff, kstride, vstride;
   static constexpr int NK = Tile<D>::KBYTES / 16 / 256;
   static constexpr int NV = Tile<D>::VBYTES / 16 / 256;
   __device__ __forceinline__ void load(int i) const {
@@ -175,7 +175,7 @@ struct StepLoads {
                           (int)(ktile + i * kstride), 0, 0);
     else
       raw_buffer_load_lds(vrs, (__attribute__((address_space(3))) uint32_t*)(vdst + (i - NK) * 256 * 16), 16,
-                          (int)voff, (int)(vtile + (i - NK) * 4096), 0, 0);
+                          (int)voff, (int)(vtile + (i - NK) * vstride), 0, 0);
   }
   __device__ __forceinline__ void load_all() const {
 #pragma unroll
@@ -234,15 +234,21 @@ __device__ __forceinline__ float tile_probs(const f32x16_t (&s)[2], float c2, fl
 
 // O^T += V^T P^T for one staged V^T tile. vlds[kk]: this lane's byte offset of its 8-key
 // chunk kk of channel row (lane & 31) inside a slot; channel tile dt is 32 rows further.
-template <int D, int SLOT>
+// With VT the slot holds a token-major V tile laid out like a K tile (key rows in kperm
+// order, chunk-swizzled) and the V^T operand comes from two LDS transpose loads.
+template <int D, int SLOT, bool VT>
 __device__ __forceinline__ void tile_values(const char* smem, const uint32_t* vlds, const bf16x8_t (&pb)[4],
                                             f32x16_t* o) {
+  const int lane = threadIdx.x & 63;
 #pragma unroll
   for (int kk = 0; kk < 4; ++kk)
 #pragma unroll
     for (int dt = 0; dt < D / 32; ++dt) {
-      const bf16x8_t vv =
-          *reinterpret_cast<const bf16x8_t*>(smem + Lds<D>::vslot(SLOT) + dt * 32 * kBlock * 2 + vlds[kk]);
+      bf16x8_t vv;
+      if constexpr (VT)
+        vv = tr_chunk<D>(smem + Lds<D>::vslot(SLOT), dt, 16 * kk, lane);
+      else
+        vv = *reinterpret_cast<const bf16x8_t*>(smem + Lds<D>::vslot(SLOT) + dt * 32 * kBlock * 2 + vlds[kk]);
       o[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vv, pb[kk], o[dt], 0, 0, 0);
     }
 }
@@ -280,14 +286,15 @@ __device__ __forceinline__ void schedule_phase_a() {
     if (i & 1) __builtin_amdgcn_sched_group_barrier(0x010, 1, 0);
   }
 }
-template <int D>
+template <int D, bool VT>
 __device__ __forceinline__ void schedule_phase_b() {
   constexpr int NPV = 4 * (D / 32);
-  __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
+  constexpr int RD = VT ? 2 : 1;  // LDS reads per value MFMA (two transpose loads, or one chunk)
+  __builtin_amdgcn_sched_group_barrier(0x100, 4 * RD, 0);
 #pragma unroll
   for (int i = 0; i < NPV; ++i) {
     __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-    __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+    __builtin_amdgcn_sched_group_barrier(0x100, RD, 0);
     __builtin_amdgcn_sched_group_barrier(0x402, 2, 0);
   }
 }
@@ -302,7 +309,7 @@ struct Walk {
 // Issues K(u+2) into K slot P and V(u+1) into V slot P^1, then, for this wave's block,
 // finishes tile u (probabilities, values) and starts tile u+1 (scores, maximum).
 // sc holds S(u) if the block keeps u; sn receives S(u+1).
-template <int D, int P, bool QKO>
+template <int D, int P, bool QKO, bool VT>
 __device__ __forceinline__ void walk_step(const AttnArgs& a, char* smem, const uint16_t* sched, Walk& wk, int mine,
                                           int w,
                                           i32x4_t krs, i32x4_t vrs, uint32_t koff,
@@ -320,7 +327,8 @@ __device__ __forceinline__ void walk_step(const AttnArgs& a, char* smem, const u
   ld.vrs = vrs;
   ld.ktile = k_tile_base<D, QKO>(wk.ef & kSchedJ, a);  // ef, en are 0 past the end
   ld.kstride = k_tile_stride<QKO>(a.g);
-  ld.vtile = (uint32_t)(wk.en & kSchedJ) * TT::VBYTES;
+  ld.vtile = VT ? k_tile_base<D, true>(wk.en & kSchedJ, a) : (uint32_t)(wk.en & kSchedJ) * TT::VBYTES;
+  ld.vstride = k_tile_stride<VT>(a.g);
   ld.koff = koff;
   ld.voff = voff;
   const int look = min(wk.u + 3, wk.n - 1);
@@ -338,9 +346,9 @@ __device__ __forceinline__ void walk_step(const AttnArgs& a, char* smem, const u
     const float psum = tile_probs(sc, c2, m_run, pb);
     schedule_phase_a<D>();
     __builtin_amdgcn_s_setprio(0);
-    tile_values<D, P>(smem, vlds, pb, o);
+    tile_values<D, P, VT>(smem, vlds, pb, o);
     const float mx = tile_max(sn);
-    schedule_phase_b<D>();
+    schedule_phase_b<D, VT>();
     __builtin_amdgcn_s_setprio(0);  // no-op for priority; closes phase B's scheduling region
     l_run += psum;
     raise_max<D>(mx, c2, m_run, l_run, o);
@@ -348,7 +356,7 @@ __device__ __forceinline__ void walk_step(const AttnArgs& a, char* smem, const u
     ld.load_all();
     bf16x8_t pb[4];
     const float psum = tile_probs(sc, c2, m_run, pb);
-    tile_values<D, P>(smem, vlds, pb, o);
+    tile_values<D, P, VT>(smem, vlds, pb, o);
     l_run += psum;
   } else if (mn) {
     tile_scores<D, P ^ 1, true>(smem, klds, qv, sn, &ld);
@@ -362,7 +370,7 @@ __device__ __forceinline__ void walk_step(const AttnArgs& a, char* smem, const u
   wk.ef = wk.u + 2 < wk.n ? __builtin_amdgcn_readfirstlane(raw) : 0;
 }
 
-template <int D, bool QKO>
+template <int D, bool QKO, bool VT>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) void k_attn_bf16(AttnArgs a) {
   using TT = Tile<D>;
   __shared__ __attribute__((aligned(1024))) char smem[Lds<D>::BYTES];
@@ -430,7 +438,11 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
   const uint32_t krow = QKO ? (uint32_t)((kr >> 3) * g.Ws + (kr & 7)) : (uint32_t)kr;
   const uint32_t koff = krow * (uint32_t)(D * 2) + (uint32_t)(((t % TT::KCH) ^ k_swz<D>(t / TT::KCH)) * 16);
   const uint32_t kstride = k_tile_stride<QKO>(g);
-  const uint32_t voff = (uint32_t)((t >> 3) * kBlock * 2 + (((t & 7) ^ v_swz(t >> 3)) * 16));
+  // V: channel-major V^T blocks, or with VT a token-major tile of the original-order V loaded
+  // exactly like a K tile in the original order.
+  const uint32_t voff = VT ? (uint32_t)((kr >> 3) * g.Ws + (kr & 7)) * (uint32_t)(D * 2) +
+                                 (uint32_t)(((t % TT::KCH) ^ k_swz<D>(t / TT::KCH)) * 16)
+                           : (uint32_t)((t >> 3) * kBlock * 2 + (((t & 7) ^ v_swz(t >> 3)) * 16));
   {
     const int r0 = lane & 31;  // rows r0 and r0 + 32 share the swizzle
 #pragma unroll
@@ -442,7 +454,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
   // (nb <= 4096 blocks of 64 tokens, d <= 128), so 32-bit offsets cover them.
   const uint32_t head_bytes = (uint32_t)(g.N * D * 2);
   const i32x4_t krs = make_rsrc(a.k + (long long)bh * g.N * D, head_bytes);
-  const i32x4_t vrs = make_rsrc(a.vt + (long long)bh * nb * D * kBlock, head_bytes);
+  const i32x4_t vrs = make_rsrc(a.vt + (long long)bh * nb * D * kBlock, head_bytes);  // = N*D per head
+  const uint32_t vstride = k_tile_stride<VT>(g);
   const int mine = (w < 2) ? kSchedA : kSchedB;
 
   f32x16_t o[D / 32];
@@ -461,7 +474,9 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
   if (wk.n > 0) {
     issue_rows<TT::KBYTES>(smem + Lds<D>::kslot(0), w, krs, k_tile_base<D, QKO>(wk.ec & kSchedJ, a), koff,
                            kstride);
-    issue_rows<TT::VBYTES>(smem + Lds<D>::vslot(0), w, vrs, (uint32_t)(wk.ec & kSchedJ) * TT::VBYTES, voff);
+    issue_rows<TT::VBYTES>(smem + Lds<D>::vslot(0), w, vrs,
+                           VT ? k_tile_base<D, true>(wk.ec & kSchedJ, a) : (uint32_t)(wk.ec & kSchedJ) * TT::VBYTES,
+                           voff, vstride);
     if (wk.n > 1)
       issue_rows<TT::KBYTES>(smem + Lds<D>::kslot(1), w, krs, k_tile_base<D, QKO>(wk.en & kSchedJ, a), koff,
                              kstride);
@@ -471,10 +486,10 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
       raise_max<D>(tile_max(s0), a.c2, m_run, l_run, o);
     }
     while (true) {
-      walk_step<D, 0, QKO>(a, smem, sched, wk, mine, w, krs, vrs, koff, voff, klds, vlds, qv, a.c2, s0, s1, o,
+      walk_step<D, 0, QKO, VT>(a, smem, sched, wk, mine, w, krs, vrs, koff, voff, klds, vlds, qv, a.c2, s0, s1, o,
                            m_run, l_run);
       if (wk.u >= wk.n) break;
-      walk_step<D, 1, QKO>(a, smem, sched, wk, mine, w, krs, vrs, koff, voff, klds, vlds, qv, a.c2, s1, s0, o,
+      walk_step<D, 1, QKO, VT>(a, smem, sched, wk, mine, w, krs, vrs, koff, voff, klds, vlds, qv, a.c2, s1, s0, o,
                            m_run, l_run);
       if (wk.u >= wk.n) break;
     }
@@ -519,6 +534,7 @@ struct AttnArgsF32 {
   float scale;
   int orig;
   int qk_orig;  // Q and K in the original token order
+  int v_orig;   // V in the original token order (else channel-major blocks)
 };
 
 template <int D>
@@ -555,9 +571,18 @@ __global__ __launch_bounds__(128) void k_attn_f32(AttnArgsF32 a) {
     const float4* vg = reinterpret_cast<const float4*>(vbase + (long long)j * D * kBlock);
     for (int u = t; u < kBlock * D / 4; u += 128) {
       const int kr = u / (D / 4);  // key row of the tile, in fractal position order
+      const int c4 = (u % (D / 4)) * 4;
       const long long kn = a.qk_orig ? token_of(g, j, kr) : (long long)j * kBlock + kr;
-      reinterpret_cast<float4*>(ks)[u] = *reinterpret_cast<const float4*>(kbase + kn * D + (u % (D / 4)) * 4);
-      reinterpret_cast<float4*>(vs)[u] = vg[u];
+      reinterpret_cast<float4*>(ks)[u] = *reinterpret_cast<const float4*>(kbase + kn * D + c4);
+      if (a.v_orig) {  // transpose the token row into the channel-major tile
+        const float4 x = *reinterpret_cast<const float4*>(vbase + token_of(g, j, kr) * D + c4);
+        vs[(c4 + 0) * kBlock + kr] = x.x;
+        vs[(c4 + 1) * kBlock + kr] = x.y;
+        vs[(c4 + 2) * kBlock + kr] = x.z;
+        vs[(c4 + 3) * kBlock + kr] = x.w;
+      } else {
+        reinterpret_cast<float4*>(vs)[u] = vg[u];
+      }
     }
     __syncthreads();
     for (int kc = 0; kc < kBlock; kc += KC) {
@@ -725,8 +750,8 @@ __global__ __launch_bounds__(1024) void k_row_order(const int32_t* __restrict__ 
 
 hipError_t launch_sparse_attn(const KGeom& g, int dtype, float scale, const void* q, const void* k,
                               const void* vt, const int32_t* counts, const int32_t* lists, void* out,
-                              int out_original_order, int qk_original_order, float* lse, int32_t* row_order,
-                              hipStream_t s) {
+                              int out_original_order, int qk_original_order, int v_original_order, float* lse,
+                              int32_t* row_order, hipStream_t s) {
   const unsigned bhs = (unsigned)(g.B * g.H);
   if (dtype == ABLA_BF16) {
     const int F = g.nbh * g.nbw;
@@ -755,16 +780,16 @@ hipError_t launch_sparse_attn(const KGeom& g, int dtype, float scale, const void
     a.magic_f = (1ull << 32) / (unsigned long long)F + 1;
     a.magic_w = (1ull << 32) / (unsigned long long)g.nbw + 1;
     const dim3 grid((unsigned)a.grid);
-    if (qk_original_order) {
-      if (g.d == 128)
-        k_attn_bf16<128, true><<<grid, 256, 0, s>>>(a);
-      else
-        k_attn_bf16<64, true><<<grid, 256, 0, s>>>(a);
-    } else {
-      if (g.d == 128)
-        k_attn_bf16<128, false><<<grid, 256, 0, s>>>(a);
-      else
-        k_attn_bf16<64, false><<<grid, 256, 0, s>>>(a);
+    const int variant = (g.d == 128 ? 4 : 0) | (qk_original_order ? 2 : 0) | (v_original_order ? 1 : 0);
+    switch (variant) {
+      case 7: k_attn_bf16<128, true, true><<<grid, 256, 0, s>>>(a); break;
+      case 6: k_attn_bf16<128, true, false><<<grid, 256, 0, s>>>(a); break;
+      case 5: k_attn_bf16<128, false, true><<<grid, 256, 0, s>>>(a); break;
+      case 4: k_attn_bf16<128, false, false><<<grid, 256, 0, s>>>(a); break;
+      case 3: k_attn_bf16<64, true, true><<<grid, 256, 0, s>>>(a); break;
+      case 2: k_attn_bf16<64, true, false><<<grid, 256, 0, s>>>(a); break;
+      case 1: k_attn_bf16<64, false, true><<<grid, 256, 0, s>>>(a); break;
+      default: k_attn_bf16<64, false, false><<<grid, 256, 0, s>>>(a); break;
     }
   } else {
     k_row_order<<<dim3(bhs), 1024, 0, s>>>(counts, row_order, g.nb);
@@ -783,6 +808,7 @@ hipError_t launch_sparse_attn(const KGeom& g, int dtype, float scale, const void
     a.scale = scale;
     a.orig = out_original_order;
     a.qk_orig = qk_original_order;
+    a.v_orig = v_original_order;
     const dim3 grid((unsigned)((long long)bhs * g.nb));
     if (g.d == 128)
       k_attn_f32<128><<<grid, 128, 0, s>>>(a);

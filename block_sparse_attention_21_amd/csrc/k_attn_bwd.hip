@@ -103,32 +103,6 @@ __device__ __forceinline__ bf16x8_t row_chunk(const char* tile, int half, int la
   return *reinterpret_cast<const bf16x8_t*>(tile + row * D * 2 + c * 16);
 }
 
-typedef short i16x4_t __attribute__((ext_vector_type(4)));
-typedef __attribute__((address_space(3))) i16x4_t* lds_i16x4_ptr;
-
-// A-operand chunk of the TRANSPOSE of a token-major tile X, read with the gfx950 LDS transpose
-// load: lane l receives X^T[dt*32 + l%32][tb + 8*(l/32) + e], e = 0..7, i.e. 8 consecutive
-// tokens of one channel. ds_read_tr16_b64 works on groups of 16 lanes: each lane names 8 bytes
-// (4 bf16) and lane i of the group receives element i%4 of the read named by lane 4e + i/4 as its
-// element e. So lane m of a group names token tb + 8*hi + 4*half + m/4, channels
-// c0 + 4*(m%4) .. +3 (c0 = dt*32 + 16*(group&1)), and lane i then holds channel c0 + i of four
-// consecutive tokens; two such reads give the 8 tokens.
-template <int D>
-__device__ __forceinline__ bf16x8_t tr_chunk(const char* tile, int dt, int tb, int lane) {
-  const int g = lane >> 4, m = lane & 15;
-  const int ch = dt * 32 + 16 * (g & 1) + 4 * (m & 3);
-  const int tok = tb + 8 * (g >> 1) + (m >> 2);
-  const int r0 = kperm(tok), r1 = kperm(tok + 4);
-  const char* p0 = tile + r0 * D * 2 + (((ch >> 3) ^ k_swz<D>(r0)) << 4) + (ch & 7) * 2;
-  const char* p1 = tile + r1 * D * 2 + (((ch >> 3) ^ k_swz<D>(r1)) << 4) + (ch & 7) * 2;
-  const i16x4_t a = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4_ptr)p0);
-  const i16x4_t b = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4_ptr)p1);
-  const i16x4_t both[2] = {a, b};
-  bf16x8_t out;
-  __builtin_memcpy(&out, both, 16);
-  return out;
-}
-
 // Write rows of one wave's transposed accumulators acc[k][r] = X^T[channel (dt0+k)*32 + 8*(r/4)
 // + 4*hi + r%4][row lane%32], k < NDT, as bf16 x * mul into the original-order tensor y, row =
 // token of (blk, row_local).

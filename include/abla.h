@@ -168,10 +168,13 @@ size_t abla_sparse_attn_workspace_bytes(const abla_geom* g);
  *           the caller's [B,H,N,d] tensors in the original token order (the kernel then
  *           gathers each 64-token block as its 8 runs of 8 tokens, so no reordered copies of
  *           Q and K are needed; the result is the same).
- * v_rt:     fractal order, ABLA_LAYOUT_BLOCK_T.
+ * v_rt:     fractal order, ABLA_LAYOUT_BLOCK_T; or, with ABLA_ATTN_V_ORIGINAL, the caller's
+ *           [B,H,N,d] V in the original token order (bf16: its tiles are staged token-major and
+ *           the V^T operand is read with the LDS transpose load).
  * counts, lists: as produced by abla_build_mask (lists ascending).
  * layout_flags: ABLA_ATTN_OUT_ORIGINAL (out in the original token order, else fractal order)
- *      | ABLA_ATTN_QK_ORIGINAL (q_r / k_r given in the original order); other bits INVALID.
+ *      | ABLA_ATTN_QK_ORIGINAL (q_r / k_r given in the original order)
+ *      | ABLA_ATTN_V_ORIGINAL (v_rt given in the original order); other bits INVALID.
  * out: [B,H,N,d], same dtype, in the order layout_flags names.
  * lse: [B,H,N] float32 or NULL: natural-log sum of exp(scale * scores) over
  *      the allowed keys, indexed in fractal order; -inf for a row whose list
@@ -184,7 +187,7 @@ size_t abla_sparse_attn_workspace_bytes(const abla_geom* g);
  * workspace: at least abla_sparse_attn_workspace_bytes(g) bytes.
  * Errors: as abla_reorder, plus INVALID for null counts/lists/out, q_r/k_r/v_rt
  * aliasing out, unknown layout_flags bits, and WORKSPACE. */
-enum { ABLA_ATTN_OUT_ORIGINAL = 1, ABLA_ATTN_QK_ORIGINAL = 2 };
+enum { ABLA_ATTN_OUT_ORIGINAL = 1, ABLA_ATTN_QK_ORIGINAL = 2, ABLA_ATTN_V_ORIGINAL = 4 };
 
 abla_status abla_sparse_attn_fwd(const abla_geom* g, int32_t dtype, float scale,
                                  const void* q_r, const void* k_r, const void* v_rt,

@@ -127,9 +127,9 @@ def test_attention_errors(A):
     assert attn_call(A, g, scale=math.nan) == 1
     assert attn_call(A, g, scale=-0.5) == 1
     assert attn_call(A, g, ws=None) == 3
-    assert attn_call(A, g, flags=4) == 1  # unknown layout flag
+    assert attn_call(A, g, flags=8) == 1  # unknown layout flag
     assert attn_call(A, g, flags=-1) == 1
-    assert attn_call(A, g, flags=3, ws=None) == 3  # both known flags pass the argument checks
+    assert attn_call(A, g, flags=7, ws=None) == 3  # the known flags pass the argument checks
     assert attn_call(A, g, ws_bytes=2 * 18 * 4 - 1) == 3
     assert attn_call(A, G(A, d=32)) == 2
     assert A.sparse_attn_workspace_bytes(A.Geometry(1, 2, 3, 16, 24, 128)) == 2 * 18 * 4 + 256

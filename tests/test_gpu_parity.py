@@ -150,9 +150,10 @@ def test_fractal_order_output_and_determinism(A):
     ("bf16", 128, (1, 1, 2, 8, 8)), ("bf16", 64, (1, 1, 5, 8, 136)),
 ])
 def test_fused_and_unfused_paths_agree(A, dtype, d, geo):
-    """Q and K read in the original order (the default path: pooling only, no reordered copies)
-    give bit-identically the output and LSE of the path that reads fractal-order copies; the
-    pooling-only pass writes the same block means as the reorder + pool pass."""
+    """Q and K read in the original order (the default path: pooling only, no reordered copies),
+    and V as well (its V^T operand through LDS transpose loads), give bit-identically the output
+    and LSE of the path that reads fractal-order copies; the pooling-only pass writes the same
+    block means as the reorder + pool pass."""
     B, H, T, Hs, Ws = geo
     geom, og = PT.geoms(B, H, T, Hs, Ws, d)
     q, k, v = make_random_qkv(B, H, T, Hs, Ws, d, dtype, seed=9, device=DEV)
@@ -160,14 +161,17 @@ def test_fused_and_unfused_paths_agree(A, dtype, d, geo):
     prm = A.MaskParams(mode="cdf", thr=0.7)
     fused = A.NablaAttention(geom, prm, dtype=q.dtype, want_lse=True)
     plain = A.NablaAttention(geom, prm, dtype=q.dtype, want_lse=True, fused=False)
+    all_orig = A.NablaAttention(geom, prm, dtype=q.dtype, want_lse=True, fuse_v=True)
     fused(q, k, v)
     plain(q, k, v)
+    all_orig(q, k, v)
     torch.cuda.synchronize()
-    assert fused.q_r is None and plain.q_r is not None
+    assert fused.q_r is None and plain.q_r is not None and all_orig.v_rt is None
     assert torch.equal(fused.qbar, plain.qbar) and torch.equal(fused.kbar, plain.kbar)
     assert torch.equal(fused.words, plain.words)
-    assert np.array_equal(_bits(fused.out), _bits(plain.out))
-    assert torch.equal(fused.lse, plain.lse)
+    for run in (fused, all_orig):
+        assert np.array_equal(_bits(run.out), _bits(plain.out))
+        assert torch.equal(run.lse, plain.lse)
 
 
 def test_graph_replay_matches_eager(A):
