@@ -194,16 +194,19 @@ def test_backward_deterministic_and_reusable_workspace(A):
         assert torch.equal(x.view(torch.int16), y.view(torch.int16))
 
 
-def _sampled_480p(A, w, og, geom, q, k, v, dout, run):
-    """Sampled blocks of two heads: (head, query blocks, key blocks, rows whose O / lse decide them)."""
+def _sampled(og, run, heads, n_rand_q=2, kcols=("max", "min", "rand")):
+    """Sampled blocks per head: (head, query blocks, key blocks, rows whose O / lse decide them).
+    Query blocks: the longest row plus random ones; key blocks: the longest / shortest column
+    and a random one, as asked."""
     gm = PT.gpu_mask(run.words, og)
     rng = np.random.default_rng(1)
     picks = []
-    for h in (0, og.H - 1):
+    for h in heads:
         m = gm[0, h]
-        qblocks = sorted(set([int(m.sum(1).argmax())] + rng.integers(0, og.nb, 2).tolist()))
+        qblocks = sorted(set([int(m.sum(1).argmax())] + rng.integers(0, og.nb, n_rand_q).tolist()))
         col = m.sum(0)
-        kblocks = sorted(set([int(col.argmax()), int(col.argmin()), int(rng.integers(0, og.nb))]))
+        pick = {"max": int(col.argmax()), "min": int(col.argmin()), "rand": int(rng.integers(0, og.nb))}
+        kblocks = sorted(set(pick[c] for c in kcols))
         need = sorted(set(qblocks).union(*[np.nonzero(m[:, j])[0].tolist() for j in kblocks]))
         picks.append((h, qblocks, kblocks, need))
     return gm, picks
@@ -227,6 +230,7 @@ def _compare_sampled(og, q, k, v, dout, gm, picks, dq, dk, dv, tag, o_given=None
         ref["dq"].append(rq)
         for j in kblocks:
             keeps = np.nonzero(m[:, j])[0]
+            print(f"  oracle backward, head {h}, key block {j}: {len(keeps)} query blocks keep it", flush=True)
             krows = PT.sample_rows(og, [j])
             qrows = PT.sample_rows(og, keeps) if len(keeps) else np.zeros(0, dtype=np.int64)
             _, rk, rv = R.masked_attention_backward_head(Qr, Kr, Vr, dOr, m, gh, scale, rows=qrows, O=Og)
@@ -241,27 +245,27 @@ def _compare_sampled(og, q, k, v, dout, gm, picks, dq, dk, dv, tag, o_given=None
         PT.compare_grad(np.concatenate(got[n]), np.concatenate(ref[n]), f"{tag} {n}")
 
 
-def _setup_480p(A):
-    w = WORKLOADS["480p"]
+def _setup(A, name, **over):
+    w = WORKLOADS[name].with_(**over) if over else WORKLOADS[name]
     geom, og = PT.geoms(w.B, w.H, w.T, w.Hs, w.Ws, w.d, w.P)
     q, k, v = make_qkv(w, device=DEV)
     dout = make_dout(w.B, w.H, geom.N, w.d, seed=7, device=DEV)
-    run = A.NablaAttention(geom, A.MaskParams(mode=w.mode, thr=w.thr, tau=w.tau, sta=tuple(w.sta), gamma=w.gamma, lam=w.lam),
-                           want_lse=True)
+    run = A.NablaAttention(geom, A.MaskParams(mode=w.mode, thr=w.thr, tau=w.tau, sta=tuple(w.sta), gamma=w.gamma,
+                                              lam=w.lam), want_lse=True)
     run(q, k, v)
     torch.cuda.synchronize()
     return w, geom, og, q, k, v, dout, run
 
 
-def test_backward_480p_kernel_parity_sampled(A):
-    """Full-size 480p (12 heads, nb = 588): the backward entry point handed the oracle's O (bf16)
-    and lse on every row that the sampled outputs depend on (the sampled query blocks and every
-    query block keeping a sampled key block). The remaining rows get O = 0 and an lse of
-    float32 max, which makes their P zero; they only feed outputs that are not compared."""
-    w, geom, og, q, k, v, dout, run = _setup_480p(A)
-    gm, picks = _sampled_480p(A, w, og, geom, q, k, v, dout, run)
+def _kernel_parity_sampled(A, tag, name, heads, n_rand_q=2, kcols=("max", "min", "rand"), **over):
+    """The backward entry point handed the oracle's O (bf16) and lse on every row that the
+    sampled outputs depend on (the sampled query blocks and every query block keeping a
+    sampled key block). The remaining rows get O = 0 and an lse of float32 max, which makes
+    their P zero; they only feed outputs that are not compared."""
+    w, geom, og, q, k, v, dout, run = _setup(A, name, **over)
+    gm, picks = _sampled(og, run, heads(og), n_rand_q, kcols)
     scale = 1.0 / math.sqrt(og.d)
-    pos = R.fractal_positions(og)
+    inv = np.argsort(R.fractal_positions(og))
     O = np.zeros((og.B, og.H, og.N, og.d))
     lse = np.full((og.B, og.H, og.N), np.finfo(np.float32).max)
     for h, _, _, need in picks:
@@ -269,22 +273,41 @@ def test_backward_480p_kernel_parity_sampled(A):
         Kr, _ = _head(k, 0, h, og)
         Vr, _ = _head(v, 0, h, og)
         rows = PT.sample_rows(og, need)
+        print(f"  oracle forward, head {h}: {len(need)} query blocks", flush=True)
         Or, lr = R.masked_attention_head(Qr, Kr, Vr, gm[0, h], gh, scale, rows=rows)
-        inv = np.argsort(pos)
         O[0, h, inv[rows]] = Or
         lse[0, h, rows] = lr
     o = torch.from_numpy(O).to(torch.bfloat16).to(DEV)
     lse_t = torch.from_numpy(lse.astype(np.float32)).to(DEV)
-    print("backward 480p full size, oracle O / lse", flush=True)
+    print(f"backward {tag} full size, oracle O / lse on {sum(len(p[3]) for p in picks)} query blocks", flush=True)
     dq, dk, dv = A.sparse_attn_bwd(q, k, v, o, dout, lse_t, run.words, run.counts, run.lists, geom)
     torch.cuda.synchronize()
-    _compare_sampled(og, q, k, v, dout, gm, picks, dq, dk, dv, "480p kernel", o_given=o)
+    _compare_sampled(og, q, k, v, dout, gm, picks, dq, dk, dv, f"{tag} kernel", o_given=o)
+
+
+def test_backward_480p_kernel_parity_sampled(A):
+    """Full-size 480p (12 heads, nb = 588), two heads, longest / shortest / random columns."""
+    _kernel_parity_sampled(A, "480p", "480p", lambda og: (0, og.H - 1))
+
+
+def test_backward_720p_kernel_parity_sampled(A):
+    """Full-size 720p (40 heads, nb = 1260): dQ on sampled query blocks of two heads, dK / dV on
+    each head's shortest column (the longest would take the oracle minutes)."""
+    _kernel_parity_sampled(A, "720p", "720p", lambda og: (0, og.H - 1), n_rand_q=1, kcols=("min",))
+
+
+def test_backward_maximum_blocks_per_row(A):
+    """nb = 4096 key blocks (16 frames of 128 x 128 tokens, one head, d = 64): column lists of
+    the largest size; dQ on two query blocks, dK / dV on the shortest column. A tight dynamic
+    threshold (tau = 0.5) keeps the columns short enough for the oracle."""
+    _kernel_parity_sampled(A, "max-nb", "480p", lambda og: (0,), n_rand_q=1, kcols=("min",),
+                           H=1, T=16, Hs=128, Ws=128, d=64, mode="dyn", tau=0.5)
 
 
 def test_backward_480p_end_to_end_sampled(A):
     """Full-size 480p, GPU forward then GPU backward, against the exact oracle gradients."""
-    w, geom, og, q, k, v, dout, run = _setup_480p(A)
-    gm, picks = _sampled_480p(A, w, og, geom, q, k, v, dout, run)
+    w, geom, og, q, k, v, dout, run = _setup(A, "480p")
+    gm, picks = _sampled(og, run, (0, og.H - 1))
     print("backward 480p full size, end to end", flush=True)
     dq, dk, dv = run.backward(q, k, v, dout)
     torch.cuda.synchronize()
