@@ -197,6 +197,12 @@ __global__ __launch_bounds__(kBwdThreads) __attribute__((amdgpu_waves_per_eu(2, 
 #pragma unroll
     for (int r = 0; r < 16; ++r) acc[dt][r] = 0.f;
 
+  // K^T operand reads: offsets inside a K tile for each channel tile (keys kh*32 ..); the
+  // second 16 keys are 16 rows further, an immediate offset.
+  uint32_t trel[2 * DT];
+#pragma unroll
+  for (int dt = 0; dt < DT; ++dt) tr_rel<D>(dt, kh * 32, lane, trel[2 * dt], trel[2 * dt + 1]);
+
   const int32_t* lst = a.lists + row * nb;
   if (cnt > 0) {
     const uint32_t j0 = (uint32_t)min(max(ld_const(lst, 0), 0), nb - 1);
@@ -233,12 +239,22 @@ __global__ __launch_bounds__(kBwdThreads) __attribute__((amdgpu_waves_per_eu(2, 
       dsb[r >> 3][r & 7] = (__bf16)(p * (dp[r] - dq_d));
     }
     // dQ^T += K^T dS^T over this wave's 32 keys; K^T comes from the K tile by transpose loads.
+    uint32_t ta[2 * DT];
+    const uint32_t kbase = lds_offset(ks_lds);
 #pragma unroll
-    for (int kk = 0; kk < 2; ++kk)
+    for (int k = 0; k < 2 * DT; ++k) ta[k] = kbase + trel[k];
+    {
+      bf16x8_t kt[DT];
+      tr_chunks_at<DT, 0>(ta, kt);
 #pragma unroll
-      for (int dt = 0; dt < DT; ++dt)
-        acc[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(tr_chunk<D>(ks_lds, dt, kh * 32 + kk * 16, lane), dsb[kk],
-                                                          acc[dt], 0, 0, 0);
+      for (int dt = 0; dt < DT; ++dt) acc[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kt[dt], dsb[0], acc[dt], 0, 0, 0);
+    }
+    {
+      bf16x8_t kt[DT];
+      tr_chunks_at<DT, 16 * D * 2>(ta, kt);
+#pragma unroll
+      for (int dt = 0; dt < DT; ++dt) acc[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kt[dt], dsb[1], acc[dt], 0, 0, 0);
+    }
   }
   // Waves (qh, 0) and (qh, 1) hold partial dQ^T over their key halves: wave (qh, kh) finishes
   // channel tiles [kh*DT/2, kh*DT/2 + DT/2) and hands the other half to its partner.
@@ -270,6 +286,43 @@ struct DkvArgs {
   KGeom g;
   float c2, scale;
 };
+
+// One 16-query half q8 of a dK/dV step: P = exp2(c2*S - L2) and dS = P * (dP - D) for this
+// lane's key and queries qh*32 + 16*q8 + 8*hi + 0..7 (registers q8*8 .. q8*8+7 of s and dp),
+// then the dV^T and dK^T products over those queries. ta: the transpose-read addresses of the
+// Q tile for queries qh*32 ..; the dO tile sits two tiles further.
+template <int D, int DT, int Q8>
+__device__ __forceinline__ void half_step(const uint32_t* ta, const float* l2_lds, const float* d_lds, int qh, int hi,
+                                          float c2, const f32x16_t& s, const f32x16_t& dp, f32x16_t* dk,
+                                          f32x16_t* dv) {
+  constexpr int TB = kBlock * D * 2;
+  const int q0 = qh * 32 + 16 * Q8 + 8 * hi;
+  float4 la, lb, da, db;
+  lds_read4x16(reinterpret_cast<const char*>(l2_lds + q0), reinterpret_cast<const char*>(l2_lds + q0 + 4),
+               reinterpret_cast<const char*>(d_lds + q0), reinterpret_cast<const char*>(d_lds + q0 + 4), la, lb, da,
+               db);
+  const float lq[8] = {la.x, la.y, la.z, la.w, lb.x, lb.y, lb.z, lb.w};
+  const float dd[8] = {da.x, da.y, da.z, da.w, db.x, db.y, db.z, db.w};
+  bf16x8_t pb, dsb;
+#pragma unroll
+  for (int e = 0; e < 8; ++e) {
+    const float p = exp2_fast(fmaf(s[Q8 * 8 + e], c2, -lq[e]));
+    pb[e] = (__bf16)p;
+    dsb[e] = (__bf16)(p * (dp[Q8 * 8 + e] - dd[e]));
+  }
+  {
+    bf16x8_t ot[DT];
+    tr_chunks_at<DT, 2 * TB + Q8 * 16 * D * 2>(ta, ot);
+#pragma unroll
+    for (int dt = 0; dt < DT; ++dt) dv[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ot[dt], pb, dv[dt], 0, 0, 0);
+  }
+  {
+    bf16x8_t qt[DT];
+    tr_chunks_at<DT, Q8 * 16 * D * 2>(ta, qt);
+#pragma unroll
+    for (int dt = 0; dt < DT; ++dt) dk[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qt[dt], dsb, dk[dt], 0, 0, 0);
+  }
+}
 
 // One workgroup per key block j, four waves: wave (kh, qh) takes keys kh*32.. and queries
 // qh*32.. of every query tile in the block's column list. Q and dO tiles (token-major) and the
@@ -330,11 +383,17 @@ __global__ __launch_bounds__(kBwdThreads) __attribute__((amdgpu_waves_per_eu(2, 
                           i * kBlock * 4, 0, 0);
     }
   };
+  // Q^T / dO^T operand reads: offsets inside a Q tile for each channel tile (queries qh*32 ..);
+  // the second 16 queries and the dO tile (two slots further) are immediate offsets.
+  uint32_t trel[2 * DT];
+#pragma unroll
+  for (int dt = 0; dt < DT; ++dt) tr_rel<D>(dt, qh * 32, lane, trel[2 * dt], trel[2 * dt + 1]);
+
   const int32_t* lst = a.col_lists + col * nb;
   if (cnt > 0) issue(0, min(max(ld_const(lst, 0), 0), nb - 1));
   for (int u = 0; u < cnt; ++u) {
     wait_vm_lgkm_barrier();  // tile u has landed; every wave is done with tile u-1
-    if (u + 1 < cnt) issue((u + 1) & 1, min(max(ld_const(lst, u + 1), 0), nb - 1));
+    const int i_next = u + 1 < cnt ? min(max(ld_const(lst, u + 1), 0), nb - 1) : -1;
     const char* q_lds = smem + (u & 1) * TB;
     const char* do_lds = smem + (2 + (u & 1)) * TB;
     const float* l2_lds = rows_lds + (u & 1) * 128;
@@ -353,35 +412,20 @@ __global__ __launch_bounds__(kBwdThreads) __attribute__((amdgpu_waves_per_eu(2, 
       s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(row_chunk<D>(q_lds, qh, lane, ks), kb[ks], s, 0, 0, 0);
       dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(row_chunk<D>(do_lds, qh, lane, ks), vb[ks], dp, 0, 0, 0);
     }
-    bf16x8_t pb[2], dsb[2];
+    // The next tile's loads go out here, after the products that read the registers this
+    // kernel keeps in scratch: a wait for those reloads would otherwise also wait for the
+    // prefetch, which shares their counter.
+    asm volatile("" ::: "memory");
+    if (i_next >= 0) issue((u + 1) & 1, i_next);
+    // Per 16-query half q8: P and dS for this lane's key, then dV^T += dO^T P and
+    // dK^T += Q^T dS over those queries, the transposed operands from transpose loads (one
+    // half's operands live at a time).
+    uint32_t ta[2 * DT];
+    const uint32_t qbase = lds_offset(q_lds);
 #pragma unroll
-    for (int q8 = 0; q8 < 2; ++q8) {
-      const int q0 = qh * 32 + 16 * q8 + 8 * hi;
-      const float4 la = *reinterpret_cast<const float4*>(l2_lds + q0);
-      const float4 lb = *reinterpret_cast<const float4*>(l2_lds + q0 + 4);
-      const float4 da = *reinterpret_cast<const float4*>(d_lds + q0);
-      const float4 db = *reinterpret_cast<const float4*>(d_lds + q0 + 4);
-      const float lq[8] = {la.x, la.y, la.z, la.w, lb.x, lb.y, lb.z, lb.w};
-      const float dd[8] = {da.x, da.y, da.z, da.w, db.x, db.y, db.z, db.w};
-#pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        const int r = q8 * 8 + e;
-        const float p = exp2_fast(fmaf(s[r], a.c2, -lq[e]));
-        pb[q8][e] = (__bf16)p;
-        dsb[q8][e] = (__bf16)(p * (dp[r] - dd[e]));
-      }
-    }
-    // dV^T += dO^T P and dK^T += Q^T dS over this wave's 32 queries; the transposed operands
-    // come from the token-major tiles by transpose loads.
-#pragma unroll
-    for (int q8 = 0; q8 < 2; ++q8)
-#pragma unroll
-      for (int dt = 0; dt < DT; ++dt) {
-        dv[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(tr_chunk<D>(do_lds, dt, qh * 32 + q8 * 16, lane), pb[q8],
-                                                         dv[dt], 0, 0, 0);
-        dk[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(tr_chunk<D>(q_lds, dt, qh * 32 + q8 * 16, lane), dsb[q8],
-                                                         dk[dt], 0, 0, 0);
-      }
+    for (int k = 0; k < 2 * DT; ++k) ta[k] = qbase + trel[k];
+    half_step<D, DT, 0>(ta, l2_lds, d_lds, qh, hi, a.c2, s, dp, dk, dv);
+    half_step<D, DT, 1>(ta, l2_lds, d_lds, qh, hi, a.c2, s, dp, dk, dv);
   }
   // Waves (kh, 0) and (kh, 1) hold partial dK^T and dV^T over their query halves: wave qh = 0
   // finishes dK, wave qh = 1 finishes dV; each hands the other its partial.

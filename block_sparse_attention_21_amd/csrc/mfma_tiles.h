@@ -136,5 +136,93 @@ __device__ __forceinline__ bf16x8_t tr_chunk(const char* tile, int dt, int tb, i
   return out;
 }
 
+// The same operands through inline asm, with the wait inside the block. The compiler's
+// wait-count pass does not prove that a ds_read_b64_tr_b16 builtin misses the LDS slot that
+// the next tile's buffer_load ... lds is filling, so before the first builtin transpose load
+// of a step it waits for every load in flight (vmcnt(0)), which stalls the next tile's
+// prefetch. The tiles read here were completed by the step's barrier and the prefetch fills
+// the other slot, so no such wait is needed; each block ends with lgkmcnt(0), so its results
+// are complete when it returns.
+__device__ __forceinline__ uint32_t lds_offset(const char* p) {
+  return (uint32_t)(uintptr_t)((const __attribute__((address_space(3))) char*)p);
+}
+// Byte offsets, relative to a token-major tile, of the two 8-byte transpose reads that give
+// lane `lane` its tr_chunk operand for channel tile dt and tokens tb + 8*(lane/32) + 0..7.
+template <int D>
+__device__ __forceinline__ void tr_rel(int dt, int tb, int lane, uint32_t& a0, uint32_t& a1) {
+  const int g = lane >> 4, m = lane & 15;
+  const int ch = dt * 32 + 16 * (g & 1) + 4 * (m & 3);
+  const int tok = tb + 8 * (g >> 1) + (m >> 2);
+  const int r0 = kperm(tok), r1 = kperm(tok + 4);
+  a0 = (uint32_t)(r0 * D * 2 + (((ch >> 3) ^ k_swz<D>(r0)) << 4) + (ch & 7) * 2);
+  a1 = (uint32_t)(r1 * D * 2 + (((ch >> 3) ^ k_swz<D>(r1)) << 4) + (ch & 7) * 2);
+}
+// out[k] = tr_chunk<D>(tile, k, tb, lane) for the NT = D/32 channel tiles, where a[2k], a[2k+1]
+// are the LDS addresses of tile + tr_rel(k, tb0, lane) and the tile / token block differs from
+// (tile, tb0) by the constant byte offset OFF. Tokens tb0 + 16*n keep the same swizzle (it
+// repeats every 16 rows), so OFF = 16*n*D*2 (plus a slot distance) is exact.
+template <int NT, int OFF>
+__device__ __forceinline__ void tr_chunks_at(const uint32_t* a, bf16x8_t (&out)[NT]);
+template <int OFF>
+__device__ __forceinline__ void tr_chunks_at_4(const uint32_t* a, bf16x8_t (&out)[4]) {
+  i16x4_t r[8];
+  asm volatile(
+      "ds_read_b64_tr_b16 %0, %8 offset:%16\n\t"
+      "ds_read_b64_tr_b16 %1, %9 offset:%16\n\t"
+      "ds_read_b64_tr_b16 %2, %10 offset:%16\n\t"
+      "ds_read_b64_tr_b16 %3, %11 offset:%16\n\t"
+      "ds_read_b64_tr_b16 %4, %12 offset:%16\n\t"
+      "ds_read_b64_tr_b16 %5, %13 offset:%16\n\t"
+      "ds_read_b64_tr_b16 %6, %14 offset:%16\n\t"
+      "ds_read_b64_tr_b16 %7, %15 offset:%16\n\t"
+      "s_waitcnt lgkmcnt(0)"
+      : "=&v"(r[0]), "=&v"(r[1]), "=&v"(r[2]), "=&v"(r[3]), "=&v"(r[4]), "=&v"(r[5]), "=&v"(r[6]), "=&v"(r[7])
+      : "v"(a[0]), "v"(a[1]), "v"(a[2]), "v"(a[3]), "v"(a[4]), "v"(a[5]), "v"(a[6]), "v"(a[7]), "i"(OFF));
+#pragma unroll
+  for (int k = 0; k < 4; ++k) {
+    const i16x4_t both[2] = {r[2 * k], r[2 * k + 1]};
+    __builtin_memcpy(&out[k], both, 16);
+  }
+}
+template <int OFF>
+__device__ __forceinline__ void tr_chunks_at_2(const uint32_t* a, bf16x8_t (&out)[2]) {
+  i16x4_t r[4];
+  asm volatile(
+      "ds_read_b64_tr_b16 %0, %4 offset:%8\n\t"
+      "ds_read_b64_tr_b16 %1, %5 offset:%8\n\t"
+      "ds_read_b64_tr_b16 %2, %6 offset:%8\n\t"
+      "ds_read_b64_tr_b16 %3, %7 offset:%8\n\t"
+      "s_waitcnt lgkmcnt(0)"
+      : "=&v"(r[0]), "=&v"(r[1]), "=&v"(r[2]), "=&v"(r[3])
+      : "v"(a[0]), "v"(a[1]), "v"(a[2]), "v"(a[3]), "i"(OFF));
+#pragma unroll
+  for (int k = 0; k < 2; ++k) {
+    const i16x4_t both[2] = {r[2 * k], r[2 * k + 1]};
+    __builtin_memcpy(&out[k], both, 16);
+  }
+}
+template <int NT, int OFF>
+__device__ __forceinline__ void tr_chunks_at(const uint32_t* a, bf16x8_t (&out)[NT]) {
+  if constexpr (NT == 4)
+    tr_chunks_at_4<OFF>(a, out);
+  else
+    tr_chunks_at_2<OFF>(a, out);
+}
+
+// Four 16-byte LDS reads through inline asm, completed inside the block (lgkmcnt(0)). For
+// LDS rows that sit next to a slot being filled by an LDS DMA: a plain read there gets a
+// wait for every load in flight, the prefetch included (see tr_chunks_at).
+__device__ __forceinline__ void lds_read4x16(const char* p0, const char* p1, const char* p2, const char* p3,
+                                             float4& r0, float4& r1, float4& r2, float4& r3) {
+  asm volatile(
+      "ds_read_b128 %0, %4\n\t"
+      "ds_read_b128 %1, %5\n\t"
+      "ds_read_b128 %2, %6\n\t"
+      "ds_read_b128 %3, %7\n\t"
+      "s_waitcnt lgkmcnt(0)"
+      : "=&v"(r0), "=&v"(r1), "=&v"(r2), "=&v"(r3)
+      : "v"(lds_offset(p0)), "v"(lds_offset(p1)), "v"(lds_offset(p2)), "v"(lds_offset(p3)));
+}
+
 }  // namespace
 }  // namespace abla
