@@ -143,6 +143,25 @@ __device__ __forceinline__ void unstash_add(const float* src, f32x16_t* acc, int
 
 constexpr int kBwdThreads = 256;  // four waves
 
+// Block visited by workgroup `wg`: the blocks of one patch in successive frames (a temporal
+// column) run back to back on one XCD, columns dealt round-robin to the 8 XCDs (workgroup w
+// runs on XCD w % 8). Temporally adjacent blocks keep largely the same key (or query) blocks,
+// so the tiles one workgroup fetches are still in that XCD's L2 for the next. The position
+// within a head maps to a column-major index (column * T + frame); columns that do not fill a
+// last round of 8 keep their column-major place. Heads run in order.
+__device__ __forceinline__ void column_order(int wg, const KGeom& g, long long& bh, int& blk) {
+  const int F = g.nbh * g.nbw, T = g.T, nb = g.nb;
+  bh = wg / nb;
+  const int pos = wg - (int)(bh * nb);
+  const int full = (F / 8) * 8 * T;  // positions in whole rounds of 8 columns
+  int cm = pos;
+  if (pos < full) {
+    const int x = pos & 7, k = pos >> 3;
+    cm = (8 * (k / T) + x) * T + k % T;
+  }
+  blk = (cm % T) * F + cm / T;
+}
+
 // ------------------------------------------------------------------- dQ
 struct DqArgs {
   const uint16_t *q_r, *k_r, *v_r, *do_r;
@@ -166,8 +185,9 @@ __global__ __launch_bounds__(kBwdThreads) __attribute__((amdgpu_waves_per_eu(2, 
   const int t = threadIdx.x, lane = t & 63, hi = lane >> 5;
   const int w = __builtin_amdgcn_readfirstlane(t >> 6);
   const int qh = w & 1, kh = w >> 1;
-  const long long bh = blockIdx.x / nb;
-  const int i = blockIdx.x - (int)(bh * nb);
+  long long bh;
+  int i;
+  column_order(blockIdx.x, g, bh, i);
   const long long row = bh * nb + i;
   const int cnt = min(max(ld_const(a.counts, row), 0), nb);
   const int q_local = qh * 32 + (lane & 31);
@@ -338,8 +358,9 @@ __global__ __launch_bounds__(kBwdThreads) __attribute__((amdgpu_waves_per_eu(2, 
   const int t = threadIdx.x, lane = t & 63, hi = lane >> 5;
   const int w = __builtin_amdgcn_readfirstlane(t >> 6);
   const int kh = w & 1, qh = w >> 1;
-  const long long bh = blockIdx.x / nb;
-  const int j = blockIdx.x - (int)(bh * nb);
+  long long bh;
+  int j;
+  column_order(blockIdx.x, g, bh, j);
   const long long col = bh * nb + j;
   const int cnt = min(max(ld_const(a.col_counts, col), 0), nb);
   const int k_local = kh * 32 + (lane & 31);
