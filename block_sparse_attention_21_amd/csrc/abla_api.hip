@@ -56,22 +56,20 @@ abla_status from_hip(hipError_t e) { return e == hipSuccess ? ABLA_OK : ABLA_ERR
 
 size_t align256(size_t n) { return (n + 255) & ~(size_t)255; }
 
-// Backward scratch: four fractal copies of a [B,H,N,d] bf16 tensor, D and L2 ([B,H,N]
-// float32), column counts [B,H,nb] and column lists [B,H,nb,nb] (int32), each 256-aligned.
+// Backward scratch: D and L2 ([B,H,N] float32), column counts [B,H,nb] and column lists
+// [B,H,nb,nb] (int32), each 256-aligned.
 size_t bwd_parts(const abla_geom* g, BwdWorkspace* ws, char* base) {
   const size_t bh = bh_of(g), nb = (size_t)nb_of(g);
   const size_t n = (size_t)g->T * (size_t)g->Hs * (size_t)g->Ws;
-  const size_t x = align256(bh * n * (size_t)g->d * 2), rows = align256(bh * n * 4);
+  const size_t rows = align256(bh * n * 4);
   const size_t cc = align256(bh * nb * 4), cl = align256(bh * nb * nb * 4);
   if (ws) {
-    uint16_t** t[4] = {&ws->q_r, &ws->k_r, &ws->v_r, &ws->do_r};
-    for (int i = 0; i < 4; ++i) *t[i] = reinterpret_cast<uint16_t*>(base + i * x);
-    ws->D = reinterpret_cast<float*>(base + 4 * x);
-    ws->L2 = reinterpret_cast<float*>(base + 4 * x + rows);
-    ws->col_counts = reinterpret_cast<int32_t*>(base + 4 * x + 2 * rows);
-    ws->col_lists = reinterpret_cast<int32_t*>(base + 4 * x + 2 * rows + cc);
+    ws->D = reinterpret_cast<float*>(base);
+    ws->L2 = reinterpret_cast<float*>(base + rows);
+    ws->col_counts = reinterpret_cast<int32_t*>(base + 2 * rows);
+    ws->col_lists = reinterpret_cast<int32_t*>(base + 2 * rows + cc);
   }
-  return 4 * x + 2 * rows + cc + cl;
+  return 2 * rows + cc + cl;
 }
 
 }  // namespace

@@ -60,9 +60,8 @@ hipError_t launch_sparse_attn(const KGeom& g, int dtype, float scale, const void
 // Device scratch of the backward pass, carved out of the caller's workspace
 // (see abla_sparse_attn_bwd_workspace_bytes).
 struct BwdWorkspace {
-  uint16_t *q_r, *k_r, *v_r, *do_r;  // token-major fractal copies, [B,H,N,d] each
-  float *D, *L2;                        // [B,H,N] fractal order
-  int32_t *col_counts, *col_lists;      // [B,H,nb], [B,H,nb,nb]
+  float *D, *L2;                    // [B,H,N] fractal order
+  int32_t *col_counts, *col_lists;  // [B,H,nb], [B,H,nb,nb]
 };
 hipError_t launch_sparse_attn_bwd(const KGeom& g, float scale, const void* q, const void* k, const void* v,
                                   const void* o, const void* dout, const float* lse, const uint32_t* words,

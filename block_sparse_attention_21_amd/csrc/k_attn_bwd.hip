@@ -7,9 +7,10 @@
 //   dV = P^T dO,  dP = dO V^T,  D_i = <dO_i, O_i>,  dS = P * (dP - D),
 //   dQ = scale * dS K,  dK = scale * dS^T Q.
 //
-// Pre-passes: token-major fractal copies of Q, K, V, dO; D and log2(e) * lse per fractal row
-// (k_bwd_delta); for every key block the ascending list of query blocks that keep it
-// (k_col_lists).
+// Pre-passes: D and log2(e) * lse per fractal row (k_bwd_delta); for every key block the
+// ascending list of query blocks that keep it (k_col_lists). Q, K, V and dO are read in their
+// original token order: a 64-token block is gathered as its 8 runs of 8 tokens, so no
+// reordered copies are made.
 //
 // k_bwd_dq, one workgroup of four waves per query block, walks the block's kept list: wave
 // (qh, kh) forms S^T = K Q^T and dP^T = V dO^T for keys kh*32.. and queries qh*32.. with the K /
@@ -85,14 +86,26 @@ __global__ __launch_bounds__(256) void k_col_lists(const uint32_t* __restrict__ 
 }
 
 // ------------------------------------------------------------------- operands
-// Offset (bytes, within a tile) of the 16-byte source chunk that LDS unit t of a token-major
-// tile holds: LDS row r = t / KCH holds row kperm(r) of the block, its chunks XOR-swizzled by
-// k_swz(r). issue_rows advances it by 4096 bytes per further load of the thread.
+// Token-major tiles gathered from a tensor in the original token order: block j is 8 runs of
+// 8 tokens (one per patch row); in LDS, row r holds token kperm(r) of the block with its
+// 16-byte chunks XOR-swizzled by k_swz(r). orig_tile_off gives thread t's fixed offset from the block's
+// corner token (LDS row r = t / KCH holds key kperm(r), kperm(r) / 8 patch rows of Ws tokens
+// and kperm(r) % 8 tokens in); consecutive loads of a thread are 16 (d = 128) or 32 (d = 64)
+// LDS rows, i.e. 2 or 4 patch rows, 512 * Ws bytes apart; orig_tile_base is the corner's byte
+// offset inside the head.
 template <int D>
-__device__ __forceinline__ uint32_t token_tile_off(int t) {
+__device__ __forceinline__ uint32_t orig_tile_off(int t, int Ws) {
   constexpr int KCH = D / 8;
   const int r = t / KCH, pc = t % KCH;
-  return (uint32_t)(kperm(r) * D * 2 + ((pc ^ k_swz<D>(r)) * 16));
+  const int kr = kperm(r);
+  return (uint32_t)(((kr >> 3) * Ws + (kr & 7)) * D * 2 + ((pc ^ k_swz<D>(r)) * 16));
+}
+template <int D>
+__device__ __forceinline__ uint32_t orig_tile_base(const KGeom& g, int j) {
+  const int F = g.nbh * g.nbw;
+  const int tf = j / F, rem = j - tf * F;
+  const int hp = rem / g.nbw, wp = rem - hp * g.nbw;
+  return (uint32_t)(((tf * g.Hs + hp * kP) * g.Ws + wp * kP) * D * 2);
 }
 
 // A-operand chunk of a token-major tile: row (half*32 + lane%32), k-step ks.
@@ -164,7 +177,7 @@ __device__ __forceinline__ void column_order(int wg, const KGeom& g, long long& 
 
 // ------------------------------------------------------------------- dQ
 struct DqArgs {
-  const uint16_t *q_r, *k_r, *v_r, *do_r;
+  const uint16_t *q, *k, *v, *dout;  // original token order
   const float *Dm, *L2;
   const int32_t *counts, *lists;
   uint16_t* dq;
@@ -195,8 +208,9 @@ __global__ __launch_bounds__(kBwdThreads) __attribute__((amdgpu_waves_per_eu(2, 
 
   bf16x8_t qv[D / 16], dov[D / 16];
   {
-    const uint16_t* qrow = a.q_r + (bh * g.N + m) * D + 8 * hi;
-    const uint16_t* drow = a.do_r + (bh * g.N + m) * D + 8 * hi;
+    const long long n = token_of(g, i, q_local);  // its token in the original order
+    const uint16_t* qrow = a.q + (bh * g.N + n) * D + 8 * hi;
+    const uint16_t* drow = a.dout + (bh * g.N + n) * D + 8 * hi;
 #pragma unroll
     for (int ks = 0; ks < D / 16; ++ks) {
       qv[ks] = *reinterpret_cast<const bf16x8_t*>(qrow + ks * 16);
@@ -207,9 +221,10 @@ __global__ __launch_bounds__(kBwdThreads) __attribute__((amdgpu_waves_per_eu(2, 
   const float dq_d = a.Dm[bh * g.N + m];
 
   const uint32_t head_bytes = (uint32_t)(g.N * D * 2);
-  const i32x4_t krs = make_rsrc(a.k_r + bh * g.N * D, head_bytes);
-  const i32x4_t vrs = make_rsrc(a.v_r + bh * g.N * D, head_bytes);
-  const uint32_t off = token_tile_off<D>(t);
+  const i32x4_t krs = make_rsrc(a.k + bh * g.N * D, head_bytes);
+  const i32x4_t vrs = make_rsrc(a.v + bh * g.N * D, head_bytes);
+  const uint32_t off = orig_tile_off<D>(t, g.Ws);
+  const uint32_t stride = 512u * (uint32_t)g.Ws;
 
   f32x16_t acc[DT];
 #pragma unroll
@@ -226,15 +241,17 @@ __global__ __launch_bounds__(kBwdThreads) __attribute__((amdgpu_waves_per_eu(2, 
   const int32_t* lst = a.lists + row * nb;
   if (cnt > 0) {
     const uint32_t j0 = (uint32_t)min(max(ld_const(lst, 0), 0), nb - 1);
-    issue_rows<TB>(smem, w, krs, j0 * TB, off);
-    issue_rows<TB>(smem + 2 * TB, w, vrs, j0 * TB, off);
+    const uint32_t b0 = orig_tile_base<D>(g, (int)j0);
+    issue_rows<TB>(smem, w, krs, b0, off, stride);
+    issue_rows<TB>(smem + 2 * TB, w, vrs, b0, off, stride);
   }
   for (int u = 0; u < cnt; ++u) {
     wait_vm_lgkm_barrier();  // tile u has landed; every wave is done with tile u-1
     if (u + 1 < cnt) {
       const uint32_t jn = (uint32_t)min(max(ld_const(lst, u + 1), 0), nb - 1);
-      issue_rows<TB>(smem + ((u + 1) & 1) * TB, w, krs, jn * TB, off);
-      issue_rows<TB>(smem + 2 * TB + ((u + 1) & 1) * TB, w, vrs, jn * TB, off);
+      const uint32_t bn = orig_tile_base<D>(g, (int)jn);
+      issue_rows<TB>(smem + ((u + 1) & 1) * TB, w, krs, bn, off, stride);
+      issue_rows<TB>(smem + 2 * TB + ((u + 1) & 1) * TB, w, vrs, bn, off, stride);
     }
     const char* ks_lds = smem + (u & 1) * TB;
     const char* vs_lds = smem + 2 * TB + (u & 1) * TB;
@@ -299,7 +316,7 @@ __global__ __launch_bounds__(kBwdThreads) __attribute__((amdgpu_waves_per_eu(2, 
 
 // ------------------------------------------------------------------- dK, dV
 struct DkvArgs {
-  const uint16_t *k_r, *v_r, *q_r, *do_r;
+  const uint16_t *k, *v, *q, *dout;  // original token order
   const float *Dm, *L2;
   const int32_t *col_counts, *col_lists;
   uint16_t *dk, *dv;
@@ -368,8 +385,9 @@ __global__ __launch_bounds__(kBwdThreads) __attribute__((amdgpu_waves_per_eu(2, 
 
   bf16x8_t kb[D / 16], vb[D / 16];
   {
-    const uint16_t* krow = a.k_r + (bh * g.N + mk) * D + 8 * hi;
-    const uint16_t* vrow = a.v_r + (bh * g.N + mk) * D + 8 * hi;
+    const long long n = token_of(g, j, k_local);  // its token in the original order
+    const uint16_t* krow = a.k + (bh * g.N + n) * D + 8 * hi;
+    const uint16_t* vrow = a.v + (bh * g.N + n) * D + 8 * hi;
 #pragma unroll
     for (int ks = 0; ks < D / 16; ++ks) {
       kb[ks] = *reinterpret_cast<const bf16x8_t*>(krow + ks * 16);
@@ -377,11 +395,12 @@ __global__ __launch_bounds__(kBwdThreads) __attribute__((amdgpu_waves_per_eu(2, 
     }
   }
   const uint32_t head_bytes = (uint32_t)(g.N * D * 2);
-  const i32x4_t qrs = make_rsrc(a.q_r + bh * g.N * D, head_bytes);
-  const i32x4_t dors = make_rsrc(a.do_r + bh * g.N * D, head_bytes);
+  const i32x4_t qrs = make_rsrc(a.q + bh * g.N * D, head_bytes);
+  const i32x4_t dors = make_rsrc(a.dout + bh * g.N * D, head_bytes);
   const i32x4_t l2rs = make_rsrc(a.L2 + bh * g.N, (uint32_t)(g.N * 4));
   const i32x4_t drs = make_rsrc(a.Dm + bh * g.N, (uint32_t)(g.N * 4));
-  const uint32_t off = token_tile_off<D>(t);
+  const uint32_t off = orig_tile_off<D>(t, g.Ws);
+  const uint32_t stride = 512u * (uint32_t)g.Ws;
 
   f32x16_t dk[DT], dv[DT];
 #pragma unroll
@@ -395,8 +414,9 @@ __global__ __launch_bounds__(kBwdThreads) __attribute__((amdgpu_waves_per_eu(2, 
   // Loads of query tile i into slot sl: Q and dO tiles, and 64 floats each of L2 and D (wave 0,
   // lanes 0-15 with 16 bytes each).
   auto issue = [&](int sl, int i) {
-    issue_rows<TB>(smem + sl * TB, w, qrs, (uint32_t)i * TB, off);
-    issue_rows<TB>(smem + (2 + sl) * TB, w, dors, (uint32_t)i * TB, off);
+    const uint32_t base = orig_tile_base<D>(g, i);
+    issue_rows<TB>(smem + sl * TB, w, qrs, base, off, stride);
+    issue_rows<TB>(smem + (2 + sl) * TB, w, dors, base, off, stride);
     if (t < 16) {
       raw_buffer_load_lds(l2rs, (__attribute__((address_space(3))) uint32_t*)(rows_lds + sl * 128), 16, t * 16,
                           i * kBlock * 4, 0, 0);
@@ -474,12 +494,9 @@ hipError_t launch_sparse_attn_bwd(const KGeom& g, float scale, const void* q, co
                                   const void* o, const void* dout, const float* lse, const uint32_t* words,
                                   const int32_t* counts, const int32_t* lists, void* dq, void* dk, void* dv,
                                   const BwdWorkspace& ws, hipStream_t s) {
-  // Token-major fractal copies of Q, K, V, dO.
+  // The kernels read Q, K, V and dO in the original token order (64-token blocks gathered as
+  // their 8 runs of 8 tokens), so no reordered copies are made.
   hipError_t e;
-  if ((e = launch_reorder(g, ABLA_BF16, 0, ABLA_LAYOUT_TOKENS, q, ws.q_r, nullptr, s)) != hipSuccess) return e;
-  if ((e = launch_reorder(g, ABLA_BF16, 0, ABLA_LAYOUT_TOKENS, k, ws.k_r, nullptr, s)) != hipSuccess) return e;
-  if ((e = launch_reorder(g, ABLA_BF16, 0, ABLA_LAYOUT_TOKENS, v, ws.v_r, nullptr, s)) != hipSuccess) return e;
-  if ((e = launch_reorder(g, ABLA_BF16, 0, ABLA_LAYOUT_TOKENS, dout, ws.do_r, nullptr, s)) != hipSuccess) return e;
 
   const long long rows = (long long)g.B * g.H * g.N;
   const unsigned bhs = (unsigned)(g.B * g.H);
@@ -498,13 +515,16 @@ hipError_t launch_sparse_attn_bwd(const KGeom& g, float scale, const void* q, co
 
   const float c2 = scale * kLog2e;
   const dim3 grid((unsigned)((long long)bhs * g.nb));
-  DqArgs qa{ws.q_r, ws.k_r, ws.v_r, ws.do_r, ws.D, ws.L2, counts, lists, static_cast<uint16_t*>(dq), g, c2, scale};
+  const uint16_t* q16 = static_cast<const uint16_t*>(q);
+  const uint16_t* k16 = static_cast<const uint16_t*>(k);
+  const uint16_t* v16 = static_cast<const uint16_t*>(v);
+  DqArgs qa{q16, k16, v16, do16, ws.D, ws.L2, counts, lists, static_cast<uint16_t*>(dq), g, c2, scale};
   if (g.d == 128)
     k_bwd_dq<128><<<grid, kBwdThreads, 0, s>>>(qa);
   else
     k_bwd_dq<64><<<grid, kBwdThreads, 0, s>>>(qa);
   if ((e = hipGetLastError()) != hipSuccess) return e;
-  DkvArgs ka{ws.k_r, ws.v_r, ws.q_r, ws.do_r, ws.D, ws.L2, ws.col_counts, ws.col_lists,
+  DkvArgs ka{k16, v16, q16, do16, ws.D, ws.L2, ws.col_counts, ws.col_lists,
              static_cast<uint16_t*>(dk), static_cast<uint16_t*>(dv), g, c2, scale};
   if (g.d == 128)
     k_bwd_dkdv<128><<<grid, kBwdThreads, 0, s>>>(ka);
