@@ -284,26 +284,29 @@ def sparse_attn_bwd_workspace_bytes(geom: Geometry) -> int:
 def sparse_attn_bwd(q, k, v, o, dout, lse, words, counts, lists, geom: Geometry, *, scale: float = 0.0,
                     dq=None, dk=None, dv=None, workspace=None):
     """abla_sparse_attn_bwd: gradients (dq, dk, dv) of the block-sparse attention, all tensors
-    [B,H,N,d] bf16 in the original token order; lse [B,H,N] float32 in fractal order from the
-    forward; words / counts / lists the mask of build_mask."""
+    [B,H,N,d] of one dtype (bf16 or float32) in the original token order; lse [B,H,N] float32 in
+    fractal order from the forward; words / counts / lists the mask of build_mask."""
     dev = _device(q)
+    dt = q.dtype
+    if dt not in _DT:
+        raise ValueError(f"unsupported dtype {dt}")
     tok = (geom.B, geom.H, geom.N, geom.d)
     for t, n in ((q, "q"), (k, "k"), (v, "v"), (o, "o"), (dout, "dout")):
-        _need(t, n, tok, torch.bfloat16, dev)
+        _need(t, n, tok, dt, dev)
     _need(lse, "lse", (geom.B, geom.H, geom.N), torch.float32, dev)
     _need(words, "words", (geom.B, geom.H, geom.nb, geom.words), torch.int32, dev)
     _need(counts, "counts", (geom.B, geom.H, geom.nb), torch.int32, dev)
     _need(lists, "lists", (geom.B, geom.H, geom.nb, geom.nb), torch.int32, dev)
-    dq = torch.empty(tok, dtype=torch.bfloat16, device=dev) if dq is None else dq
-    dk = torch.empty(tok, dtype=torch.bfloat16, device=dev) if dk is None else dk
-    dv = torch.empty(tok, dtype=torch.bfloat16, device=dev) if dv is None else dv
+    dq = torch.empty(tok, dtype=dt, device=dev) if dq is None else dq
+    dk = torch.empty(tok, dtype=dt, device=dev) if dk is None else dk
+    dv = torch.empty(tok, dtype=dt, device=dev) if dv is None else dv
     for t, n in ((dq, "dq"), (dk, "dk"), (dv, "dv")):
-        _need(t, n, tok, torch.bfloat16, dev)
+        _need(t, n, tok, dt, dev)
     nbytes = sparse_attn_bwd_workspace_bytes(geom)
     if workspace is None:
         workspace = torch.empty(max(nbytes, 1), dtype=torch.uint8, device=dev)
     g = geom.c()
-    _check(_lib.abla_sparse_attn_bwd(ctypes.byref(g), _DT[torch.bfloat16], float(scale), _ptr(q), _ptr(k), _ptr(v),
+    _check(_lib.abla_sparse_attn_bwd(ctypes.byref(g), _DT[dt], float(scale), _ptr(q), _ptr(k), _ptr(v),
                                      _ptr(o), _ptr(dout), _ptr(lse), _ptr(words), _ptr(counts), _ptr(lists),
                                      _ptr(dq), _ptr(dk), _ptr(dv), _ptr(workspace), workspace.numel(), _stream(q)),
            "abla_sparse_attn_bwd")
@@ -376,7 +379,7 @@ class NablaAttention:
 
     def backward(self, q, k, v, dout, workspace=None):
         """Gradients (dq, dk, dv) of the last __call__(q, k, v) for the incoming gradient dout
-        (all [B,H,N,d] bf16, original order). Needs want_lse=True (the forward's log-sum-exp)."""
+        (all [B,H,N,d], original order). Needs want_lse=True (the forward's log-sum-exp)."""
         if self.lse is None:
             raise ValueError("backward needs the forward's log-sum-exp: construct with want_lse=True")
         return sparse_attn_bwd(q, k, v, self.out, dout, self.lse, self.words, self.counts, self.lists, self.geom,
@@ -411,3 +414,32 @@ def kept_flops(geom: Geometry, total_kept_blocks: int) -> float:
 
 def default_scale(geom: Geometry) -> float:
     return 1.0 / math.sqrt(geom.d)
+
+
+class _NablaAttentionFn(torch.autograd.Function):
+    """Forward: the whole path (pooling, mask, block-sparse attention); backward:
+    abla_sparse_attn_bwd through the same mask. The mask is a selection, so no gradient flows
+    through it (the gradient is that of attention restricted to the kept blocks)."""
+
+    @staticmethod
+    def forward(ctx, q, k, v, geom, params, scale):
+        run = NablaAttention(geom, params, dtype=q.dtype, device=q.device, scale=scale, want_lse=True)
+        out = run(q, k, v)
+        ctx.geom, ctx.scale = geom, scale
+        ctx.save_for_backward(q, k, v, out, run.lse, run.words, run.counts, run.lists)
+        return out
+
+    @staticmethod
+    def backward(ctx, dout):
+        q, k, v, out, lse, words, counts, lists = ctx.saved_tensors
+        dq, dk, dv = sparse_attn_bwd(q, k, v, out, dout.contiguous(), lse, words, counts, lists, ctx.geom,
+                                     scale=ctx.scale)
+        return dq, dk, dv, None, None, None
+
+
+def nabla_attention(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, geom: Geometry, params: MaskParams,
+                    scale: float = 0.0) -> torch.Tensor:
+    """Differentiable block-sparse attention: O = NablaAttention(geom, params)(q, k, v) for
+    [B,H,N,d] tensors (bf16 or float32) in the original token order, with gradients for q, k
+    and v from abla_sparse_attn_bwd on the same mask."""
+    return _NablaAttentionFn.apply(q, k, v, geom, params, scale)

@@ -177,12 +177,11 @@ abla_status abla_sparse_attn_bwd(const abla_geom* g, int32_t dtype, float scale,
   abla_status st = check_geom(g);
   if (st != ABLA_OK) return st;
   if (!valid_dtype(dtype)) return ABLA_ERR_INVALID;
-  if (dtype != ABLA_BF16) return ABLA_ERR_UNSUPPORTED;
   if (!q || !k || !v || !o || !dout || !lse || !mask_words || !counts || !lists || !dq || !dk || !dv)
     return ABLA_ERR_INVALID;
   if (isnan(scale) || scale < 0.f || isinf(scale)) return ABLA_ERR_INVALID;
   if (nb_of(g) > kMaxBlocks) return ABLA_ERR_UNSUPPORTED;
-  const size_t bytes = tok_elems(g) * 2;
+  const size_t bytes = tok_elems(g) * elem_bytes(dtype);
   const void* ins[5] = {q, k, v, o, dout};
   void* outs[3] = {dq, dk, dv};
   for (int a = 0; a < 3; ++a) {
@@ -195,8 +194,8 @@ abla_status abla_sparse_attn_bwd(const abla_geom* g, int32_t dtype, float scale,
   BwdWorkspace ws;
   bwd_parts(g, &ws, static_cast<char*>(workspace));
   const float s = scale > 0.f ? scale : 1.0f / sqrtf((float)g->d);
-  return from_hip(launch_sparse_attn_bwd(make_kgeom(*g), s, q, k, v, o, dout, lse, mask_words, counts, lists, dq,
-                                         dk, dv, ws, (hipStream_t)stream));
+  return from_hip(launch_sparse_attn_bwd(make_kgeom(*g), dtype, s, q, k, v, o, dout, lse, mask_words, counts, lists,
+                                         dq, dk, dv, ws, (hipStream_t)stream));
 }
 
 }  // extern "C"

@@ -63,9 +63,9 @@ struct BwdWorkspace {
   float *D, *L2;                    // [B,H,N] fractal order
   int32_t *col_counts, *col_lists;  // [B,H,nb], [B,H,nb,nb]
 };
-hipError_t launch_sparse_attn_bwd(const KGeom& g, float scale, const void* q, const void* k, const void* v,
-                                  const void* o, const void* dout, const float* lse, const uint32_t* words,
-                                  const int32_t* counts, const int32_t* lists, void* dq, void* dk, void* dv,
-                                  const BwdWorkspace& ws, hipStream_t s);
+hipError_t launch_sparse_attn_bwd(const KGeom& g, int dtype, float scale, const void* q, const void* k,
+                                  const void* v, const void* o, const void* dout, const float* lse,
+                                  const uint32_t* words, const int32_t* counts, const int32_t* lists, void* dq,
+                                  void* dk, void* dv, const BwdWorkspace& ws, hipStream_t s);
 
 }  // namespace abla

@@ -488,18 +488,215 @@ __global__ __launch_bounds__(kBwdThreads) __attribute__((amdgpu_waves_per_eu(2, 
   }
 }
 
+// ------------------------------------------------------------------- float32 path
+// Plain float32 arithmetic throughout (no rounding of P or dS), two threads per row as in the
+// float32 forward: thread pair (2r, 2r+1) holds row r, each half of the channels; the dot
+// products are combined with one lane swap. Inputs and outputs in the original token order.
+
+// D[m] = <dO[n], O[n]> (float32) and the natural-log lse of fractal row m of token n.
+template <int D>
+__global__ __launch_bounds__(256) void k_bwd_delta_f32(const float* __restrict__ o, const float* __restrict__ dout,
+                                                       const float* __restrict__ lse, float* __restrict__ Dm,
+                                                       float* __restrict__ Lr, KGeom g) {
+  constexpr int LPR = D / 4;
+  const long long rows = (long long)g.B * g.H * g.N;
+  const long long row = ((long long)blockIdx.x * 256 + threadIdx.x) / LPR;
+  const int sub = threadIdx.x % LPR;
+  float acc = 0.f;
+  if (row < rows) {
+    const long long bh = row / g.N;
+    const int m = (int)(row - bh * g.N);
+    const long long off = (bh * g.N + token_of(g, m / kBlock, m % kBlock)) * D + sub * 4;
+    const float4 a = *reinterpret_cast<const float4*>(o + off);
+    const float4 b = *reinterpret_cast<const float4*>(dout + off);
+    acc = fmaf(a.x, b.x, fmaf(a.y, b.y, fmaf(a.z, b.z, a.w * b.w)));
+  }
+#pragma unroll
+  for (int s = 1; s < LPR; s <<= 1) acc += __shfl_xor(acc, s);
+  if (row < rows && sub == 0) {
+    Dm[row] = acc;
+    Lr[row] = lse[row];
+  }
+}
+
+// Stage the 64 rows of block blk (original order) of one head into an LDS tile [64][D].
+template <int D>
+__device__ __forceinline__ void stage_rows_f32(float* tile, const float* head, const KGeom& g, int blk) {
+  for (int u = threadIdx.x; u < kBlock * D / 4; u += 128) {
+    const int rr = u / (D / 4), c4 = (u % (D / 4)) * 4;
+    *reinterpret_cast<float4*>(tile + rr * D + c4) =
+        *reinterpret_cast<const float4*>(head + token_of(g, blk, rr) * D + c4);
+  }
+}
+
+struct BwdF32Args {
+  const float *q, *k, *v, *dout, *Dm, *Lr;
+  const int32_t *counts, *lists, *col_counts, *col_lists;
+  float *dq, *dk, *dv;
+  KGeom g;
+  float scale;
+};
+
+// dQ: one workgroup per query block, walking its kept list.
+template <int D>
+__global__ __launch_bounds__(128) void k_bwd_dq_f32(BwdF32Args a) {
+  constexpr int H2 = D / 2;
+  __shared__ __attribute__((aligned(16))) float ks[kBlock * D];
+  __shared__ __attribute__((aligned(16))) float vs[kBlock * D];
+  const KGeom& g = a.g;
+  const int nb = g.nb, t = threadIdx.x, r = t >> 1, half = t & 1;
+  const long long bh = blockIdx.x / nb;
+  const int i = blockIdx.x - (int)(bh * nb);
+  const long long row = bh * nb + i;
+  const int cnt = min(max(a.counts[row], 0), nb);
+  const long long n = token_of(g, i, r);
+  const float* qrow = a.q + (bh * g.N + n) * D + half * H2;
+  const float* drow = a.dout + (bh * g.N + n) * D + half * H2;
+  float qv[H2], dov[H2], acc[H2];
+#pragma unroll
+  for (int c = 0; c < H2; ++c) {
+    qv[c] = qrow[c];
+    dov[c] = drow[c];
+    acc[c] = 0.f;
+  }
+  const long long m = bh * g.N + (long long)i * kBlock + r;
+  const float lq = a.Lr[m], dd = a.Dm[m];
+  const float* kh = a.k + bh * g.N * D;
+  const float* vh = a.v + bh * g.N * D;
+  for (int u = 0; u < cnt; ++u) {
+    const int j = min(max(a.lists[row * nb + u], 0), nb - 1);
+    stage_rows_f32<D>(ks, kh, g, j);
+    stage_rows_f32<D>(vs, vh, g, j);
+    __syncthreads();
+    for (int kk = 0; kk < kBlock; ++kk) {
+      const float* krow = ks + kk * D + half * H2;
+      const float* vrow = vs + kk * D + half * H2;
+      float sp = 0.f, dpp = 0.f;
+#pragma unroll
+      for (int c = 0; c < H2; ++c) {
+        sp = fmaf(qv[c], krow[c], sp);
+        dpp = fmaf(dov[c], vrow[c], dpp);
+      }
+      const float so = __shfl_xor(sp, 1), dpo = __shfl_xor(dpp, 1);
+      const float s = half ? so + sp : sp + so;
+      const float dp = half ? dpo + dpp : dpp + dpo;
+      const float p = expf(s * a.scale - lq);
+      const float ds = p * (dp - dd);
+#pragma unroll
+      for (int c = 0; c < H2; ++c) acc[c] = fmaf(ds, krow[c], acc[c]);
+    }
+    __syncthreads();
+  }
+  float* orow = a.dq + (bh * g.N + n) * D + half * H2;
+#pragma unroll
+  for (int c = 0; c < H2; ++c) orow[c] = acc[c] * a.scale;
+}
+
+// dK, dV: one workgroup per key block, walking its column list.
+template <int D>
+__global__ __launch_bounds__(128) void k_bwd_dkdv_f32(BwdF32Args a) {
+  constexpr int H2 = D / 2;
+  __shared__ __attribute__((aligned(16))) float qs[kBlock * D];
+  __shared__ __attribute__((aligned(16))) float dos[kBlock * D];
+  __shared__ float ls[kBlock], dds[kBlock];
+  const KGeom& g = a.g;
+  const int nb = g.nb, t = threadIdx.x, r = t >> 1, half = t & 1;
+  const long long bh = blockIdx.x / nb;
+  const int j = blockIdx.x - (int)(bh * nb);
+  const long long col = bh * nb + j;
+  const int cnt = min(max(a.col_counts[col], 0), nb);
+  const long long n = token_of(g, j, r);
+  const float* krow = a.k + (bh * g.N + n) * D + half * H2;
+  const float* vrow = a.v + (bh * g.N + n) * D + half * H2;
+  float kv[H2], vv[H2], dk[H2], dv[H2];
+#pragma unroll
+  for (int c = 0; c < H2; ++c) {
+    kv[c] = krow[c];
+    vv[c] = vrow[c];
+    dk[c] = 0.f;
+    dv[c] = 0.f;
+  }
+  const float* qh = a.q + bh * g.N * D;
+  const float* dh = a.dout + bh * g.N * D;
+  for (int u = 0; u < cnt; ++u) {
+    const int i = min(max(a.col_lists[col * nb + u], 0), nb - 1);
+    stage_rows_f32<D>(qs, qh, g, i);
+    stage_rows_f32<D>(dos, dh, g, i);
+    if (t < kBlock) {
+      ls[t] = a.Lr[bh * g.N + (long long)i * kBlock + t];
+      dds[t] = a.Dm[bh * g.N + (long long)i * kBlock + t];
+    }
+    __syncthreads();
+    for (int qq = 0; qq < kBlock; ++qq) {
+      const float* qrow = qs + qq * D + half * H2;
+      const float* drow = dos + qq * D + half * H2;
+      float sp = 0.f, dpp = 0.f;
+#pragma unroll
+      for (int c = 0; c < H2; ++c) {
+        sp = fmaf(qrow[c], kv[c], sp);
+        dpp = fmaf(drow[c], vv[c], dpp);
+      }
+      const float so = __shfl_xor(sp, 1), dpo = __shfl_xor(dpp, 1);
+      const float s = half ? so + sp : sp + so;
+      const float dp = half ? dpo + dpp : dpp + dpo;
+      const float p = expf(s * a.scale - ls[qq]);
+      const float ds = p * (dp - dds[qq]);
+#pragma unroll
+      for (int c = 0; c < H2; ++c) {
+        dv[c] = fmaf(p, drow[c], dv[c]);
+        dk[c] = fmaf(ds, qrow[c], dk[c]);
+      }
+    }
+    __syncthreads();
+  }
+  float* dkrow = a.dk + (bh * g.N + n) * D + half * H2;
+  float* dvrow = a.dv + (bh * g.N + n) * D + half * H2;
+#pragma unroll
+  for (int c = 0; c < H2; ++c) {
+    dkrow[c] = dk[c] * a.scale;
+    dvrow[c] = dv[c];
+  }
+}
+
 }  // namespace
 
-hipError_t launch_sparse_attn_bwd(const KGeom& g, float scale, const void* q, const void* k, const void* v,
-                                  const void* o, const void* dout, const float* lse, const uint32_t* words,
-                                  const int32_t* counts, const int32_t* lists, void* dq, void* dk, void* dv,
-                                  const BwdWorkspace& ws, hipStream_t s) {
+hipError_t launch_sparse_attn_bwd(const KGeom& g, int dtype, float scale, const void* q, const void* k,
+                                  const void* v, const void* o, const void* dout, const float* lse,
+                                  const uint32_t* words, const int32_t* counts, const int32_t* lists, void* dq,
+                                  void* dk, void* dv, const BwdWorkspace& ws, hipStream_t s) {
   // The kernels read Q, K, V and dO in the original token order (64-token blocks gathered as
   // their 8 runs of 8 tokens), so no reordered copies are made.
   hipError_t e;
 
   const long long rows = (long long)g.B * g.H * g.N;
   const unsigned bhs = (unsigned)(g.B * g.H);
+  if (dtype == ABLA_F32) {
+    const unsigned fgrid = (unsigned)((rows * (g.d / 4) + 255) / 256);
+    const float* of = static_cast<const float*>(o);
+    const float* dof = static_cast<const float*>(dout);
+    if (g.d == 128)
+      k_bwd_delta_f32<128><<<dim3(fgrid), 256, 0, s>>>(of, dof, lse, ws.D, ws.L2, g);
+    else
+      k_bwd_delta_f32<64><<<dim3(fgrid), 256, 0, s>>>(of, dof, lse, ws.D, ws.L2, g);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+    k_col_lists<<<dim3((unsigned)((g.nb + 255) / 256), bhs), 256, 0, s>>>(words, ws.col_counts, ws.col_lists,
+                                                                         g.nb, (g.nb + 31) / 32);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+    BwdF32Args fa{static_cast<const float*>(q), static_cast<const float*>(k), static_cast<const float*>(v), dof,
+                  ws.D, ws.L2, counts, lists, ws.col_counts, ws.col_lists, static_cast<float*>(dq),
+                  static_cast<float*>(dk), static_cast<float*>(dv), g, scale};
+    const dim3 grid((unsigned)((long long)bhs * g.nb));
+    if (g.d == 128) {
+      k_bwd_dq_f32<128><<<grid, 128, 0, s>>>(fa);
+      if ((e = hipGetLastError()) != hipSuccess) return e;
+      k_bwd_dkdv_f32<128><<<grid, 128, 0, s>>>(fa);
+    } else {
+      k_bwd_dq_f32<64><<<grid, 128, 0, s>>>(fa);
+      if ((e = hipGetLastError()) != hipSuccess) return e;
+      k_bwd_dkdv_f32<64><<<grid, 128, 0, s>>>(fa);
+    }
+    return hipGetLastError();
+  }
   const int lpr = g.d / 8;
   const unsigned dgrid = (unsigned)((rows * lpr + 255) / 256);
   const uint16_t* o16 = static_cast<const uint16_t*>(o);

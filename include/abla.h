@@ -206,19 +206,20 @@ size_t abla_sparse_attn_bwd_workspace_bytes(const abla_geom* g);
  *   dV = P^T dO,  dP = dO V^T,  D = rowsum(dO * O),  dS = P * (dP - D),
  *   dQ = scale * dS K,  dK = scale * dS^T Q.
  *
- * q, k, v, o, dout: [B,H,N,d] bf16 in the ORIGINAL token order (o is the forward's output,
- *   dout the incoming gradient).
+ * q, k, v, o, dout: [B,H,N,d] of `dtype` (bf16 or float32) in the ORIGINAL token order (o is
+ *   the forward's output, dout the incoming gradient).
  * lse: [B,H,N] float32 in fractal order, as written by abla_sparse_attn_fwd for the same inputs
  *   (natural log); P is recomputed from it.
  * mask_words, counts, lists: the mask of abla_build_mask (words and lists must agree).
- * dq, dk, dv: [B,H,N,d] bf16 outputs in the original order; no overlap with each other or the
- *   inputs. Rows of dq whose block keeps nothing are 0; keys no block keeps get dk = dv = 0.
+ * dq, dk, dv: [B,H,N,d] outputs of `dtype` in the original order; no overlap with each other or
+ *   the inputs. Rows of dq whose block keeps nothing are 0; keys no block keeps get dk = dv = 0.
  * scale: 0 means 1/sqrt(d); it must equal the forward's.
- * Arithmetic: bf16 matrix-core products with float32 accumulation; P and dS are rounded to bf16
- *   for the products, D is summed in float32, the outputs are rounded once.
+ * Arithmetic: bf16 inputs use bf16 matrix-core products with float32 accumulation; P and dS are
+ *   rounded to bf16 for the products, D is summed in float32, the outputs are rounded once.
+ *   float32 inputs are computed in float32 throughout.
  * workspace: at least abla_sparse_attn_bwd_workspace_bytes(g) bytes.
  * Errors: INVALID for null pointers, NaN/negative scale, unknown dtype, overlapping outputs;
- * UNSUPPORTED for float32 inputs, nb > 4096 and the geometry limits of abla_reorder;
+ * UNSUPPORTED for nb > 4096 and the geometry limits of abla_reorder;
  * WORKSPACE if the workspace is missing or too small. */
 abla_status abla_sparse_attn_bwd(const abla_geom* g, int32_t dtype, float scale, const void* q, const void* k,
                                  const void* v, const void* o, const void* dout, const float* lse,

@@ -97,6 +97,10 @@ def compare_attention(out_gpu: np.ndarray, out_ref: np.ndarray, dtype: str):
 
 BWD_REL_L2 = 1e-2
 BWD_MAX_REL = 2e-2
+# float32 gradients: no rounding of P, dS or the outputs, float32 sums of a few thousand terms
+# (relative error of order 1e-6); the bar leaves two orders of magnitude.
+BWD_F32_REL_L2 = 1e-4
+BWD_F32_MAX_REL = 1e-3
 
 
 def grad_errors(gpu: np.ndarray, ref: np.ndarray):
@@ -108,11 +112,12 @@ def grad_errors(gpu: np.ndarray, ref: np.ndarray):
     return float(np.linalg.norm(d) / np.linalg.norm(ref)), float(d.max()) / peak
 
 
-def compare_grad(gpu: np.ndarray, ref: np.ndarray, name: str):
+def compare_grad(gpu: np.ndarray, ref: np.ndarray, name: str, dtype: str = "bf16"):
     """Gradient rule: relative L2 and max error relative to the largest reference entry."""
     rel, mx = grad_errors(gpu, ref)
-    assert rel <= BWD_REL_L2, f"{name}: rel L2 {rel:.3e}"
-    assert mx <= BWD_MAX_REL, f"{name}: max err / max |ref| {mx:.3e}"
+    bar_rel, bar_max = (BWD_REL_L2, BWD_MAX_REL) if dtype == "bf16" else (BWD_F32_REL_L2, BWD_F32_MAX_REL)
+    assert rel <= bar_rel, f"{name}: rel L2 {rel:.3e}"
+    assert mx <= bar_max, f"{name}: max err / max |ref| {mx:.3e}"
     return rel, mx
 
 

@@ -149,7 +149,7 @@ def test_backward_errors(A):
     for n in ("q", "k", "v", "o", "dout", "lse", "words", "counts", "lists", "dq", "dk", "dv"):
         assert bwd_call(A, g, **{n: None}) == 1, n
     assert bwd_call(A, g, dtype=3) == 1
-    assert bwd_call(A, g, dtype=0) == 2  # float32 gradients are not implemented
+    assert bwd_call(A, g, dtype=0, ws=None) == 3  # float32 passes the argument checks
     assert bwd_call(A, g, scale=math.nan) == 1
     assert bwd_call(A, g, scale=-1.0) == 1
     assert bwd_call(A, g, dk=ctypes.c_void_p(1 << 32)) == 1  # dk aliases q

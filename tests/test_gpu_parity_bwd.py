@@ -44,8 +44,8 @@ def _head(x, b, h, og):
     return R.reorder(R.to64(x[b, h]), gh), gh
 
 
-def _oracle_forward(q, k, v, gm, og):
-    """Oracle O (original order, rounded to bf16) and lse (fractal order, float32) on mask gm."""
+def _oracle_forward(q, k, v, gm, og, dtype=torch.bfloat16):
+    """Oracle O (original order, rounded to `dtype`) and lse (fractal order, float32) on mask gm."""
     scale = 1.0 / math.sqrt(og.d)
     O = np.empty((og.B, og.H, og.N, og.d))
     lse = np.empty((og.B, og.H, og.N))
@@ -56,11 +56,11 @@ def _oracle_forward(q, k, v, gm, og):
             Vr, _ = _head(v, b, h, og)
             Or, lse[b, h] = R.masked_attention_head(Qr, Kr, Vr, gm[b, h], gh, scale)
             O[b, h] = R.inverse_reorder(Or, gh)
-    o = torch.from_numpy(O).to(torch.bfloat16).to(DEV)
+    o = torch.from_numpy(O).to(dtype).to(DEV)
     return o, torch.from_numpy(lse.astype(np.float32)).to(DEV)
 
 
-def _check_full(og, q, k, v, dout, gm, dq, dk, dv, tag, o_given=None):
+def _check_full(og, q, k, v, dout, gm, dq, dk, dv, tag, o_given=None, dtype="bf16"):
     """Every element of the three gradients against the oracle, head by head. With o_given
     the oracle takes D from that (bf16) forward output."""
     scale = 1.0 / math.sqrt(og.d)
@@ -80,7 +80,7 @@ def _check_full(og, q, k, v, dout, gm, dq, dk, dv, tag, o_given=None):
     errs = {n: PT.grad_errors(np.stack(got[n]), np.stack(ref[n])) for n in NAMES}
     print(f"{tag}: " + ", ".join(f"{n} rel {r:.2e} max {m:.2e}" for n, (r, m) in errs.items()), flush=True)
     for n in NAMES:
-        PT.compare_grad(np.stack(got[n]), np.stack(ref[n]), f"{tag} {n}")
+        PT.compare_grad(np.stack(got[n]), np.stack(ref[n]), f"{tag} {n}", dtype)
     return errs
 
 
@@ -312,3 +312,58 @@ def test_backward_480p_end_to_end_sampled(A):
     dq, dk, dv = run.backward(q, k, v, dout)
     torch.cuda.synchronize()
     _compare_sampled(og, q, k, v, dout, gm, picks, dq, dk, dv, "480p e2e")
+
+
+def test_autograd_function_matches_entry_points(A):
+    """nabla_attention under torch.autograd gives the forward output and, from backward(), the
+    gradients of the explicit entry-point calls, bit for bit."""
+    B, H, T, Hs, Ws, d = 1, 2, 3, 24, 40, 128
+    geom, og = PT.geoms(B, H, T, Hs, Ws, d)
+    q, k, v, dout = _inputs(B, H, T, Hs, Ws, d, seed=31)
+    prm = A.MaskParams(mode="cdf", thr=0.8)
+    qa, ka, va = (x.clone().requires_grad_(True) for x in (q, k, v))
+    out = A.nabla_attention(qa, ka, va, geom, prm)
+    out.backward(dout)
+    run = A.NablaAttention(geom, prm, want_lse=True)
+    run(q, k, v)
+    dq, dk, dv = run.backward(q, k, v, dout)
+    torch.cuda.synchronize()
+    assert torch.equal(out.detach().view(torch.int16), run.out.view(torch.int16))
+    for got, want in ((qa.grad, dq), (ka.grad, dk), (va.grad, dv)):
+        assert torch.equal(got.view(torch.int16), want.view(torch.int16))
+
+
+@pytest.mark.parametrize("d,geo", [(64, (1, 2, 8, 16, 16)), (128, (1, 1, 3, 16, 24)), (64, (2, 1, 3, 24, 40))])
+def test_backward_f32_kernel_parity(A, d, geo):
+    """float32 backward on the oracle's O (float32) and lse, every element."""
+    B, H, T, Hs, Ws = geo
+    geom, og = PT.geoms(B, H, T, Hs, Ws, d)
+    q, k, v = make_random_qkv(B, H, T, Hs, Ws, d, "f32", seed=41, device=DEV)
+    k = k + 0.25 * q
+    dout = make_dout(B, H, geom.N, d, seed=42, device=DEV).float()
+    run = A.NablaAttention(geom, A.MaskParams(mode="cdf", thr=0.8), dtype=torch.float32, want_lse=True)
+    run(q, k, v)
+    torch.cuda.synchronize()
+    gm = PT.gpu_mask(run.words, og)
+    o, lse = _oracle_forward(q, k, v, gm, og, dtype=torch.float32)
+    print(f"backward f32 d{d} nb{geom.nb}", flush=True)
+    dq, dk, dv = A.sparse_attn_bwd(q, k, v, o, dout, lse, run.words, run.counts, run.lists, geom)
+    torch.cuda.synchronize()
+    _check_full(og, q, k, v, dout, gm, dq, dk, dv, f"f32-d{d}", o_given=o, dtype="f32")
+
+
+def test_backward_tiny_workload_end_to_end(A):
+    """The tiny workload (float32, d = 64) through the autograd function, against the exact oracle."""
+    w = WORKLOADS["tiny"]
+    geom, og = PT.geoms(w.B, w.H, w.T, w.Hs, w.Ws, w.d, w.P)
+    q, k, v = make_qkv(w, device=DEV)
+    dout = make_dout(w.B, w.H, geom.N, w.d, seed=43, device=DEV).float()
+    prm = A.MaskParams(mode=w.mode, thr=w.thr, tau=w.tau, sta=tuple(w.sta))
+    qa, ka, va = (x.clone().requires_grad_(True) for x in (q, k, v))
+    out = A.nabla_attention(qa, ka, va, geom, prm)
+    out.backward(dout)
+    torch.cuda.synchronize()
+    run = A.NablaAttention(geom, prm, dtype=torch.float32)
+    run(q, k, v)
+    torch.cuda.synchronize()
+    _check_full(og, q, k, v, dout, PT.gpu_mask(run.words, og), qa.grad, ka.grad, va.grad, "tiny e2e", dtype="f32")
