@@ -15,6 +15,8 @@ with HIP events on the stream the kernels run on. `cpu_baseline` times the CPU
 oracle on a bounded sample of the same workload and scales it to the layer.
 
 Usage: python bench.py [--gpus 1] [--steps 10] [--warmup 20] [--workload 480p] [--secondary 720p] [--graph]
+       python bench.py --report          (per-pass table over every workload, and the backward)
+       python bench.py --backward --workload 720p   (abla_sparse_attn_bwd timing, one JSON line)
 """
 import argparse
 import json
