@@ -88,7 +88,7 @@ __global__ __launch_bounds__(256) void k_col_lists(const uint32_t* __restrict__ 
 // ------------------------------------------------------------------- operands
 // Token-major tiles gathered from a tensor in the original token order: block j is 8 runs of
 // 8 tokens (one per patch row); in LDS, row r holds token kperm(r) of the block with its
-// 16-byte chunks XOR-swizzled by k_swz(r). orig_tile_off gives thread t's fixed offset from the block's
+// 16-byte chunks XOR-swizzled by kt_swz(r). orig_tile_off gives thread t's fixed offset from the block's
 // corner token (LDS row r = t / KCH holds key kperm(r), kperm(r) / 8 patch rows of Ws tokens
 // and kperm(r) % 8 tokens in); consecutive loads of a thread are 16 (d = 128) or 32 (d = 64)
 // LDS rows, i.e. 2 or 4 patch rows, 512 * Ws bytes apart; orig_tile_base is the corner's byte
@@ -98,7 +98,7 @@ __device__ __forceinline__ uint32_t orig_tile_off(int t, int Ws) {
   constexpr int KCH = D / 8;
   const int r = t / KCH, pc = t % KCH;
   const int kr = kperm(r);
-  return (uint32_t)(((kr >> 3) * Ws + (kr & 7)) * D * 2 + ((pc ^ k_swz<D>(r)) * 16));
+  return (uint32_t)(((kr >> 3) * Ws + (kr & 7)) * D * 2 + ((pc ^ kt_swz<D>(r)) * 16));
 }
 template <int D>
 __device__ __forceinline__ uint32_t orig_tile_base(const KGeom& g, int j) {
@@ -112,7 +112,7 @@ __device__ __forceinline__ uint32_t orig_tile_base(const KGeom& g, int j) {
 template <int D>
 __device__ __forceinline__ bf16x8_t row_chunk(const char* tile, int half, int lane, int ks) {
   const int row = half * 32 + (lane & 31);
-  const int c = (ks * 2 + (lane >> 5)) ^ k_swz<D>(row);
+  const int c = (ks * 2 + (lane >> 5)) ^ kt_swz<D>(row);
   return *reinterpret_cast<const bf16x8_t*>(tile + row * D * 2 + c * 16);
 }
 

@@ -23,10 +23,27 @@ struct Tile {
   static constexpr int VLOADS = VUNITS / 256;
 };
 
-// 16-byte chunk swizzles (bank-conflict-free MFMA operand reads).
+// 16-byte chunk swizzles (bank-conflict-free MFMA operand reads): row r's chunk c of a
+// token-major tile sits at position c ^ k_swz(r). Spreads the row operand reads (each lane a
+// 16-byte chunk, consecutive rows at one logical chunk) over all banks.
 template <int D>
 __device__ __forceinline__ int k_swz(int r) {
   return D == 128 ? (r & 15) : ((r >> 1) & 7);
+}
+
+// Swizzle of the tiles that are also read with transpose loads (the backward's): besides the
+// row reads, each half-wave of a transpose load reads 4 rows x 4 consecutive chunks, which
+// k_swz maps onto the same banks. For d = 128 (16 chunks per row) the table A[r%4] ^ (r/4)%4
+// with A = {0, 6, 10, 12} is a bijection on 16 rows and gives the 4 rows of a transpose load
+// distinct chunk groups in both a 32- and a 64-bank LDS model (checked by enumeration on the
+// host); for d = 64 (8 chunks) 2*(r%4) + (r/4)%2 does so except for a few two-way collisions of
+// row reads 8 rows apart. Both repeat every 16 rows.
+template <int D>
+__device__ __forceinline__ int kt_swz(int r) {
+  if constexpr (D == 128)
+    return (((r & 1) ? 6 : 0) ^ ((r & 2) ? 10 : 0)) ^ ((r >> 2) & 3);
+  else
+    return ((r & 3) << 1) | ((r >> 2) & 1);
 }
 __device__ __forceinline__ int v_swz(int d) { return (d >> 1) & 7; }
 
@@ -146,16 +163,17 @@ __device__ __forceinline__ bf16x8_t tr_chunk(const char* tile, int dt, int tb, i
 __device__ __forceinline__ uint32_t lds_offset(const char* p) {
   return (uint32_t)(uintptr_t)((const __attribute__((address_space(3))) char*)p);
 }
-// Byte offsets, relative to a token-major tile, of the two 8-byte transpose reads that give
-// lane `lane` its tr_chunk operand for channel tile dt and tokens tb + 8*(lane/32) + 0..7.
+// Byte offsets, relative to a token-major tile laid out with kt_swz, of the two 8-byte
+// transpose reads that give lane `lane` its operand (as tr_chunk) for channel tile dt and tokens
+// tb + 8*(lane/32) + 0..7.
 template <int D>
 __device__ __forceinline__ void tr_rel(int dt, int tb, int lane, uint32_t& a0, uint32_t& a1) {
   const int g = lane >> 4, m = lane & 15;
   const int ch = dt * 32 + 16 * (g & 1) + 4 * (m & 3);
   const int tok = tb + 8 * (g >> 1) + (m >> 2);
   const int r0 = kperm(tok), r1 = kperm(tok + 4);
-  a0 = (uint32_t)(r0 * D * 2 + (((ch >> 3) ^ k_swz<D>(r0)) << 4) + (ch & 7) * 2);
-  a1 = (uint32_t)(r1 * D * 2 + (((ch >> 3) ^ k_swz<D>(r1)) << 4) + (ch & 7) * 2);
+  a0 = (uint32_t)(r0 * D * 2 + (((ch >> 3) ^ kt_swz<D>(r0)) << 4) + (ch & 7) * 2);
+  a1 = (uint32_t)(r1 * D * 2 + (((ch >> 3) ^ kt_swz<D>(r1)) << 4) + (ch & 7) * 2);
 }
 // out[k] = tr_chunk<D>(tile, k, tb, lane) for the NT = D/32 channel tiles, where a[2k], a[2k+1]
 // are the LDS addresses of tile + tr_rel(k, tb0, lane) and the tile / token block differs from
