@@ -93,6 +93,10 @@ constexpr float kRescaleLog2 = 8.0f;
 // two 4-wave workgroups per CU.
 constexpr int kXcdSlots = 64;
 
+// Column order (short lists): runs of G adjacent temporal columns of one head, G*C close to
+// the workgroups one XCD holds at once.
+__device__ __forceinline__ int column_run_width(int C) { return max(1, (kXcdSlots + C / 2) / C); }
+
 // LDS map of the bf16 kernel: two K slots, two V^T slots, then the pair's schedule.
 template <int D>
 struct Lds {
@@ -388,32 +392,20 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
   const int nb = g.nb;
   const int F = g.nbh * g.nbw;
 
-  // Long lists: plain dispatch order. The resident workgroups of all eight XCDs then work
-  // on the same one or two heads at a time, whose K/V (tens of MB) stay in the shared
-  // last-level cache; grouping consecutive items per XCD instead spreads eight heads over
-  // the XCDs and measured slower once their K/V outgrow that cache.
-  int logical = blockIdx.x;
+  // Visiting order: item blockIdx.x of the table k_xcd_order wrote (column order, short
+  // lists), else position blockIdx.x of the per-head longest-first order (long lists), in
+  // plain dispatch order: the resident workgroups of all eight XCDs then work on the same
+  // one or two heads at a time, whose K/V (tens of MB) stay in the shared last-level cache.
+  int bh, pair;
   if (ld_const(a.walk_mode, 0)) {
-    // Column order (columns = the C frame pairs of one patch, patches in raster order):
-    // runs of G consecutive columns are dealt round-robin to the 8 XCDs (workgroups are
-    // dispatched to XCD blockIdx % 8), with G*C about the 64 workgroups an XCD holds at
-    // once (32 CUs, two workgroups each). On XCD x queue rank k then runs column
-    // 8G*(k / (G*C)) + G*x + (k / C) % G, frame pair k % C: the workgroups resident on an
-    // XCD are temporally adjacent pairs of a few spatially adjacent patches, whose kept
-    // key blocks largely coincide, so their tiles hit in that XCD's L2. Columns that do
-    // not fill a last round keep the plain mapping.
-    const int C = a.pairs / F;
-    const int G = max(1, (kXcdSlots + C / 2) / C);
-    const int full = (a.grid / (8 * G * C)) * 8 * G * C;
-    if (logical < full) {
-      const int x = logical & 7, k = logical >> 3;
-      const int col = (k / (G * C)) * 8 * G + x * G + (k / C) % G;
-      logical = col * C + k % C;
-    }
+    const int gi = ld_const(a.order, (long long)blockIdx.x);
+    bh = gi / a.pairs;
+    pair = gi - bh * a.pairs;
+  } else {
+    bh = blockIdx.x / a.pairs;
+    const int pos = blockIdx.x - bh * a.pairs;
+    pair = ld_const(a.order, (long long)bh * a.pairs + pos);
   }
-  const int bh = logical / a.pairs;
-  const int pos = logical - bh * a.pairs;
-  const int pair = ld_const(a.order, (long long)bh * a.pairs + pos);
   const int blk_a = (pair / F) * 2 * F + pair % F;
   const int blk_b = blk_a + F < nb ? blk_a + F : -1;
   const int my_blk = (w < 2) ? blk_a : blk_b;
@@ -666,12 +658,8 @@ __device__ void desc_exclusive_scan(int* h, int n, int* part) {
 // Visiting order of the query-block pairs (i, i + F) of each (b, h), F = nbh*nbw; pair p covers
 // blocks a = (p / F)*2F + p % F and a + F, so pair tp*F + s is frame pair tp of patch s.
 // Two orders, chosen once per launch from the mean kept count per row over all heads:
-//  - short lists (mean <= kColumnMaxCount): column order. Patches in raster order, each
-//    patch's C frame pairs in time order; the attention kernel deals runs of adjacent
-//    columns to the XCDs. The workgroups resident on an XCD are then temporally adjacent
-//    pairs of neighbouring patches, which share most key blocks, so their tile loads hit
-//    in L2. (Patches longest-first by total kept count measured 4-7% slower at 480p: the
-//    columns an XCD held were then spatially scattered.)
+//  - short lists (mean <= kColumnMaxCount): column order, built by k_xcd_order for the whole
+//    launch (below).
 //  - otherwise: pairs longest-first by their kept count (counting sort), so the long rows
 //    do not form the tail; with long lists neighbouring workgroups start too far apart
 //    for L2 reuse and the balance matters more.
@@ -698,14 +686,9 @@ __global__ __launch_bounds__(1024) void k_pair_order(const int32_t* __restrict__
   for (int w = 0; w < 16; ++w) total += wsum[w];
   const bool column = total <= (long long)kColumnMaxCount * rows;
   if (bh == 0 && t == 0) mode_out[0] = column ? 1 : 0;
+  if (column) return;  // k_xcd_order writes the whole order
 
   auto blk_count = [&](int blk) { return min(max(c[blk], 0), nb); };
-  if (column) {
-    const int C = pairs / F;
-    for (int s = t; s < F; s += 1024)
-      for (int tp = 0; tp < C; ++tp) order[bh * pairs + (long long)s * C + tp] = tp * F + s;
-    return;
-  }
   const int kmax = 2 * nb;
   auto key = [&](int pr) {
     const int blk = (pr / F) * 2 * F + pr % F;
@@ -721,6 +704,98 @@ __global__ __launch_bounds__(1024) void k_pair_order(const int32_t* __restrict__
   for (int pr = t; pr < pairs; pr += 1024) {
     const int pos = atomicAdd(&hist[key(pr)], 1);
     order[bh * pairs + pos] = pr;
+  }
+}
+
+// Column order for the whole launch (short lists). Workgroup b runs on XCD b % 8 (round-robin
+// dispatch), so the table lists, for every XCD, the queue of pairs it will run:
+//  1. Runs: G adjacent temporal columns (patches in raster order) of one head, each
+//     column's frame pairs in time order, dealt round-robin to the 8 XCDs: on XCD x queue
+//     rank k holds column 8G*(k / (G*C)) + G*x + (k / C) % G, frame pair k % C (columns
+//     that do not fill a last round keep the plain mapping). The workgroups an XCD holds at
+//     once then come from one run: temporally adjacent pairs of neighbouring patches, whose
+//     kept key blocks largely coincide, so their tiles hit in that XCD's L2.
+//  2. Long pairs first: within each XCD's queue, the pairs whose kept count exceeds 1.25x
+//     the mean move to the front (both parts keep their queue order). Started late, the
+//     longest pairs formed a tail in which most of an XCD's slots sat idle (72% slot use at
+//     480p, 59% with the dynamic threshold).
+// One workgroup; the eight XCD queues are partitioned by two waves each.
+__global__ __launch_bounds__(1024) void k_xcd_order(const int32_t* __restrict__ counts, int32_t* __restrict__ order,
+                                                    const int32_t* __restrict__ mode, int nb, int F, int pairs,
+                                                    int bhs) {
+  __shared__ long long wsum[16];
+  __shared__ int wpart[16];
+  if (ld_const(mode, 0) == 0) return;
+  const int t = threadIdx.x, lane = t & 63, wv = t >> 6;
+  const int C = pairs / F;
+  const int G = column_run_width(C);
+  const int grid = bhs * pairs;
+  const int full = (grid / (8 * G * C)) * 8 * G * C;
+
+  auto pair_cost = [&](int gi) {
+    const int h = gi / pairs, pair = gi - h * pairs;
+    const int blk = (pair / F) * 2 * F + pair % F;
+    const int32_t* c = counts + (long long)h * nb;
+    int k = min(max(c[blk], 0), nb);
+    if (blk + F < nb) k += min(max(c[blk + F], 0), nb);
+    return k;
+  };
+  long long part = 0;
+  for (int gi = t; gi < grid; gi += 1024) part += pair_cost(gi);
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) part += __shfl_xor(part, o);
+  if (lane == 0) wsum[wv] = part;
+  __syncthreads();
+  long long total = 0;
+  for (int w = 0; w < 16; ++w) total += wsum[w];
+
+  // XCD x = two waves; its queue rank k is workgroup 8k + x.
+  const int x = t >> 7, gt = t & 127;
+  const int n_x = (grid - x + 7) / 8;
+  const int n_max = (grid + 7) / 8;
+  auto item = [&](int k) {
+    const int b = 8 * k + x;
+    int logical = b;
+    if (b < full) {
+      const int col = (k / (G * C)) * 8 * G + x * G + (k / C) % G;
+      logical = col * C + k % C;
+    }
+    const int h = logical / pairs, pos = logical - h * pairs;
+    return h * pairs + (pos % C) * F + pos / C;  // column pos / C, frame pair pos % C
+  };
+  auto is_long = [&](int gi) { return 4ll * pair_cost(gi) * grid > 5ll * total; };
+
+  int cnt = 0;
+  for (int k = gt; k < n_x; k += 128) cnt += is_long(item(k)) ? 1 : 0;
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) cnt += __shfl_xor(cnt, o);
+  if (lane == 0) wpart[wv] = cnt;
+  __syncthreads();
+  int base_l = 0, base_s = wpart[2 * x] + wpart[2 * x + 1];
+  __syncthreads();
+  for (int c0 = 0; c0 < n_max; c0 += 128) {
+    const int k = c0 + gt;
+    const bool valid = k < n_x;
+    const int gi = valid ? item(k) : 0;
+    const bool lg = valid && is_long(gi);
+    const int v = (lg ? 1 : 0) | ((valid && !lg) ? 1 << 16 : 0);  // two counts <= 128, packed
+    int incl = v;
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+      const int y = __shfl_up(incl, o);
+      if (lane >= o) incl += y;
+    }
+    if (lane == 63) wpart[wv] = incl;
+    __syncthreads();
+    const int w0 = wpart[2 * x], both = w0 + wpart[2 * x + 1];
+    const int ex = ((wv & 1) ? w0 : 0) + incl - v;
+    if (valid) {
+      const int p = lg ? base_l + (ex & 0xffff) : base_s + (ex >> 16);
+      order[8 * p + x] = gi;
+    }
+    base_l += both & 0xffff;
+    base_s += both >> 16;
+    __syncthreads();
   }
 }
 
@@ -755,6 +830,7 @@ hipError_t launch_sparse_attn(const KGeom& g, int dtype, float scale, const void
     const int pairs = ((g.T + 1) / 2) * F;
     int32_t* mode = row_order + (long long)bhs * g.nb;  // after the order array (pairs <= nb per head)
     k_pair_order<<<dim3(bhs), 1024, 0, s>>>(counts, row_order, mode, g.nb, F, pairs, (long long)bhs * g.nb);
+    k_xcd_order<<<1, 1024, 0, s>>>(counts, row_order, mode, g.nb, F, pairs, (int)bhs);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     AttnArgs a;
