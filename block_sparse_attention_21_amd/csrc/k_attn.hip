@@ -392,7 +392,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
   const int nb = g.nb;
   const int F = g.nbh * g.nbw;
 
-  // Visiting order: item blockIdx.x of the table k_xcd_order wrote (column order, short
+  // Visiting order: item blockIdx.x of the table xcd_queue wrote (column order, short
   // lists), else position blockIdx.x of the per-head longest-first order (long lists), in
   // plain dispatch order: the resident workgroups of all eight XCDs then work on the same
   // one or two heads at a time, whose K/V (tens of MB) stay in the shared last-level cache.
@@ -655,15 +655,98 @@ __device__ void desc_exclusive_scan(int* h, int n, int* part) {
   __syncthreads();
 }
 
+// Column order for the whole launch (short lists). Workgroup b runs on XCD b % 8 (round-robin
+// dispatch), so the table lists, for every XCD, the queue of pairs it will run:
+//  1. Runs: G adjacent temporal columns (patches in raster order) of one head, each
+//     column's frame pairs in time order, dealt round-robin to the 8 XCDs: on XCD x queue
+//     rank k holds column 8G*(k / (G*C)) + G*x + (k / C) % G, frame pair k % C (columns
+//     that do not fill a last round keep the plain mapping). The workgroups an XCD holds at
+//     once then come from one run: temporally adjacent pairs of neighbouring patches, whose
+//     kept key blocks largely coincide, so their tiles hit in that XCD's L2.
+//  2. Long pairs first: within each XCD's queue, the pairs whose kept count exceeds 1.25x
+//     the mean move to the front (both parts keep their queue order). Started late, the
+//     longest pairs formed a tail in which most of an XCD's slots sat idle (72% slot use at
+//     480p, 59% with the dynamic threshold).
+// Workgroup x of k_pair_order writes the queue of XCD x; `total` is the sum of all kept
+// counts (each row belongs to exactly one pair), `wpart` 16 ints of LDS.
+__device__ void xcd_queue(const int32_t* __restrict__ counts, int32_t* __restrict__ order, int nb, int F, int pairs,
+                          int bhs, int x, long long total, int* wpart) {
+  const int t = threadIdx.x, lane = t & 63, wv = t >> 6;
+  const int C = pairs / F;
+  const int G = column_run_width(C);
+  const int grid = bhs * pairs;
+  const int full = (grid / (8 * G * C)) * 8 * G * C;
+
+  auto item = [&](int k) {  // queue rank k of this XCD = workgroup 8k + x
+    const int b = 8 * k + x;
+    int logical = b;
+    if (b < full) {
+      const int col = (k / (G * C)) * 8 * G + x * G + (k / C) % G;
+      logical = col * C + k % C;
+    }
+    const int h = logical / pairs, pos = logical - h * pairs;
+    return h * pairs + (pos % C) * F + pos / C;  // column pos / C, frame pair pos % C
+  };
+  auto is_long = [&](int gi) {  // kept count above 1.25x the mean pair's
+    const int h = gi / pairs, pair = gi - h * pairs;
+    const int blk = (pair / F) * 2 * F + pair % F;
+    const int32_t* c = counts + (long long)h * nb;
+    int k = min(max(c[blk], 0), nb);
+    if (blk + F < nb) k += min(max(c[blk + F], 0), nb);
+    return 4ll * k * grid > 5ll * total;
+  };
+  auto block_scan = [&](int v, int& total_out) {  // exclusive prefix of v over the workgroup
+    int incl = v;
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+      const int y = __shfl_up(incl, o);
+      if (lane >= o) incl += y;
+    }
+    __syncthreads();
+    if (lane == 63) wpart[wv] = incl;
+    __syncthreads();
+    int base = 0, all = 0;
+    for (int w = 0; w < 16; ++w) {
+      base += w < wv ? wpart[w] : 0;
+      all += wpart[w];
+    }
+    total_out = all;
+    return base + incl - v;
+  };
+
+  const int n_x = (grid - x + 7) / 8;
+  int cnt = 0;
+  for (int k = t; k < n_x; k += 1024) cnt += is_long(item(k)) ? 1 : 0;
+  int nlong;
+  block_scan(cnt, nlong);
+  int base_l = 0, base_s = nlong;
+  for (int c0 = 0; c0 < n_x; c0 += 1024) {
+    const int k = c0 + t;
+    const bool valid = k < n_x;
+    const int gi = valid ? item(k) : 0;
+    const bool lg = valid && is_long(gi);
+    int both;
+    const int v = (lg ? 1 : 0) | ((valid && !lg) ? 1 << 16 : 0);  // two counts <= 1024, packed
+    const int ex = block_scan(v, both);
+    if (valid) {
+      const int p = lg ? base_l + (ex & 0xffff) : base_s + (ex >> 16);
+      order[8 * p + x] = gi;
+    }
+    base_l += both & 0xffff;
+    base_s += both >> 16;
+  }
+}
+
 // Visiting order of the query-block pairs (i, i + F) of each (b, h), F = nbh*nbw; pair p covers
 // blocks a = (p / F)*2F + p % F and a + F, so pair tp*F + s is frame pair tp of patch s.
 // Two orders, chosen once per launch from the mean kept count per row over all heads:
-//  - short lists (mean <= kColumnMaxCount): column order, built by k_xcd_order for the whole
-//    launch (below).
+//  - short lists (mean <= kColumnMaxCount): column order for the whole launch, the queues of
+//    the 8 XCDs written by workgroups 0-7 (xcd_queue above).
 //  - otherwise: pairs longest-first by their kept count (counting sort), so the long rows
 //    do not form the tail; with long lists neighbouring workgroups start too far apart
 //    for L2 reuse and the balance matters more.
 // Every workgroup computes the same mean (a fixed-order sum); workgroup 0 stores the mode.
+// The grid is max(B*H, 8) workgroups.
 constexpr int kColumnMaxCount = 96;
 
 __global__ __launch_bounds__(1024) void k_pair_order(const int32_t* __restrict__ counts, int32_t* __restrict__ order,
@@ -686,7 +769,12 @@ __global__ __launch_bounds__(1024) void k_pair_order(const int32_t* __restrict__
   for (int w = 0; w < 16; ++w) total += wsum[w];
   const bool column = total <= (long long)kColumnMaxCount * rows;
   if (bh == 0 && t == 0) mode_out[0] = column ? 1 : 0;
-  if (column) return;  // k_xcd_order writes the whole order
+  const int bhs = (int)(rows / nb);
+  if (column) {
+    if (bh < 8) xcd_queue(counts, order, nb, F, pairs, bhs, (int)bh, total, scan_part);
+    return;
+  }
+  if (bh >= bhs) return;
 
   auto blk_count = [&](int blk) { return min(max(c[blk], 0), nb); };
   const int kmax = 2 * nb;
@@ -704,98 +792,6 @@ __global__ __launch_bounds__(1024) void k_pair_order(const int32_t* __restrict__
   for (int pr = t; pr < pairs; pr += 1024) {
     const int pos = atomicAdd(&hist[key(pr)], 1);
     order[bh * pairs + pos] = pr;
-  }
-}
-
-// Column order for the whole launch (short lists). Workgroup b runs on XCD b % 8 (round-robin
-// dispatch), so the table lists, for every XCD, the queue of pairs it will run:
-//  1. Runs: G adjacent temporal columns (patches in raster order) of one head, each
-//     column's frame pairs in time order, dealt round-robin to the 8 XCDs: on XCD x queue
-//     rank k holds column 8G*(k / (G*C)) + G*x + (k / C) % G, frame pair k % C (columns
-//     that do not fill a last round keep the plain mapping). The workgroups an XCD holds at
-//     once then come from one run: temporally adjacent pairs of neighbouring patches, whose
-//     kept key blocks largely coincide, so their tiles hit in that XCD's L2.
-//  2. Long pairs first: within each XCD's queue, the pairs whose kept count exceeds 1.25x
-//     the mean move to the front (both parts keep their queue order). Started late, the
-//     longest pairs formed a tail in which most of an XCD's slots sat idle (72% slot use at
-//     480p, 59% with the dynamic threshold).
-// One workgroup; the eight XCD queues are partitioned by two waves each.
-__global__ __launch_bounds__(1024) void k_xcd_order(const int32_t* __restrict__ counts, int32_t* __restrict__ order,
-                                                    const int32_t* __restrict__ mode, int nb, int F, int pairs,
-                                                    int bhs) {
-  __shared__ long long wsum[16];
-  __shared__ int wpart[16];
-  if (ld_const(mode, 0) == 0) return;
-  const int t = threadIdx.x, lane = t & 63, wv = t >> 6;
-  const int C = pairs / F;
-  const int G = column_run_width(C);
-  const int grid = bhs * pairs;
-  const int full = (grid / (8 * G * C)) * 8 * G * C;
-
-  auto pair_cost = [&](int gi) {
-    const int h = gi / pairs, pair = gi - h * pairs;
-    const int blk = (pair / F) * 2 * F + pair % F;
-    const int32_t* c = counts + (long long)h * nb;
-    int k = min(max(c[blk], 0), nb);
-    if (blk + F < nb) k += min(max(c[blk + F], 0), nb);
-    return k;
-  };
-  long long part = 0;
-  for (int gi = t; gi < grid; gi += 1024) part += pair_cost(gi);
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) part += __shfl_xor(part, o);
-  if (lane == 0) wsum[wv] = part;
-  __syncthreads();
-  long long total = 0;
-  for (int w = 0; w < 16; ++w) total += wsum[w];
-
-  // XCD x = two waves; its queue rank k is workgroup 8k + x.
-  const int x = t >> 7, gt = t & 127;
-  const int n_x = (grid - x + 7) / 8;
-  const int n_max = (grid + 7) / 8;
-  auto item = [&](int k) {
-    const int b = 8 * k + x;
-    int logical = b;
-    if (b < full) {
-      const int col = (k / (G * C)) * 8 * G + x * G + (k / C) % G;
-      logical = col * C + k % C;
-    }
-    const int h = logical / pairs, pos = logical - h * pairs;
-    return h * pairs + (pos % C) * F + pos / C;  // column pos / C, frame pair pos % C
-  };
-  auto is_long = [&](int gi) { return 4ll * pair_cost(gi) * grid > 5ll * total; };
-
-  int cnt = 0;
-  for (int k = gt; k < n_x; k += 128) cnt += is_long(item(k)) ? 1 : 0;
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) cnt += __shfl_xor(cnt, o);
-  if (lane == 0) wpart[wv] = cnt;
-  __syncthreads();
-  int base_l = 0, base_s = wpart[2 * x] + wpart[2 * x + 1];
-  __syncthreads();
-  for (int c0 = 0; c0 < n_max; c0 += 128) {
-    const int k = c0 + gt;
-    const bool valid = k < n_x;
-    const int gi = valid ? item(k) : 0;
-    const bool lg = valid && is_long(gi);
-    const int v = (lg ? 1 : 0) | ((valid && !lg) ? 1 << 16 : 0);  // two counts <= 128, packed
-    int incl = v;
-#pragma unroll
-    for (int o = 1; o < 64; o <<= 1) {
-      const int y = __shfl_up(incl, o);
-      if (lane >= o) incl += y;
-    }
-    if (lane == 63) wpart[wv] = incl;
-    __syncthreads();
-    const int w0 = wpart[2 * x], both = w0 + wpart[2 * x + 1];
-    const int ex = ((wv & 1) ? w0 : 0) + incl - v;
-    if (valid) {
-      const int p = lg ? base_l + (ex & 0xffff) : base_s + (ex >> 16);
-      order[8 * p + x] = gi;
-    }
-    base_l += both & 0xffff;
-    base_s += both >> 16;
-    __syncthreads();
   }
 }
 
@@ -829,8 +825,8 @@ hipError_t launch_sparse_attn(const KGeom& g, int dtype, float scale, const void
     const int F = g.nbh * g.nbw;
     const int pairs = ((g.T + 1) / 2) * F;
     int32_t* mode = row_order + (long long)bhs * g.nb;  // after the order array (pairs <= nb per head)
-    k_pair_order<<<dim3(bhs), 1024, 0, s>>>(counts, row_order, mode, g.nb, F, pairs, (long long)bhs * g.nb);
-    k_xcd_order<<<1, 1024, 0, s>>>(counts, row_order, mode, g.nb, F, pairs, (int)bhs);
+    k_pair_order<<<dim3(bhs > 8 ? bhs : 8), 1024, 0, s>>>(counts, row_order, mode, g.nb, F, pairs,
+                                                           (long long)bhs * g.nb);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     AttnArgs a;
