@@ -56,8 +56,8 @@ abla_status from_hip(hipError_t e) { return e == hipSuccess ? ABLA_OK : ABLA_ERR
 
 size_t align256(size_t n) { return (n + 255) & ~(size_t)255; }
 
-// Backward scratch: D and L2 ([B,H,N] float32), column counts [B,H,nb] and column lists
-// [B,H,nb,nb] (int32), each 256-aligned.
+// Backward scratch: D and L2 ([B,H,N] float32), column counts [B,H,nb], column lists
+// [B,H,nb,nb] and the workgroup visiting order [B,H,nb] (int32), each 256-aligned.
 size_t bwd_parts(const abla_geom* g, BwdWorkspace* ws, char* base) {
   const size_t bh = bh_of(g), nb = (size_t)nb_of(g);
   const size_t n = (size_t)g->T * (size_t)g->Hs * (size_t)g->Ws;
@@ -68,8 +68,9 @@ size_t bwd_parts(const abla_geom* g, BwdWorkspace* ws, char* base) {
     ws->L2 = reinterpret_cast<float*>(base + rows);
     ws->col_counts = reinterpret_cast<int32_t*>(base + 2 * rows);
     ws->col_lists = reinterpret_cast<int32_t*>(base + 2 * rows + cc);
+    ws->order = reinterpret_cast<int32_t*>(base + 2 * rows + cc + cl);
   }
-  return 2 * rows + cc + cl;
+  return 2 * rows + 2 * cc + cl;
 }
 
 }  // namespace

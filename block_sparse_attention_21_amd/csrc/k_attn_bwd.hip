@@ -175,11 +175,103 @@ __device__ __forceinline__ void column_order(int wg, const KGeom& g, long long& 
   blk = (cm % T) * F + cm / T;
 }
 
+// The bf16 kernels read their block from a table: the column order above. When the list
+// lengths are heavy-tailed (the longest above 3x the mean), each XCD's queue (the workgroups
+// w with w % 8 == x, in order) is partitioned so that the blocks whose list is longer than
+// 1.25x the mean come first, both parts in queue order. Started late, the longest lists
+// formed a tail in which a quarter of the slots sat idle (dQ at 480p: 73% slot use).
+// Workgroup x writes the queue of XCD x; `cnt` holds the list lengths (counts for dQ,
+// column counts for dK/dV); order[w] = bh * nb + block.
+__global__ __launch_bounds__(1024) void k_bwd_order(const int32_t* __restrict__ cnt, int32_t* __restrict__ order,
+                                                    KGeom g, int bhs) {
+  __shared__ long long wsum[16];
+  __shared__ int wpart[16];
+  const int t = threadIdx.x, lane = t & 63, wv = t >> 6;
+  const int x = blockIdx.x, nb = g.nb;
+  const int grid = bhs * nb;
+  long long part = 0;
+  int mx = 0;
+  for (int r = t; r < grid; r += 1024) {
+    const int c = min(max(cnt[r], 0), nb);
+    part += c;
+    mx = max(mx, c);
+  }
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) {
+    part += __shfl_xor(part, o);
+    mx = max(mx, __shfl_xor(mx, o));
+  }
+  if (lane == 0) {
+    wsum[wv] = part;
+    wpart[wv] = mx;
+  }
+  __syncthreads();
+  long long total = 0;
+  for (int w = 0; w < 16; ++w) {
+    total += wsum[w];
+    mx = max(mx, wpart[w]);
+  }
+
+  auto item = [&](int k) {  // queue rank k of this XCD = workgroup 8k + x
+    long long bh;
+    int blk;
+    column_order(8 * k + x, g, bh, blk);
+    return (int)bh * nb + blk;
+  };
+  auto is_long = [&](int gi) { return 4ll * min(max(cnt[gi], 0), nb) * grid > 5ll * total; };
+  auto block_scan = [&](int v, int& total_out) {  // exclusive prefix of v over the workgroup
+    int incl = v;
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+      const int y = __shfl_up(incl, o);
+      if (lane >= o) incl += y;
+    }
+    __syncthreads();
+    if (lane == 63) wpart[wv] = incl;
+    __syncthreads();
+    int base = 0, all = 0;
+    for (int w = 0; w < 16; ++w) {
+      base += w < wv ? wpart[w] : 0;
+      all += wpart[w];
+    }
+    total_out = all;
+    return base + incl - v;
+  };
+  const int n_x = (grid - x + 7) / 8;
+  // Without a heavy tail (longest list at most 3x the mean) the plain column order is kept:
+  // at 720p moving the longer lists forward only cost L2 reuse.
+  if ((long long)mx * grid <= 3ll * total) {
+    for (int k = t; k < n_x; k += 1024) order[8 * k + x] = item(k);
+    return;
+  }
+  int c = 0;
+  for (int k = t; k < n_x; k += 1024) c += is_long(item(k)) ? 1 : 0;
+  int nlong;
+  block_scan(c, nlong);
+  int base_l = 0, base_s = nlong;
+  for (int c0 = 0; c0 < n_x; c0 += 1024) {
+    const int k = c0 + t;
+    const bool valid = k < n_x;
+    const int gi = valid ? item(k) : 0;
+    const bool lg = valid && is_long(gi);
+    int both;
+    const int v = (lg ? 1 : 0) | ((valid && !lg) ? 1 << 16 : 0);  // two counts <= 1024, packed
+    const int ex = block_scan(v, both);
+    if (valid) {
+      const int p = lg ? base_l + (ex & 0xffff) : base_s + (ex >> 16);
+      order[8 * p + x] = gi;
+    }
+    base_l += both & 0xffff;
+    base_s += both >> 16;
+  }
+}
+
 // ------------------------------------------------------------------- dQ
 struct DqArgs {
   const uint16_t *q, *k, *v, *dout;  // original token order
   const float *Dm, *L2;
   const int32_t *counts, *lists;
+  const int32_t* order;  // visiting order (k_bwd_order)
   uint16_t* dq;
   KGeom g;
   float c2, scale;
@@ -198,9 +290,9 @@ __global__ __launch_bounds__(kBwdThreads) __attribute__((amdgpu_waves_per_eu(2, 
   const int t = threadIdx.x, lane = t & 63, hi = lane >> 5;
   const int w = __builtin_amdgcn_readfirstlane(t >> 6);
   const int qh = w & 1, kh = w >> 1;
-  long long bh;
-  int i;
-  column_order(blockIdx.x, g, bh, i);
+  const int gi = ld_const(a.order, (long long)blockIdx.x);
+  const long long bh = gi / nb;
+  const int i = gi - (int)bh * nb;
   const long long row = bh * nb + i;
   const int cnt = min(max(ld_const(a.counts, row), 0), nb);
   const int q_local = qh * 32 + (lane & 31);
@@ -319,6 +411,7 @@ struct DkvArgs {
   const uint16_t *k, *v, *q, *dout;  // original token order
   const float *Dm, *L2;
   const int32_t *col_counts, *col_lists;
+  const int32_t* order;  // visiting order (k_bwd_order)
   uint16_t *dk, *dv;
   KGeom g;
   float c2, scale;
@@ -375,9 +468,9 @@ __global__ __launch_bounds__(kBwdThreads) __attribute__((amdgpu_waves_per_eu(2, 
   const int t = threadIdx.x, lane = t & 63, hi = lane >> 5;
   const int w = __builtin_amdgcn_readfirstlane(t >> 6);
   const int kh = w & 1, qh = w >> 1;
-  long long bh;
-  int j;
-  column_order(blockIdx.x, g, bh, j);
+  const int gi = ld_const(a.order, (long long)blockIdx.x);
+  const long long bh = gi / nb;
+  const int j = gi - (int)bh * nb;
   const long long col = bh * nb + j;
   const int cnt = min(max(ld_const(a.col_counts, col), 0), nb);
   const int k_local = kh * 32 + (lane & 31);
@@ -715,13 +808,17 @@ hipError_t launch_sparse_attn_bwd(const KGeom& g, int dtype, float scale, const 
   const uint16_t* q16 = static_cast<const uint16_t*>(q);
   const uint16_t* k16 = static_cast<const uint16_t*>(k);
   const uint16_t* v16 = static_cast<const uint16_t*>(v);
-  DqArgs qa{q16, k16, v16, do16, ws.D, ws.L2, counts, lists, static_cast<uint16_t*>(dq), g, c2, scale};
+  k_bwd_order<<<8, 1024, 0, s>>>(counts, ws.order, g, (int)bhs);
+  if ((e = hipGetLastError()) != hipSuccess) return e;
+  DqArgs qa{q16, k16, v16, do16, ws.D, ws.L2, counts, lists, ws.order, static_cast<uint16_t*>(dq), g, c2, scale};
   if (g.d == 128)
     k_bwd_dq<128><<<grid, kBwdThreads, 0, s>>>(qa);
   else
     k_bwd_dq<64><<<grid, kBwdThreads, 0, s>>>(qa);
   if ((e = hipGetLastError()) != hipSuccess) return e;
-  DkvArgs ka{k16, v16, q16, do16, ws.D, ws.L2, ws.col_counts, ws.col_lists,
+  k_bwd_order<<<8, 1024, 0, s>>>(ws.col_counts, ws.order, g, (int)bhs);
+  if ((e = hipGetLastError()) != hipSuccess) return e;
+  DkvArgs ka{k16, v16, q16, do16, ws.D, ws.L2, ws.col_counts, ws.col_lists, ws.order,
              static_cast<uint16_t*>(dk), static_cast<uint16_t*>(dv), g, c2, scale};
   if (g.d == 128)
     k_bwd_dkdv<128><<<grid, kBwdThreads, 0, s>>>(ka);

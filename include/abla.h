@@ -195,8 +195,9 @@ abla_status abla_sparse_attn_fwd(const abla_geom* g, int32_t dtype, float scale,
                                  void* out, int32_t layout_flags, float* lse,
                                  void* workspace, size_t workspace_bytes, void* stream);
 
-/* Bytes of scratch abla_sparse_attn_bwd needs: two [B,H,N] float32 rows (D and log2(e)*lse)
- * and the column counts [B,H,nb] and lists [B,H,nb,nb] int32, each rounded up to 256 bytes.
+/* Bytes of scratch abla_sparse_attn_bwd needs: two [B,H,N] float32 rows (D and log2(e)*lse),
+ * the column counts [B,H,nb] and lists [B,H,nb,nb] int32 and a [B,H,nb] int32 workgroup
+ * visiting order, each rounded up to 256 bytes.
  * (The kernels read q, k, v and dout in their original token order; no copies are made.) */
 size_t abla_sparse_attn_bwd_workspace_bytes(const abla_geom* g);
 

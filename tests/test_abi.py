@@ -159,8 +159,8 @@ def test_backward_errors(A):
     def al(n):
         return (n + 255) // 256 * 256
 
-    # B*H = 2, N = 1152, nb = 18: D and L2 rows, column counts, column lists
-    assert need == 2 * al(2 * 1152 * 4) + al(2 * 18 * 4) + al(2 * 18 * 18 * 4)
+    # B*H = 2, N = 1152, nb = 18: D and L2 rows, column counts and visiting order, column lists
+    assert need == 2 * al(2 * 1152 * 4) + 2 * al(2 * 18 * 4) + al(2 * 18 * 18 * 4)
     assert bwd_call(A, g, ws_bytes=need - 1) == 3
     assert bwd_call(A, G(A, d=32)) == 2
 
