@@ -52,6 +52,7 @@ def _load():
     G = ctypes.POINTER(_Geom)
     sigs = {
         "abla_reorder": (i32, [G, i32, i32, i32, vp, vp, vp, vp]),
+        "abla_pool_qk_reorder_v": (i32, [G, i32, vp, vp, vp, vp, vp, vp, vp]),
         "abla_build_mask_workspace_bytes": (sz, [G]),
         "abla_build_mask": (i32, [G, ctypes.POINTER(_MaskParams), vp, vp, vp, vp, vp, vp, sz, vp]),
         "abla_sparse_attn_workspace_bytes": (sz, [G]),
@@ -68,7 +69,7 @@ def _load():
 
 
 _lib = _load()
-EXPORTED = ("abla_reorder", "abla_build_mask_workspace_bytes", "abla_build_mask", "abla_sparse_attn_workspace_bytes",
+EXPORTED = ("abla_reorder", "abla_pool_qk_reorder_v", "abla_build_mask_workspace_bytes", "abla_build_mask", "abla_sparse_attn_workspace_bytes",
             "abla_sparse_attn_fwd", "abla_sparse_attn_bwd_workspace_bytes", "abla_sparse_attn_bwd", "abla_status_str",
             "abla_version")
 
@@ -196,6 +197,31 @@ def reorder(x: torch.Tensor, geom: Geometry, *, inverse: bool = False, layout: s
     if pool_only:
         return pooled
     return (out, pooled) if pooled is not None else out
+
+
+def pool_qk_reorder_v(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, geom: Geometry, *,
+                      qbar: Optional[torch.Tensor] = None, kbar: Optional[torch.Tensor] = None,
+                      v_rt: Optional[torch.Tensor] = None):
+    """abla_pool_qk_reorder_v: float64 block means of q and k and v in channel-major fractal
+    blocks, in one launch. Returns (qbar, kbar, v_rt)."""
+    dev = _device(q)
+    if q.dtype not in _DT:
+        raise ValueError(f"unsupported dtype {q.dtype}")
+    shape = (geom.B, geom.H, geom.N, geom.d)
+    for name, x in (("q", q), ("k", k), ("v", v)):
+        _need(x, name, shape, q.dtype, dev)
+    pshape = (geom.B, geom.H, geom.nb, geom.d)
+    qbar = torch.empty(pshape, dtype=torch.float64, device=dev) if qbar is None else qbar
+    kbar = torch.empty(pshape, dtype=torch.float64, device=dev) if kbar is None else kbar
+    vshape = (geom.B, geom.H, geom.nb, geom.d, 64)
+    v_rt = torch.empty(vshape, dtype=q.dtype, device=dev) if v_rt is None else v_rt
+    _need(qbar, "qbar", pshape, torch.float64, dev)
+    _need(kbar, "kbar", pshape, torch.float64, dev)
+    _need(v_rt, "v_rt", vshape, q.dtype, dev)
+    g = geom.c()
+    _check(_lib.abla_pool_qk_reorder_v(ctypes.byref(g), _DT[q.dtype], _ptr(q), _ptr(k), _ptr(v), _ptr(qbar),
+                                       _ptr(kbar), _ptr(v_rt), _stream(q)), "abla_pool_qk_reorder_v")
+    return qbar, kbar, v_rt
 
 
 def build_mask_workspace_bytes(geom: Geometry) -> int:
@@ -347,6 +373,11 @@ class NablaAttention:
         self.ws_attn = torch.empty(max(sparse_attn_workspace_bytes(g), 1), dtype=torch.uint8, device=dev)
 
     def reorder_pool(self, q, k, v):
+        if self.fused and not self.fuse_v:
+            # One launch: Q and K pooled in place, V reordered channel-major.
+            pool_qk_reorder_v(q, k, v, self.geom, qbar=self.qbar, kbar=self.kbar, v_rt=self.v_rt)
+            self._q, self._k, self._v = q, k, v
+            return
         if self.fused:
             reorder(q, self.geom, pooled=self.qbar, pool_only=True)
             reorder(k, self.geom, pooled=self.kbar, pool_only=True)

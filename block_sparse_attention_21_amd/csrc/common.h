@@ -50,6 +50,8 @@ __device__ __forceinline__ float bf16_to_f32(uint16_t b) { return __uint_as_floa
 // Launchers (one per kernel family). Each returns hipGetLastError() after enqueueing.
 hipError_t launch_reorder(const KGeom& g, int dtype, int inverse, int layout, const void* x, void* y,
                           double* pooled, hipStream_t s);
+hipError_t launch_pool_qk_reorder_v(const KGeom& g, int dtype, const void* q, const void* k, const void* v,
+                                    double* qbar, double* kbar, void* vrt, hipStream_t s);
 hipError_t launch_build_mask(const KGeom& g, const abla_mask_params& p, const double* qbar, const double* kbar,
                              uint32_t* words, int32_t* counts, int32_t* lists, double* scores, hipStream_t s);
 hipError_t launch_sparse_attn(const KGeom& g, int dtype, float scale, const void* q, const void* k,

@@ -51,20 +51,26 @@ __device__ __forceinline__ void add_chunk<uint16_t>(double* acc, const uint4& v)
   }
 }
 
-// Forward: original order -> fractal order (token rows, or channel-major blocks); with
-// STORE = false only the pooled means are written.
+// LDS bytes of one block move: the channel-major transpose tile, or the pooling partials.
+template <typename E, int D>
+constexpr int kSmemBytes = (kBlock * D * (int)sizeof(E)) > (kThreads * Shape<E, D>::EPC * 8)
+                               ? kBlock * D * (int)sizeof(E)
+                               : kThreads * Shape<E, D>::EPC * 8;
+
+// Forward, one 64-token block `blk` (over B*H*nb): original order -> fractal order (token
+// rows, or channel-major blocks); with STORE = false only the pooled means are written.
+// smem: kSmemBytes<E, D> bytes, 16-byte aligned.
 template <typename E, int D, bool POOL, bool BLOCK_T, bool STORE = true>
-__global__ __launch_bounds__(kThreads) void k_reorder_fwd(const E* __restrict__ x, E* __restrict__ y,
-                                                          double* __restrict__ pooled, KGeom g) {
+__device__ __forceinline__ void reorder_block(const E* __restrict__ x, E* __restrict__ y, double* __restrict__ pooled,
+                                              const KGeom& g, int blk, char* smem) {
   using S = Shape<E, D>;
   // Channel-major transpose tile: token row r holds its D elements as CPR 16-byte chunks, chunk
   // cc stored at position cc ^ ((r / EPC) % CPR). The gathers below (EPC tokens of one channel
   // per lane, one group of EPC tokens per lane of a run of kBlock/EPC lanes) then hit distinct
   // banks, and the 16-byte row writes stay conflict-free.
-  __shared__ __attribute__((aligned(16))) E tile[BLOCK_T ? kBlock * D : 1];
-  __shared__ double red[POOL ? kThreads * S::EPC : 1];
+  E* tile = reinterpret_cast<E*>(smem);
+  double* red = reinterpret_cast<double*>(smem);
 
-  const int blk = blockIdx.x;
   const int bh = blk / g.nb;
   const int i = blk - bh * g.nb;
   const int t = threadIdx.x;
@@ -112,6 +118,7 @@ __global__ __launch_bounds__(kThreads) void k_reorder_fwd(const E* __restrict__ 
   }
 
   if constexpr (POOL) {
+    if constexpr (BLOCK_T) __syncthreads();  // the partials reuse the transpose tile's LDS
 #pragma unroll
     for (int e = 0; e < S::EPC; ++e) red[t * S::EPC + e] = acc[e];
     __syncthreads();
@@ -123,6 +130,33 @@ __global__ __launch_bounds__(kThreads) void k_reorder_fwd(const E* __restrict__ 
       pooled[((long long)bh * g.nb + i) * D + c] = s * (1.0 / kBlock);
     }
   }
+}
+
+template <typename E, int D, bool POOL, bool BLOCK_T, bool STORE = true>
+__global__ __launch_bounds__(kThreads) void k_reorder_fwd(const E* __restrict__ x, E* __restrict__ y,
+                                                          double* __restrict__ pooled, KGeom g) {
+  __shared__ __attribute__((aligned(16))) char smem[kSmemBytes<E, D>];
+  reorder_block<E, D, POOL, BLOCK_T, STORE>(x, y, pooled, g, blockIdx.x, smem);
+}
+
+// The layer's first step in one launch: workgroups [0, n) pool Q, [n, 2n) pool K (both read
+// in the original order, not copied), [2n, 3n) reorder V into channel-major blocks, with
+// n = B*H*nb. One grid instead of three saves two launch gaps and two ramp-down tails.
+template <typename E, int D>
+__global__ __launch_bounds__(kThreads) void k_pool_qk_reorder_v(const E* __restrict__ q, const E* __restrict__ k,
+                                                                const E* __restrict__ v, double* __restrict__ qbar,
+                                                                double* __restrict__ kbar, E* __restrict__ vrt,
+                                                                KGeom g) {
+  __shared__ __attribute__((aligned(16))) char smem[kSmemBytes<E, D>];
+  const int n = g.B * g.H * g.nb;
+  const int which = blockIdx.x / n;
+  const int blk = blockIdx.x - which * n;
+  if (which == 0)
+    reorder_block<E, D, true, false, false>(q, nullptr, qbar, g, blk, smem);
+  else if (which == 1)
+    reorder_block<E, D, true, false, false>(k, nullptr, kbar, g, blk, smem);
+  else
+    reorder_block<E, D, false, true, true>(v, vrt, nullptr, g, blk, smem);
 }
 
 // Inverse: fractal order (token rows) -> original order.
@@ -169,7 +203,26 @@ hipError_t dispatch(const KGeom& g, int inverse, int layout, const void* x, void
   return hipGetLastError();
 }
 
+template <typename E, int D>
+hipError_t dispatch_qkv(const KGeom& g, const void* q, const void* k, const void* v, double* qbar, double* kbar,
+                        void* vrt, hipStream_t s) {
+  const dim3 grid((unsigned)(3LL * g.B * g.H * g.nb));
+  k_pool_qk_reorder_v<E, D><<<grid, kThreads, 0, s>>>(static_cast<const E*>(q), static_cast<const E*>(k),
+                                                      static_cast<const E*>(v), qbar, kbar, static_cast<E*>(vrt), g);
+  return hipGetLastError();
+}
+
 }  // namespace
+
+hipError_t launch_pool_qk_reorder_v(const KGeom& g, int dtype, const void* q, const void* k, const void* v,
+                                    double* qbar, double* kbar, void* vrt, hipStream_t s) {
+  if (dtype == ABLA_F32) {
+    return g.d == 64 ? dispatch_qkv<float, 64>(g, q, k, v, qbar, kbar, vrt, s)
+                     : dispatch_qkv<float, 128>(g, q, k, v, qbar, kbar, vrt, s);
+  }
+  return g.d == 64 ? dispatch_qkv<uint16_t, 64>(g, q, k, v, qbar, kbar, vrt, s)
+                   : dispatch_qkv<uint16_t, 128>(g, q, k, v, qbar, kbar, vrt, s);
+}
 
 hipError_t launch_reorder(const KGeom& g, int dtype, int inverse, int layout, const void* x, void* y,
                           double* pooled, hipStream_t s) {

@@ -8,6 +8,7 @@
  * Attention for Long Video Diffusion" (Methodology A, Dynamic-Threshold mode):
  *
  *   abla_reorder          fractal flattening of the tokens + block mean-pooling
+ *   abla_pool_qk_reorder_v  the layer's first step (Q, K pooling, V reorder) in one launch
  *   abla_build_mask       reduced attention over pooled blocks, per-row CDF cut
  *                         (or logit threshold), OR the sliding-tile window
  *   abla_sparse_attn_fwd  attention restricted to the kept 64 x 64 blocks
@@ -107,6 +108,21 @@ typedef struct {
  * {64, 128}, more than 2^31 - 1 tokens per head or B*H*nb above 2^31 - 1. */
 abla_status abla_reorder(const abla_geom* g, int32_t dtype, int32_t inverse, int32_t layout,
                          const void* x, void* y, double* pooled, void* stream);
+
+/* The first step of a layer in one launch: block means of q and k, and v reordered into
+ * channel-major blocks. Results are identical to three abla_reorder calls:
+ *   abla_reorder(q, y = NULL, qbar), abla_reorder(k, y = NULL, kbar) (pooling only; q and k
+ *   stay in the original order for abla_sparse_attn_fwd with ABLA_ATTN_QK_ORIGINAL), and
+ *   abla_reorder(v, v_rt, layout ABLA_LAYOUT_BLOCK_T, no pooling).
+ * Source: NABLA, Method -- "Fractal Flattening" and "down-sampling" (as abla_reorder).
+ * q, k, v: [B,H,N,d] of `dtype` in the original token order.
+ * qbar, kbar: [B,H,nb,d] float64 outputs; v_rt: [B,H,nb,d,64] of `dtype` output.
+ * One grid of 3*B*H*nb workgroups instead of three launches.
+ * Errors: INVALID for null pointers, unknown dtype, bad geometry, an output overlapping an
+ * input or another output; UNSUPPORTED for the geometry limits of abla_reorder or
+ * 3*B*H*nb above 2^31 - 1. */
+abla_status abla_pool_qk_reorder_v(const abla_geom* g, int32_t dtype, const void* q, const void* k, const void* v,
+                                   double* qbar, double* kbar, void* v_rt, void* stream);
 
 /* Bytes of scratch abla_build_mask needs: B*H*nb*nb*8 (the float64 pooled score matrix;
  * not used by the STATIC mode). */

@@ -31,7 +31,7 @@ def declared_functions():
 
 def test_exports_every_declared_symbol(A):
     names = declared_functions()
-    assert len(names) == 9
+    assert len(names) == 10
     lib = ctypes.CDLL(LIB)
     for n in names:
         assert hasattr(lib, n), n
@@ -75,6 +75,25 @@ def test_reorder_argument_errors(A):
     assert reorder(A, g, inverse=1, pooled=ctypes.c_void_p(0x7000000)) == 1
     assert reorder(A, g, inverse=2) == 1
     assert A._lib.abla_reorder(None, 1, 0, 0, FAKE, FAKE2, None, None) == 1
+
+
+def qkv_call(A, g, dtype=1, q=ctypes.c_void_p(1 << 32), k=ctypes.c_void_p(2 << 32), v=ctypes.c_void_p(3 << 32),
+             qbar=ctypes.c_void_p(4 << 32), kbar=ctypes.c_void_p(5 << 32), v_rt=ctypes.c_void_p(6 << 32)):
+    return A._lib.abla_pool_qk_reorder_v(ctypes.byref(g), dtype, q, k, v, qbar, kbar, v_rt, None)
+
+
+def test_pool_qk_reorder_v_errors(A):
+    g = G(A)
+    for n in ("q", "k", "v", "qbar", "kbar", "v_rt"):
+        assert qkv_call(A, g, **{n: None}) == 1, n
+    assert qkv_call(A, g, dtype=7) == 1
+    assert qkv_call(A, g, v_rt=ctypes.c_void_p(1 << 32)) == 1  # v_rt aliases q
+    assert qkv_call(A, g, qbar=ctypes.c_void_p((3 << 32) + 64)) == 1  # qbar inside v
+    assert qkv_call(A, g, kbar=ctypes.c_void_p((4 << 32) + 8)) == 1  # kbar overlaps qbar
+    assert qkv_call(A, g, v_rt=ctypes.c_void_p((5 << 32) + 8)) == 1  # v_rt overlaps kbar
+    assert qkv_call(A, G(A, d=96)) == 2
+    assert qkv_call(A, G(A, B=0)) == 1
+    assert A._lib.abla_pool_qk_reorder_v(None, 1, FAKE, FAKE, FAKE, FAKE2, FAKE2, FAKE2, None) == 1
 
 
 def mask_call(A, g, p, ws=FAKE, ws_bytes=1 << 40, q=FAKE, k=FAKE, words=FAKE2, counts=FAKE2):

@@ -64,6 +64,31 @@ def test_reorder_and_pool(A, dtype, d, geo):
     np.testing.assert_allclose(pooled.cpu().numpy(), pref, rtol=1e-13, atol=1e-15)
 
 
+@pytest.mark.parametrize("dtype,d,geo", [
+    ("f32", 64, (1, 2, 8, 16, 16)), ("bf16", 128, (1, 3, 3, 24, 40)), ("bf16", 64, (2, 1, 2, 16, 8)),
+    ("f32", 128, (1, 1, 5, 8, 24)), ("bf16", 128, (1, 1, 1, 8, 8)),
+])
+def test_pool_qk_reorder_v(A, dtype, d, geo):
+    """The one-launch first step: Q and K block means and V's channel-major fractal blocks equal
+    the oracle's (V bit-exact, means to float64 rounding) and, bit for bit, the three separate
+    abla_reorder passes."""
+    B, H, T, Hs, Ws = geo
+    geom, og = PT.geoms(B, H, T, Hs, Ws, d)
+    q, k, v = make_random_qkv(B, H, T, Hs, Ws, d, dtype, seed=4, device=DEV)
+    qbar, kbar, v_rt = A.pool_qk_reorder_v(q, k, v, geom)
+    sq = A.reorder(q, geom, pool_only=True)
+    sk = A.reorder(k, geom, pool_only=True)
+    sv = A.reorder(v, geom, layout="block_t")
+    torch.cuda.synchronize()
+    assert torch.equal(qbar, sq) and torch.equal(kbar, sk)
+    assert np.array_equal(_bits(v_rt), _bits(sv))
+    ref_t = R.reorder(_bits(v), og).reshape(B, H, og.nb, 64, d).transpose(0, 1, 2, 4, 3)
+    assert np.array_equal(_bits(v_rt), ref_t)
+    for got, x in ((qbar, q), (kbar, k)):
+        np.testing.assert_allclose(got.cpu().numpy(), R.block_means(R.reorder(R.to64(x), og), og),
+                                   rtol=1e-13, atol=1e-15)
+
+
 # ---------------------------------------------------------------- small end-to-end, every element
 SMALL = [
     # (name, dtype, d, (B,H,T,Hs,Ws), MaskParams kwargs)
