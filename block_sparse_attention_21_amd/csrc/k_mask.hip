@@ -47,18 +47,21 @@ namespace {
 // Kbar rows give bit-identical scores.
 typedef double f64x4_t __attribute__((ext_vector_type(4)));
 
-template <int TM>
+template <int TM, int D>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void k_scores(
-    const double* __restrict__ qbar, const double* __restrict__ kbar, double* __restrict__ S, int nb, int d,
-    double scale) {
+    const double* __restrict__ qbar, const double* __restrict__ kbar, double* __restrict__ S, int nb, double scale) {
   constexpr int NT = TM / 32;  // 16x16 tiles per wave side
+  constexpr int NC = D / 16;   // channel chunks
+  // With 64 x 64 tiles the next chunk's operands are loaded while this chunk's products run
+  // (two register buffers); 128 x 128 tiles have no registers to spare for that.
+  constexpr int NB = TM == 64 ? 2 : 1;
   const int t = threadIdx.x, lane = t & 63, w = t >> 6;
   const int r16 = lane & 15, kq = lane >> 4;
   const int i0 = blockIdx.y * TM + (w >> 1) * (TM / 2);
   const int j0 = blockIdx.x * TM + (w & 1) * (TM / 2);
   const long long bh = blockIdx.z;
-  const double* qh = qbar + bh * nb * d;
-  const double* kh = kbar + bh * nb * d;
+  const double* qh = qbar + bh * nb * D;
+  const double* kh = kbar + bh * nb * D;
 
   f64x4_t acc[NT][NT];
 #pragma unroll
@@ -66,37 +69,44 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void k
 #pragma unroll
     for (int b = 0; b < NT; ++b) acc[a][b] = f64x4_t{0.0, 0.0, 0.0, 0.0};
 
-  for (int k0 = 0; k0 < d; k0 += 16) {
-    double av[NT][4], bv[NT][4];
+  double av[NB][NT][4], bv[NB][NT][4];
+  auto load = [&](int k0, double (&qa)[NT][4], double (&kb)[NT][4]) {
 #pragma unroll
     for (int a = 0; a < NT; ++a) {
       const int i = i0 + a * 16 + r16;
       double2 x = make_double2(0.0, 0.0), y = x;
       if (i < nb) {
-        const double2* src = reinterpret_cast<const double2*>(qh + (long long)i * d + k0 + 4 * kq);
+        const double2* src = reinterpret_cast<const double2*>(qh + (long long)i * D + k0 + 4 * kq);
         x = src[0];
         y = src[1];
       }
-      av[a][0] = x.x; av[a][1] = x.y; av[a][2] = y.x; av[a][3] = y.y;
+      qa[a][0] = x.x; qa[a][1] = x.y; qa[a][2] = y.x; qa[a][3] = y.y;
     }
 #pragma unroll
     for (int b = 0; b < NT; ++b) {
       const int j = j0 + b * 16 + r16;
       double2 x = make_double2(0.0, 0.0), y = x;
       if (j < nb) {
-        const double2* src = reinterpret_cast<const double2*>(kh + (long long)j * d + k0 + 4 * kq);
+        const double2* src = reinterpret_cast<const double2*>(kh + (long long)j * D + k0 + 4 * kq);
         x = src[0];
         y = src[1];
       }
-      bv[b][0] = x.x; bv[b][1] = x.y; bv[b][2] = y.x; bv[b][3] = y.y;
+      kb[b][0] = x.x; kb[b][1] = x.y; kb[b][2] = y.x; kb[b][3] = y.y;
     }
+  };
+  load(0, av[0], bv[0]);
+#pragma unroll
+  for (int c = 0; c < NC; ++c) {
+    const int cur = NB == 2 ? (c & 1) : 0;
+    if (NB == 2 && c + 1 < NC) load((c + 1) * 16, av[cur ^ 1], bv[cur ^ 1]);
 #pragma unroll
     for (int st = 0; st < 4; ++st)
 #pragma unroll
       for (int a = 0; a < NT; ++a)
 #pragma unroll
         for (int b = 0; b < NT; ++b)
-          acc[a][b] = __builtin_amdgcn_mfma_f64_16x16x4f64(av[a][st], bv[b][st], acc[a][b], 0, 0, 0);
+          acc[a][b] = __builtin_amdgcn_mfma_f64_16x16x4f64(av[cur][a][st], bv[cur][b][st], acc[a][b], 0, 0, 0);
+    if (NB == 1 && c + 1 < NC) load((c + 1) * 16, av[0], bv[0]);
   }
 #pragma unroll
   for (int a = 0; a < NT; ++a)
@@ -518,11 +528,18 @@ hipError_t launch_build_mask(const KGeom& g, const abla_mask_params& p, const do
     // 128 x 128 tiles when they fill the GPU several times over, else 64 x 64.
     const long long t128 = (g.nb + 127) / 128;
     if (t128 * t128 * g.B * g.H >= 2048) {
-      k_scores<128><<<dim3((unsigned)t128, (unsigned)t128, (unsigned)(g.B * g.H)), 256, 0, s>>>(qbar, kbar, scores,
-                                                                                             g.nb, g.d, scale);
+      const dim3 grid((unsigned)t128, (unsigned)t128, (unsigned)(g.B * g.H));
+      if (g.d == 128)
+        k_scores<128, 128><<<grid, 256, 0, s>>>(qbar, kbar, scores, g.nb, scale);
+      else
+        k_scores<128, 64><<<grid, 256, 0, s>>>(qbar, kbar, scores, g.nb, scale);
     } else {
       const unsigned t64 = (unsigned)((g.nb + 63) / 64);
-      k_scores<64><<<dim3(t64, t64, (unsigned)(g.B * g.H)), 256, 0, s>>>(qbar, kbar, scores, g.nb, g.d, scale);
+      const dim3 grid(t64, t64, (unsigned)(g.B * g.H));
+      if (g.d == 128)
+        k_scores<64, 128><<<grid, 256, 0, s>>>(qbar, kbar, scores, g.nb, scale);
+      else
+        k_scores<64, 64><<<grid, 256, 0, s>>>(qbar, kbar, scores, g.nb, scale);
     }
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
