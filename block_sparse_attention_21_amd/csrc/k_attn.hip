@@ -92,6 +92,7 @@ constexpr float kRescaleLog2 = 8.0f;
 // Attention workgroups resident on one XCD at a time: 32 CUs (MI355X: 256 CUs in 8 XCDs),
 // two 4-wave workgroups per CU.
 constexpr int kXcdSlots = 64;
+constexpr int kQueueTail = 2 * kXcdSlots;
 
 // Column order (short lists): runs of G adjacent temporal columns of one head, G*C close to
 // the workgroups one XCD holds at once.
@@ -667,10 +668,11 @@ __device__ void desc_exclusive_scan(int* h, int n, int* part) {
 //     the mean move to the front (both parts keep their queue order). Started late, the
 //     longest pairs formed a tail in which most of an XCD's slots sat idle (72% slot use at
 //     480p, 59% with the dynamic threshold).
+//  3. Short pairs last: the final 2 x 64 positions of each queue are written longest-first.
 // Workgroup x of k_pair_order writes the queue of XCD x; `total` is the sum of all kept
 // counts (each row belongs to exactly one pair), `wpart` 16 ints of LDS.
 __device__ void xcd_queue(const int32_t* __restrict__ counts, int32_t* __restrict__ order, int nb, int F, int pairs,
-                          int bhs, int x, long long total, int* wpart) {
+                          int bhs, int x, long long total, int* wpart, int* tail_gi, int* tail_cost) {
   const int t = threadIdx.x, lane = t & 63, wv = t >> 6;
   const int C = pairs / F;
   const int G = column_run_width(C);
@@ -687,14 +689,15 @@ __device__ void xcd_queue(const int32_t* __restrict__ counts, int32_t* __restric
     const int h = logical / pairs, pos = logical - h * pairs;
     return h * pairs + (pos % C) * F + pos / C;  // column pos / C, frame pair pos % C
   };
-  auto is_long = [&](int gi) {  // kept count above 1.25x the mean pair's
+  auto pair_cost = [&](int gi) {  // kept count of the pair
     const int h = gi / pairs, pair = gi - h * pairs;
     const int blk = (pair / F) * 2 * F + pair % F;
     const int32_t* c = counts + (long long)h * nb;
     int k = min(max(c[blk], 0), nb);
     if (blk + F < nb) k += min(max(c[blk + F], 0), nb);
-    return 4ll * k * grid > 5ll * total;
+    return k;
   };
+  auto is_long = [&](int gi) { return 4ll * pair_cost(gi) * grid > 5ll * total; };  // above 1.25x the mean
   auto block_scan = [&](int v, int& total_out) {  // exclusive prefix of v over the workgroup
     int incl = v;
 #pragma unroll
@@ -719,6 +722,10 @@ __device__ void xcd_queue(const int32_t* __restrict__ counts, int32_t* __restric
   for (int k = t; k < n_x; k += 1024) cnt += is_long(item(k)) ? 1 : 0;
   int nlong;
   block_scan(cnt, nlong);
+  // The last kQueueTail positions (two generations of the XCD's resident workgroups) are
+  // collected in LDS and then written longest-first, so the queue ends with its shortest
+  // pairs and the XCD's slots drain together.
+  const int tail0 = max(n_x - kQueueTail, 0);
   int base_l = 0, base_s = nlong;
   for (int c0 = 0; c0 < n_x; c0 += 1024) {
     const int k = c0 + t;
@@ -730,10 +737,23 @@ __device__ void xcd_queue(const int32_t* __restrict__ counts, int32_t* __restric
     const int ex = block_scan(v, both);
     if (valid) {
       const int p = lg ? base_l + (ex & 0xffff) : base_s + (ex >> 16);
-      order[8 * p + x] = gi;
+      if (p >= tail0) {
+        tail_gi[p - tail0] = gi;
+        tail_cost[p - tail0] = pair_cost(gi);
+      } else {
+        order[8 * p + x] = gi;
+      }
     }
     base_l += both & 0xffff;
     base_s += both >> 16;
+  }
+  __syncthreads();
+  const int nt = n_x - tail0;
+  if (t < nt) {
+    const int c = tail_cost[t];
+    int rank = 0;
+    for (int u = 0; u < nt; ++u) rank += (tail_cost[u] > c) || (tail_cost[u] == c && u < t);
+    order[8 * (tail0 + rank) + x] = tail_gi[t];
   }
 }
 
@@ -771,7 +791,7 @@ __global__ __launch_bounds__(1024) void k_pair_order(const int32_t* __restrict__
   if (bh == 0 && t == 0) mode_out[0] = column ? 1 : 0;
   const int bhs = (int)(rows / nb);
   if (column) {
-    if (bh < 8) xcd_queue(counts, order, nb, F, pairs, bhs, (int)bh, total, scan_part);
+    if (bh < 8) xcd_queue(counts, order, nb, F, pairs, bhs, (int)bh, total, scan_part, hist, hist + kQueueTail);
     return;
   }
   if (bh >= bhs) return;
