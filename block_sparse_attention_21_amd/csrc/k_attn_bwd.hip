@@ -179,13 +179,16 @@ __device__ __forceinline__ void column_order(int wg, const KGeom& g, long long& 
 // lengths are heavy-tailed (the longest above 3x the mean), each XCD's queue (the workgroups
 // w with w % 8 == x, in order) is partitioned so that the blocks whose list is longer than
 // 1.25x the mean come first, both parts in queue order. Started late, the longest lists
-// formed a tail in which a quarter of the slots sat idle (dQ at 480p: 73% slot use).
-// Workgroup x writes the queue of XCD x; `cnt` holds the list lengths (counts for dQ,
-// column counts for dK/dV); order[w] = bh * nb + block.
+// formed a tail in which a quarter of the slots sat idle (dQ at 480p: 73% slot use). In
+// either case the queue's last 128 positions (two generations of the XCD's resident
+// workgroups) are written longest-first. Workgroup x writes the queue of XCD x; `cnt` holds
+// the list lengths (counts for dQ, column counts for dK/dV); order[w] = bh * nb + block.
+constexpr int kBwdQueueTail = 128;
 __global__ __launch_bounds__(1024) void k_bwd_order(const int32_t* __restrict__ cnt, int32_t* __restrict__ order,
                                                     KGeom g, int bhs) {
   __shared__ long long wsum[16];
   __shared__ int wpart[16];
+  __shared__ int tail_gi[kBwdQueueTail], tail_cost[kBwdQueueTail];
   const int t = threadIdx.x, lane = t & 63, wv = t >> 6;
   const int x = blockIdx.x, nb = g.nb;
   const int grid = bhs * nb;
@@ -218,7 +221,7 @@ __global__ __launch_bounds__(1024) void k_bwd_order(const int32_t* __restrict__ 
     column_order(8 * k + x, g, bh, blk);
     return (int)bh * nb + blk;
   };
-  auto is_long = [&](int gi) { return 4ll * min(max(cnt[gi], 0), nb) * grid > 5ll * total; };
+  auto cost = [&](int gi) { return min(max(cnt[gi], 0), nb); };
   auto block_scan = [&](int v, int& total_out) {  // exclusive prefix of v over the workgroup
     int incl = v;
 #pragma unroll
@@ -238,31 +241,47 @@ __global__ __launch_bounds__(1024) void k_bwd_order(const int32_t* __restrict__ 
     return base + incl - v;
   };
   const int n_x = (grid - x + 7) / 8;
-  // Without a heavy tail (longest list at most 3x the mean) the plain column order is kept:
-  // at 720p moving the longer lists forward only cost L2 reuse.
-  if ((long long)mx * grid <= 3ll * total) {
-    for (int k = t; k < n_x; k += 1024) order[8 * k + x] = item(k);
-    return;
-  }
-  int c = 0;
-  for (int k = t; k < n_x; k += 1024) c += is_long(item(k)) ? 1 : 0;
-  int nlong;
-  block_scan(c, nlong);
-  int base_l = 0, base_s = nlong;
-  for (int c0 = 0; c0 < n_x; c0 += 1024) {
-    const int k = c0 + t;
-    const bool valid = k < n_x;
-    const int gi = valid ? item(k) : 0;
-    const bool lg = valid && is_long(gi);
-    int both;
-    const int v = (lg ? 1 : 0) | ((valid && !lg) ? 1 << 16 : 0);  // two counts <= 1024, packed
-    const int ex = block_scan(v, both);
-    if (valid) {
-      const int p = lg ? base_l + (ex & 0xffff) : base_s + (ex >> 16);
+  const int tail0 = max(n_x - kBwdQueueTail, 0);
+  // Position p of the queue gets item gi: the last kBwdQueueTail positions are collected in
+  // LDS and written longest-first at the end, so the queue ends with its shortest lists.
+  auto place = [&](int p, int gi) {
+    if (p >= tail0) {
+      tail_gi[p - tail0] = gi;
+      tail_cost[p - tail0] = cost(gi);
+    } else {
       order[8 * p + x] = gi;
     }
-    base_l += both & 0xffff;
-    base_s += both >> 16;
+  };
+  // Without a heavy tail (longest list at most 3x the mean) the column order is kept up to
+  // the queue's end: at 720p moving the longer lists forward only cost L2 reuse.
+  if ((long long)mx * grid <= 3ll * total) {
+    for (int k = t; k < n_x; k += 1024) place(k, item(k));
+  } else {
+    int c = 0;
+    for (int k = t; k < n_x; k += 1024) c += 4ll * cost(item(k)) * grid > 5ll * total ? 1 : 0;
+    int nlong;
+    block_scan(c, nlong);
+    int base_l = 0, base_s = nlong;
+    for (int c0 = 0; c0 < n_x; c0 += 1024) {
+      const int k = c0 + t;
+      const bool valid = k < n_x;
+      const int gi = valid ? item(k) : 0;
+      const bool lg = valid && 4ll * cost(gi) * grid > 5ll * total;
+      int both;
+      const int v = (lg ? 1 : 0) | ((valid && !lg) ? 1 << 16 : 0);  // two counts <= 1024, packed
+      const int ex = block_scan(v, both);
+      if (valid) place(lg ? base_l + (ex & 0xffff) : base_s + (ex >> 16), gi);
+      base_l += both & 0xffff;
+      base_s += both >> 16;
+    }
+  }
+  __syncthreads();
+  const int nt = n_x - tail0;
+  if (t < nt) {
+    const int c = tail_cost[t];
+    int rank = 0;
+    for (int u = 0; u < nt; ++u) rank += (tail_cost[u] > c) || (tail_cost[u] == c && u < t);
+    order[8 * (tail0 + rank) + x] = tail_gi[t];
   }
 }
 
