@@ -243,7 +243,7 @@ def report(args):
               f"{attn_tf / MFMA_BF16_PEAK_TFLOPS:.3f} | {attn_tf / gemm:.3f} | {heads} |", flush=True)
         fwd_attn_ms[w.name + (f"-tau{w.tau}" if w.mode == "dyn" else "")] = r["ms_attn"]
         del r
-    print("\nBackward (abla_sparse_attn_bwd, every pass: 7 fractal copies, D / column lists, dQ, dK+dV), "
+    print("\nBackward (abla_sparse_attn_bwd, every pass: D and L2 rows, column lists, visiting order, dQ, dK+dV), "
           "bf16 workloads:\n")
     print("| workload | keep | backward ms | algorithmic TFLOP/s (10*64^2*d per kept pair) | of 2.5 PF | "
           "issued MFMA TFLOP/s (14*64^2*d) | backward / forward attention |")
