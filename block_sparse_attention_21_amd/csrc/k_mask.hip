@@ -170,11 +170,15 @@ constexpr int kDigitBits = 8;  // one bucket per thread: cheap clears and scans 
 constexpr int kBuckets = 1 << kDigitBits;
 constexpr int kBucketsPerThread = kBuckets / kSelThreads;
 
+constexpr int kDirect = 64;  // a selected bucket with at most this many keys is resolved directly
+
 struct RadixScratch {
   unsigned long long mass[kBuckets];
   unsigned int cnt[kBuckets];
   unsigned long long part[kWaves];  // per-wave bucket-mass totals
   unsigned long long cand_cum[kSelThreads];
+  unsigned long long cand[kDirect];  // keys of a small selected bucket
+  int ncand;
   int bsel;
   unsigned long long found;
 };
@@ -183,7 +187,9 @@ struct RadixScratch {
 // is < thr_fx: the last rank the CDF cut keeps. MSB-first radix select below the row's
 // common key prefix: each pass histograms (count, exact fixed-point mass) the next
 // 8-bit digit of the keys that match the prefix fixed so far and descends into the
-// lowest bucket whose top key is still kept. Stops when that bucket holds one key.
+// lowest bucket whose top key is still kept. Stops when that bucket holds one key, or (rows
+// of at most 1024 blocks) resolves a bucket of at most kDirect keys by comparing them
+// directly: rows of near-equal probabilities otherwise took up to 7 passes.
 template <int NPT>
 __device__ unsigned long long radix_last_kept(const unsigned long long* key, int t, int nb,
                                               unsigned long long thr_fx, RadixScratch& rs) {
@@ -275,8 +281,30 @@ __device__ unsigned long long radix_last_kept(const unsigned long long* key, int
     const unsigned int n_in = rs.cnt[bs];
     pmask |= dmask << shift;
     pval |= (unsigned long long)bs << shift;
+    if (t == 0) rs.ncand = 0;
     __syncthreads();  // the next pass clears the histogram
     if (n_in == 1 || shift == 0) break;
+    if constexpr (NPT <= 4) {  // (the larger rows keep their occupancy: no extra registers)
+      if (n_in <= kDirect) {
+        // Few keys left in the bucket: the last kept key is the smallest K among them whose
+        // mass above (the bucket's `above` plus the larger keys of the bucket) is < thr_fx;
+        // the bucket's largest key always qualifies. Same answer as further passes.
+#pragma unroll
+        for (int k = 0; k < NPT; ++k)
+          if (t + kSelThreads * k < nb && (key[k] & pmask) == pval) rs.cand[atomicAdd(&rs.ncand, 1)] = key[k];
+        if (t == 0) rs.found = ~0ull;
+        __syncthreads();
+        if (t < (int)n_in) {
+          const unsigned long long kk = rs.cand[t];
+          unsigned long long m = above;
+          for (int u = 0; u < (int)n_in; ++u)
+            if (rs.cand[u] > kk) m += mass_fx(rs.cand[u]);
+          if (m < thr_fx) atomicMin(&rs.found, kk);
+        }
+        __syncthreads();
+        return rs.found;
+      }
+    }
   }
   if (shift == 0) return pval;
   // The single key in the selected bucket.
