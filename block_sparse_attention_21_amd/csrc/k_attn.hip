@@ -661,7 +661,7 @@ __device__ void desc_exclusive_scan(int* h, int n, int* part) {
 //  1. Runs: G adjacent temporal columns (patches in raster order) of one head, each
 //     column's frame pairs in time order, dealt round-robin to the 8 XCDs: on XCD x queue
 //     rank k holds column 8G*(k / (G*C)) + G*x + (k / C) % G, frame pair k % C (columns
-//     that do not fill a last round keep the plain mapping). The workgroups an XCD holds at
+//     that do not fill a last cycle over the 8 XCDs keep the plain mapping). The workgroups an XCD holds at
 //     once then come from one run: temporally adjacent pairs of neighbouring patches, whose
 //     kept key blocks largely coincide, so their tiles hit in that XCD's L2.
 //  2. Long pairs first: within each XCD's queue, the pairs whose kept count exceeds 1.25x
@@ -670,7 +670,8 @@ __device__ void desc_exclusive_scan(int* h, int n, int* part) {
 //     480p, 59% with the dynamic threshold).
 //  3. Short pairs last: the final 2 x 64 positions of each queue are written longest-first.
 // Workgroup x of k_pair_order writes the queue of XCD x; `total` is the sum of all kept
-// counts (each row belongs to exactly one pair), `wpart` 16 ints of LDS.
+// counts (each row belongs to exactly one pair); `wpart` (16 ints), `tail_gi` and `tail_cost`
+// (kQueueTail ints each) are LDS scratch.
 __device__ void xcd_queue(const int32_t* __restrict__ counts, int32_t* __restrict__ order, int nb, int F, int pairs,
                           int bhs, int x, long long total, int* wpart, int* tail_gi, int* tail_cost) {
   const int t = threadIdx.x, lane = t & 63, wv = t >> 6;

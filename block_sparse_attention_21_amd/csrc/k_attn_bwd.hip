@@ -161,12 +161,12 @@ constexpr int kBwdThreads = 256;  // four waves
 // runs on XCD w % 8). Temporally adjacent blocks keep largely the same key (or query) blocks,
 // so the tiles one workgroup fetches are still in that XCD's L2 for the next. The position
 // within a head maps to a column-major index (column * T + frame); columns that do not fill a
-// last round of 8 keep their column-major place. Heads run in order.
+// last cycle over the 8 XCDs keep their column-major place. Heads run in order.
 __device__ __forceinline__ void column_order(int wg, const KGeom& g, long long& bh, int& blk) {
   const int F = g.nbh * g.nbw, T = g.T, nb = g.nb;
   bh = wg / nb;
   const int pos = wg - (int)(bh * nb);
-  const int full = (F / 8) * 8 * T;  // positions in whole rounds of 8 columns
+  const int full = (F / 8) * 8 * T;  // positions in whole cycles of 8 columns
   int cm = pos;
   if (pos < full) {
     const int x = pos & 7, k = pos >> 3;
