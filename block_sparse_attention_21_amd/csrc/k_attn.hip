@@ -114,6 +114,22 @@ constexpr int kSchedJ = 0xfff;
 constexpr int kSchedA = 1 << 12;
 constexpr int kSchedB = 1 << 13;
 
+// Query blocks of pair p (F = nbh*nbw blocks per frame, nb = T*F): pair tp*F + s covers patch
+// s in frames 2*tp and 2*tp + 1. With T odd the last frame has no temporal partner: there
+// pair (T-1)/2 * F + s joins the horizontally adjacent patches s and s+1 for even s (s + 1 < F;
+// for s = F-1 with F odd, block a alone), and the odd s are empty items (a = -1), so those
+// blocks do not run with half of their workgroup idle.
+__device__ __forceinline__ void pair_blocks(int p, int F, int nb, int& a, int& b) {
+  a = (p / F) * 2 * F + p % F;
+  if (a + F < nb) {
+    b = a + F;
+  } else if ((p % F) & 1) {
+    a = b = -1;
+  } else {
+    b = p % F + 1 < F ? a + 1 : -1;
+  }
+}
+
 // Merge the two ascending kept lists of the pair into one ascending schedule in LDS
 // (the union of the two sets, each entry flagged with the blocks that keep it), through
 // two bitmaps and a prefix count of their OR. Returns the schedule length. Uses the
@@ -407,8 +423,9 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
     const int pos = blockIdx.x - bh * a.pairs;
     pair = ld_const(a.order, (long long)bh * a.pairs + pos);
   }
-  const int blk_a = (pair / F) * 2 * F + pair % F;
-  const int blk_b = blk_a + F < nb ? blk_a + F : -1;
+  int blk_a, blk_b;
+  pair_blocks(pair, F, nb, blk_a, blk_b);
+  if (blk_a < 0) return;  // an empty item (the odd patch of a last-frame pair)
   const int my_blk = (w < 2) ? blk_a : blk_b;
   const bool active = my_blk >= 0;
 
@@ -692,10 +709,11 @@ __device__ void xcd_queue(const int32_t* __restrict__ counts, int32_t* __restric
   };
   auto pair_cost = [&](int gi) {  // kept count of the pair
     const int h = gi / pairs, pair = gi - h * pairs;
-    const int blk = (pair / F) * 2 * F + pair % F;
+    int ba, bb;
+    pair_blocks(pair, F, nb, ba, bb);
     const int32_t* c = counts + (long long)h * nb;
-    int k = min(max(c[blk], 0), nb);
-    if (blk + F < nb) k += min(max(c[blk + F], 0), nb);
+    int k = ba >= 0 ? min(max(c[ba], 0), nb) : 0;
+    if (bb >= 0) k += min(max(c[bb], 0), nb);
     return k;
   };
   auto is_long = [&](int gi) { return 4ll * pair_cost(gi) * grid > 5ll * total; };  // above 1.25x the mean
@@ -759,7 +777,8 @@ __device__ void xcd_queue(const int32_t* __restrict__ counts, int32_t* __restric
 }
 
 // Visiting order of the query-block pairs (i, i + F) of each (b, h), F = nbh*nbw; pair p covers
-// blocks a = (p / F)*2F + p % F and a + F, so pair tp*F + s is frame pair tp of patch s.
+// blocks a = (p / F)*2F + p % F and a + F, so pair tp*F + s is frame pair tp of patch s (the
+// last frame of an odd T pairs neighbouring patches instead: pair_blocks).
 // Two orders, chosen once per launch from the mean kept count per row over all heads:
 //  - short lists (mean <= kColumnMaxCount): column order for the whole launch, the queues of
 //    the 8 XCDs written by workgroups 0-7 (xcd_queue above).
@@ -800,9 +819,10 @@ __global__ __launch_bounds__(1024) void k_pair_order(const int32_t* __restrict__
   auto blk_count = [&](int blk) { return min(max(c[blk], 0), nb); };
   const int kmax = 2 * nb;
   auto key = [&](int pr) {
-    const int blk = (pr / F) * 2 * F + pr % F;
-    int k = blk_count(blk);
-    if (blk + F < nb) k += blk_count(blk + F);
+    int ba, bb;
+    pair_blocks(pr, F, nb, ba, bb);
+    int k = ba >= 0 ? blk_count(ba) : 0;
+    if (bb >= 0) k += blk_count(bb);
     return k;
   };
   for (int v = t; v <= kmax; v += 1024) hist[v] = 0;
