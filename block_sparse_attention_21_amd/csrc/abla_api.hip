@@ -3,6 +3,8 @@
 #include <limits.h>
 #include <math.h>
 
+#include <initializer_list>
+
 #include "common.h"
 
 using namespace abla;
@@ -37,6 +39,17 @@ size_t tok_elems(const abla_geom* g) {
   return bh_of(g) * (size_t)g->T * (size_t)g->Hs * (size_t)g->Ws * (size_t)g->d;
 }
 
+size_t tokens_of(const abla_geom* g) { return (size_t)g->T * (size_t)g->Hs * (size_t)g->Ws; }
+// Bytes of the mask outputs and of the pooled vectors.
+size_t words_bytes(const abla_geom* g) {
+  const size_t nb = (size_t)nb_of(g);
+  return bh_of(g) * nb * ((nb + 31) / 32) * 4;
+}
+size_t counts_bytes(const abla_geom* g) { return bh_of(g) * (size_t)nb_of(g) * 4; }
+size_t lists_bytes(const abla_geom* g) { return bh_of(g) * (size_t)nb_of(g) * (size_t)nb_of(g) * 4; }
+size_t pooled_bytes(const abla_geom* g) { return bh_of(g) * (size_t)nb_of(g) * (size_t)g->d * sizeof(double); }
+size_t rows_bytes(const abla_geom* g) { return bh_of(g) * tokens_of(g) * 4; }
+
 bool window_ok(int32_t t, int32_t h, int32_t w) {
   if (t == 0 && h == 0 && w == 0) return true;
   for (int32_t v : {t, h, w})
@@ -50,6 +63,25 @@ bool overlaps(const void* a, size_t na, const void* b, size_t nb) {
   const char* pa = static_cast<const char*>(a);
   const char* pb = static_cast<const char*>(b);
   return pa < pb + nb && pb < pa + na;
+}
+
+// A device buffer named in an argument check: base pointer and byte length.
+struct Span {
+  const void* p;
+  size_t n;
+};
+
+// True if some written span overlaps another written span or a read span (NULL spans and
+// empty ones are skipped).
+bool conflicts(std::initializer_list<Span> writes, std::initializer_list<Span> reads) {
+  for (auto w = writes.begin(); w != writes.end(); ++w) {
+    if (!w->p || !w->n) continue;
+    for (auto v = w + 1; v != writes.end(); ++v)
+      if (v->p && v->n && overlaps(w->p, w->n, v->p, v->n)) return true;
+    for (const Span& r : reads)
+      if (r.p && r.n && overlaps(w->p, w->n, r.p, r.n)) return true;
+  }
+  return false;
 }
 
 abla_status from_hip(hipError_t e) { return e == hipSuccess ? ABLA_OK : ABLA_ERR_HIP; }
@@ -151,6 +183,12 @@ abla_status abla_build_mask(const abla_geom* g, const abla_mask_params* p, const
   if (!window_ok(p->sta_t, p->sta_h, p->sta_w)) return ABLA_ERR_INVALID;
   if (nb_of(g) > kMaxBlocks) return ABLA_ERR_UNSUPPORTED;
   if (scored && (!workspace || workspace_bytes < abla_build_mask_workspace_bytes(g))) return ABLA_ERR_WORKSPACE;
+  // Outputs (and the scratch) overlap neither each other nor the pooled vectors.
+  const size_t pb = scored ? pooled_bytes(g) : 0;
+  if (conflicts({{mask_words, words_bytes(g)}, {counts, counts_bytes(g)}, {lists, lists ? lists_bytes(g) : 0},
+                 {workspace, scored ? abla_build_mask_workspace_bytes(g) : 0}},
+                {{qbar, pb}, {kbar, pb}}))
+    return ABLA_ERR_INVALID;
   return from_hip(launch_build_mask(make_kgeom(*g), *p, qbar, kbar, mask_words, counts, lists,
                                     static_cast<double*>(workspace), (hipStream_t)stream));
 }
@@ -176,6 +214,10 @@ abla_status abla_sparse_attn_fwd(const abla_geom* g, int32_t dtype, float scale,
   if (overlaps(out, bytes, q_r, bytes) || overlaps(out, bytes, k_r, bytes) || overlaps(out, bytes, v_rt, bytes))
     return ABLA_ERR_INVALID;
   if (!workspace || workspace_bytes < abla_sparse_attn_workspace_bytes(g)) return ABLA_ERR_WORKSPACE;
+  // out, lse and the scratch overlap neither each other nor any input.
+  if (conflicts({{out, bytes}, {lse, lse ? rows_bytes(g) : 0}, {workspace, abla_sparse_attn_workspace_bytes(g)}},
+                {{q_r, bytes}, {k_r, bytes}, {v_rt, bytes}, {counts, counts_bytes(g)}, {lists, lists_bytes(g)}}))
+    return ABLA_ERR_INVALID;
   const float s = scale > 0.f ? scale : 1.0f / sqrtf((float)g->d);
   return from_hip(launch_sparse_attn(make_kgeom(*g), dtype, s, q_r, k_r, v_rt, counts, lists, out,
                                      (layout_flags & ABLA_ATTN_OUT_ORIGINAL) != 0,
@@ -211,6 +253,11 @@ abla_status abla_sparse_attn_bwd(const abla_geom* g, int32_t dtype, float scale,
       if (overlaps(outs[a], bytes, outs[b], bytes)) return ABLA_ERR_INVALID;
   }
   if (!workspace || workspace_bytes < abla_sparse_attn_bwd_workspace_bytes(g)) return ABLA_ERR_WORKSPACE;
+  // The scratch overlaps no input and no output; the outputs overlap none of the mask inputs.
+  if (conflicts({{dq, bytes}, {dk, bytes}, {dv, bytes}, {workspace, abla_sparse_attn_bwd_workspace_bytes(g)}},
+                {{q, bytes}, {k, bytes}, {v, bytes}, {o, bytes}, {dout, bytes}, {lse, rows_bytes(g)},
+                 {mask_words, words_bytes(g)}, {counts, counts_bytes(g)}, {lists, lists_bytes(g)}}))
+    return ABLA_ERR_INVALID;
   BwdWorkspace ws;
   bwd_parts(g, &ws, static_cast<char*>(workspace));
   const float s = scale > 0.f ? scale : 1.0f / sqrtf((float)g->d);

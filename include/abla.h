@@ -161,7 +161,7 @@ size_t abla_build_mask_workspace_bytes(const abla_geom* g);
  * NULL in STATIC mode).
  * Errors: INVALID for null inputs/outputs, unknown mode or cut algorithm, NaN thr/tau, negative
  * or NaN pool_scale, gamma or lambda outside [0, 1] in STATIC mode, windows that are even,
- * negative or partly zero;
+ * negative or partly zero, and outputs or the workspace overlapping each other or qbar/kbar;
  * UNSUPPORTED for nb > 4096 or the geometry limits of abla_reorder;
  * WORKSPACE if the workspace is missing or too small. */
 abla_status abla_build_mask(const abla_geom* g, const abla_mask_params* p,
@@ -201,8 +201,8 @@ size_t abla_sparse_attn_workspace_bytes(const abla_geom* g);
  * to bf16 for the value product and the output is rounded once. float32
  * inputs are computed in float32 throughout.
  * workspace: at least abla_sparse_attn_workspace_bytes(g) bytes.
- * Errors: as abla_reorder, plus INVALID for null counts/lists/out, q_r/k_r/v_rt
- * aliasing out, unknown layout_flags bits, and WORKSPACE. */
+ * Errors: as abla_reorder, plus INVALID for null counts/lists/out, out, lse or the
+ * workspace overlapping each other or any input, unknown layout_flags bits, and WORKSPACE. */
 enum { ABLA_ATTN_OUT_ORIGINAL = 1, ABLA_ATTN_QK_ORIGINAL = 2, ABLA_ATTN_V_ORIGINAL = 4 };
 
 abla_status abla_sparse_attn_fwd(const abla_geom* g, int32_t dtype, float scale,
@@ -235,7 +235,8 @@ size_t abla_sparse_attn_bwd_workspace_bytes(const abla_geom* g);
  *   rounded to bf16 for the products, D is summed in float32, the outputs are rounded once.
  *   float32 inputs are computed in float32 throughout.
  * workspace: at least abla_sparse_attn_bwd_workspace_bytes(g) bytes.
- * Errors: INVALID for null pointers, NaN/negative scale, unknown dtype, overlapping outputs;
+ * Errors: INVALID for null pointers, NaN/negative scale, unknown dtype, an output or the
+ * workspace overlapping another output or any input;
  * UNSUPPORTED for nb > 4096 and the geometry limits of abla_reorder;
  * WORKSPACE if the workspace is missing or too small. */
 abla_status abla_sparse_attn_bwd(const abla_geom* g, int32_t dtype, float scale, const void* q, const void* k,

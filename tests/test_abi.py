@@ -130,6 +130,21 @@ def test_mask_pointer_workspace_and_size_errors(A):
     assert mask_call(A, g, st, q=None, counts=None, ws=None) == 1
 
 
+def test_mask_output_overlaps(A):
+    g, p = G(A), A.MaskParams().c()
+    # distinct fake buffers 4 GiB apart; every call fails validation before any launch
+    q, k, words, counts, lists, ws = (ctypes.c_void_p(i << 32) for i in range(1, 7))
+    def call(**over):
+        a = dict(q=q, k=k, words=words, counts=counts, lists=lists, ws=ws)
+        a.update(over)
+        return A._lib.abla_build_mask(ctypes.byref(g), ctypes.byref(p), a["q"], a["k"], a["words"], a["counts"],
+                                      a["lists"], a["ws"], 1 << 40, None)
+    assert call(counts=words) == 1
+    assert call(lists=ctypes.c_void_p((2 << 32) + 8)) == 1  # lists overlaps kbar
+    assert call(ws=ctypes.c_void_p((5 << 32) - 64)) == 1  # workspace runs into lists
+    assert call(words=ctypes.c_void_p((1 << 32) + 128)) == 1  # mask words inside qbar
+
+
 def attn_call(A, g, dtype=1, scale=0.0, q=FAKE, k=ctypes.c_void_p(0x20000), v=ctypes.c_void_p(0x30000),
               counts=FAKE, lists=FAKE, out=FAKE2, ws=FAKE, ws_bytes=1 << 40, flags=1):
     return A._lib.abla_sparse_attn_fwd(ctypes.byref(g), dtype, scale, q, k, v, counts, lists, out, flags, None, ws,
@@ -151,6 +166,18 @@ def test_attention_errors(A):
     assert attn_call(A, g, flags=7, ws=None) == 3  # the known flags pass the argument checks
     assert attn_call(A, g, ws_bytes=2 * 18 * 4 - 1) == 3
     assert attn_call(A, G(A, d=32)) == 2
+    # lse and the workspace overlap neither each other nor an input or out
+    far = dict(q=ctypes.c_void_p(1 << 32), k=ctypes.c_void_p(2 << 32), v=ctypes.c_void_p(3 << 32),
+               counts=ctypes.c_void_p(4 << 32), lists=ctypes.c_void_p(5 << 32), out=ctypes.c_void_p(6 << 32),
+               ws=ctypes.c_void_p(7 << 32))
+    def fwd(lse, **over):
+        a = dict(far)
+        a.update(over)
+        return A._lib.abla_sparse_attn_fwd(ctypes.byref(g), 1, 0.0, a["q"], a["k"], a["v"], a["counts"], a["lists"],
+                                           a["out"], 1, lse, a["ws"], 1 << 40, None)
+    assert fwd(ctypes.c_void_p((6 << 32) + 16)) == 1  # lse inside out
+    assert fwd(ctypes.c_void_p(8 << 32), ws=ctypes.c_void_p((4 << 32) + 4)) == 1  # workspace on counts
+    assert fwd(ctypes.c_void_p(8 << 32), ws=ctypes.c_void_p((8 << 32) + 4)) == 1  # workspace on lse
     assert A.sparse_attn_workspace_bytes(A.Geometry(1, 2, 3, 16, 24, 128)) == 2 * 18 * 4 + 256
 
 
@@ -174,6 +201,9 @@ def test_backward_errors(A):
     assert bwd_call(A, g, dk=ctypes.c_void_p(1 << 32)) == 1  # dk aliases q
     assert bwd_call(A, g, dv=ctypes.c_void_p(10 << 32)) == 1  # dv aliases dq
     assert bwd_call(A, g, ws=None) == 3
+    assert bwd_call(A, g, ws=ctypes.c_void_p((7 << 32) + 64)) == 1  # workspace inside the mask words
+    assert bwd_call(A, g, dq=ctypes.c_void_p(6 << 32)) == 1  # dq aliases lse
+    assert bwd_call(A, g, dk=ctypes.c_void_p((9 << 32) - 64)) == 1  # dk runs into the lists
     need = A.sparse_attn_bwd_workspace_bytes(A.Geometry(1, 2, 3, 16, 24, 128))
     def al(n):
         return (n + 255) // 256 * 256
