@@ -40,8 +40,11 @@ namespace {
 // same peak rate as float64 FMA but a quarter of the operand traffic per FMA).
 // Operand layout of one 16x16x4 product: lane l holds A[l % 16][l / 16] and
 // B[l / 16][l % 16]; the result register r of lane l is D[4r + l / 16][l % 16].
-// A workgroup of four waves computes a TM x TM tile, each wave a (TM/2)^2 quarter as
-// (TM/32)^2 16x16 tiles. The reduction runs in chunks of 16 channels; within a chunk,
+// A workgroup computes a TM x TM tile: at TM = 32 one wave takes it whole as 2 x 2 16x16
+// tiles; at TM = 128 four waves each take a 64 x 64 quarter as 4 x 4 tiles. The reduction
+// runs in chunks of 16 channels, the next chunk's operands loaded after this chunk's
+// products (no second register buffer: the lower register count lets more waves hide the
+// load latency). Within a chunk,
 // product step s uses channel k0 + 4*(l / 16) + s in lane l for both operands, so every
 // output element sums its 128 (or 64) products in one fixed order, and two identical
 // Kbar rows give bit-identical scores.
@@ -50,15 +53,13 @@ typedef double f64x4_t __attribute__((ext_vector_type(4)));
 template <int TM, int D>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void k_scores(
     const double* __restrict__ qbar, const double* __restrict__ kbar, double* __restrict__ S, int nb, double scale) {
-  constexpr int NT = TM / 32;  // 16x16 tiles per wave side
-  constexpr int NC = D / 16;   // channel chunks
-  // With 64 x 64 tiles the next chunk's operands are loaded while this chunk's products run
-  // (two register buffers); 128 x 128 tiles have no registers to spare for that.
-  constexpr int NB = TM == 64 ? 2 : 1;
+  static_assert(TM == 32 || TM == 128, "one wave per 32 x 32 tile, or four per 128 x 128 tile");
+  constexpr int NT = TM == 32 ? 2 : 4;  // 16x16 tiles per wave side
+  constexpr int NC = D / 16;            // channel chunks
   const int t = threadIdx.x, lane = t & 63, w = t >> 6;
   const int r16 = lane & 15, kq = lane >> 4;
-  const int i0 = blockIdx.y * TM + (w >> 1) * (TM / 2);
-  const int j0 = blockIdx.x * TM + (w & 1) * (TM / 2);
+  const int i0 = blockIdx.y * TM + (TM == 32 ? 0 : (w >> 1) * 64);
+  const int j0 = blockIdx.x * TM + (TM == 32 ? 0 : (w & 1) * 64);
   const long long bh = blockIdx.z;
   const double* qh = qbar + bh * nb * D;
   const double* kh = kbar + bh * nb * D;
@@ -69,7 +70,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void k
 #pragma unroll
     for (int b = 0; b < NT; ++b) acc[a][b] = f64x4_t{0.0, 0.0, 0.0, 0.0};
 
-  double av[NB][NT][4], bv[NB][NT][4];
+  double av[NT][4], bv[NT][4];
   auto load = [&](int k0, double (&qa)[NT][4], double (&kb)[NT][4]) {
 #pragma unroll
     for (int a = 0; a < NT; ++a) {
@@ -94,19 +95,17 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void k
       kb[b][0] = x.x; kb[b][1] = x.y; kb[b][2] = y.x; kb[b][3] = y.y;
     }
   };
-  load(0, av[0], bv[0]);
+  load(0, av, bv);
 #pragma unroll
   for (int c = 0; c < NC; ++c) {
-    const int cur = NB == 2 ? (c & 1) : 0;
-    if (NB == 2 && c + 1 < NC) load((c + 1) * 16, av[cur ^ 1], bv[cur ^ 1]);
 #pragma unroll
     for (int st = 0; st < 4; ++st)
 #pragma unroll
       for (int a = 0; a < NT; ++a)
 #pragma unroll
         for (int b = 0; b < NT; ++b)
-          acc[a][b] = __builtin_amdgcn_mfma_f64_16x16x4f64(av[cur][a][st], bv[cur][b][st], acc[a][b], 0, 0, 0);
-    if (NB == 1 && c + 1 < NC) load((c + 1) * 16, av[0], bv[0]);
+          acc[a][b] = __builtin_amdgcn_mfma_f64_16x16x4f64(av[a][st], bv[b][st], acc[a][b], 0, 0, 0);
+    if (c + 1 < NC) load((c + 1) * 16, av, bv);
   }
 #pragma unroll
   for (int a = 0; a < NT; ++a)
@@ -553,7 +552,7 @@ hipError_t launch_build_mask(const KGeom& g, const abla_mask_params& p, const do
                              uint32_t* words, int32_t* counts, int32_t* lists, double* scores, hipStream_t s) {
   if (p.mode != ABLA_MASK_STATIC) {
     const double scale = p.pool_scale > 0.0 ? p.pool_scale : 1.0 / sqrt((double)g.d);
-    // 128 x 128 tiles when they fill the GPU several times over, else 64 x 64.
+    // 128 x 128 tiles when they fill the GPU several times over, else 32 x 32 (one wave each).
     const long long t128 = (g.nb + 127) / 128;
     if (t128 * t128 * g.B * g.H >= 2048) {
       const dim3 grid((unsigned)t128, (unsigned)t128, (unsigned)(g.B * g.H));
@@ -562,12 +561,12 @@ hipError_t launch_build_mask(const KGeom& g, const abla_mask_params& p, const do
       else
         k_scores<128, 64><<<grid, 256, 0, s>>>(qbar, kbar, scores, g.nb, scale);
     } else {
-      const unsigned t64 = (unsigned)((g.nb + 63) / 64);
-      const dim3 grid(t64, t64, (unsigned)(g.B * g.H));
+      const unsigned t32 = (unsigned)((g.nb + 31) / 32);
+      const dim3 grid(t32, t32, (unsigned)(g.B * g.H));
       if (g.d == 128)
-        k_scores<64, 128><<<grid, 256, 0, s>>>(qbar, kbar, scores, g.nb, scale);
+        k_scores<32, 128><<<grid, 64, 0, s>>>(qbar, kbar, scores, g.nb, scale);
       else
-        k_scores<64, 64><<<grid, 256, 0, s>>>(qbar, kbar, scores, g.nb, scale);
+        k_scores<32, 64><<<grid, 64, 0, s>>>(qbar, kbar, scores, g.nb, scale);
     }
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
