@@ -81,6 +81,34 @@ def timed(fn, reps, stream):
     return start.elapsed_time(end) / reps
 
 
+def per_launch(fn, reps, stream, flush=None):
+    """Milliseconds of each of reps launches of fn(), HIP events on `stream` around each one;
+    flush(), when given, runs before each launch outside its events."""
+    import torch
+    pairs = []
+    torch.cuda.synchronize()
+    for _ in range(reps):
+        if flush is not None:
+            flush()
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record(stream)
+        fn()
+        b.record(stream)
+        pairs.append((a, b))
+    torch.cuda.synchronize()
+    return sorted(a.elapsed_time(b) for a, b in pairs)
+
+
+def median(xs):
+    xs = sorted(xs)
+    n = len(xs)
+    return xs[n // 2] if n % 2 else 0.5 * (xs[n // 2 - 1] + xs[n // 2])
+
+
+# Bytes written between launches of the cold-cache timing: twice the 256 MB last-level cache.
+EVICT_BYTES = 512 << 20
+
+
 def measure(name, steps, warmup, use_graph=False):
     import torch
     import block_sparse_attention_21_amd as A
@@ -112,6 +140,13 @@ def measure(name, steps, warmup, use_graph=False):
     ms_mask = timed(run.mask, steps, stream)
     ms_attn = timed(run.attend, steps, stream)
 
+    # Then the spread of single steps, and single steps each started after writing EVICT_BYTES
+    # of scratch (so no input is left in the last-level cache).
+    warm = per_launch(step, steps, stream)
+    scratch = torch.empty(EVICT_BYTES // 4, dtype=torch.float32, device="cuda")
+    cold = per_launch(step, steps, stream, flush=lambda: scratch.fill_(1.0))
+    del scratch
+
     kept = int(run.counts.sum().item())
     total = w.B * w.H * w.nb * w.nb
     dense = A.dense_flops(geom)
@@ -124,7 +159,7 @@ def measure(name, steps, warmup, use_graph=False):
     reorder_bytes = 4 * tensor_bytes + 2 * pooled_bytes
     return dict(
         w=w, geom=geom, kept=kept, keep_fraction=kept / total, ms_step=ms_step, wall_ms_step=wall, ms_eager=ms_eager,
-        graph=graph is not None,
+        graph=graph is not None, warm=warm, cold=cold,
         ms_reorder=ms_reorder, ms_mask=ms_mask, ms_attn=ms_attn, dense_flops=dense, kept_flops=kept_fl,
         reorder_gbs=reorder_bytes / (ms_reorder * 1e-3) / 1e9, tensor_bytes=tensor_bytes,
         counts=run.counts, run=run, q=q, k=k, v=v,
@@ -219,8 +254,9 @@ def report(args):
     print(f"bf16 GEMM reference (torch.matmul {n}^3): {gemm:,.0f} TFLOP/s\n")
     fwd_attn_ms = {}
     print("| workload | mask | keep | reorder ms (TB/s) | mask ms (GB/s) | attention ms | layer ms | "
+          "single layers: median / min / cold median ms | "
           "dense-eq TFLOP/s (layer / attn) | actual TFLOP/s | of 2.5 PF | of GEMM ref | keep per head |")
-    print("|---|---|---|---|---|---|---|---|---|---|---|---|")
+    print("|---|---|---|---|---|---|---|---|---|---|---|---|---|")
     for w in cases:
         r = measure(w, args.steps, args.warmup)
         g = r["geom"]
@@ -238,6 +274,7 @@ def report(args):
         print(f"| {w.name} ({w.dtype}, {w.N} tok) | {mode} | {r['keep_fraction']:.4f} | "
               f"{r['ms_reorder']:.4f} ({r['reorder_gbs'] / 1e3:.2f}) | {r['ms_mask']:.4f} "
               f"({mask_bytes / (r['ms_mask'] * 1e-3) / 1e9:,.0f}) | {r['ms_attn']:.4f} | {r['ms_step']:.4f} | "
+              f"{median(r['warm']):.4f} / {r['warm'][0]:.4f} / {median(r['cold']):.4f} | "
               f"{r['dense_flops'] / (r['ms_step'] * 1e-3) / 1e12:,.1f} / "
               f"{r['dense_flops'] / (r['ms_attn'] * 1e-3) / 1e12:,.1f} | {attn_tf:,.1f} | "
               f"{attn_tf / MFMA_BF16_PEAK_TFLOPS:.3f} | {attn_tf / gemm:.3f} | {heads} |", flush=True)
@@ -321,6 +358,10 @@ def main():
         },
         "ms_per_layer": round(r["ms_step"], 4),
         "ms_per_layer_eager": round(r["ms_eager"], 4),
+        "single_steps": {"reps": len(r["warm"]), "ms_median": round(median(r["warm"]), 4),
+                         "ms_min": round(r["warm"][0], 4)},
+        "cold_cache": {"reps": len(r["cold"]), "evict_bytes": EVICT_BYTES, "ms_median": round(median(r["cold"]), 4),
+                       "ms_min": round(r["cold"][0], 4)},
         "ms_per_stage": {"reorder_pool_qkv": round(r["ms_reorder"], 4), "mask": round(r["ms_mask"], 4),
                          "attention": round(r["ms_attn"], 4)},
         "keep_fraction": round(r["keep_fraction"], 5),
@@ -347,6 +388,8 @@ def main():
             "ms_per_stage": {"reorder_pool_qkv": round(s["ms_reorder"], 4), "mask": round(s["ms_mask"], 4),
                              "attention": round(s["ms_attn"], 4)},
             "reorder_pool_gbs": round(s["reorder_gbs"], 1),
+            "single_steps_ms_median": round(median(s["warm"]), 4),
+            "cold_cache_ms_median": round(median(s["cold"]), 4),
         }
         del s
     if args.cpu_seconds > 0:
