@@ -526,15 +526,13 @@ __global__ __launch_bounds__(kSelThreads) void k_select(const double* __restrict
   for (int w = t; w < W; w += kSelThreads) words[row * W + w] = wbits[w];
   __syncthreads();
   if (lists) {
+    // Each kept block j goes to its rank among the kept blocks: the kept count before its
+    // word plus the kept bits below it in the word (consecutive threads, consecutive slots).
     int32_t* lrow = lists + row * nb;
-    for (int w = t; w < W; w += kSelThreads) {
-      uint32_t b = wbits[w];
-      int o = wpre[w];
-      while (b) {
-        const int bit = __ffs(b) - 1;
-        lrow[o++] = w * 32 + bit;
-        b &= b - 1;
-      }
+#pragma unroll
+    for (int k = 0; k < NPT; ++k) {
+      const int j = t + kSelThreads * k;
+      if (keep[k]) lrow[wpre[j >> 5] + __popc(wbits[j >> 5] & ((1u << (j & 31)) - 1u))] = j;
     }
   }
 }
