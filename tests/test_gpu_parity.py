@@ -240,6 +240,30 @@ def test_binding_errors_on_device(A):
         A.reorder(x[..., :64], geom)
 
 
+def test_overlapping_buffers_rejected_on_device(A):
+    # Real device buffers with an empty mask (a launch would only write zeros), aliased so that
+    # the entry points must refuse them before launching.
+    geom = A.Geometry(1, 1, 1, 8, 8, 128)
+    q, k, v = (torch.randn(1, 1, 64, 128, device=DEV).to(torch.bfloat16) for _ in range(3))
+    v_rt = torch.zeros(1, 1, 1, 128, 64, dtype=torch.bfloat16, device=DEV)
+    counts = torch.zeros(1, 1, 1, dtype=torch.int32, device=DEV)
+    lists = torch.zeros(1, 1, 1, 1, dtype=torch.int32, device=DEV)
+    words = torch.zeros(1, 1, 1, 1, dtype=torch.int32, device=DEV)
+    buf = torch.zeros(1024, dtype=torch.float32, device=DEV)
+    lse = buf[:64].view(1, 1, 64)
+    with pytest.raises(A.AblaError) as e:  # the workspace (large enough) holds lse
+        A.sparse_attn_fwd(q, k, v_rt, counts, lists, geom, qk_original_order=True, lse=lse,
+                          workspace=buf.view(torch.uint8))
+    assert e.value.code == A.ERR_INVALID
+    o = torch.zeros_like(q)
+    dq, dk, dv = (torch.empty_like(q) for _ in range(3))
+    with pytest.raises(A.AblaError) as e:  # the workspace is dq's memory
+        A.sparse_attn_bwd(q, k, v, o, o, lse, words, counts, lists, geom, dq=dq, dk=dk, dv=dv,
+                          workspace=dq.view(torch.uint8).flatten())
+    assert e.value.code == A.ERR_INVALID
+    torch.cuda.synchronize()
+
+
 # ---------------------------------------------------------------- the five workloads at full size
 def _workload(A, name, **over):
     w = WORKLOADS[name].with_(**over) if over else WORKLOADS[name]
