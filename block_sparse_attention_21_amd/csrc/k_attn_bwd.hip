@@ -393,11 +393,13 @@ __global__ __launch_bounds__(kBwdThreads) __attribute__((amdgpu_waves_per_eu(2, 
     }
     // Register r holds key kh*32 + 16*(r/8) + 8*hi + r%8 of this lane's query.
     bf16x8_t dsb[2];
+    __builtin_amdgcn_s_setprio(1);  // exponential phase at raised priority, as in dK/dV
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
       const float p = exp2_fast(fmaf(s[r], a.c2, -l2));
       dsb[r >> 3][r & 7] = (__bf16)(p * (dp[r] - dq_d));
     }
+    __builtin_amdgcn_s_setprio(0);
     // dQ^T += K^T dS^T over this wave's 32 keys; K^T comes from the K tile by transpose loads.
     uint32_t ta[2 * DT];
     const uint32_t kbase = lds_offset(ks_lds);
@@ -465,12 +467,16 @@ __device__ __forceinline__ void half_step(const uint32_t* ta, const float* l2_ld
   const float lq[8] = {la.x, la.y, la.z, la.w, lb.x, lb.y, lb.z, lb.w};
   const float dd[8] = {da.x, da.y, da.z, da.w, db.x, db.y, db.z, db.w};
   bf16x8_t pb, dsb;
+  // The exponential phase runs at raised wave priority (as in the forward): the two waves
+  // sharing a SIMD then tend to overlap one's VALU work with the other's products.
+  __builtin_amdgcn_s_setprio(1);
 #pragma unroll
   for (int e = 0; e < 8; ++e) {
     const float p = exp2_fast(fmaf(s[Q8 * 8 + e], c2, -lq[e]));
     pb[e] = (__bf16)p;
     dsb[e] = (__bf16)(p * (dp[Q8 * 8 + e] - dd[e]));
   }
+  __builtin_amdgcn_s_setprio(0);
   {
     bf16x8_t ot[DT];
     tr_chunks_at<DT, 2 * TB + Q8 * 16 * D * 2>(ta, ot);
