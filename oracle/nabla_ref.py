@@ -385,6 +385,34 @@ def masked_attention_head(Qr, Kr, Vr, block_mask, g: Geom, scale: float,
     return O, lse
 
 
+def masked_attention_blocks(Qr, Kr, Vr, block_mask, g: Geom, scale: float, blocks):
+    """The rows of the given query blocks of one head (fractal order), each attending only to
+    the tokens of the key blocks its mask row keeps. Same definition as masked_attention_head
+    (a dropped key's weight is exp(-inf) = 0, so leaving it out changes nothing); the cost is
+    the kept fraction of the dense row. Returns (O [len(blocks)*bs, d], lse [len(blocks)*bs])
+    with the rows of block blocks[n] at n*bs .. n*bs + bs - 1.
+    """
+    Qr = np.asarray(Qr, np.float64)
+    Kr = np.asarray(Kr, np.float64)
+    Vr = np.asarray(Vr, np.float64)
+    bs = g.bs
+    O = np.zeros((len(blocks) * bs, Vr.shape[-1]))
+    lse = np.full(len(blocks) * bs, -np.inf)
+    within = np.arange(bs)
+    for n, i in enumerate(blocks):
+        kept = np.nonzero(block_mask[i])[0]
+        if len(kept) == 0:
+            continue
+        keys = (kept[:, None] * bs + within[None, :]).reshape(-1)
+        sc = scale * (Qr[i * bs:(i + 1) * bs] @ Kr[keys].T)
+        mx = sc.max(axis=1)
+        e = np.exp(sc - mx[:, None])
+        z = e.sum(axis=1)
+        O[n * bs:(n + 1) * bs] = (e @ Vr[keys]) / z[:, None]
+        lse[n * bs:(n + 1) * bs] = mx + np.log(z)
+    return O, lse
+
+
 def masked_attention_backward_head(Qr, Kr, Vr, dOr, block_mask, g: Geom, scale: float,
                                    rows: Optional[np.ndarray] = None, O: Optional[np.ndarray] = None,
                                    chunk: int = 256):

@@ -7,6 +7,7 @@ softmax) and the hand-worked examples in tests/golden/. The mutation test at
 the bottom plants plausible mistakes in the oracle and checks that some pin
 fails for each one.
 """
+import dataclasses
 import itertools
 import json
 import math
@@ -495,6 +496,132 @@ def test_p17_static_special_cases():
     assert np.array_equal(a.mask[0, 1], expect)
 
 
+# ---------------------------------------------------------------- kept blocks only
+def test_gathered_attention_equals_masked_rows():
+    """masked_attention_blocks (only the kept key blocks' tokens) equals the dense masked rows of
+    masked_attention_head, on random masks with an empty row, a full row and single blocks."""
+    g = R.Geom(B=1, H=1, T=3, Hs=16, Ws=24, d=16)
+    Q, K, V = (_rand((g.N, g.d), s) for s in (21, 22, 23))
+    rng = np.random.default_rng(5)
+    m = rng.random((g.nb, g.nb)) < 0.3
+    m[0] = False
+    m[1] = True
+    m[2] = False
+    m[2, g.nb - 1] = True
+    blocks = [0, 1, 2, 7, g.nb - 1, 4]
+    O, lse = R.masked_attention_blocks(Q, K, V, m, g, 0.3, blocks)
+    rows = np.concatenate([np.arange(b * g.bs, (b + 1) * g.bs) for b in blocks])
+    O_ref, lse_ref = R.masked_attention_head(Q, K, V, m, g, 0.3, rows=rows)
+    np.testing.assert_allclose(O, O_ref, rtol=1e-12, atol=1e-12)
+    assert np.array_equal(np.isneginf(lse), np.isneginf(lse_ref))
+    fin = np.isfinite(lse_ref)
+    np.testing.assert_allclose(lse[fin], lse_ref[fin], rtol=1e-12, atol=1e-12)
+    assert not O[: g.bs].any()
+
+
+# ---------------------------------------------------------------- the parity band
+# Mask comparison rule: a block whose decision sits within 1e-5 of its threshold may differ
+# between two correct implementations (CDF: |C_excl - thr|; dynamic: |S - (max S - tau)|);
+# sliding-tile blocks are always kept and never exempt. exemption_sets computes that set.
+def _one_row(mode, thr_or_tau, p=None, s=None, sta=()):
+    """MaskResult of one row ([1, 1, 1, n]) from given probabilities (CDF) or logits (dynamic),
+    selected by the oracle's own row functions; sta lists the row's sliding-tile blocks."""
+    n = len(p if p is not None else s)
+    sta_row = np.zeros((1, n), dtype=bool)
+    sta_row[0, list(sta)] = True
+    if mode == "cdf":
+        p = np.asarray(p, np.float64)
+        sel, cex = R.cdf_select_row(p, thr_or_tau)
+        res = R.MaskResult(S=np.log(p)[None, None, None], Pm=p[None, None, None], sel=sel[None, None, None],
+                           sta=sta_row, mask=(sel | sta_row[0])[None, None, None], c_excl=cex[None, None, None])
+        return res, R.MaskParams(mode="cdf", thr=thr_or_tau, sta=(1, 1, 1))
+    s = np.asarray(s, np.float64)
+    sel = R.dyn_select_row(s, thr_or_tau)
+    e = np.exp(s - s.max())
+    res = R.MaskResult(S=s[None, None, None], Pm=(e / e.sum())[None, None, None], sel=sel[None, None, None],
+                       sta=sta_row, mask=(sel | sta_row[0])[None, None, None], c_excl=None)
+    return res, R.MaskParams(mode="dyn", tau=thr_or_tau, sta=(1, 1, 1))
+
+
+def test_band_golden_rows():
+    """Hand-worked rows (tests/golden/band_examples.json): the exempt blocks and the kept set."""
+    with open(os.path.join(GOLDEN, "band_examples.json")) as f:
+        gold = json.load(f)
+    band = gold["band"]
+    for mode, key, par in (("cdf", "p", "thr"), ("dyn", "s", "tau")):
+        for r in gold[mode]:
+            kw = {key: r[key]}
+            res, prm = _one_row(mode, r[par], sta=r["sta"], **kw)
+            ex = R.exemption_sets(res, prm, band)[0, 0, 0]
+            assert np.nonzero(ex)[0].tolist() == r["exempt"], r
+            assert np.nonzero(res.mask[0, 0, 0])[0].tolist() == sorted(set(r["kept"]) | set(r["sta"])), r
+
+
+def test_band_golden_rows_through_the_mask_builder():
+    """The same rows through build_block_mask: d = 1, pool_scale 1, every pooled query 1 and
+    pooled key j = log p_j (CDF) or s_j (dynamic), so row i's logits are the given row; one
+    frame of n patches with a 1 x 1 x 1 window makes block i the only sliding-tile block of
+    row i."""
+    with open(os.path.join(GOLDEN, "band_examples.json")) as f:
+        gold = json.load(f)
+    for mode, key, par in (("cdf", "p", "thr"), ("dyn", "s", "tau")):
+        for r in gold[mode]:
+            if r["sta"]:  # rows with their own window list repeat a row without one
+                continue
+            vals = np.asarray(r[key], np.float64)
+            n = len(vals)
+            g = R.Geom(1, 1, 1, 8, 8 * n, 1, 8)
+            kbar = (np.log(vals) if mode == "cdf" else vals).reshape(1, 1, n, 1)
+            prm = R.MaskParams(mode=mode, thr=r[par] if mode == "cdf" else 0.9, tau=r[par] if mode == "dyn" else 4.0,
+                               pool_scale=1.0, sta=(1, 1, 1))
+            res = R.build_block_mask(np.ones((1, 1, n, 1)), kbar, g, prm)
+            ex = R.exemption_sets(res, prm, gold["band"])
+            for i in range(n):
+                assert np.nonzero(ex[0, 0, i])[0].tolist() == [j for j in r["exempt"] if j != i], (r, i)
+                assert np.nonzero(res.mask[0, 0, i])[0].tolist() == sorted(set(r["kept"]) | {i}), (r, i)
+
+
+@pytest.mark.parametrize("seed", range(10))
+def test_band_bruteforce_rows(seed):
+    """Random rows with ties: C_excl summed in exact rationals straight from its definition (the
+    mass of every block with a larger probability, or an equal one and a lower index), the
+    thresholds placed inside, on and just outside the band around each block, and the exempt
+    set compared with |C_excl - thr| <= 1e-5 minus the sliding-tile blocks. The dynamic mode the
+    same way on the logits."""
+    rng = np.random.default_rng(200 + seed)
+    n = int(rng.integers(2, 13))
+    ints = rng.integers(1, 40, size=n)
+    if seed % 2 and n > 2:
+        ints[rng.integers(1, n)] = ints[0]
+    tot = int(ints.sum())
+    pf = [Fraction(int(v), tot) for v in ints]
+    p = np.array([float(f) for f in pf])
+    C = [sum((pf[k] for k in range(n) if pf[k] > pf[j] or (pf[k] == pf[j] and k < j)), Fraction(0))
+         for j in range(n)]
+    sta = [j for j in range(n) if rng.random() < 0.25]
+    band = Fraction(1e-5)
+    offsets = (0.0, 4e-6, -7e-6, 9.9e-6, -9.9e-6, 1.05e-5, -1.2e-5, 3e-5)
+    for js in range(n):
+        for off in offsets:
+            thr = float(C[js]) + off
+            if not 0.0 < thr < 1.0:
+                continue
+            res, prm = _one_row("cdf", thr, p=p, sta=sta)
+            np.testing.assert_allclose(res.c_excl[0, 0, 0], [float(c) for c in C], rtol=0, atol=1e-15)
+            want = [j for j in range(n) if abs(C[j] - Fraction(thr)) <= band and j not in sta]
+            assert np.nonzero(R.exemption_sets(res, prm)[0, 0, 0])[0].tolist() == want, (js, off)
+    s = np.round(rng.standard_normal(n) * 3, 3)
+    for js in range(n):
+        for off in offsets:
+            tau = float(s.max() - s[js]) - off  # edge = s[js] + off
+            if tau < 0:
+                continue
+            res, prm = _one_row("dyn", tau, s=s, sta=sta)
+            edge = Fraction(float(s.max())) - Fraction(tau)
+            want = [j for j in range(n) if abs(Fraction(float(s[j])) - edge) <= band and j not in sta]
+            assert np.nonzero(R.exemption_sets(res, prm)[0, 0, 0])[0].tolist() == want, (js, off)
+
+
 # ---------------------------------------------------------------- planted mistakes
 PINS = [
     test_p1_full_threshold_is_full_attention,
@@ -520,11 +647,16 @@ PINS = [
     test_p15_static_counts_hand_values,
     test_p16_static_mask_bruteforce,
     test_p17_static_special_cases,
+    test_gathered_attention_equals_masked_rows,
+    test_band_golden_rows,
+    test_band_golden_rows_through_the_mask_builder,
+    lambda: [test_band_bruteforce_rows(s) for s in (0, 1, 2)],
 ]
 
 
 _ORIG = {n: getattr(R, n) for n in ("cdf_select_row", "sta_block_mask", "masked_attention_head", "reorder",
-                                    "masked_attention_backward_head", "static_ratio_counts")}
+                                    "masked_attention_backward_head", "static_ratio_counts", "exemption_sets",
+                                    "masked_attention_blocks")}
 
 
 def _m_sort_ascending(p):
@@ -656,6 +788,32 @@ def _m_static_decay_from_one(g, gamma, lam):
     return np.concatenate([c[1:], c[-1:]])
 
 
+def _m_gathered_transposed(Qr, Kr, Vr, block_mask, g, scale, blocks):
+    return _ORIG['masked_attention_blocks'](Qr, Kr, Vr, block_mask.T, g, scale, blocks)
+
+
+def _m_band_wide(res, prm, band=1e-5):
+    return _ORIG['exemption_sets'](res, prm, 1e-3)
+
+
+def _m_band_keeps_sta(res, prm, band=1e-5):
+    return _ORIG['exemption_sets'](res, prm, band) | (_ORIG['exemption_sets'](
+        dataclasses.replace(res, sta=np.zeros_like(res.sta)), prm, band))
+
+
+def _m_band_dyn_on_probs(res, prm, band=1e-5):
+    if prm.mode != "dyn":
+        return _ORIG['exemption_sets'](res, prm, band)
+    edge = res.Pm.max(axis=-1, keepdims=True) * math.exp(-prm.tau)
+    return (np.abs(res.Pm - edge) <= band) & ~res.sta
+
+
+def _m_band_inclusive_mass(res, prm, band=1e-5):
+    if prm.mode != "cdf" or not 0 < prm.thr < 1:
+        return _ORIG['exemption_sets'](res, prm, band)
+    return (np.abs(res.c_excl + res.Pm - prm.thr) <= band) & ~res.sta
+
+
 MUTATIONS = {
     "rank ascending": ("rank_order", _m_sort_ascending),
     "ties high index first": ("rank_order", _m_tie_high_first),
@@ -681,6 +839,11 @@ MUTATIONS = {
     "static ties high index first": ("static_ratio_ranks", _m_static_tie_high),
     "static floor ignored": ("static_ratio_counts", _m_static_no_floor),
     "static decay one frame early": ("static_ratio_counts", _m_static_decay_from_one),
+    "gathered attention with the mask transposed": ("masked_attention_blocks", _m_gathered_transposed),
+    "band 1e-3 instead of 1e-5": ("exemption_sets", _m_band_wide),
+    "band exempts sliding-tile blocks": ("exemption_sets", _m_band_keeps_sta),
+    "dynamic band on probabilities": ("exemption_sets", _m_band_dyn_on_probs),
+    "band on the inclusive mass": ("exemption_sets", _m_band_inclusive_mass),
 }
 
 
