@@ -14,14 +14,15 @@
 //            GEMM written to the caller's workspace (fixed summation order).
 //  k_select  one workgroup per row (b, h, i): row max, softmax, then either
 //            the CDF cut or the logit threshold; OR the STA window; pack bits,
-//            count, list. The CDF cut ranks 64-bit keys holding the
-//            probability's exponent and top 40 mantissa bits above 13 bits of
-//            ~j (P descending, then j ascending) and finds the last kept rank:
-//            the smallest key K with (mass of keys above K) < thr. Two
-//            algorithms give the same bits: a radix select over the keys with
-//            exact mass histograms (8-bit digits below the row's common key
-//            prefix, one bucket per thread), or an
-//            LDS-resident bitonic sort followed by an exclusive prefix sum.
+//            count, list. The CDF cut ranks the blocks by (P descending, j
+//            ascending) with P's full float64 value as the sort key, and finds
+//            the last kept rank: the smallest key K that has a kept block, and
+//            how many of the blocks tied at K are kept (the lowest indices
+//            first). Two algorithms give the same bits: a radix select over the
+//            keys with exact mass histograms (8-bit digits below the row's
+//            common key prefix, one bucket per thread) followed by a tie count,
+//            or an LDS-resident bitonic sort of (key, index) pairs followed by
+//            an exclusive prefix sum.
 //
 // The decisions are taken in float64 so that two blocks whose probabilities
 // agree to float32 precision are still ranked as exactly as the definition
@@ -151,19 +152,33 @@ __device__ __forceinline__ double wave_sum(double v) {
   return v;
 }
 
-constexpr int kIdxBits = 13;  // block index field of a sort key (nb <= 4096 < 2^13)
-
-// Sort key: probability bits (sign 0, exponent, top 40 mantissa bits) above ~j.
-__device__ __forceinline__ unsigned long long make_key(double p, int j) {
-  const unsigned long long pb = (unsigned long long)__double_as_longlong(p) >> 12;
-  return (pb << kIdxBits) | (unsigned long long)((1 << kIdxBits) - 1 - j);
+// Sort key of a probability: its float64 bits. P >= 0, so the sign bit is 0 and the integer
+// order of the bits is the order of the values; equal probabilities give equal keys, and the
+// ranking breaks those ties by the lower block index separately (tie_kept, the tie ranks).
+__device__ __forceinline__ unsigned long long make_key(double p) {
+  return (unsigned long long)__double_as_longlong(p);
 }
 
-// Probability carried by a key (its truncated value) in 2^-62 fixed point; exact conversion.
+// Probability of a key in 2^-62 fixed point, floor(P * 2^62) (P <= 1: no overflow).
 __device__ __forceinline__ unsigned long long mass_fx(unsigned long long key) {
-  const double p = __longlong_as_double((long long)((key >> kIdxBits) << 12));
-  return (unsigned long long)(p * 4611686018427387904.0);
+  return (unsigned long long)(__longlong_as_double((long long)key) * 4611686018427387904.0);
 }
+
+// Of n blocks tied at a key of mass m, ranked after blocks of total mass `above` (< thr):
+// how many are kept. Tie rank r is kept iff above + r*m < thr, i.e. r < ceil((thr - above)/m).
+__device__ __forceinline__ unsigned int tie_kept(unsigned long long above, unsigned long long m, unsigned int n,
+                                                 unsigned long long thr) {
+  if (m == 0) return n;
+  const unsigned long long k = (thr - above + m - 1) / m;
+  return k < n ? (unsigned int)k : n;
+}
+
+// Result of the CDF cut of one row: every block with a key above `key` is kept, and of the
+// n_tie blocks whose key equals `key` the n_keep with the lowest indices.
+struct Cut {
+  unsigned long long key;
+  unsigned int n_keep, n_tie;
+};
 
 constexpr int kDigitBits = 8;  // one bucket per thread: cheap clears and scans per pass
 constexpr int kBuckets = 1 << kDigitBits;
@@ -180,18 +195,20 @@ struct RadixScratch {
   int ncand;
   int bsel;
   unsigned long long found;
+  unsigned int n_keep, n_tie;
 };
 
-// Smallest key K among this row's keys such that the total mass of the keys above K
-// is < thr_fx: the last rank the CDF cut keeps. MSB-first radix select below the row's
-// common key prefix: each pass histograms (count, exact fixed-point mass) the next
-// 8-bit digit of the keys that match the prefix fixed so far and descends into the
-// lowest bucket whose top key is still kept. Stops when that bucket holds one key, or (rows
-// of at most 1024 blocks) resolves a bucket of at most kDirect keys by comparing them
-// directly: rows of near-equal probabilities otherwise took up to 7 passes.
+// The CDF cut of one row: the smallest key K that has a kept block (the mass of the keys
+// above K is < thr_fx) and how many of the blocks tied at K are kept. MSB-first radix select
+// below the row's common key prefix: each pass histograms (count, exact fixed-point mass) the
+// next 8-bit digit of the keys that match the prefix fixed so far and descends into the lowest
+// bucket whose top key is still kept. Stops when that bucket holds one key or one key value
+// (a tie class: every bit fixed), or (rows of at most 1024 blocks) resolves a bucket of at most
+// kDirect keys by comparing them directly: rows of near-equal probabilities otherwise took
+// up to 7 passes. Every thread returns the same result.
 template <int NPT>
-__device__ unsigned long long radix_last_kept(const unsigned long long* key, int t, int nb,
-                                              unsigned long long thr_fx, RadixScratch& rs) {
+__device__ Cut radix_cut(const unsigned long long* key, int t, int nb, unsigned long long thr_fx,
+                         RadixScratch& rs) {
   const int lane = t & 63, wv = t >> 6;
   // All keys of the row share the bits above the highest bit in which the largest and
   // the smallest key differ (sign and high exponent bits, typically): start the digits
@@ -222,7 +239,7 @@ __device__ unsigned long long radix_last_kept(const unsigned long long* key, int
     kmin = rs.cand_cum[w] < kmin ? rs.cand_cum[w] : kmin;
   }
   __syncthreads();
-  if (kmax == kmin) return kmax;  // one key (or all equal): it is the last kept
+  if (kmax == kmin) return Cut{kmax, tie_kept(0, mass_fx(kmax), (unsigned)nb, thr_fx), (unsigned)nb};
   int shift = 64 - __clzll((long long)(kmax ^ kmin));  // bits below the common prefix
   unsigned long long pmask = shift == 64 ? 0ull : ~((1ull << shift) - 1);
   unsigned long long pval = kmax & pmask, above = 0;
@@ -282,12 +299,14 @@ __device__ unsigned long long radix_last_kept(const unsigned long long* key, int
     pval |= (unsigned long long)bs << shift;
     if (t == 0) rs.ncand = 0;
     __syncthreads();  // the next pass clears the histogram
-    if (n_in == 1 || shift == 0) break;
+    // Every bit fixed: the bucket is one key value held by n_in tied blocks.
+    if (shift == 0) return Cut{pval, tie_kept(above, mass_fx(pval), n_in, thr_fx), n_in};
+    if (n_in == 1) break;
     if constexpr (NPT <= 4) {  // (the larger rows keep their occupancy: no extra registers)
       if (n_in <= kDirect) {
-        // Few keys left in the bucket: the last kept key is the smallest K among them whose
-        // mass above (the bucket's `above` plus the larger keys of the bucket) is < thr_fx;
-        // the bucket's largest key always qualifies. Same answer as further passes.
+        // Few keys left in the bucket: K is the smallest among them whose mass above (the
+        // bucket's `above` plus the larger keys of the bucket) is < thr_fx; the bucket's
+        // largest key always qualifies. Then the blocks tied at K. Same answer as further passes.
 #pragma unroll
         for (int k = 0; k < NPT; ++k)
           if (t + kSelThreads * k < nb && (key[k] & pmask) == pval) rs.cand[atomicAdd(&rs.ncand, 1)] = key[k];
@@ -301,37 +320,79 @@ __device__ unsigned long long radix_last_kept(const unsigned long long* key, int
           if (m < thr_fx) atomicMin(&rs.found, kk);
         }
         __syncthreads();
-        return rs.found;
+        if (t == 0) {
+          const unsigned long long kk = rs.found;
+          unsigned long long m = above;
+          unsigned int n = 0;
+          for (int u = 0; u < (int)n_in; ++u) {
+            if (rs.cand[u] > kk) m += mass_fx(rs.cand[u]);
+            n += rs.cand[u] == kk;
+          }
+          rs.n_tie = n;
+          rs.n_keep = tie_kept(m, mass_fx(kk), n, thr_fx);
+        }
+        __syncthreads();
+        return Cut{rs.found, rs.n_keep, rs.n_tie};
       }
     }
   }
-  if (shift == 0) return pval;
   // The single key in the selected bucket.
 #pragma unroll
   for (int k = 0; k < NPT; ++k)
     if (t + kSelThreads * k < nb && (key[k] & pmask) == pval) rs.found = key[k];
   __syncthreads();
-  return rs.found;
+  return Cut{rs.found, 1u, 1u};
 }
 
-template <int NPT>
+// Exclusive prefix of the popcounts of W bit words (W <= 128) in pre[]: wave 0, two words per
+// lane. Returns the total (in wave 0). No barrier.
+__device__ __forceinline__ int words_prefix(const uint32_t* bits, int* pre, int W, int t) {
+  const int lane = t & 63;
+  int total = 0;
+  if (t < 64) {
+    const int w0 = 2 * lane;
+    const int c0 = w0 < W ? __popc(bits[w0]) : 0;
+    const int c1 = w0 + 1 < W ? __popc(bits[w0 + 1]) : 0;
+    int incl = c0 + c1;
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+      const int v = __shfl_up(incl, o);
+      if (lane >= o) incl += v;
+    }
+    const int excl = incl - c0 - c1;
+    if (w0 < W) pre[w0] = excl;
+    if (w0 + 1 < W) pre[w0 + 1] = excl + c0;
+    total = __shfl(incl, 63);
+  }
+  return total;
+}
+
+// Rank of block j among the set blocks, in index order, from the words and their prefix.
+__device__ __forceinline__ int bit_rank(const uint32_t* bits, const int* pre, int j) {
+  return pre[j >> 5] + __popc(bits[j >> 5] & ((1u << (j & 31)) - 1u));
+}
+
+template <int NPT, bool BITONIC>
 __global__ __launch_bounds__(kSelThreads) void k_select(const double* __restrict__ S, uint32_t* __restrict__ words,
                                                         int32_t* __restrict__ counts, int32_t* __restrict__ lists,
                                                         KGeom g, SelArgs a) {
   constexpr int CAP = kSelThreads * NPT;
   constexpr int KEYS_WORDS = (sizeof(RadixScratch) + 7) / 8 > CAP ? (sizeof(RadixScratch) + 7) / 8 : CAP;
   __shared__ unsigned long long keys[KEYS_WORDS];  // bitonic keys, or the radix-select scratch
+  __shared__ uint16_t idx[BITONIC ? CAP : 1];      // bitonic: the block index of each key
   __shared__ uint32_t wbits[CAP / 32];
   __shared__ int wpre[CAP / 32];
   __shared__ double redf[kWaves];
   __shared__ unsigned long long redu[kWaves];
-  __shared__ unsigned long long kmin_s;
+  __shared__ unsigned long long kstar_s;
+  __shared__ int jstar_s;
 
   const int t = threadIdx.x, lane = t & 63, wv = t >> 6;
   const long long row = blockIdx.x;
   const int nb = g.nb;
   const int i = (int)(row % nb);
   const double* Srow = S + row * nb;
+  const int W = a.W;
 
   const bool scored = a.mode != ABLA_MASK_STATIC;
   double s[NPT];
@@ -415,22 +476,52 @@ __global__ __launch_bounds__(kSelThreads) void k_select(const double* __restrict
 #pragma unroll
     for (int k = 0; k < NPT; ++k) {
       const int j = t + kSelThreads * k;
-      key[k] = j < nb ? make_key(e[k] / z, j) : 0ull;
+      key[k] = j < nb ? make_key(e[k] / z) : 0ull;
     }
-    if (a.cut == ABLA_CUT_RADIX) {
-      const unsigned long long km = radix_last_kept<NPT>(key, t, nb, a.thr_fx, *reinterpret_cast<RadixScratch*>(keys));
-      if (t == 0) kmin_s = km;
-      __syncthreads();
+    if constexpr (!BITONIC) {
+      const Cut c = radix_cut<NPT>(key, t, nb, a.thr_fx, *reinterpret_cast<RadixScratch*>(keys));
+      if (c.n_keep >= c.n_tie) {
+#pragma unroll
+        for (int k = 0; k < NPT; ++k) keep[k] = (t + kSelThreads * k < nb) && key[k] >= c.key;
+      } else {
+        // Only some of the blocks tied at the cut's key are kept: the lowest indices. Rank the
+        // tied blocks by index with a ballot per 64 consecutive blocks and a prefix of the
+        // words' popcounts (the same layout as the packed mask below).
+#pragma unroll
+        for (int k = 0; k < NPT; ++k) {
+          const unsigned long long b = __ballot((t + kSelThreads * k < nb) && key[k] == c.key);
+          if (lane == 0) {
+            const int w0 = (kSelThreads * k + 64 * wv) >> 5;
+            wbits[w0] = (uint32_t)b;
+            wbits[w0 + 1] = (uint32_t)(b >> 32);
+          }
+        }
+        __syncthreads();
+        words_prefix(wbits, wpre, W, t);
+        __syncthreads();
+#pragma unroll
+        for (int k = 0; k < NPT; ++k) {
+          const int j = t + kSelThreads * k;
+          keep[k] = j < nb && (key[k] > c.key || (key[k] == c.key && bit_rank(wbits, wpre, j) < (int)c.n_keep));
+        }
+        __syncthreads();  // the packing below reuses the words
+      }
     } else {
+      // Bitonic sort of (key, index) pairs in ranking order: key descending, index ascending.
+      // Padding entries (key 0, index 0xffff) rank after every block.
 #pragma unroll
       for (int k = 0; k < NPT; ++k) {
         const int j = t + kSelThreads * k;
-        if (j < a.np) keys[j] = key[k];
+        if (j < a.np) {
+          keys[j] = key[k];
+          idx[j] = (uint16_t)(j < nb ? j : 0xffff);
+        }
       }
-      if (t == 0) kmin_s = ~0ull;
+      if (t == 0) {
+        kstar_s = ~0ull;
+        jstar_s = -1;
+      }
       __syncthreads();
-
-      // Bitonic sort, descending.
       const int np = a.np;
       for (int size = 2; size <= np; size <<= 1) {
         for (int stride = size >> 1; stride > 0; stride >>= 1) {
@@ -438,10 +529,14 @@ __global__ __launch_bounds__(kSelThreads) void k_select(const double* __restrict
             const int lo = ((pidx & ~(stride - 1)) << 1) | (pidx & (stride - 1));
             const int hi = lo + stride;
             const unsigned long long x = keys[lo], y = keys[hi];
-            const bool desc = (lo & size) == 0;
-            if (desc ? (x < y) : (x > y)) {
+            const int xi = idx[lo], yi = idx[hi];
+            const bool y_first = y > x || (y == x && yi < xi);  // y ranks before x
+            const bool ranked = (lo & size) == 0;               // this run in ranking order
+            if (ranked ? y_first : !y_first) {
               keys[lo] = y;
               keys[hi] = x;
+              idx[lo] = (uint16_t)yi;
+              idx[hi] = (uint16_t)xi;
             }
           }
           __syncthreads();
@@ -465,7 +560,7 @@ __global__ __launch_bounds__(kSelThreads) void k_select(const double* __restrict
       __syncthreads();
       unsigned long long before = incl - local;
       for (int w = 0; w < wv; ++w) before += redu[w];
-      // Walk the segment: rank r is kept iff the mass before it is < thr.
+      // Walk the segment: rank r is kept iff the mass before it is < thr; record the last kept.
       unsigned long long c = before;
       for (int q = 0; q < seg; ++q) {
         const int pos = p0 + q;
@@ -473,14 +568,21 @@ __global__ __launch_bounds__(kSelThreads) void k_select(const double* __restrict
         const bool kp = c < a.thr_fx;
         const unsigned long long mq = mass_fx(keys[pos]);
         const bool next_kept = (pos + 1 < nb) && (c + mq < a.thr_fx);
-        if (kp && !next_kept) kmin_s = keys[pos];
+        if (kp && !next_kept) {
+          kstar_s = keys[pos];
+          jstar_s = idx[pos];
+        }
         c += mq;
       }
       __syncthreads();
-    }
-    const unsigned long long kmin = kmin_s;
+      const unsigned long long kstar = kstar_s;
+      const int jstar = jstar_s;
 #pragma unroll
-    for (int k = 0; k < NPT; ++k) keep[k] = (t + kSelThreads * k < nb) && key[k] >= kmin;
+      for (int k = 0; k < NPT; ++k) {
+        const int j = t + kSelThreads * k;
+        keep[k] = j < nb && (key[k] > kstar || (key[k] == kstar && j <= jstar));
+      }
+    }
   }
 
   // Sliding-tile window around block i.
@@ -506,23 +608,8 @@ __global__ __launch_bounds__(kSelThreads) void k_select(const double* __restrict
     }
   }
   __syncthreads();
-  const int W = a.W;
-  // Exclusive prefix of the words' popcounts (W <= 128): wave 0, two words per lane.
-  if (wv == 0) {
-    const int w0 = 2 * lane;
-    const int c0 = w0 < W ? __popc(wbits[w0]) : 0;
-    const int c1 = w0 + 1 < W ? __popc(wbits[w0 + 1]) : 0;
-    int incl = c0 + c1;
-#pragma unroll
-    for (int o = 1; o < 64; o <<= 1) {
-      const int v = __shfl_up(incl, o);
-      if (lane >= o) incl += v;
-    }
-    const int excl = incl - c0 - c1;
-    if (w0 < W) wpre[w0] = excl;
-    if (w0 + 1 < W) wpre[w0 + 1] = excl + c0;
-    if (lane == 63) counts[row] = incl;
-  }
+  const int total = words_prefix(wbits, wpre, W, t);
+  if (t == 0) counts[row] = total;
   for (int w = t; w < W; w += kSelThreads) words[row * W + w] = wbits[w];
   __syncthreads();
   if (lists) {
@@ -532,7 +619,7 @@ __global__ __launch_bounds__(kSelThreads) void k_select(const double* __restrict
 #pragma unroll
     for (int k = 0; k < NPT; ++k) {
       const int j = t + kSelThreads * k;
-      if (keep[k]) lrow[wpre[j >> 5] + __popc(wbits[j >> 5] & ((1u << (j & 31)) - 1u))] = j;
+      if (keep[k]) lrow[bit_rank(wbits, wpre, j)] = j;
     }
   }
 }
@@ -540,8 +627,11 @@ __global__ __launch_bounds__(kSelThreads) void k_select(const double* __restrict
 template <int NPT>
 void launch_select(const KGeom& g, const double* S, uint32_t* words, int32_t* counts, int32_t* lists,
                    const SelArgs& a, hipStream_t s) {
-  k_select<NPT><<<dim3((unsigned)((long long)g.B * g.H * g.nb)), kSelThreads, 0, s>>>(S, words, counts, lists, g,
-                                                                                   a);
+  const dim3 grid((unsigned)((long long)g.B * g.H * g.nb));
+  if (a.mode == ABLA_MASK_CDF && a.cut == ABLA_CUT_BITONIC)
+    k_select<NPT, true><<<grid, kSelThreads, 0, s>>>(S, words, counts, lists, g, a);
+  else
+    k_select<NPT, false><<<grid, kSelThreads, 0, s>>>(S, words, counts, lists, g, a);
 }
 
 }  // namespace
