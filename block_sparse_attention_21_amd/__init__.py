@@ -348,6 +348,9 @@ class NablaAttention:
     are first copied to fractal order (reorder + pool in one pass) and the attention
     reads the copies; the results are identical. Intermediate results stay available as
     attributes (q_r, k_r when not fused, v_rt, qbar, kbar, words, counts, lists, lse).
+
+    __call__ returns self.out, the same tensor on every call: the next call overwrites it. Keep
+    a result across calls with .clone(), or pass out= to have the attention write elsewhere.
     """
 
     def __init__(self, geom: Geometry, params: MaskParams, dtype=torch.bfloat16, device="cuda",
@@ -367,6 +370,7 @@ class NablaAttention:
         self.counts = torch.empty((g.B, g.H, g.nb), dtype=torch.int32, device=dev)
         self.lists = torch.empty((g.B, g.H, g.nb, g.nb), dtype=torch.int32, device=dev)
         self.out = torch.empty(tok, dtype=dtype, device=dev)
+        self._o = self.out
         self.lse = torch.empty((g.B, g.H, g.N), dtype=torch.float32, device=dev) if want_lse else None
         self.ws_mask = (None if params.mode == "static" else
                         torch.empty(max(build_mask_workspace_bytes(g), 1), dtype=torch.uint8, device=dev))
@@ -392,28 +396,32 @@ class NablaAttention:
         build_mask(self.qbar, self.kbar, self.geom, self.params, words=self.words, counts=self.counts,
                    lists=self.lists, workspace=self.ws_mask)
 
-    def attend(self):
+    def attend(self, out: Optional[torch.Tensor] = None):
+        out = self.out if out is None else out
+        self._o = out  # what the last forward wrote: the backward reads it
         if self.fused:
             v = self._v if self.fuse_v else self.v_rt
             sparse_attn_fwd(self._q, self._k, v, self.counts, self.lists, self.geom, scale=self.scale,
-                            qk_original_order=True, v_original_order=self.fuse_v, out=self.out, lse=self.lse,
+                            qk_original_order=True, v_original_order=self.fuse_v, out=out, lse=self.lse,
                             workspace=self.ws_attn)
         else:
             sparse_attn_fwd(self.q_r, self.k_r, self.v_rt, self.counts, self.lists, self.geom, scale=self.scale,
-                            out=self.out, lse=self.lse, workspace=self.ws_attn)
+                            out=out, lse=self.lse, workspace=self.ws_attn)
+        return out
 
-    def __call__(self, q, k, v):
+    def __call__(self, q, k, v, out: Optional[torch.Tensor] = None):
+        """The whole path; returns `out` if given ([B,H,N,d], the inputs' dtype), else self.out
+        (reused by the next call)."""
         self.reorder_pool(q, k, v)
         self.mask()
-        self.attend()
-        return self.out
+        return self.attend(out)
 
     def backward(self, q, k, v, dout, workspace=None):
         """Gradients (dq, dk, dv) of the last __call__(q, k, v) for the incoming gradient dout
         (all [B,H,N,d], original order). Needs want_lse=True (the forward's log-sum-exp)."""
         if self.lse is None:
             raise ValueError("backward needs the forward's log-sum-exp: construct with want_lse=True")
-        return sparse_attn_bwd(q, k, v, self.out, dout, self.lse, self.words, self.counts, self.lists, self.geom,
+        return sparse_attn_bwd(q, k, v, self._o, dout, self.lse, self.words, self.counts, self.lists, self.geom,
                                scale=self.scale, workspace=workspace)
 
     def capture(self, q, k, v):

@@ -84,6 +84,14 @@ bool conflicts(std::initializer_list<Span> writes, std::initializer_list<Span> r
   return false;
 }
 
+// Every device pointer must be 16-byte aligned: the kernels move 16-byte vectors and issue
+// 16-byte buffer loads from these bases. NULL passes (optional arguments are checked apart).
+bool aligned16(std::initializer_list<const void*> ps) {
+  for (const void* p : ps)
+    if (reinterpret_cast<uintptr_t>(p) & 15u) return false;
+  return true;
+}
+
 abla_status from_hip(hipError_t e) { return e == hipSuccess ? ABLA_OK : ABLA_ERR_HIP; }
 
 size_t align256(size_t n) { return (n + 255) & ~(size_t)255; }
@@ -132,6 +140,7 @@ abla_status abla_reorder(const abla_geom* g, int32_t dtype, int32_t inverse, int
   if (inverse && (layout != ABLA_LAYOUT_TOKENS || pooled)) return ABLA_ERR_INVALID;
   // y may be NULL only to pool without reordering (forward, token layout, pooled given).
   if (!y && (inverse || layout != ABLA_LAYOUT_TOKENS || !pooled)) return ABLA_ERR_INVALID;
+  if (!aligned16({x, y, pooled})) return ABLA_ERR_INVALID;
   const size_t bytes = tok_elems(g) * elem_bytes(dtype);
   if (y && overlaps(x, bytes, y, bytes)) return ABLA_ERR_INVALID;
   if (pooled) {
@@ -146,6 +155,7 @@ abla_status abla_pool_qk_reorder_v(const abla_geom* g, int32_t dtype, const void
   abla_status st = check_geom(g);
   if (st != ABLA_OK) return st;
   if (!valid_dtype(dtype) || !q || !k || !v || !qbar || !kbar || !v_rt) return ABLA_ERR_INVALID;
+  if (!aligned16({q, k, v, qbar, kbar, v_rt})) return ABLA_ERR_INVALID;
   if ((long double)3 * bh_of(g) * nb_of(g) > (long double)INT_MAX) return ABLA_ERR_UNSUPPORTED;  // grid size
   const size_t bytes = tok_elems(g) * elem_bytes(dtype);
   const size_t pbytes = bh_of(g) * (size_t)nb_of(g) * (size_t)g->d * sizeof(double);
@@ -175,6 +185,7 @@ abla_status abla_build_mask(const abla_geom* g, const abla_mask_params* p, const
   if (p->mode != ABLA_MASK_CDF && p->mode != ABLA_MASK_DYN && p->mode != ABLA_MASK_STATIC) return ABLA_ERR_INVALID;
   const bool scored = p->mode != ABLA_MASK_STATIC;
   if (scored && (!qbar || !kbar)) return ABLA_ERR_INVALID;
+  if (!aligned16({qbar, kbar, mask_words, counts, lists, workspace})) return ABLA_ERR_INVALID;
   if (!scored && !(p->gamma >= 0.0 && p->gamma <= 1.0 && p->lambda >= 0.0 && p->lambda <= 1.0))
     return ABLA_ERR_INVALID;  // also rejects NaN
   if (p->cut != ABLA_CUT_RADIX && p->cut != ABLA_CUT_BITONIC) return ABLA_ERR_INVALID;
@@ -206,6 +217,7 @@ abla_status abla_sparse_attn_fwd(const abla_geom* g, int32_t dtype, float scale,
   abla_status st = check_geom(g);
   if (st != ABLA_OK) return st;
   if (!valid_dtype(dtype) || !q_r || !k_r || !v_rt || !counts || !lists || !out) return ABLA_ERR_INVALID;
+  if (!aligned16({q_r, k_r, v_rt, counts, lists, out, lse, workspace})) return ABLA_ERR_INVALID;
   if (layout_flags & ~(ABLA_ATTN_OUT_ORIGINAL | ABLA_ATTN_QK_ORIGINAL | ABLA_ATTN_V_ORIGINAL))
     return ABLA_ERR_INVALID;
   if (isnan(scale) || scale < 0.f || isinf(scale)) return ABLA_ERR_INVALID;
@@ -241,6 +253,7 @@ abla_status abla_sparse_attn_bwd(const abla_geom* g, int32_t dtype, float scale,
   if (!valid_dtype(dtype)) return ABLA_ERR_INVALID;
   if (!q || !k || !v || !o || !dout || !lse || !mask_words || !counts || !lists || !dq || !dk || !dv)
     return ABLA_ERR_INVALID;
+  if (!aligned16({q, k, v, o, dout, lse, mask_words, counts, lists, dq, dk, dv, workspace})) return ABLA_ERR_INVALID;
   if (isnan(scale) || scale < 0.f || isinf(scale)) return ABLA_ERR_INVALID;
   if (nb_of(g) > kMaxBlocks) return ABLA_ERR_UNSUPPORTED;
   const size_t bytes = tok_elems(g) * elem_bytes(dtype);

@@ -26,7 +26,8 @@
  *   where i is its block: each patch is one contiguous run, frames stay
  *   outermost ("Fractal Flattening", NABLA Method section).
  * - All pointers are device pointers owned by the caller, contiguous,
- *   row-major and 16-byte aligned. The library never allocates, frees or
+ *   row-major and 16-byte aligned (a misaligned pointer is rejected with
+ *   ABLA_ERR_INVALID). The library never allocates, frees or
  *   synchronises, keeps no pointer after a call returns and has no mutable
  *   global state. Work is enqueued on `stream` (a hipStream_t; NULL is the
  *   default stream) and results are valid when the stream reaches them.
@@ -47,7 +48,7 @@ extern "C" {
 
 typedef enum {
   ABLA_OK = 0,
-  ABLA_ERR_INVALID = 1,     /* null pointer, bad size, NaN threshold, even window, aliasing */
+  ABLA_ERR_INVALID = 1,     /* null or misaligned pointer, bad size, NaN threshold, even window, aliasing */
   ABLA_ERR_UNSUPPORTED = 2, /* valid but not implemented: P*P != 64, d not in {64,128}, nb > 4096 */
   ABLA_ERR_WORKSPACE = 3,   /* workspace pointer null or smaller than the *_workspace_bytes value */
   ABLA_ERR_HIP = 4          /* a kernel launch failed */

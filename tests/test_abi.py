@@ -219,3 +219,43 @@ def test_binding_rejects_cpu_tensors(A):
     geom = A.Geometry(1, 1, 1, 8, 8, 64)
     with pytest.raises(ValueError):
         A.reorder(torch.zeros(1, 1, 64, 64), geom)
+
+
+# ---------------------------------------------------------------- 16-byte alignment
+def _p(i, shift=0):
+    return ctypes.c_void_p((i << 34) + shift)  # far apart: no two buffers overlap
+
+
+def _entry_calls(A):
+    """For every computing entry point: (number of pointer arguments, call(pointers)) such that
+    distinct, aligned, non-overlapping fake buffers pass validation."""
+    g = G(A)
+    geom = A.Geometry(1, 2, 3, 16, 24, 128)
+    p = A.MaskParams(mode="cdf", thr=0.5).c()
+    L = A._lib
+    ws_mask = A.build_mask_workspace_bytes(geom)
+    ws_attn = A.sparse_attn_workspace_bytes(geom)
+    ws_bwd = A.sparse_attn_bwd_workspace_bytes(geom)
+    return {
+        "abla_reorder": (3, lambda P: L.abla_reorder(ctypes.byref(g), 1, 0, 0, *P, None)),
+        "abla_pool_qk_reorder_v": (6, lambda P: L.abla_pool_qk_reorder_v(ctypes.byref(g), 1, *P, None)),
+        "abla_build_mask": (6, lambda P: L.abla_build_mask(ctypes.byref(g), ctypes.byref(p), *P, ws_mask, None)),
+        "abla_sparse_attn_fwd": (8, lambda P: L.abla_sparse_attn_fwd(ctypes.byref(g), 1, 0.0, *P[:6], 3, *P[6:],
+                                                                      ws_attn, None)),
+        "abla_sparse_attn_bwd": (13, lambda P: L.abla_sparse_attn_bwd(ctypes.byref(g), 1, 0.0, *P, ws_bwd, None)),
+    }
+
+
+def test_misaligned_pointers_rejected(A):
+    """Each device pointer of each computing entry point must be 16-byte aligned: shifting any one
+    of them by 8 bytes (or 4) turns a call that passes validation into ABLA_ERR_INVALID. Host
+    only: the unshifted calls fail at the launch (ABLA_ERR_HIP) because no device is visible,
+    which shows that they passed every argument check."""
+    import torch
+    if torch.cuda.is_available():
+        pytest.skip("host-only check: the unshifted calls would launch on a visible device")
+    for name, (n, call) in _entry_calls(A).items():
+        assert call([_p(i + 1) for i in range(n)]) == 4, name
+        for slot in range(n):
+            for shift in (8, 4):
+                assert call([_p(i + 1, shift if i == slot else 0) for i in range(n)]) == 1, (name, slot, shift)
