@@ -57,6 +57,7 @@ def _load():
         "abla_build_mask": (i32, [G, ctypes.POINTER(_MaskParams), vp, vp, vp, vp, vp, vp, sz, vp]),
         "abla_sparse_attn_workspace_bytes": (sz, [G]),
         "abla_sparse_attn_fwd": (i32, [G, i32, f32, vp, vp, vp, vp, vp, vp, i32, vp, vp, sz, vp]),
+        "abla_sparse_attn_fwd_noalloc": (i32, [G, i32, f32, vp, vp, vp, vp, vp, vp, i32, vp, vp]),
         "abla_sparse_attn_bwd_workspace_bytes": (sz, [G]),
         "abla_sparse_attn_bwd": (i32, [G, i32, f32] + [vp] * 13 + [sz, vp]),
         "abla_status_str": (ctypes.c_char_p, [i32]),
@@ -69,9 +70,9 @@ def _load():
 
 
 _lib = _load()
-EXPORTED = ("abla_reorder", "abla_pool_qk_reorder_v", "abla_build_mask_workspace_bytes", "abla_build_mask", "abla_sparse_attn_workspace_bytes",
-            "abla_sparse_attn_fwd", "abla_sparse_attn_bwd_workspace_bytes", "abla_sparse_attn_bwd", "abla_status_str",
-            "abla_version")
+EXPORTED = ("abla_reorder", "abla_pool_qk_reorder_v", "abla_build_mask_workspace_bytes", "abla_build_mask",
+            "abla_sparse_attn_workspace_bytes", "abla_sparse_attn_fwd", "abla_sparse_attn_fwd_noalloc",
+            "abla_sparse_attn_bwd_workspace_bytes", "abla_sparse_attn_bwd", "abla_status_str", "abla_version")
 
 
 def status_str(code: int) -> str:
@@ -300,6 +301,34 @@ def sparse_attn_fwd(q_r: torch.Tensor, k_r: torch.Tensor, v_rt: torch.Tensor, co
                                      _ptr(counts), _ptr(lists), _ptr(out), flags, _ptr(lse),
                                      _ptr(workspace), workspace.numel(), _stream(q_r)), "abla_sparse_attn_fwd")
     return (out, lse) if lse is not None else out
+
+
+def sparse_attn_fwd_noalloc(q_r: torch.Tensor, k_r: torch.Tensor, v_rt: torch.Tensor, counts: torch.Tensor,
+                            lists: torch.Tensor, geom: Geometry, out: torch.Tensor, *, scale: float = 0.0,
+                            out_original_order: bool = True, qk_original_order: bool = False,
+                            v_original_order: bool = False, lse: Optional[torch.Tensor] = None):
+    """abla_sparse_attn_fwd_noalloc: sparse_attn_fwd with the library's own scratch, for callers
+    that cannot allocate; `out` (and `lse` if wanted) must be given. Returns out."""
+    dev = _device(q_r)
+    dt = q_r.dtype
+    if dt not in _DT:
+        raise ValueError(f"unsupported dtype {dt}")
+    tok = (geom.B, geom.H, geom.N, geom.d)
+    _need(q_r, "q_r", tok, dt, dev)
+    _need(k_r, "k_r", tok, dt, dev)
+    _need(v_rt, "v_rt", tok if v_original_order else (geom.B, geom.H, geom.nb, geom.d, 64), dt, dev)
+    _need(counts, "counts", (geom.B, geom.H, geom.nb), torch.int32, dev)
+    _need(lists, "lists", (geom.B, geom.H, geom.nb, geom.nb), torch.int32, dev)
+    _need(out, "out", tok, dt, dev)
+    if lse is not None:
+        _need(lse, "lse", (geom.B, geom.H, geom.N), torch.float32, dev)
+    g = geom.c()
+    flags = ((ATTN_OUT_ORIGINAL if out_original_order else 0) | (ATTN_QK_ORIGINAL if qk_original_order else 0)
+             | (ATTN_V_ORIGINAL if v_original_order else 0))
+    _check(_lib.abla_sparse_attn_fwd_noalloc(ctypes.byref(g), _DT[dt], float(scale), _ptr(q_r), _ptr(k_r),
+                                             _ptr(v_rt), _ptr(counts), _ptr(lists), _ptr(out), flags, _ptr(lse),
+                                             _stream(q_r)), "abla_sparse_attn_fwd_noalloc")
+    return out
 
 
 def sparse_attn_bwd_workspace_bytes(geom: Geometry) -> int:

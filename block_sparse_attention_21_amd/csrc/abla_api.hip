@@ -113,6 +113,37 @@ size_t bwd_parts(const abla_geom* g, BwdWorkspace* ws, char* base) {
   return 2 * rows + 2 * cc + cl;
 }
 
+// Argument checks of the attention forward, all but the scratch: pointers, flags, scale,
+// limits, 16-byte alignment, and out / lse overlapping each other or any input.
+abla_status check_fwd(const abla_geom* g, int32_t dtype, float scale, const void* q_r, const void* k_r,
+                      const void* v_rt, const int32_t* counts, const int32_t* lists, void* out,
+                      int32_t layout_flags, float* lse) {
+  abla_status st = check_geom(g);
+  if (st != ABLA_OK) return st;
+  if (!valid_dtype(dtype) || !q_r || !k_r || !v_rt || !counts || !lists || !out) return ABLA_ERR_INVALID;
+  if (!aligned16({q_r, k_r, v_rt, counts, lists, out, lse})) return ABLA_ERR_INVALID;
+  if (layout_flags & ~(ABLA_ATTN_OUT_ORIGINAL | ABLA_ATTN_QK_ORIGINAL | ABLA_ATTN_V_ORIGINAL))
+    return ABLA_ERR_INVALID;
+  if (isnan(scale) || scale < 0.f || isinf(scale)) return ABLA_ERR_INVALID;
+  if (nb_of(g) > kMaxBlocks) return ABLA_ERR_UNSUPPORTED;
+  const size_t bytes = tok_elems(g) * elem_bytes(dtype);
+  if (conflicts({{out, bytes}, {lse, lse ? rows_bytes(g) : 0}},
+                {{q_r, bytes}, {k_r, bytes}, {v_rt, bytes}, {counts, counts_bytes(g)}, {lists, lists_bytes(g)}}))
+    return ABLA_ERR_INVALID;
+  return ABLA_OK;
+}
+
+abla_status launch_fwd(const abla_geom* g, int32_t dtype, float scale, const void* q_r, const void* k_r,
+                       const void* v_rt, const int32_t* counts, const int32_t* lists, void* out,
+                       int32_t layout_flags, float* lse, int32_t* scratch, void* stream) {
+  const float s = scale > 0.f ? scale : 1.0f / sqrtf((float)g->d);
+  return from_hip(launch_sparse_attn(make_kgeom(*g), dtype, s, q_r, k_r, v_rt, counts, lists, out,
+                                     (layout_flags & ABLA_ATTN_OUT_ORIGINAL) != 0,
+                                     (layout_flags & ABLA_ATTN_QK_ORIGINAL) != 0,
+                                     (layout_flags & ABLA_ATTN_V_ORIGINAL) != 0, lse, scratch,
+                                     (hipStream_t)stream));
+}
+
 }  // namespace
 
 extern "C" {
@@ -214,28 +245,30 @@ abla_status abla_sparse_attn_fwd(const abla_geom* g, int32_t dtype, float scale,
                                  const void* k_r, const void* v_rt, const int32_t* counts, const int32_t* lists,
                                  void* out, int32_t layout_flags, float* lse, void* workspace,
                                  size_t workspace_bytes, void* stream) {
-  abla_status st = check_geom(g);
+  abla_status st = check_fwd(g, dtype, scale, q_r, k_r, v_rt, counts, lists, out, layout_flags, lse);
   if (st != ABLA_OK) return st;
-  if (!valid_dtype(dtype) || !q_r || !k_r || !v_rt || !counts || !lists || !out) return ABLA_ERR_INVALID;
-  if (!aligned16({q_r, k_r, v_rt, counts, lists, out, lse, workspace})) return ABLA_ERR_INVALID;
-  if (layout_flags & ~(ABLA_ATTN_OUT_ORIGINAL | ABLA_ATTN_QK_ORIGINAL | ABLA_ATTN_V_ORIGINAL))
-    return ABLA_ERR_INVALID;
-  if (isnan(scale) || scale < 0.f || isinf(scale)) return ABLA_ERR_INVALID;
-  if (nb_of(g) > kMaxBlocks) return ABLA_ERR_UNSUPPORTED;
-  const size_t bytes = tok_elems(g) * elem_bytes(dtype);
-  if (overlaps(out, bytes, q_r, bytes) || overlaps(out, bytes, k_r, bytes) || overlaps(out, bytes, v_rt, bytes))
-    return ABLA_ERR_INVALID;
+  if (!aligned16({workspace})) return ABLA_ERR_INVALID;
   if (!workspace || workspace_bytes < abla_sparse_attn_workspace_bytes(g)) return ABLA_ERR_WORKSPACE;
-  // out, lse and the scratch overlap neither each other nor any input.
-  if (conflicts({{out, bytes}, {lse, lse ? rows_bytes(g) : 0}, {workspace, abla_sparse_attn_workspace_bytes(g)}},
+  // The scratch overlaps neither an output nor any input.
+  const size_t bytes = tok_elems(g) * elem_bytes(dtype);
+  if (conflicts({{workspace, abla_sparse_attn_workspace_bytes(g)}, {out, bytes}, {lse, lse ? rows_bytes(g) : 0}},
                 {{q_r, bytes}, {k_r, bytes}, {v_rt, bytes}, {counts, counts_bytes(g)}, {lists, lists_bytes(g)}}))
     return ABLA_ERR_INVALID;
-  const float s = scale > 0.f ? scale : 1.0f / sqrtf((float)g->d);
-  return from_hip(launch_sparse_attn(make_kgeom(*g), dtype, s, q_r, k_r, v_rt, counts, lists, out,
-                                     (layout_flags & ABLA_ATTN_OUT_ORIGINAL) != 0,
-                                     (layout_flags & ABLA_ATTN_QK_ORIGINAL) != 0,
-                                     (layout_flags & ABLA_ATTN_V_ORIGINAL) != 0, lse,
-                                     static_cast<int32_t*>(workspace), (hipStream_t)stream));
+  return launch_fwd(g, dtype, scale, q_r, k_r, v_rt, counts, lists, out, layout_flags, lse,
+                    static_cast<int32_t*>(workspace), stream);
+}
+
+abla_status abla_sparse_attn_fwd_noalloc(const abla_geom* g, int32_t dtype, float scale, const void* q_r,
+                                         const void* k_r, const void* v_rt, const int32_t* counts,
+                                         const int32_t* lists, void* out, int32_t layout_flags, float* lse,
+                                         void* stream) {
+  abla_status st = check_fwd(g, dtype, scale, q_r, k_r, v_rt, counts, lists, out, layout_flags, lse);
+  if (st != ABLA_OK) return st;
+  if (abla_sparse_attn_workspace_bytes(g) > kNoAllocScratchBytes) return ABLA_ERR_WORKSPACE;
+  void* scratch = nullptr;
+  if (noalloc_scratch(&scratch) != hipSuccess) return ABLA_ERR_HIP;
+  return launch_fwd(g, dtype, scale, q_r, k_r, v_rt, counts, lists, out, layout_flags, lse,
+                    static_cast<int32_t*>(scratch), stream);
 }
 
 size_t abla_sparse_attn_bwd_workspace_bytes(const abla_geom* g) {

@@ -59,6 +59,11 @@ hipError_t launch_sparse_attn(const KGeom& g, int dtype, float scale, const void
                               int out_original_order, int qk_original_order, int v_original_order, float* lse,
                               int32_t* row_order, hipStream_t s);
 
+// Scratch of abla_sparse_attn_fwd_noalloc: a file-scope device array of this many bytes (one
+// copy per GPU). Its device address on the current device, looked up once per device.
+constexpr size_t kNoAllocScratchBytes = size_t(1) << 20;
+hipError_t noalloc_scratch(void** ptr);
+
 // Device scratch of the backward pass, carved out of the caller's workspace
 // (see abla_sparse_attn_bwd_workspace_bytes).
 struct BwdWorkspace {

@@ -33,6 +33,8 @@
 // float32 path (k_attn_f32): plain FMA arithmetic, two threads per query row.
 #include <math.h>
 
+#include <mutex>
+
 #include "common.h"
 #include "mfma_tiles.h"
 
@@ -926,6 +928,35 @@ hipError_t launch_sparse_attn(const KGeom& g, int dtype, float scale, const void
       k_attn_f32<64><<<grid, 128, 0, s>>>(a);
   }
   return hipGetLastError();
+}
+
+// Scratch of the allocation-free forward (abla_sparse_attn_fwd_noalloc): the visiting order
+// and walk-mode word that launch_sparse_attn otherwise keeps in the caller's workspace. Each
+// GPU the library runs on holds its own copy until the process ends; every call on that GPU
+// shares it (k_pair_order or k_row_order rewrite all of it before the attention reads it, so
+// nothing needs clearing), and calls that overlap on one GPU race.
+static __device__ __attribute__((aligned(256))) char scratch[kNoAllocScratchBytes];
+
+constexpr int kMaxDevices = 64;
+
+// Device address of `scratch` on the current device. The array's name in host code is only a
+// host-side handle; its address on each device comes from hipGetSymbolAddress, once per device.
+hipError_t noalloc_scratch(void** ptr) {
+  static std::mutex mu;
+  static void* per_device[kMaxDevices] = {};
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lock(mu);
+  if (!per_device[dev]) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return e;
+    per_device[dev] = p;
+  }
+  *ptr = per_device[dev];
+  return hipSuccess;
 }
 
 }  // namespace abla

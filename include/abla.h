@@ -212,6 +212,19 @@ abla_status abla_sparse_attn_fwd(const abla_geom* g, int32_t dtype, float scale,
                                  void* out, int32_t layout_flags, float* lse,
                                  void* workspace, size_t workspace_bytes, void* stream);
 
+/* abla_sparse_attn_fwd without a workspace argument, for callers that cannot allocate device
+ * memory (code under HIP graph capture, tight serving loops, harnesses that forbid allocation).
+ * Arguments, results and errors are those of abla_sparse_attn_fwd, computed by the same kernels.
+ * Its scratch (the visiting order, abla_sparse_attn_workspace_bytes(g) bytes) lives in a
+ * 1 MiB array inside the library, one per GPU, kept until the process ends; the call allocates
+ * nothing. Limit: B*H*nb*4 + 256 <= 1 MiB (B*H*nb <= 262080 query blocks), else
+ * ABLA_ERR_WORKSPACE before anything is enqueued. Every call on one GPU shares that GPU's
+ * array: calls that overlap in time on one GPU (different streams, or host threads) race. */
+abla_status abla_sparse_attn_fwd_noalloc(const abla_geom* g, int32_t dtype, float scale, const void* q_r,
+                                         const void* k_r, const void* v_rt, const int32_t* counts,
+                                         const int32_t* lists, void* out, int32_t layout_flags, float* lse,
+                                         void* stream);
+
 /* Bytes of scratch abla_sparse_attn_bwd needs: two [B,H,N] float32 rows (D and log2(e)*lse),
  * the column counts [B,H,nb] and lists [B,H,nb,nb] int32 and a [B,H,nb] int32 workgroup
  * visiting order, each rounded up to 256 bytes.

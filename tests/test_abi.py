@@ -31,7 +31,7 @@ def declared_functions():
 
 def test_exports_every_declared_symbol(A):
     names = declared_functions()
-    assert len(names) == 10
+    assert len(names) == 11
     lib = ctypes.CDLL(LIB)
     for n in names:
         assert hasattr(lib, n), n
@@ -242,6 +242,8 @@ def _entry_calls(A):
         "abla_build_mask": (6, lambda P: L.abla_build_mask(ctypes.byref(g), ctypes.byref(p), *P, ws_mask, None)),
         "abla_sparse_attn_fwd": (8, lambda P: L.abla_sparse_attn_fwd(ctypes.byref(g), 1, 0.0, *P[:6], 3, *P[6:],
                                                                       ws_attn, None)),
+        "abla_sparse_attn_fwd_noalloc": (7, lambda P: L.abla_sparse_attn_fwd_noalloc(ctypes.byref(g), 1, 0.0,
+                                                                                      *P[:6], 3, P[6], None)),
         "abla_sparse_attn_bwd": (13, lambda P: L.abla_sparse_attn_bwd(ctypes.byref(g), 1, 0.0, *P, ws_bwd, None)),
     }
 
@@ -259,3 +261,28 @@ def test_misaligned_pointers_rejected(A):
         for slot in range(n):
             for shift in (8, 4):
                 assert call([_p(i + 1, shift if i == slot else 0) for i in range(n)]) == 1, (name, slot, shift)
+
+
+def test_noalloc_forward_limits(A):
+    """The allocation-free forward has the forward's argument checks and refuses, before touching
+    any device, a geometry whose visiting order exceeds its 1 MiB built-in scratch."""
+    import torch
+    if torch.cuda.is_available():
+        pytest.skip("host-only check: a call that passed validation would launch on a visible device")
+    L = A._lib
+
+    def call(g, P=None, flags=3):
+        P = P or [_p(i + 1) for i in range(7)]
+        return L.abla_sparse_attn_fwd_noalloc(ctypes.byref(g), 1, 0.0, *P[:6], flags, P[6], None)
+
+    big = G(A, H=256, T=21, Hs=48, Ws=80)  # 256 * 1260 query blocks: 1.29 MB of visiting order
+    assert A.sparse_attn_workspace_bytes(A.Geometry(1, 256, 21, 48, 80, 128)) > (1 << 20)
+    assert call(big) == 3
+    fits = G(A, H=200, T=21, Hs=48, Ws=80)  # 252000 blocks: fits, fails only at the launch here
+    assert call(fits) == 4
+    g = G(A)
+    assert call(g, flags=8) == 1
+    assert call(g, P=[_p(1), None] + [_p(i + 1) for i in range(2, 7)]) == 1
+    assert call(g, P=[_p(i + 1) for i in range(5)] + [_p(1), _p(7)]) == 1  # out is q
+    assert L.abla_sparse_attn_fwd_noalloc(ctypes.byref(G(A, d=96)), 1, 0.0, *[_p(i + 1) for i in range(6)], 3,
+                                          _p(7), None) == 2
