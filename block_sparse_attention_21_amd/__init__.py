@@ -372,7 +372,8 @@ class NablaAttention:
     """The whole forward path for one geometry, with every buffer allocated once.
 
     __call__(q, k, v) runs: pool Q and K into block means, reorder V (channel-major
-    blocks), build the mask, block-sparse attention reading Q and K in their original
+    blocks; skipped for float32, whose attention reads V in the original order unless
+    fuse_v=False), build the mask, block-sparse attention reading Q and K in their original
     order and writing the output in the original token order. With fused=False, Q and K
     are first copied to fractal order (reorder + pool in one pass) and the attention
     reads the copies; the results are identical. Intermediate results stay available as
@@ -383,8 +384,12 @@ class NablaAttention:
     """
 
     def __init__(self, geom: Geometry, params: MaskParams, dtype=torch.bfloat16, device="cuda",
-                 scale: float = 0.0, want_lse: bool = False, fused: bool = True, fuse_v: bool = False):
+                 scale: float = 0.0, want_lse: bool = False, fused: bool = True, fuse_v: Optional[bool] = None):
         self.geom, self.params, self.scale, self.fused = geom, params, scale, fused
+        # float32 stages its tiles through registers, so V in the original order costs nothing
+        # there; bf16 reads V^T operands from channel-major blocks (one LDS read per product).
+        if fuse_v is None:
+            fuse_v = dtype == torch.float32
         self.fuse_v = fused and fuse_v
         dev = torch.device(device)
         g = geom

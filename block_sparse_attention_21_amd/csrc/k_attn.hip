@@ -30,7 +30,7 @@
 // (neighbouring workgroups then share key blocks in L2); with long lists, longest-first
 // per head so the long rows of the kept-count distribution do not form the tail.
 //
-// float32 path (k_attn_f32): plain FMA arithmetic, two threads per query row.
+// float32 path (k_attn_f32): float32 matrix cores, four waves per query block.
 #include <math.h>
 
 #include <mutex>
@@ -540,113 +540,255 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
   }
 }
 
-// float32 path: 128 threads per query block, thread pair (2r, 2r+1) owns query row r,
-// each holding half of the channels.
+// float32 path on the float32 matrix cores (v_mfma_f32_32x32x2_f32). One workgroup of four waves
+// per query block; wave (qh, kh) = (w & 1, w >> 1) takes queries qh*32 .. +31 against keys
+// kh*32 .. +31 of every kept tile, with its own online softmax; the two key halves are merged
+// through LDS at the end. Operand layout of one 32x32x2 product: lane l supplies A[l % 32][l / 32]
+// and B[l / 32][l % 32]; accumulator register r of lane l is D[8(r/4) + 4(l/32) + r%4][l % 32].
+//   S^T = K Q^T: lane l supplies channel (l/32)*d/2 + s of its key and of its query at step s
+//     (the two lane halves reduce over the two channel halves; d/2 products in all).
+//   O^T += V^T P^T: A = V^T with channel row i of tile ct = channel (d/32)*i + ct, so that a lane
+//     reads the d/32 channels of all tiles as one vector; B = P^T at step r is register r of the
+//     probabilities (keys 8(r/4) + r%4 in lanes 0-31, that + 4 in lanes 32-63), no data movement.
+// K and V tiles are staged token-major in LDS (16-byte chunk c of row r at c ^ (r & 7)), double
+// buffered through registers: the next tile's global loads are issued before this tile's products
+// and stored to the other slot after them, one barrier per tile. The softmax works in log2 units
+// (exp2 of scale * log2(e) * s minus the running maximum) and rescales whenever the maximum grows.
 struct AttnArgsF32 {
   const float* q;
   const float* k;
-  const float* vt;
+  const float* v;  // token-major in the original order (v_orig), else channel-major blocks [nb, d, 64]
   const int32_t* counts;
   const int32_t* lists;
   const int32_t* order;
   float* out;
   float* lse;
   KGeom g;
-  float scale;
+  float c2;  // scale * log2(e)
   int orig;
-  int qk_orig;  // Q and K in the original token order
-  int v_orig;   // V in the original token order (else channel-major blocks)
 };
 
 template <int D>
-__global__ __launch_bounds__(128) void k_attn_f32(AttnArgsF32 a) {
-  constexpr int H2 = D / 2;
-  constexpr int KC = 16;  // keys per softmax chunk
-  __shared__ __attribute__((aligned(16))) float ks[kBlock * D];
-  __shared__ __attribute__((aligned(16))) float vs[D * kBlock];
-  const int t = threadIdx.x;
-  const int r = t >> 1, half = t & 1;
+struct F32Tile {
+  static constexpr int CH = D / 4;          // 16-byte chunks per token row
+  static constexpr int BYTES = 64 * D * 4;  // one K or V tile
+  static constexpr int NLD = 64 * CH / 256; // 16-byte loads per thread per tile (each of K, V)
+  static constexpr int CPL = D / 32;        // output channel tiles; channels per lane read of V
+};
+
+__device__ __forceinline__ uint32_t f32_swz(int row, int chunk, int D) {
+  return (uint32_t)(row * D * 4 + ((chunk ^ (row & 7)) << 4));
+}
+
+// Token offset of tile row r from its block's first token: r in fractal order, or (r / 8) rows
+// of Ws tokens and r % 8 tokens past the block's corner in the original order.
+__device__ __forceinline__ long long f32_row_off(const KGeom& g, int r, bool orig) {
+  return orig ? (long long)(r >> 3) * g.Ws + (r & 7) : (long long)r;
+}
+__device__ __forceinline__ long long f32_block_base(const KGeom& g, int j, bool orig) {
+  if (!orig) return (long long)j * kBlock;
+  const int F = g.nbh * g.nbw;
+  const int tj = j / F, rem = j - tj * F, hp = rem / g.nbw, wp = rem - hp * g.nbw;
+  return ((long long)tj * g.Hs + hp * kP) * g.Ws + wp * kP;
+}
+
+// This thread's 16-byte chunks of K tile j and V tile j into registers (K first).
+template <int D, bool QKO, bool VORIG>
+__device__ __forceinline__ void f32_load_tile(const KGeom& g, const float* kbase, const float* vbase, int j, int t,
+                                              float4 (&stg)[2 * F32Tile<D>::NLD]) {
+  constexpr int CH = F32Tile<D>::CH, NLD = F32Tile<D>::NLD;
+  const long long kb = f32_block_base(g, j, QKO), vb = f32_block_base(g, j, true);
+#pragma unroll
+  for (int it = 0; it < NLD; ++it) {
+    const int u = t + 256 * it;
+    const int r = u / CH, c = u % CH;
+    stg[it] = *reinterpret_cast<const float4*>(kbase + (kb + f32_row_off(g, r, QKO)) * D + 4 * c);
+    if constexpr (VORIG)
+      stg[NLD + it] = *reinterpret_cast<const float4*>(vbase + (vb + f32_row_off(g, r, true)) * D + 4 * c);
+    else  // chunk u of the channel-major block: channel u / 16, keys 4*(u % 16) .. +3
+      stg[NLD + it] = *reinterpret_cast<const float4*>(vbase + (long long)j * D * kBlock + 4 * u);
+  }
+}
+
+// The staged chunks into LDS slot `slot`, both tiles token-major and swizzled.
+template <int D, bool VORIG>
+__device__ __forceinline__ void f32_store_tile(char* smem, int slot, int t, const float4 (&stg)[2 * F32Tile<D>::NLD]) {
+  constexpr int CH = F32Tile<D>::CH, NLD = F32Tile<D>::NLD;
+  char* kd = smem + slot * 2 * F32Tile<D>::BYTES;
+  char* vd = kd + F32Tile<D>::BYTES;
+#pragma unroll
+  for (int it = 0; it < NLD; ++it) {
+    const int u = t + 256 * it;
+    const int r = u / CH, c = u % CH;
+    *reinterpret_cast<float4*>(kd + f32_swz(r, c, D)) = stg[it];
+    if constexpr (VORIG) {
+      *reinterpret_cast<float4*>(vd + f32_swz(r, c, D)) = stg[NLD + it];
+    } else {
+      const int ch = u >> 4, k0 = (u & 15) * 4;
+      *reinterpret_cast<float*>(vd + f32_swz(k0, ch >> 2, D) + (ch & 3) * 4) = stg[NLD + it].x;
+      *reinterpret_cast<float*>(vd + f32_swz(k0 + 1, ch >> 2, D) + (ch & 3) * 4) = stg[NLD + it].y;
+      *reinterpret_cast<float*>(vd + f32_swz(k0 + 2, ch >> 2, D) + (ch & 3) * 4) = stg[NLD + it].z;
+      *reinterpret_cast<float*>(vd + f32_swz(k0 + 3, ch >> 2, D) + (ch & 3) * 4) = stg[NLD + it].w;
+    }
+  }
+}
+
+template <int D, bool QKO, bool VORIG>
+__global__ __launch_bounds__(256) void k_attn_f32(AttnArgsF32 a) {
+  using TT = F32Tile<D>;
+  constexpr int NLD = TT::NLD, CPL = TT::CPL;
+  __shared__ __attribute__((aligned(16))) char smem[4 * TT::BYTES];  // K0, V0, K1, V1
+  const int t = threadIdx.x, lane = t & 63, w = t >> 6;
+  const int qh = w & 1, kh = w >> 1, hf = lane >> 5, m = lane & 31;
   const KGeom& g = a.g;
   const int nb = g.nb;
   const int bh = blockIdx.x / nb;
   const int pos = blockIdx.x - bh * nb;
-  const int i = a.order ? a.order[(long long)bh * nb + pos] : pos;
+  const int i = a.order[(long long)bh * nb + pos];
   const long long row = (long long)bh * nb + i;
   const int cnt = min(max(a.counts[row], 0), nb);
   const int32_t* lst = a.lists + row * nb;
 
-  float q[H2], o[H2];
-  const long long qn = a.qk_orig ? token_of(g, i, r) : (long long)i * kBlock + r;
-  const float* qrow = a.q + ((long long)bh * g.N + qn) * D + half * H2;
+  // Q operand: Q[query qh*32 + m][hf*D/2 + s] for s = 0 .. D/2 - 1.
+  float qv[D / 2];
+  {
+    const int qr = qh * 32 + m;
+    const long long qn = QKO ? token_of(g, i, qr) : (long long)i * kBlock + qr;
+    const float4* src = reinterpret_cast<const float4*>(a.q + ((long long)bh * g.N + qn) * D + hf * (D / 2));
 #pragma unroll
-  for (int c = 0; c < H2; ++c) {
-    q[c] = qrow[c];
-    o[c] = 0.f;
+    for (int c = 0; c < D / 8; ++c) {
+      const float4 x = src[c];
+      qv[4 * c] = x.x;
+      qv[4 * c + 1] = x.y;
+      qv[4 * c + 2] = x.z;
+      qv[4 * c + 3] = x.w;
+    }
   }
-  float m_run = -INFINITY, l_run = 0.f;
   const float* kbase = a.k + (long long)bh * g.N * D;
-  const float* vbase = a.vt + (long long)bh * nb * D * kBlock;
+  const float* vbase = a.v + (long long)bh * g.N * D;  // both V layouts hold N*D floats per head
+  float4 stg[2 * NLD];  // the next tile: NLD chunks of K, then NLD of V
 
-  for (int tt = 0; tt < cnt; ++tt) {
-    const int j = min(max(lst[tt], 0), nb - 1);
-    const float4* vg = reinterpret_cast<const float4*>(vbase + (long long)j * D * kBlock);
-    for (int u = t; u < kBlock * D / 4; u += 128) {
-      const int kr = u / (D / 4);  // key row of the tile, in fractal position order
-      const int c4 = (u % (D / 4)) * 4;
-      const long long kn = a.qk_orig ? token_of(g, j, kr) : (long long)j * kBlock + kr;
-      reinterpret_cast<float4*>(ks)[u] = *reinterpret_cast<const float4*>(kbase + kn * D + c4);
-      if (a.v_orig) {  // transpose the token row into the channel-major tile
-        const float4 x = *reinterpret_cast<const float4*>(vbase + token_of(g, j, kr) * D + c4);
-        vs[(c4 + 0) * kBlock + kr] = x.x;
-        vs[(c4 + 1) * kBlock + kr] = x.y;
-        vs[(c4 + 2) * kBlock + kr] = x.z;
-        vs[(c4 + 3) * kBlock + kr] = x.w;
-      } else {
-        reinterpret_cast<float4*>(vs)[u] = vg[u];
-      }
-    }
-    __syncthreads();
-    for (int kc = 0; kc < kBlock; kc += KC) {
-      float s[KC];
-      float mx = -INFINITY;
+  f32x16_t o[CPL];
 #pragma unroll
-      for (int kk = 0; kk < KC; ++kk) {
-        const float* krow = ks + (kc + kk) * D + half * H2;
-        float part = 0.f;
+  for (int ct = 0; ct < CPL; ++ct)
 #pragma unroll
-        for (int c = 0; c < H2; ++c) part = fmaf(q[c], krow[c], part);
-        const float other = __shfl_xor(part, 1);
-        s[kk] = (half ? other + part : part + other) * a.scale;
-        mx = fmaxf(mx, s[kk]);
-      }
-      const float m_new = fmaxf(m_run, mx);
-      const float alpha = expf(m_run - m_new);
-      float psum = 0.f;
-#pragma unroll
-      for (int kk = 0; kk < KC; ++kk) {
-        s[kk] = expf(s[kk] - m_new);
-        psum += s[kk];
-      }
-      l_run = l_run * alpha + psum;
-      m_run = m_new;
-#pragma unroll
-      for (int c = 0; c < H2; ++c) {
-        float acc = o[c] * alpha;
-        const float* vcol = vs + (half * H2 + c) * kBlock + kc;
-#pragma unroll
-        for (int kk = 0; kk < KC; ++kk) acc = fmaf(s[kk], vcol[kk], acc);
-        o[c] = acc;
-      }
-    }
+    for (int r = 0; r < 16; ++r) o[ct][r] = 0.f;
+  float m_run = -INFINITY, l_run = 0.f;
+  const float c2 = a.c2;
+  const int krow = kh * 32 + m;  // this lane's key row of a tile in S^T
+
+  // List entries are read one step before their tile's loads are issued; past the end of the
+  // list the loads fetch tile 0 into the slot that is not read again (no branches around them).
+  auto entry = [&](int u) { return u < cnt ? min(max(lst[u], 0), nb - 1) : 0; };
+  int j_next = entry(1);
+  if (cnt > 0) {
+    f32_load_tile<D, QKO, VORIG>(g, kbase, vbase, entry(0), t, stg);
+    f32_store_tile<D, VORIG>(smem, 0, t, stg);
     __syncthreads();
   }
-  const float inv = cnt > 0 ? 1.0f / l_run : 0.f;
-  const long long n = a.orig ? token_of(g, i, r) : (long long)i * kBlock + r;
-  float* orow = a.out + ((long long)bh * g.N + n) * D + half * H2;
+  for (int u = 0; u < cnt; ++u) {
+    const int j_after = entry(u + 2);
+    f32_load_tile<D, QKO, VORIG>(g, kbase, vbase, j_next, t, stg);
+    j_next = j_after;
+    const char* ks = smem + (u & 1) * 2 * TT::BYTES;
+    const char* vs = ks + TT::BYTES;
+    // S^T for keys kh*32 + (0..31) x queries qh*32 + (0..31): four accumulators (one per channel
+    // step of a chunk) so that consecutive products are independent; added at the end.
+    f32x16_t sa[4];
 #pragma unroll
-  for (int c = 0; c < H2; ++c) orow[c] = o[c] * inv;
-  if (a.lse && half == 0)
-    a.lse[(long long)bh * g.N + (long long)i * kBlock + r] = cnt > 0 ? m_run + logf(l_run) : -INFINITY;
+    for (int e = 0; e < 4; ++e)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) sa[e][r] = 0.f;
+#pragma unroll
+    for (int c4 = 0; c4 < D / 8; ++c4) {
+      const float4 kk = *reinterpret_cast<const float4*>(ks + f32_swz(krow, hf * (D / 8) + c4, D));
+      sa[0] = __builtin_amdgcn_mfma_f32_32x32x2f32(kk.x, qv[4 * c4], sa[0], 0, 0, 0);
+      sa[1] = __builtin_amdgcn_mfma_f32_32x32x2f32(kk.y, qv[4 * c4 + 1], sa[1], 0, 0, 0);
+      sa[2] = __builtin_amdgcn_mfma_f32_32x32x2f32(kk.z, qv[4 * c4 + 2], sa[2], 0, 0, 0);
+      sa[3] = __builtin_amdgcn_mfma_f32_32x32x2f32(kk.w, qv[4 * c4 + 3], sa[3], 0, 0, 0);
+    }
+    f32x16_t s0;
+#pragma unroll
+    for (int r = 0; r < 16; ++r) s0[r] = (sa[0][r] + sa[1][r]) + (sa[2][r] + sa[3][r]);
+    float mx = -INFINITY;
+#pragma unroll
+    for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s0[r]);
+    const float m_new = fmaxf(m_run, swap_max(mx) * c2);
+    const float alpha = exp2_fast(m_run - m_new);  // 0 on the first tile (m_run = -inf)
+    m_run = m_new;
+    float ps = 0.f;
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      s0[r] = exp2_fast(fmaf(s0[r], c2, -m_new));
+      ps += s0[r];
+    }
+    l_run = l_run * alpha + ps;
+#pragma unroll
+    for (int ct = 0; ct < CPL; ++ct)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) o[ct][r] *= alpha;
+    // O^T += V^T P^T, 16 steps of two keys each.
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      const int key = kh * 32 + 8 * (r >> 2) + 4 * hf + (r & 3);
+      if constexpr (CPL == 4) {
+        const float4 vv = *reinterpret_cast<const float4*>(vs + f32_swz(key, m, D));
+        o[0] = __builtin_amdgcn_mfma_f32_32x32x2f32(vv.x, s0[r], o[0], 0, 0, 0);
+        o[1] = __builtin_amdgcn_mfma_f32_32x32x2f32(vv.y, s0[r], o[1], 0, 0, 0);
+        o[2] = __builtin_amdgcn_mfma_f32_32x32x2f32(vv.z, s0[r], o[2], 0, 0, 0);
+        o[3] = __builtin_amdgcn_mfma_f32_32x32x2f32(vv.w, s0[r], o[3], 0, 0, 0);
+      } else {
+        const float2 vv = *reinterpret_cast<const float2*>(vs + f32_swz(key, m >> 1, D) + (m & 1) * 8);
+        o[0] = __builtin_amdgcn_mfma_f32_32x32x2f32(vv.x, s0[r], o[0], 0, 0, 0);
+        o[1] = __builtin_amdgcn_mfma_f32_32x32x2f32(vv.y, s0[r], o[1], 0, 0, 0);
+      }
+    }
+    f32_store_tile<D, VORIG>(smem, (u + 1) & 1, t, stg);
+    __syncthreads();
+  }
+
+  // Merge the two key halves: wave (qh, 1) hands its running maximum, sum and output to (qh, 0).
+  const float l_tot = swap_sum(l_run);
+  float* xo = reinterpret_cast<float*>(smem) + qh * (CPL * 16 * 64 + 128);  // [CPL][16][64], m, l
+  if (cnt > 0 && kh == 1) {
+#pragma unroll
+    for (int ct = 0; ct < CPL; ++ct)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) xo[(ct * 16 + r) * 64 + lane] = o[ct][r];
+    xo[CPL * 16 * 64 + lane] = m_run;
+    xo[CPL * 16 * 64 + 64 + lane] = l_tot;
+  }
+  __syncthreads();
+  if (kh == 1) return;
+  float inv = 0.f, lse2 = -INFINITY;
+  if (cnt > 0) {
+    const float m1 = xo[CPL * 16 * 64 + lane], l1 = xo[CPL * 16 * 64 + 64 + lane];
+    const float mm = fmaxf(m_run, m1);
+    const float a0 = exp2_fast(m_run - mm), a1 = exp2_fast(m1 - mm);
+    const float l = l_tot * a0 + l1 * a1;
+#pragma unroll
+    for (int ct = 0; ct < CPL; ++ct)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) o[ct][r] = o[ct][r] * a0 + xo[(ct * 16 + r) * 64 + lane] * a1;
+    inv = 1.0f / l;
+    lse2 = mm + log2f(l);
+  }
+  // Output row of query qh*32 + m: register r holds channels CPL*i .. CPL*i + CPL-1 (one per
+  // tile), i = 8(r/4) + 4*hf + r%4.
+  const int qr = qh * 32 + m;
+  const long long n = a.orig ? token_of(g, i, qr) : (long long)i * kBlock + qr;
+  float* orow = a.out + ((long long)bh * g.N + n) * D;
+#pragma unroll
+  for (int r = 0; r < 16; ++r) {
+    const int ci = 8 * (r >> 2) + 4 * hf + (r & 3);
+    if constexpr (CPL == 4)
+      *reinterpret_cast<float4*>(orow + 4 * ci) =
+          make_float4(o[0][r] * inv, o[1][r] * inv, o[2][r] * inv, o[3][r] * inv);
+    else
+      *reinterpret_cast<float2*>(orow + 2 * ci) = make_float2(o[0][r] * inv, o[1][r] * inv);
+  }
+  if (a.lse && hf == 0)
+    a.lse[(long long)bh * g.N + (long long)i * kBlock + qr] = cnt > 0 ? lse2 * 0.6931471805599453f : -INFINITY;
 }
 
 // In place: h[v] <- sum of h[v'] for v' > v (the first position of key v in descending
@@ -910,22 +1052,27 @@ hipError_t launch_sparse_attn(const KGeom& g, int dtype, float scale, const void
     AttnArgsF32 a;
     a.q = static_cast<const float*>(q);
     a.k = static_cast<const float*>(k);
-    a.vt = static_cast<const float*>(vt);
+    a.v = static_cast<const float*>(vt);
     a.counts = counts;
     a.lists = lists;
     a.order = row_order;
     a.out = static_cast<float*>(out);
     a.lse = lse;
     a.g = g;
-    a.scale = scale;
+    a.c2 = scale * 1.4426950408889634f;
     a.orig = out_original_order;
-    a.qk_orig = qk_original_order;
-    a.v_orig = v_original_order;
     const dim3 grid((unsigned)((long long)bhs * g.nb));
-    if (g.d == 128)
-      k_attn_f32<128><<<grid, 128, 0, s>>>(a);
-    else
-      k_attn_f32<64><<<grid, 128, 0, s>>>(a);
+    const int variant = (g.d == 128 ? 4 : 0) | (qk_original_order ? 2 : 0) | (v_original_order ? 1 : 0);
+    switch (variant) {
+      case 7: k_attn_f32<128, true, true><<<grid, 256, 0, s>>>(a); break;
+      case 6: k_attn_f32<128, true, false><<<grid, 256, 0, s>>>(a); break;
+      case 5: k_attn_f32<128, false, true><<<grid, 256, 0, s>>>(a); break;
+      case 4: k_attn_f32<128, false, false><<<grid, 256, 0, s>>>(a); break;
+      case 3: k_attn_f32<64, true, true><<<grid, 256, 0, s>>>(a); break;
+      case 2: k_attn_f32<64, true, false><<<grid, 256, 0, s>>>(a); break;
+      case 1: k_attn_f32<64, false, true><<<grid, 256, 0, s>>>(a); break;
+      default: k_attn_f32<64, false, false><<<grid, 256, 0, s>>>(a); break;
+    }
   }
   return hipGetLastError();
 }

@@ -265,7 +265,7 @@ def test_overlapping_buffers_rejected_on_device(A):
 
 
 # ---------------------------------------------------------------- the five workloads at full size
-def _workload(A, name, fuse_v=False, **over):
+def _workload(A, name, fuse_v=None, **over):
     """Run one workload at full size. The output and LSE buffers are filled with NaN first, so
     a row the kernels never write is seen by _check_written."""
     w = WORKLOADS[name].with_(**over) if over else WORKLOADS[name]
