@@ -99,6 +99,32 @@ def per_launch(fn, reps, stream, flush=None):
     return sorted(a.elapsed_time(b) for a, b in pairs)
 
 
+def mfma_loop_peak(kind=0, grid=2048, iters=20000, warm=12, reps=8):
+    """Sustained matrix-core rate on this board (TFLOP/s): libabla_probe's loop of independent
+    MFMAs with no memory traffic (kind 0: bf16 32x32x16, kind 1: float32 32x32x2), eight
+    workgroups per CU, timed with HIP events after enough launches for the clocks to settle."""
+    import ctypes
+    import torch
+    lib = ctypes.CDLL(os.path.join(ROOT, "block_sparse_attention_21_amd", "libabla_probe.so"))
+    lib.abla_probe_mfma.restype = ctypes.c_int32
+    lib.abla_probe_mfma.argtypes = [ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, ctypes.c_void_p, ctypes.c_void_p]
+    lib.abla_probe_mfma_flops.restype = ctypes.c_double
+    lib.abla_probe_mfma_flops.argtypes = [ctypes.c_int32, ctypes.c_int32, ctypes.c_int32]
+    sink = torch.zeros(grid, dtype=torch.float32, device="cuda")
+    stream = torch.cuda.current_stream()
+
+    def launch():
+        rc = lib.abla_probe_mfma(kind, grid, iters, ctypes.c_void_p(sink.data_ptr()),
+                                 ctypes.c_void_p(stream.cuda_stream))
+        if rc != 0:
+            raise RuntimeError(f"abla_probe_mfma failed ({rc})")
+
+    for _ in range(warm):
+        launch()
+    ms = timed(launch, reps, stream)
+    return lib.abla_probe_mfma_flops(kind, grid, iters) / (ms * 1e-3) / 1e12
+
+
 def median(xs):
     xs = sorted(xs)
     n = len(xs)
@@ -201,6 +227,23 @@ def cpu_baseline(r, budget_s):
     from oracle import nabla_ref as R
 
     w = r["w"]
+    cores = len(os.sched_getaffinity(0))
+    blas = {}
+    try:
+        from threadpoolctl import threadpool_info, threadpool_limits
+        threadpool_limits(cores)  # every BLAS pool at the cores this process may use
+        pools = [i for i in threadpool_info() if i.get("user_api") == "blas"]
+        if pools:
+            blas = {"blas": f"{pools[0].get('internal_api')} {pools[0].get('version')}",
+                    "blas_threads": int(pools[0].get("num_threads", cores))}
+    except Exception:
+        pass
+    cpu_model = "unknown"
+    try:
+        with open("/proc/cpuinfo") as f:
+            cpu_model = next(l.split(":", 1)[1].strip() for l in f if l.startswith("model name"))
+    except (OSError, StopIteration):
+        pass
     g1 = R.Geom(1, 1, w.T, w.Hs, w.Ws, w.d, w.P)
     prm = R.MaskParams(mode=w.mode, thr=w.thr, tau=w.tau, sta=tuple(w.sta), gamma=w.gamma, lam=w.lam)
     q, k, v = (x[0, 0].float().cpu().numpy().astype(np.float64) for x in (r["q"], r["k"], r["v"]))
@@ -221,14 +264,10 @@ def cpu_baseline(r, budget_s):
     t_attn = time.perf_counter() - t1
     head_s = t_mask + t_attn * g1.nb / max(done, 1)
     layer_s = head_s * w.B * w.H
-    try:
-        from threadpoolctl import threadpool_info
-        cores = max((i.get("num_threads", 1) for i in threadpool_info()), default=1)
-    except Exception:
-        cores = len(os.sched_getaffinity(0))
     return {
-        "value": r["dense_flops"] / layer_s / 1e12, "unit": "TFLOP/s (dense-equivalent)", "cores": int(cores),
-        "kind": "oracle", "ms_per_layer_est": layer_s * 1e3,
+        "value": r["dense_flops"] / layer_s / 1e12, "unit": "TFLOP/s (dense-equivalent)",
+        "cores": int(blas.get("blas_threads", cores)), "affinity_cores": cores, "cpu_model": cpu_model,
+        "blas": blas.get("blas", "unknown"), "kind": "oracle", "ms_per_layer_est": layer_s * 1e3,
         "sample": f"1 of {w.B * w.H} heads: reorder+pool+mask in full ({t_mask:.2f} s) and masked attention on "
                   f"{done} of {g1.nb} query blocks ({t_attn:.2f} s), scaled by blocks and heads; float64 numpy",
     }
@@ -251,12 +290,16 @@ def report(args):
     cases = [WORKLOADS["tiny"], WORKLOADS["480p"], WORKLOADS["720p"], WORKLOADS["480p-dyn"],
              WORKLOADS["480p-dyn"].with_(tau=2.0), WORKLOADS["480p-dyn"].with_(tau=8.0), WORKLOADS["480p-static"],
              WORKLOADS["long"]]
-    print(f"bf16 GEMM reference (torch.matmul {n}^3): {gemm:,.0f} TFLOP/s\n")
+    loop_bf16, loop_f32 = mfma_loop_peak(0), mfma_loop_peak(1)
+    print(f"bf16 GEMM reference (torch.matmul {n}^3): {gemm:,.0f} TFLOP/s; matrix-core loops on this board "
+          f"(libabla_probe, no memory traffic): bf16 {loop_bf16:,.0f} TFLOP/s, float32 {loop_f32:,.1f} TFLOP/s "
+          f"(datasheet {MFMA_BF16_PEAK_TFLOPS:,.0f} / {FP32_PEAK_TFLOPS})\n")
     fwd_attn_ms = {}
     print("| workload | mask | keep | reorder ms (TB/s) | mask ms (GB/s) | attention ms | layer ms | "
           "single layers: median / min / cold median ms | "
-          "dense-eq TFLOP/s (layer / attn) | actual TFLOP/s | of 2.5 PF | of GEMM ref | keep per head |")
-    print("|---|---|---|---|---|---|---|---|---|---|---|---|---|")
+          "dense-eq TFLOP/s (layer / attn) | actual TFLOP/s | of datasheet peak | of MFMA loop | of GEMM ref | "
+          "keep per head |")
+    print("|---|---|---|---|---|---|---|---|---|---|---|---|---|---|")
     for w in cases:
         r = measure(w, args.steps, args.warmup)
         g = r["geom"]
@@ -268,6 +311,7 @@ def report(args):
         # Scored modes also read the pooled vectors and write + read the float64 score matrix.
         mask_bytes = out_bytes + (0 if w.mode == "static" else 2 * pooled + 2 * g.B * g.H * g.nb * g.nb * 8)
         attn_tf = r["kept_flops"] / (r["ms_attn"] * 1e-3) / 1e12
+        peak, loop = (MFMA_BF16_PEAK_TFLOPS, loop_bf16) if w.dtype == "bf16" else (FP32_PEAK_TFLOPS, loop_f32)
         mode = {"cdf": f"cdf {w.thr}", "dyn": f"dyn tau={w.tau}",
                 "static": f"static gamma={w.gamma} lambda={w.lam}"}[w.mode]
         heads = ", ".join(f"{x:.3f}" for x in per_head[:12]) + (" ..." if len(per_head) > 12 else "")
@@ -277,7 +321,7 @@ def report(args):
               f"{median(r['warm']):.4f} / {r['warm'][0]:.4f} / {median(r['cold']):.4f} | "
               f"{r['dense_flops'] / (r['ms_step'] * 1e-3) / 1e12:,.1f} / "
               f"{r['dense_flops'] / (r['ms_attn'] * 1e-3) / 1e12:,.1f} | {attn_tf:,.1f} | "
-              f"{attn_tf / MFMA_BF16_PEAK_TFLOPS:.3f} | {attn_tf / gemm:.3f} | {heads} |", flush=True)
+              f"{attn_tf / peak:.3f} | {attn_tf / loop:.3f} | {attn_tf / gemm:.3f} | {heads} |", flush=True)
         fwd_attn_ms[w.name + (f"-tau{w.tau}" if w.mode == "dyn" else "")] = r["ms_attn"]
         del r
     print("\nBackward (abla_sparse_attn_bwd, every pass: D and L2 rows, column lists, visiting order, dQ, dK+dV), "
@@ -333,6 +377,7 @@ def main():
         return
     r = measure(args.workload, args.steps, args.warmup, use_graph=args.graph)
     w, geom = r["w"], r["geom"]
+    loop_peak = mfma_loop_peak(0)
     value = r["dense_flops"] / (r["ms_step"] * 1e-3) / 1e12
     attn_tflops = r["kept_flops"] / (r["ms_attn"] * 1e-3) / 1e12
     traffic = traffic_for(args.traffic, w.name)
@@ -375,6 +420,8 @@ def main():
             "unit": "TFLOP/s",
             "frac": round(attn_tflops / MFMA_BF16_PEAK_TFLOPS, 4),
             "traffic": traffic,
+            "mfma_loop_peak": round(loop_peak, 1),
+            "frac_of_mfma_loop": round(attn_tflops / loop_peak, 4),
         },
     }
     if args.secondary:
@@ -384,6 +431,7 @@ def main():
             "effective_tflops": round(s["dense_flops"] / (s["ms_step"] * 1e-3) / 1e12, 3),
             "attention_actual_tflops": round(s["kept_flops"] / (s["ms_attn"] * 1e-3) / 1e12, 2),
             "mfma_frac": round(s["kept_flops"] / (s["ms_attn"] * 1e-3) / 1e12 / MFMA_BF16_PEAK_TFLOPS, 4),
+            "frac_of_mfma_loop": round(s["kept_flops"] / (s["ms_attn"] * 1e-3) / 1e12 / loop_peak, 4),
             "keep_fraction": round(s["keep_fraction"], 5),
             "ms_per_stage": {"reorder_pool_qkv": round(s["ms_reorder"], 4), "mask": round(s["ms_mask"], 4),
                              "attention": round(s["ms_attn"], 4)},

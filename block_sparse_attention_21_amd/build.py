@@ -13,9 +13,11 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(PKG, "libabla.so")
+PROBE_LIB = os.path.join(PKG, "libabla_probe.so")  # matrix-core rate probes for the benchmark
 OBJ = os.path.join(PKG, "_build")
 
 SOURCES = ["abla_api.hip", "k_reorder.hip", "k_mask.hip", "k_attn.hip", "k_attn_bwd.hip"]
+PROBE_SOURCES = ["probe_mfma.hip"]
 
 FLAGS = [
     "--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC",
@@ -45,16 +47,20 @@ def _run(cmd, verbose):
 
 
 def build(verbose: bool = False) -> str:
-    """Compile every source and link libabla.so; always rebuilds. Returns the library path."""
+    """Compile every source and link libabla.so (and the benchmark's libabla_probe.so); always
+    rebuilds. Returns the path of libabla.so."""
     os.makedirs(OBJ, exist_ok=True)
     cc = hipcc()
-    objs = [os.path.join(OBJ, s.replace(".hip", ".o")) for s in SOURCES]
-    jobs = [[cc, *FLAGS, "-c", os.path.join(CSRC, s), "-o", o] for s, o in zip(SOURCES, objs)]
+    srcs = SOURCES + PROBE_SOURCES
+    objs = {s: os.path.join(OBJ, s.replace(".hip", ".o")) for s in srcs}
+    jobs = [[cc, *FLAGS, "-c", os.path.join(CSRC, s), "-o", objs[s]] for s in srcs]
     with ThreadPoolExecutor(max_workers=min(4, os.cpu_count() or 1)) as ex:
         list(ex.map(lambda c: _run(c, verbose), jobs))
-    tmp = LIB + ".tmp"
-    _run([cc, "--offload-arch=gfx950", "-shared", "-fPIC", "-Wl,--no-undefined", *objs, "-o", tmp], verbose)
-    os.replace(tmp, LIB)
+    for lib, group in ((LIB, SOURCES), (PROBE_LIB, PROBE_SOURCES)):
+        tmp = lib + ".tmp"
+        _run([cc, "--offload-arch=gfx950", "-shared", "-fPIC", "-Wl,--no-undefined", *[objs[s] for s in group],
+              "-o", tmp], verbose)
+        os.replace(tmp, lib)
     return LIB
 
 

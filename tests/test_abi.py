@@ -286,3 +286,24 @@ def test_noalloc_forward_limits(A):
     assert call(g, P=[_p(i + 1) for i in range(5)] + [_p(1), _p(7)]) == 1  # out is q
     assert L.abla_sparse_attn_fwd_noalloc(ctypes.byref(G(A, d=96)), 1, 0.0, *[_p(i + 1) for i in range(6)], 3,
                                           _p(7), None) == 2
+
+
+def test_probe_library_exports():
+    """The benchmark's matrix-core probe library exports what include/abla_probe.h declares and
+    rejects bad arguments before launching."""
+    path = os.path.join(ROOT, "block_sparse_attention_21_amd", "libabla_probe.so")
+    with open(os.path.join(ROOT, "include", "abla_probe.h")) as f:
+        names = sorted(set(re.findall(r"^\s*(?:int32_t|double)\s+(abla_[a-z_0-9]+)\s*\(", f.read(), re.MULTILINE)))
+    assert names == ["abla_probe_mfma", "abla_probe_mfma_flops"]
+    lib = ctypes.CDLL(path)
+    for n in names:
+        assert hasattr(lib, n), n
+    lib.abla_probe_mfma.restype = ctypes.c_int32
+    lib.abla_probe_mfma.argtypes = [ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, ctypes.c_void_p, ctypes.c_void_p]
+    lib.abla_probe_mfma_flops.restype = ctypes.c_double
+    lib.abla_probe_mfma_flops.argtypes = [ctypes.c_int32, ctypes.c_int32, ctypes.c_int32]
+    assert lib.abla_probe_mfma(2, 1, 1, FAKE, None) == 1
+    assert lib.abla_probe_mfma(0, 0, 1, FAKE, None) == 1
+    assert lib.abla_probe_mfma(0, 1, 1, None, None) == 1
+    assert lib.abla_probe_mfma_flops(0, 1, 1) == 2.0 * 32 * 32 * 16 * 16
+    assert lib.abla_probe_mfma_flops(1, 2, 3) == 2.0 * 32 * 32 * 2 * 16 * 6
