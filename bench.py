@@ -99,17 +99,66 @@ def per_launch(fn, reps, stream, flush=None):
     return sorted(a.elapsed_time(b) for a, b in pairs)
 
 
+def _probe_lib():
+    import ctypes
+    lib = ctypes.CDLL(os.path.join(ROOT, "block_sparse_attention_21_amd", "libabla_probe.so"))
+    lib.abla_probe_mfma.restype = ctypes.c_int32
+    lib.abla_probe_mfma.argtypes = [ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, ctypes.c_void_p, ctypes.c_void_p]
+    lib.abla_probe_mfma_flops.restype = ctypes.c_double
+    lib.abla_probe_mfma_flops.argtypes = [ctypes.c_int32, ctypes.c_int32, ctypes.c_int32]
+    lib.abla_probe_stream.restype = ctypes.c_int32
+    lib.abla_probe_stream.argtypes = [ctypes.c_int32, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int64,
+                                      ctypes.c_void_p]
+    return lib
+
+
+def hbm_stream_peak(copy, mib=2048, warm=3, reps=10):
+    """Sustained HBM rate on this board (GB/s): libabla_probe's stream of 16-byte loads over `mib`
+    MiB (8x the last-level cache), 32 KiB per workgroup, read-only or a copy (read + write bytes)."""
+    import ctypes
+    import torch
+    lib = _probe_lib()
+    nbytes = mib << 20
+    src = torch.ones(nbytes // 4, dtype=torch.float32, device="cuda")
+    dst = torch.empty(nbytes // 4 if copy else 4, dtype=torch.float32, device="cuda")
+    stream = torch.cuda.current_stream()
+
+    def launch():
+        rc = lib.abla_probe_stream(int(copy), ctypes.c_void_p(src.data_ptr()), ctypes.c_void_p(dst.data_ptr()),
+                                   nbytes, ctypes.c_void_p(stream.cuda_stream))
+        if rc != 0:
+            raise RuntimeError(f"abla_probe_stream failed ({rc})")
+
+    for _ in range(warm):
+        launch()
+    ms = timed(launch, reps, stream)
+    return nbytes * (2 if copy else 1) / (ms * 1e-3) / 1e9
+
+
+def graph_ms(fn, launches=10, reps=5):
+    """Milliseconds per call of fn() with launch gaps removed: `launches` calls captured in one
+    HIP graph, replayed `reps` times (fn must be capturable: no allocation, no memset)."""
+    import torch
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        fn()
+    torch.cuda.current_stream().wait_stream(side)
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        for _ in range(launches):
+            fn()
+    g.replay()
+    return timed(g.replay, reps, torch.cuda.current_stream()) / launches
+
+
 def mfma_loop_peak(kind=0, grid=2048, iters=20000, warm=12, reps=8):
     """Sustained matrix-core rate on this board (TFLOP/s): libabla_probe's loop of independent
     MFMAs with no memory traffic (kind 0: bf16 32x32x16, kind 1: float32 32x32x2), eight
     workgroups per CU, timed with HIP events after enough launches for the clocks to settle."""
     import ctypes
     import torch
-    lib = ctypes.CDLL(os.path.join(ROOT, "block_sparse_attention_21_amd", "libabla_probe.so"))
-    lib.abla_probe_mfma.restype = ctypes.c_int32
-    lib.abla_probe_mfma.argtypes = [ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, ctypes.c_void_p, ctypes.c_void_p]
-    lib.abla_probe_mfma_flops.restype = ctypes.c_double
-    lib.abla_probe_mfma_flops.argtypes = [ctypes.c_int32, ctypes.c_int32, ctypes.c_int32]
+    lib = _probe_lib()
     sink = torch.zeros(grid, dtype=torch.float32, device="cuda")
     stream = torch.cuda.current_stream()
 
@@ -163,6 +212,7 @@ def measure(name, steps, warmup, use_graph=False):
 
     # Per-stage averages (same inputs, state left by the path).
     ms_reorder = timed(lambda: run.reorder_pool(q, k, v), steps, stream)
+    ms_reorder_graph = graph_ms(lambda: run.reorder_pool(q, k, v))
     ms_mask = timed(run.mask, steps, stream)
     ms_attn = timed(run.attend, steps, stream)
 
@@ -188,6 +238,7 @@ def measure(name, steps, warmup, use_graph=False):
         graph=graph is not None, warm=warm, cold=cold,
         ms_reorder=ms_reorder, ms_mask=ms_mask, ms_attn=ms_attn, dense_flops=dense, kept_flops=kept_fl,
         reorder_gbs=reorder_bytes / (ms_reorder * 1e-3) / 1e9, tensor_bytes=tensor_bytes,
+        ms_reorder_graph=ms_reorder_graph, reorder_gbs_graph=reorder_bytes / (ms_reorder_graph * 1e-3) / 1e9,
         counts=run.counts, run=run, q=q, k=k, v=v,
     )
 
@@ -291,11 +342,13 @@ def report(args):
              WORKLOADS["480p-dyn"].with_(tau=2.0), WORKLOADS["480p-dyn"].with_(tau=8.0), WORKLOADS["480p-static"],
              WORKLOADS["long"]]
     loop_bf16, loop_f32 = mfma_loop_peak(0), mfma_loop_peak(1)
+    hbm_read, hbm_copy = hbm_stream_peak(False), hbm_stream_peak(True)
     print(f"bf16 GEMM reference (torch.matmul {n}^3): {gemm:,.0f} TFLOP/s; matrix-core loops on this board "
           f"(libabla_probe, no memory traffic): bf16 {loop_bf16:,.0f} TFLOP/s, float32 {loop_f32:,.1f} TFLOP/s "
-          f"(datasheet {MFMA_BF16_PEAK_TFLOPS:,.0f} / {FP32_PEAK_TFLOPS})\n")
+          f"(datasheet {MFMA_BF16_PEAK_TFLOPS:,.0f} / {FP32_PEAK_TFLOPS}); HBM streams (libabla_probe, 2 GiB): "
+          f"read {hbm_read:,.0f} GB/s, copy {hbm_copy:,.0f} GB/s (datasheet {HBM_PEAK_GBS:,.0f})\n")
     fwd_attn_ms = {}
-    print("| workload | mask | keep | reorder ms (TB/s) | mask ms (GB/s) | attention ms | layer ms | "
+    print("| workload | mask | keep | first step ms (TB/s); kernel-only from a graph | mask ms (GB/s) | attention ms | layer ms | "
           "single layers: median / min / cold median ms | "
           "dense-eq TFLOP/s (layer / attn) | actual TFLOP/s | of datasheet peak | of MFMA loop | of GEMM ref | "
           "keep per head |")
@@ -316,7 +369,8 @@ def report(args):
                 "static": f"static gamma={w.gamma} lambda={w.lam}"}[w.mode]
         heads = ", ".join(f"{x:.3f}" for x in per_head[:12]) + (" ..." if len(per_head) > 12 else "")
         print(f"| {w.name} ({w.dtype}, {w.N} tok) | {mode} | {r['keep_fraction']:.4f} | "
-              f"{r['ms_reorder']:.4f} ({r['reorder_gbs'] / 1e3:.2f}) | {r['ms_mask']:.4f} "
+              f"{r['ms_reorder']:.4f} ({r['reorder_gbs'] / 1e3:.2f}); {r['ms_reorder_graph']:.4f} "
+              f"({r['reorder_gbs_graph'] / 1e3:.2f}) | {r['ms_mask']:.4f} "
               f"({mask_bytes / (r['ms_mask'] * 1e-3) / 1e9:,.0f}) | {r['ms_attn']:.4f} | {r['ms_step']:.4f} | "
               f"{median(r['warm']):.4f} / {r['warm'][0]:.4f} / {median(r['cold']):.4f} | "
               f"{r['dense_flops'] / (r['ms_step'] * 1e-3) / 1e12:,.1f} / "
@@ -377,7 +431,10 @@ def main():
         return
     r = measure(args.workload, args.steps, args.warmup, use_graph=args.graph)
     w, geom = r["w"], r["geom"]
-    loop_peak = mfma_loop_peak(0)
+    f32 = w.dtype == "f32"
+    loop_peak = mfma_loop_peak(1 if f32 else 0)
+    peak = FP32_PEAK_TFLOPS if f32 else MFMA_BF16_PEAK_TFLOPS
+    hbm_read, hbm_copy = hbm_stream_peak(False), hbm_stream_peak(True)
     value = r["dense_flops"] / (r["ms_step"] * 1e-3) / 1e12
     attn_tflops = r["kept_flops"] / (r["ms_attn"] * 1e-3) / 1e12
     traffic = traffic_for(args.traffic, w.name)
@@ -412,13 +469,21 @@ def main():
         "keep_fraction": round(r["keep_fraction"], 5),
         "attention_actual_tflops": round(attn_tflops, 2),
         "reorder_pool_gbs": round(r["reorder_gbs"], 1),
+        "first_step": {
+            "kernel": "k_pool_qk_reorder_v (pool Q and K, reorder V)", "bound": "hbm",
+            "gbs_stage": round(r["reorder_gbs"], 1),
+            "gbs_kernel_graph": round(r["reorder_gbs_graph"], 1),
+            "ms_kernel_graph": round(r["ms_reorder_graph"], 4),
+            "peak": HBM_PEAK_GBS, "frac_kernel": round(r["reorder_gbs_graph"] / HBM_PEAK_GBS, 4),
+            "hbm_read_probe_gbs": round(hbm_read, 1), "hbm_copy_probe_gbs": round(hbm_copy, 1),
+        },
         "roofline": {
-            "kernel": "k_attn_bf16 (block-sparse attention forward)",
+            "kernel": ("k_attn_f32" if f32 else "k_attn_bf16") + " (block-sparse attention forward)",
             "bound": "mfma",
             "achieved": round(attn_tflops, 2),
-            "peak": MFMA_BF16_PEAK_TFLOPS,
+            "peak": peak,
             "unit": "TFLOP/s",
-            "frac": round(attn_tflops / MFMA_BF16_PEAK_TFLOPS, 4),
+            "frac": round(attn_tflops / peak, 4),
             "traffic": traffic,
             "mfma_loop_peak": round(loop_peak, 1),
             "frac_of_mfma_loop": round(attn_tflops / loop_peak, 4),
@@ -431,11 +496,13 @@ def main():
             "effective_tflops": round(s["dense_flops"] / (s["ms_step"] * 1e-3) / 1e12, 3),
             "attention_actual_tflops": round(s["kept_flops"] / (s["ms_attn"] * 1e-3) / 1e12, 2),
             "mfma_frac": round(s["kept_flops"] / (s["ms_attn"] * 1e-3) / 1e12 / MFMA_BF16_PEAK_TFLOPS, 4),
-            "frac_of_mfma_loop": round(s["kept_flops"] / (s["ms_attn"] * 1e-3) / 1e12 / loop_peak, 4),
+            "frac_of_mfma_loop": (round(s["kept_flops"] / (s["ms_attn"] * 1e-3) / 1e12 / loop_peak, 4)
+                                  if s["w"].dtype == w.dtype else None),
             "keep_fraction": round(s["keep_fraction"], 5),
             "ms_per_stage": {"reorder_pool_qkv": round(s["ms_reorder"], 4), "mask": round(s["ms_mask"], 4),
                              "attention": round(s["ms_attn"], 4)},
             "reorder_pool_gbs": round(s["reorder_gbs"], 1),
+            "reorder_pool_gbs_kernel_graph": round(s["reorder_gbs_graph"], 1),
             "single_steps_ms_median": round(median(s["warm"]), 4),
             "cold_cache_ms_median": round(median(s["cold"]), 4),
         }

@@ -1,7 +1,9 @@
-// Matrix-core rate probes for the benchmark: loops of independent MFMAs with no memory traffic,
-// timed on the board to give the sustained bf16 (v_mfma_f32_32x32x16_bf16) and float32
-// (v_mfma_f32_32x32x2_f32) rates that the attention kernels are compared against, next to the
+// Rate probes for the benchmark, timed on the board to give what it sustains, next to the
 // datasheet peaks. Not part of the attention path.
+//  - Matrix cores: loops of independent MFMAs with no memory traffic, bf16
+//    (v_mfma_f32_32x32x16_bf16) and float32 (v_mfma_f32_32x32x2_f32).
+//  - HBM: streams of 16-byte loads over a buffer (read-only, and a copy), one contiguous
+//    32 KiB span per workgroup, eight loads in flight per thread.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -47,6 +49,30 @@ __global__ __launch_bounds__(256) void k_mfma_loop(int iters, float* __restrict_
   if (s == -1.0f) sink[blockIdx.x] = s;  // sums of positive products: never true; keeps the loop
 }
 
+// Streams of 16-byte chunks, one contiguous 32 KiB span per workgroup (as the attention path's
+// kernels move their blocks): each thread issues its eight loads before using any. Read-only
+// (each thread folds its chunks into one word, stored only if it is a pattern no input gives)
+// or a copy to `dst`.
+constexpr int kStreamLoads = 8;
+constexpr long long kStreamSpan = 256 * kStreamLoads;  // chunks per workgroup (32 KiB)
+
+template <bool COPY>
+__global__ __launch_bounds__(256) void k_stream(const uint4* __restrict__ src, uint4* __restrict__ dst) {
+  const long long base = (long long)blockIdx.x * kStreamSpan + threadIdx.x;
+  uint4 v[kStreamLoads];
+#pragma unroll
+  for (int u = 0; u < kStreamLoads; ++u) v[u] = src[base + 256 * u];
+  if constexpr (COPY) {
+#pragma unroll
+    for (int u = 0; u < kStreamLoads; ++u) dst[base + 256 * u] = v[u];
+  } else {
+    unsigned int fold = 0;
+#pragma unroll
+    for (int u = 0; u < kStreamLoads; ++u) fold ^= v[u].x ^ v[u].y ^ v[u].z ^ v[u].w;
+    if (fold == 0x9E3779B9u) dst[0] = make_uint4(fold, 0, 0, 0);
+  }
+}
+
 }  // namespace
 
 extern "C" {
@@ -63,6 +89,19 @@ int32_t abla_probe_mfma(int32_t kind, int32_t grid, int32_t iters, float* sink, 
 double abla_probe_mfma_flops(int32_t kind, int32_t grid, int32_t iters) {
   const double per = kind == 0 ? 2.0 * 32 * 32 * 16 : 2.0 * 32 * 32 * 2;  // one MFMA
   return per * kChains * 4.0 /* waves */ * (double)grid * (double)iters;
+}
+
+int32_t abla_probe_stream(int32_t copy, const void* src, void* dst, int64_t bytes, void* stream) {
+  const long long span = kStreamSpan * 16;
+  if (!src || !dst || bytes < span || bytes % span || bytes / span > 0x7fffffffLL || (copy != 0 && copy != 1))
+    return 1;
+  if ((reinterpret_cast<uintptr_t>(src) | reinterpret_cast<uintptr_t>(dst)) & 15u) return 1;
+  const dim3 grid((unsigned)(bytes / span));
+  if (copy)
+    k_stream<true><<<grid, 256, 0, (hipStream_t)stream>>>(static_cast<const uint4*>(src), static_cast<uint4*>(dst));
+  else
+    k_stream<false><<<grid, 256, 0, (hipStream_t)stream>>>(static_cast<const uint4*>(src), static_cast<uint4*>(dst));
+  return hipGetLastError() == hipSuccess ? 0 : 4;
 }
 
 }  // extern "C"

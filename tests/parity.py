@@ -11,7 +11,9 @@ bf16 for the products (relative error <= 2^-9 each) and the results to bf16 (ano
 2^-9): about 2e-3 in relative L2 for sums of many terms, so 1e-2 leaves a 5x margin.
 """
 import dataclasses
+import json
 import math
+import os
 
 import numpy as np
 import torch
@@ -44,6 +46,16 @@ class MaskReport:
     exempt_diff: int
     kept: int
     total: int
+    band: int = 0  # blocks inside the band (where a difference would be allowed)
+
+
+def record(**fields):
+    """Append one JSON line of parity statistics to the file ABLA_PARITY_RECORDS names (if any)."""
+    path = os.environ.get("ABLA_PARITY_RECORDS")
+    if not path:
+        return
+    with open(path, "a") as f:
+        f.write(json.dumps(fields) + "\n")
 
 
 def check_mask(words, counts, lists, mres: R.MaskResult, prm: R.MaskParams, og: R.Geom, heads=None) -> MaskReport:
@@ -76,7 +88,7 @@ def check_mask(words, counts, lists, mres: R.MaskResult, prm: R.MaskParams, og: 
         for idx in np.ndindex(gm.shape[:-1]):
             n = c[idx]
             assert np.array_equal(L[idx][:n], np.nonzero(gm[idx])[0]), idx
-    return MaskReport(int(diff.sum()), int((diff & ex).sum()), int(gm.sum()), int(gm.size))
+    return MaskReport(int(diff.sum()), int((diff & ex).sum()), int(gm.sum()), int(gm.size), int(ex.sum()))
 
 
 def gpu_mask(words, og: R.Geom) -> np.ndarray:

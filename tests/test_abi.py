@@ -294,7 +294,7 @@ def test_probe_library_exports():
     path = os.path.join(ROOT, "block_sparse_attention_21_amd", "libabla_probe.so")
     with open(os.path.join(ROOT, "include", "abla_probe.h")) as f:
         names = sorted(set(re.findall(r"^\s*(?:int32_t|double)\s+(abla_[a-z_0-9]+)\s*\(", f.read(), re.MULTILINE)))
-    assert names == ["abla_probe_mfma", "abla_probe_mfma_flops"]
+    assert names == ["abla_probe_mfma", "abla_probe_mfma_flops", "abla_probe_stream"]
     lib = ctypes.CDLL(path)
     for n in names:
         assert hasattr(lib, n), n
@@ -307,3 +307,11 @@ def test_probe_library_exports():
     assert lib.abla_probe_mfma(0, 1, 1, None, None) == 1
     assert lib.abla_probe_mfma_flops(0, 1, 1) == 2.0 * 32 * 32 * 16 * 16
     assert lib.abla_probe_mfma_flops(1, 2, 3) == 2.0 * 32 * 32 * 2 * 16 * 6
+    lib.abla_probe_stream.restype = ctypes.c_int32
+    lib.abla_probe_stream.argtypes = [ctypes.c_int32, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int64,
+                                      ctypes.c_void_p]
+    assert lib.abla_probe_stream(0, None, FAKE2, 1 << 20, None) == 1
+    assert lib.abla_probe_stream(1, FAKE, FAKE2, (1 << 20) + 16, None) == 1
+    assert lib.abla_probe_stream(1, FAKE, FAKE2, 1 << 14, None) == 1
+    assert lib.abla_probe_stream(2, FAKE, FAKE2, 1 << 20, None) == 1
+    assert lib.abla_probe_stream(0, ctypes.c_void_p(0x10008), FAKE2, 1 << 20, None) == 1

@@ -306,7 +306,11 @@ def _head_arrays(og, q, k, v, h):
     return gh, Qr, Kr, Vr
 
 
-def _check_blocks(og, q, k, v, run, picks, dtype):
+def _keep_per_head(run, og):
+    return [round(float(x), 5) for x in (run.counts.double().sum(-1) / (og.nb * og.nb)).flatten().tolist()]
+
+
+def _check_blocks(og, q, k, v, run, picks, dtype, lse_err=None):
     """Attention of the chosen query blocks ({head: [blocks]}) against the oracle on the GPU's
     own mask (only the kept key blocks, masked_attention_blocks); output in the original order,
     LSE in fractal order."""
@@ -323,6 +327,8 @@ def _check_blocks(og, q, k, v, run, picks, dtype):
         assert np.array_equal(np.isneginf(lse_gpu), np.isneginf(lse_ref))
         fin = np.isfinite(lse_ref)
         np.testing.assert_allclose(lse_gpu[fin], lse_ref[fin], rtol=0, atol=2e-3 if dtype == "bf16" else 1e-4)
+        if lse_err is not None and fin.any():
+            lse_err.append(float(np.abs(lse_gpu[fin] - lse_ref[fin]).max()))
         gpu_all.append(O_gpu)
         ref_all.append(O_ref)
     return PT.compare_attention(np.concatenate(gpu_all), np.concatenate(ref_all), dtype)
@@ -362,6 +368,10 @@ def test_workload_tiny(A):
     assert rep.diff == 0
     ref = R.nabla_attention(q, k, v, og, op, block_mask=PT.gpu_mask(run.words, og))
     max_abs, rel = PT.compare_attention(run.out.cpu().numpy(), ref.O, "f32")
+    lse_err = float(np.abs(run.lse.cpu().numpy() - ref.lse_r).max())
+    PT.record(workload="tiny", dtype="f32", keep=rep.kept / rep.total, keep_per_head=_keep_per_head(run, og),
+              mask_bits=rep.total, mask_diff=rep.diff, band_blocks=rep.band, band_diff=rep.exempt_diff,
+              rows_compared=og.B * og.H * og.N, max_abs=max_abs, rel_l2=rel, lse_max_abs=lse_err)
     print(f"tiny: keep {rep.kept / rep.total:.4f}, max|dO| {max_abs:.2e}")
 
 
@@ -380,8 +390,12 @@ def test_workload_full_size(A, name):
         picks[og.H - 1] = list(range(og.nb))
     else:
         picks = _frame_picks(og, run, all_heads=(name == "720p"))
-    max_abs, rel = _check_blocks(og, q, k, v, run, picks, w.dtype)
+    lse_err = []
+    max_abs, rel = _check_blocks(og, q, k, v, run, picks, w.dtype, lse_err)
     n_rows = sum(len(b) for b in picks.values()) * og.bs
+    PT.record(workload=name, dtype=w.dtype, keep=rep.kept / rep.total, keep_per_head=_keep_per_head(run, og),
+              mask_bits=rep.total, mask_diff=rep.diff, band_blocks=rep.band, band_diff=rep.exempt_diff,
+              rows_compared=n_rows, max_abs=max_abs, rel_l2=rel, lse_max_abs=max(lse_err))
     print(f"{name}: keep {rep.kept / rep.total:.4f}, band diffs {rep.exempt_diff}, {n_rows} rows compared, "
           f"max|dO| {max_abs:.2e}, rel {rel:.2e}")
 
@@ -553,6 +567,9 @@ def test_static_masks_bit_exact(A, name, over):
 def test_dyn_tau_sweep_masks(A, tau):
     w, geom, og, prm, q, k, v, run = _workload(A, "480p-dyn", tau=tau)
     mres, rep = _check_workload_mask(A, w, og, prm, q, k, run)
+    PT.record(workload=f"480p-dyn tau={tau}", dtype=w.dtype, keep=rep.kept / rep.total,
+              keep_per_head=_keep_per_head(run, og), mask_bits=rep.total, mask_diff=rep.diff, band_blocks=rep.band,
+              band_diff=rep.exempt_diff)
     print(f"480p-dyn tau={tau}: keep {rep.kept / rep.total:.4f}, band diffs {rep.exempt_diff}")
 
 
