@@ -262,22 +262,39 @@ __device__ __forceinline__ float tile_probs(const f32x16_t (&s)[2], float c2, fl
 // O^T += V^T P^T for one staged V^T tile. vlds[kk]: this lane's byte offset of its 8-key
 // chunk kk of channel row (lane & 31) inside a slot; channel tile dt is 32 rows further.
 // With VT the slot holds a token-major V tile laid out like a K tile (key rows in kperm
-// order, chunk-swizzled) and the V^T operand comes from two LDS transpose loads.
+// order, chunk-swizzled with kt_swz) and the V^T operand comes from two LDS transpose loads
+// per channel tile: vlds[2*dt], vlds[2*dt + 1] are their LDS addresses for keys 0..15 of V
+// slot 0, and keys 16*kk of slot SLOT sit a constant offset further. The transpose loads go
+// through tr_chunks_at (the wait inside the asm block), so they do not make the compiler wait
+// for the next tiles' loads, which fill the other slots.
 template <int D, int SLOT, bool VT>
 __device__ __forceinline__ void tile_values(const char* smem, const uint32_t* vlds, const bf16x8_t (&pb)[4],
                                             f32x16_t* o) {
-  const int lane = threadIdx.x & 63;
+  if constexpr (VT) {
+    constexpr int DT = D / 32;
+    constexpr int S = Lds<D>::vslot(SLOT) - Lds<D>::vslot(0);
 #pragma unroll
-  for (int kk = 0; kk < 4; ++kk)
+    for (int kk = 0; kk < 4; ++kk) {
+      bf16x8_t vv[DT];
+      switch (kk) {  // the offset is an immediate of the transpose loads
+        case 0: tr_chunks_at<DT, S>(vlds, vv); break;
+        case 1: tr_chunks_at<DT, S + 16 * D * 2>(vlds, vv); break;
+        case 2: tr_chunks_at<DT, S + 32 * D * 2>(vlds, vv); break;
+        default: tr_chunks_at<DT, S + 48 * D * 2>(vlds, vv); break;
+      }
 #pragma unroll
-    for (int dt = 0; dt < D / 32; ++dt) {
-      bf16x8_t vv;
-      if constexpr (VT)
-        vv = tr_chunk<D>(smem + Lds<D>::vslot(SLOT), dt, 16 * kk, lane);
-      else
-        vv = *reinterpret_cast<const bf16x8_t*>(smem + Lds<D>::vslot(SLOT) + dt * 32 * kBlock * 2 + vlds[kk]);
-      o[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vv, pb[kk], o[dt], 0, 0, 0);
+      for (int dt = 0; dt < DT; ++dt) o[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vv[dt], pb[kk], o[dt], 0, 0, 0);
     }
+  } else {
+#pragma unroll
+    for (int kk = 0; kk < 4; ++kk)
+#pragma unroll
+      for (int dt = 0; dt < D / 32; ++dt) {
+        const bf16x8_t vv =
+            *reinterpret_cast<const bf16x8_t*>(smem + Lds<D>::vslot(SLOT) + dt * 32 * kBlock * 2 + vlds[kk]);
+        o[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vv, pb[kk], o[dt], 0, 0, 0);
+      }
+  }
 }
 
 // Raise the running maximum when a tile's maximum exceeds it by more than 2^8 (log2 units).
@@ -316,12 +333,12 @@ __device__ __forceinline__ void schedule_phase_a() {
 template <int D, bool VT>
 __device__ __forceinline__ void schedule_phase_b() {
   constexpr int NPV = 4 * (D / 32);
-  constexpr int RD = VT ? 2 : 1;  // LDS reads per value MFMA (two transpose loads, or one chunk)
-  __builtin_amdgcn_sched_group_barrier(0x100, 4 * RD, 0);
+  constexpr int RD = VT ? 0 : 1;  // LDS reads per value MFMA (the transpose loads are asm blocks)
+  if constexpr (RD) __builtin_amdgcn_sched_group_barrier(0x100, 4 * RD, 0);
 #pragma unroll
   for (int i = 0; i < NPV; ++i) {
     __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-    __builtin_amdgcn_sched_group_barrier(0x100, RD, 0);
+    if constexpr (RD) __builtin_amdgcn_sched_group_barrier(0x100, RD, 0);
     __builtin_amdgcn_sched_group_barrier(0x402, 2, 0);
   }
 }
@@ -452,7 +469,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
 
   // Per-thread global byte offsets of its 16-byte tile loads, and per-lane LDS byte
   // offsets of its MFMA operand chunks (both the same for every tile).
-  uint32_t klds[D / 16], vlds[4];
+  uint32_t klds[D / 16], vlds[VT ? 2 * (D / 32) : 4];
   // K: LDS row r of a tile holds key kperm(r) of the block; in the original order that key
   // sits (kperm(r) / 8) rows of Ws tokens and kperm(r) % 8 tokens past the block's corner.
   const int kr = kperm(t / TT::KCH);
@@ -462,14 +479,24 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
   // V: channel-major V^T blocks, or with VT a token-major tile of the original-order V loaded
   // exactly like a K tile in the original order.
   const uint32_t voff = VT ? (uint32_t)((kr >> 3) * g.Ws + (kr & 7)) * (uint32_t)(D * 2) +
-                                 (uint32_t)(((t % TT::KCH) ^ k_swz<D>(t / TT::KCH)) * 16)
+                                 (uint32_t)(((t % TT::KCH) ^ kt_swz<D>(t / TT::KCH)) * 16)
                            : (uint32_t)((t >> 3) * kBlock * 2 + (((t & 7) ^ v_swz(t >> 3)) * 16));
   {
     const int r0 = lane & 31;  // rows r0 and r0 + 32 share the swizzle
 #pragma unroll
     for (int ks = 0; ks < D / 16; ++ks) klds[ks] = (uint32_t)(r0 * D * 2 + (((ks * 2 + hi) ^ k_swz<D>(r0)) * 16));
+    if constexpr (VT) {
+      const uint32_t vbase = lds_offset(smem + Lds<D>::vslot(0));
 #pragma unroll
-    for (int kk = 0; kk < 4; ++kk) vlds[kk] = (uint32_t)(r0 * kBlock * 2 + (((2 * kk + hi) ^ v_swz(r0)) * 16));
+      for (int dt = 0; dt < D / 32; ++dt) {
+        tr_rel<D>(dt, 0, lane, vlds[2 * dt], vlds[2 * dt + 1]);
+        vlds[2 * dt] += vbase;
+        vlds[2 * dt + 1] += vbase;
+      }
+    } else {
+#pragma unroll
+      for (int kk = 0; kk < 4; ++kk) vlds[kk] = (uint32_t)(r0 * kBlock * 2 + (((2 * kk + hi) ^ v_swz(r0)) * 16));
+    }
   }
   // One resource per head: K and V^T of head bh are each N*D*2 bytes, at most 64 MiB
   // (nb <= 4096 blocks of 64 tokens, d <= 128), so 32-bit offsets cover them.

@@ -137,14 +137,18 @@ typedef __attribute__((address_space(3))) i16x4_t* lds_i16x4_ptr;
 // element e. So lane m of a group names token tb + 8*hi + 4*half + m/4, channels
 // c0 + 4*(m%4) .. +3 (c0 = dt*32 + 16*(group&1)), and lane i then holds channel c0 + i of four
 // consecutive tokens; two such reads give the 8 tokens.
-template <int D>
+// KT: the tile is laid out with kt_swz (conflict-free for transpose reads), else with k_swz.
+template <int D, bool KT = false>
 __device__ __forceinline__ bf16x8_t tr_chunk(const char* tile, int dt, int tb, int lane) {
   const int g = lane >> 4, m = lane & 15;
   const int ch = dt * 32 + 16 * (g & 1) + 4 * (m & 3);
-  const int tok = tb + 8 * (g >> 1) + (m >> 2);
+  // tb is a multiple of 16 and kperm and both swizzles repeat every 16 rows, so the lane's part
+  // of the address is formed from its row within the 16 and tb only adds a constant.
+  const int tok = 8 * (g >> 1) + (m >> 2);
   const int r0 = kperm(tok), r1 = kperm(tok + 4);
-  const char* p0 = tile + r0 * D * 2 + (((ch >> 3) ^ k_swz<D>(r0)) << 4) + (ch & 7) * 2;
-  const char* p1 = tile + r1 * D * 2 + (((ch >> 3) ^ k_swz<D>(r1)) << 4) + (ch & 7) * 2;
+  const int s0 = KT ? kt_swz<D>(r0) : k_swz<D>(r0), s1 = KT ? kt_swz<D>(r1) : k_swz<D>(r1);
+  const char* p0 = tile + (tb + r0) * D * 2 + (((ch >> 3) ^ s0) << 4) + (ch & 7) * 2;
+  const char* p1 = tile + (tb + r1) * D * 2 + (((ch >> 3) ^ s1) << 4) + (ch & 7) * 2;
   const i16x4_t a = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4_ptr)p0);
   const i16x4_t b = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4_ptr)p1);
   const i16x4_t both[2] = {a, b};
@@ -175,7 +179,7 @@ __device__ __forceinline__ void tr_rel(int dt, int tb, int lane, uint32_t& a0, u
   a0 = (uint32_t)(r0 * D * 2 + (((ch >> 3) ^ kt_swz<D>(r0)) << 4) + (ch & 7) * 2);
   a1 = (uint32_t)(r1 * D * 2 + (((ch >> 3) ^ kt_swz<D>(r1)) << 4) + (ch & 7) * 2);
 }
-// out[k] = tr_chunk<D>(tile, k, tb, lane) for the NT = D/32 channel tiles, where a[2k], a[2k+1]
+// out[k] = tr_chunk<D, true>(tile, k, tb, lane) for the NT = D/32 channel tiles, where a[2k], a[2k+1]
 // are the LDS addresses of tile + tr_rel(k, tb0, lane) and the tile / token block differs from
 // (tile, tb0) by the constant byte offset OFF. Tokens tb0 + 16*n keep the same swizzle (it
 // repeats every 16 rows), so OFF = 16*n*D*2 (plus a slot distance) is exact.
