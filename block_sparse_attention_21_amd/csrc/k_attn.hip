@@ -21,8 +21,9 @@
 //                 4-7 and 8-11 of every 16 swapped, so each V^T read is one chunk.
 // Software pipeline: K tiles run one step ahead of V^T tiles (two LDS slots each),
 // so while a wave turns the scores of tile u into probabilities it already runs
-// the score MFMAs of tile u+1, and the value MFMAs of tile u run under the
-// maximum of tile u+1 (an explicit MFMA / LDS-read / VALU interleave). One barrier
+// the score MFMAs of tile u+1 (an explicit MFMA / LDS-read / VALU interleave). The
+// probabilities use the running maximum of the earlier tiles; only when a lane's sum
+// of them exceeds 256 is the tile's own maximum taken and the row rebased. One barrier
 // per step. Tiles move global -> LDS directly (buffer_load ... lds), with a per-row
 // XOR swizzle of 16-byte chunks so the MFMA operand reads are free of bank
 // conflicts. The visiting order of the pairs (k_pair_order) depends on the list
@@ -87,9 +88,13 @@ __device__ __forceinline__ uint32_t k_tile_stride(const KGeom& g) {
   return ORIG ? 512u * (uint32_t)g.Ws : 4096u;
 }
 
-// Rescale the running output only when a row maximum grows by more than 2^8 in the
-// exponent; below that the stale maximum keeps every probability <= 256.
-constexpr float kRescaleLog2 = 8.0f;
+// Probabilities are formed against the running maximum of the tiles before (no per-tile
+// maximum). A tile is accepted as long as each lane's sum of its 32 probabilities stays
+// <= 256, which bounds every probability by 256 (fp32 and bf16 hold that without loss of
+// relative precision, and 256 * 64 keys * #tiles stays far from overflow); otherwise (the
+// first tile, or a maximum that grew by about 2^5 or more) the tile's maximum is taken, the
+// running state rescaled and the probabilities formed again.
+constexpr float kProbSumBound = 256.0f;
 
 // Attention workgroups resident on one XCD at a time: 32 CUs (MI355X: 256 CUs in 8 XCDs),
 // two 4-wave workgroups per CU.
@@ -246,6 +251,9 @@ __device__ __forceinline__ float tile_max(const f32x16_t (&s)[2]) {
 
 // Probabilities exp2(c2*s - m) rounded to bf16 in the V^T-operand order; returns their
 // float32 sum over this lane's 32 keys (four partial sums, no long dependency chain).
+// (Summing the bf16-rounded values instead, with bf16 pair dot products, saves 16 adds
+// per tile but moves the log-sum-exp by up to 2^-8; it measured within the run-to-run
+// spread, so the float32 sum stays.)
 __device__ __forceinline__ float tile_probs(const f32x16_t (&s)[2], float c2, float m, bf16x8_t (&pb)[4]) {
   float ps[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
@@ -297,26 +305,27 @@ __device__ __forceinline__ void tile_values(const char* smem, const uint32_t* vl
   }
 }
 
-// Raise the running maximum when a tile's maximum exceeds it by more than 2^8 (log2 units).
+// Rebase on tile s: the running maximum becomes max(m_run, tile maximum), the running sum
+// and output are rescaled to it and the probabilities formed again (all <= 1 now); returns
+// their sum. Wave-uniform (called under a ballot).
 template <int D>
-__device__ __forceinline__ void raise_max(float mx_raw, float c2, float& m_run, float& l_run, f32x16_t* o) {
-  const float mx = mx_raw * c2;
-  if (__builtin_amdgcn_ballot_w64(mx > m_run + kRescaleLog2)) {
-    const float m_new = fmaxf(m_run, mx);
-    const float alpha = exp2_fast(m_run - m_new);
-    m_run = m_new;
-    l_run *= alpha;
+__device__ __forceinline__ float rebase_tile(const f32x16_t (&s)[2], float c2, float& m_run, float& l_run, f32x16_t* o,
+                                          bf16x8_t (&pb)[4]) {
+  const float m_new = fmaxf(m_run, tile_max(s) * c2);
+  const float alpha = exp2_fast(m_run - m_new);  // 0 on the first tile (m_run = -inf)
+  m_run = m_new;
+  l_run *= alpha;
 #pragma unroll
-    for (int dt = 0; dt < D / 32; ++dt)
+  for (int dt = 0; dt < D / 32; ++dt)
 #pragma unroll
-      for (int r = 0; r < 16; ++r) o[dt][r] *= alpha;
-  }
+    for (int r = 0; r < 16; ++r) o[dt][r] *= alpha;
+  return tile_probs(s, c2, m_run, pb);
 }
 
 // Instruction interleave of the steady state, in two scheduling regions. Phase A: the
 // next tile's score MFMAs run under this tile's exp/convert/sum work and the step's tile
-// loads. Phase B: the value MFMAs run under the next tile's maximum. Masks: 0x008 MFMA,
-// 0x100 LDS read, 0x402 VALU or transcendental, 0x010 vector memory.
+// loads. Phase B: the value MFMAs and their LDS reads. Masks: 0x008 MFMA, 0x100 LDS read,
+// 0x402 VALU or transcendental, 0x010 vector memory.
 template <int D>
 __device__ __forceinline__ void schedule_phase_a() {
   constexpr int NS = 2 * (D / 16);
@@ -339,7 +348,6 @@ __device__ __forceinline__ void schedule_phase_b() {
   for (int i = 0; i < NPV; ++i) {
     __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
     if constexpr (RD) __builtin_amdgcn_sched_group_barrier(0x100, RD, 0);
-    __builtin_amdgcn_sched_group_barrier(0x402, 2, 0);
   }
 }
 
@@ -351,7 +359,7 @@ struct Walk {
 // One step of the schedule at position u, whose K/V^T slots have parity P:
 //   K(u) in K slot P (already consumed), K(u+1) in K slot P^1, V(u) in V slot P.
 // Issues K(u+2) into K slot P and V(u+1) into V slot P^1, then, for this wave's block,
-// finishes tile u (probabilities, values) and starts tile u+1 (scores, maximum).
+// finishes tile u (probabilities, values) and starts tile u+1 (scores).
 // sc holds S(u) if the block keeps u; sn receives S(u+1).
 template <int D, int P, bool QKO, bool VT>
 __device__ __forceinline__ void walk_step(const AttnArgs& a, char* smem, const uint16_t* sched, Walk& wk, int mine,
@@ -387,24 +395,23 @@ __device__ __forceinline__ void walk_step(const AttnArgs& a, char* smem, const u
     // measured 3-8% faster than equal priorities.
     __builtin_amdgcn_s_setprio(1);
     tile_scores<D, P ^ 1, true>(smem, klds, qv, sn, &ld);
-    const float psum = tile_probs(sc, c2, m_run, pb);
+    float psum = tile_probs(sc, c2, m_run, pb);
     schedule_phase_a<D>();
     __builtin_amdgcn_s_setprio(0);
+    if (__builtin_amdgcn_ballot_w64(!(psum <= kProbSumBound))) psum = rebase_tile<D>(sc, c2, m_run, l_run, o, pb);
     tile_values<D, P, VT>(smem, vlds, pb, o);
-    const float mx = tile_max(sn);
     schedule_phase_b<D, VT>();
     __builtin_amdgcn_s_setprio(0);  // no-op for priority; closes phase B's scheduling region
     l_run += psum;
-    raise_max<D>(mx, c2, m_run, l_run, o);
   } else if (mc) {
     ld.load_all();
     bf16x8_t pb[4];
-    const float psum = tile_probs(sc, c2, m_run, pb);
+    float psum = tile_probs(sc, c2, m_run, pb);
+    if (__builtin_amdgcn_ballot_w64(!(psum <= kProbSumBound))) psum = rebase_tile<D>(sc, c2, m_run, l_run, o, pb);
     tile_values<D, P, VT>(smem, vlds, pb, o);
     l_run += psum;
   } else if (mn) {
     tile_scores<D, P ^ 1, true>(smem, klds, qv, sn, &ld);
-    raise_max<D>(tile_max(sn), c2, m_run, l_run, o);
   } else {
     ld.load_all();
   }
@@ -529,10 +536,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
       issue_rows<TT::KBYTES>(smem + Lds<D>::kslot(1), w, krs, k_tile_base<D, QKO>(wk.en & kSchedJ, a), koff,
                              kstride);
     wait_vm_lgkm_barrier();
-    if (wk.ec & mine) {
-      tile_scores<D, 0, false>(smem, klds, qv, s0, nullptr);
-      raise_max<D>(tile_max(s0), a.c2, m_run, l_run, o);
-    }
+    if (wk.ec & mine) tile_scores<D, 0, false>(smem, klds, qv, s0, nullptr);
     while (true) {
       walk_step<D, 0, QKO, VT>(a, smem, sched, wk, mine, w, krs, vrs, koff, voff, klds, vlds, qv, a.c2, s0, s1, o,
                            m_run, l_run);
