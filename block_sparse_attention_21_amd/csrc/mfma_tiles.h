@@ -130,34 +130,17 @@ __device__ __forceinline__ void issue_rows(char* dst_slot, int w, i32x4_t rsrc, 
 typedef short i16x4_t __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) i16x4_t* lds_i16x4_ptr;
 
-// A-operand chunk of the TRANSPOSE of a token-major tile X, read with the gfx950 LDS transpose
-// load: lane l receives X^T[dt*32 + l%32][tb + 8*(l/32) + e], e = 0..7, i.e. 8 consecutive
-// tokens of one channel. ds_read_tr16_b64 works on groups of 16 lanes: each lane names 8 bytes
-// (4 bf16) and lane i of the group receives element i%4 of the read named by lane 4e + i/4 as its
-// element e. So lane m of a group names token tb + 8*hi + 4*half + m/4, channels
-// c0 + 4*(m%4) .. +3 (c0 = dt*32 + 16*(group&1)), and lane i then holds channel c0 + i of four
-// consecutive tokens; two such reads give the 8 tokens.
-// KT: the tile is laid out with kt_swz (conflict-free for transpose reads), else with k_swz.
-template <int D, bool KT = false>
-__device__ __forceinline__ bf16x8_t tr_chunk(const char* tile, int dt, int tb, int lane) {
-  const int g = lane >> 4, m = lane & 15;
-  const int ch = dt * 32 + 16 * (g & 1) + 4 * (m & 3);
-  // tb is a multiple of 16 and kperm and both swizzles repeat every 16 rows, so the lane's part
-  // of the address is formed from its row within the 16 and tb only adds a constant.
-  const int tok = 8 * (g >> 1) + (m >> 2);
-  const int r0 = kperm(tok), r1 = kperm(tok + 4);
-  const int s0 = KT ? kt_swz<D>(r0) : k_swz<D>(r0), s1 = KT ? kt_swz<D>(r1) : k_swz<D>(r1);
-  const char* p0 = tile + (tb + r0) * D * 2 + (((ch >> 3) ^ s0) << 4) + (ch & 7) * 2;
-  const char* p1 = tile + (tb + r1) * D * 2 + (((ch >> 3) ^ s1) << 4) + (ch & 7) * 2;
-  const i16x4_t a = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4_ptr)p0);
-  const i16x4_t b = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4_ptr)p1);
-  const i16x4_t both[2] = {a, b};
-  bf16x8_t out;
-  __builtin_memcpy(&out, both, 16);
-  return out;
-}
-
-// The same operands through inline asm, with the wait inside the block. The compiler's
+// Transposed operands. The A operand of a product over the TRANSPOSE of a token-major tile X
+// (channel rows, token columns) is read with the gfx950 LDS transpose load: lane l needs
+// X^T[dt*32 + l%32][tb + 8*(l/32) + e], e = 0..7, i.e. 8 consecutive tokens of one channel.
+// ds_read_b64_tr_b16 works on groups of 16 lanes: each lane names 8 bytes (4 bf16) and lane i
+// of the group receives element i%4 of the read named by lane 4e + i/4 as its element e. So
+// lane m of a group names token tb + 8*hi + 4*half + m/4, channels c0 + 4*(m%4) .. +3
+// (c0 = dt*32 + 16*(group&1)), and lane i then holds channel c0 + i of four consecutive
+// tokens; two such reads give the 8 tokens (established with an in-bounds probe). Tiles read
+// this way are laid out with kt_swz.
+//
+// The transpose reads go through inline asm, with the wait inside the block. The compiler's
 // wait-count pass does not prove that a ds_read_b64_tr_b16 builtin misses the LDS slot that
 // the next tile's buffer_load ... lds is filling, so before the first builtin transpose load
 // of a step it waits for every load in flight (vmcnt(0)), which stalls the next tile's
@@ -168,8 +151,8 @@ __device__ __forceinline__ uint32_t lds_offset(const char* p) {
   return (uint32_t)(uintptr_t)((const __attribute__((address_space(3))) char*)p);
 }
 // Byte offsets, relative to a token-major tile laid out with kt_swz, of the two 8-byte
-// transpose reads that give lane `lane` its operand (as tr_chunk) for channel tile dt and tokens
-// tb + 8*(lane/32) + 0..7.
+// transpose reads that give lane `lane` its operand for channel tile dt and tokens
+// tb + 8*(lane/32) + 0..7 (the layout above).
 template <int D>
 __device__ __forceinline__ void tr_rel(int dt, int tb, int lane, uint32_t& a0, uint32_t& a1) {
   const int g = lane >> 4, m = lane & 15;
@@ -179,8 +162,9 @@ __device__ __forceinline__ void tr_rel(int dt, int tb, int lane, uint32_t& a0, u
   a0 = (uint32_t)(r0 * D * 2 + (((ch >> 3) ^ kt_swz<D>(r0)) << 4) + (ch & 7) * 2);
   a1 = (uint32_t)(r1 * D * 2 + (((ch >> 3) ^ kt_swz<D>(r1)) << 4) + (ch & 7) * 2);
 }
-// out[k] = tr_chunk<D, true>(tile, k, tb, lane) for the NT = D/32 channel tiles, where a[2k], a[2k+1]
-// are the LDS addresses of tile + tr_rel(k, tb0, lane) and the tile / token block differs from
+// out[k] = the transposed operand of channel tile k (tokens tb .. of the tile), for the NT = D/32
+// channel tiles, where a[2k], a[2k+1] are the LDS addresses of tile + tr_rel(k, tb0, lane) and the
+// tile / token block differs from
 // (tile, tb0) by the constant byte offset OFF. Tokens tb0 + 16*n keep the same swizzle (it
 // repeats every 16 rows), so OFF = 16*n*D*2 (plus a slot distance) is exact.
 template <int NT, int OFF>
