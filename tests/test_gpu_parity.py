@@ -139,6 +139,52 @@ def test_small_end_to_end(A, case):
     print(f"{name}: kept {rep.kept}/{rep.total}, band diffs {rep.exempt_diff}, max|dO| {max_abs:.2e}, rel {rel:.2e}")
 
 
+# ---------------------------------------------------------------- running maximum across tiles
+def _ramp_qkv(order, d, fuse_seed=11):
+    """Q and K whose scores grow (or fall, or jump) by about 6 nats from one key block to the
+    next in the walk order: every key of block j is a_j * u plus noise and every query c * u plus
+    noise, with a_j from `order`; V i.i.d. normal. bf16, B = 1, H = 2, 2 x 32 x 32 tokens."""
+    B, H, T, Hs, Ws = 1, 2, 2, 32, 32
+    g = torch.Generator().manual_seed(fuse_seed)
+    N = T * Hs * Ws
+    t, y, x = np.meshgrid(np.arange(T), np.arange(Hs), np.arange(Ws), indexing="ij")
+    blk = ((t * (Hs // 8) + y // 8) * (Ws // 8) + x // 8).reshape(-1)  # key block of each token
+    a = torch.tensor(np.asarray(order, dtype=np.float64)[blk], dtype=torch.float32)
+    u = torch.randn((H, 1, d), generator=g)
+    c = 6.0 * math.sqrt(d) / (u * u).sum(-1, keepdim=True)  # c * |u|^2 / sqrt(d) = 6 nats per unit of a_j
+    q = (c * u + 0.3 * torch.randn((H, N, d), generator=g)).unsqueeze(0)
+    k = (a[None, :, None] * u + 0.3 * torch.randn((H, N, d), generator=g)).unsqueeze(0)
+    v = torch.randn((B, H, N, d), generator=g)
+    return (B, H, T, Hs, Ws), q.to(torch.bfloat16).to(DEV), k.to(torch.bfloat16).to(DEV), v.to(torch.bfloat16).to(DEV)
+
+
+@pytest.mark.parametrize("fuse_v", [False, True], ids=["v-blocks", "v-original"])
+@pytest.mark.parametrize("shape", ["rising", "falling", "jumping"])
+def test_running_maximum_across_tiles(A, shape, fuse_v):
+    """Probabilities are formed against the running maximum of the earlier tiles and the row is
+    rebased when a tile's probabilities exceed it: with scores rising ~6 nats per key block
+    every tile rebases, falling only the first does, jumping mixes both; the row maxima reach
+    ~190 nats, so any missed rebase overflows. Every element against the oracle (full mask)."""
+    nb = 32
+    order = {"rising": np.arange(1, nb + 1), "falling": np.arange(nb, 0, -1),
+             "jumping": (np.arange(nb) * 7) % nb + 1}[shape]
+    for d in (64, 128):
+        geo, q, k, v = _ramp_qkv(order, d)
+        geom, og = PT.geoms(*geo, d)
+        prm = A.MaskParams(mode="cdf", thr=1.0)
+        run = A.NablaAttention(geom, prm, dtype=q.dtype, want_lse=True, fuse_v=fuse_v)
+        run(q, k, v)
+        torch.cuda.synchronize()
+        assert int(run.counts.min()) == nb
+        op = PT.oracle_params(prm)
+        ref = R.nabla_attention(q, k, v, og, op, block_mask=PT.gpu_mask(run.words, og))
+        assert np.isfinite(ref.lse_r).all() and ref.lse_r.max() > 150.0
+        max_abs, rel = PT.compare_attention(run.out.float().cpu().numpy(), ref.O, "bf16")
+        lse = run.lse.cpu().numpy()
+        np.testing.assert_allclose(lse, ref.lse_r, rtol=0, atol=2e-3)
+        print(f"{shape} d={d} fuse_v={fuse_v}: max|dO| {max_abs:.2e} rel {rel:.2e}, max lse {lse.max():.1f}")
+
+
 def test_empty_rows_give_zero(A):
     geom, og, prm, q, k, v, run = _run_small(A, "bf16", 128, (1, 2, 2, 16, 16), dict(mode="cdf", thr=0.0,
                                                                                      sta=(0, 0, 0)))
