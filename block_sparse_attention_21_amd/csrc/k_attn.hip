@@ -536,7 +536,10 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
       issue_rows<TT::KBYTES>(smem + Lds<D>::kslot(1), w, krs, k_tile_base<D, QKO>(wk.en & kSchedJ, a), koff,
                              kstride);
     wait_vm_lgkm_barrier();
-    if (wk.ec & mine) tile_scores<D, 0, false>(smem, klds, qv, s0, nullptr);
+    if (wk.ec & mine) {
+      tile_scores<D, 0, false>(smem, klds, qv, s0, nullptr);
+      m_run = tile_max(s0) * a.c2;  // the first tile's maximum, so its probabilities need no rebase
+    }
     while (true) {
       walk_step<D, 0, QKO, VT>(a, smem, sched, wk, mine, w, krs, vrs, koff, voff, klds, vlds, qv, a.c2, s0, s1, o,
                            m_run, l_run);
