@@ -123,8 +123,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void k
 }
 
 // ---------------------------------------------------------------- select
-constexpr int kSelThreads = 256;
-constexpr int kWaves = kSelThreads / 64;
+constexpr int kSelThreads = 256;  // threads per row for rows of more than 768 blocks
 
 struct SelArgs {
   int mode;        // ABLA_MASK_CDF / ABLA_MASK_DYN / ABLA_MASK_STATIC
@@ -182,15 +181,15 @@ struct Cut {
 
 constexpr int kDigitBits = 8;  // one bucket per thread: cheap clears and scans per pass
 constexpr int kBuckets = 1 << kDigitBits;
-constexpr int kBucketsPerThread = kBuckets / kSelThreads;
 
 constexpr int kDirect = 64;  // a selected bucket with at most this many keys is resolved directly
 
+template <int NT>
 struct RadixScratch {
   unsigned long long mass[kBuckets];
   unsigned int cnt[kBuckets];
-  unsigned long long part[kWaves];  // per-wave bucket-mass totals
-  unsigned long long cand_cum[kSelThreads];
+  unsigned long long part[NT / 64];  // per-wave bucket-mass totals
+  unsigned long long cand_cum[NT];
   unsigned long long cand[kDirect];  // keys of a small selected bucket
   int ncand;
   int bsel;
@@ -206,9 +205,11 @@ struct RadixScratch {
 // (a tie class: every bit fixed), or (rows of at most 1024 blocks) resolves a bucket of at most
 // kDirect keys by comparing them directly: rows of near-equal probabilities otherwise took
 // up to 7 passes. Every thread returns the same result.
-template <int NPT>
+template <int NT, int NPT>
 __device__ Cut radix_cut(const unsigned long long* key, int t, int nb, unsigned long long thr_fx,
-                         RadixScratch& rs) {
+                         RadixScratch<NT>& rs) {
+  constexpr int kWaves = NT / 64;
+  constexpr int kBucketsPerThread = kBuckets / NT;
   const int lane = t & 63, wv = t >> 6;
   // All keys of the row share the bits above the highest bit in which the largest and
   // the smallest key differ (sign and high exponent bits, typically): start the digits
@@ -216,7 +217,7 @@ __device__ Cut radix_cut(const unsigned long long* key, int t, int nb, unsigned 
   unsigned long long kmax = 0, kmin = ~0ull;
 #pragma unroll
   for (int k = 0; k < NPT; ++k)
-    if (t + kSelThreads * k < nb) {
+    if (t + NT * k < nb) {
       kmax = key[k] > kmax ? key[k] : kmax;
       kmin = key[k] < kmin ? key[k] : kmin;
     }
@@ -247,7 +248,7 @@ __device__ Cut radix_cut(const unsigned long long* key, int t, int nb, unsigned 
     const int db = shift >= kDigitBits ? kDigitBits : shift;
     shift -= db;
     const unsigned long long dmask = (1ull << db) - 1;
-    for (int b = t; b < kBuckets; b += kSelThreads) {
+    for (int b = t; b < kBuckets; b += NT) {
       rs.mass[b] = 0;
       rs.cnt[b] = 0;
     }
@@ -255,7 +256,7 @@ __device__ Cut radix_cut(const unsigned long long* key, int t, int nb, unsigned 
     __syncthreads();
 #pragma unroll
     for (int k = 0; k < NPT; ++k) {
-      if (t + kSelThreads * k < nb && (key[k] & pmask) == pval) {
+      if (t + NT * k < nb && (key[k] & pmask) == pval) {
         const int d = (int)((key[k] >> shift) & dmask);
         atomicAdd(&rs.mass[d], mass_fx(key[k]));
         atomicAdd(&rs.cnt[d], 1u);
@@ -302,14 +303,14 @@ __device__ Cut radix_cut(const unsigned long long* key, int t, int nb, unsigned 
     // Every bit fixed: the bucket is one key value held by n_in tied blocks.
     if (shift == 0) return Cut{pval, tie_kept(above, mass_fx(pval), n_in, thr_fx), n_in};
     if (n_in == 1) break;
-    if constexpr (NPT <= 4) {  // (the larger rows keep their occupancy: no extra registers)
+    if constexpr (NT * NPT <= 1024) {  // (the larger rows keep their occupancy: no extra registers)
       if (n_in <= kDirect) {
         // Few keys left in the bucket: K is the smallest among them whose mass above (the
         // bucket's `above` plus the larger keys of the bucket) is < thr_fx; the bucket's
         // largest key always qualifies. Then the blocks tied at K. Same answer as further passes.
 #pragma unroll
         for (int k = 0; k < NPT; ++k)
-          if (t + kSelThreads * k < nb && (key[k] & pmask) == pval) rs.cand[atomicAdd(&rs.ncand, 1)] = key[k];
+          if (t + NT * k < nb && (key[k] & pmask) == pval) rs.cand[atomicAdd(&rs.ncand, 1)] = key[k];
         if (t == 0) rs.found = ~0ull;
         __syncthreads();
         if (t < (int)n_in) {
@@ -339,7 +340,7 @@ __device__ Cut radix_cut(const unsigned long long* key, int t, int nb, unsigned 
   // The single key in the selected bucket.
 #pragma unroll
   for (int k = 0; k < NPT; ++k)
-    if (t + kSelThreads * k < nb && (key[k] & pmask) == pval) rs.found = key[k];
+    if (t + NT * k < nb && (key[k] & pmask) == pval) rs.found = key[k];
   __syncthreads();
   return Cut{rs.found, 1u, 1u};
 }
@@ -372,12 +373,13 @@ __device__ __forceinline__ int bit_rank(const uint32_t* bits, const int* pre, in
   return pre[j >> 5] + __popc(bits[j >> 5] & ((1u << (j & 31)) - 1u));
 }
 
-template <int NPT, bool BITONIC>
-__global__ __launch_bounds__(kSelThreads) void k_select(const double* __restrict__ S, uint32_t* __restrict__ words,
+template <int NT, int NPT, bool BITONIC>
+__global__ __launch_bounds__(NT) void k_select(const double* __restrict__ S, uint32_t* __restrict__ words,
                                                         int32_t* __restrict__ counts, int32_t* __restrict__ lists,
                                                         KGeom g, SelArgs a) {
-  constexpr int CAP = kSelThreads * NPT;
-  constexpr int KEYS_WORDS = (sizeof(RadixScratch) + 7) / 8 > CAP ? (sizeof(RadixScratch) + 7) / 8 : CAP;
+  constexpr int kWaves = NT / 64;
+  constexpr int CAP = NT * NPT;
+  constexpr int KEYS_WORDS = (sizeof(RadixScratch<NT>) + 7) / 8 > CAP ? (sizeof(RadixScratch<NT>) + 7) / 8 : CAP;
   __shared__ unsigned long long keys[KEYS_WORDS];  // bitonic keys, or the radix-select scratch
   __shared__ uint16_t idx[BITONIC ? CAP : 1];      // bitonic: the block index of each key
   __shared__ uint32_t wbits[CAP / 32];
@@ -399,7 +401,7 @@ __global__ __launch_bounds__(kSelThreads) void k_select(const double* __restrict
   double mx = -INFINITY;
 #pragma unroll
   for (int k = 0; k < NPT; ++k) {
-    const int j = t + kSelThreads * k;
+    const int j = t + NT * k;
     s[k] = (scored && j < nb) ? Srow[j] : -INFINITY;
     mx = fmax(mx, s[k]);
   }
@@ -422,7 +424,7 @@ __global__ __launch_bounds__(kSelThreads) void k_select(const double* __restrict
     int* kc_s = rank_s + F;
     const int ti = i / F, pi = i - ti * F;
     const int hi = pi / g.nbw, wi = pi - hi * g.nbw;
-    for (int p = t; p < F; p += kSelThreads) {
+    for (int p = t; p < F; p += NT) {
       const int hp = p / g.nbw, wp = p - hp * g.nbw;
       const int d2p = (hp - hi) * (hp - hi) + (wp - wi) * (wp - wi);
       int r = 0;
@@ -433,7 +435,7 @@ __global__ __launch_bounds__(kSelThreads) void k_select(const double* __restrict
       }
       rank_s[p] = r;
     }
-    for (int dt = t; dt < g.T; dt += kSelThreads) {
+    for (int dt = t; dt < g.T; dt += NT) {
       double ratio = 1.0;
       for (int k = 0; k < dt; ++k) ratio = ratio * a.gamma;  // the float64 products of the definition
       kc_s[dt] = min(F, max(a.floor_k, (int)ceil((double)F * ratio)));
@@ -441,7 +443,7 @@ __global__ __launch_bounds__(kSelThreads) void k_select(const double* __restrict
     __syncthreads();
 #pragma unroll
     for (int k = 0; k < NPT; ++k) {
-      const int j = t + kSelThreads * k;
+      const int j = t + NT * k;
       if (j < nb) {
         const int tj = j / F;
         keep[k] = rank_s[j - tj * F] < kc_s[abs(tj - ti)];
@@ -452,17 +454,17 @@ __global__ __launch_bounds__(kSelThreads) void k_select(const double* __restrict
   } else if (a.mode == ABLA_MASK_DYN) {
     const double edge = mx - a.tau;
 #pragma unroll
-    for (int k = 0; k < NPT; ++k) keep[k] = (t + kSelThreads * k < nb) && s[k] >= edge;
+    for (int k = 0; k < NPT; ++k) keep[k] = (t + NT * k < nb) && s[k] >= edge;
   } else if (a.cdf_all || a.cdf_none) {
 #pragma unroll
-    for (int k = 0; k < NPT; ++k) keep[k] = a.cdf_all && (t + kSelThreads * k < nb);
+    for (int k = 0; k < NPT; ++k) keep[k] = a.cdf_all && (t + NT * k < nb);
   } else {
     // Softmax of the row (max-shifted exponentials, fixed-order sum).
     double e[NPT];
     double z = 0.0;
 #pragma unroll
     for (int k = 0; k < NPT; ++k) {
-      e[k] = (t + kSelThreads * k < nb) ? exp(s[k] - mx) : 0.0;
+      e[k] = (t + NT * k < nb) ? exp(s[k] - mx) : 0.0;
       z += e[k];
     }
     z = wave_sum(z);
@@ -475,23 +477,23 @@ __global__ __launch_bounds__(kSelThreads) void k_select(const double* __restrict
     unsigned long long key[NPT];
 #pragma unroll
     for (int k = 0; k < NPT; ++k) {
-      const int j = t + kSelThreads * k;
+      const int j = t + NT * k;
       key[k] = j < nb ? make_key(e[k] / z) : 0ull;
     }
     if constexpr (!BITONIC) {
-      const Cut c = radix_cut<NPT>(key, t, nb, a.thr_fx, *reinterpret_cast<RadixScratch*>(keys));
+      const Cut c = radix_cut<NT, NPT>(key, t, nb, a.thr_fx, *reinterpret_cast<RadixScratch<NT>*>(keys));
       if (c.n_keep >= c.n_tie) {
 #pragma unroll
-        for (int k = 0; k < NPT; ++k) keep[k] = (t + kSelThreads * k < nb) && key[k] >= c.key;
+        for (int k = 0; k < NPT; ++k) keep[k] = (t + NT * k < nb) && key[k] >= c.key;
       } else {
         // Only some of the blocks tied at the cut's key are kept: the lowest indices. Rank the
         // tied blocks by index with a ballot per 64 consecutive blocks and a prefix of the
         // words' popcounts (the same layout as the packed mask below).
 #pragma unroll
         for (int k = 0; k < NPT; ++k) {
-          const unsigned long long b = __ballot((t + kSelThreads * k < nb) && key[k] == c.key);
+          const unsigned long long b = __ballot((t + NT * k < nb) && key[k] == c.key);
           if (lane == 0) {
-            const int w0 = (kSelThreads * k + 64 * wv) >> 5;
+            const int w0 = (NT * k + 64 * wv) >> 5;
             wbits[w0] = (uint32_t)b;
             wbits[w0 + 1] = (uint32_t)(b >> 32);
           }
@@ -501,7 +503,7 @@ __global__ __launch_bounds__(kSelThreads) void k_select(const double* __restrict
         __syncthreads();
 #pragma unroll
         for (int k = 0; k < NPT; ++k) {
-          const int j = t + kSelThreads * k;
+          const int j = t + NT * k;
           keep[k] = j < nb && (key[k] > c.key || (key[k] == c.key && bit_rank(wbits, wpre, j) < (int)c.n_keep));
         }
         __syncthreads();  // the packing below reuses the words
@@ -511,7 +513,7 @@ __global__ __launch_bounds__(kSelThreads) void k_select(const double* __restrict
       // Padding entries (key 0, index 0xffff) rank after every block.
 #pragma unroll
       for (int k = 0; k < NPT; ++k) {
-        const int j = t + kSelThreads * k;
+        const int j = t + NT * k;
         if (j < a.np) {
           keys[j] = key[k];
           idx[j] = (uint16_t)(j < nb ? j : 0xffff);
@@ -525,7 +527,7 @@ __global__ __launch_bounds__(kSelThreads) void k_select(const double* __restrict
       const int np = a.np;
       for (int size = 2; size <= np; size <<= 1) {
         for (int stride = size >> 1; stride > 0; stride >>= 1) {
-          for (int pidx = t; pidx < (np >> 1); pidx += kSelThreads) {
+          for (int pidx = t; pidx < (np >> 1); pidx += NT) {
             const int lo = ((pidx & ~(stride - 1)) << 1) | (pidx & (stride - 1));
             const int hi = lo + stride;
             const unsigned long long x = keys[lo], y = keys[hi];
@@ -544,7 +546,7 @@ __global__ __launch_bounds__(kSelThreads) void k_select(const double* __restrict
       }
 
       // Exclusive prefix sum of the sorted masses; thread t owns a contiguous segment.
-      const int seg = (np + kSelThreads - 1) / kSelThreads;
+      const int seg = (np + NT - 1) / NT;
       const int p0 = t * seg;
       unsigned long long local = 0;
       for (int q = 0; q < seg; ++q)
@@ -579,7 +581,7 @@ __global__ __launch_bounds__(kSelThreads) void k_select(const double* __restrict
       const int jstar = jstar_s;
 #pragma unroll
       for (int k = 0; k < NPT; ++k) {
-        const int j = t + kSelThreads * k;
+        const int j = t + NT * k;
         keep[k] = j < nb && (key[k] > kstar || (key[k] == kstar && j <= jstar));
       }
     }
@@ -591,7 +593,7 @@ __global__ __launch_bounds__(kSelThreads) void k_select(const double* __restrict
     const int ti = i / per_frame, hi = (i % per_frame) / g.nbw, wi = i % g.nbw;
 #pragma unroll
     for (int k = 0; k < NPT; ++k) {
-      const int j = t + kSelThreads * k;
+      const int j = t + NT * k;
       const int tj = j / per_frame, hj = (j % per_frame) / g.nbw, wj = j % g.nbw;
       keep[k] = keep[k] || (j < nb && abs(tj - ti) <= a.rt && abs(hj - hi) <= a.rh && abs(wj - wi) <= a.rw);
     }
@@ -602,7 +604,7 @@ __global__ __launch_bounds__(kSelThreads) void k_select(const double* __restrict
   for (int k = 0; k < NPT; ++k) {
     const unsigned long long b = __ballot(keep[k]);
     if (lane == 0) {
-      const int w0 = (kSelThreads * k + 64 * wv) >> 5;
+      const int w0 = (NT * k + 64 * wv) >> 5;
       wbits[w0] = (uint32_t)b;
       wbits[w0 + 1] = (uint32_t)(b >> 32);
     }
@@ -610,7 +612,7 @@ __global__ __launch_bounds__(kSelThreads) void k_select(const double* __restrict
   __syncthreads();
   const int total = words_prefix(wbits, wpre, W, t);
   if (t == 0) counts[row] = total;
-  for (int w = t; w < W; w += kSelThreads) words[row * W + w] = wbits[w];
+  for (int w = t; w < W; w += NT) words[row * W + w] = wbits[w];
   __syncthreads();
   if (lists) {
     // Each kept block j goes to its rank among the kept blocks: the kept count before its
@@ -618,20 +620,23 @@ __global__ __launch_bounds__(kSelThreads) void k_select(const double* __restrict
     int32_t* lrow = lists + row * nb;
 #pragma unroll
     for (int k = 0; k < NPT; ++k) {
-      const int j = t + kSelThreads * k;
+      const int j = t + NT * k;
       if (keep[k]) lrow[bit_rank(wbits, wpre, j)] = j;
     }
   }
 }
 
-template <int NPT>
+template <int NT, int NPT>
 void launch_select(const KGeom& g, const double* S, uint32_t* words, int32_t* counts, int32_t* lists,
                    const SelArgs& a, hipStream_t s) {
   const dim3 grid((unsigned)((long long)g.B * g.H * g.nb));
-  if (a.mode == ABLA_MASK_CDF && a.cut == ABLA_CUT_BITONIC)
-    k_select<NPT, true><<<grid, kSelThreads, 0, s>>>(S, words, counts, lists, g, a);
-  else
-    k_select<NPT, false><<<grid, kSelThreads, 0, s>>>(S, words, counts, lists, g, a);
+  if constexpr (NT == kSelThreads) {  // the bitonic sort needs np <= NT * NPT keys of LDS
+    if (a.mode == ABLA_MASK_CDF && a.cut == ABLA_CUT_BITONIC) {
+      k_select<NT, NPT, true><<<grid, NT, 0, s>>>(S, words, counts, lists, g, a);
+      return;
+    }
+  }
+  k_select<NT, NPT, false><<<grid, NT, 0, s>>>(S, words, counts, lists, g, a);
 }
 
 }  // namespace
@@ -680,16 +685,30 @@ hipError_t launch_build_mask(const KGeom& g, const abla_mask_params& p, const do
   a.W = (g.nb + 31) / 32;
   a.gamma = p.gamma;
   a.floor_k = (int)ceil((double)(g.nbh * g.nbw) * p.lambda);
-  if (np <= 256)
-    launch_select<1>(g, scores, words, counts, lists, a, s);
+  // Rows of up to 640 blocks (radix cut or no sort): one wave per row, so the row's steps
+  // synchronise within the wave and more rows are in flight per CU; up to 1280 blocks two
+  // waves. At most 10-12 keys per thread keeps the registers low enough for that occupancy
+  // (the 16-key rows of up to 4096 blocks run at 3 waves per SIMD). The bitonic cross-check
+  // sorts np >= nb keys in LDS and keeps the four-wave rows of np / 256 keys per thread.
+  const bool bitonic = p.mode == ABLA_MASK_CDF && p.cut == ABLA_CUT_BITONIC;
+  if (!bitonic && g.nb <= 256)
+    launch_select<64, 4>(g, scores, words, counts, lists, a, s);
+  else if (!bitonic && g.nb <= 640)
+    launch_select<64, 10>(g, scores, words, counts, lists, a, s);
+  else if (!bitonic && g.nb <= 1280)
+    launch_select<128, 10>(g, scores, words, counts, lists, a, s);
+  else if (!bitonic && g.nb > 2048 && g.nb <= 3072)
+    launch_select<kSelThreads, 12>(g, scores, words, counts, lists, a, s);
+  else if (np <= 256)
+    launch_select<kSelThreads, 1>(g, scores, words, counts, lists, a, s);
   else if (np <= 512)
-    launch_select<2>(g, scores, words, counts, lists, a, s);
+    launch_select<kSelThreads, 2>(g, scores, words, counts, lists, a, s);
   else if (np <= 1024)
-    launch_select<4>(g, scores, words, counts, lists, a, s);
+    launch_select<kSelThreads, 4>(g, scores, words, counts, lists, a, s);
   else if (np <= 2048)
-    launch_select<8>(g, scores, words, counts, lists, a, s);
+    launch_select<kSelThreads, 8>(g, scores, words, counts, lists, a, s);
   else
-    launch_select<16>(g, scores, words, counts, lists, a, s);
+    launch_select<kSelThreads, 16>(g, scores, words, counts, lists, a, s);
   return hipGetLastError();
 }
 
