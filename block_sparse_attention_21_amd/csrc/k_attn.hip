@@ -54,7 +54,9 @@ struct AttnArgs {
   float* lse;
   KGeom g;
   int pairs;    // query-block pairs per (b, h): ceil(T/2) * nbh * nbw
-  int grid;     // total workgroups
+  int grid;     // work items (query-block pairs over all heads)
+  int main_grid;  // items 0 .. main_grid-1 belong to workgroups 0 .. main_grid-1 (see claim_item)
+  int32_t* tail_cnt;  // items claimed by the tail workgroups (zeroed by k_pair_order)
   float c2;     // scale * log2(e)
   float scale;
   int orig;
@@ -351,6 +353,24 @@ __device__ __forceinline__ void schedule_phase_b() {
   }
 }
 
+// Items main_grid .. grid-1 (the last positions of every XCD's queue: its shortest pairs,
+// longest-first) are not tied to a workgroup. Workgroups are dealt to the XCDs round-robin and
+// each XCD runs its share in order, so an XCD whose share of the static items took less time
+// reaches its tail workgroups earlier; each of those takes the next unclaimed item from one
+// counter, and the XCDs that finish first take more of the tail. There are kTailOversub tail
+// workgroups per tail item (an XCD can take up to a quarter of the tail; the surplus exit at
+// once): 2 measured better than 4 (fewer empty workgroups) at 480p, 480p-dyn and on the long
+// clip. `slot` is one int of LDS. Returns the item, or -1 when none is left.
+constexpr int kTailOversub = 2;
+__device__ __forceinline__ int claim_item(const AttnArgs& a, int* slot) {
+  if ((int)blockIdx.x < a.main_grid) return (int)blockIdx.x;
+  if (threadIdx.x == 0) *slot = atomicAdd(a.tail_cnt, 1);  // a vector-memory atomic, one lane
+  __syncthreads();
+  const int it = a.main_grid + *slot;
+  __syncthreads();  // the slot is LDS the schedule reuses
+  return it < a.grid ? it : -1;
+}
+
 struct Walk {
   int u, n;        // position in the schedule and its length
   int ec, en, ef;  // entries u, u+1, u+2 (0 past the end)
@@ -435,18 +455,21 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
   const int nb = g.nb;
   const int F = g.nbh * g.nbw;
 
-  // Visiting order: item blockIdx.x of the table xcd_queue wrote (column order, short
-  // lists), else position blockIdx.x of the per-head longest-first order (long lists), in
-  // plain dispatch order: the resident workgroups of all eight XCDs then work on the same
-  // one or two heads at a time, whose K/V (tens of MB) stay in the shared last-level cache.
+  // Work item: item blockIdx.x, or for the tail workgroups the next unclaimed item (claim_item).
+  const int item = claim_item(a, reinterpret_cast<int*>(sched));
+  if (item < 0) return;  // every item is taken (uniform across the workgroup)
+  // Visiting order: entry `item` of the table xcd_queue wrote (column order, short lists),
+  // else position `item` of the per-head longest-first order (long lists), in plain dispatch
+  // order: the resident workgroups of all eight XCDs then work on the same one or two heads
+  // at a time, whose K/V (tens of MB) stay in the shared last-level cache.
   int bh, pair;
   if (ld_const(a.walk_mode, 0)) {
-    const int gi = ld_const(a.order, (long long)blockIdx.x);
+    const int gi = ld_const(a.order, (long long)item);
     bh = gi / a.pairs;
     pair = gi - bh * a.pairs;
   } else {
-    bh = blockIdx.x / a.pairs;
-    const int pos = blockIdx.x - bh * a.pairs;
+    bh = item / a.pairs;
+    const int pos = item - bh * a.pairs;
     pair = ld_const(a.order, (long long)bh * a.pairs + pos);
   }
   int blk_a, blk_b;
@@ -986,7 +1009,10 @@ __global__ __launch_bounds__(1024) void k_pair_order(const int32_t* __restrict__
   long long total = 0;
   for (int w = 0; w < 16; ++w) total += wsum[w];
   const bool column = total <= (long long)kColumnMaxCount * rows;
-  if (bh == 0 && t == 0) mode_out[0] = column ? 1 : 0;
+  if (bh == 0 && t == 0) {
+    mode_out[0] = column ? 1 : 0;
+    mode_out[1] = 0;  // the attention's tail counter (claim_item)
+  }
   const int bhs = (int)(rows / nb);
   if (column) {
     if (bh < 8) xcd_queue(counts, order, nb, F, pairs, bhs, (int)bh, total, scan_part, hist, hist + kQueueTail);
@@ -1061,13 +1087,16 @@ hipError_t launch_sparse_attn(const KGeom& g, int dtype, float scale, const void
     a.g = g;
     a.pairs = pairs;
     a.grid = (int)((long long)bhs * pairs);
+    // The last kQueueTail positions of each XCD's queue (its shortest pairs) form the tail.
+    a.main_grid = max(0, a.grid / 8 - kQueueTail) * 8;
+    a.tail_cnt = mode + 1;
     a.scale = scale;
     a.c2 = scale * 1.4426950408889634f;
     a.orig = out_original_order;
     a.qk_orig = qk_original_order;
     a.magic_f = (1ull << 32) / (unsigned long long)F + 1;
     a.magic_w = (1ull << 32) / (unsigned long long)g.nbw + 1;
-    const dim3 grid((unsigned)a.grid);
+    const dim3 grid((unsigned)(a.main_grid + kTailOversub * (a.grid - a.main_grid)));
     const int variant = (g.d == 128 ? 4 : 0) | (qk_original_order ? 2 : 0) | (v_original_order ? 1 : 0);
     switch (variant) {
       case 7: k_attn_bf16<128, true, true><<<grid, 256, 0, s>>>(a); break;
