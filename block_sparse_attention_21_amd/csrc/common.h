@@ -70,6 +70,7 @@ struct BwdWorkspace {
   float *D, *L2;                    // [B,H,N] fractal order
   int32_t *col_counts, *col_lists;  // [B,H,nb], [B,H,nb,nb]
   int32_t* order;                   // [B,H,nb] workgroup visiting order (dQ, then dK/dV)
+  int32_t* tail_cnt;                // one int after the order: items claimed by tail workgroups
 };
 hipError_t launch_sparse_attn_bwd(const KGeom& g, int dtype, float scale, const void* q, const void* k,
                                   const void* v, const void* o, const void* dout, const float* lse,

@@ -196,8 +196,23 @@ __device__ __forceinline__ void column_order(int wg, const KGeom& g, long long& 
 // workgroups) are written longest-first. Workgroup x writes the queue of XCD x; `cnt` holds
 // the list lengths (counts for dQ, column counts for dK/dV); order[w] = bh * nb + block.
 constexpr int kBwdQueueTail = 128;
+
+// Items main .. grid-1 (the last kBwdQueueTail positions of every XCD's queue, its shortest
+// lists, longest-first) are claimed at run time by kBwdTailOversub workgroups per item, so the
+// XCDs that finish their static share first take more of them (as the forward's claim_item).
+// `slot` is one int of LDS; returns the item or -1.
+constexpr int kBwdTailOversub = 2;
+__device__ __forceinline__ int bwd_claim_item(int main, int grid, int32_t* tail_cnt, int* slot) {
+  if ((int)blockIdx.x < main) return (int)blockIdx.x;
+  if (threadIdx.x == 0) *slot = atomicAdd(tail_cnt, 1);  // a vector-memory atomic, one lane
+  __syncthreads();
+  const int it = main + *slot;
+  __syncthreads();  // the slot is LDS the tiles reuse
+  return it < grid ? it : -1;
+}
 __global__ __launch_bounds__(1024) void k_bwd_order(const int32_t* __restrict__ cnt, int32_t* __restrict__ order,
-                                                    KGeom g, int bhs) {
+                                                    int32_t* __restrict__ tail_cnt, KGeom g, int bhs) {
+  if (blockIdx.x == 0 && threadIdx.x == 0) *tail_cnt = 0;  // for bwd_claim_item
   __shared__ long long wsum[16];
   __shared__ int wpart[16];
   __shared__ int tail_gi[kBwdQueueTail], tail_cost[kBwdQueueTail];
@@ -303,6 +318,8 @@ struct DqArgs {
   const float *Dm, *L2;
   const int32_t *counts, *lists;
   const int32_t* order;  // visiting order (k_bwd_order)
+  int32_t* tail_cnt;
+  int main_grid, items;
   uint16_t* dq;
   KGeom g;
   float c2, scale;
@@ -321,7 +338,9 @@ __global__ __launch_bounds__(kBwdThreads) __attribute__((amdgpu_waves_per_eu(2, 
   const int t = threadIdx.x, lane = t & 63, hi = lane >> 5;
   const int w = __builtin_amdgcn_readfirstlane(t >> 6);
   const int qh = w & 1, kh = w >> 1;
-  const int gi = ld_const(a.order, (long long)blockIdx.x);
+  const int item = bwd_claim_item(a.main_grid, a.items, a.tail_cnt, reinterpret_cast<int*>(smem));
+  if (item < 0) return;
+  const int gi = ld_const(a.order, (long long)item);
   const long long bh = gi / nb;
   const int i = gi - (int)bh * nb;
   const long long row = bh * nb + i;
@@ -445,6 +464,8 @@ struct DkvArgs {
   const float *Dm, *L2;
   const int32_t *col_counts, *col_lists;
   const int32_t* order;  // visiting order (k_bwd_order)
+  int32_t* tail_cnt;
+  int main_grid, items;
   uint16_t *dk, *dv;
   KGeom g;
   float c2, scale;
@@ -505,7 +526,9 @@ __global__ __launch_bounds__(kBwdThreads) __attribute__((amdgpu_waves_per_eu(2, 
   const int t = threadIdx.x, lane = t & 63, hi = lane >> 5;
   const int w = __builtin_amdgcn_readfirstlane(t >> 6);
   const int kh = w & 1, qh = w >> 1;
-  const int gi = ld_const(a.order, (long long)blockIdx.x);
+  const int item = bwd_claim_item(a.main_grid, a.items, a.tail_cnt, reinterpret_cast<int*>(smem));
+  if (item < 0) return;
+  const int gi = ld_const(a.order, (long long)item);
   const long long bh = gi / nb;
   const int j = gi - (int)bh * nb;
   const long long col = bh * nb + j;
@@ -841,22 +864,25 @@ hipError_t launch_sparse_attn_bwd(const KGeom& g, int dtype, float scale, const 
   if ((e = hipGetLastError()) != hipSuccess) return e;
 
   const float c2 = scale * kLog2e;
-  const dim3 grid((unsigned)((long long)bhs * g.nb));
+  const int items = (int)((long long)bhs * g.nb);
+  const int main_grid = max(0, items / 8 - kBwdQueueTail) * 8;
+  const dim3 grid((unsigned)(main_grid + kBwdTailOversub * (items - main_grid)));
   const uint16_t* q16 = static_cast<const uint16_t*>(q);
   const uint16_t* k16 = static_cast<const uint16_t*>(k);
   const uint16_t* v16 = static_cast<const uint16_t*>(v);
-  k_bwd_order<<<8, 1024, 0, s>>>(counts, ws.order, g, (int)bhs);
+  k_bwd_order<<<8, 1024, 0, s>>>(counts, ws.order, ws.tail_cnt, g, (int)bhs);
   if ((e = hipGetLastError()) != hipSuccess) return e;
-  DqArgs qa{q16, k16, v16, do16, ws.D, ws.L2, counts, lists, ws.order, static_cast<uint16_t*>(dq), g, c2, scale};
+  DqArgs qa{q16, k16, v16, do16, ws.D, ws.L2, counts, lists, ws.order, ws.tail_cnt, main_grid, items,
+            static_cast<uint16_t*>(dq), g, c2, scale};
   if (g.d == 128)
     k_bwd_dq<128><<<grid, kBwdThreads, 0, s>>>(qa);
   else
     k_bwd_dq<64><<<grid, kBwdThreads, 0, s>>>(qa);
   if ((e = hipGetLastError()) != hipSuccess) return e;
-  k_bwd_order<<<8, 1024, 0, s>>>(ws.col_counts, ws.order, g, (int)bhs);
+  k_bwd_order<<<8, 1024, 0, s>>>(ws.col_counts, ws.order, ws.tail_cnt, g, (int)bhs);
   if ((e = hipGetLastError()) != hipSuccess) return e;
-  DkvArgs ka{k16, v16, q16, do16, ws.D, ws.L2, ws.col_counts, ws.col_lists, ws.order,
-             static_cast<uint16_t*>(dk), static_cast<uint16_t*>(dv), g, c2, scale};
+  DkvArgs ka{k16, v16, q16, do16, ws.D, ws.L2, ws.col_counts, ws.col_lists, ws.order, ws.tail_cnt, main_grid,
+             items, static_cast<uint16_t*>(dk), static_cast<uint16_t*>(dv), g, c2, scale};
   if (g.d == 128)
     k_bwd_dkdv<128><<<grid, kBwdThreads, 0, s>>>(ka);
   else
