@@ -239,7 +239,8 @@ abla_status abla_build_mask(const abla_geom* g, const abla_mask_params* p, const
 
 size_t abla_sparse_attn_workspace_bytes(const abla_geom* g) {
   if (check_geom(g) != ABLA_OK) return 0;
-  // Visiting order (at most nb ints per (b, h)), then one int of walk mode, padded to 256 bytes.
+  // Visiting order (at most nb ints per (b, h)), then the walk mode and the counter of the
+  // dynamically claimed items (one int each), padded to 256 bytes.
   return bh_of(g) * (size_t)nb_of(g) * sizeof(int32_t) + 256;
 }
 
