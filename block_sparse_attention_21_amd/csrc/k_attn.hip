@@ -55,7 +55,7 @@ struct AttnArgs {
   KGeom g;
   int pairs;    // query-block pairs per (b, h): ceil(T/2) * nbh * nbw
   int grid;     // work items (query-block pairs over all heads)
-  int main_grid;  // items 0 .. main_grid-1 belong to workgroups 0 .. main_grid-1 (see claim_item)
+  int main_col, main_long;  // items 0 .. main-1 belong to workgroups 0 .. main-1, per walk mode (claim_item)
   int32_t* tail_cnt;  // items claimed by the tail workgroups (zeroed by k_pair_order)
   float c2;     // scale * log2(e)
   float scale;
@@ -353,8 +353,9 @@ __device__ __forceinline__ void schedule_phase_b() {
   }
 }
 
-// Items main_grid .. grid-1 (the last positions of every XCD's queue: its shortest pairs,
-// longest-first) are not tied to a workgroup. Workgroups are dealt to the XCDs round-robin and
+// Items main .. grid-1 (the last positions of every XCD's queue: its shortest pairs,
+// longest-first) are not tied to a workgroup; main depends on the walk mode (a longer dynamic
+// tail for long lists, where the XCDs also differ in speed). Workgroups are dealt to the XCDs round-robin and
 // each XCD runs its share in order, so an XCD whose share of the static items took less time
 // reaches its tail workgroups earlier; each of those takes the next unclaimed item from one
 // counter, and the XCDs that finish first take more of the tail. There are kTailOversub tail
@@ -363,10 +364,11 @@ __device__ __forceinline__ void schedule_phase_b() {
 // clip. `slot` is one int of LDS. Returns the item, or -1 when none is left.
 constexpr int kTailOversub = 2;
 __device__ __forceinline__ int claim_item(const AttnArgs& a, int* slot) {
-  if ((int)blockIdx.x < a.main_grid) return (int)blockIdx.x;
+  const int main = ld_const(a.walk_mode, 0) ? a.main_col : a.main_long;
+  if ((int)blockIdx.x < main) return (int)blockIdx.x;
   if (threadIdx.x == 0) *slot = atomicAdd(a.tail_cnt, 1);  // a vector-memory atomic, one lane
   __syncthreads();
-  const int it = a.main_grid + *slot;
+  const int it = main + *slot;
   __syncthreads();  // the slot is LDS the schedule reuses
   return it < a.grid ? it : -1;
 }
@@ -1087,8 +1089,11 @@ hipError_t launch_sparse_attn(const KGeom& g, int dtype, float scale, const void
     a.g = g;
     a.pairs = pairs;
     a.grid = (int)((long long)bhs * pairs);
-    // The last kQueueTail positions of each XCD's queue (its shortest pairs) form the tail.
-    a.main_grid = max(0, a.grid / 8 - kQueueTail) * 8;
+    // The last kQueueTail positions of each XCD's queue (its shortest pairs) form the tail in
+    // column order, 1.5 kQueueTail positions for long lists (720p: -1.1% against 128 positions;
+    // 480p and 480p-dyn lose 0.7-2% with the longer tail).
+    a.main_col = max(0, a.grid / 8 - kQueueTail) * 8;
+    a.main_long = max(0, a.grid / 8 - 3 * kQueueTail / 2) * 8;
     a.tail_cnt = mode + 1;
     a.scale = scale;
     a.c2 = scale * 1.4426950408889634f;
@@ -1096,7 +1101,8 @@ hipError_t launch_sparse_attn(const KGeom& g, int dtype, float scale, const void
     a.qk_orig = qk_original_order;
     a.magic_f = (1ull << 32) / (unsigned long long)F + 1;
     a.magic_w = (1ull << 32) / (unsigned long long)g.nbw + 1;
-    const dim3 grid((unsigned)(a.main_grid + kTailOversub * (a.grid - a.main_grid)));
+    // Enough tail workgroups for either mode (the column mode's extra ones exit at once).
+    const dim3 grid((unsigned)(a.main_long + kTailOversub * (a.grid - a.main_long)));
     const int variant = (g.d == 128 ? 4 : 0) | (qk_original_order ? 2 : 0) | (v_original_order ? 1 : 0);
     switch (variant) {
       case 7: k_attn_bf16<128, true, true><<<grid, 256, 0, s>>>(a); break;
