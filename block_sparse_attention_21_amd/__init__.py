@@ -23,7 +23,7 @@ F32, BF16 = 0, 1
 LAYOUT_TOKENS, LAYOUT_BLOCK_T = 0, 1
 MASK_CDF, MASK_DYN, MASK_STATIC = 0, 1, 2
 ATTN_OUT_ORIGINAL, ATTN_QK_ORIGINAL, ATTN_V_ORIGINAL = 1, 2, 4
-CUT_RADIX, CUT_BITONIC = 0, 1
+CUT_RADIX, CUT_BITONIC, CUT_RADIX_WIDE = 0, 1, 2
 
 
 class AblaError(RuntimeError):
@@ -115,7 +115,9 @@ class Geometry:
 class MaskParams:
     """mode 'cdf' (thr), 'dyn' (tau) or 'static' (gamma, lam: retention decay per frame of
     distance and its long-range floor); pool_scale 0 -> 1/sqrt(d); sta (0,0,0) -> no sliding-tile
-    window; cut 'radix' (default) or 'bitonic' (how the CDF cut is found; same result)."""
+    window; cut 'radix' (default), 'bitonic' (how the CDF cut is found; same result) or
+    'radix-wide' (the radix cut with four waves per row in every mode; same result, another
+    workgroup size)."""
 
     mode: str = "cdf"
     thr: float = 0.9
@@ -129,7 +131,8 @@ class MaskParams:
     def c(self) -> _MaskParams:
         modes = {"cdf": MASK_CDF, "dyn": MASK_DYN, "static": MASK_STATIC}
         mode = modes.get(self.mode, -1) if isinstance(self.mode, str) else self.mode
-        cut = {"radix": CUT_RADIX, "bitonic": CUT_BITONIC}.get(self.cut, -1) if isinstance(self.cut, str) else self.cut
+        cuts = {"radix": CUT_RADIX, "bitonic": CUT_BITONIC, "radix-wide": CUT_RADIX_WIDE}
+        cut = cuts.get(self.cut, -1) if isinstance(self.cut, str) else self.cut
         return _MaskParams(mode, self.thr, self.tau, self.pool_scale, *self.sta, cut, self.gamma, self.lam)
 
 

@@ -221,7 +221,8 @@ abla_status abla_build_mask(const abla_geom* g, const abla_mask_params* p, const
   if (!aligned16({qbar, kbar, mask_words, counts, lists, workspace})) return ABLA_ERR_INVALID;
   if (!scored && !(p->gamma >= 0.0 && p->gamma <= 1.0 && p->lambda >= 0.0 && p->lambda <= 1.0))
     return ABLA_ERR_INVALID;  // also rejects NaN
-  if (p->cut != ABLA_CUT_RADIX && p->cut != ABLA_CUT_BITONIC) return ABLA_ERR_INVALID;
+  if (p->cut != ABLA_CUT_RADIX && p->cut != ABLA_CUT_BITONIC && p->cut != ABLA_CUT_RADIX_WIDE)
+    return ABLA_ERR_INVALID;
   if (isnan(p->thr) || isnan(p->tau) || isnan(p->pool_scale) || p->pool_scale < 0.0 || isinf(p->pool_scale))
     return ABLA_ERR_INVALID;
   if (!window_ok(p->sta_t, p->sta_h, p->sta_w)) return ABLA_ERR_INVALID;

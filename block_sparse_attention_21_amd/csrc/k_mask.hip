@@ -689,15 +689,17 @@ hipError_t launch_build_mask(const KGeom& g, const abla_mask_params& p, const do
   // synchronise within the wave and more rows are in flight per CU; up to 1280 blocks two
   // waves. At most 10-12 keys per thread keeps the registers low enough for that occupancy
   // (the 16-key rows of up to 4096 blocks run at 3 waves per SIMD). The bitonic cross-check
-  // sorts np >= nb keys in LDS and keeps the four-wave rows of np / 256 keys per thread.
+  // sorts np >= nb keys in LDS and keeps the four-wave rows of np / 256 keys per thread; the
+  // wide radix form takes those four-wave rows too.
   const bool bitonic = p.mode == ABLA_MASK_CDF && p.cut == ABLA_CUT_BITONIC;
-  if (!bitonic && g.nb <= 256)
+  const bool narrow = !bitonic && p.cut != ABLA_CUT_RADIX_WIDE;
+  if (narrow && g.nb <= 256)
     launch_select<64, 4>(g, scores, words, counts, lists, a, s);
-  else if (!bitonic && g.nb <= 640)
+  else if (narrow && g.nb <= 640)
     launch_select<64, 10>(g, scores, words, counts, lists, a, s);
-  else if (!bitonic && g.nb <= 1280)
+  else if (narrow && g.nb <= 1280)
     launch_select<128, 10>(g, scores, words, counts, lists, a, s);
-  else if (!bitonic && g.nb > 2048 && g.nb <= 3072)
+  else if (narrow && g.nb > 2048 && g.nb <= 3072)
     launch_select<kSelThreads, 12>(g, scores, words, counts, lists, a, s);
   else if (np <= 256)
     launch_select<kSelThreads, 1>(g, scores, words, counts, lists, a, s);

@@ -71,11 +71,17 @@ typedef struct {
 
 typedef enum { ABLA_MASK_CDF = 0, ABLA_MASK_DYN = 1, ABLA_MASK_STATIC = 2 } abla_mask_mode;
 
-/* How the CDF cut finds the last kept rank of a row. Both give the same bits.
- * ABLA_CUT_RADIX:   radix select on the 64-bit (probability, ~index) keys with exact
- *                   fixed-point mass histograms (default; no full sort).
- * ABLA_CUT_BITONIC: full LDS bitonic sort of the keys, then an exact prefix sum. */
-typedef enum { ABLA_CUT_RADIX = 0, ABLA_CUT_BITONIC = 1 } abla_cut_algorithm;
+/* How the CDF cut finds the last kept rank of a row. All give the same bits.
+ * ABLA_CUT_RADIX:      radix select on the 64-bit (probability, ~index) keys with exact
+ *                      fixed-point mass histograms (default; no full sort). Rows of up
+ *                      to 1280 blocks run on one or two waves each.
+ * ABLA_CUT_BITONIC:    full LDS bitonic sort of the keys, then an exact prefix sum.
+ * ABLA_CUT_RADIX_WIDE: the radix select with four waves per row whatever nb is, so the
+ *                      same rows run at another workgroup size and LDS partition (a
+ *                      cross-check for races). It applies to every mode: DYN and STATIC
+ *                      rows then run on four waves too; the other values leave them on
+ *                      the default width. */
+typedef enum { ABLA_CUT_RADIX = 0, ABLA_CUT_BITONIC = 1, ABLA_CUT_RADIX_WIDE = 2 } abla_cut_algorithm;
 
 typedef struct {
   int32_t mode;       /* abla_mask_mode */
@@ -83,7 +89,7 @@ typedef struct {
   double tau;         /* DYN mode: keep j iff S_ij >= max_j S_ij - tau (pooled, scaled logits) */
   double pool_scale;  /* scale of the pooled logits; 0 means 1/sqrt(d) */
   int32_t sta_t, sta_h, sta_w; /* sliding-tile window in blocks, odd; all 0 = no STA */
-  int32_t cut;        /* abla_cut_algorithm (CDF mode) */
+  int32_t cut;        /* abla_cut_algorithm */
   double gamma;       /* STATIC mode: retention decay per frame of temporal distance, in [0, 1] */
   double lambda;      /* STATIC mode: long-range floor of the retention ratio, in [0, 1] */
 } abla_mask_params;

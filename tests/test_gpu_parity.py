@@ -656,3 +656,42 @@ def test_cut_algorithms_agree_small(A):
                for c in ("radix", "bitonic")]
         torch.cuda.synchronize()
         assert torch.equal(res[0][0], res[1][0]) and torch.equal(res[0][1], res[1][1]), geo
+
+
+# ---------------------------------------------------------------- one mask at two workgroup sizes
+def _masks_equal(a, b, nb):
+    assert torch.equal(a[0], b[0]) and torch.equal(a[1], b[1])
+    valid = torch.arange(nb, device=DEV)[None, None, None, :] < a[1][..., None]
+    assert torch.equal(torch.where(valid, a[2], 0), torch.where(valid, b[2], 0))
+
+
+@pytest.mark.parametrize("name", ["480p", "480p-dyn", "480p-static", "720p"])
+def test_select_widths_agree(A, name):
+    """The row selection on its default width (one wave per row at 480p, two at 720p) and on four
+    waves per row ('radix-wide') gives the same bits, counts and lists in every mode: a race in
+    the row's LDS steps would show as a difference between the two partitions."""
+    import dataclasses
+    w = WORKLOADS[name]
+    geom, og = PT.geoms(w.B, w.H, w.T, w.Hs, w.Ws, w.d, w.P)
+    q, k, _ = make_qkv(w, device=DEV)
+    _, qbar = A.reorder(q, geom, want_pooled=True)
+    _, kbar = A.reorder(k, geom, want_pooled=True)
+    base = A.MaskParams(mode=w.mode, thr=w.thr, tau=w.tau, sta=tuple(w.sta), gamma=w.gamma, lam=w.lam)
+    res = [A.build_mask(qbar, kbar, geom, dataclasses.replace(base, cut=c)) for c in ("radix", "radix-wide")]
+    torch.cuda.synchronize()
+    _masks_equal(res[0], res[1], geom.nb)
+
+
+def test_select_widths_agree_small(A):
+    """Rows of at most 256 blocks (64 threads by default) against four waves, in the three modes."""
+    for geo in [(1, 2, 3, 24, 88), (1, 1, 1, 8, 8), (1, 2, 2, 16, 16), (1, 1, 5, 16, 24)]:
+        B, H, T, Hs, Ws = geo
+        geom, og = PT.geoms(B, H, T, Hs, Ws, 128)
+        q, k, _ = make_random_qkv(B, H, T, Hs, Ws, 128, "bf16", seed=12, device=DEV)
+        _, qbar = A.reorder(q, geom, want_pooled=True)
+        _, kbar = A.reorder((k.float() + q.float()).to(q.dtype), geom, want_pooled=True)
+        for prm in (dict(mode="cdf", thr=0.7), dict(mode="dyn", tau=2.0), dict(mode="static", gamma=0.5, lam=0.05)):
+            res = [A.build_mask(qbar, kbar, geom, A.MaskParams(sta=(3, 3, 3), cut=c, **prm))
+                   for c in ("radix", "radix-wide")]
+            torch.cuda.synchronize()
+            _masks_equal(res[0], res[1], geom.nb)
