@@ -695,3 +695,33 @@ def test_select_widths_agree_small(A):
                    for c in ("radix", "radix-wide")]
             torch.cuda.synchronize()
             _masks_equal(res[0], res[1], geom.nb)
+
+
+# ---------------------------------------------------------------- more rows than one launch holds
+@pytest.mark.parametrize("prm", [dict(mode="cdf", thr=0.5, cut="radix"), dict(mode="cdf", thr=0.5, cut="radix-wide"),
+                                 dict(mode="dyn", tau=0.25)])
+def test_mask_launches_split_over_many_rows(A, prm):
+    """2^22 + 5 heads of two blocks: the score tiles and the mask rows run in several launches of
+    at most 2^22 workgroups. Block 0 has pooled key +e0 and block 1 -e0, and each query row is
+    +-2 e0 with a sign pattern over the rows, so its pooled logits are +-0.25 and -+0.25 and it
+    keeps exactly its larger block (CDF thr 0.5: that block holds 62% of the mass; DYN: the other
+    is 0.5 below the maximum). Outputs are pre-filled so an unwritten row shows."""
+    H = (1 << 22) + 5
+    geom = A.Geometry(B=1, H=H, T=2, Hs=8, Ws=8, d=64)
+    assert geom.nb == 2
+    row = torch.arange(H * 2, device=DEV).view(1, H, 2)
+    sign = torch.where(row % 3 == 0, 1.0, -1.0).to(torch.float64)
+    qbar = torch.zeros(1, H, 2, 64, dtype=torch.float64, device=DEV)
+    qbar[..., 0] = 2.0 * sign
+    kbar = torch.zeros_like(qbar)
+    kbar[:, :, 0, 0] = 1.0
+    kbar[:, :, 1, 0] = -1.0
+    words = torch.full((1, H, 2, 1), -1, dtype=torch.int32, device=DEV)
+    counts = torch.full((1, H, 2), -1, dtype=torch.int32, device=DEV)
+    lists = torch.full((1, H, 2, 2), -1, dtype=torch.int32, device=DEV)
+    A.build_mask(qbar, kbar, geom, A.MaskParams(sta=(0, 0, 0), **prm), words=words, counts=counts, lists=lists)
+    torch.cuda.synchronize()
+    kept = torch.where(sign > 0, 0, 1).to(torch.int32)
+    assert bool((counts == 1).all())
+    assert torch.equal(words[..., 0], torch.bitwise_left_shift(torch.ones_like(kept), kept))
+    assert torch.equal(lists[..., 0], kept)
