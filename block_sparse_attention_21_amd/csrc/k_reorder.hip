@@ -139,24 +139,26 @@ __device__ __forceinline__ void reorder_block(const E* __restrict__ x, E* __rest
 
 template <typename E, int D, bool POOL, bool BLOCK_T, bool STORE = true>
 __global__ __launch_bounds__(kThreads) void k_reorder_fwd(const E* __restrict__ x, E* __restrict__ y,
-                                                          double* __restrict__ pooled, KGeom g) {
+                                                          double* __restrict__ pooled, KGeom g, int first) {
   __shared__ __attribute__((aligned(16))) char smem[kSmemBytes<E, D>];
-  reorder_block<E, D, POOL, BLOCK_T, STORE>(x, y, pooled, g, blockIdx.x, smem);
+  reorder_block<E, D, POOL, BLOCK_T, STORE>(x, y, pooled, g, first + (int)blockIdx.x, smem);
 }
 
 // The layer's first step in one launch: workgroup 3b pools Q's block b, 3b+1 pools K's (both
 // read in the original order, not copied) and 3b+2 reorders V's into a channel-major block,
-// b < n = B*H*nb. One grid instead of three saves two launch gaps and two ramp-down tails;
+// b < n = B*H*nb (workgroup `first` + blockIdx.x of the whole grid, which larger inputs split
+// into several launches). One grid instead of three saves two launch gaps and two ramp-down tails;
 // interleaving the read-only pooling with the read-write reorder (rather than Q, then K,
 // then V) measured 5% faster at 480p and 720p (5.6 TB/s for the stage).
 template <typename E, int D>
 __global__ __launch_bounds__(kThreads) void k_pool_qk_reorder_v(const E* __restrict__ q, const E* __restrict__ k,
                                                                 const E* __restrict__ v, double* __restrict__ qbar,
                                                                 double* __restrict__ kbar, E* __restrict__ vrt,
-                                                                KGeom g) {
+                                                                KGeom g, int first) {
   __shared__ __attribute__((aligned(16))) char smem[kSmemBytes<E, D>];
-  const int which = blockIdx.x % 3;
-  const int blk = blockIdx.x / 3;
+  const int wg = first + (int)blockIdx.x;
+  const int which = wg % 3;
+  const int blk = wg / 3;
   if (which == 0)
     reorder_block<E, D, true, false, false>(q, nullptr, qbar, g, blk, smem);
   else if (which == 1)
@@ -167,9 +169,10 @@ __global__ __launch_bounds__(kThreads) void k_pool_qk_reorder_v(const E* __restr
 
 // Inverse: fractal order (token rows) -> original order.
 template <typename E, int D>
-__global__ __launch_bounds__(kThreads) void k_reorder_inv(const E* __restrict__ x, E* __restrict__ y, KGeom g) {
+__global__ __launch_bounds__(kThreads) void k_reorder_inv(const E* __restrict__ x, E* __restrict__ y, KGeom g,
+                                                          int first) {
   using S = Shape<E, D>;
-  const int blk = blockIdx.x;
+  const int blk = first + (int)blockIdx.x;
   const int bh = blk / g.nb;
   const int i = blk - bh * g.nb;
   const int t = threadIdx.x;
@@ -185,26 +188,33 @@ __global__ __launch_bounds__(kThreads) void k_reorder_inv(const E* __restrict__ 
   }
 }
 
+// Grids of at most 2^22 workgroups: a grid dimension holds at most 2^32 work-items, and the
+// block count B*H*nb (times 3 for the first step) may exceed 2^24.
+constexpr int kChunk = 1 << 22;
+
 template <typename E, int D>
 hipError_t dispatch(const KGeom& g, int inverse, int layout, const void* x, void* y, double* pooled,
                     hipStream_t s) {
-  const dim3 grid((unsigned)(g.B * g.H * g.nb));
+  const int total = (int)(g.B * g.H * g.nb);
   const E* xi = static_cast<const E*>(x);
   E* yo = static_cast<E*>(y);
-  if (inverse) {
-    k_reorder_inv<E, D><<<grid, kThreads, 0, s>>>(xi, yo, g);
-  } else if (layout == ABLA_LAYOUT_BLOCK_T) {
-    if (pooled)
-      k_reorder_fwd<E, D, true, true><<<grid, kThreads, 0, s>>>(xi, yo, pooled, g);
-    else
-      k_reorder_fwd<E, D, false, true><<<grid, kThreads, 0, s>>>(xi, yo, nullptr, g);
-  } else if (!yo) {
-    k_reorder_fwd<E, D, true, false, false><<<grid, kThreads, 0, s>>>(xi, nullptr, pooled, g);
-  } else {
-    if (pooled)
-      k_reorder_fwd<E, D, true, false><<<grid, kThreads, 0, s>>>(xi, yo, pooled, g);
-    else
-      k_reorder_fwd<E, D, false, false><<<grid, kThreads, 0, s>>>(xi, yo, nullptr, g);
+  for (int first = 0; first < total; first += kChunk) {
+    const dim3 grid((unsigned)min(kChunk, total - first));
+    if (inverse) {
+      k_reorder_inv<E, D><<<grid, kThreads, 0, s>>>(xi, yo, g, first);
+    } else if (layout == ABLA_LAYOUT_BLOCK_T) {
+      if (pooled)
+        k_reorder_fwd<E, D, true, true><<<grid, kThreads, 0, s>>>(xi, yo, pooled, g, first);
+      else
+        k_reorder_fwd<E, D, false, true><<<grid, kThreads, 0, s>>>(xi, yo, nullptr, g, first);
+    } else if (!yo) {
+      k_reorder_fwd<E, D, true, false, false><<<grid, kThreads, 0, s>>>(xi, nullptr, pooled, g, first);
+    } else {
+      if (pooled)
+        k_reorder_fwd<E, D, true, false><<<grid, kThreads, 0, s>>>(xi, yo, pooled, g, first);
+      else
+        k_reorder_fwd<E, D, false, false><<<grid, kThreads, 0, s>>>(xi, yo, nullptr, g, first);
+    }
   }
   return hipGetLastError();
 }
@@ -212,9 +222,11 @@ hipError_t dispatch(const KGeom& g, int inverse, int layout, const void* x, void
 template <typename E, int D>
 hipError_t dispatch_qkv(const KGeom& g, const void* q, const void* k, const void* v, double* qbar, double* kbar,
                         void* vrt, hipStream_t s) {
-  const dim3 grid((unsigned)(3LL * g.B * g.H * g.nb));
-  k_pool_qk_reorder_v<E, D><<<grid, kThreads, 0, s>>>(static_cast<const E*>(q), static_cast<const E*>(k),
-                                                      static_cast<const E*>(v), qbar, kbar, static_cast<E*>(vrt), g);
+  const int total = (int)(3LL * g.B * g.H * g.nb);
+  for (int first = 0; first < total; first += kChunk)
+    k_pool_qk_reorder_v<E, D><<<dim3((unsigned)min(kChunk, total - first)), kThreads, 0, s>>>(
+        static_cast<const E*>(q), static_cast<const E*>(k), static_cast<const E*>(v), qbar, kbar,
+        static_cast<E*>(vrt), g, first);
   return hipGetLastError();
 }
 

@@ -725,3 +725,62 @@ def test_mask_launches_split_over_many_rows(A, prm):
     assert bool((counts == 1).all())
     assert torch.equal(words[..., 0], torch.bitwise_left_shift(torch.ones_like(kept), kept))
     assert torch.equal(lists[..., 0], kept)
+
+
+def _head_pattern(H, dtype):
+    """x[0, h, n, c] = ((3n + 5c) mod 23) - 11 + (h mod 7): small integers, exact in bf16, built
+    without a full-size integer temporary. Returns (x, pattern[64, 64], offsets[H])."""
+    n = torch.arange(64, device=DEV)
+    pat = ((3 * n[:, None] + 5 * n[None, :]) % 23 - 11).to(dtype)
+    off = (torch.arange(H, device=DEV) % 7).to(dtype)
+    x = torch.empty(1, H, 64, 64, dtype=dtype, device=DEV)
+    torch.add(pat[None, None], off[None, :, None, None], out=x)
+    return x, pat, off
+
+
+def test_first_step_launches_split_over_many_blocks(A):
+    """1,398,110 heads of one 8x8 patch in one frame (3*B*H*nb just above 2^22 workgroups, so the
+    first step runs in two launches). With one block per head the fractal order is the original
+    order: the V block must be the head's tile transposed (channel-major) and the pooled means the
+    column means, exactly."""
+    H = 1_398_110
+    geom = A.Geometry(B=1, H=H, T=1, Hs=8, Ws=8, d=64)
+    assert 3 * H * geom.nb > (1 << 22)
+    q, pat, off = _head_pattern(H, torch.bfloat16)
+    k = q.neg()
+    qbar = torch.full((1, H, 1, 64), math.nan, dtype=torch.float64, device=DEV)
+    kbar = torch.full_like(qbar, math.nan)
+    v_rt = torch.zeros(1, H, 1, 64, 64, dtype=torch.bfloat16, device=DEV)
+    A.pool_qk_reorder_v(q, k, q, geom, qbar=qbar, kbar=kbar, v_rt=v_rt)
+    torch.cuda.synchronize()
+    mean = pat.double().mean(dim=0)[None, :] + off.double()[:, None]  # [H, 64]
+    assert torch.equal(qbar.view(H, 64), mean)
+    assert torch.equal(kbar.view(H, 64), -mean)
+    for h0 in range(0, H, 1 << 18):
+        h1 = min(H, h0 + (1 << 18))
+        assert torch.equal(v_rt[0, h0:h1, 0], q[0, h0:h1].transpose(1, 2))
+
+
+def test_reorder_launches_split_over_many_blocks(A):
+    """2^22 + 3 heads of one block: the reorder grid runs in two launches. Forward into the
+    channel-major layout with pooling (the transposed tile and the column means), then the inverse
+    of the token layout (the identity for one block per head)."""
+    H = (1 << 22) + 3
+    geom = A.Geometry(B=1, H=H, T=1, Hs=8, Ws=8, d=64)
+    x, pat, off = _head_pattern(H, torch.bfloat16)
+    y = torch.zeros(1, H, 1, 64, 64, dtype=torch.bfloat16, device=DEV)
+    pooled = torch.full((1, H, 1, 64), math.nan, dtype=torch.float64, device=DEV)
+    A.reorder(x, geom, layout="block_t", out=y, pooled=pooled)
+    torch.cuda.synchronize()
+    assert torch.equal(pooled.view(H, 64), pat.double().mean(dim=0)[None, :] + off.double()[:, None])
+    for h0 in range(0, H, 1 << 19):
+        h1 = min(H, h0 + (1 << 19))
+        assert torch.equal(y[0, h0:h1, 0], x[0, h0:h1].transpose(1, 2))
+    del pooled
+    z = y.view(1, H, 64, 64)
+    z.zero_()
+    A.reorder(x, geom, inverse=True, out=z)
+    torch.cuda.synchronize()
+    for h0 in range(0, H, 1 << 19):
+        h1 = min(H, h0 + (1 << 19))
+        assert torch.equal(z[0, h0:h1], x[0, h0:h1])
