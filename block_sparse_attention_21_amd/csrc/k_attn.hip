@@ -988,9 +988,14 @@ __device__ void xcd_queue(const int32_t* __restrict__ counts, int32_t* __restric
 //  - otherwise: pairs longest-first by their kept count (counting sort), so the long rows
 //    do not form the tail; with long lists neighbouring workgroups start too far apart
 //    for L2 reuse and the balance matters more.
-// Every workgroup computes the same mean (a fixed-order sum); workgroup 0 stores the mode.
-// The grid is max(B*H, 8) workgroups.
+// Every workgroup computes the same mean (a fixed-order sum over all rows, or, beyond
+// kMeanSample rows, over kMeanSample evenly spaced ones scaled to the row count, so that the
+// work per workgroup stays bounded); workgroup 0 stores the mode. The grid is
+// min(max(B*H, 8), kOrderGrid) workgroups; in the longest-first mode each takes the heads
+// blockIdx.x, blockIdx.x + gridDim.x, ...
 constexpr int kColumnMaxCount = 96;
+constexpr long long kMeanSample = 1 << 16;
+constexpr int kOrderGrid = 4096;
 
 __global__ __launch_bounds__(1024) void k_pair_order(const int32_t* __restrict__ counts, int32_t* __restrict__ order,
                                                      int32_t* __restrict__ mode_out, int nb, int F, int pairs,
@@ -999,65 +1004,75 @@ __global__ __launch_bounds__(1024) void k_pair_order(const int32_t* __restrict__
   __shared__ int scan_part[16];
   __shared__ long long wsum[16];
   const int t = threadIdx.x, lane = t & 63, wv = t >> 6;
-  const long long bh = blockIdx.x;
-  const int32_t* c = counts + bh * nb;
 
+  const long long nsum = rows < kMeanSample ? rows : kMeanSample;
   long long part = 0;
-  for (long long r = t; r < rows; r += 1024) part += min(max(counts[r], 0), nb);
+  for (long long k = t; k < nsum; k += 1024) {
+    const long long r = nsum == rows ? k : k * rows / kMeanSample;
+    part += min(max(counts[r], 0), nb);
+  }
 #pragma unroll
   for (int o = 32; o > 0; o >>= 1) part += __shfl_xor(part, o);
   if (lane == 0) wsum[wv] = part;
   __syncthreads();
   long long total = 0;
   for (int w = 0; w < 16; ++w) total += wsum[w];
+  if (nsum != rows) total = total * rows / kMeanSample;
   const bool column = total <= (long long)kColumnMaxCount * rows;
-  if (bh == 0 && t == 0) {
+  if (blockIdx.x == 0 && t == 0) {
     mode_out[0] = column ? 1 : 0;
     mode_out[1] = 0;  // the attention's tail counter (claim_item)
   }
   const int bhs = (int)(rows / nb);
   if (column) {
-    if (bh < 8) xcd_queue(counts, order, nb, F, pairs, bhs, (int)bh, total, scan_part, hist, hist + kQueueTail);
+    if (blockIdx.x < 8)
+      xcd_queue(counts, order, nb, F, pairs, bhs, (int)blockIdx.x, total, scan_part, hist, hist + kQueueTail);
     return;
   }
-  if (bh >= bhs) return;
 
-  auto blk_count = [&](int blk) { return min(max(c[blk], 0), nb); };
   const int kmax = 2 * nb;
-  auto key = [&](int pr) {
-    int ba, bb;
-    pair_blocks(pr, F, nb, ba, bb);
-    int k = ba >= 0 ? blk_count(ba) : 0;
-    if (bb >= 0) k += blk_count(bb);
-    return k;
-  };
-  for (int v = t; v <= kmax; v += 1024) hist[v] = 0;
-  __syncthreads();
-  for (int pr = t; pr < pairs; pr += 1024) atomicAdd(&hist[key(pr)], 1);
-  __syncthreads();
-  desc_exclusive_scan(hist, kmax + 1, scan_part);
-  for (int pr = t; pr < pairs; pr += 1024) {
-    const int pos = atomicAdd(&hist[key(pr)], 1);
-    order[bh * pairs + pos] = pr;
+  for (long long bh = blockIdx.x; bh < bhs; bh += gridDim.x) {
+    const int32_t* c = counts + bh * nb;
+    auto blk_count = [&](int blk) { return min(max(c[blk], 0), nb); };
+    auto key = [&](int pr) {
+      int ba, bb;
+      pair_blocks(pr, F, nb, ba, bb);
+      int k = ba >= 0 ? blk_count(ba) : 0;
+      if (bb >= 0) k += blk_count(bb);
+      return k;
+    };
+    __syncthreads();  // the previous head's placement is done with hist
+    for (int v = t; v <= kmax; v += 1024) hist[v] = 0;
+    __syncthreads();
+    for (int pr = t; pr < pairs; pr += 1024) atomicAdd(&hist[key(pr)], 1);
+    __syncthreads();
+    desc_exclusive_scan(hist, kmax + 1, scan_part);
+    for (int pr = t; pr < pairs; pr += 1024) {
+      const int pos = atomicAdd(&hist[key(pr)], 1);
+      order[bh * pairs + pos] = pr;
+    }
   }
 }
 
-// Longest-first order of the query blocks of each (b, h), for the float32 path.
+// Longest-first order of the query blocks of each (b, h), for the float32 path; workgroup
+// blockIdx.x takes the heads blockIdx.x, blockIdx.x + gridDim.x, ...
 __global__ __launch_bounds__(1024) void k_row_order(const int32_t* __restrict__ counts, int32_t* __restrict__ order,
-                                                    int nb) {
+                                                    int nb, int bhs) {
   __shared__ int hist[kMaxBlocks + 1];
   __shared__ int scan_part[16];
   const int t = threadIdx.x;
-  const long long bh = blockIdx.x;
-  const int32_t* c = counts + bh * nb;
-  for (int v = t; v <= nb; v += 1024) hist[v] = 0;
-  __syncthreads();
-  for (int r = t; r < nb; r += 1024) atomicAdd(&hist[min(max(c[r], 0), nb)], 1);
-  __syncthreads();
-  desc_exclusive_scan(hist, nb + 1, scan_part);
-  for (int r = t; r < nb; r += 1024) {
-    const int p = atomicAdd(&hist[min(max(c[r], 0), nb)], 1);
-    order[bh * nb + p] = r;
+  for (long long bh = blockIdx.x; bh < bhs; bh += gridDim.x) {
+    const int32_t* c = counts + bh * nb;
+    __syncthreads();  // the previous head's placement is done with hist
+    for (int v = t; v <= nb; v += 1024) hist[v] = 0;
+    __syncthreads();
+    for (int r = t; r < nb; r += 1024) atomicAdd(&hist[min(max(c[r], 0), nb)], 1);
+    __syncthreads();
+    desc_exclusive_scan(hist, nb + 1, scan_part);
+    for (int r = t; r < nb; r += 1024) {
+      const int p = atomicAdd(&hist[min(max(c[r], 0), nb)], 1);
+      order[bh * nb + p] = r;
+    }
   }
 }
 
@@ -1072,8 +1087,8 @@ hipError_t launch_sparse_attn(const KGeom& g, int dtype, float scale, const void
     const int F = g.nbh * g.nbw;
     const int pairs = ((g.T + 1) / 2) * F;
     int32_t* mode = row_order + (long long)bhs * g.nb;  // after the order array (pairs <= nb per head)
-    k_pair_order<<<dim3(bhs > 8 ? bhs : 8), 1024, 0, s>>>(counts, row_order, mode, g.nb, F, pairs,
-                                                           (long long)bhs * g.nb);
+    k_pair_order<<<dim3(bhs < 8 ? 8 : bhs > kOrderGrid ? kOrderGrid : bhs), 1024, 0, s>>>(
+        counts, row_order, mode, g.nb, F, pairs, (long long)bhs * g.nb);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     AttnArgs a;
@@ -1115,7 +1130,7 @@ hipError_t launch_sparse_attn(const KGeom& g, int dtype, float scale, const void
       default: k_attn_bf16<64, false, false><<<grid, 256, 0, s>>>(a); break;
     }
   } else {
-    k_row_order<<<dim3(bhs), 1024, 0, s>>>(counts, row_order, g.nb);
+    k_row_order<<<dim3(bhs > kOrderGrid ? kOrderGrid : bhs), 1024, 0, s>>>(counts, row_order, g.nb, (int)bhs);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     AttnArgsF32 a;

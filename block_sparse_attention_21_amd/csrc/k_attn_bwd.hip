@@ -73,14 +73,16 @@ __global__ __launch_bounds__(256) void k_bwd_delta(const uint16_t* __restrict__ 
 // For key block j of each (b, h): the ascending list of query blocks whose mask row keeps j.
 // One wave per key block (four per workgroup): lane l tests row i0 + l, and a ballot places
 // the keeping rows of each 64-row chunk in order. (One thread per key block scanning all nb
-// rows left the GPU nearly idle: 36 workgroups at 480p.)
+// rows left the GPU nearly idle: 36 workgroups at 480p.) A one-dimensional grid of
+// ceil(nb / kColWaves) workgroups per (b, h).
 constexpr int kColWaves = 4;
 __global__ __launch_bounds__(64 * kColWaves) void k_col_lists(const uint32_t* __restrict__ words,
                                                               int32_t* __restrict__ col_counts,
                                                               int32_t* __restrict__ col_lists, int nb, int W) {
-  const long long bh = blockIdx.y;
+  const int per_head = (nb + kColWaves - 1) / kColWaves;
+  const long long bh = blockIdx.x / per_head;
   const int lane = threadIdx.x & 63;
-  const int j = blockIdx.x * kColWaves + (threadIdx.x >> 6);
+  const int j = ((int)blockIdx.x - (int)bh * per_head) * kColWaves + (threadIdx.x >> 6);
   if (j >= nb) return;  // whole waves
   const uint32_t* wcol = words + bh * nb * W + (j >> 5);
   const int bit = j & 31;
@@ -832,7 +834,7 @@ hipError_t launch_sparse_attn_bwd(const KGeom& g, int dtype, float scale, const 
     else
       k_bwd_delta_f32<64><<<dim3(fgrid), 256, 0, s>>>(of, dof, lse, ws.D, ws.L2, g);
     if ((e = hipGetLastError()) != hipSuccess) return e;
-    k_col_lists<<<dim3((unsigned)((g.nb + kColWaves - 1) / kColWaves), bhs), 64 * kColWaves, 0, s>>>(
+    k_col_lists<<<dim3((unsigned)((g.nb + kColWaves - 1) / kColWaves) * bhs), 64 * kColWaves, 0, s>>>(
         words, ws.col_counts, ws.col_lists, g.nb, (g.nb + 31) / 32);
     if ((e = hipGetLastError()) != hipSuccess) return e;
     BwdF32Args fa{static_cast<const float*>(q), static_cast<const float*>(k), static_cast<const float*>(v), dof,
@@ -859,7 +861,7 @@ hipError_t launch_sparse_attn_bwd(const KGeom& g, int dtype, float scale, const 
   else
     k_bwd_delta<64><<<dim3(dgrid), 256, 0, s>>>(o16, do16, lse, ws.D, ws.L2, g);
   if ((e = hipGetLastError()) != hipSuccess) return e;
-  k_col_lists<<<dim3((unsigned)((g.nb + kColWaves - 1) / kColWaves), bhs), 64 * kColWaves, 0, s>>>(
+  k_col_lists<<<dim3((unsigned)((g.nb + kColWaves - 1) / kColWaves) * bhs), 64 * kColWaves, 0, s>>>(
       words, ws.col_counts, ws.col_lists, g.nb, (g.nb + 31) / 32);
   if ((e = hipGetLastError()) != hipSuccess) return e;
 

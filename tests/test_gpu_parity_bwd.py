@@ -212,7 +212,7 @@ def _sampled(og, run, heads, n_rand_q=2, kcols=("max", "min", "rand")):
     return gm, picks
 
 
-def _compare_sampled(og, q, k, v, dout, gm, picks, dq, dk, dv, tag, o_given=None):
+def _compare_sampled(og, q, k, v, dout, gm, picks, dq, dk, dv, tag, o_given=None, dtype="bf16"):
     scale = 1.0 / math.sqrt(og.d)
     inv = np.argsort(R.fractal_positions(og))
     got = {n: [] for n in NAMES}
@@ -242,7 +242,7 @@ def _compare_sampled(og, q, k, v, dout, gm, picks, dq, dk, dv, tag, o_given=None
     errs = {n: PT.grad_errors(np.concatenate(got[n]), np.concatenate(ref[n])) for n in NAMES}
     print(f"{tag}: " + ", ".join(f"{n} rel {r:.2e} max {m:.2e}" for n, (r, m) in errs.items()), flush=True)
     for n in NAMES:
-        PT.compare_grad(np.concatenate(got[n]), np.concatenate(ref[n]), f"{tag} {n}")
+        PT.compare_grad(np.concatenate(got[n]), np.concatenate(ref[n]), f"{tag} {n}", dtype)
 
 
 def _setup(A, name, **over):
@@ -367,3 +367,45 @@ def test_backward_tiny_workload_end_to_end(A):
     run(q, k, v)
     torch.cuda.synchronize()
     _check_full(og, q, k, v, dout, PT.gpu_mask(run.words, og), qa.grad, ka.grad, va.grad, "tiny e2e", dtype="f32")
+
+
+MANY = [
+    # (name, dtype, d, (B, H, T, Hs, Ws), MaskParams kwargs)
+    ("4100-heads-long-lists", "bf16", 64, (1, 4100, 4, 40, 40), dict(mode="dyn", tau=1e9)),  # keep all, nb = 100
+    ("65600-heads-one-block", "bf16", 64, (1, 65600, 1, 8, 8), dict(mode="cdf", thr=0.5)),
+    ("4100-heads-f32", "f32", 64, (1, 4100, 4, 8, 8), dict(mode="cdf", thr=0.9)),
+]
+
+
+@pytest.mark.parametrize("case", MANY, ids=[c[0] for c in MANY])
+def test_many_heads_end_to_end(A, case):
+    """More (b, h) than the visiting-order kernels have workgroups (4096: each then takes several
+    heads; 4100 heads of 100 blocks put the bf16 forward in its longest-first mode, the float32
+    forward orders its rows the same way) and 65,600 one-block heads for the column lists' grid.
+    Forward output and LSE of whole heads, and the gradients of the GPU's own forward on sampled
+    blocks, against the oracle on the first head, the heads either side of 4096 and the last."""
+    name, dtype, d, geo, pkw = case
+    B, H, T, Hs, Ws = geo
+    geom, og = PT.geoms(B, H, T, Hs, Ws, d)
+    q, k, v = make_random_qkv(B, H, T, Hs, Ws, d, dtype, seed=51, device=DEV)
+    k = (k.float() + 0.25 * q.float()).to(q.dtype)
+    dout = make_dout(B, H, geom.N, d, seed=52, device=DEV).to(q.dtype)
+    run = A.NablaAttention(geom, A.MaskParams(**pkw), dtype=q.dtype, want_lse=True)
+    run(q, k, v)
+    dq, dk, dv = run.backward(q, k, v, dout)
+    torch.cuda.synchronize()
+    heads = sorted({0, 4095, 4096, H - 1} & set(range(H)))
+    gm = PT.gpu_mask(run.words, og)
+    scale = 1.0 / math.sqrt(og.d)
+    for h in heads:
+        Qr, gh = _head(q, 0, h, og)
+        Kr, _ = _head(k, 0, h, og)
+        Vr, _ = _head(v, 0, h, og)
+        Or, lse = R.masked_attention_head(Qr, Kr, Vr, gm[0, h], gh, scale)
+        PT.compare_attention(run.out[0, h].float().cpu().numpy(), R.inverse_reorder(Or, gh), dtype)
+        got = run.lse[0, h].cpu().numpy()
+        assert np.array_equal(np.isneginf(got), np.isneginf(lse))
+        fin = np.isfinite(lse)
+        np.testing.assert_allclose(got[fin], lse[fin], rtol=0, atol=2e-3 if dtype == "bf16" else 1e-4)
+    _, picks = _sampled(og, run, heads, n_rand_q=1, kcols=("min",))
+    _compare_sampled(og, q, k, v, dout, gm, picks, dq, dk, dv, f"{name} e2e", dtype=dtype)
