@@ -477,16 +477,20 @@ struct DkvArgs {
 // lane's key and queries qh*32 + 16*q8 + 8*hi + 0..7 (registers q8*8 .. q8*8+7 of s and dp),
 // then the dV^T and dK^T products over those queries. ta: the transpose-read addresses of the
 // Q tile for queries qh*32 ..; the dO tile sits two tiles further.
-template <int D, int DT, int Q8>
-__device__ __forceinline__ void half_step(const uint32_t* ta, const float* l2_lds, const float* d_lds, int qh, int hi,
-                                          float c2, const f32x16_t& s, const f32x16_t& dp, f32x16_t* dk,
-                                          f32x16_t* dv) {
+// Transpose-read addresses base + rel[k], formed right before each read block (an asm add is
+// not merged with the others, so the sums hold registers only while the reads are issued).
+template <int N>
+__device__ __forceinline__ void tr_addrs(const uint32_t* rel, uint32_t base, uint32_t (&out)[N]) {
+#pragma unroll
+  for (int k = 0; k < N; ++k) asm volatile("v_add_u32 %0, %1, %2" : "=v"(out[k]) : "s"(base), "v"(rel[k]));
+}
+
+template <int D, int DT, int Q8, typename NextLoads>
+__device__ __forceinline__ void half_step(const uint32_t* trel, uint32_t qbase, const f32x4v_t (&l2r)[2],
+                                          const f32x4v_t (&dr)[2], int hi, float c2, const f32x16_t& s,
+                                          const f32x16_t& dp, f32x16_t* dk, f32x16_t* dv, NextLoads next_loads) {
   constexpr int TB = kBlock * D * 2;
-  const int q0 = qh * 32 + 16 * Q8 + 8 * hi;
-  float4 la, lb, da, db;
-  lds_read4x16(reinterpret_cast<const char*>(l2_lds + q0), reinterpret_cast<const char*>(l2_lds + q0 + 4),
-               reinterpret_cast<const char*>(d_lds + q0), reinterpret_cast<const char*>(d_lds + q0 + 4), la, lb, da,
-               db);
+  const f32x4v_t la = l2r[0], lb = l2r[1], da = dr[0], db = dr[1];
   const float lq[8] = {la.x, la.y, la.z, la.w, lb.x, lb.y, lb.z, lb.w};
   const float dd[8] = {da.x, da.y, da.z, da.w, db.x, db.y, db.z, db.w};
   bf16x8_t pb, dsb;
@@ -500,14 +504,21 @@ __device__ __forceinline__ void half_step(const uint32_t* ta, const float* l2_ld
     dsb[e] = (__bf16)(p * (dp[Q8 * 8 + e] - dd[e]));
   }
   __builtin_amdgcn_s_setprio(0);
+  asm volatile("" ::: "memory");
+  next_loads();  // the next half's L2 / D, once this half's are consumed
+  asm volatile("" ::: "memory");
   {
     bf16x8_t ot[DT];
+    uint32_t ta[2 * DT];
+    tr_addrs(trel, qbase, ta);
     tr_chunks_at<DT, 2 * TB + Q8 * 16 * D * 2>(ta, ot);
 #pragma unroll
     for (int dt = 0; dt < DT; ++dt) dv[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ot[dt], pb, dv[dt], 0, 0, 0);
   }
   {
     bf16x8_t qt[DT];
+    uint32_t ta[2 * DT];
+    tr_addrs(trel, qbase, ta);
     tr_chunks_at<DT, Q8 * 16 * D * 2>(ta, qt);
 #pragma unroll
     for (int dt = 0; dt < DT; ++dt) dk[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qt[dt], dsb, dk[dt], 0, 0, 0);
@@ -515,14 +526,17 @@ __device__ __forceinline__ void half_step(const uint32_t* ta, const float* l2_ld
 }
 
 // One workgroup per key block j, four waves: wave (kh, qh) takes keys kh*32.. and queries
-// qh*32.. of every query tile in the block's column list. Q and dO tiles (token-major) and the
-// tiles' L2 / D rows are double-buffered in LDS.
+// qh*32.. of every query tile in the block's column list. Q and dO tiles (token-major) are
+// double-buffered in LDS; the key block's V tile stays in LDS for the whole walk (the B
+// operand of dP, read like a Q tile), its K rows in registers. Lane l's key is the one in LDS
+// row kh*32 + l%32 of such a tile (the tiles' row permutation), and the tiles' L2 / D rows come
+// straight from global memory (two 32-byte runs per lane and step, issued before the
+// products). Keeping V in registers too spilled 20 registers per lane at two waves per SIMD.
 template <int D>
 __global__ __launch_bounds__(kBwdThreads) __attribute__((amdgpu_waves_per_eu(2, 2))) void k_bwd_dkdv(DkvArgs a) {
   constexpr int TB = kBlock * D * 2;
   constexpr int DT = D / 32;
-  __shared__ __attribute__((aligned(1024))) char smem[4 * TB + 4 * kBlock * 4];  // Q0,Q1,dO0,dO1, L2/D x2
-  float* rows_lds = reinterpret_cast<float*>(smem + 4 * TB);                     // [slot][L2 | D][64]
+  __shared__ __attribute__((aligned(1024))) char smem[5 * TB];  // Q0, Q1, dO0, dO1, V of block j
   const KGeom& g = a.g;
   const int nb = g.nb;
   const int t = threadIdx.x, lane = t & 63, hi = lane >> 5;
@@ -535,27 +549,27 @@ __global__ __launch_bounds__(kBwdThreads) __attribute__((amdgpu_waves_per_eu(2, 
   const int j = gi - (int)bh * nb;
   const long long col = bh * nb + j;
   const int cnt = min(max(ld_const(a.col_counts, col), 0), nb);
-  const int k_local = kh * 32 + (lane & 31);
-  const long long mk = (long long)j * kBlock + k_local;  // fractal row of this lane's key
+  const int k_local = kperm(kh * 32 + (lane & 31));
 
-  bf16x8_t kb[D / 16], vb[D / 16];
-  {
-    const long long n = token_of(g, j, k_local);  // its token in the original order
-    const uint16_t* krow = a.k + (bh * g.N + n) * D + 8 * hi;
-    const uint16_t* vrow = a.v + (bh * g.N + n) * D + 8 * hi;
-#pragma unroll
-    for (int ks = 0; ks < D / 16; ++ks) {
-      kb[ks] = *reinterpret_cast<const bf16x8_t*>(krow + ks * 16);
-      vb[ks] = *reinterpret_cast<const bf16x8_t*>(vrow + ks * 16);
-    }
-  }
   const uint32_t head_bytes = (uint32_t)(g.N * D * 2);
   const i32x4_t qrs = make_rsrc(a.q + bh * g.N * D, head_bytes);
   const i32x4_t dors = make_rsrc(a.dout + bh * g.N * D, head_bytes);
-  const i32x4_t l2rs = make_rsrc(a.L2 + bh * g.N, (uint32_t)(g.N * 4));
-  const i32x4_t drs = make_rsrc(a.Dm + bh * g.N, (uint32_t)(g.N * 4));
   const uint32_t off = orig_tile_off<D>(t, g.Ws);
   const uint32_t stride = 512u * (uint32_t)g.Ws;
+  // The V rows of this wave's keys, addressed like its Q rows (the swizzle repeats every 16
+  // rows, so the two differ by a wave-uniform offset and share the per-lane offsets).
+  const char* v_lds_q = smem + 4 * TB + (kh - qh) * 32 * D * 2;
+  issue_rows<TB>(smem + 4 * TB, w, make_rsrc(a.v + bh * g.N * D, head_bytes), orig_tile_base<D>(g, j), off, stride);
+  bf16x8_t kb[D / 16];
+  {
+    const long long n = token_of(g, j, k_local);  // its token in the original order
+    const uint16_t* krow = a.k + (bh * g.N + n) * D + 8 * hi;
+#pragma unroll
+    for (int ks = 0; ks < D / 16; ++ks) kb[ks] = *reinterpret_cast<const bf16x8_t*>(krow + ks * 16);
+  }
+  const i32x4_t l2rs = make_rsrc(a.L2 + bh * g.N, (uint32_t)(g.N * 4));
+  const i32x4_t drs = make_rsrc(a.Dm + bh * g.N, (uint32_t)(g.N * 4));
+  const int rows_off = (qh * 32 + 8 * hi) * 4;  // byte offset of this lane's first query in a tile
 
   f32x16_t dk[DT], dv[DT];
 #pragma unroll
@@ -566,18 +580,11 @@ __global__ __launch_bounds__(kBwdThreads) __attribute__((amdgpu_waves_per_eu(2, 
       dv[dt][r] = 0.f;
     }
 
-  // Loads of query tile i into slot sl: Q and dO tiles, and 64 floats each of L2 and D (wave 0,
-  // lanes 0-15 with 16 bytes each).
+  // Loads of query tile i into slot sl: Q and dO tiles.
   auto issue = [&](int sl, int i) {
     const uint32_t base = orig_tile_base<D>(g, i);
     issue_rows<TB>(smem + sl * TB, w, qrs, base, off, stride);
     issue_rows<TB>(smem + (2 + sl) * TB, w, dors, base, off, stride);
-    if (t < 16) {
-      raw_buffer_load_lds(l2rs, (__attribute__((address_space(3))) uint32_t*)(rows_lds + sl * 128), 16, t * 16,
-                          i * kBlock * 4, 0, 0);
-      raw_buffer_load_lds(drs, (__attribute__((address_space(3))) uint32_t*)(rows_lds + sl * 128 + 64), 16, t * 16,
-                          i * kBlock * 4, 0, 0);
-    }
   };
   // Q^T / dO^T operand reads: offsets inside a Q tile for each channel tile (queries qh*32 ..);
   // the second 16 queries and the dO tile (two slots further) are immediate offsets.
@@ -586,14 +593,13 @@ __global__ __launch_bounds__(kBwdThreads) __attribute__((amdgpu_waves_per_eu(2, 
   for (int dt = 0; dt < DT; ++dt) tr_rel<D>(dt, qh * 32, lane, trel[2 * dt], trel[2 * dt + 1]);
 
   const int32_t* lst = a.col_lists + col * nb;
-  if (cnt > 0) issue(0, min(max(ld_const(lst, 0), 0), nb - 1));
+  int i_cur = cnt > 0 ? min(max(ld_const(lst, 0), 0), nb - 1) : 0;
+  if (cnt > 0) issue(0, i_cur);
   for (int u = 0; u < cnt; ++u) {
-    wait_vm_lgkm_barrier();  // tile u has landed; every wave is done with tile u-1
+    wait_vm_lgkm_barrier();  // tile u (and, first, the V tile) has landed; every wave is done with tile u-1
     const int i_next = u + 1 < cnt ? min(max(ld_const(lst, u + 1), 0), nb - 1) : -1;
     const char* q_lds = smem + (u & 1) * TB;
     const char* do_lds = smem + (2 + (u & 1)) * TB;
-    const float* l2_lds = rows_lds + (u & 1) * 128;
-    const float* d_lds = l2_lds + 64;
 
     // S = Q K^T and dP = dO V^T for queries qh*32.. (rows) and this lane's key (column):
     // register r holds query qh*32 + 16*(r/8) + 8*hi + r%8.
@@ -606,22 +612,35 @@ __global__ __launch_bounds__(kBwdThreads) __attribute__((amdgpu_waves_per_eu(2, 
 #pragma unroll
     for (int ks = 0; ks < D / 16; ++ks) {
       s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(row_chunk<D>(q_lds, qh, lane, ks), kb[ks], s, 0, 0, 0);
-      dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(row_chunk<D>(do_lds, qh, lane, ks), vb[ks], dp, 0, 0, 0);
+      dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(row_chunk<D>(do_lds, qh, lane, ks),
+                                                   row_chunk<D>(v_lds_q, qh, lane, ks), dp, 0, 0, 0);
     }
     // The next tile's loads go out here, after the products that read the registers this
     // kernel keeps in scratch: a wait for those reloads would otherwise also wait for the
     // prefetch, which shares their counter.
+    // L2 and D of queries qh*32 + 16*q8 + 8*hi + 0..7 of tile u, each half q8's loaded just
+    // before the half before it, so that they hold no registers during the products.
+    const int tile_off = i_cur * kBlock * 4;
+    f32x4v_t l2r[2], dr[2];
+    l2r[0] = raw_buffer_load_f32x4(l2rs, rows_off, tile_off, 0);
+    l2r[1] = raw_buffer_load_f32x4(l2rs, rows_off + 16, tile_off, 0);
+    dr[0] = raw_buffer_load_f32x4(drs, rows_off, tile_off, 0);
+    dr[1] = raw_buffer_load_f32x4(drs, rows_off + 16, tile_off, 0);
     asm volatile("" ::: "memory");
     if (i_next >= 0) issue((u + 1) & 1, i_next);
     // Per 16-query half q8: P and dS for this lane's key, then dV^T += dO^T P and
     // dK^T += Q^T dS over those queries, the transposed operands from transpose loads (one
     // half's operands live at a time).
-    uint32_t ta[2 * DT];
-    const uint32_t qbase = lds_offset(q_lds);
-#pragma unroll
-    for (int k = 0; k < 2 * DT; ++k) ta[k] = qbase + trel[k];
-    half_step<D, DT, 0>(ta, l2_lds, d_lds, qh, hi, a.c2, s, dp, dk, dv);
-    half_step<D, DT, 1>(ta, l2_lds, d_lds, qh, hi, a.c2, s, dp, dk, dv);
+    const uint32_t qbase = __builtin_amdgcn_readfirstlane(lds_offset(q_lds));
+    f32x4v_t l2s[2], ds[2];
+    half_step<D, DT, 0>(trel, qbase, l2r, dr, hi, a.c2, s, dp, dk, dv, [&] {
+      l2s[0] = raw_buffer_load_f32x4(l2rs, rows_off + 64, tile_off, 0);
+      l2s[1] = raw_buffer_load_f32x4(l2rs, rows_off + 80, tile_off, 0);
+      ds[0] = raw_buffer_load_f32x4(drs, rows_off + 64, tile_off, 0);
+      ds[1] = raw_buffer_load_f32x4(drs, rows_off + 80, tile_off, 0);
+    });
+    half_step<D, DT, 1>(trel, qbase, l2s, ds, hi, a.c2, s, dp, dk, dv, [] {});
+    i_cur = i_next;
   }
   // Waves (kh, 0) and (kh, 1) hold partial dK^T and dV^T over their query halves: wave qh = 0
   // finishes dK, wave qh = 1 finishes dV; each hands the other its partial.

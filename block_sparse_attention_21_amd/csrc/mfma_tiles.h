@@ -99,6 +99,11 @@ __device__ void raw_buffer_load_lds(i32x4_t rsrc, __attribute__((address_space(3
                                     int voffset, int soffset, int offset, int aux)
     __asm("llvm.amdgcn.raw.buffer.load.lds");
 
+// Plain 16-byte buffer load into registers (bounds-checked against the resource's size).
+typedef float f32x4v_t __attribute__((ext_vector_type(4)));
+__device__ f32x4v_t raw_buffer_load_f32x4(i32x4_t rsrc, int voffset, int soffset, int aux)
+    __asm("llvm.amdgcn.raw.buffer.load.v4f32");
+
 __device__ __forceinline__ i32x4_t make_rsrc(const void* base, uint32_t bytes) {
   const uint64_t p = reinterpret_cast<uint64_t>(base);
   i32x4_t r;
