@@ -507,21 +507,26 @@ __device__ __forceinline__ void half_step(const uint32_t* trel, uint32_t qbase, 
   asm volatile("" ::: "memory");
   next_loads();  // the next half's L2 / D, once this half's are consumed
   asm volatile("" ::: "memory");
-  {
-    bf16x8_t ot[DT];
-    uint32_t ta[2 * DT];
-    tr_addrs(trel, qbase, ta);
-    tr_chunks_at<DT, 2 * TB + Q8 * 16 * D * 2>(ta, ot);
+  // Two channel tiles' transposed operands at a time (fewer registers held by the reads).
 #pragma unroll
-    for (int dt = 0; dt < DT; ++dt) dv[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ot[dt], pb, dv[dt], 0, 0, 0);
+  for (int h2 = 0; h2 < DT / 2; ++h2) {
+    bf16x8_t ot[2];
+    uint32_t ta[4];
+    tr_addrs(trel + 4 * h2, qbase, ta);
+    tr_chunks_at<2, 2 * TB + Q8 * 16 * D * 2>(ta, ot);
+#pragma unroll
+    for (int e = 0; e < 2; ++e)
+      dv[2 * h2 + e] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ot[e], pb, dv[2 * h2 + e], 0, 0, 0);
   }
-  {
-    bf16x8_t qt[DT];
-    uint32_t ta[2 * DT];
-    tr_addrs(trel, qbase, ta);
-    tr_chunks_at<DT, Q8 * 16 * D * 2>(ta, qt);
 #pragma unroll
-    for (int dt = 0; dt < DT; ++dt) dk[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qt[dt], dsb, dk[dt], 0, 0, 0);
+  for (int h2 = 0; h2 < DT / 2; ++h2) {
+    bf16x8_t qt[2];
+    uint32_t ta[4];
+    tr_addrs(trel + 4 * h2, qbase, ta);
+    tr_chunks_at<2, Q8 * 16 * D * 2>(ta, qt);
+#pragma unroll
+    for (int e = 0; e < 2; ++e)
+      dk[2 * h2 + e] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qt[e], dsb, dk[2 * h2 + e], 0, 0, 0);
   }
 }
 

@@ -220,20 +220,5 @@ __device__ __forceinline__ void tr_chunks_at(const uint32_t* a, bf16x8_t (&out)[
     tr_chunks_at_2<OFF>(a, out);
 }
 
-// Four 16-byte LDS reads through inline asm, completed inside the block (lgkmcnt(0)). For
-// LDS rows that sit next to a slot being filled by an LDS DMA: a plain read there gets a
-// wait for every load in flight, the prefetch included (see tr_chunks_at).
-__device__ __forceinline__ void lds_read4x16(const char* p0, const char* p1, const char* p2, const char* p3,
-                                             float4& r0, float4& r1, float4& r2, float4& r3) {
-  asm volatile(
-      "ds_read_b128 %0, %4\n\t"
-      "ds_read_b128 %1, %5\n\t"
-      "ds_read_b128 %2, %6\n\t"
-      "ds_read_b128 %3, %7\n\t"
-      "s_waitcnt lgkmcnt(0)"
-      : "=&v"(r0), "=&v"(r1), "=&v"(r2), "=&v"(r3)
-      : "v"(lds_offset(p0)), "v"(lds_offset(p1)), "v"(lds_offset(p2)), "v"(lds_offset(p3)));
-}
-
 }  // namespace
 }  // namespace abla
