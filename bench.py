@@ -203,18 +203,34 @@ def measure(name, steps, warmup, use_graph=False):
         step()
     torch.cuda.synchronize()
 
-    # The timed region: exactly `steps` whole-path steps.
+    # The timed region: exactly `steps` whole-path steps. Eagerly launched, each step's attention
+    # call (the visiting-order kernel and the attention kernel) sits between two HIP events on
+    # the stream, which gives the attention's duration inside the layer from the same steps.
+    marks = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
+    done = []
+
+    def step_marked():
+        run.reorder_pool(q, k, v)
+        run.mask()
+        a, b = marks[len(done)]
+        a.record(stream)
+        run.attend()
+        b.record(stream)
+        done.append(1)
+
     torch.cuda.synchronize()
     t0 = time.perf_counter()
-    ms_step = timed(step, steps, stream)
+    ms_step = timed(step if graph is not None else step_marked, steps, stream)
     wall = (time.perf_counter() - t0) * 1e3 / steps
+    ms_attn_layer = sum(a.elapsed_time(b) for a, b in marks) / steps if graph is None else None
     ms_eager = timed(lambda: run(q, k, v), steps, stream) if graph is not None else ms_step
 
     # Per-stage averages (same inputs, state left by the path).
     ms_reorder = timed(lambda: run.reorder_pool(q, k, v), steps, stream)
     ms_reorder_graph = graph_ms(lambda: run.reorder_pool(q, k, v))
     ms_mask = timed(run.mask, steps, stream)
-    ms_attn = timed(run.attend, steps, stream)
+    ms_attn_stage = timed(run.attend, steps, stream)  # back to back, no other stage between
+    ms_attn = ms_attn_layer if ms_attn_layer is not None else ms_attn_stage
 
     # Then the spread of single steps, and single steps each started after writing EVICT_BYTES
     # of scratch (so no input is left in the last-level cache).
@@ -236,7 +252,8 @@ def measure(name, steps, warmup, use_graph=False):
     return dict(
         w=w, geom=geom, kept=kept, keep_fraction=kept / total, ms_step=ms_step, wall_ms_step=wall, ms_eager=ms_eager,
         graph=graph is not None, warm=warm, cold=cold,
-        ms_reorder=ms_reorder, ms_mask=ms_mask, ms_attn=ms_attn, dense_flops=dense, kept_flops=kept_fl,
+        ms_reorder=ms_reorder, ms_mask=ms_mask, ms_attn=ms_attn, ms_attn_stage=ms_attn_stage,
+        attn_in_layer=ms_attn_layer is not None, dense_flops=dense, kept_flops=kept_fl,
         reorder_gbs=reorder_bytes / (ms_reorder * 1e-3) / 1e9, tensor_bytes=tensor_bytes,
         ms_reorder_graph=ms_reorder_graph, reorder_gbs_graph=reorder_bytes / (ms_reorder_graph * 1e-3) / 1e9,
         counts=run.counts, run=run, q=q, k=k, v=v,
@@ -348,7 +365,8 @@ def report(args):
           f"(datasheet {MFMA_BF16_PEAK_TFLOPS:,.0f} / {FP32_PEAK_TFLOPS}); HBM streams (libabla_probe, 2 GiB): "
           f"read {hbm_read:,.0f} GB/s, copy {hbm_copy:,.0f} GB/s (datasheet {HBM_PEAK_GBS:,.0f})\n")
     fwd_attn_ms = {}
-    print("| workload | mask | keep | first step ms (TB/s); kernel-only from a graph | mask ms (GB/s) | attention ms | layer ms | "
+    print("| workload | mask | keep | first step ms (TB/s); kernel-only from a graph | mask ms (GB/s) | "
+          "attention ms: in the layer / back to back | layer ms | "
           "single layers: median / min / cold median ms | "
           "dense-eq TFLOP/s (layer / attn) | actual TFLOP/s | of datasheet peak | of MFMA loop | of GEMM ref | "
           "keep per head |")
@@ -371,7 +389,8 @@ def report(args):
         print(f"| {w.name} ({w.dtype}, {w.N} tok) | {mode} | {r['keep_fraction']:.4f} | "
               f"{r['ms_reorder']:.4f} ({r['reorder_gbs'] / 1e3:.2f}); {r['ms_reorder_graph']:.4f} "
               f"({r['reorder_gbs_graph'] / 1e3:.2f}) | {r['ms_mask']:.4f} "
-              f"({mask_bytes / (r['ms_mask'] * 1e-3) / 1e9:,.0f}) | {r['ms_attn']:.4f} | {r['ms_step']:.4f} | "
+              f"({mask_bytes / (r['ms_mask'] * 1e-3) / 1e9:,.0f}) | {r['ms_attn']:.4f} / {r['ms_attn_stage']:.4f} | "
+              f"{r['ms_step']:.4f} | "
               f"{median(r['warm']):.4f} / {r['warm'][0]:.4f} / {median(r['cold']):.4f} | "
               f"{r['dense_flops'] / (r['ms_step'] * 1e-3) / 1e12:,.1f} / "
               f"{r['dense_flops'] / (r['ms_attn'] * 1e-3) / 1e12:,.1f} | {attn_tf:,.1f} | "
@@ -465,7 +484,8 @@ def main():
         "cold_cache": {"reps": len(r["cold"]), "evict_bytes": EVICT_BYTES, "ms_median": round(median(r["cold"]), 4),
                        "ms_min": round(r["cold"][0], 4)},
         "ms_per_stage": {"reorder_pool_qkv": round(r["ms_reorder"], 4), "mask": round(r["ms_mask"], 4),
-                         "attention": round(r["ms_attn"], 4)},
+                         "attention": round(r["ms_attn_stage"], 4)},
+        "ms_attention_in_layer": round(r["ms_attn"], 4) if r["attn_in_layer"] else None,
         "keep_fraction": round(r["keep_fraction"], 5),
         "attention_actual_tflops": round(attn_tflops, 2),
         "reorder_pool_gbs": round(r["reorder_gbs"], 1),
@@ -480,6 +500,10 @@ def main():
         "roofline": {
             "kernel": ("k_attn_f32" if f32 else "k_attn_bf16") + " (block-sparse attention forward)",
             "bound": "mfma",
+            "ms_per_launch": round(r["ms_attn"], 4),
+            "timing": ("HIP events around the attention entry point (visiting-order kernel + attention kernel) "
+                       "inside each timed step" if r["attn_in_layer"] else
+                       "HIP events around back-to-back attention entry-point calls (graph mode)"),
             "achieved": round(attn_tflops, 2),
             "peak": peak,
             "unit": "TFLOP/s",
@@ -500,7 +524,8 @@ def main():
                                   if s["w"].dtype == w.dtype else None),
             "keep_fraction": round(s["keep_fraction"], 5),
             "ms_per_stage": {"reorder_pool_qkv": round(s["ms_reorder"], 4), "mask": round(s["ms_mask"], 4),
-                             "attention": round(s["ms_attn"], 4)},
+                             "attention": round(s["ms_attn_stage"], 4)},
+            "ms_attention_in_layer": round(s["ms_attn"], 4) if s["attn_in_layer"] else None,
             "reorder_pool_gbs": round(s["reorder_gbs"], 1),
             "reorder_pool_gbs_kernel_graph": round(s["reorder_gbs_graph"], 1),
             "single_steps_ms_median": round(median(s["warm"]), 4),
