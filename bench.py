@@ -201,6 +201,8 @@ def measure(name, steps, warmup, use_graph=False):
     step = graph.replay if graph is not None else (lambda: run(q, k, v))
     for _ in range(warmup):
         step()
+    if run._decide_v:  # no warm-up step made the V-path choice: make it outside the timed region
+        run(q, k, v)
     torch.cuda.synchronize()
 
     # The timed region: exactly `steps` whole-path steps. Eagerly launched, each step's attention
@@ -247,16 +249,17 @@ def measure(name, steps, warmup, use_graph=False):
     tensor_bytes = w.B * w.H * w.N * w.d * elem
     pooled_bytes = w.B * w.H * w.nb * w.d * 8
     # Q and K are read once for pooling (the attention reads them in the original order); V is
-    # read and written channel-major; plus the pooled means.
-    reorder_bytes = 4 * tensor_bytes + 2 * pooled_bytes
+    # read and written channel-major unless the attention reads it in the original order; plus
+    # the pooled means.
+    reorder_bytes = (2 if run.fuse_v else 4) * tensor_bytes + 2 * pooled_bytes
     return dict(
         w=w, geom=geom, kept=kept, keep_fraction=kept / total, ms_step=ms_step, wall_ms_step=wall, ms_eager=ms_eager,
         graph=graph is not None, warm=warm, cold=cold,
         ms_reorder=ms_reorder, ms_mask=ms_mask, ms_attn=ms_attn, ms_attn_stage=ms_attn_stage,
         attn_in_layer=ms_attn_layer is not None, dense_flops=dense, kept_flops=kept_fl,
-        reorder_gbs=reorder_bytes / (ms_reorder * 1e-3) / 1e9, tensor_bytes=tensor_bytes,
+        reorder_gbs=reorder_bytes / (ms_reorder * 1e-3) / 1e9, tensor_bytes=tensor_bytes, reorder_bytes=reorder_bytes,
         ms_reorder_graph=ms_reorder_graph, reorder_gbs_graph=reorder_bytes / (ms_reorder_graph * 1e-3) / 1e9,
-        counts=run.counts, run=run, q=q, k=k, v=v,
+        counts=run.counts, run=run, q=q, k=k, v=v, v_original=run.fuse_v,
     )
 
 
@@ -476,6 +479,7 @@ def main():
             "blocks": w.nb, "mask": w.mode, "thr": w.thr if w.mode == "cdf" else None,
             "tau": w.tau if w.mode == "dyn" else None, "sta": list(w.sta), "parallelism": "none (1 GPU)",
             "launch": "hip graph replay of the whole step" if r["graph"] else "eager",
+            "v_read": "original order (no V pass)" if r["v_original"] else "channel-major blocks (V pass)",
         },
         "ms_per_layer": round(r["ms_step"], 4),
         "ms_per_layer_eager": round(r["ms_eager"], 4),
@@ -490,7 +494,8 @@ def main():
         "attention_actual_tflops": round(attn_tflops, 2),
         "reorder_pool_gbs": round(r["reorder_gbs"], 1),
         "first_step": {
-            "kernel": "k_pool_qk_reorder_v (pool Q and K, reorder V)", "bound": "hbm",
+            "kernel": "k_pool_qk_reorder_v (pool Q and K" + (")" if r["v_original"] else ", reorder V)"),
+            "bound": "hbm", "bytes": int(r["reorder_bytes"]),
             "gbs_stage": round(r["reorder_gbs"], 1),
             "gbs_kernel_graph": round(r["reorder_gbs_graph"], 1),
             "ms_kernel_graph": round(r["ms_reorder_graph"], 4),

@@ -203,25 +203,31 @@ def reorder(x: torch.Tensor, geom: Geometry, *, inverse: bool = False, layout: s
     return (out, pooled) if pooled is not None else out
 
 
-def pool_qk_reorder_v(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, geom: Geometry, *,
+def pool_qk_reorder_v(q: torch.Tensor, k: torch.Tensor, v: Optional[torch.Tensor], geom: Geometry, *,
                       qbar: Optional[torch.Tensor] = None, kbar: Optional[torch.Tensor] = None,
                       v_rt: Optional[torch.Tensor] = None):
     """abla_pool_qk_reorder_v: float64 block means of q and k and v in channel-major fractal
-    blocks, in one launch. Returns (qbar, kbar, v_rt)."""
+    blocks, in one launch. Returns (qbar, kbar, v_rt); with v None only q and k are pooled
+    (v_rt None)."""
     dev = _device(q)
     if q.dtype not in _DT:
         raise ValueError(f"unsupported dtype {q.dtype}")
     shape = (geom.B, geom.H, geom.N, geom.d)
-    for name, x in (("q", q), ("k", k), ("v", v)):
+    for name, x in (("q", q), ("k", k)) + ((("v", v),) if v is not None else ()):
         _need(x, name, shape, q.dtype, dev)
     pshape = (geom.B, geom.H, geom.nb, geom.d)
     qbar = torch.empty(pshape, dtype=torch.float64, device=dev) if qbar is None else qbar
     kbar = torch.empty(pshape, dtype=torch.float64, device=dev) if kbar is None else kbar
     vshape = (geom.B, geom.H, geom.nb, geom.d, 64)
-    v_rt = torch.empty(vshape, dtype=q.dtype, device=dev) if v_rt is None else v_rt
+    if v is None:
+        if v_rt is not None:
+            raise ValueError("v_rt is an output of the V reorder; pass v with it")
+    elif v_rt is None:
+        v_rt = torch.empty(vshape, dtype=q.dtype, device=dev)
     _need(qbar, "qbar", pshape, torch.float64, dev)
     _need(kbar, "kbar", pshape, torch.float64, dev)
-    _need(v_rt, "v_rt", vshape, q.dtype, dev)
+    if v_rt is not None:
+        _need(v_rt, "v_rt", vshape, q.dtype, dev)
     g = geom.c()
     _check(_lib.abla_pool_qk_reorder_v(ctypes.byref(g), _DT[q.dtype], _ptr(q), _ptr(k), _ptr(v), _ptr(qbar),
                                        _ptr(kbar), _ptr(v_rt), _stream(q)), "abla_pool_qk_reorder_v")
@@ -371,6 +377,13 @@ def sparse_attn_bwd(q, k, v, o, dout, lse, words, counts, lists, geom: Geometry,
     return dq, dk, dv
 
 
+# Mean kept blocks per mask row up to which the bf16 attention reads V in the original order by
+# default: short lists spend little time on V^T reads, so the V reorder pass costs more than its
+# channel-major operands save (whole layer at 480p, mean 56 blocks: 1-3% faster without the pass;
+# at 720p, mean 523: 3% slower).
+FUSE_V_MAX_MEAN_COUNT = 60
+
+
 class NablaAttention:
     """The whole forward path for one geometry, with every buffer allocated once.
 
@@ -384,13 +397,23 @@ class NablaAttention:
 
     __call__ returns self.out, the same tensor on every call: the next call overwrites it. Keep
     a result across calls with .clone(), or pass out= to have the attention write elsewhere.
+
+    fuse_v: True reads V in its original order in the attention (no V reorder); False reorders
+    V into channel-major blocks in the first step; None (the default) takes True for float32
+    and, for bfloat16, decides on the first call from its mask: True when the mean kept count
+    per row is at most FUSE_V_MAX_MEAN_COUNT blocks (short lists, where skipping the V pass
+    saves more than the original-order V reads cost), else False. Both give bit-identical
+    outputs. The decision reads the counts back once (a stream synchronisation on the first
+    call only, which capture() makes outside the graph).
     """
 
     def __init__(self, geom: Geometry, params: MaskParams, dtype=torch.bfloat16, device="cuda",
                  scale: float = 0.0, want_lse: bool = False, fused: bool = True, fuse_v: Optional[bool] = None):
         self.geom, self.params, self.scale, self.fused = geom, params, scale, fused
         # float32 stages its tiles through registers, so V in the original order costs nothing
-        # there; bf16 reads V^T operands from channel-major blocks (one LDS read per product).
+        # there; bf16 reads V^T operands from channel-major blocks (one LDS read per product)
+        # unless the lists are short (the first call decides).
+        self._decide_v = fused and fuse_v is None and dtype != torch.float32
         if fuse_v is None:
             fuse_v = dtype == torch.float32
         self.fuse_v = fused and fuse_v
@@ -414,20 +437,16 @@ class NablaAttention:
         self.ws_attn = torch.empty(max(sparse_attn_workspace_bytes(g), 1), dtype=torch.uint8, device=dev)
 
     def reorder_pool(self, q, k, v):
-        if self.fused and not self.fuse_v:
-            # One launch: Q and K pooled in place, V reordered channel-major.
-            pool_qk_reorder_v(q, k, v, self.geom, qbar=self.qbar, kbar=self.kbar, v_rt=self.v_rt)
+        if self.fused:
+            # One launch: Q and K pooled in place, and V reordered channel-major unless the
+            # attention reads it in the original order.
+            pool_qk_reorder_v(q, k, None if self.fuse_v else v, self.geom, qbar=self.qbar, kbar=self.kbar,
+                              v_rt=None if self.fuse_v else self.v_rt)
             self._q, self._k, self._v = q, k, v
             return
-        if self.fused:
-            reorder(q, self.geom, pooled=self.qbar, pool_only=True)
-            reorder(k, self.geom, pooled=self.kbar, pool_only=True)
-            self._q, self._k, self._v = q, k, v
-        else:
-            reorder(q, self.geom, out=self.q_r, pooled=self.qbar)
-            reorder(k, self.geom, out=self.k_r, pooled=self.kbar)
-        if not self.fuse_v:
-            reorder(v, self.geom, layout="block_t", out=self.v_rt)
+        reorder(q, self.geom, out=self.q_r, pooled=self.qbar)
+        reorder(k, self.geom, out=self.k_r, pooled=self.kbar)
+        reorder(v, self.geom, layout="block_t", out=self.v_rt)
 
     def mask(self):
         build_mask(self.qbar, self.kbar, self.geom, self.params, words=self.words, counts=self.counts,
@@ -451,7 +470,18 @@ class NablaAttention:
         (reused by the next call)."""
         self.reorder_pool(q, k, v)
         self.mask()
+        if self._decide_v:
+            self.choose_v_path()
         return self.attend(out)
+
+    def choose_v_path(self):
+        """The fuse_v=None decision from the current mask (reads the counts back: synchronises)."""
+        self._decide_v = False
+        g = self.geom
+        mean = float(self.counts.sum().item()) / (g.B * g.H * g.nb)
+        if mean <= FUSE_V_MAX_MEAN_COUNT:
+            self.fuse_v = True
+            self.v_rt = None
 
     def backward(self, q, k, v, dout, workspace=None):
         """Gradients (dq, dk, dv) of the last __call__(q, k, v) for the incoming gradient dout
@@ -499,7 +529,10 @@ class _NablaAttentionFn(torch.autograd.Function):
 
     @staticmethod
     def forward(ctx, q, k, v, geom, params, scale):
-        run = NablaAttention(geom, params, dtype=q.dtype, device=q.device, scale=scale, want_lse=True)
+        # A new object per call: the V path is fixed (channel-major pass for bf16) rather than
+        # decided from the mask, which would synchronise on every call.
+        run = NablaAttention(geom, params, dtype=q.dtype, device=q.device, scale=scale, want_lse=True,
+                             fuse_v=q.dtype == torch.float32)
         out = run(q, k, v)
         ctx.geom, ctx.scale = geom, scale
         ctx.save_for_backward(q, k, v, out, run.lse, run.words, run.counts, run.lists)

@@ -187,18 +187,21 @@ abla_status abla_pool_qk_reorder_v(const abla_geom* g, int32_t dtype, const void
                                    double* qbar, double* kbar, void* v_rt, void* stream) {
   abla_status st = check_geom(g);
   if (st != ABLA_OK) return st;
-  if (!valid_dtype(dtype) || !q || !k || !v || !qbar || !kbar || !v_rt) return ABLA_ERR_INVALID;
-  if (!aligned16({q, k, v, qbar, kbar, v_rt})) return ABLA_ERR_INVALID;
+  if (!valid_dtype(dtype) || !q || !k || !qbar || !kbar || (!v != !v_rt)) return ABLA_ERR_INVALID;
+  const bool with_v = v != nullptr;  // else pool q and k only
+  if (!aligned16({q, k, qbar, kbar}) || (with_v && !aligned16({v, v_rt}))) return ABLA_ERR_INVALID;
   if ((long double)3 * bh_of(g) * nb_of(g) > (long double)INT_MAX) return ABLA_ERR_UNSUPPORTED;  // grid size
   const size_t bytes = tok_elems(g) * elem_bytes(dtype);
   const size_t pbytes = bh_of(g) * (size_t)nb_of(g) * (size_t)g->d * sizeof(double);
+  const size_t vbytes = with_v ? bytes : 0;  // overlaps() of an empty range is false
   // Outputs must overlap no input and no other output.
   const void* ins[3] = {q, k, v};
   for (const void* in : ins)
-    if (overlaps(v_rt, bytes, in, bytes) || overlaps(qbar, pbytes, in, bytes) || overlaps(kbar, pbytes, in, bytes))
+    if (in && (overlaps(v_rt, vbytes, in, bytes) || overlaps(qbar, pbytes, in, bytes) ||
+               overlaps(kbar, pbytes, in, bytes)))
       return ABLA_ERR_INVALID;
-  if (overlaps(qbar, pbytes, kbar, pbytes) || overlaps(qbar, pbytes, v_rt, bytes) ||
-      overlaps(kbar, pbytes, v_rt, bytes))
+  if (overlaps(qbar, pbytes, kbar, pbytes) || overlaps(qbar, pbytes, v_rt, vbytes) ||
+      overlaps(kbar, pbytes, v_rt, vbytes))
     return ABLA_ERR_INVALID;
   return from_hip(launch_pool_qk_reorder_v(make_kgeom(*g), dtype, q, k, v, qbar, kbar, v_rt, (hipStream_t)stream));
 }

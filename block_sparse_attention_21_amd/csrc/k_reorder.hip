@@ -149,21 +149,23 @@ __global__ __launch_bounds__(kThreads) void k_reorder_fwd(const E* __restrict__ 
 // b < n = B*H*nb (workgroup `first` + blockIdx.x of the whole grid, which larger inputs split
 // into several launches). One grid instead of three saves two launch gaps and two ramp-down tails;
 // interleaving the read-only pooling with the read-write reorder (rather than Q, then K,
-// then V) measured 5% faster at 480p and 720p (5.6 TB/s for the stage).
-template <typename E, int D>
+// then V) measured 5% faster at 480p and 720p (5.6 TB/s for the stage). With WITH_V false
+// the grid is 2*n workgroups pooling Q (2b) and K (2b+1) only.
+template <typename E, int D, bool WITH_V>
 __global__ __launch_bounds__(kThreads) void k_pool_qk_reorder_v(const E* __restrict__ q, const E* __restrict__ k,
                                                                 const E* __restrict__ v, double* __restrict__ qbar,
                                                                 double* __restrict__ kbar, E* __restrict__ vrt,
                                                                 KGeom g, int first) {
   __shared__ __attribute__((aligned(16))) char smem[kSmemBytes<E, D>];
+  constexpr int kParts = WITH_V ? 3 : 2;
   const int wg = first + (int)blockIdx.x;
-  const int which = wg % 3;
-  const int blk = wg / 3;
+  const int which = wg % kParts;
+  const int blk = wg / kParts;
   if (which == 0)
     reorder_block<E, D, true, false, false>(q, nullptr, qbar, g, blk, smem);
   else if (which == 1)
     reorder_block<E, D, true, false, false>(k, nullptr, kbar, g, blk, smem);
-  else
+  else if constexpr (WITH_V)
     reorder_block<E, D, false, true, true>(v, vrt, nullptr, g, blk, smem);
 }
 
@@ -222,11 +224,18 @@ hipError_t dispatch(const KGeom& g, int inverse, int layout, const void* x, void
 template <typename E, int D>
 hipError_t dispatch_qkv(const KGeom& g, const void* q, const void* k, const void* v, double* qbar, double* kbar,
                         void* vrt, hipStream_t s) {
-  const int total = (int)(3LL * g.B * g.H * g.nb);
-  for (int first = 0; first < total; first += kChunk)
-    k_pool_qk_reorder_v<E, D><<<dim3((unsigned)min(kChunk, total - first)), kThreads, 0, s>>>(
-        static_cast<const E*>(q), static_cast<const E*>(k), static_cast<const E*>(v), qbar, kbar,
-        static_cast<E*>(vrt), g, first);
+  const bool with_v = v != nullptr;
+  const int total = (int)((with_v ? 3LL : 2LL) * g.B * g.H * g.nb);
+  for (int first = 0; first < total; first += kChunk) {
+    const dim3 grid((unsigned)min(kChunk, total - first));
+    if (with_v)
+      k_pool_qk_reorder_v<E, D, true><<<grid, kThreads, 0, s>>>(static_cast<const E*>(q), static_cast<const E*>(k),
+                                                                static_cast<const E*>(v), qbar, kbar,
+                                                                static_cast<E*>(vrt), g, first);
+    else
+      k_pool_qk_reorder_v<E, D, false><<<grid, kThreads, 0, s>>>(static_cast<const E*>(q), static_cast<const E*>(k),
+                                                                 nullptr, qbar, kbar, nullptr, g, first);
+  }
   return hipGetLastError();
 }
 

@@ -124,10 +124,12 @@ abla_status abla_reorder(const abla_geom* g, int32_t dtype, int32_t inverse, int
  * Source: NABLA, Method -- "Fractal Flattening" and "down-sampling" (as abla_reorder).
  * q, k, v: [B,H,N,d] of `dtype` in the original token order.
  * qbar, kbar: [B,H,nb,d] float64 outputs; v_rt: [B,H,nb,d,64] of `dtype` output.
- * One grid of 3*B*H*nb workgroups instead of three launches.
- * Errors: INVALID for null pointers, unknown dtype, bad geometry, an output overlapping an
- * input or another output; UNSUPPORTED for the geometry limits of abla_reorder or
- * 3*B*H*nb above 2^31 - 1. */
+ * One grid of 3*B*H*nb workgroups instead of three launches. With v = v_rt = NULL only q
+ * and k are pooled, in one grid of 2*B*H*nb workgroups (the first step when the attention
+ * reads V in the original order, ABLA_ATTN_V_ORIGINAL).
+ * Errors: INVALID for a null q, k, qbar or kbar, exactly one of v and v_rt null, unknown
+ * dtype, bad geometry, an output overlapping an input or another output; UNSUPPORTED for
+ * the geometry limits of abla_reorder or 3*B*H*nb above 2^31 - 1. */
 abla_status abla_pool_qk_reorder_v(const abla_geom* g, int32_t dtype, const void* q, const void* k, const void* v,
                                    double* qbar, double* kbar, void* v_rt, void* stream);
 

@@ -94,6 +94,12 @@ def test_pool_qk_reorder_v_errors(A):
     assert qkv_call(A, G(A, d=96)) == 2
     assert qkv_call(A, G(A, B=0)) == 1
     assert A._lib.abla_pool_qk_reorder_v(None, 1, FAKE, FAKE, FAKE, FAKE2, FAKE2, FAKE2, None) == 1
+    # The pooling-only form (v = v_rt = NULL) checks the rest the same way.
+    for n in ("q", "k", "qbar", "kbar"):
+        assert qkv_call(A, g, v=None, v_rt=None, **{n: None}) == 1, n
+    assert qkv_call(A, g, v=None, v_rt=None, kbar=ctypes.c_void_p((1 << 32) + 64)) == 1  # kbar inside q
+    assert qkv_call(A, g, v=None, v_rt=None, dtype=7) == 1
+    assert qkv_call(A, G(A, d=96), v=None, v_rt=None) == 2
 
 
 def mask_call(A, g, p, ws=FAKE, ws_bytes=1 << 40, q=FAKE, k=FAKE, words=FAKE2, counts=FAKE2):

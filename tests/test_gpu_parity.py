@@ -79,8 +79,10 @@ def test_pool_qk_reorder_v(A, dtype, d, geo):
     sq = A.reorder(q, geom, pool_only=True)
     sk = A.reorder(k, geom, pool_only=True)
     sv = A.reorder(v, geom, layout="block_t")
+    pq, pk, none = A.pool_qk_reorder_v(q, k, None, geom)  # the pooling-only form
     torch.cuda.synchronize()
     assert torch.equal(qbar, sq) and torch.equal(kbar, sk)
+    assert none is None and torch.equal(pq, sq) and torch.equal(pk, sk)
     assert np.array_equal(_bits(v_rt), _bits(sv))
     ref_t = R.reorder(_bits(v), og).reshape(B, H, og.nb, 64, d).transpose(0, 1, 2, 4, 3)
     assert np.array_equal(_bits(v_rt), ref_t)
@@ -784,3 +786,29 @@ def test_reorder_launches_split_over_many_blocks(A):
     for h0 in range(0, H, 1 << 19):
         h1 = min(H, h0 + (1 << 19))
         assert torch.equal(z[0, h0:h1], x[0, h0:h1])
+
+
+# ---------------------------------------------------------------- the default V path
+@pytest.mark.parametrize("over,short", [(dict(mode="dyn", tau=2.0), True), (dict(mode="cdf", thr=1.0), False)],
+                         ids=["short-lists", "long-lists"])
+def test_default_v_path_follows_the_mask(A, over, short):
+    """fuse_v=None (bf16) picks the original-order V read when the first mask's mean kept count
+    per row is at most FUSE_V_MAX_MEAN_COUNT, the channel-major V pass otherwise; either way the
+    outputs equal both explicit paths bit for bit, on the first call and on the next. Inputs:
+    the video recipe at 12 x 32 x 64 tokens (384 blocks), two heads."""
+    w = WORKLOADS["480p"].with_(H=2, T=12, Hs=32, Ws=64, **over)
+    geom, og = PT.geoms(w.B, w.H, w.T, w.Hs, w.Ws, w.d, w.P)
+    q, k, v = make_qkv(w, device=DEV)
+    p = A.MaskParams(mode=w.mode, thr=w.thr, tau=w.tau, sta=tuple(w.sta))
+    auto = A.NablaAttention(geom, p, want_lse=True)
+    fixed = {fv: A.NablaAttention(geom, p, want_lse=True, fuse_v=fv) for fv in (False, True)}
+    for call in range(2):
+        auto(q, k, v)
+        for run in fixed.values():
+            run(q, k, v)
+        torch.cuda.synchronize()
+        mean = float(auto.counts.sum()) / (w.B * w.H * geom.nb)
+        assert (mean <= A.FUSE_V_MAX_MEAN_COUNT) == short, mean
+        assert auto.fuse_v == short and (auto.v_rt is None) == short
+        for run in fixed.values():
+            assert torch.equal(auto.out, run.out) and torch.equal(auto.lse, run.lse), call
