@@ -389,7 +389,8 @@ def report(args):
         mode = {"cdf": f"cdf {w.thr}", "dyn": f"dyn tau={w.tau}",
                 "static": f"static gamma={w.gamma} lambda={w.lam}"}[w.mode]
         heads = ", ".join(f"{x:.3f}" for x in per_head[:12]) + (" ..." if len(per_head) > 12 else "")
-        print(f"| {w.name} ({w.dtype}, {w.N} tok) | {mode} | {r['keep_fraction']:.4f} | "
+        vpath = "V original order" if r["v_original"] else "V pass"
+        print(f"| {w.name} ({w.dtype}, {w.N} tok; {vpath}) | {mode} | {r['keep_fraction']:.4f} | "
               f"{r['ms_reorder']:.4f} ({r['reorder_gbs'] / 1e3:.2f}); {r['ms_reorder_graph']:.4f} "
               f"({r['reorder_gbs_graph'] / 1e3:.2f}) | {r['ms_mask']:.4f} "
               f"({mask_bytes / (r['ms_mask'] * 1e-3) / 1e9:,.0f}) | {r['ms_attn']:.4f} / {r['ms_attn_stage']:.4f} | "
