@@ -892,34 +892,40 @@ __device__ void desc_exclusive_scan(int* h, int n, int* part) {
 // Workgroup x of k_pair_order writes the queue of XCD x; `total` is the sum of all kept
 // counts (each row belongs to exactly one pair); `wpart` (16 ints), `tail_gi` and `tail_cost`
 // (kQueueTail ints each) are LDS scratch.
-__device__ void xcd_queue(const int32_t* __restrict__ counts, int32_t* __restrict__ order, int nb, int F, int pairs,
-                          int bhs, int x, long long total, int* wpart, int* tail_gi, int* tail_cost) {
-  const int t = threadIdx.x, lane = t & 63, wv = t >> 6;
+// Queue rank k of XCD x in the column order (workgroup 8k + x): the pair index (b, h, pair)
+// flattened, before the long-first and tail reorderings.
+__device__ __forceinline__ int column_item(int k, int x, int F, int pairs, int bhs) {
   const int C = pairs / F;
   const int G = column_run_width(C);
-  const int grid = bhs * pairs;
-  const int full = (grid / (8 * G * C)) * 8 * G * C;
+  const int full = (bhs * pairs / (8 * G * C)) * 8 * G * C;
+  const int b = 8 * k + x;
+  int logical = b;
+  if (b < full) {
+    const int col = (k / (G * C)) * 8 * G + x * G + (k / C) % G;
+    logical = col * C + k % C;
+  }
+  const int h = logical / pairs, pos = logical - h * pairs;
+  return h * pairs + (pos % C) * F + pos / C;  // column pos / C, frame pair pos % C
+}
+// Kept count of pair gi (the sum of its blocks' list lengths).
+__device__ __forceinline__ int pair_cost(const int32_t* __restrict__ counts, int gi, int nb, int F, int pairs) {
+  const int h = gi / pairs, pair = gi - h * pairs;
+  int ba, bb;
+  pair_blocks(pair, F, nb, ba, bb);
+  const int32_t* c = counts + (long long)h * nb;
+  int k = ba >= 0 ? min(max(c[ba], 0), nb) : 0;
+  if (bb >= 0) k += min(max(c[bb], 0), nb);
+  return k;
+}
 
-  auto item = [&](int k) {  // queue rank k of this XCD = workgroup 8k + x
-    const int b = 8 * k + x;
-    int logical = b;
-    if (b < full) {
-      const int col = (k / (G * C)) * 8 * G + x * G + (k / C) % G;
-      logical = col * C + k % C;
-    }
-    const int h = logical / pairs, pos = logical - h * pairs;
-    return h * pairs + (pos % C) * F + pos / C;  // column pos / C, frame pair pos % C
-  };
-  auto pair_cost = [&](int gi) {  // kept count of the pair
-    const int h = gi / pairs, pair = gi - h * pairs;
-    int ba, bb;
-    pair_blocks(pair, F, nb, ba, bb);
-    const int32_t* c = counts + (long long)h * nb;
-    int k = ba >= 0 ? min(max(c[ba], 0), nb) : 0;
-    if (bb >= 0) k += min(max(c[bb], 0), nb);
-    return k;
-  };
-  auto is_long = [&](int gi) { return 4ll * pair_cost(gi) * grid > 5ll * total; };  // above 1.25x the mean
+// pre_gi / pre_cost: this thread's queue item k = t and its cost, already fetched by the
+// caller when the queue has at most 1024 items (else ignored and fetched here).
+__device__ void xcd_queue(const int32_t* __restrict__ counts, int32_t* __restrict__ order, int nb, int F, int pairs,
+                          int bhs, int x, long long total, int* wpart, int* tail_gi, int* tail_cost, int pre_gi,
+                          int pre_cost) {
+  const int t = threadIdx.x, lane = t & 63, wv = t >> 6;
+  const int grid = bhs * pairs;
+  auto long_cost = [&](int cost) { return 4ll * cost * grid > 5ll * total; };  // above 1.25x the mean
   auto block_scan = [&](int v, int& total_out) {  // exclusive prefix of v over the workgroup
     int incl = v;
 #pragma unroll
@@ -940,8 +946,13 @@ __device__ void xcd_queue(const int32_t* __restrict__ counts, int32_t* __restric
   };
 
   const int n_x = (grid - x + 7) / 8;
+  const bool one = n_x <= 1024;  // one item per thread: its gi and cost stay in registers
   int cnt = 0;
-  for (int k = t; k < n_x; k += 1024) cnt += is_long(item(k)) ? 1 : 0;
+  if (one)
+    cnt = t < n_x && long_cost(pre_cost) ? 1 : 0;
+  else
+    for (int k = t; k < n_x; k += 1024)
+      cnt += long_cost(pair_cost(counts, column_item(k, x, F, pairs, bhs), nb, F, pairs));
   int nlong;
   block_scan(cnt, nlong);
   // The last kQueueTail positions (two generations of the XCD's resident workgroups) are
@@ -952,8 +963,9 @@ __device__ void xcd_queue(const int32_t* __restrict__ counts, int32_t* __restric
   for (int c0 = 0; c0 < n_x; c0 += 1024) {
     const int k = c0 + t;
     const bool valid = k < n_x;
-    const int gi = valid ? item(k) : 0;
-    const bool lg = valid && is_long(gi);
+    const int gi = !valid ? 0 : one ? pre_gi : column_item(k, x, F, pairs, bhs);
+    const int cost = !valid ? 0 : one ? pre_cost : pair_cost(counts, gi, nb, F, pairs);
+    const bool lg = valid && long_cost(cost);
     int both;
     const int v = (lg ? 1 : 0) | ((valid && !lg) ? 1 << 16 : 0);  // two counts <= 1024, packed
     const int ex = block_scan(v, both);
@@ -961,7 +973,7 @@ __device__ void xcd_queue(const int32_t* __restrict__ counts, int32_t* __restric
       const int p = lg ? base_l + (ex & 0xffff) : base_s + (ex >> 16);
       if (p >= tail0) {
         tail_gi[p - tail0] = gi;
-        tail_cost[p - tail0] = pair_cost(gi);
+        tail_cost[p - tail0] = cost;
       } else {
         order[8 * p + x] = gi;
       }
@@ -1004,6 +1016,19 @@ __global__ __launch_bounds__(1024) void k_pair_order(const int32_t* __restrict__
   __shared__ int scan_part[16];
   __shared__ long long wsum[16];
   const int t = threadIdx.x, lane = t & 63, wv = t >> 6;
+  const int bhs = (int)(rows / nb);
+
+  // Workgroups 0-7 write the XCD queues if the lists are short: with one queue item per thread
+  // they fetch its kept count now, while the mean is summed (both loads in flight at once).
+  int pre_gi = 0, pre_cost = 0;
+  if (blockIdx.x < 8) {
+    const int x = (int)blockIdx.x;
+    const int n_x = (bhs * pairs - x + 7) / 8;
+    if (n_x <= 1024 && t < n_x) {
+      pre_gi = column_item(t, x, F, pairs, bhs);
+      pre_cost = pair_cost(counts, pre_gi, nb, F, pairs);
+    }
+  }
 
   const long long nsum = rows < kMeanSample ? rows : kMeanSample;
   long long part = 0;
@@ -1023,10 +1048,10 @@ __global__ __launch_bounds__(1024) void k_pair_order(const int32_t* __restrict__
     mode_out[0] = column ? 1 : 0;
     mode_out[1] = 0;  // the attention's tail counter (claim_item)
   }
-  const int bhs = (int)(rows / nb);
   if (column) {
     if (blockIdx.x < 8)
-      xcd_queue(counts, order, nb, F, pairs, bhs, (int)blockIdx.x, total, scan_part, hist, hist + kQueueTail);
+      xcd_queue(counts, order, nb, F, pairs, bhs, (int)blockIdx.x, total, scan_part, hist, hist + kQueueTail, pre_gi,
+                pre_cost);
     return;
   }
 
