@@ -21,7 +21,8 @@
 //
 // k_bwd_dkdv, one workgroup of four waves per key block, walks the key block's column list with
 // the roles of Q and K swapped: S = Q K^T and dP = dO V^T with the query rows permuted, then
-// dV^T += dO^T P and dK^T += Q^T dS with dO^T and Q^T read by transpose loads.
+// dV^T += dO^T P and dK^T += Q^T dS with dO^T and Q^T read by transpose loads; the key block's V
+// tile stays in LDS for the whole walk.
 //
 // Both kernels double-buffer their tiles in LDS (the loads of tile u+1 run during the products
 // of tile u) and write their gradient rows in the original token order. bf16 inputs and
@@ -535,8 +536,11 @@ __device__ __forceinline__ void half_step(const uint32_t* trel, uint32_t qbase, 
 // double-buffered in LDS; the key block's V tile stays in LDS for the whole walk (the B
 // operand of dP, read like a Q tile), its K rows in registers. Lane l's key is the one in LDS
 // row kh*32 + l%32 of such a tile (the tiles' row permutation), and the tiles' L2 / D rows come
-// straight from global memory (two 32-byte runs per lane and step, issued before the
-// products). Keeping V in registers too spilled 20 registers per lane at two waves per SIMD.
+// straight from global memory by buffer loads (32 bytes of each per lane and 16-query half: the
+// first half's after the S and dP products, the second's during the first half). The transposed
+// Q and dO operands are read two channel tiles at a time. With V in registers as well, or four
+// channel tiles' operands read at once, the kernel spilled at two waves per SIMD (20 and 6
+// registers per lane).
 template <int D>
 __global__ __launch_bounds__(kBwdThreads) __attribute__((amdgpu_waves_per_eu(2, 2))) void k_bwd_dkdv(DkvArgs a) {
   constexpr int TB = kBlock * D * 2;
