@@ -767,6 +767,24 @@ def test_first_step_launches_split_over_many_blocks(A):
         assert torch.equal(v_rt[0, h0:h1, 0], q[0, h0:h1].transpose(1, 2))
 
 
+def test_pooling_only_first_step_split_over_many_blocks(A):
+    """The pooling-only form of the first step (v = v_rt = NULL) over 2^21 + 3 one-block heads:
+    2*B*H*nb just above 2^22 workgroups, two launches; the means exactly."""
+    H = (1 << 21) + 3
+    geom = A.Geometry(B=1, H=H, T=1, Hs=8, Ws=8, d=64)
+    assert 2 * H * geom.nb > (1 << 22)
+    q, pat, off = _head_pattern(H, torch.bfloat16)
+    k = q.neg()
+    qbar = torch.full((1, H, 1, 64), math.nan, dtype=torch.float64, device=DEV)
+    kbar = torch.full_like(qbar, math.nan)
+    _, _, none = A.pool_qk_reorder_v(q, k, None, geom, qbar=qbar, kbar=kbar)
+    torch.cuda.synchronize()
+    mean = pat.double().mean(dim=0)[None, :] + off.double()[:, None]
+    assert none is None
+    assert torch.equal(qbar.view(H, 64), mean)
+    assert torch.equal(kbar.view(H, 64), -mean)
+
+
 def test_reorder_launches_split_over_many_blocks(A):
     """2^22 + 3 heads of one block: the reorder grid runs in two launches. Forward into the
     channel-major layout with pooling (the transposed tile and the column means), then the inverse
