@@ -1,9 +1,10 @@
 """Benchmark of the block-sparse attention forward layer on one MI355X.
 
 One step = the whole path over one layer's Q/K/V already resident in HBM:
-block means of Q and K (one read each), reorder V (channel-major blocks), build
-the mask, block-sparse attention reading Q and K in the original order and
-writing O in the original order.
+block means of Q and K (one read each), reorder V into channel-major blocks in the
+same launch (unless the first call's mask selected reading V in the original order),
+build the mask, block-sparse attention reading Q and K in the original order and
+writing O in the original order. `timed_steps_ms` lists each timed step's duration.
 
 Prints ONE JSON line. `value` is the dense-equivalent throughput
 4*B*H*N^2*d / (time per layer); `ms_per_step` is the time per layer. Steps are
@@ -209,9 +210,11 @@ def measure(name, steps, warmup, use_graph=False):
     # call (the visiting-order kernel and the attention kernel) sits between two HIP events on
     # the stream, which gives the attention's duration inside the layer from the same steps.
     marks = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
+    starts = [torch.cuda.Event(enable_timing=True) for _ in range(steps)]
     done = []
 
     def step_marked():
+        starts[len(done)].record(stream)
         run.reorder_pool(q, k, v)
         run.mask()
         a, b = marks[len(done)]
@@ -225,6 +228,9 @@ def measure(name, steps, warmup, use_graph=False):
     ms_step = timed(step if graph is not None else step_marked, steps, stream)
     wall = (time.perf_counter() - t0) * 1e3 / steps
     ms_attn_layer = sum(a.elapsed_time(b) for a, b in marks) / steps if graph is None else None
+    # Each timed step from its start to the next step's start (the last one to its attention's end).
+    step_ms = ([starts[i].elapsed_time(starts[i + 1]) for i in range(steps - 1)]
+               + [starts[-1].elapsed_time(marks[-1][1])]) if graph is None else None
     ms_eager = timed(lambda: run(q, k, v), steps, stream) if graph is not None else ms_step
 
     # Per-stage averages (same inputs, state left by the path).
@@ -259,7 +265,7 @@ def measure(name, steps, warmup, use_graph=False):
         attn_in_layer=ms_attn_layer is not None, dense_flops=dense, kept_flops=kept_fl,
         reorder_gbs=reorder_bytes / (ms_reorder * 1e-3) / 1e9, tensor_bytes=tensor_bytes, reorder_bytes=reorder_bytes,
         ms_reorder_graph=ms_reorder_graph, reorder_gbs_graph=reorder_bytes / (ms_reorder_graph * 1e-3) / 1e9,
-        counts=run.counts, run=run, q=q, k=k, v=v, v_original=run.fuse_v,
+        counts=run.counts, run=run, q=q, k=k, v=v, v_original=run.fuse_v, step_ms=step_ms,
     )
 
 
@@ -484,6 +490,7 @@ def main():
         },
         "ms_per_layer": round(r["ms_step"], 4),
         "ms_per_layer_eager": round(r["ms_eager"], 4),
+        "timed_steps_ms": [round(x, 4) for x in r["step_ms"]] if r["step_ms"] is not None else None,
         "single_steps": {"reps": len(r["warm"]), "ms_median": round(median(r["warm"]), 4),
                          "ms_min": round(r["warm"][0], 4)},
         "cold_cache": {"reps": len(r["cold"]), "evict_bytes": EVICT_BYTES, "ms_median": round(median(r["cold"]), 4),
