@@ -486,6 +486,9 @@ SPARSE = [
     ("video-dyn-tau2", dict(H=2, T=12, Hs=32, Ws=64, mode="dyn", tau=2.0)),
     ("video-cdf-no-sta", dict(H=2, T=16, Hs=32, Ws=56, mode="cdf", thr=0.7, sta=(0, 0, 0))),
     ("video-dyn-odd-T", dict(H=2, T=11, Hs=40, Ws=64, mode="dyn", tau=3.0)),
+    # head dim 64 (its own kernel instances): keep about 7 % and 11 %, the second with an odd T
+    ("video-d64-dyn", dict(H=2, T=12, Hs=32, Ws=64, d=64, mode="dyn", tau=2.0)),
+    ("video-d64-cdf-odd-T", dict(H=2, T=13, Hs=32, Ws=64, d=64, mode="cdf", thr=0.5)),
 ]
 
 
