@@ -237,6 +237,7 @@ def measure(name, steps, warmup, use_graph=False):
     ms_reorder = timed(lambda: run.reorder_pool(q, k, v), steps, stream)
     ms_reorder_graph = graph_ms(lambda: run.reorder_pool(q, k, v))
     ms_mask = timed(run.mask, steps, stream)
+    ms_mask_graph = graph_ms(run.mask)
     ms_attn_stage = timed(run.attend, steps, stream)  # back to back, no other stage between
     ms_attn = ms_attn_layer if ms_attn_layer is not None else ms_attn_stage
 
@@ -261,7 +262,8 @@ def measure(name, steps, warmup, use_graph=False):
     return dict(
         w=w, geom=geom, kept=kept, keep_fraction=kept / total, ms_step=ms_step, wall_ms_step=wall, ms_eager=ms_eager,
         graph=graph is not None, warm=warm, cold=cold,
-        ms_reorder=ms_reorder, ms_mask=ms_mask, ms_attn=ms_attn, ms_attn_stage=ms_attn_stage,
+        ms_reorder=ms_reorder, ms_mask=ms_mask, ms_mask_graph=ms_mask_graph, ms_attn=ms_attn,
+        ms_attn_stage=ms_attn_stage,
         attn_in_layer=ms_attn_layer is not None, dense_flops=dense, kept_flops=kept_fl,
         reorder_gbs=reorder_bytes / (ms_reorder * 1e-3) / 1e9, tensor_bytes=tensor_bytes, reorder_bytes=reorder_bytes,
         ms_reorder_graph=ms_reorder_graph, reorder_gbs_graph=reorder_bytes / (ms_reorder_graph * 1e-3) / 1e9,
@@ -374,7 +376,7 @@ def report(args):
           f"(datasheet {MFMA_BF16_PEAK_TFLOPS:,.0f} / {FP32_PEAK_TFLOPS}); HBM streams (libabla_probe, 2 GiB): "
           f"read {hbm_read:,.0f} GB/s, copy {hbm_copy:,.0f} GB/s (datasheet {HBM_PEAK_GBS:,.0f})\n")
     fwd_attn_ms = {}
-    print("| workload | mask | keep | first step ms (TB/s); kernel-only from a graph | mask ms (GB/s) | "
+    print("| workload | mask | keep | first step ms (TB/s); kernel-only from a graph | mask ms (GB/s); from a graph | "
           "attention ms: in the layer / back to back | layer ms | "
           "single layers: median / min / cold median ms | "
           "dense-eq TFLOP/s (layer / attn) | actual TFLOP/s | of datasheet peak | of MFMA loop | of GEMM ref | "
@@ -399,7 +401,8 @@ def report(args):
         print(f"| {w.name} ({w.dtype}, {w.N} tok; {vpath}) | {mode} | {r['keep_fraction']:.4f} | "
               f"{r['ms_reorder']:.4f} ({r['reorder_gbs'] / 1e3:.2f}); {r['ms_reorder_graph']:.4f} "
               f"({r['reorder_gbs_graph'] / 1e3:.2f}) | {r['ms_mask']:.4f} "
-              f"({mask_bytes / (r['ms_mask'] * 1e-3) / 1e9:,.0f}) | {r['ms_attn']:.4f} / {r['ms_attn_stage']:.4f} | "
+              f"({mask_bytes / (r['ms_mask'] * 1e-3) / 1e9:,.0f}); {r['ms_mask_graph']:.4f} | "
+              f"{r['ms_attn']:.4f} / {r['ms_attn_stage']:.4f} | "
               f"{r['ms_step']:.4f} | "
               f"{median(r['warm']):.4f} / {r['warm'][0]:.4f} / {median(r['cold']):.4f} | "
               f"{r['dense_flops'] / (r['ms_step'] * 1e-3) / 1e12:,.1f} / "
@@ -496,6 +499,7 @@ def main():
         "cold_cache": {"reps": len(r["cold"]), "evict_bytes": EVICT_BYTES, "ms_median": round(median(r["cold"]), 4),
                        "ms_min": round(r["cold"][0], 4)},
         "ms_per_stage": {"reorder_pool_qkv": round(r["ms_reorder"], 4), "mask": round(r["ms_mask"], 4),
+                         "mask_kernel_graph": round(r["ms_mask_graph"], 4),
                          "attention": round(r["ms_attn_stage"], 4)},
         "ms_attention_in_layer": round(r["ms_attn"], 4) if r["attn_in_layer"] else None,
         "keep_fraction": round(r["keep_fraction"], 5),
@@ -537,6 +541,7 @@ def main():
                                   if s["w"].dtype == w.dtype else None),
             "keep_fraction": round(s["keep_fraction"], 5),
             "ms_per_stage": {"reorder_pool_qkv": round(s["ms_reorder"], 4), "mask": round(s["ms_mask"], 4),
+                             "mask_kernel_graph": round(s["ms_mask_graph"], 4),
                              "attention": round(s["ms_attn_stage"], 4)},
             "ms_attention_in_layer": round(s["ms_attn"], 4) if s["attn_in_layer"] else None,
             "reorder_pool_gbs": round(s["reorder_gbs"], 1),
