@@ -28,8 +28,9 @@
  * - All pointers are device pointers owned by the caller, contiguous,
  *   row-major and 16-byte aligned (a misaligned pointer is rejected with
  *   ABLA_ERR_INVALID). The library never allocates, frees or
- *   synchronises, keeps no pointer after a call returns and has no mutable
- *   global state. Work is enqueued on `stream` (a hipStream_t; NULL is the
+ *   synchronises and keeps no pointer after a call returns; its only mutable
+ *   global state is the scratch array of abla_sparse_attn_fwd_noalloc (one
+ *   per GPU, below). Work is enqueued on `stream` (a hipStream_t; NULL is the
  *   default stream) and results are valid when the stream reaches them.
  * - Arguments are validated on the host before anything is enqueued, so
  *   every ABLA_ERR_INVALID / _UNSUPPORTED / _WORKSPACE return has enqueued
